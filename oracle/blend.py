@@ -1,0 +1,314 @@
+"""Oracle blending: position remap + stitch, KV deviation, selection, selective recompute.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Readings taken where the pages leave a step open (each is listed with its reason in the
+design notes of the repository):
+
+* selection layer ``s`` is a 0-based layer index; layers < s are recomputed on every row
+  (CacheBlend, "The Chicken-and-Egg Problem": fully prefill an early layer, pick its HKVD
+  tokens, reuse that set for the remaining layers; Request Order Matters §2.2: one
+  selection at a configured layer, no reranking),
+* the deviation is the squared L2 norm of K only, over all kv heads and head dims
+  (Request Order Matters §2.2 Eq. 1), accumulated in fp64 and returned as fp32,
+* budget k = max(1, floor(rho * N)) for rho > 0 and 0 for rho = 0, in integer arithmetic
+  with rho given as a rational (Request Order Matters §2.2 Eq. 2; QCFuse §2.1.3 Eq. 6),
+* token top-k orders by (deviation descending, index ascending); NaN counts as +inf and
+  -0 equals +0; the output is ascending,
+* document-aligned spans (Request Order Matters §2.3): span score is the fp64 sequential
+  sum over the span divided by its length (Eq. 3), spans rank by (score desc, span index
+  asc), whole spans are taken while they fit and the walk stops at the first that does not,
+  and the remainder r is the window [a, a+r) of that span with the largest fp64 total,
+  computed as P[a+r] - P[a] over the span's fp64 running sum P; ties take the smallest a,
+* the query U follows the context, is never ranked and is recomputed at every layer >= s
+  (QCFuse §2.1.1: U is processed online and is not part of the reusable cache),
+* at layer s only the selected rows and U replace the stitched cache (QCFuse Eq. 7).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .model import rms_norm, rope, layer_rows, k_rows, full_prefill
+
+
+# ------------------------------------------------------------------ budget
+
+def budget(n_ctx: int, rho_num: int, rho_den: int) -> int:
+    """Request Order Matters §2.2 Eq. 2: k = max(1, floor(r * N)); k = 0 when r = 0
+    (the direct-reuse endpoint of QCFuse §4.1.4). r = rho_num / rho_den, integers only."""
+    if rho_num < 0 or rho_den <= 0 or rho_num > rho_den:
+        raise ValueError("ratio must be in [0, 1]")
+    if rho_num == 0 or n_ctx == 0:
+        return 0
+    return max(1, (n_ctx * rho_num) // rho_den)
+
+
+# ------------------------------------------------------------------ position remap + stitch
+
+def reposition(k_rows_at_src, delta: int, theta: float, ft=np.float32):
+    """QCFuse Eq. 4 remap Pi_i for RoPE keys: a key encoded at position p moves to p + delta by
+    one more rotation by delta (CacheBlend, "Why You Can't Just Concatenate": re-positioned
+    by composing rotations). k_rows_at_src: [n, Hkv, hd]."""
+    n = k_rows_at_src.shape[0]
+    return rope(k_rows_at_src, np.full(n, delta, dtype=np.int64), theta, ft)
+
+
+def stitch(k_store, v_store, chunk_table, n_ctx, layers: Sequence[int], theta, ft=np.float32,
+           k_out=None, v_out=None, n_total: Optional[int] = None):
+    """QCFuse Eq. 4: KV^PIC(C) = [Pi_1(KV_1); ...; Pi_m(KV_m)].
+
+    k_store/v_store: [Ly, rows, Hkv, hd]; chunk_table: rows of (store_row, src_pos, dst_pos,
+    length): the chunk's cache rows start at ``store_row`` and were encoded at positions
+    src_pos.. ; they land at request rows dst_pos.. . Keys are rotated by dst - src, values
+    are copied. Returns (K, V) of shape [Ly, n_total, Hkv, hd] (rows >= n_ctx left zero)."""
+    ly, _, hkv, hd = k_store.shape
+    n_total = n_ctx if n_total is None else n_total
+    if k_out is None:
+        k_out = np.zeros((ly, n_total, hkv, hd), dtype=ft)
+        v_out = np.zeros_like(k_out)
+    for l in layers:
+        for (row, src, dst, ln) in chunk_table:
+            k_out[l, dst:dst + ln] = reposition(np.asarray(k_store[l, row:row + ln]), dst - src, theta, ft)
+            v_out[l, dst:dst + ln] = np.asarray(v_store[l, row:row + ln], dtype=ft)
+    return k_out, v_out
+
+
+# ------------------------------------------------------------------ deviation
+
+def kv_deviation(k_new, k_ref):
+    """Request Order Matters §2.2 Eq. 1: d_i = ||K_i^current - K_i^cached||_2^2 over every kv head
+    and head dim, accumulated in fp64, returned as fp32 [n]."""
+    a = np.asarray(k_new, dtype=np.float64).reshape(len(k_new), -1)
+    b = np.asarray(k_ref, dtype=np.float64).reshape(len(k_ref), -1)
+    diff = a - b
+    return np.sum(diff * diff, axis=1).astype(np.float32)
+
+
+# ------------------------------------------------------------------ selection
+
+def _canonical(d):
+    d = np.array(d, dtype=np.float32, copy=True)
+    d[np.isnan(d)] = np.float32(np.inf)
+    d[d == 0] = np.float32(0.0)  # -0 -> +0
+    return d
+
+
+def select_topk(d, k: int) -> np.ndarray:
+    """Token top-k (CacheBlend, "Quantifying the Damage": HKVD tokens are the top r% by
+    deviation; Request Order Matters §2.2: LMCache picks the k largest d_i). Order:
+    deviation descending, lower index first among equals. Output: ascending int32 [k]."""
+    d = _canonical(d)
+    n = len(d)
+    if not 0 <= k <= n:
+        raise ValueError("k out of range")
+    order = np.argsort(-d, kind="stable")  # stable: equal values keep index order
+    return np.sort(order[:k]).astype(np.int32)
+
+
+def _seq_sum(x) -> float:
+    s = 0.0
+    for v in x:
+        s += float(v)
+    return s
+
+
+def select_doc_spans(d, k: int, bounds) -> np.ndarray:
+    """Document-aligned selection (Request Order Matters §2.3 and Eq. 3).
+
+    bounds: strictly increasing span boundaries, bounds[0] = 0, bounds[-1] = len(d).
+    1. rho_j = S_j / |S_j| with S_j the fp64 sum of the span in index order.
+    2. rank spans by rho_j descending, lower span index first among equals.
+    3. walk the ranking taking whole spans while they fit in the remaining budget; stop at
+       the first span that does not fit.
+    4. if r > 0 tokens remain, take from that span the window [a, a+r) whose fp64 total
+       P[a+r] - P[a] (P = the span's running fp64 sum from its start) is largest, smallest a
+       first among equals.
+    Output: ascending int32 [k]."""
+    d = _canonical(d)
+    bounds = [int(b) for b in bounds]
+    n = len(d)
+    if not 0 <= k <= n:
+        raise ValueError("k out of range")
+    if bounds[0] != 0 or bounds[-1] != n or any(b1 <= b0 for b0, b1 in zip(bounds, bounds[1:])):
+        raise ValueError("bad span bounds")
+    spans = list(zip(bounds[:-1], bounds[1:]))
+    score = [_seq_sum(d[a:b]) / float(b - a) for a, b in spans]
+    ranking = sorted(range(len(spans)), key=lambda j: (-score[j], j))
+    chosen: List[int] = []
+    remaining = k
+    for j in ranking:
+        if remaining == 0:
+            break
+        a, b = spans[j]
+        if b - a <= remaining:
+            chosen.extend(range(a, b))
+            remaining -= b - a
+            continue
+        # first span that does not fit: best window of length `remaining` inside it
+        run = [0.0]
+        for v in d[a:b]:
+            run.append(run[-1] + float(v))
+        best_a, best = a, None
+        for start in range(0, (b - a) - remaining + 1):
+            tot = run[start + remaining] - run[start]
+            if best is None or tot > best:
+                best, best_a = tot, a + start
+        chosen.extend(range(best_a, best_a + remaining))
+        remaining = 0
+        break
+    return np.array(sorted(chosen), dtype=np.int32)
+
+
+# ------------------------------------------------------------------ blended prefill
+
+@dataclasses.dataclass
+class BlendResult:
+    k: np.ndarray        # fused K [Ly, L, Hkv, hd]
+    v: np.ndarray        # fused V
+    out: np.ndarray      # RMSNorm(h) of the query rows [U, d]
+    sel: np.ndarray      # selected context positions, ascending [k]
+    dev: np.ndarray      # deviation at the selection layer [N] (empty for full prefill)
+    hidden: np.ndarray   # residual stream [L, d] after the last layer
+
+
+def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer: int, k: int,
+                  mode: str = "token", span_bounds=None, ft=np.float32, n_layers=None) -> BlendResult:
+    """Blended prefill of one request: context C (n_ctx rows) followed by the query U.
+
+    1. Stitch: layers s..Ly-1 of the request cache are the remapped chunk caches (QCFuse Eq. 4).
+    2. h = embedding of every token.
+    3. Layers l < s: ordinary prefill of all rows (their K/V overwrite the cache).
+    4. Layer s: current keys of the context rows, deviation against the stitched keys
+       (Request Order Matters Eq. 1), then the recompute set P (top-k or document spans).
+    5. sel = P followed by the query rows N..L-1; layers l >= s run only on ``sel``: fresh
+       K/V are scattered into the cache at sel, the selected rows attend over the fused cache
+       and only their hidden rows change (CacheBlend "Selective Recompute Without Skipping";
+       QCFuse Eq. 7).
+    6. Output: the fused K/V of every layer and RMSNorm of the query rows.
+
+    mode "all" is ordinary full prefill of every row at every layer (QCFuse Eq. 2)."""
+    cfg = model.cfg
+    ly = cfg.n_layers if n_layers is None else n_layers
+    tokens = np.asarray(tokens)
+    L = len(tokens)
+    N = int(n_ctx)
+    hkv, hd = cfg.n_kv_heads, cfg.head_dim
+    kc = np.zeros((ly, L, hkv, hd), dtype=ft)
+    vc = np.zeros_like(kc)
+    h = np.asarray(model.embed[tokens], dtype=ft)
+    pos_all = np.arange(L)
+    if mode == "all":
+        for l in range(ly):
+            h = layer_rows(cfg, model.layer(l), h, pos_all, kc[l], vc[l], ft)
+        out = rms_norm(h[N:], model.final_norm, cfg.rms_eps, ft)
+        return BlendResult(kc, vc, out, np.arange(N, dtype=np.int32), np.zeros(0, np.float32), h)
+
+    s = int(sel_layer)
+    if not 0 <= s < ly:
+        raise ValueError("selection layer out of range")
+    stitch(k_store, v_store, chunk_table, N, range(s, ly), cfg.rope_theta, ft, kc, vc)
+    for l in range(s):
+        h = layer_rows(cfg, model.layer(l), h, pos_all, kc[l], vc[l], ft)
+
+    w_s = model.layer(s)
+    if N > 0:
+        k_cur = k_rows(cfg, w_s, h[:N], np.arange(N), ft)
+        dev = kv_deviation(k_cur, kc[s, :N])
+    else:
+        dev = np.zeros(0, np.float32)
+    if mode == "token":
+        P = select_topk(dev, k)
+    elif mode == "doc":
+        P = select_doc_spans(dev, k, span_bounds)
+    else:
+        raise ValueError("unknown mode " + str(mode))
+    sel = np.concatenate([P.astype(np.int64), np.arange(N, L)])
+    for l in range(s, ly):
+        w = w_s if l == s else model.layer(l)
+        if len(sel):
+            h[sel] = layer_rows(cfg, w, h[sel], sel, kc[l], vc[l], ft)
+    out = rms_norm(h[N:], model.final_norm, cfg.rms_eps, ft)
+    return BlendResult(kc, vc, out, P, dev, h)
+
+
+def direct_reuse(model, tokens, n_ctx, k_store, v_store, chunk_table, ft=np.float32, n_layers=None):
+    """The rho = 0 endpoint written from its own definition (QCFuse §2.1.2): the context cache is
+    the stitched chunk caches at every layer, untouched; only the query rows are computed,
+    attending over that cache. Returns (K, V, normed query hidden)."""
+    cfg = model.cfg
+    ly = cfg.n_layers if n_layers is None else n_layers
+    tokens = np.asarray(tokens)
+    L, N = len(tokens), int(n_ctx)
+    kc, vc = stitch(k_store, v_store, chunk_table, N, range(ly), cfg.rope_theta, ft, n_total=L)
+    hq = np.asarray(model.embed[tokens[N:]], dtype=ft)
+    pos = np.arange(N, L)
+    for l in range(ly):
+        hq = layer_rows(cfg, model.layer(l), hq, pos, kc[l], vc[l], ft)
+    return kc, vc, rms_norm(hq, model.final_norm, cfg.rms_eps, ft)
+
+
+# ------------------------------------------------------------------ rolling window
+
+class RollingWindow:
+    """Rolling agent window (Request Order Matters §2.1 and §4.1): a window of ``n_docs``
+    documents; each step evicts the oldest, appends a new document and asks a fresh query.
+    The store persists across steps: a new document gets a standalone prefill at position 0;
+    in write-back mode every document's fused K/V and its new base position are written back
+    after the step (§5: each call both consumes and updates the cache state), in pristine
+    mode the store keeps the standalone caches."""
+
+    def __init__(self, model, n_docs, doc_len, n_query, rho_num, rho_den, mode="doc",
+                 sel_layer=1, write_back=True, ft=np.float32, n_layers=None, doc_tokens=None,
+                 query_tokens=None):
+        self.model = model
+        self.n_docs, self.doc_len, self.n_query = n_docs, doc_len, n_query
+        self.rho = (rho_num, rho_den)
+        self.mode, self.s, self.write_back = mode, sel_layer, write_back
+        self.ft = ft
+        self.n_layers = model.cfg.n_layers if n_layers is None else n_layers
+        self.doc_tokens = doc_tokens
+        self.query_tokens = query_tokens
+        self.store = {}   # doc id -> [K (Ly, len, Hkv, hd), V, base position]
+        self.t = 0
+
+    def window(self, t):
+        return list(range(t, t + self.n_docs))
+
+    def _ensure(self, j):
+        if j not in self.store:
+            toks = self.doc_tokens(j)
+            kc, vc = chunk_prefill_for(self.model, toks, self.ft, self.n_layers)
+            self.store[j] = [kc, vc, 0]
+
+    def step(self):
+        t = self.t
+        docs = self.window(t)
+        for j in list(self.store):
+            if j not in docs:
+                del self.store[j]
+        for j in docs:
+            self._ensure(j)
+        toks = np.concatenate([self.doc_tokens(j) for j in docs] + [self.query_tokens(t)]).astype(np.int32)
+        N = self.n_docs * self.doc_len
+        k_store = np.concatenate([self.store[j][0] for j in docs], axis=1)
+        v_store = np.concatenate([self.store[j][1] for j in docs], axis=1)
+        table = [(i * self.doc_len, self.store[j][2], i * self.doc_len, self.doc_len)
+                 for i, j in enumerate(docs)]
+        k = budget(N, *self.rho)
+        bounds = [i * self.doc_len for i in range(self.n_docs + 1)]
+        res = blend_prefill(self.model, toks, N, k_store, v_store, table, self.s, k, self.mode,
+                            bounds, self.ft, self.n_layers)
+        if self.write_back:
+            for i, j in enumerate(docs):
+                a = i * self.doc_len
+                self.store[j] = [res.k[:, a:a + self.doc_len].copy(), res.v[:, a:a + self.doc_len].copy(), a]
+        self.t += 1
+        return res, toks, table
+
+
+def chunk_prefill_for(model, toks, ft, n_layers):
+    kc, vc, _, _ = full_prefill(model, toks, ft, n_layers)
+    return kc, vc
