@@ -1,0 +1,209 @@
+/*
+ * cf.h — C ABI of libcf: blended prefill (CacheBlend-style selective KV recompute) on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method, in the pages' terms:
+ *  - QCFuse: Query-Aware Cache Fusion via Compressed View for Efficient RAG Serving, §2.1:
+ *    a request is context chunks c_1..c_m (N tokens) followed by a query U (Table 1, Eq. 1);
+ *    each chunk has its own cache prefilled standalone at local positions 0.. (Eq. 3); at
+ *    request time the caches are position-remapped and stitched in order (Eq. 4); a set P of
+ *    context positions (ratio rho = |P|/N, Eq. 6) is recomputed under the current request and
+ *    replaces the stitched entries (Eq. 7).
+ *  - CacheBlend: Reusing KV Caches When Your Text Isn't a Prefix: RoPE keys move by composing
+ *    rotations ("Why You Can't Just Concatenate"); P is the high-KV-deviation tokens
+ *    ("Quantifying the Damage"); each layer recomputes only the selected rows, scatters their
+ *    K/V into the blended cache, lets them attend over the full blended K/V and updates only
+ *    their hidden rows ("Selective Recompute Without Skipping"); the selection is made once on
+ *    an early layer ("The Chicken-and-Egg Problem").
+ *  - Request Order Matters: Cache-History Sensitivity in Selective KV-Cache Reuse for Rolling
+ *    Agents: deviation d_i = ||K_i^current - K_i^cached||_2^2 (§2.2 Eq. 1), budget
+ *    k = max(1, floor(r N)) (Eq. 2), one selection at a configured layer, document-aligned
+ *    spans (§2.3, Eq. 3).
+ *
+ * General rules for every entry point
+ *  - Memory: every tensor argument is a device pointer owned by the caller unless the
+ *    argument says "host". The library never frees, retains or reallocates caller memory.
+ *    Scratch memory is a caller-provided device workspace whose size comes from the matching
+ *    *_workspace_size query; the library allocates only the RoPE tables of a cf_ctx.
+ *  - Layout: row-major. A K or V cache layer is [rows][n_kv_heads][head_dim]; layer l of a
+ *    multi-layer cache starts at base + l * layer_stride elements. Weight matrices are
+ *    [out_features][in_features] (y = x W^T). Element type is the model dtype (CF_F32 or CF_BF16)
+ *    except where an argument says fp32.
+ *  - Streams: work is enqueued on `stream` (NULL = the null stream); no call synchronises the
+ *    host with the device. Calls on different streams touching disjoint buffers are
+ *    independent; calls that share buffers must be ordered by the caller.
+ *  - Errors: arguments are validated on the host before anything is enqueued. On failure the
+ *    call returns a non-zero cf_status, enqueues nothing, and cf_last_error() describes the
+ *    problem. A failed launch returns CF_EHIP. Faults inside kernels surface at the caller's
+ *    next synchronisation. Device-side index arrays (sel, tokens) are clamped inside the
+ *    kernels so that bad values cannot read or write out of bounds; results are then
+ *    unspecified. No C++ exception crosses this interface.
+ */
+#ifndef CF_H
+#define CF_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CF_OK = 0,
+  CF_EINVAL = 1,        /* bad pointer, range or ordering */
+  CF_ESHAPE = 2,        /* inconsistent sizes */
+  CF_EDTYPE = 3,        /* unknown element type */
+  CF_EUNSUPPORTED = 4,  /* valid but not implemented here (e.g. head_dim not 64/128) */
+  CF_EWORKSPACE = 5,    /* workspace missing or smaller than the size query returned */
+  CF_EHIP = 6           /* a HIP runtime call failed */
+} cf_status;
+
+typedef enum { CF_F32 = 0, CF_BF16 = 1 } cf_dtype;
+
+typedef enum {
+  CF_SEL_TOKEN_TOPK = 0, /* the k tokens of largest deviation (CacheBlend HKVD top-r%) */
+  CF_SEL_DOC_SPANS = 1,  /* document-aligned spans (Request Order Matters §2.3) */
+  CF_SEL_ALL = 2         /* every row at every layer: ordinary full prefill (QCFuse Eq. 2) */
+} cf_select_mode;
+
+/* Decoder shape. Pre-norm layer: RMSNorm -> Q,K,V projections -> optional per-head RMS
+ * qk-norm -> RoPE -> causal grouped-query attention (query head h reads kv head
+ * h / (n_q_heads / n_kv_heads)) -> O projection + residual -> RMSNorm -> SwiGLU
+ * (silu(x Wg^T) * (x Wu^T)) Wd^T + residual. RoPE rotates the pair (x_j, x_{j+hd/2}) by
+ * pos * rope_theta^(-2j/hd). */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab, qk_norm;
+  float rope_theta, rms_eps;
+  int32_t dtype; /* cf_dtype of matrices, embedding and K/V caches */
+} cf_model_cfg;
+
+/* Device pointers of one layer. Gains are fp32; matrices are the model dtype. */
+typedef struct {
+  const float* attn_norm; /* [d_model] */
+  const void* wq;         /* [n_q_heads*head_dim][d_model] */
+  const void* wk;         /* [n_kv_heads*head_dim][d_model] */
+  const void* wv;         /* [n_kv_heads*head_dim][d_model] */
+  const void* wo;         /* [d_model][n_q_heads*head_dim] */
+  const float* mlp_norm;  /* [d_model] */
+  const void* w_gate;     /* [d_ffn][d_model] */
+  const void* w_up;       /* [d_ffn][d_model] */
+  const void* w_down;     /* [d_model][d_ffn] */
+  const float* q_norm;    /* [head_dim], used iff qk_norm, else may be NULL */
+  const float* k_norm;    /* [head_dim], used iff qk_norm, else may be NULL */
+} cf_layer_weights;
+
+/* Opaque context: a copy of the model shape, the device it was created on, and RoPE cos/sin
+ * tables for offsets 0..max_pos-1 (angles computed in fp64 on the host, stored fp32). */
+typedef struct cf_ctx cf_ctx;
+
+/* Create a context on `device` (a HIP device ordinal). Requires head_dim in {64, 128},
+ * n_q_heads a multiple of n_kv_heads, d_model, d_ffn and head dims multiples of 8, and
+ * max_pos >= the largest position or re-position offset used later. Allocates the RoPE
+ * tables (the only memory the library owns); `*out` receives the context. */
+cf_status cf_ctx_create(const cf_model_cfg* cfg, int32_t max_pos, int32_t device, cf_ctx** out);
+void cf_ctx_destroy(cf_ctx* ctx);
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char* cf_last_error(void);
+
+/* Library version and build string. */
+const char* cf_version(void);
+
+/* --------------------------------------------------------------------- cf_rope_reposition
+ * QCFuse Eq. 4 (position remap Pi_i and stitching) with CacheBlend's rotation composition.
+ * For each chunk i of the host table chunk_tab[m][4] = {store_row, src_pos, dst_pos, len}
+ * and each layer l in [layer_begin, layer_end):
+ *   K_blend[l][dst_pos + t] = R(dst_pos - src_pos) K_store[l][store_row + t]
+ *   V_blend[l][dst_pos + t] = V_store[l][store_row + t]            for t < len,
+ * where R(delta) rotates each pair (x_j, x_{j+hd/2}) of every kv head by delta * omega_j
+ * (delta may be negative). Rows are kvd = n_kv_heads * head_dim elements wide.
+ * store_rows / blend_rows bound the row indices; strides are in elements and must be at
+ * least rows * kvd. |dst_pos - src_pos| must be < max_pos of the context. Chunk
+ * destinations must not overlap. Up to CF_MAX_CHUNKS chunks per call. */
+#define CF_MAX_CHUNKS 256
+cf_status cf_rope_reposition(const cf_ctx* ctx, const void* k_store, const void* v_store,
+                             int64_t store_layer_stride, int32_t store_rows, void* k_blend,
+                             void* v_blend, int64_t blend_layer_stride, int32_t blend_rows,
+                             const int32_t* chunk_tab /* host [m][4] */, int32_t m,
+                             int32_t layer_begin, int32_t layer_end, hipStream_t stream);
+
+/* --------------------------------------------------------------------- cf_kv_deviation
+ * Request Order Matters §2.2 Eq. 1: dev[i] = sum_c (k_new[i][c] - k_ref[i][c])^2 over the
+ * kv_dim entries of row i, accumulated in fp32. Rows are ld_new / ld_ref elements apart;
+ * new_dtype / ref_dtype are cf_dtype values. dev: fp32 [n_tok]. */
+cf_status cf_kv_deviation(const void* k_new, int32_t new_dtype, int64_t ld_new, const void* k_ref,
+                          int32_t ref_dtype, int64_t ld_ref, float* dev, int32_t n_tok,
+                          int32_t kv_dim, hipStream_t stream);
+
+/* --------------------------------------------------------------------- cf_topk_select
+ * Choose k of the n positions by their deviation dev (fp32 [n]) and write them ascending to
+ * out_idx (int32 [k]).
+ *  CF_SEL_TOKEN_TOPK: the k largest values (CacheBlend HKVD; Request Order Matters §2.2).
+ *    Total order: value descending, then index ascending; NaN ranks as +inf, -0 equals +0.
+ *  CF_SEL_DOC_SPANS: Request Order Matters §2.3, Eq. 3. span_bounds (host, [n_spans+1],
+ *    strictly increasing, 0 .. n) delimit the spans. Spans rank by (fp64 sequential span sum
+ *    / span length) descending, lower span index first; whole spans are taken while they fit
+ *    in the remaining budget, the walk stopping at the first span that does not; the r tokens
+ *    still owed are the window [a, a+r) of that span maximising P[a+r] - P[a], P being the
+ *    span's fp64 running sum from its start (smallest a among equals). Exactly k tokens.
+ * Results are exact (bit-identical to any implementation of the same order). 0 <= k <= n.
+ * n_spans <= CF_MAX_SPANS. ws: device workspace of cf_topk_workspace_size(n, mode) bytes. */
+#define CF_MAX_SPANS 256
+size_t cf_topk_workspace_size(int32_t n, int32_t mode);
+cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode,
+                         const int32_t* span_bounds /* host */, int32_t n_spans, int32_t* out_idx,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------- cf_blend_layer
+ * One decoder layer run only on the rows sel[0..n_sel) (CacheBlend, "Selective Recompute
+ * Without Skipping"): gather + RMSNorm -> Q,K,V on those rows -> qk-norm + RoPE at position
+ * sel[j] -> scatter K,V into k_cache/v_cache at rows sel[j] -> each selected row attends over
+ * cache rows t <= sel[j] of the full blended cache -> O projection + residual -> SwiGLU MLP +
+ * residual, written back to hidden[sel[j]] only. Rows not in sel are untouched.
+ *  hidden:  fp32 [L][d_model], updated in place at the selected rows.
+ *  k_cache, v_cache: this layer's cache [L][n_kv_heads][head_dim] (model dtype).
+ *  sel: device int32 [n_sel], strictly ascending, values in [0, L).
+ *  ws: device workspace of cf_blend_layer_workspace_size(ctx, L, n_sel) bytes.
+ * With sel = 0..L-1 this is one layer of ordinary causal prefill. */
+size_t cf_blend_layer_workspace_size(const cf_ctx* ctx, int32_t L, int32_t n_sel);
+cf_status cf_blend_layer(const cf_ctx* ctx, const cf_layer_weights* w /* host struct */,
+                         float* hidden, void* k_cache, void* v_cache, const int32_t* sel,
+                         int32_t n_sel, int32_t L, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------- cf_blend_prefill
+ * The whole blended prefill of one request (N context tokens then U query tokens, L = N+U):
+ *  1. cf_rope_reposition of layers sel_layer..n_layers-1 from the chunk store into k_out/v_out.
+ *  2. hidden = embedding rows of tokens (device int32 [L]; ids outside [0, vocab) give NaN
+ *     rows).
+ *  3. layers l < sel_layer: every row (ordinary prefill; their K/V overwrite k_out/v_out[l]).
+ *  4. layer sel_layer: current keys of the N context rows, deviation against the stitched keys
+ *     (cf_kv_deviation), selection of k positions (cf_topk_select with `mode`).
+ *  5. sel = those positions followed by N..L-1; layers sel_layer.. run cf_blend_layer on sel.
+ *  6. out_hidden (fp32 [U][d_model]) = final RMSNorm of the U query rows.
+ * mode CF_SEL_ALL runs every layer on every row instead (store arguments unused and may be
+ * NULL; k ignored): this is ordinary full prefill, used both for standalone chunk caches and
+ * as the baseline. Positions are 0..L-1.
+ *  layers: host array [n_layers] of device-pointer structs; embed [vocab][d_model];
+ *  final_norm fp32 [d_model]; chunk store as in cf_rope_reposition;
+ *  k_out/v_out: [n_layers] layers of [L][kvd], out_layer_stride elements apart (>= L*kvd);
+ *  out_sel: optional device int32 [k], the selected context positions ascending;
+ *  out_dev: optional device fp32 [N], the deviation at the selection layer.
+ *  0 <= k <= N; 0 <= sel_layer < n_layers; ws from cf_blend_prefill_workspace_size. */
+size_t cf_blend_prefill_workspace_size(const cf_ctx* ctx, int32_t N, int32_t U, int32_t k,
+                                       int32_t mode);
+cf_status cf_blend_prefill(const cf_ctx* ctx, const cf_layer_weights* layers, const void* embed,
+                           const float* final_norm, const int32_t* tokens, int32_t N, int32_t U,
+                           const void* k_store, const void* v_store, int64_t store_layer_stride,
+                           int32_t store_rows, const int32_t* chunk_tab /* host [m][4] */,
+                           int32_t m, int32_t sel_layer, int32_t k, int32_t mode,
+                           const int32_t* span_bounds /* host */, int32_t n_spans, void* k_out,
+                           void* v_out, int64_t out_layer_stride, float* out_hidden,
+                           int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CF_H */

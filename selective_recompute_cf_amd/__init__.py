@@ -1,0 +1,236 @@
+"""Python binding of libcf (blended prefill on AMD MI355X).
+
+Argument marshalling only: every call forwards device pointers of torch tensors and torch's
+current HIP stream to the C entry points declared in include/cf.h, and every step of the
+path runs in libcf's HIP kernels. The shared library must be built first
+(``python -m selective_recompute_cf_amd.build``); without it every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcf.so")
+
+CF_OK, CF_EINVAL, CF_ESHAPE, CF_EDTYPE, CF_EUNSUPPORTED, CF_EWORKSPACE, CF_EHIP = range(7)
+CF_F32, CF_BF16 = 0, 1
+CF_SEL_TOKEN_TOPK, CF_SEL_DOC_SPANS, CF_SEL_ALL = 0, 1, 2
+MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL}
+EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
+           "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
+           "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
+           "cf_blend_prefill"]
+
+
+class CfError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libcf status {status}: {msg}")
+        self.status = status
+
+
+class ModelCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "d_ffn", "vocab", "qk_norm")] + \
+               [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down", "q_norm", "k_norm")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcf.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m selective_recompute_cf_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "cf_ctx_create": (i32, [ctypes.POINTER(ModelCfg), i32, i32, ctypes.POINTER(vp)]),
+        "cf_ctx_destroy": (None, [vp]),
+        "cf_last_error": (ctypes.c_char_p, []),
+        "cf_version": (ctypes.c_char_p, []),
+        "cf_rope_reposition": (i32, [vp, vp, vp, i64, i32, vp, vp, i64, i32, vp, i32, i32, i32, vp]),
+        "cf_kv_deviation": (i32, [vp, i32, i64, vp, i32, i64, vp, i32, i32, vp]),
+        "cf_topk_workspace_size": (sz, [i32, i32]),
+        "cf_topk_select": (i32, [vp, i32, i32, i32, vp, i32, vp, vp, sz, vp]),
+        "cf_blend_layer_workspace_size": (sz, [vp, i32, i32]),
+        "cf_blend_layer": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, vp, i32, i32, vp, sz, vp]),
+        "cf_blend_prefill_workspace_size": (sz, [vp, i32, i32, i32, i32]),
+        "cf_blend_prefill": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32, vp,
+                                   i32, i32, i32, i32, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != CF_OK:
+        raise CfError(status, lib().cf_last_error().decode())
+
+
+def version() -> str:
+    return lib().cf_version().decode()
+
+
+# ----------------------------------------------------------------------------- torch plumbing
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _host_i32(rows: Optional[Iterable[Iterable[int]]]):
+    if rows is None:
+        return None, 0
+    flat: List[int] = [int(v) for r in rows for v in (r if isinstance(r, (list, tuple)) else [r])]
+    arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    return arr, len(flat)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return CF_BF16
+    if t.dtype == torch.float32:
+        return CF_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class Context:
+    """A cf_ctx: model shape + RoPE tables on one device."""
+
+    def __init__(self, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab, qk_norm,
+                 rope_theta, rms_eps, dtype: str, max_pos: int, device: int = 0):
+        self.cfg = ModelCfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab, int(bool(qk_norm)),
+                            float(rope_theta), float(rms_eps), CF_BF16 if dtype == "bf16" else CF_F32)
+        self.dtype = dtype
+        self.device = device
+        self.max_pos = max_pos
+        h = ctypes.c_void_p()
+        _check(lib().cf_ctx_create(ctypes.byref(self.cfg), max_pos, device, ctypes.byref(h)))
+        self.handle = h
+
+    @classmethod
+    def from_model_cfg(cls, m, max_pos: int, device: int = 0, dtype: Optional[str] = None):
+        return cls(m.n_layers, m.d_model, m.n_q_heads, m.n_kv_heads, m.head_dim, m.d_ffn, m.vocab, m.qk_norm,
+                   m.rope_theta, m.rms_eps, dtype or m.dtype, max_pos, device)
+
+    def close(self):
+        if getattr(self, "handle", None) and self.handle.value:
+            lib().cf_ctx_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def kv_dim(self) -> int:
+        return self.cfg.n_kv_heads * self.cfg.head_dim
+
+    # ------------------------------------------------------------------ entry points
+    def rope_reposition(self, k_store, v_store, k_blend, v_blend, chunk_tab: Sequence[Sequence[int]],
+                        layer_begin: int, layer_end: int, store_rows: Optional[int] = None,
+                        blend_rows: Optional[int] = None, store_layer_stride: Optional[int] = None,
+                        blend_layer_stride: Optional[int] = None):
+        """Tensors [Ly, rows, kvd] (or any layout with the given strides, in elements)."""
+        tab, nflat = _host_i32(chunk_tab)
+        sr = store_rows if store_rows is not None else k_store.shape[-2]
+        br = blend_rows if blend_rows is not None else k_blend.shape[-2]
+        sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
+        bls = blend_layer_stride if blend_layer_stride is not None else br * self.kv_dim
+        _check(lib().cf_rope_reposition(self.handle, _ptr(k_store), _ptr(v_store), sls, sr, _ptr(k_blend),
+                                        _ptr(v_blend), bls, br, tab, nflat // 4, layer_begin, layer_end,
+                                        _stream(k_blend.device)))
+
+    def blend_layer_workspace_size(self, L: int, n_sel: int) -> int:
+        return int(lib().cf_blend_layer_workspace_size(self.handle, L, n_sel))
+
+    def blend_layer(self, weights: LayerWeights, hidden, k_cache, v_cache, sel, ws):
+        n_sel = 0 if sel is None else int(sel.numel())
+        _check(lib().cf_blend_layer(self.handle, ctypes.byref(weights), _ptr(hidden), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(sel), n_sel, hidden.shape[0], _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(hidden.device)))
+
+    def blend_prefill_workspace_size(self, N: int, U: int, k: int, mode: str) -> int:
+        return int(lib().cf_blend_prefill_workspace_size(self.handle, N, U, k, MODES[mode]))
+
+    def blend_prefill(self, layers, embed, final_norm, tokens, N: int, U: int, k_store, v_store,
+                      chunk_tab, sel_layer: int, k: int, mode: str, span_bounds, k_out, v_out, out_hidden,
+                      ws, out_sel=None, out_dev=None, store_rows: Optional[int] = None,
+                      store_layer_stride: Optional[int] = None, out_layer_stride: Optional[int] = None):
+        """layers: a ctypes array of LayerWeights (see ``layer_array``)."""
+        tab, nflat = _host_i32(chunk_tab)
+        spans, nb = _host_i32(span_bounds)
+        sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
+        sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
+        ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        _check(lib().cf_blend_prefill(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
+                                      _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, k,
+                                      MODES[mode], spans, max(0, nb - 1), _ptr(k_out), _ptr(v_out), ols,
+                                      _ptr(out_hidden), _ptr(out_sel), _ptr(out_dev), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(tokens.device)))
+
+
+def layer_struct(t: dict) -> LayerWeights:
+    """LayerWeights from a dict of device tensors (keys as in cf_layer_weights)."""
+    return LayerWeights(*[_ptr(t.get(n)) for n, _ in LayerWeights._fields_])
+
+
+def layer_array(layers: Sequence[dict]):
+    arr = (LayerWeights * len(layers))()
+    for i, t in enumerate(layers):
+        arr[i] = layer_struct(t)
+    return arr
+
+
+def kv_deviation(k_new, k_ref, dev, kv_dim: Optional[int] = None):
+    """dev[i] = sum_c (k_new[i, c] - k_ref[i, c])^2; 2-D tensors [n, >= kv_dim]."""
+    n = k_new.shape[0]
+    kvd = kv_dim if kv_dim is not None else k_new.shape[1]
+    _check(lib().cf_kv_deviation(_ptr(k_new), _dtype_code(k_new), k_new.stride(0), _ptr(k_ref), _dtype_code(k_ref),
+                                 k_ref.stride(0), _ptr(dev), n, kvd, _stream(dev.device)))
+
+
+def topk_workspace_size(n: int, mode: str) -> int:
+    return int(lib().cf_topk_workspace_size(n, MODES[mode]))
+
+
+def topk_select(dev, k: int, out_idx, mode: str = "token", span_bounds=None, ws=None):
+    spans, nb = _host_i32(span_bounds)
+    _check(lib().cf_topk_select(_ptr(dev), dev.numel(), k, MODES[mode], spans, max(0, nb - 1), _ptr(out_idx),
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev.device)))
+
+
+def budget(n_ctx: int, rho_num: int, rho_den: int) -> int:
+    """k = max(1, floor(rho * N)) for rho > 0, 0 for rho = 0, in integer arithmetic
+    (Request Order Matters §2.2 Eq. 2)."""
+    if rho_num < 0 or rho_den <= 0 or rho_num > rho_den:
+        raise ValueError("ratio must be in [0, 1]")
+    if rho_num == 0 or n_ctx == 0:
+        return 0
+    return max(1, (n_ctx * rho_num) // rho_den)

@@ -1,0 +1,541 @@
+// libcf host side: argument validation, workspace layout, launch plan and the C ABI of
+// include/cf.h. Every step of the path is a kernel launch on the caller's stream; the host
+// never waits for the device inside a call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "cf.h"
+#include "kernels.h"
+
+struct cf_ctx {
+  cf_model_cfg cfg;
+  int device;
+  int max_pos;
+  int n_cu;
+  float* cos_t;  // [max_pos][head_dim/2]
+  float* sin_t;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+cf_status fail(cf_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define CF_CHECK(cond, status, ...) \
+  do {                              \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define CF_HIP(expr)                                                                         \
+  do {                                                                                       \
+    hipError_t e_ = (expr);                                                                  \
+    if (e_ != hipSuccess) return fail(CF_EHIP, "%s: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Makes the context's device current for the duration of a call and restores the caller's.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+cf::Dt dt_of(const cf_ctx* c) { return c->cfg.dtype == CF_BF16 ? cf::BF16 : cf::F32; }
+size_t esize(const cf_ctx* c) { return c->cfg.dtype == CF_BF16 ? 2 : 4; }
+size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ------------------------------------------------------------------ workspace of one layer pass
+struct LayerWs {
+  size_t x, qkv, q, ao, hs, act, gu, part, opart, mlpart, total;
+  int attn_splits, attn_split_len, gemm_splits;
+};
+
+LayerWs layer_ws(const cf_ctx* c, int L, int R) {
+  const cf_model_cfg& m = c->cfg;
+  const size_t es = esize(c);
+  const size_t d = m.d_model, qd = (size_t)m.n_q_heads * m.head_dim, kvd = (size_t)m.n_kv_heads * m.head_dim;
+  const size_t F = m.d_ffn;
+  LayerWs w{};
+  cf::attn_plan(dt_of(c), R, L, m.n_q_heads, m.n_kv_heads, m.head_dim, c->n_cu, &w.attn_splits, &w.attn_split_len);
+  w.gemm_splits = std::max(cf::gemm_splits(dt_of(c), R, (int)d, (int)qd, cf::EPI_RESID, c->n_cu),
+                           cf::gemm_splits(dt_of(c), R, (int)d, (int)F, cf::EPI_RESID, c->n_cu));
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  w.x = take((size_t)R * d * es);
+  w.qkv = take((size_t)R * (qd + 2 * kvd) * 4);
+  w.q = take((size_t)R * qd * es);
+  w.ao = take((size_t)R * qd * es);
+  w.hs = take((size_t)R * d * 4);
+  w.act = take((size_t)R * F * es);
+  w.gu = take(m.dtype == CF_BF16 ? 0 : (size_t)R * 2 * F * 4);
+  w.part = take(w.gemm_splits > 1 ? (size_t)w.gemm_splits * R * d * 4 : 0);
+  w.opart = take(w.attn_splits > 1 ? (size_t)w.attn_splits * R * qd * 4 : 0);
+  w.mlpart = take(w.attn_splits > 1 ? (size_t)w.attn_splits * R * m.n_q_heads * 2 * 4 : 0);
+  w.total = off;
+  return w;
+}
+
+struct PrefillWs {
+  size_t hidden, sel, ident, dev, topk, layer, total;
+};
+
+PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode) {
+  const int L = N + U;
+  PrefillWs p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  p.hidden = take((size_t)L * c->cfg.d_model * 4);
+  p.sel = take((size_t)L * 4);
+  p.ident = take((size_t)L * 4);
+  p.dev = take((size_t)std::max(N, 1) * 4);
+  p.topk = take(mode == CF_SEL_DOC_SPANS ? (size_t)(N + 1) * 8 : 0);
+  // the layer scratch serves full-row layers (R = L) and selected-row layers (R = k + U)
+  const LayerWs a = layer_ws(c, L, L), b = layer_ws(c, L, std::min(L, k + U));
+  p.layer = take(std::max(a.total, b.total));
+  p.total = off;
+  return p;
+}
+
+cf_status check_layer(const cf_ctx* c, const cf_layer_weights* w, int idx) {
+  CF_CHECK(w, CF_EINVAL, "layer %d: null weight struct", idx);
+  const void* ptrs[] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
+  const char* names[] = {"attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"};
+  for (int i = 0; i < 9; ++i) {
+    CF_CHECK(ptrs[i], CF_EINVAL, "layer %d: %s is NULL", idx, names[i]);
+    CF_CHECK(aligned16(ptrs[i]), CF_EINVAL, "layer %d: %s is not 16-byte aligned", idx, names[i]);
+  }
+  if (c->cfg.qk_norm) {
+    CF_CHECK(w->q_norm && w->k_norm, CF_EINVAL, "layer %d: qk_norm model needs q_norm and k_norm", idx);
+  }
+  return CF_OK;
+}
+
+// ------------------------------------------------------------------ one layer on rows `sel`
+cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, void* kc, void* vc,
+                    const int* sel, int n, int L, char* ws, const LayerWs& lw, hipStream_t st) {
+  if (n == 0) return CF_OK;
+  const cf_model_cfg& m = c->cfg;
+  const cf::Dt dt = dt_of(c);
+  const int d = m.d_model, hd = m.head_dim, qd = m.n_q_heads * hd, kvd = m.n_kv_heads * hd, F = m.d_ffn;
+  void* X = ws + lw.x;
+  float* QKV = reinterpret_cast<float*>(ws + lw.qkv);
+  void* Q = ws + lw.q;
+  void* AO = ws + lw.ao;
+  float* HS = reinterpret_cast<float*>(ws + lw.hs);
+  void* ACT = ws + lw.act;
+
+  CF_HIP(cf::launch_rmsnorm_rows(dt, hidden, sel, n, L, d, w->attn_norm, m.rms_eps, X, d, st));
+  cf::GemmArgs g{};
+  g.dt = dt;
+  g.A = X; g.lda = d;
+  g.B[0] = w->wq; g.B[1] = w->wk; g.B[2] = w->wv; g.nb0 = qd; g.nb1 = qd + kvd;
+  g.M = n; g.N = qd + 2 * kvd; g.K = d; g.splits = 1; g.epi = cf::EPI_F32; g.C = QKV; g.ldc = qd + 2 * kvd;
+  CF_HIP(cf::launch_gemm(g, st));
+
+  cf::QkvPost qp{};
+  qp.qkv = QKV; qp.ld = qd + 2 * kvd; qp.rows = sel; qp.n = n; qp.L = L;
+  qp.hq = m.n_q_heads; qp.hkv = m.n_kv_heads; qp.hd = hd; qp.qk_norm = m.qk_norm;
+  qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = m.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
+  qp.q_out = Q; qp.k_cache = kc; qp.v_cache = vc;
+  CF_HIP(cf::launch_qkv_post(dt, qp, st));
+
+  cf::AttnArgs at{};
+  at.dt = dt; at.q = Q; at.ldq = qd; at.pos = sel; at.n = n; at.k = kc; at.v = vc; at.L = L;
+  at.hq = m.n_q_heads; at.hkv = m.n_kv_heads; at.hd = hd; at.out = AO; at.ldo = qd;
+  cf::attn_plan(dt, n, L, m.n_q_heads, m.n_kv_heads, hd, c->n_cu, &at.splits, &at.split_len);
+  at.o_part = reinterpret_cast<float*>(ws + lw.opart);
+  at.ml_part = reinterpret_cast<float*>(ws + lw.mlpart);
+  CF_HIP(cf::launch_attention(at, st));
+
+  float* part = reinterpret_cast<float*>(ws + lw.part);
+  auto resid_gemm = [&](const void* A, int lda, const void* B, int K, const float* resid, const int* rrows,
+                        float* out, const int* orows) -> cf_status {
+    cf::GemmArgs r{};
+    r.dt = dt; r.A = A; r.lda = lda; r.B[0] = r.B[1] = r.B[2] = B; r.nb0 = r.nb1 = d;
+    r.M = n; r.N = d; r.K = K; r.L = L;
+    r.splits = cf::gemm_splits(dt, n, d, K, cf::EPI_RESID, c->n_cu);
+    if (r.splits > 1) {
+      r.epi = cf::EPI_PARTIAL; r.C = part; r.ldc = d;
+      CF_HIP(cf::launch_gemm(r, st));
+      CF_HIP(cf::launch_splitk_reduce(part, r.splits, n, d, resid, rrows, out, orows, L, st));
+    } else {
+      r.epi = cf::EPI_RESID; r.resid = resid; r.resid_rows = rrows; r.out = out; r.out_rows = orows;
+      CF_HIP(cf::launch_gemm(r, st));
+    }
+    return CF_OK;
+  };
+  cf_status s = resid_gemm(AO, qd, w->wo, qd, hidden, sel, HS, nullptr);
+  if (s != CF_OK) return s;
+
+  CF_HIP(cf::launch_rmsnorm_rows(dt, HS, nullptr, n, n, d, w->mlp_norm, m.rms_eps, X, d, st));
+  cf::GemmArgs gu{};
+  gu.dt = dt; gu.A = X; gu.lda = d; gu.B[0] = w->w_gate; gu.B[1] = w->w_up; gu.B[2] = w->w_up;
+  gu.M = n; gu.K = d; gu.splits = 1;
+  if (dt == cf::BF16) {
+    gu.N = F; gu.nb0 = F; gu.nb1 = F; gu.epi = cf::EPI_SWIGLU; gu.act = ACT; gu.ld_act = F;
+    CF_HIP(cf::launch_gemm(gu, st));
+  } else {
+    float* GU = reinterpret_cast<float*>(ws + lw.gu);
+    gu.N = 2 * F; gu.nb0 = F; gu.nb1 = 2 * F; gu.epi = cf::EPI_F32; gu.C = GU; gu.ldc = 2 * F;
+    CF_HIP(cf::launch_gemm(gu, st));
+    CF_HIP(cf::launch_swiglu(dt, GU, n, F, ACT, st));
+  }
+  return resid_gemm(ACT, F, w->w_down, F, HS, nullptr, hidden, sel);
+}
+
+cf_status check_ctx(const cf_ctx* c) {
+  CF_CHECK(c, CF_EINVAL, "null context");
+  return CF_OK;
+}
+
+cf_status check_chunks(const cf_ctx* c, const int32_t* tab, int m, int store_rows, int blend_rows,
+                       int N_cover) {
+  CF_CHECK(m >= 0 && m <= CF_MAX_CHUNKS, CF_EINVAL, "chunk count %d outside [0, %d]", m, CF_MAX_CHUNKS);
+  CF_CHECK(m == 0 || tab, CF_EINVAL, "null chunk table");
+  std::vector<std::pair<int, int>> dst;
+  for (int i = 0; i < m; ++i) {
+    const int row = tab[4 * i], src = tab[4 * i + 1], dp = tab[4 * i + 2], len = tab[4 * i + 3];
+    CF_CHECK(len > 0, CF_EINVAL, "chunk %d: length %d", i, len);
+    CF_CHECK(row >= 0 && (int64_t)row + len <= store_rows, CF_EINVAL, "chunk %d: store rows [%d, %d) outside [0, %d)",
+             i, row, row + len, store_rows);
+    CF_CHECK(dp >= 0 && (int64_t)dp + len <= blend_rows, CF_EINVAL, "chunk %d: rows [%d, %d) outside [0, %d)", i, dp,
+             dp + len, blend_rows);
+    CF_CHECK(src >= 0, CF_EINVAL, "chunk %d: negative source position", i);
+    CF_CHECK(std::abs((int64_t)dp - src) < c->max_pos, CF_EINVAL, "chunk %d: offset %d not below max_pos %d", i,
+             dp - src, c->max_pos);
+    dst.push_back({dp, len});
+  }
+  std::sort(dst.begin(), dst.end());
+  for (size_t i = 1; i < dst.size(); ++i)
+    CF_CHECK(dst[i - 1].first + dst[i - 1].second <= dst[i].first, CF_EINVAL, "chunk destinations overlap");
+  if (N_cover >= 0) {
+    int at = 0;
+    for (auto& p : dst) {
+      CF_CHECK(p.first == at, CF_EINVAL, "chunks do not tile the context rows [0, %d)", N_cover);
+      at += p.second;
+    }
+    CF_CHECK(at == N_cover, CF_EINVAL, "chunks cover %d rows, context has %d", at, N_cover);
+  }
+  return CF_OK;
+}
+
+cf_status enqueue_reposition(const cf_ctx* c, const void* ks, const void* vs, int64_t sls, void* kb, void* vb,
+                             int64_t bls, const int32_t* tab, int m, int lb, int le, hipStream_t st) {
+  const int kvd = c->cfg.n_kv_heads * c->cfg.head_dim;
+  for (int c0 = 0; c0 < m; c0 += cf::CHUNKS_PER_LAUNCH) {
+    cf::ChunkBatch cb{};
+    cb.n = std::min(cf::CHUNKS_PER_LAUNCH, m - c0);
+    cb.blk0[0] = 0;
+    for (int i = 0; i < cb.n; ++i) {
+      const int32_t* t = tab + 4 * (c0 + i);
+      cb.row[i] = t[0];
+      cb.dst[i] = t[2];
+      cb.len[i] = t[3];
+      cb.delta[i] = t[2] - t[1];
+      cb.blk0[i + 1] = cb.blk0[i] + (t[3] + cf::REPOS_ROWS_PER_BLOCK - 1) / cf::REPOS_ROWS_PER_BLOCK;
+    }
+    CF_HIP(cf::launch_reposition(dt_of(c), ks, vs, sls, kb, vb, bls, cb, kvd, c->cfg.head_dim, c->cos_t, c->sin_t,
+                                 lb, le - lb, st));
+  }
+  return CF_OK;
+}
+
+cf_status check_spans(const int32_t* b, int ns, int n) {
+  CF_CHECK(ns >= 1 && ns <= CF_MAX_SPANS, CF_EINVAL, "span count %d outside [1, %d]", ns, CF_MAX_SPANS);
+  CF_CHECK(b, CF_EINVAL, "null span bounds");
+  CF_CHECK(b[0] == 0 && b[ns] == n, CF_EINVAL, "span bounds must run from 0 to %d", n);
+  for (int i = 0; i < ns; ++i) CF_CHECK(b[i] < b[i + 1], CF_EINVAL, "span bounds not strictly increasing at %d", i);
+  return CF_OK;
+}
+
+cf_status enqueue_select(const float* dev, int n, int k, int mode, const int32_t* bounds, int ns, int* out,
+                         double* ws, hipStream_t st) {
+  if (k == 0) return CF_OK;
+  if (mode == CF_SEL_TOKEN_TOPK) {
+    CF_HIP(cf::launch_topk_token(dev, n, k, out, st));
+  } else {
+    cf::SpanArgs sp{};
+    sp.n_spans = ns;
+    for (int i = 0; i <= ns; ++i) sp.b[i] = bounds[i];
+    CF_HIP(cf::launch_topk_spans(dev, n, k, sp, out, ws, st));
+  }
+  return CF_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* cf_last_error(void) { return g_err.c_str(); }
+
+const char* cf_version(void) { return "libcf 0.1 (gfx950)"; }
+
+cf_status cf_ctx_create(const cf_model_cfg* cfg, int32_t max_pos, int32_t device, cf_ctx** out) {
+  g_err.clear();
+  CF_CHECK(cfg && out, CF_EINVAL, "null argument");
+  const cf_model_cfg& m = *cfg;
+  CF_CHECK(m.dtype == CF_F32 || m.dtype == CF_BF16, CF_EDTYPE, "unknown dtype %d", m.dtype);
+  CF_CHECK(m.n_layers > 0 && m.d_model > 0 && m.n_q_heads > 0 && m.n_kv_heads > 0 && m.d_ffn > 0 && m.vocab > 0,
+           CF_ESHAPE, "non-positive model dimension");
+  CF_CHECK(m.head_dim == 64 || m.head_dim == 128, CF_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", m.head_dim);
+  CF_CHECK(m.n_q_heads % m.n_kv_heads == 0, CF_ESHAPE, "n_q_heads %% n_kv_heads != 0");
+  CF_CHECK(m.n_q_heads / m.n_kv_heads <= 16 && 64 % (m.n_q_heads / m.n_kv_heads) == 0, CF_EUNSUPPORTED,
+           "query heads per kv head must divide 64 and be <= 16");
+  CF_CHECK(m.d_model % 8 == 0 && m.d_ffn % 8 == 0, CF_EUNSUPPORTED, "d_model and d_ffn must be multiples of 8");
+  CF_CHECK(m.rope_theta > 0.f && m.rms_eps >= 0.f, CF_EINVAL, "bad rope_theta or rms_eps");
+  CF_CHECK(max_pos > 0, CF_EINVAL, "max_pos must be positive");
+  int ndev = 0;
+  CF_HIP(hipGetDeviceCount(&ndev));
+  CF_CHECK(device >= 0 && device < ndev, CF_EINVAL, "device %d outside [0, %d)", device, ndev);
+  DeviceGuard guard(device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice(%d) failed", device);
+  cf_ctx* c = new cf_ctx{};
+  c->cfg = m;
+  c->device = device;
+  c->max_pos = max_pos;
+  if (hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || c->n_cu <= 0)
+    c->n_cu = 256;
+  const int half = m.head_dim / 2;
+  std::vector<float> cs((size_t)max_pos * half), sn((size_t)max_pos * half);
+  for (int p = 0; p < max_pos; ++p)
+    for (int j = 0; j < half; ++j) {
+      const double omega = std::pow((double)m.rope_theta, -2.0 * j / (double)m.head_dim);
+      const double ang = (double)p * omega;
+      cs[(size_t)p * half + j] = (float)std::cos(ang);
+      sn[(size_t)p * half + j] = (float)std::sin(ang);
+    }
+  const size_t bytes = cs.size() * sizeof(float);
+  hipError_t e = hipMalloc(&c->cos_t, bytes);
+  if (e == hipSuccess) e = hipMalloc(&c->sin_t, bytes);
+  if (e == hipSuccess) e = hipMemcpy(c->cos_t, cs.data(), bytes, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->sin_t, sn.data(), bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (c->cos_t) (void)hipFree(c->cos_t);
+    if (c->sin_t) (void)hipFree(c->sin_t);
+    delete c;
+    return fail(CF_EHIP, "RoPE table allocation: %s", hipGetErrorString(e));
+  }
+  *out = c;
+  return CF_OK;
+}
+
+void cf_ctx_destroy(cf_ctx* c) {
+  if (!c) return;
+  DeviceGuard guard(c->device);
+  if (c->cos_t) (void)hipFree(c->cos_t);
+  if (c->sin_t) (void)hipFree(c->sin_t);
+  delete c;
+}
+
+cf_status cf_rope_reposition(const cf_ctx* c, const void* k_store, const void* v_store, int64_t sls,
+                             int32_t store_rows, void* k_blend, void* v_blend, int64_t bls, int32_t blend_rows,
+                             const int32_t* tab, int32_t m, int32_t lb, int32_t le, hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  const int64_t kvd = (int64_t)c->cfg.n_kv_heads * c->cfg.head_dim;
+  CF_CHECK(lb >= 0 && lb <= le && le <= c->cfg.n_layers, CF_EINVAL, "layer range [%d, %d) outside [0, %d]", lb, le,
+           c->cfg.n_layers);
+  CF_CHECK(store_rows >= 0 && blend_rows >= 0, CF_EINVAL, "negative row count");
+  if (cf_status s = check_chunks(c, tab, m, store_rows, blend_rows, -1)) return s;
+  if (m == 0 || lb == le) return CF_OK;
+  CF_CHECK(k_store && v_store && k_blend && v_blend, CF_EINVAL, "null cache pointer");
+  CF_CHECK(aligned16(k_store) && aligned16(v_store) && aligned16(k_blend) && aligned16(v_blend), CF_EINVAL,
+           "cache pointers must be 16-byte aligned");
+  CF_CHECK(sls >= store_rows * kvd && bls >= blend_rows * kvd && sls % 8 == 0 && bls % 8 == 0, CF_ESHAPE,
+           "layer strides must hold rows * kvd elements and be multiples of 8");
+  DeviceGuard guard(c->device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  return enqueue_reposition(c, k_store, v_store, sls, k_blend, v_blend, bls, tab, m, lb, le, st);
+}
+
+cf_status cf_kv_deviation(const void* k_new, int32_t new_dtype, int64_t ld_new, const void* k_ref, int32_t ref_dtype,
+                          int64_t ld_ref, float* dev, int32_t n_tok, int32_t kv_dim, hipStream_t st) {
+  g_err.clear();
+  CF_CHECK((new_dtype == CF_F32 || new_dtype == CF_BF16) && (ref_dtype == CF_F32 || ref_dtype == CF_BF16), CF_EDTYPE,
+           "unknown dtype");
+  CF_CHECK(n_tok >= 0 && kv_dim > 0 && kv_dim % 8 == 0, CF_ESHAPE, "kv_dim must be a positive multiple of 8");
+  if (n_tok == 0) return CF_OK;
+  CF_CHECK(k_new && k_ref && dev, CF_EINVAL, "null pointer");
+  CF_CHECK(aligned16(k_new) && aligned16(k_ref), CF_EINVAL, "key pointers must be 16-byte aligned");
+  CF_CHECK(ld_new >= kv_dim && ld_ref >= kv_dim && ld_new % 8 == 0 && ld_ref % 8 == 0, CF_ESHAPE,
+           "row strides must be >= kv_dim and multiples of 8");
+  CF_HIP(cf::launch_deviation(new_dtype == CF_BF16 ? cf::BF16 : cf::F32, k_new, ld_new,
+                              ref_dtype == CF_BF16 ? cf::BF16 : cf::F32, k_ref, ld_ref, dev, n_tok, kv_dim, st));
+  return CF_OK;
+}
+
+size_t cf_topk_workspace_size(int32_t n, int32_t mode) {
+  return mode == CF_SEL_DOC_SPANS && n >= 0 ? al((size_t)(n + 1) * 8) : 0;
+}
+
+cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode, const int32_t* bounds, int32_t ns,
+                         int32_t* out, void* ws, size_t ws_bytes, hipStream_t st) {
+  g_err.clear();
+  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || mode == CF_SEL_DOC_SPANS, CF_EINVAL, "mode %d is not a selection mode", mode);
+  CF_CHECK(n >= 0 && k >= 0 && k <= n, CF_EINVAL, "need 0 <= k <= n (k=%d, n=%d)", k, n);
+  if (mode == CF_SEL_DOC_SPANS) {
+    if (cf_status s = check_spans(bounds, ns, n)) return s;
+    CF_CHECK(k == 0 || (ws && ws_bytes >= cf_topk_workspace_size(n, mode)), CF_EWORKSPACE,
+             "span mode needs %zu workspace bytes", cf_topk_workspace_size(n, mode));
+  }
+  if (k == 0) return CF_OK;
+  CF_CHECK(dev && out, CF_EINVAL, "null pointer");
+  return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), st);
+}
+
+size_t cf_blend_layer_workspace_size(const cf_ctx* c, int32_t L, int32_t n_sel) {
+  if (!c || L <= 0 || n_sel < 0) return 0;
+  return layer_ws(c, L, std::min(n_sel, L)).total;
+}
+
+cf_status cf_blend_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, void* kc, void* vc,
+                         const int32_t* sel, int32_t n_sel, int32_t L, void* ws, size_t ws_bytes, hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  CF_CHECK(L > 0 && L <= c->max_pos, CF_EINVAL, "L=%d outside [1, max_pos=%d]", L, c->max_pos);
+  CF_CHECK(n_sel >= 0 && n_sel <= L, CF_EINVAL, "n_sel=%d outside [0, L=%d]", n_sel, L);
+  if (cf_status s = check_layer(c, w, 0)) return s;
+  if (n_sel == 0) return CF_OK;
+  CF_CHECK(hidden && kc && vc && sel, CF_EINVAL, "null pointer");
+  CF_CHECK(aligned16(hidden) && aligned16(kc) && aligned16(vc), CF_EINVAL, "buffers must be 16-byte aligned");
+  LayerWs lw = layer_ws(c, L, n_sel);
+  CF_CHECK(ws && aligned16(ws) && ws_bytes >= lw.total, CF_EWORKSPACE, "workspace: need %zu bytes, got %zu", lw.total,
+           ws_bytes);
+  DeviceGuard guard(c->device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  return run_layer(c, w, hidden, kc, vc, sel, n_sel, L, static_cast<char*>(ws), lw, st);
+}
+
+size_t cf_blend_prefill_workspace_size(const cf_ctx* c, int32_t N, int32_t U, int32_t k, int32_t mode) {
+  if (!c || N < 0 || U < 0 || N + U <= 0) return 0;
+  if (mode == CF_SEL_ALL) k = N;
+  return prefill_ws(c, N, U, std::max(0, std::min(k, N)), mode).total;
+}
+
+cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* embed, const float* final_norm,
+                           const int32_t* tokens, int32_t N, int32_t U, const void* k_store, const void* v_store,
+                           int64_t sls, int32_t store_rows, const int32_t* tab, int32_t m, int32_t s_layer, int32_t k,
+                           int32_t mode, const int32_t* bounds, int32_t ns, void* k_out, void* v_out, int64_t ols,
+                           float* out_hidden, int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
+                           hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  const cf_model_cfg& mc = c->cfg;
+  const int L = N + U;
+  const int64_t kvd = (int64_t)mc.n_kv_heads * mc.head_dim;
+  CF_CHECK(N >= 0 && U >= 0 && L > 0, CF_EINVAL, "need N, U >= 0 and N + U > 0");
+  CF_CHECK(L <= c->max_pos, CF_EINVAL, "L=%d exceeds max_pos=%d", L, c->max_pos);
+  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || mode == CF_SEL_DOC_SPANS || mode == CF_SEL_ALL, CF_EINVAL, "unknown mode %d",
+           mode);
+  CF_CHECK(layers, CF_EINVAL, "null layer array");
+  for (int l = 0; l < mc.n_layers; ++l)
+    if (cf_status s = check_layer(c, layers + l, l)) return s;
+  CF_CHECK(embed && final_norm && tokens, CF_EINVAL, "null embed, final_norm or tokens");
+  CF_CHECK(aligned16(embed), CF_EINVAL, "embedding must be 16-byte aligned");
+  CF_CHECK(k_out && v_out && aligned16(k_out) && aligned16(v_out), CF_EINVAL, "k_out/v_out null or misaligned");
+  CF_CHECK(ols >= L * kvd && ols % 8 == 0, CF_ESHAPE, "out_layer_stride must be >= L*kvd and a multiple of 8");
+  CF_CHECK(U == 0 || out_hidden, CF_EINVAL, "out_hidden is NULL but U > 0");
+  const bool full = mode == CF_SEL_ALL;
+  if (!full) {
+    CF_CHECK(s_layer >= 0 && s_layer < mc.n_layers, CF_EINVAL, "sel_layer %d outside [0, %d)", s_layer, mc.n_layers);
+    CF_CHECK(k >= 0 && k <= N, CF_EINVAL, "k=%d outside [0, N=%d]", k, N);
+    if (N > 0) {
+      CF_CHECK(k_store && v_store && aligned16(k_store) && aligned16(v_store), CF_EINVAL,
+               "chunk store null or misaligned");
+      CF_CHECK(store_rows >= 0 && sls >= store_rows * kvd && sls % 8 == 0, CF_ESHAPE,
+               "store_layer_stride must hold store_rows*kvd elements and be a multiple of 8");
+    }
+    if (cf_status s = check_chunks(c, tab, m, store_rows, N, N)) return s;
+    if (mode == CF_SEL_DOC_SPANS && N > 0)
+      if (cf_status s = check_spans(bounds, ns, N)) return s;
+  } else {
+    k = N;
+  }
+  const PrefillWs pw = prefill_ws(c, N, U, k, mode);
+  CF_CHECK(ws && aligned16(ws) && ws_bytes >= pw.total, CF_EWORKSPACE, "workspace: need %zu bytes, got %zu", pw.total,
+           ws_bytes);
+  DeviceGuard guard(c->device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+
+  char* W = static_cast<char*>(ws);
+  float* hidden = reinterpret_cast<float*>(W + pw.hidden);
+  int* sel = reinterpret_cast<int*>(W + pw.sel);
+  float* dev = reinterpret_cast<float*>(W + pw.dev);
+  char* lws = W + pw.layer;
+  int* ident = reinterpret_cast<int*>(W + pw.ident);
+  const cf::Dt dt = dt_of(c);
+  const LayerWs lw_full = layer_ws(c, L, L);
+  auto K_l = [&](int l) { return static_cast<char*>(k_out) + (size_t)l * ols * esize(c); };
+  auto V_l = [&](int l) { return static_cast<char*>(v_out) + (size_t)l * ols * esize(c); };
+
+  const int first_sel = full ? mc.n_layers : s_layer;
+  if (!full && N > 0 && first_sel < mc.n_layers)
+    if (cf_status s = enqueue_reposition(c, k_store, v_store, sls, k_out, v_out, ols, tab, m, first_sel,
+                                         mc.n_layers, st))
+      return s;
+  CF_HIP(cf::launch_embed(dt, tokens, L, embed, mc.vocab, mc.d_model, hidden, st));
+  CF_HIP(cf::launch_iota(ident, L, 0, st));
+  for (int l = 0; l < first_sel; ++l)
+    if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), ident, L, L, lws, lw_full, st)) return s;
+
+  if (!full) {
+    const cf_layer_weights* w = layers + s_layer;
+    const int n_sel = k + U;
+    if (N > 0) {
+      // current keys of the context rows at the selection layer and their deviation
+      void* X = lws + lw_full.x;  // the full-row layout holds N rows of X and of K
+      float* KN = reinterpret_cast<float*>(lws + lw_full.qkv);
+      CF_HIP(cf::launch_rmsnorm_rows(dt, hidden, nullptr, N, L, mc.d_model, w->attn_norm, mc.rms_eps, X, mc.d_model,
+                                     st));
+      cf::GemmArgs g{};
+      g.dt = dt; g.A = X; g.lda = mc.d_model; g.B[0] = g.B[1] = g.B[2] = w->wk; g.nb0 = g.nb1 = (int)kvd;
+      g.M = N; g.N = (int)kvd; g.K = mc.d_model; g.splits = 1; g.epi = cf::EPI_F32; g.C = KN; g.ldc = kvd;
+      CF_HIP(cf::launch_gemm(g, st));
+      cf::QkvPost qp{};
+      qp.qkv = KN; qp.ld = kvd; qp.rows = nullptr; qp.n = N; qp.L = L;
+      qp.hq = mc.n_q_heads; qp.hkv = mc.n_kv_heads; qp.hd = mc.head_dim; qp.qk_norm = mc.qk_norm;
+      qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = mc.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
+      qp.dev = dev; qp.k_ref = K_l(s_layer);
+      CF_HIP(cf::launch_qkv_post(dt, qp, st));
+      if (cf_status s = enqueue_select(dev, N, k, mode, bounds, ns, sel, reinterpret_cast<double*>(W + pw.topk), st))
+        return s;
+      if (out_dev) CF_HIP(cf::launch_copy_f32(out_dev, dev, N, st));
+      if (out_sel) CF_HIP(cf::launch_copy_i32(out_sel, sel, k, st));
+    }
+    CF_HIP(cf::launch_iota(sel + k, U, N, st));
+    const LayerWs lw_sel = layer_ws(c, L, n_sel);
+    for (int l = s_layer; l < mc.n_layers; ++l)
+      if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st)) return s;
+  }
+  if (U > 0)
+    CF_HIP(cf::launch_rmsnorm_rows(cf::F32, hidden + (size_t)N * mc.d_model, nullptr, U, U, mc.d_model, final_norm,
+                                   mc.rms_eps, out_hidden, mc.d_model, st));
+  return CF_OK;
+}
+
+}  // extern "C"

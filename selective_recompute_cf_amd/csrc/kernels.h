@@ -1,0 +1,92 @@
+// Host-side launchers of the libcf kernels (internal; the public interface is include/cf.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cf {
+
+enum Dt { F32 = 0, BF16 = 1 };
+
+// ----------------------------------------------------------------- row kernels (rows.hip)
+constexpr int CHUNKS_PER_LAUNCH = 64;
+struct ChunkBatch {
+  int n;
+  int row[CHUNKS_PER_LAUNCH];
+  int dst[CHUNKS_PER_LAUNCH];
+  int len[CHUNKS_PER_LAUNCH];
+  int delta[CHUNKS_PER_LAUNCH];
+  int blk0[CHUNKS_PER_LAUNCH + 1];  // first block of each chunk (prefix sums of row blocks)
+};
+constexpr int REPOS_ROWS_PER_BLOCK = 4;
+
+hipError_t launch_reposition(Dt dt, const void* ks, const void* vs, int64_t sls, void* kb, void* vb,
+                             int64_t bls, const ChunkBatch& cb, int kvd, int hd, const float* cos_t,
+                             const float* sin_t, int layer_begin, int n_layers, hipStream_t st);
+hipError_t launch_embed(Dt dt, const int* tok, int L, const void* emb, int vocab, int d, float* h,
+                        hipStream_t st);
+// out[j] = RMSNorm(x[rows ? rows[j] : j]) * g, written as `out_dt` with row stride ldo.
+hipError_t launch_rmsnorm_rows(Dt out_dt, const float* x, const int* rows, int n, int L, int d,
+                               const float* g, float eps, void* out, int64_t ldo, hipStream_t st);
+// Post-process fp32 projection rows: qk-norm, RoPE at pos = rows[j], Q -> q_out (model dtype),
+// K/V scattered into the cache at row pos. With dev != nullptr, only K is present (ld = kvd),
+// positions are j, and dev[j] = sum (rope(k) - k_ref[j])^2; nothing is stored.
+struct QkvPost {
+  const float* qkv; int64_t ld;
+  const int* rows; int n; int L;
+  int hq, hkv, hd; int qk_norm; const float* qn; const float* kn; float eps;
+  const float* cos_t; const float* sin_t;
+  void* q_out; void* k_cache; void* v_cache;
+  float* dev; const void* k_ref;
+};
+hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st);
+hipError_t launch_iota(int* out, int n, int start, hipStream_t st);
+hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st);
+hipError_t launch_copy_f32(float* dst, const float* src, int n, hipStream_t st);
+// out[out_rows[m]][c] = resid[resid_rows[m]][c] + sum_s part[s][m][c]   (rows may be null)
+hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, const float* resid,
+                                const int* resid_rows, float* out, const int* out_rows, int L,
+                                hipStream_t st);
+// act[m][c] = silu(gu[m][c]) * gu[m][F + c]  (fp32 path)
+hipError_t launch_swiglu(Dt dt, const float* gu, int M, int F, void* act, hipStream_t st);
+hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void* b, int64_t ldb,
+                            float* dev, int n, int kvd, hipStream_t st);
+
+// ----------------------------------------------------------------- GEMM (gemm.hip)
+enum Epi { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PARTIAL = 3 };
+struct GemmArgs {
+  Dt dt;
+  const void* A; int64_t lda;          // [M][K]
+  const void* B[3]; int nb0, nb1;      // weights [n][K] (row stride K): cols [0,nb0) from B[0],
+                                       // [nb0,nb1) from B[1], [nb1,N) from B[2]
+  int M, N, K;
+  int splits;                          // split-K factor (>= 1); EPI_PARTIAL writes part[s]
+  int epi;
+  float* C; int64_t ldc;               // EPI_F32 / EPI_PARTIAL destination ([splits][M][ldc])
+  void* act; int64_t ld_act;           // EPI_SWIGLU: N = d_ffn, B[0] = gate, B[1] = up
+  const float* resid; const int* resid_rows; float* out; const int* out_rows; int L;  // EPI_RESID
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+int gemm_splits(Dt dt, int M, int N, int K, int epi, int n_cu);
+
+// ----------------------------------------------------------------- attention (attn.hip)
+struct AttnArgs {
+  Dt dt;
+  const void* q; int64_t ldq;          // [n][hq*hd]
+  const int* pos; int n;               // absolute positions, ascending
+  const void* k; const void* v; int L; // cache [L][hkv*hd]
+  int hq, hkv, hd;
+  void* out; int64_t ldo;              // [n][hq*hd] (model dtype)
+  int splits; int split_len;           // split-KV: keys [s*split_len, (s+1)*split_len)
+  float* o_part; float* ml_part;       // [splits][n][hq][hd], [splits][n][hq][2]
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len);
+
+// ----------------------------------------------------------------- selection (topk.hip)
+constexpr int MAX_SPANS = 256;
+struct SpanArgs { int n_spans; int b[MAX_SPANS + 1]; };
+hipError_t launch_topk_token(const float* dev, int n, int k, int* out, hipStream_t st);
+hipError_t launch_topk_spans(const float* dev, int n, int k, const SpanArgs& sp, int* out,
+                             double* ws, hipStream_t st);
+
+}  // namespace cf

@@ -1,0 +1,334 @@
+// Row-wise and element-wise kernels of libcf (HBM-bound): RoPE re-positioning and stitching,
+// embedding gather, RMSNorm gather, projection post-processing (qk-norm, RoPE, K/V scatter,
+// fused KV deviation), split-K reduction with residual, SwiGLU, standalone deviation.
+#include "common.h"
+#include "kernels.h"
+
+namespace cf {
+
+// ----------------------------------------------------------------------------- re-position
+// QCFuse Eq. 4 (remap + stitch) with the rotation composition of CacheBlend ("Why You Can't
+// Just Concatenate"): a key encoded at p is moved to p + delta by rotating every pair
+// (x_j, x_{j+hd/2}) by delta * omega_j; values are copied. One block moves up to
+// REPOS_ROWS_PER_BLOCK rows of one chunk of one layer; each thread moves 8 pairs of K
+// (two 16-byte loads for bf16) or 8 elements of V per step.
+template <typename T>
+__global__ __launch_bounds__(256) void reposition_kernel(const T* __restrict__ ks, const T* __restrict__ vs,
+                                                         int64_t sls, T* __restrict__ kb, T* __restrict__ vb,
+                                                         int64_t bls, ChunkBatch cb, int kvd, int hd,
+                                                         const float* __restrict__ cos_t,
+                                                         const float* __restrict__ sin_t, int layer_begin) {
+  const int blk = blockIdx.x;
+  int c = 0;
+  while (c + 1 < cb.n && cb.blk0[c + 1] <= blk) ++c;
+  const int r0 = (blk - cb.blk0[c]) * REPOS_ROWS_PER_BLOCK;
+  const int nrows = min(REPOS_ROWS_PER_BLOCK, cb.len[c] - r0);
+  const int64_t l = layer_begin + blockIdx.y;
+  const int64_t src_row = cb.row[c] + r0, dst_row = cb.dst[c] + r0;
+  const T* ksrc = ks + l * sls + src_row * kvd;
+  const T* vsrc = vs + l * sls + src_row * kvd;
+  T* kdst = kb + l * bls + dst_row * kvd;
+  T* vdst = vb + l * bls + dst_row * kvd;
+  const int delta = cb.delta[c];
+  const int half = hd / 2;
+  const float sgn = delta < 0 ? -1.f : 1.f;
+  const float* cs = cos_t + (int64_t)abs(delta) * half;
+  const float* sn = sin_t + (int64_t)abs(delta) * half;
+
+  const int upr = kvd / 16;  // units of 8 pairs per row
+  for (int u = threadIdx.x; u < nrows * upr; u += blockDim.x) {
+    const int row = u / upr, w = u % upr;
+    const int head = w / (half / 8), j0 = (w % (half / 8)) * 8;
+    const int64_t off = (int64_t)row * kvd + head * hd + j0;
+    float x1[8], x2[8], c8[8], s8[8];
+    load8(ksrc + off, x1);
+    load8(ksrc + off + half, x2);
+    load8(cs + j0, c8);
+    load8(sn + j0, s8);
+    float y1[8], y2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = sgn * s8[e];
+      y1[e] = x1[e] * c8[e] - x2[e] * s;
+      y2[e] = x1[e] * s + x2[e] * c8[e];
+    }
+    store8(kdst + off, y1);
+    store8(kdst + off + half, y2);
+  }
+  const int vpr = kvd / 8;
+  for (int u = threadIdx.x; u < nrows * vpr; u += blockDim.x) {
+    const int64_t off = (int64_t)(u / vpr) * kvd + (u % vpr) * 8;
+    copy8(vdst + off, vsrc + off);
+  }
+}
+
+hipError_t launch_reposition(Dt dt, const void* ks, const void* vs, int64_t sls, void* kb, void* vb,
+                             int64_t bls, const ChunkBatch& cb, int kvd, int hd, const float* cos_t,
+                             const float* sin_t, int layer_begin, int n_layers, hipStream_t st) {
+  const int nblk = cb.blk0[cb.n];
+  if (nblk == 0 || n_layers == 0) return hipSuccess;
+  dim3 grid(nblk, n_layers);
+  if (dt == BF16)
+    hipLaunchKernelGGL(reposition_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)ks, (const bf16*)vs,
+                       sls, (bf16*)kb, (bf16*)vb, bls, cb, kvd, hd, cos_t, sin_t, layer_begin);
+  else
+    hipLaunchKernelGGL(reposition_kernel<float>, grid, dim3(256), 0, st, (const float*)ks, (const float*)vs,
+                       sls, (float*)kb, (float*)vb, bls, cb, kvd, hd, cos_t, sin_t, layer_begin);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- embedding
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int* __restrict__ tok, const T* __restrict__ emb,
+                                                    int vocab, int d, float* __restrict__ h) {
+  const int r = blockIdx.x;
+  const int t = tok[r];
+  const bool ok = t >= 0 && t < vocab;
+  const T* src = emb + (int64_t)(ok ? t : 0) * d;
+  float* dst = h + (int64_t)r * d;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float v[8];
+    load8(src + c, v);
+    if (!ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = __builtin_nanf("");
+    }
+    store8(dst + c, v);
+  }
+}
+
+hipError_t launch_embed(Dt dt, const int* tok, int L, const void* emb, int vocab, int d, float* h,
+                        hipStream_t st) {
+  if (L == 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(L), dim3(256), 0, st, tok, (const bf16*)emb, vocab, d, h);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(L), dim3(256), 0, st, tok, (const float*)emb, vocab, d, h);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- RMSNorm rows
+template <typename To>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, const int* __restrict__ rows,
+                                                           int L, int d, const float* __restrict__ g, float eps,
+                                                           To* __restrict__ out, int64_t ldo) {
+  __shared__ float red[4];
+  const int j = blockIdx.x;
+  const int r = rows ? clampi(rows[j], 0, L - 1) : j;
+  const float* xr = x + (int64_t)r * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float v[8];
+    load8(xr + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  To* o = out + (int64_t)j * ldo;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float v[8], gg[8];
+    load8(xr + c, v);
+    load8(g + c, gg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * gg[e];
+    store8(o + c, v);
+  }
+}
+
+hipError_t launch_rmsnorm_rows(Dt out_dt, const float* x, const int* rows, int n, int L, int d,
+                               const float* g, float eps, void* out, int64_t ldo, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (out_dt == BF16)
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<bf16>, dim3(n), dim3(256), 0, st, x, rows, L, d, g, eps, (bf16*)out, ldo);
+  else
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<float>, dim3(n), dim3(256), 0, st, x, rows, L, d, g, eps, (float*)out, ldo);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- QKV post
+// One block per projected row. Wave w handles heads w, w+4, ...; lane j < hd/2 owns the RoPE
+// pair (j, j + hd/2) of its head. qk-norm (per-head RMS over hd) happens before RoPE, as in the
+// decoder definition. In deviation mode (p.dev set) the rows hold K only and the rotated keys
+// are compared with the stitched keys instead of being stored (Request Order Matters Eq. 1).
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
+  __shared__ float red[4];
+  const int j = blockIdx.x;
+  const int w = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  const int hd = p.hd, half = hd / 2;
+  const bool devmode = p.dev != nullptr;
+  const int pos = devmode ? j : clampi(p.rows[j], 0, p.L - 1);
+  const float* src = p.qkv + (int64_t)j * p.ld;
+  const float c = lane < half ? p.cos_t[(int64_t)pos * half + lane] : 0.f;
+  const float s = lane < half ? p.sin_t[(int64_t)pos * half + lane] : 0.f;
+  const int nq = devmode ? 0 : p.hq;
+  const int nkv = p.hkv;
+  const int nh = nq + nkv + (devmode ? 0 : nkv);
+  const int koff = nq * hd, voff = koff + nkv * hd;
+  const int qd = p.hq * hd, kvd = nkv * hd;
+  float dacc = 0.f;
+  for (int h = w; h < nh; h += blockDim.x / WAVE) {
+    if (h < nq + nkv) {
+      const bool isq = h < nq;
+      const int hh = isq ? h : h - nq;
+      const float* x = src + (isq ? hh * hd : koff + hh * hd);
+      float x1 = lane < half ? x[lane] : 0.f;
+      float x2 = lane < half ? x[lane + half] : 0.f;
+      if (p.qk_norm) {
+        const float ss = wave_sum(x1 * x1 + x2 * x2);
+        const float inv = 1.0f / sqrtf(ss / (float)hd + p.eps);
+        const float* gn = isq ? p.qn : p.kn;
+        if (lane < half) {
+          x1 = x1 * inv * gn[lane];
+          x2 = x2 * inv * gn[lane + half];
+        }
+      }
+      const float y1 = x1 * c - x2 * s;
+      const float y2 = x1 * s + x2 * c;
+      if (lane < half) {
+        if (isq) {
+          T* q = (T*)p.q_out + (int64_t)j * qd + hh * hd;
+          q[lane] = from_f<T>(y1);
+          q[lane + half] = from_f<T>(y2);
+        } else if (devmode) {
+          const T* r = (const T*)p.k_ref + (int64_t)j * kvd + hh * hd;
+          const float d1 = y1 - to_f(r[lane]), d2 = y2 - to_f(r[lane + half]);
+          dacc += d1 * d1 + d2 * d2;
+        } else {
+          T* kc = (T*)p.k_cache + (int64_t)pos * kvd + hh * hd;
+          kc[lane] = from_f<T>(y1);
+          kc[lane + half] = from_f<T>(y2);
+        }
+      }
+    } else {
+      const int hh = h - nq - nkv;
+      T* vc = (T*)p.v_cache + (int64_t)pos * kvd + hh * hd;
+      for (int e = lane; e < hd; e += WAVE) vc[e] = from_f<T>(src[voff + hh * hd + e]);
+    }
+  }
+  if (devmode) {
+    dacc = block_sum(dacc, red);
+    if (threadIdx.x == 0) p.dev[j] = dacc;
+  }
+}
+
+hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st) {
+  if (p.n == 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL(qkv_post_kernel<bf16>, dim3(p.n), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(qkv_post_kernel<float>, dim3(p.n), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- small helpers
+__global__ void iota_kernel(int* out, int n, int start) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = start + i;
+}
+hipError_t launch_iota(int* out, int n, int start, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(iota_kernel, dim3((n + 255) / 256), dim3(256), 0, st, out, n, start);
+  return hipGetLastError();
+}
+template <typename T>
+__global__ void copy_kernel(T* dst, const T* src, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_kernel<int>, dim3((n + 255) / 256), dim3(256), 0, st, dst, src, n);
+  return hipGetLastError();
+}
+hipError_t launch_copy_f32(float* dst, const float* src, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, st, dst, src, n);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- split-K reduce
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                            const float* __restrict__ resid, const int* __restrict__ rrows,
+                                                            float* __restrict__ out, const int* __restrict__ orows, int L) {
+  const int m = blockIdx.x;
+  const int64_t rr = rrows ? clampi(rrows[m], 0, L - 1) : m;
+  const int64_t orr = orows ? clampi(orows[m], 0, L - 1) : m;
+  for (int c = threadIdx.x * 4; c < N; c += blockDim.x * 4) {
+    float4 a = resid ? *reinterpret_cast<const float4*>(resid + rr * N + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < splits; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(part + ((int64_t)s * M + m) * N + c);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    *reinterpret_cast<float4*>(out + orr * N + c) = a;
+  }
+}
+hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, const float* resid,
+                                const int* resid_rows, float* out, const int* out_rows, int L,
+                                hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(M), dim3(256), 0, st, part, splits, M, N, resid, resid_rows,
+                     out, out_rows, L);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- SwiGLU (fp32 path)
+template <typename T>
+__global__ void swiglu_kernel(const float* __restrict__ gu, int M, int F, T* __restrict__ act) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * F) return;
+  const int64_t m = i / F, c = i % F;
+  const float g = gu[m * 2 * F + c], u = gu[m * 2 * F + F + c];
+  act[i] = from_f<T>(g / (1.0f + expf(-g)) * u);
+}
+hipError_t launch_swiglu(Dt dt, const float* gu, int M, int F, void* act, hipStream_t st) {
+  const int64_t n = (int64_t)M * F;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dt == BF16)
+    hipLaunchKernelGGL(swiglu_kernel<bf16>, grid, dim3(256), 0, st, gu, M, F, (bf16*)act);
+  else
+    hipLaunchKernelGGL(swiglu_kernel<float>, grid, dim3(256), 0, st, gu, M, F, (float*)act);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- deviation
+// Request Order Matters §2.2 Eq. 1 on two key arrays: one block per token, fp32 accumulation.
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void deviation_kernel(const TA* __restrict__ a, int64_t lda, const TB* __restrict__ b,
+                                                        int64_t ldb, float* __restrict__ dev, int kvd) {
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  const TA* ar = a + (int64_t)i * lda;
+  const TB* br = b + (int64_t)i * ldb;
+  float acc = 0.f;
+  for (int c = threadIdx.x * 8; c < kvd; c += blockDim.x * 8) {
+    float x[8], y[8];
+    load8(ar + c, x);
+    load8(br + c, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = x[e] - y[e];
+      acc += t * t;
+    }
+  }
+  acc = block_sum(acc, red);
+  if (threadIdx.x == 0) dev[i] = acc;
+}
+hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void* b, int64_t ldb,
+                            float* dev, int n, int kvd, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const dim3 g(n), blk(256);
+  if (dn == BF16 && dr == BF16)
+    hipLaunchKernelGGL((deviation_kernel<bf16, bf16>), g, blk, 0, st, (const bf16*)a, lda, (const bf16*)b, ldb, dev, kvd);
+  else if (dn == F32 && dr == BF16)
+    hipLaunchKernelGGL((deviation_kernel<float, bf16>), g, blk, 0, st, (const float*)a, lda, (const bf16*)b, ldb, dev, kvd);
+  else if (dn == BF16 && dr == F32)
+    hipLaunchKernelGGL((deviation_kernel<bf16, float>), g, blk, 0, st, (const bf16*)a, lda, (const float*)b, ldb, dev, kvd);
+  else
+    hipLaunchKernelGGL((deviation_kernel<float, float>), g, blk, 0, st, (const float*)a, lda, (const float*)b, ldb, dev, kvd);
+  return hipGetLastError();
+}
+
+}  // namespace cf

@@ -1,0 +1,97 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and compare with the oracle."""
+import sys
+
+import numpy as np
+
+import selective_recompute_cf_amd as cf
+from selective_recompute_cf_amd.device import DeviceModel, to_device
+
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-2)}  # (atol, rtol): |gpu - ref| <= atol + rtol |ref|
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def host(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def compare(name, gpu, ref, dtype=None, atol=None, rtol=None, frac=1.0):
+    """Elementwise |gpu - ref| <= atol + rtol |ref| (all elements, or at least `frac` of them)."""
+    if atol is None:
+        atol, rtol = TOL[dtype]
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    err = np.abs(gpu - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    nrel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
+    stats = dict(max_abs=float(err.max(initial=0.0)), norm_rel=nrel, bad=int(bad.sum()), n=int(err.size))
+    say(f"  {name}: max_abs={stats['max_abs']:.3e} norm_rel={nrel:.3e} out_of_tol={stats['bad']}/{stats['n']}")
+    assert np.isfinite(gpu).all(), f"{name}: non-finite GPU values"
+    assert bad.sum() <= (1.0 - frac) * err.size, f"{name}: {int(bad.sum())} of {err.size} outside tolerance"
+    return stats
+
+
+def overlap(a, b) -> float:
+    a, b = set(np.asarray(a).tolist()), set(np.asarray(b).tolist())
+    return 1.0 if not a and not b else len(a & b) / max(len(a), 1)
+
+
+def context(cfg, max_pos, dtype=None):
+    return cf.Context.from_model_cfg(cfg, max_pos=max_pos, dtype=dtype)
+
+
+def gpu_chunk_store(ctx, dm, chunks):
+    """Standalone prefill of every chunk at positions 0.. (mode "all"), written straight into one
+    store [Ly, rows, kvd]. Returns (k_store, v_store, chunk rows)."""
+    import torch
+    Ly, kvd = dm.n_layers, ctx.kv_dim
+    rows = sum(len(c) for c in chunks)
+    dt = torch_dtype(dm.dtype)
+    ks = torch.zeros(Ly, rows, kvd, dtype=dt, device="cuda")
+    vs = torch.zeros_like(ks)
+    r0, starts = 0, []
+    for c in chunks:
+        n = len(c)
+        tok = torch.from_numpy(np.asarray(c, np.int32)).cuda()
+        ws = torch.empty(ctx.blend_prefill_workspace_size(n, 0, n, "all"), dtype=torch.uint8, device="cuda")
+        ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok, n, 0, None, None, None, 0, 0, "all", None,
+                          ks[:, r0:], vs[:, r0:], None, ws, out_layer_stride=rows * kvd)
+        starts.append(r0)
+        r0 += n
+    return ks, vs, starts
+
+
+def gpu_blend(ctx, dm, tokens, N, k_store, v_store, table, sel_layer, k, mode, spans=None):
+    """One cf_blend_prefill call; returns dict of host arrays."""
+    import torch
+    L = len(tokens)
+    U = L - N
+    Ly, kvd, d = dm.n_layers, ctx.kv_dim, dm.cfg.d_model
+    dt = torch_dtype(dm.dtype)
+    k_out = torch.zeros(Ly, L, kvd, dtype=dt, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    out = torch.zeros(max(U, 1), d, dtype=torch.float32, device="cuda")
+    kk = N if mode == "all" else k
+    sel = torch.full((max(kk, 1),), -1, dtype=torch.int32, device="cuda")
+    dev = torch.zeros(max(N, 1), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ctx.blend_prefill_workspace_size(N, U, kk, mode), dtype=torch.uint8, device="cuda")
+    tok = torch.from_numpy(np.asarray(tokens, np.int32)).cuda()
+    ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok, N, U, k_store, v_store, table, sel_layer, k, mode,
+                      spans, k_out, v_out, out if U else None, ws, out_sel=None if mode == "all" else sel,
+                      out_dev=None if mode == "all" else dev)
+    torch.cuda.synchronize()
+    r = dict(k=host(k_out), v=host(v_out), out=host(out)[:U])
+    if mode != "all":
+        r["sel"] = sel.cpu().numpy()[:k]
+        r["dev"] = dev.cpu().numpy()[:N]
+    return r

@@ -1,0 +1,88 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports every entry point
+include/cf.h declares, and rejects bad arguments before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import selective_recompute_cf_amd as cf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "cf.h")).read()
+    return sorted(set(re.findall(r"\b(cf_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(cf.LIB_PATH):
+        from selective_recompute_cf_amd import build
+        build.build()
+    return cf.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(cf.EXPORTS) == names
+
+
+def test_version_string(L):
+    assert "gfx950" in cf.version()
+
+
+def test_topk_validation(L):
+    assert L.cf_topk_select(None, 10, 11, 0, None, 0, None, None, 0, None) == cf.CF_EINVAL
+    assert "k" in L.cf_last_error().decode()
+    assert L.cf_topk_select(None, 10, -1, 0, None, 0, None, None, 0, None) == cf.CF_EINVAL
+    assert L.cf_topk_select(None, 10, 2, 7, None, 0, None, None, 0, None) == cf.CF_EINVAL
+    # k = 0 enqueues nothing and succeeds
+    assert L.cf_topk_select(None, 10, 0, 0, None, 0, None, None, 0, None) == cf.CF_OK
+    # span bounds must start at 0, end at n and increase strictly
+    for b in ([0, 5, 9], [1, 5, 10], [0, 5, 5, 10], [0, 12]):
+        arr = (ctypes.c_int32 * len(b))(*b)
+        assert L.cf_topk_select(None, 10, 0, 1, arr, len(b) - 1, None, None, 0, None) == cf.CF_EINVAL, b
+    good = (ctypes.c_int32 * 3)(0, 4, 10)
+    assert L.cf_topk_select(None, 10, 3, 1, good, 2, None, None, 0, None) == cf.CF_EWORKSPACE
+    assert cf.topk_workspace_size(10, "doc") >= 88 and cf.topk_workspace_size(10, "token") == 0
+
+
+def test_deviation_validation(L):
+    assert L.cf_kv_deviation(None, 5, 8, None, 0, 8, None, 4, 8, None) == cf.CF_EDTYPE
+    assert L.cf_kv_deviation(None, 0, 8, None, 0, 8, None, 4, 12, None) == cf.CF_ESHAPE
+    assert L.cf_kv_deviation(None, 0, 8, None, 0, 8, None, 0, 8, None) == cf.CF_OK
+    assert L.cf_kv_deviation(None, 0, 8, None, 0, 8, None, 4, 8, None) == cf.CF_EINVAL
+
+
+def test_null_context_rejected(L):
+    assert L.cf_rope_reposition(None, None, None, 0, 0, None, None, 0, 0, None, 0, 0, 0, None) == cf.CF_EINVAL
+    assert L.cf_blend_layer(None, None, None, None, None, None, 0, 1, None, 0, None) == cf.CF_EINVAL
+    assert L.cf_blend_prefill(None, None, None, None, None, 1, 0, None, None, 0, 0, None, 0, 0, 0, 0, None, 0,
+                              None, None, 0, None, None, None, None, 0, None) == cf.CF_EINVAL
+    assert L.cf_blend_layer_workspace_size(None, 10, 5) == 0
+    assert L.cf_blend_prefill_workspace_size(None, 10, 5, 3, 0) == 0
+
+
+def test_context_rejects_bad_shapes(L):
+    h = ctypes.c_void_p()
+    bad = [cf.ModelCfg(2, 256, 4, 2, 96, 688, 1000, 0, 1e4, 1e-5, 0),    # head_dim 96
+           cf.ModelCfg(2, 256, 4, 3, 64, 688, 1000, 0, 1e4, 1e-5, 0),    # 4 % 3
+           cf.ModelCfg(2, 256, 4, 2, 64, 688, 1000, 0, 1e4, 1e-5, 7),    # dtype
+           cf.ModelCfg(2, 260, 4, 2, 64, 688, 1000, 0, 1e4, 1e-5, 0)]    # d % 8
+    want = [cf.CF_EUNSUPPORTED, cf.CF_ESHAPE, cf.CF_EDTYPE, cf.CF_EUNSUPPORTED]
+    for c, w in zip(bad, want):
+        assert L.cf_ctx_create(ctypes.byref(c), 1024, 0, ctypes.byref(h)) == w
+
+
+def test_budget_host_logic_agrees_with_oracle():
+    for n in [0, 1, 7, 10, 512, 3072, 7720, 10240, 16384]:
+        for num, den in [(0, 100), (1, 100), (5, 100), (15, 100), (29, 100), (30, 100), (1, 3), (100, 100)]:
+            assert cf.budget(n, num, den) == oracle.budget(n, num, den)
+    with pytest.raises(ValueError):
+        cf.budget(10, 101, 100)

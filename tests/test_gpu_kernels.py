@@ -1,0 +1,138 @@
+"""GPU parity of the HBM-bound steps through the C ABI: RoPE re-position + stitch, KV deviation,
+token top-k and document-aligned selection (bit-exact on identical deviation arrays)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import selective_recompute_cf_amd as cf
+from tests import _golden
+from tests._gpu import compare, context, host, say, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+@pytest.mark.parametrize("dtype,hd", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_reposition_matches_oracle(dtype, hd):
+    """QCFuse Eq. 4 with rotation composition: chunks of ragged length, negative and positive
+    offsets, a layer range that leaves layer 0 untouched."""
+    torch = _torch()
+    cfg = synth.TINY.replace(head_dim=hd, n_kv_heads=2, dtype=dtype)
+    kvd = cfg.kv_dim
+    Ly, rows, L = 3, 300, 400
+    say(f"reposition dtype={dtype} hd={hd}")
+    ctx = context(cfg, max_pos=2048)
+    ks = synth.normal_array([7, 1], (Ly, rows, cfg.n_kv_heads, hd))
+    vs = synth.normal_array([7, 2], (Ly, rows, cfg.n_kv_heads, hd))
+    if dtype == "bf16":
+        ks, vs = synth.bf16_round(ks), synth.bf16_round(vs)
+    table = [(0, 0, 0, 37), (37, 0, 37, 100), (137, 512, 137, 61), (198, 1000, 198 + 50, 102), (10, 3, 380, 20)]
+    dt = torch_dtype(dtype)
+    k_store = torch.from_numpy(ks.reshape(Ly, rows, kvd)).to(dt).cuda()
+    v_store = torch.from_numpy(vs.reshape(Ly, rows, kvd)).to(dt).cuda()
+    k_blend = torch.full((Ly, L, kvd), 7.0, dtype=dt, device="cuda")
+    v_blend = torch.full((Ly, L, kvd), 7.0, dtype=dt, device="cuda")
+    ctx.rope_reposition(k_store, v_store, k_blend, v_blend, table, 1, 3)
+    torch.cuda.synchronize()
+    kref, vref = oracle.stitch(ks, vs, table, L, range(1, 3), cfg.rope_theta,
+                               np.float64, n_total=L)
+    kb, vb = host(k_blend).reshape(Ly, L, cfg.n_kv_heads, hd), host(v_blend).reshape(Ly, L, cfg.n_kv_heads, hd)
+    covered = np.zeros(L, bool)
+    for _, _, dst, ln in table:
+        covered[dst:dst + ln] = True
+    tol = (1e-5, 1e-5) if dtype == "f32" else (1e-6, 2.0 ** -8)
+    compare("K", kb[1:, covered], kref[1:, covered], atol=tol[0], rtol=tol[1])
+    np.testing.assert_array_equal(vb[1:, covered], vref[1:, covered])
+    assert np.all(kb[0] == 7.0) and np.all(kb[1:, ~covered] == 7.0)
+
+
+def test_reposition_rejects_bad_chunks():
+    torch = _torch()
+    cfg = synth.TINY
+    ctx = context(cfg, max_pos=1024)
+    a = torch.zeros(2, 64, cfg.kv_dim, device="cuda")
+    with pytest.raises(cf.CfError):
+        ctx.rope_reposition(a, a, a, a, [(0, 0, 40, 30)], 0, 2)   # dst past the blended rows
+    with pytest.raises(cf.CfError):
+        ctx.rope_reposition(a, a, a, a, [(0, 0, 0, 10), (10, 0, 5, 10)], 0, 2)  # overlap
+    with pytest.raises(cf.CfError):
+        ctx.rope_reposition(a, a, a, a, [(0, 2000, 0, 10)], 0, 2)  # offset beyond max_pos
+
+
+@pytest.mark.parametrize("dn,dr", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+def test_deviation_matches_oracle(dn, dr):
+    torch = _torch()
+    n, kvd = 777, 1024
+    a = synth.normal_array([8, 1], (n, kvd))
+    b = a + 0.3 * synth.normal_array([8, 2], (n, kvd))
+    if dn == "bf16":
+        a = synth.bf16_round(a)
+    if dr == "bf16":
+        b = synth.bf16_round(b)
+    ta = torch.from_numpy(a).to(torch_dtype(dn)).cuda()
+    tb = torch.from_numpy(b).to(torch_dtype(dr)).cuda()
+    dev = torch.zeros(n, device="cuda")
+    cf.kv_deviation(ta, tb, dev)
+    torch.cuda.synchronize()
+    compare("dev", dev.cpu().numpy(), oracle.kv_deviation(a, b), atol=0.0, rtol=1e-5)
+
+
+def _gpu_topk(d, k, mode="token", bounds=None):
+    torch = _torch()
+    dev = torch.from_numpy(np.asarray(d, np.float32)).cuda()
+    out = torch.full((max(k, 1),), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(cf.topk_workspace_size(len(d), mode), 1), dtype=torch.uint8, device="cuda")
+    cf.topk_select(dev, k, out, mode, bounds, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()[:k].tolist()
+
+
+@pytest.mark.parametrize("case", _golden.topk_cases())
+def test_topk_golden(case):
+    d, k, want = case
+    assert _gpu_topk(d, k) == want
+
+
+@pytest.mark.parametrize("n", [1, 7, 100, 1000, 1025, 3072, 10240, 16384, 100003])
+def test_topk_bit_exact_vs_oracle(n):
+    rng = np.random.default_rng(n)
+    say(f"topk n={n}")
+    for trial in range(3):
+        if trial == 0:
+            d = rng.random(n).astype(np.float32)
+        elif trial == 1:  # heavy ties, zeros of both signs, inf, nan, denormals
+            d = rng.choice(np.array([0.0, -0.0, 1e-45, 3e-45, 0.5, 2.0, np.inf, np.nan], np.float32), n)
+        else:  # sums of squares: skewed, as deviations are
+            d = (rng.standard_normal(n).astype(np.float32) ** 2) * np.float32(3.0)
+        for k in sorted({0, 1, n // 7, n // 2, n - 1, n}):
+            if 0 <= k <= n:
+                assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (n, trial, k)
+
+
+@pytest.mark.parametrize("case", _golden.doc_span_cases())
+def test_doc_spans_golden(case):
+    d, b, k, want = case
+    assert _gpu_topk(d, k, "doc", b) == want
+
+
+@pytest.mark.parametrize("n_spans,span_len", [(1, 50), (5, 7), (20, 512), (84, 92), (256, 40)])
+def test_doc_spans_bit_exact_vs_oracle(n_spans, span_len):
+    rng = np.random.default_rng(n_spans * 1000 + span_len)
+    lens = np.maximum(1, rng.integers(span_len // 2, span_len * 3 // 2 + 1, n_spans))
+    bounds = [0] + np.cumsum(lens).tolist()
+    n = bounds[-1]
+    say(f"spans n_spans={n_spans} n={n}")
+    for trial in range(3):
+        if trial == 0:
+            d = rng.random(n).astype(np.float32)
+        elif trial == 1:
+            d = rng.integers(0, 3, n).astype(np.float32)
+        else:
+            d = (rng.standard_normal(n).astype(np.float32) ** 2)
+        for k in sorted({0, 1, n // 20, n // 3, n - 1, n}):
+            assert _gpu_topk(d, k, "doc", bounds) == oracle.select_doc_spans(d, k, bounds).tolist(), (trial, k)
