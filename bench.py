@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of blended prefill (CacheBlend-style selective KV recompute) on one MI355X.
+
+One step = one cf_blend_prefill call over one request of the Llama-3-8B-shaped random-init bf16
+model (32 layers, d 4096, 32/8 heads, FFN 14336): 6 chunks x 512 tokens + a 64-token query,
+chunk caches from standalone prefill at position 0 (prepared before timing, as offline cache
+preparation is outside TTFT in QCFuse §4.1.4), RoPE re-position + stitch, layer 0 recomputed on
+every row, deviation and token top-15% on layer 1, selective recompute of layers 1..31.
+Weights, chunk store, tokens, outputs and workspace are resident in HBM before timing.
+
+Prints ONE JSON line: context tokens/s (N x steps / wall time), the roofline of the dominant
+kernel (the projection GEMM, timed live with HIP events on its stream), the other kernels'
+fractions, the speedup over the library's own full prefill at each recompute ratio, and the CPU
+oracle's throughput on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--store-cache", default=None,
+                    help="load the chunk store from this file if it exists, else build it and save it there")
+    ap.add_argument("--prepare-only", action="store_true", help="build (and save) the chunk store, then exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path has no multi-GPU mode",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import selective_recompute_cf_amd as cf
+    from selective_recompute_cf_amd import roofline as rl
+    from selective_recompute_cf_amd.device import DeviceModel
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    cfg = w.model
+    N, U, L = w.n_ctx, w.n_query, w.n_total
+    k = cf.budget(N, w.rho_num, w.rho_den)
+    kvd, Ly = cfg.kv_dim, cfg.n_layers
+    log(f"[bench] workload {w.name}: N={N} U={U} k={k} layers={Ly}; generating and uploading weights")
+    t0 = time.time()
+    dm = DeviceModel(synth.Model(cfg, cache_layers=False))
+    log(f"[bench] weights on GPU ({dm.weight_bytes() / 1e9:.1f} GB) in {time.time() - t0:.1f}s")
+    ctx = cf.Context.from_model_cfg(cfg, max_pos=L + 1)
+    chunks, _, toks = synth.request_tokens(w)
+    tok_dev = torch.from_numpy(toks).cuda()
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    table = [(i * w.chunk_len, 0, i * w.chunk_len, w.chunk_len) for i in range(w.n_chunks)]
+    spans = [i * w.chunk_len for i in range(w.n_chunks + 1)]
+
+    # ---------------------------------------------------------------- chunk store (untimed)
+    if args.store_cache and os.path.exists(args.store_cache):
+        st = torch.load(args.store_cache, weights_only=True)
+        ks, vs = st["k"].cuda(), st["v"].cuda()
+        log(f"[bench] chunk store loaded from {args.store_cache}")
+    else:
+        ks = torch.zeros(Ly, N, kvd, dtype=dt, device="cuda")
+        vs = torch.zeros_like(ks)
+        for i, c in enumerate(chunks):
+            r0 = i * w.chunk_len
+            n = len(c)
+            wsc = torch.empty(ctx.blend_prefill_workspace_size(n, 0, n, "all"), dtype=torch.uint8, device="cuda")
+            ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, torch.from_numpy(c).cuda(), n, 0, None, None,
+                              None, 0, 0, "all", None, ks[:, r0:], vs[:, r0:], None, wsc, out_layer_stride=N * kvd)
+        torch.cuda.synchronize()
+        if args.store_cache:
+            torch.save({"k": ks.cpu(), "v": vs.cpu()}, args.store_cache)
+            log(f"[bench] chunk store saved to {args.store_cache}")
+    if args.prepare_only:
+        return
+
+    sweep = [0, 5, 10, 15, 30, 50, 100]
+    k_of = {r: cf.budget(N, r, 100) for r in sweep}
+    ws_bytes = max([ctx.blend_prefill_workspace_size(N, U, kk, w.mode) for kk in list(k_of.values()) + [k]] +
+                   [ctx.blend_prefill_workspace_size(N, U, N, "all")])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    k_out = torch.zeros(Ly, L, kvd, dtype=dt, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    out = torch.zeros(max(U, 1), cfg.d_model, dtype=torch.float32, device="cuda")
+    sel = torch.zeros(N, dtype=torch.int32, device="cuda")
+
+    def blend(kk=k):
+        ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, ks, vs, table, w.sel_layer, kk, w.mode,
+                          spans, k_out, v_out, out if U else None, ws, out_sel=sel)
+
+    def full():
+        ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, None, None, None, 0, 0, "all", None,
+                          k_out, v_out, out if U else None, ws)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t_start = time.perf_counter()
+        ev[0].record()
+        for i in range(steps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return wall, per
+
+    # ---------------------------------------------------------------- headline timing
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps")
+    wall, per = timed(blend, args.steps, args.warmup)
+    value = N * args.steps / wall
+    ms_step = wall / args.steps * 1e3
+    sel_host = sel[:k].cpu().numpy()
+    log(f"[bench] {ms_step:.3f} ms/step (median event {statistics.median(per):.3f} ms) -> {value:.0f} ctx tokens/s")
+
+    # ---------------------------------------------------------------- per-kernel timing (HIP events)
+    P = args.profile_steps
+    cf.profile_enable(True)
+    for _ in range(P):
+        blend()
+    torch.cuda.synchronize()
+    rep = cf.profile_report()
+    cf.profile_enable(False)
+    shape = rl.shape_of(cfg)
+    work = rl.blend_step_work(shape, N, U, k, w.sel_layer, sel_host)
+    kernels = {}
+    for name, (launches, ms) in sorted(rep.items()):
+        ent = {"launches_per_step": launches / P, "us_per_launch": ms / launches * 1e3 if launches else None,
+               "ms_per_step": ms / P}
+        if name in work and ms > 0:
+            if name.startswith("gemm/") or name == "attention":
+                ach = work[name] / (ms / P / 1e3) / 1e12
+                ent.update(achieved=ach, unit="TFLOP/s", peak=rl.BF16_PEAK_TFLOPS, frac=ach / rl.BF16_PEAK_TFLOPS,
+                           algorithmic_flops_per_step=work[name])
+            else:
+                ach = work[name] / (ms / P / 1e3) / 1e9
+                ent.update(achieved=ach, unit="GB/s", peak=rl.HBM_PEAK_GBS, frac=ach / rl.HBM_PEAK_GBS,
+                           algorithmic_bytes_per_step=work[name])
+        kernels[name] = ent
+    g_launch = sum(v[0] for n, v in rep.items() if n.startswith("gemm/"))
+    g_ms = sum(v[1] for n, v in rep.items() if n.startswith("gemm/"))
+    g_flops = rl.gemm_flops(work) * P
+    g_ach = g_flops / (g_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(g_ach, 2), "peak": rl.BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g_ach / rl.BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "gemm_bf16_kernel",
+                "avg_launch_us": round(g_ms / g_launch * 1e3, 2),
+                "flops_per_launch": g_flops / g_launch, "launches_per_step": g_launch / P}
+    log(f"[bench] gemm: {g_ach:.1f} TFLOP/s ({roofline['frac'] * 100:.1f}% of bf16 peak), "
+        f"{roofline['avg_launch_us']} us/launch")
+
+    # ---------------------------------------------------------------- speedup over full prefill per ratio
+    sweep_res = None
+    if not args.no_sweep:
+        _, pf = timed(full, 5, 2)
+        t_full = statistics.median(pf)
+        sweep_res = {"full_prefill_ms": round(t_full, 3), "ratios": {}}
+        for r in sweep:
+            _, pb = timed(lambda: blend(k_of[r]), 5, 2)
+            tb = statistics.median(pb)
+            sweep_res["ratios"][f"{r}%"] = {"k": k_of[r], "blend_ms": round(tb, 3), "speedup": round(t_full / tb, 3)}
+        log(f"[bench] full prefill {t_full:.2f} ms; speedups " +
+            ", ".join(f"{r}: {v['speedup']}x" for r, v in sweep_res["ratios"].items()))
+
+    # ---------------------------------------------------------------- CPU oracle baseline (bounded sample)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, k)
+
+    line = {
+        "metric": "blended-prefill context tokens/s per GPU at r=15%",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "median_step_ms_events": round(statistics.median(per), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded uniform-random tokens, N(0,0.02) random-init weights)",
+        "config": {"workload": w.name, "model_shape": cfg.name, "layers": Ly, "n_ctx": N, "n_query": U,
+                   "chunks": f"{w.n_chunks}x{w.chunk_len}", "recompute_ratio": f"{w.rho_num}/{w.rho_den}",
+                   "k": k, "selection": w.mode, "selection_layer": w.sel_layer,
+                   "all_tokens_per_s": round((N + U) * args.steps / wall, 1)},
+        "roofline": roofline,
+        "kernels": kernels,
+        "speedup_vs_full_prefill": sweep_res,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, k):
+    """The oracle (numpy, as written) on the host cores: blended prefill of the same request at full
+    width and length with 2 and with 4 layers; the per-layer cost of a selected-row layer is the
+    difference, extrapolated to the full depth. Chunk caches for the sample are prepared untimed."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    import synth
+
+    cores = len(os.sched_getaffinity(0))
+    cfg = w.model
+    N = w.n_ctx
+    log(f"[bench] CPU oracle sample on {cores} host threads")
+    ctx_mgr = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        model = synth.Model(cfg)
+        chunks, _, toks = synth.request_tokens(w)
+        ks, vs, tab, row = [], [], [], 0
+        for c in chunks:
+            a, b = oracle.chunk_prefill(model, c, np.float32, 4)
+            ks.append(a)
+            vs.append(b)
+            tab.append((row, 0, row, len(c)))
+            row += len(c)
+        ks, vs = np.concatenate(ks, 1), np.concatenate(vs, 1)
+        spans = [i * w.chunk_len for i in range(w.n_chunks + 1)]
+        times = {}
+        for ly in (2, 4):
+            t0 = time.perf_counter()
+            oracle.blend_prefill(model, toks, N, ks[:ly], vs[:ly], tab, w.sel_layer, k, w.mode, spans, np.float32, ly)
+            times[ly] = time.perf_counter() - t0
+        per_layer = max(0.0, (times[4] - times[2]) / 2)
+        t_full = times[2] + (cfg.n_layers - 2) * per_layer
+    finally:
+        if ctx_mgr is not None:
+            ctx_mgr.__exit__(None, None, None)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    log(f"[bench] CPU oracle: 2 layers {times[2]:.2f}s, 4 layers {times[4]:.2f}s -> {t_full:.1f}s extrapolated")
+    return {"value": round(N / t_full, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{w.name}: oracle blend_prefill at full width and length timed with 2 and 4 layers "
+                       f"({times[2]:.2f}s, {times[4]:.2f}s); selected-row layer cost extrapolated to "
+                       f"{cfg.n_layers} layers = {t_full:.1f}s per request (extrapolated)"),
+            "cpu_model": cpu_model}
+
+
+if __name__ == "__main__":
+    main()

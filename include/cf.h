@@ -111,6 +111,14 @@ const char* cf_last_error(void);
 /* Library version and build string. */
 const char* cf_version(void);
 
+/* Kernel timing for diagnostics and benchmarks. While enabled (on != 0), every kernel libcf
+ * enqueues is bracketed by two HIP events recorded on the stream it runs on.
+ * cf_profile_report() waits for those events and returns a JSON object
+ * {"name": [launches, total_ms], ...} for the launches since the previous report; the text stays
+ * valid until the next call. Process-wide, not thread-safe; costs a few microseconds per launch. */
+cf_status cf_profile_enable(int32_t on);
+const char* cf_profile_report(void);
+
 /* --------------------------------------------------------------------- cf_rope_reposition
  * QCFuse Eq. 4 (position remap Pi_i and stitching) with CacheBlend's rotation composition.
  * For each chunk i of the host table chunk_tab[m][4] = {store_row, src_pos, dst_pos, len}

@@ -18,13 +18,13 @@ default (fp64 where a step says so, and fp64 throughout when asked), following:
   Agents, §2.2 Eq. 1 (deviation), Eq. 2 (budget), §2.3 Eq. 3 (span score and the
   document-aligned policy), §4.1 (rolling window).
 """
-from .model import (rms_norm, rope, rope_angles, causal_attention, layer_rows, full_prefill,
+from .model import (rms_norm, rope, rope_angles, causal_attention, layer_rows, full_prefill, bf16_round,
                     chunk_prefill)
 from .blend import (budget, reposition, stitch, kv_deviation, select_topk, select_doc_spans,
                     blend_prefill, direct_reuse, RollingWindow, BlendResult)
 
 __all__ = [
-    "rms_norm", "rope", "rope_angles", "causal_attention", "layer_rows", "full_prefill",
+    "bf16_round", "rms_norm", "rope", "rope_angles", "causal_attention", "layer_rows", "full_prefill",
     "chunk_prefill", "budget", "reposition", "stitch", "kv_deviation", "select_topk",
     "select_doc_spans", "blend_prefill", "direct_reuse", "RollingWindow", "BlendResult",
 ]

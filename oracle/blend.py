@@ -31,7 +31,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .model import rms_norm, rope, layer_rows, k_rows, full_prefill
+from .model import rms_norm, rope, layer_rows, k_rows, full_prefill, rounding, _r
 
 
 # ------------------------------------------------------------------ budget
@@ -57,13 +57,14 @@ def reposition(k_rows_at_src, delta: int, theta: float, ft=np.float32):
 
 
 def stitch(k_store, v_store, chunk_table, n_ctx, layers: Sequence[int], theta, ft=np.float32,
-           k_out=None, v_out=None, n_total: Optional[int] = None):
+           k_out=None, v_out=None, n_total: Optional[int] = None, rnd=None):
     """QCFuse Eq. 4: KV^PIC(C) = [Pi_1(KV_1); ...; Pi_m(KV_m)].
 
     k_store/v_store: [Ly, rows, Hkv, hd]; chunk_table: rows of (store_row, src_pos, dst_pos,
     length): the chunk's cache rows start at ``store_row`` and were encoded at positions
     src_pos.. ; they land at request rows dst_pos.. . Keys are rotated by dst - src, values
-    are copied. Returns (K, V) of shape [Ly, n_total, Hkv, hd] (rows >= n_ctx left zero)."""
+    are copied. Returns (K, V) of shape [Ly, n_total, Hkv, hd] (rows >= n_ctx left zero).
+    ``rnd`` rounds the rotated keys as they are stored (bf16 caches)."""
     ly, _, hkv, hd = k_store.shape
     n_total = n_ctx if n_total is None else n_total
     if k_out is None:
@@ -71,7 +72,7 @@ def stitch(k_store, v_store, chunk_table, n_ctx, layers: Sequence[int], theta, f
         v_out = np.zeros_like(k_out)
     for l in layers:
         for (row, src, dst, ln) in chunk_table:
-            k_out[l, dst:dst + ln] = reposition(np.asarray(k_store[l, row:row + ln]), dst - src, theta, ft)
+            k_out[l, dst:dst + ln] = _r(rnd, reposition(np.asarray(k_store[l, row:row + ln]), dst - src, theta, ft), ft)
             v_out[l, dst:dst + ln] = np.asarray(v_store[l, row:row + ln], dtype=ft)
     return k_out, v_out
 
@@ -175,7 +176,8 @@ class BlendResult:
 
 
 def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer: int, k: int,
-                  mode: str = "token", span_bounds=None, ft=np.float32, n_layers=None) -> BlendResult:
+                  mode: str = "token", span_bounds=None, ft=np.float32, n_layers=None,
+                  bf16_ops=None) -> BlendResult:
     """Blended prefill of one request: context C (n_ctx rows) followed by the query U.
 
     1. Stitch: layers s..Ly-1 of the request cache are the remapped chunk caches (QCFuse Eq. 4).
@@ -200,22 +202,23 @@ def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer
     vc = np.zeros_like(kc)
     h = np.asarray(model.embed[tokens], dtype=ft)
     pos_all = np.arange(L)
+    rnd = rounding(cfg, bf16_ops)
     if mode == "all":
         for l in range(ly):
-            h = layer_rows(cfg, model.layer(l), h, pos_all, kc[l], vc[l], ft)
+            h = layer_rows(cfg, model.layer(l), h, pos_all, kc[l], vc[l], ft, bf16_ops)
         out = rms_norm(h[N:], model.final_norm, cfg.rms_eps, ft)
         return BlendResult(kc, vc, out, np.arange(N, dtype=np.int32), np.zeros(0, np.float32), h)
 
     s = int(sel_layer)
     if not 0 <= s < ly:
         raise ValueError("selection layer out of range")
-    stitch(k_store, v_store, chunk_table, N, range(s, ly), cfg.rope_theta, ft, kc, vc)
+    stitch(k_store, v_store, chunk_table, N, range(s, ly), cfg.rope_theta, ft, kc, vc, rnd=rnd)
     for l in range(s):
-        h = layer_rows(cfg, model.layer(l), h, pos_all, kc[l], vc[l], ft)
+        h = layer_rows(cfg, model.layer(l), h, pos_all, kc[l], vc[l], ft, bf16_ops)
 
     w_s = model.layer(s)
     if N > 0:
-        k_cur = k_rows(cfg, w_s, h[:N], np.arange(N), ft)
+        k_cur = k_rows(cfg, w_s, h[:N], np.arange(N), ft, bf16_ops)
         dev = kv_deviation(k_cur, kc[s, :N])
     else:
         dev = np.zeros(0, np.float32)
@@ -229,12 +232,13 @@ def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer
     for l in range(s, ly):
         w = w_s if l == s else model.layer(l)
         if len(sel):
-            h[sel] = layer_rows(cfg, w, h[sel], sel, kc[l], vc[l], ft)
+            h[sel] = layer_rows(cfg, w, h[sel], sel, kc[l], vc[l], ft, bf16_ops)
     out = rms_norm(h[N:], model.final_norm, cfg.rms_eps, ft)
     return BlendResult(kc, vc, out, P, dev, h)
 
 
-def direct_reuse(model, tokens, n_ctx, k_store, v_store, chunk_table, ft=np.float32, n_layers=None):
+def direct_reuse(model, tokens, n_ctx, k_store, v_store, chunk_table, ft=np.float32, n_layers=None,
+                 bf16_ops=None):
     """The rho = 0 endpoint written from its own definition (QCFuse §2.1.2): the context cache is
     the stitched chunk caches at every layer, untouched; only the query rows are computed,
     attending over that cache. Returns (K, V, normed query hidden)."""
@@ -242,11 +246,12 @@ def direct_reuse(model, tokens, n_ctx, k_store, v_store, chunk_table, ft=np.floa
     ly = cfg.n_layers if n_layers is None else n_layers
     tokens = np.asarray(tokens)
     L, N = len(tokens), int(n_ctx)
-    kc, vc = stitch(k_store, v_store, chunk_table, N, range(ly), cfg.rope_theta, ft, n_total=L)
+    kc, vc = stitch(k_store, v_store, chunk_table, N, range(ly), cfg.rope_theta, ft, n_total=L,
+                    rnd=rounding(cfg, bf16_ops))
     hq = np.asarray(model.embed[tokens[N:]], dtype=ft)
     pos = np.arange(N, L)
     for l in range(ly):
-        hq = layer_rows(cfg, model.layer(l), hq, pos, kc[l], vc[l], ft)
+        hq = layer_rows(cfg, model.layer(l), hq, pos, kc[l], vc[l], ft, bf16_ops)
     return kc, vc, rms_norm(hq, model.final_norm, cfg.rms_eps, ft)
 
 

@@ -13,10 +13,38 @@ primitive used, and no step is fused or reordered.
 Conventions: matrices are [out, in] (y = x @ W.T); RoPE rotates the pair (x_j, x_{j+hd/2})
 by the angle pos * theta^(-2j/hd); attention lets a query at position p see cache rows t <= p;
 query head h reads kv head h // (Hq / Hkv).
+
+Arithmetic: everything runs in ``ft`` (fp32 by default) on the model's stored weights and
+embeddings (bf16-valued for bf16 models). With ``bf16_ops=True`` the oracle instead follows the
+arithmetic of a BF16 serving stack (QCFuse §4.1.1 serves BF16): every operand of a matrix
+product (the normed rows, Q, the softmax weights, the attention output, the SwiGLU activation;
+weights and K/V are bf16 already) and every K/V cache entry is rounded to bf16
+(round-to-nearest-even) while sums stay fp32. That mode measures how far bf16 arithmetic itself
+lands from the fp32 result, which calibrates the tolerance of bf16 comparisons.
 """
 from __future__ import annotations
 
 import numpy as np
+
+
+def bf16_round(x):
+    """Nearest bfloat16 value of each fp32 element (ties to even), returned as fp32: add
+    0x7FFF plus the lowest kept bit to the fp32 bit pattern and clear the low 16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    keep_lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + keep_lsb) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def rounding(cfg, bf16_ops=None):
+    """The rounding applied to matrix-product operands and K/V cache entries: bf16 when
+    ``bf16_ops`` is true (and the model is bf16), none otherwise (see above)."""
+    use = bool(bf16_ops) and getattr(cfg, "dtype", "f32") == "bf16"
+    return bf16_round if use else None
+
+
+def _r(rnd, x, ft):
+    return x if rnd is None else np.asarray(rnd(x), dtype=ft)
 
 
 def rms_norm(x, gain, eps, ft=np.float32):
@@ -53,10 +81,11 @@ def rope(x, pos, theta, ft=np.float32):
     return out.astype(ft)
 
 
-def causal_attention(q, q_pos, k_cache, v_cache, ft=np.float32):
+def causal_attention(q, q_pos, k_cache, v_cache, ft=np.float32, rnd=None):
     """Softmax attention of queries q [n, Hq, hd] sitting at absolute positions q_pos [n] over
     the cache rows k_cache/v_cache [L, Hkv, hd]; row t is visible to a query at p iff t <= p.
-    Scale 1/sqrt(hd); query head h uses kv head h // (Hq / Hkv)."""
+    Scale 1/sqrt(hd); query head h uses kv head h // (Hq / Hkv). ``rnd`` (if given) rounds the
+    unnormalised softmax weights, the operand of the product with V."""
     q = np.asarray(q, dtype=ft)
     kc = np.asarray(k_cache, dtype=ft)
     vc = np.asarray(v_cache, dtype=ft)
@@ -73,8 +102,7 @@ def causal_attention(q, q_pos, k_cache, v_cache, ft=np.float32):
         s = np.where(visible, s, ft(-np.inf))
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
-        p = p / p.sum(axis=1, keepdims=True)
-        out[:, h, :] = p @ vc[:, g, :]
+        out[:, h, :] = (_r(rnd, p, ft) @ vc[:, g, :]) / p.sum(axis=1, keepdims=True)
     return out
 
 
@@ -82,7 +110,7 @@ def silu(z):
     return z / (1 + np.exp(-z))
 
 
-def layer_rows(cfg, w, h_rows, pos, k_cache, v_cache, ft=np.float32):
+def layer_rows(cfg, w, h_rows, pos, k_cache, v_cache, ft=np.float32, bf16_ops=None):
     """One decoder layer applied to the rows ``h_rows`` [n, d] sitting at positions ``pos``.
 
     The rows' fresh K and V are written into ``k_cache``/``v_cache`` [L, Hkv, hd] at rows
@@ -94,7 +122,8 @@ def layer_rows(cfg, w, h_rows, pos, k_cache, v_cache, ft=np.float32):
     n = h_rows.shape[0]
     hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     eps = cfg.rms_eps
-    a = rms_norm(h_rows, w.attn_norm, eps, ft)
+    rnd = rounding(cfg, bf16_ops)
+    a = _r(rnd, rms_norm(h_rows, w.attn_norm, eps, ft), ft)
     q = (a @ np.asarray(w.wq, ft).T).reshape(n, hq, hd)
     k = (a @ np.asarray(w.wk, ft).T).reshape(n, hkv, hd)
     v = (a @ np.asarray(w.wv, ft).T).reshape(n, hkv, hd)
@@ -103,27 +132,28 @@ def layer_rows(cfg, w, h_rows, pos, k_cache, v_cache, ft=np.float32):
         k = rms_norm(k, w.k_norm, eps, ft)
     q = rope(q, pos, cfg.rope_theta, ft)
     k = rope(k, pos, cfg.rope_theta, ft)
-    k_cache[pos] = k
-    v_cache[pos] = v
-    o = causal_attention(q, pos, k_cache, v_cache, ft).reshape(n, hq * hd)
-    h1 = np.asarray(h_rows, ft) + o @ np.asarray(w.wo, ft).T
-    b = rms_norm(h1, w.mlp_norm, eps, ft)
+    k_cache[pos] = _r(rnd, k, ft)
+    v_cache[pos] = _r(rnd, v, ft)
+    o = causal_attention(_r(rnd, q, ft), pos, k_cache, v_cache, ft, rnd).reshape(n, hq * hd)
+    h1 = np.asarray(h_rows, ft) + _r(rnd, o, ft) @ np.asarray(w.wo, ft).T
+    b = _r(rnd, rms_norm(h1, w.mlp_norm, eps, ft), ft)
     act = silu(b @ np.asarray(w.w_gate, ft).T) * (b @ np.asarray(w.w_up, ft).T)
-    return h1 + act @ np.asarray(w.w_down, ft).T
+    return h1 + _r(rnd, act, ft) @ np.asarray(w.w_down, ft).T
 
 
-def k_rows(cfg, w, h_rows, pos, ft=np.float32):
+def k_rows(cfg, w, h_rows, pos, ft=np.float32, bf16_ops=None):
     """Current keys of the given rows: RoPE_pos(knorm(RMSNorm(h) @ Wk^T)) -> [n, Hkv, hd].
-    These are the K_i^current of Request Order Matters §2.2 Eq. 1."""
+    These are the K_i^current of Request Order Matters §2.2 Eq. 1 (kept unrounded: they are
+    compared, not stored)."""
     n = h_rows.shape[0]
-    a = rms_norm(h_rows, w.attn_norm, cfg.rms_eps, ft)
+    a = _r(rounding(cfg, bf16_ops), rms_norm(h_rows, w.attn_norm, cfg.rms_eps, ft), ft)
     k = (a @ np.asarray(w.wk, ft).T).reshape(n, cfg.n_kv_heads, cfg.head_dim)
     if cfg.qk_norm:
         k = rms_norm(k, w.k_norm, cfg.rms_eps, ft)
     return rope(k, pos, cfg.rope_theta, ft)
 
 
-def full_prefill(model, tokens, ft=np.float32, n_layers=None):
+def full_prefill(model, tokens, ft=np.float32, n_layers=None, bf16_ops=None):
     """QCFuse §2.1.1 Eq. 2: every layer on every token at positions 0..n-1, causal.
 
     model: object with ``cfg``, ``embed`` [vocab, d], ``final_norm`` [d], ``layer(l)``.
@@ -137,12 +167,12 @@ def full_prefill(model, tokens, ft=np.float32, n_layers=None):
     h = np.asarray(model.embed[tokens], dtype=ft)
     pos = np.arange(n)
     for l in range(ly):
-        h = layer_rows(cfg, model.layer(l), h, pos, kc[l], vc[l], ft)
+        h = layer_rows(cfg, model.layer(l), h, pos, kc[l], vc[l], ft, bf16_ops)
     return kc, vc, rms_norm(h, model.final_norm, cfg.rms_eps, ft), h
 
 
-def chunk_prefill(model, chunk, ft=np.float32, n_layers=None):
+def chunk_prefill(model, chunk, ft=np.float32, n_layers=None, bf16_ops=None):
     """QCFuse §2.1.2 Eq. 3: a chunk's own cache, prefilled standalone at local positions
     0..|c|-1. Returns (K [Ly, |c|, Hkv, hd], V)."""
-    kc, vc, _, _ = full_prefill(model, chunk, ft, n_layers)
+    kc, vc, _, _ = full_prefill(model, chunk, ft, n_layers, bf16_ops)
     return kc, vc

@@ -21,7 +21,7 @@ MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
            "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
-           "cf_blend_prefill"]
+           "cf_blend_prefill", "cf_profile_enable", "cf_profile_report"]
 
 
 class CfError(RuntimeError):
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         "cf_ctx_destroy": (None, [vp]),
         "cf_last_error": (ctypes.c_char_p, []),
         "cf_version": (ctypes.c_char_p, []),
+        "cf_profile_enable": (i32, [i32]),
+        "cf_profile_report": (ctypes.c_char_p, []),
         "cf_rope_reposition": (i32, [vp, vp, vp, i64, i32, vp, vp, i64, i32, vp, i32, i32, i32, vp]),
         "cf_kv_deviation": (i32, [vp, i32, i64, vp, i32, i64, vp, i32, i32, vp]),
         "cf_topk_workspace_size": (sz, [i32, i32]),
@@ -83,6 +85,17 @@ def _check(status: int):
 
 def version() -> str:
     return lib().cf_version().decode()
+
+
+def profile_enable(on: bool = True):
+    """Bracket every libcf kernel launch with HIP events (see cf_profile_enable)."""
+    _check(lib().cf_profile_enable(1 if on else 0))
+
+
+def profile_report() -> dict:
+    """{kernel name: (launches, total ms)} since the previous report (waits for the events)."""
+    import json
+    return {k: (int(v[0]), float(v[1])) for k, v in json.loads(lib().cf_profile_report().decode()).items()}
 
 
 # ----------------------------------------------------------------------------- torch plumbing

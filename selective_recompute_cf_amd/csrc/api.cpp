@@ -48,6 +48,41 @@ cf_status fail(cf_status s, const char* fmt, ...) {
     if (e_ != hipSuccess) return fail(CF_EHIP, "%s: %s", #expr, hipGetErrorString(e_));      \
   } while (0)
 
+// ------------------------------------------------------------------ optional kernel timing
+// While enabled, each launch is bracketed by two HIP events recorded on the launch's own
+// stream; cf_profile_report() waits for them and sums the elapsed times per kernel name.
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+std::string g_report;
+
+hipEvent_t prof_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F launch) {
+  if (!g_prof) return launch();
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (a) (void)hipEventRecord(a, st);
+  const hipError_t e = launch();
+  if (b) (void)hipEventRecord(b, st);
+  if (a && b) g_recs.push_back({name, a, b});
+  return e;
+}
+#define CF_RUN(name, expr) CF_HIP(timed(name, st, [&]() { return (expr); }))
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Makes the context's device current for the duration of a call and restores the caller's.
@@ -148,20 +183,20 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   float* HS = reinterpret_cast<float*>(ws + lw.hs);
   void* ACT = ws + lw.act;
 
-  CF_HIP(cf::launch_rmsnorm_rows(dt, hidden, sel, n, L, d, w->attn_norm, m.rms_eps, X, d, st));
+  CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, sel, n, L, d, w->attn_norm, m.rms_eps, X, d, st));
   cf::GemmArgs g{};
   g.dt = dt;
   g.A = X; g.lda = d;
   g.B[0] = w->wq; g.B[1] = w->wk; g.B[2] = w->wv; g.nb0 = qd; g.nb1 = qd + kvd;
   g.M = n; g.N = qd + 2 * kvd; g.K = d; g.splits = 1; g.epi = cf::EPI_F32; g.C = QKV; g.ldc = qd + 2 * kvd;
-  CF_HIP(cf::launch_gemm(g, st));
+  CF_RUN("gemm/qkv", cf::launch_gemm(g, st));
 
   cf::QkvPost qp{};
   qp.qkv = QKV; qp.ld = qd + 2 * kvd; qp.rows = sel; qp.n = n; qp.L = L;
   qp.hq = m.n_q_heads; qp.hkv = m.n_kv_heads; qp.hd = hd; qp.qk_norm = m.qk_norm;
   qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = m.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
   qp.q_out = Q; qp.k_cache = kc; qp.v_cache = vc;
-  CF_HIP(cf::launch_qkv_post(dt, qp, st));
+  CF_RUN("qkv_post", cf::launch_qkv_post(dt, qp, st));
 
   cf::AttnArgs at{};
   at.dt = dt; at.q = Q; at.ldq = qd; at.pos = sel; at.n = n; at.k = kc; at.v = vc; at.L = L;
@@ -169,42 +204,43 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   cf::attn_plan(dt, n, L, m.n_q_heads, m.n_kv_heads, hd, c->n_cu, &at.splits, &at.split_len);
   at.o_part = reinterpret_cast<float*>(ws + lw.opart);
   at.ml_part = reinterpret_cast<float*>(ws + lw.mlpart);
-  CF_HIP(cf::launch_attention(at, st));
+  CF_RUN("attention", cf::launch_attention(at, st));
+  if (at.splits > 1) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
 
   float* part = reinterpret_cast<float*>(ws + lw.part);
-  auto resid_gemm = [&](const void* A, int lda, const void* B, int K, const float* resid, const int* rrows,
-                        float* out, const int* orows) -> cf_status {
+  auto resid_gemm = [&](const char* name, const void* A, int lda, const void* B, int K, const float* resid,
+                        const int* rrows, float* out, const int* orows) -> cf_status {
     cf::GemmArgs r{};
     r.dt = dt; r.A = A; r.lda = lda; r.B[0] = r.B[1] = r.B[2] = B; r.nb0 = r.nb1 = d;
     r.M = n; r.N = d; r.K = K; r.L = L;
     r.splits = cf::gemm_splits(dt, n, d, K, cf::EPI_RESID, c->n_cu);
     if (r.splits > 1) {
       r.epi = cf::EPI_PARTIAL; r.C = part; r.ldc = d;
-      CF_HIP(cf::launch_gemm(r, st));
-      CF_HIP(cf::launch_splitk_reduce(part, r.splits, n, d, resid, rrows, out, orows, L, st));
+      CF_RUN(name, cf::launch_gemm(r, st));
+      CF_RUN("splitk_reduce", cf::launch_splitk_reduce(part, r.splits, n, d, resid, rrows, out, orows, L, st));
     } else {
       r.epi = cf::EPI_RESID; r.resid = resid; r.resid_rows = rrows; r.out = out; r.out_rows = orows;
-      CF_HIP(cf::launch_gemm(r, st));
+      CF_RUN(name, cf::launch_gemm(r, st));
     }
     return CF_OK;
   };
-  cf_status s = resid_gemm(AO, qd, w->wo, qd, hidden, sel, HS, nullptr);
+  cf_status s = resid_gemm("gemm/o", AO, qd, w->wo, qd, hidden, sel, HS, nullptr);
   if (s != CF_OK) return s;
 
-  CF_HIP(cf::launch_rmsnorm_rows(dt, HS, nullptr, n, n, d, w->mlp_norm, m.rms_eps, X, d, st));
+  CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, HS, nullptr, n, n, d, w->mlp_norm, m.rms_eps, X, d, st));
   cf::GemmArgs gu{};
   gu.dt = dt; gu.A = X; gu.lda = d; gu.B[0] = w->w_gate; gu.B[1] = w->w_up; gu.B[2] = w->w_up;
   gu.M = n; gu.K = d; gu.splits = 1;
   if (dt == cf::BF16) {
     gu.N = F; gu.nb0 = F; gu.nb1 = F; gu.epi = cf::EPI_SWIGLU; gu.act = ACT; gu.ld_act = F;
-    CF_HIP(cf::launch_gemm(gu, st));
+    CF_RUN("gemm/gate_up", cf::launch_gemm(gu, st));
   } else {
     float* GU = reinterpret_cast<float*>(ws + lw.gu);
     gu.N = 2 * F; gu.nb0 = F; gu.nb1 = 2 * F; gu.epi = cf::EPI_F32; gu.C = GU; gu.ldc = 2 * F;
-    CF_HIP(cf::launch_gemm(gu, st));
-    CF_HIP(cf::launch_swiglu(dt, GU, n, F, ACT, st));
+    CF_RUN("gemm/gate_up", cf::launch_gemm(gu, st));
+    CF_RUN("swiglu", cf::launch_swiglu(dt, GU, n, F, ACT, st));
   }
-  return resid_gemm(ACT, F, w->w_down, F, HS, nullptr, hidden, sel);
+  return resid_gemm("gemm/down", ACT, F, w->w_down, F, HS, nullptr, hidden, sel);
 }
 
 cf_status check_ctx(const cf_ctx* c) {
@@ -258,8 +294,8 @@ cf_status enqueue_reposition(const cf_ctx* c, const void* ks, const void* vs, in
       cb.delta[i] = t[2] - t[1];
       cb.blk0[i + 1] = cb.blk0[i] + (t[3] + cf::REPOS_ROWS_PER_BLOCK - 1) / cf::REPOS_ROWS_PER_BLOCK;
     }
-    CF_HIP(cf::launch_reposition(dt_of(c), ks, vs, sls, kb, vb, bls, cb, kvd, c->cfg.head_dim, c->cos_t, c->sin_t,
-                                 lb, le - lb, st));
+    CF_RUN("reposition", cf::launch_reposition(dt_of(c), ks, vs, sls, kb, vb, bls, cb, kvd, c->cfg.head_dim,
+                                               c->cos_t, c->sin_t, lb, le - lb, st));
   }
   return CF_OK;
 }
@@ -276,12 +312,12 @@ cf_status enqueue_select(const float* dev, int n, int k, int mode, const int32_t
                          double* ws, hipStream_t st) {
   if (k == 0) return CF_OK;
   if (mode == CF_SEL_TOKEN_TOPK) {
-    CF_HIP(cf::launch_topk_token(dev, n, k, out, st));
+    CF_RUN("topk_token", cf::launch_topk_token(dev, n, k, out, st));
   } else {
     cf::SpanArgs sp{};
     sp.n_spans = ns;
     for (int i = 0; i <= ns; ++i) sp.b[i] = bounds[i];
-    CF_HIP(cf::launch_topk_spans(dev, n, k, sp, out, ws, st));
+    CF_RUN("topk_spans", cf::launch_topk_spans(dev, n, k, sp, out, ws, st));
   }
   return CF_OK;
 }
@@ -294,6 +330,39 @@ extern "C" {
 const char* cf_last_error(void) { return g_err.c_str(); }
 
 const char* cf_version(void) { return "libcf 0.1 (gfx950)"; }
+
+cf_status cf_profile_enable(int32_t on) {
+  g_err.clear();
+  g_prof = on != 0;
+  return CF_OK;
+}
+
+const char* cf_profile_report(void) {
+  std::vector<std::pair<std::string, std::pair<long, double>>> acc;
+  for (const ProfRec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) ms = -1.f;
+    auto it = std::find_if(acc.begin(), acc.end(), [&](const auto& p) { return p.first == r.name; });
+    if (it == acc.end()) {
+      acc.push_back({r.name, {0, 0.0}});
+      it = acc.end() - 1;
+    }
+    it->second.first += 1;
+    it->second.second += ms;
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  g_report = "{";
+  char buf[160];
+  for (size_t i = 0; i < acc.size(); ++i) {
+    snprintf(buf, sizeof buf, "%s\"%s\": [%ld, %.6f]", i ? ", " : "", acc[i].first.c_str(), acc[i].second.first,
+             acc[i].second.second);
+    g_report += buf;
+  }
+  g_report += "}";
+  return g_report.c_str();
+}
 
 cf_status cf_ctx_create(const cf_model_cfg* cfg, int32_t max_pos, int32_t device, cf_ctx** out) {
   g_err.clear();
@@ -384,7 +453,7 @@ cf_status cf_kv_deviation(const void* k_new, int32_t new_dtype, int64_t ld_new, 
   CF_CHECK(aligned16(k_new) && aligned16(k_ref), CF_EINVAL, "key pointers must be 16-byte aligned");
   CF_CHECK(ld_new >= kv_dim && ld_ref >= kv_dim && ld_new % 8 == 0 && ld_ref % 8 == 0, CF_ESHAPE,
            "row strides must be >= kv_dim and multiples of 8");
-  CF_HIP(cf::launch_deviation(new_dtype == CF_BF16 ? cf::BF16 : cf::F32, k_new, ld_new,
+  CF_RUN("deviation", cf::launch_deviation(new_dtype == CF_BF16 ? cf::BF16 : cf::F32, k_new, ld_new,
                               ref_dtype == CF_BF16 ? cf::BF16 : cf::F32, k_ref, ld_ref, dev, n_tok, kv_dim, st));
   return CF_OK;
 }
@@ -498,8 +567,8 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
     if (cf_status s = enqueue_reposition(c, k_store, v_store, sls, k_out, v_out, ols, tab, m, first_sel,
                                          mc.n_layers, st))
       return s;
-  CF_HIP(cf::launch_embed(dt, tokens, L, embed, mc.vocab, mc.d_model, hidden, st));
-  CF_HIP(cf::launch_iota(ident, L, 0, st));
+  CF_RUN("embed", cf::launch_embed(dt, tokens, L, embed, mc.vocab, mc.d_model, hidden, st));
+  CF_RUN("iota", cf::launch_iota(ident, L, 0, st));
   for (int l = 0; l < first_sel; ++l)
     if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), ident, L, L, lws, lw_full, st)) return s;
 
@@ -510,30 +579,30 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
       // current keys of the context rows at the selection layer and their deviation
       void* X = lws + lw_full.x;  // the full-row layout holds N rows of X and of K
       float* KN = reinterpret_cast<float*>(lws + lw_full.qkv);
-      CF_HIP(cf::launch_rmsnorm_rows(dt, hidden, nullptr, N, L, mc.d_model, w->attn_norm, mc.rms_eps, X, mc.d_model,
-                                     st));
+      CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, nullptr, N, L, mc.d_model, w->attn_norm, mc.rms_eps, X,
+                                                     mc.d_model, st));
       cf::GemmArgs g{};
       g.dt = dt; g.A = X; g.lda = mc.d_model; g.B[0] = g.B[1] = g.B[2] = w->wk; g.nb0 = g.nb1 = (int)kvd;
       g.M = N; g.N = (int)kvd; g.K = mc.d_model; g.splits = 1; g.epi = cf::EPI_F32; g.C = KN; g.ldc = kvd;
-      CF_HIP(cf::launch_gemm(g, st));
+      CF_RUN("gemm/k_sel", cf::launch_gemm(g, st));
       cf::QkvPost qp{};
       qp.qkv = KN; qp.ld = kvd; qp.rows = nullptr; qp.n = N; qp.L = L;
       qp.hq = mc.n_q_heads; qp.hkv = mc.n_kv_heads; qp.hd = mc.head_dim; qp.qk_norm = mc.qk_norm;
       qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = mc.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
       qp.dev = dev; qp.k_ref = K_l(s_layer);
-      CF_HIP(cf::launch_qkv_post(dt, qp, st));
+      CF_RUN("qkv_post", cf::launch_qkv_post(dt, qp, st));
       if (cf_status s = enqueue_select(dev, N, k, mode, bounds, ns, sel, reinterpret_cast<double*>(W + pw.topk), st))
         return s;
-      if (out_dev) CF_HIP(cf::launch_copy_f32(out_dev, dev, N, st));
-      if (out_sel) CF_HIP(cf::launch_copy_i32(out_sel, sel, k, st));
+      if (out_dev) CF_RUN("copy", cf::launch_copy_f32(out_dev, dev, N, st));
+      if (out_sel) CF_RUN("copy", cf::launch_copy_i32(out_sel, sel, k, st));
     }
-    CF_HIP(cf::launch_iota(sel + k, U, N, st));
+    CF_RUN("iota", cf::launch_iota(sel + k, U, N, st));
     const LayerWs lw_sel = layer_ws(c, L, n_sel);
     for (int l = s_layer; l < mc.n_layers; ++l)
       if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st)) return s;
   }
   if (U > 0)
-    CF_HIP(cf::launch_rmsnorm_rows(cf::F32, hidden + (size_t)N * mc.d_model, nullptr, U, U, mc.d_model, final_norm,
+    CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(cf::F32, hidden + (size_t)N * mc.d_model, nullptr, U, U, mc.d_model, final_norm,
                                    mc.rms_eps, out_hidden, mc.d_model, st));
   return CF_OK;
 }

@@ -28,7 +28,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * KB];
   const int G = a.hq / a.hkv;
   const int rpt = 64 / G;  // selected rows per block
-  const int j0 = blockIdx.x * rpt, g = blockIdx.y, split = blockIdx.z;
+  // logical tile: query tile fastest, then split, then kv head: tiles reading the same K/V head
+  // are neighbours and run on the same XCD
+  const int q_tiles = (a.n + rpt - 1) / rpt;
+  const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
+  const int j0 = (lt % q_tiles) * rpt, split = (lt / q_tiles) % a.splits, g = lt / (q_tiles * a.splits);
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
   const int lg = lane / 16, lr = lane % 16;
   const int r = w * 16 + lr;
@@ -205,8 +209,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 // Combine split-KV partials: weights 2^(m_s - max m) (scores are in log2 units).
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int j = blockIdx.x;
-  for (int idx = threadIdx.x; idx < a.hq * a.hd; idx += blockDim.x) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)a.n * a.hq * a.hd) return;
+  const int j = (int)(gid / (a.hq * a.hd));
+  {
+    const int idx = (int)(gid % (a.hq * a.hd));
     const int head = idx / a.hd, d = idx % a.hd;
     float mx = -INFINITY;
     for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.ml_part[(((int64_t)s * a.n + j) * a.hq + head) * 2]);
@@ -268,6 +275,19 @@ __global__ __launch_bounds__(256) void attn_simple_kernel(AttnArgs a) {
   }
 }
 
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st) {
+  if (a.n == 0 || a.splits <= 1) return hipSuccess;
+  {
+    const int64_t total = (int64_t)a.n * a.hq * a.hd;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (a.dt == BF16)
+      hipLaunchKernelGGL(attn_merge_kernel<bf16>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(attn_merge_kernel<float>, grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len) {
   *splits = 1;
   *split_len = ((L + KB - 1) / KB) * KB;
@@ -284,14 +304,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n == 0) return hipSuccess;
   if (a.dt == BF16) {
     const int G = a.hq / a.hkv, rpt = 64 / G;
-    dim3 grid((a.n + rpt - 1) / rpt, a.hkv, a.splits);
+    dim3 grid(((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
     if (a.hd == 128)
       hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel<bf16>, dim3(a.n), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(attn_simple_kernel<float>, dim3(a.n), dim3(256), 0, st, a);
   }

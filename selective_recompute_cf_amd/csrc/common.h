@@ -79,4 +79,15 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Workgroups of a 1-D grid are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8),
+// each with its own L2. This maps b to a logical tile id so that every XCD works through one
+// contiguous range of tiles: neighbouring tiles (which share operands) then run on the same XCD
+// at the same time and share its L2. Bijective on [0, n).
+constexpr int N_XCD = 8;
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int full = (n / N_XCD) * N_XCD;
+  if (b >= full) return b;
+  return (b % N_XCD) * (full / N_XCD) + b / N_XCD;
+}
+
 }  // namespace cf

@@ -33,7 +33,11 @@ __device__ __forceinline__ const bf16* b_row_ptr(const GemmArgs& a, int n_tile, 
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM * BK];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * BK];
-  const int n_tile = blockIdx.x, m_tile = blockIdx.y, split = blockIdx.z;
+  // logical tile: M fastest, so the M tiles that share a weight tile are neighbours (same XCD)
+  const int m_tiles = (a.M + BM - 1) / BM;
+  const int n_tiles = a.epi == EPI_SWIGLU ? (a.N + 63) / 64 : (a.N + BN - 1) / BN;
+  const int t = xcd_tile(blockIdx.x, m_tiles * n_tiles * a.splits);
+  const int m_tile = t % m_tiles, n_tile = (t / m_tiles) % n_tiles, split = t / (m_tiles * n_tiles);
   const int m0 = m_tile * BM;
   const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
   const int wm = wave / 2, wn = wave % 2;
@@ -229,7 +233,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.dt == BF16) {
     const int ncols = a.epi == EPI_SWIGLU ? (a.N + 63) / 64 : (a.N + BN - 1) / BN;
-    dim3 grid(ncols, (a.M + BM - 1) / BM, a.splits);
+    dim3 grid(ncols * ((a.M + BM - 1) / BM) * a.splits);
     hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, a);
   } else {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, 1);

@@ -79,7 +79,8 @@ struct AttnArgs {
   int splits; int split_len;           // split-KV: keys [s*split_len, (s+1)*split_len)
   float* o_part; float* ml_part;       // [splits][n][hq][hd], [splits][n][hq][2]
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);        // main pass
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st);  // split-KV merge (splits > 1)
 void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len);
 
 // ----------------------------------------------------------------- selection (topk.hip)

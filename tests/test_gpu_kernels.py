@@ -22,7 +22,7 @@ def test_reposition_matches_oracle(dtype, hd):
     """QCFuse Eq. 4 with rotation composition: chunks of ragged length, negative and positive
     offsets, a layer range that leaves layer 0 untouched."""
     torch = _torch()
-    cfg = synth.TINY.replace(head_dim=hd, n_kv_heads=2, dtype=dtype)
+    cfg = synth.TINY.replace(head_dim=hd, n_kv_heads=2, dtype=dtype, n_layers=3)
     kvd = cfg.kv_dim
     Ly, rows, L = 3, 300, 400
     say(f"reposition dtype={dtype} hd={hd}")

@@ -441,6 +441,30 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(synth.bf16_round(x), want)
 
 
+def test_oracle_bf16_rounding_matches_torch():
+    """The oracle's own bf16 rounding (used for bf16-model arithmetic) against torch's conversion."""
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * s for s in (1e-3, 1.0, 300.0)] +
+                       [np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0, -0.0, 3e-39], np.float32)])
+    want = torch.tensor(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(oracle.bf16_round(x), want)
+
+
+def test_bf16_model_pure_math_path_matches_torch_and_rounding_is_small():
+    """For a bf16 model the oracle is the same textbook decoder (torch pin); in its bf16-arithmetic
+    mode it stays within a rounding-sized distance of it and stores bf16 K/V."""
+    cfg = TINY.replace(dtype="bf16")
+    model = _Model(cfg)
+    toks = np.random.default_rng(14).integers(0, cfg.vocab, 40)
+    K, V, out, _ = oracle.full_prefill(model, toks, F64, n_layers=2)
+    K2, V2, out2 = _torch_decoder(model, toks, 2)
+    np.testing.assert_allclose(out, out2, rtol=1e-9, atol=1e-10)
+    Kb, Vb, outb, _ = oracle.full_prefill(model, toks, np.float32, n_layers=2, bf16_ops=True)
+    assert np.array_equal(oracle.bf16_round(Kb), Kb) and np.array_equal(oracle.bf16_round(Vb), Vb)
+    rel = np.linalg.norm(outb - out) / np.linalg.norm(out)
+    assert 1e-5 < rel < 2e-2
+
+
 def test_synthetic_inputs_are_deterministic():
     a = synth.layer_weights(TINY, 1)
     b = synth.layer_weights(TINY, 1)
