@@ -104,32 +104,53 @@ size_t esize(const cf_ctx* c) { return c->cfg.dtype == CF_BF16 ? 2 : 4; }
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ------------------------------------------------------------------ workspace of one layer pass
-struct LayerWs {
-  size_t x, qkv, q, ao, hs, act, gu, part, opart, mlpart, total;
-  int attn_splits, attn_split_len, gemm_splits;
+struct LayerPlan {
+  cf::GemmPlan qkv, o, gu, down, ksel;
+  int attn_splits, attn_split_len;
 };
 
-LayerWs layer_ws(const cf_ctx* c, int L, int R) {
+LayerPlan layer_plan(const cf_ctx* c, int L, int R, int ksel_rows) {
+  const cf_model_cfg& m = c->cfg;
+  const cf::Dt dt = dt_of(c);
+  const int d = m.d_model, qd = m.n_q_heads * m.head_dim, kvd = m.n_kv_heads * m.head_dim, F = m.d_ffn;
+  LayerPlan p{};
+  p.qkv = cf::gemm_plan(dt, R, qd + 2 * kvd, d, false, true, c->n_cu);
+  p.o = cf::gemm_plan(dt, R, d, qd, false, true, c->n_cu);
+  p.gu = cf::gemm_plan(dt, R, F, d, true, false, c->n_cu);
+  p.down = cf::gemm_plan(dt, R, d, F, false, true, c->n_cu);
+  p.ksel = cf::gemm_plan(dt, ksel_rows, kvd, d, false, true, c->n_cu);
+  cf::attn_plan(dt, R, L, m.n_q_heads, m.n_kv_heads, m.head_dim, c->n_cu, &p.attn_splits, &p.attn_split_len);
+  return p;
+}
+
+struct LayerWs {
+  size_t x, qkv, q, ao, hs, act, gu, part, opart, mlpart, total;
+  LayerPlan plan;
+};
+
+// Scratch of one layer pass over R rows of an L-row request; ksel_rows > 0 also sizes the
+// selection-layer key projection of that many context rows (it reuses x and qkv).
+LayerWs layer_ws(const cf_ctx* c, int L, int R, int ksel_rows = 0) {
   const cf_model_cfg& m = c->cfg;
   const size_t es = esize(c);
   const size_t d = m.d_model, qd = (size_t)m.n_q_heads * m.head_dim, kvd = (size_t)m.n_kv_heads * m.head_dim;
   const size_t F = m.d_ffn;
   LayerWs w{};
-  cf::attn_plan(dt_of(c), R, L, m.n_q_heads, m.n_kv_heads, m.head_dim, c->n_cu, &w.attn_splits, &w.attn_split_len);
-  w.gemm_splits = std::max(cf::gemm_splits(dt_of(c), R, (int)d, (int)qd, cf::EPI_RESID, c->n_cu),
-                           cf::gemm_splits(dt_of(c), R, (int)d, (int)F, cf::EPI_RESID, c->n_cu));
+  w.plan = layer_plan(c, L, R, ksel_rows);
+  const LayerPlan& p = w.plan;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
-  w.x = take((size_t)R * d * es);
-  w.qkv = take((size_t)R * (qd + 2 * kvd) * 4);
+  w.x = take((size_t)std::max(R, ksel_rows) * d * es);
+  w.qkv = take(std::max((size_t)p.qkv.splits * R * (qd + 2 * kvd), (size_t)p.ksel.splits * ksel_rows * kvd) * 4);
   w.q = take((size_t)R * qd * es);
   w.ao = take((size_t)R * qd * es);
   w.hs = take((size_t)R * d * 4);
   w.act = take((size_t)R * F * es);
   w.gu = take(m.dtype == CF_BF16 ? 0 : (size_t)R * 2 * F * 4);
-  w.part = take(w.gemm_splits > 1 ? (size_t)w.gemm_splits * R * d * 4 : 0);
-  w.opart = take(w.attn_splits > 1 ? (size_t)w.attn_splits * R * qd * 4 : 0);
-  w.mlpart = take(w.attn_splits > 1 ? (size_t)w.attn_splits * R * m.n_q_heads * 2 * 4 : 0);
+  const int ps = std::max(p.o.splits, p.down.splits);
+  w.part = take(ps > 1 ? (size_t)ps * R * d * 4 : 0);
+  w.opart = take(p.attn_splits > 1 ? (size_t)p.attn_splits * R * qd * 4 : 0);
+  w.mlpart = take(p.attn_splits > 1 ? (size_t)p.attn_splits * R * m.n_q_heads * 2 * 4 : 0);
   w.total = off;
   return w;
 }
@@ -149,7 +170,7 @@ PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode) {
   p.dev = take((size_t)std::max(N, 1) * 4);
   p.topk = take(mode == CF_SEL_DOC_SPANS ? (size_t)(N + 1) * 8 : 0);
   // the layer scratch serves full-row layers (R = L) and selected-row layers (R = k + U)
-  const LayerWs a = layer_ws(c, L, L), b = layer_ws(c, L, std::min(L, k + U));
+  const LayerWs a = layer_ws(c, L, L, mode == CF_SEL_ALL ? 0 : N), b = layer_ws(c, L, std::min(L, k + U));
   p.layer = take(std::max(a.total, b.total));
   p.total = off;
   return p;
@@ -183,16 +204,19 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   float* HS = reinterpret_cast<float*>(ws + lw.hs);
   void* ACT = ws + lw.act;
 
+  const LayerPlan& P = lw.plan;
   CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, sel, n, L, d, w->attn_norm, m.rms_eps, X, d, st));
   cf::GemmArgs g{};
-  g.dt = dt;
+  g.dt = dt; g.cfg = P.qkv.cfg; g.splits = P.qkv.splits;
   g.A = X; g.lda = d;
   g.B[0] = w->wq; g.B[1] = w->wk; g.B[2] = w->wv; g.nb0 = qd; g.nb1 = qd + kvd;
-  g.M = n; g.N = qd + 2 * kvd; g.K = d; g.splits = 1; g.epi = cf::EPI_F32; g.C = QKV; g.ldc = qd + 2 * kvd;
+  g.M = n; g.N = qd + 2 * kvd; g.K = d; g.epi = g.splits > 1 ? cf::EPI_PARTIAL : cf::EPI_F32;
+  g.C = QKV; g.ldc = qd + 2 * kvd;
   CF_RUN("gemm/qkv", cf::launch_gemm(g, st));
 
   cf::QkvPost qp{};
   qp.qkv = QKV; qp.ld = qd + 2 * kvd; qp.rows = sel; qp.n = n; qp.L = L;
+  qp.splits = g.splits; qp.split_stride = (int64_t)n * (qd + 2 * kvd);
   qp.hq = m.n_q_heads; qp.hkv = m.n_kv_heads; qp.hd = hd; qp.qk_norm = m.qk_norm;
   qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = m.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
   qp.q_out = Q; qp.k_cache = kc; qp.v_cache = vc;
@@ -201,36 +225,37 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   cf::AttnArgs at{};
   at.dt = dt; at.q = Q; at.ldq = qd; at.pos = sel; at.n = n; at.k = kc; at.v = vc; at.L = L;
   at.hq = m.n_q_heads; at.hkv = m.n_kv_heads; at.hd = hd; at.out = AO; at.ldo = qd;
-  cf::attn_plan(dt, n, L, m.n_q_heads, m.n_kv_heads, hd, c->n_cu, &at.splits, &at.split_len);
+  at.splits = P.attn_splits; at.split_len = P.attn_split_len;
   at.o_part = reinterpret_cast<float*>(ws + lw.opart);
   at.ml_part = reinterpret_cast<float*>(ws + lw.mlpart);
   CF_RUN("attention", cf::launch_attention(at, st));
   if (at.splits > 1) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
 
   float* part = reinterpret_cast<float*>(ws + lw.part);
-  auto resid_gemm = [&](const char* name, const void* A, int lda, const void* B, int K, const float* resid,
-                        const int* rrows, float* out, const int* orows) -> cf_status {
+  auto proj = [&](const cf::GemmPlan& pl, const void* A, int lda, const void* B, int K) {
     cf::GemmArgs r{};
-    r.dt = dt; r.A = A; r.lda = lda; r.B[0] = r.B[1] = r.B[2] = B; r.nb0 = r.nb1 = d;
+    r.dt = dt; r.cfg = pl.cfg; r.splits = pl.splits;
+    r.A = A; r.lda = lda; r.B[0] = r.B[1] = r.B[2] = B; r.nb0 = r.nb1 = d;
     r.M = n; r.N = d; r.K = K; r.L = L;
-    r.splits = cf::gemm_splits(dt, n, d, K, cf::EPI_RESID, c->n_cu);
-    if (r.splits > 1) {
-      r.epi = cf::EPI_PARTIAL; r.C = part; r.ldc = d;
-      CF_RUN(name, cf::launch_gemm(r, st));
-      CF_RUN("splitk_reduce", cf::launch_splitk_reduce(part, r.splits, n, d, resid, rrows, out, orows, L, st));
-    } else {
-      r.epi = cf::EPI_RESID; r.resid = resid; r.resid_rows = rrows; r.out = out; r.out_rows = orows;
-      CF_RUN(name, cf::launch_gemm(r, st));
-    }
-    return CF_OK;
+    return r;
   };
-  cf_status s = resid_gemm("gemm/o", AO, qd, w->wo, qd, hidden, sel, HS, nullptr);
-  if (s != CF_OK) return s;
+  // O projection + residual (+ the MLP RMSNorm when split-K needs a reduction pass anyway)
+  cf::GemmArgs o = proj(P.o, AO, qd, w->wo, qd);
+  if (o.splits > 1) {
+    o.epi = cf::EPI_PARTIAL; o.C = part; o.ldc = d;
+    CF_RUN("gemm/o", cf::launch_gemm(o, st));
+    CF_RUN("reduce_resid_norm", cf::launch_reduce_resid_norm(dt, part, o.splits, n, d, hidden, sel, L, HS,
+                                                              w->mlp_norm, m.rms_eps, X, st));
+  } else {
+    o.epi = cf::EPI_RESID; o.resid = hidden; o.resid_rows = sel; o.out = HS; o.out_rows = nullptr;
+    CF_RUN("gemm/o", cf::launch_gemm(o, st));
+    CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, HS, nullptr, n, n, d, w->mlp_norm, m.rms_eps, X, d, st));
+  }
 
-  CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, HS, nullptr, n, n, d, w->mlp_norm, m.rms_eps, X, d, st));
   cf::GemmArgs gu{};
-  gu.dt = dt; gu.A = X; gu.lda = d; gu.B[0] = w->w_gate; gu.B[1] = w->w_up; gu.B[2] = w->w_up;
-  gu.M = n; gu.K = d; gu.splits = 1;
+  gu.dt = dt; gu.cfg = P.gu.cfg; gu.splits = 1;
+  gu.A = X; gu.lda = d; gu.B[0] = w->w_gate; gu.B[1] = w->w_up; gu.B[2] = w->w_up;
+  gu.M = n; gu.K = d;
   if (dt == cf::BF16) {
     gu.N = F; gu.nb0 = F; gu.nb1 = F; gu.epi = cf::EPI_SWIGLU; gu.act = ACT; gu.ld_act = F;
     CF_RUN("gemm/gate_up", cf::launch_gemm(gu, st));
@@ -240,7 +265,17 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
     CF_RUN("gemm/gate_up", cf::launch_gemm(gu, st));
     CF_RUN("swiglu", cf::launch_swiglu(dt, GU, n, F, ACT, st));
   }
-  return resid_gemm("gemm/down", ACT, F, w->w_down, F, HS, nullptr, hidden, sel);
+  // down projection + residual, written back to the selected rows
+  cf::GemmArgs dn = proj(P.down, ACT, F, w->w_down, F);
+  if (dn.splits > 1) {
+    dn.epi = cf::EPI_PARTIAL; dn.C = part; dn.ldc = d;
+    CF_RUN("gemm/down", cf::launch_gemm(dn, st));
+    CF_RUN("splitk_reduce", cf::launch_splitk_reduce(part, dn.splits, n, d, HS, nullptr, hidden, sel, L, st));
+  } else {
+    dn.epi = cf::EPI_RESID; dn.resid = HS; dn.resid_rows = nullptr; dn.out = hidden; dn.out_rows = sel;
+    CF_RUN("gemm/down", cf::launch_gemm(dn, st));
+  }
+  return CF_OK;
 }
 
 cf_status check_ctx(const cf_ctx* c) {
@@ -558,7 +593,7 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
   char* lws = W + pw.layer;
   int* ident = reinterpret_cast<int*>(W + pw.ident);
   const cf::Dt dt = dt_of(c);
-  const LayerWs lw_full = layer_ws(c, L, L);
+  const LayerWs lw_full = layer_ws(c, L, L, full ? 0 : N);
   auto K_l = [&](int l) { return static_cast<char*>(k_out) + (size_t)l * ols * esize(c); };
   auto V_l = [&](int l) { return static_cast<char*>(v_out) + (size_t)l * ols * esize(c); };
 
@@ -582,11 +617,14 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
       CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, nullptr, N, L, mc.d_model, w->attn_norm, mc.rms_eps, X,
                                                      mc.d_model, st));
       cf::GemmArgs g{};
-      g.dt = dt; g.A = X; g.lda = mc.d_model; g.B[0] = g.B[1] = g.B[2] = w->wk; g.nb0 = g.nb1 = (int)kvd;
-      g.M = N; g.N = (int)kvd; g.K = mc.d_model; g.splits = 1; g.epi = cf::EPI_F32; g.C = KN; g.ldc = kvd;
+      g.dt = dt; g.cfg = lw_full.plan.ksel.cfg; g.splits = lw_full.plan.ksel.splits;
+      g.A = X; g.lda = mc.d_model; g.B[0] = g.B[1] = g.B[2] = w->wk; g.nb0 = g.nb1 = (int)kvd;
+      g.M = N; g.N = (int)kvd; g.K = mc.d_model; g.epi = g.splits > 1 ? cf::EPI_PARTIAL : cf::EPI_F32;
+      g.C = KN; g.ldc = kvd;
       CF_RUN("gemm/k_sel", cf::launch_gemm(g, st));
       cf::QkvPost qp{};
       qp.qkv = KN; qp.ld = kvd; qp.rows = nullptr; qp.n = N; qp.L = L;
+      qp.splits = g.splits; qp.split_stride = (int64_t)N * kvd;
       qp.hq = mc.n_q_heads; qp.hkv = mc.n_kv_heads; qp.hd = mc.head_dim; qp.qk_norm = mc.qk_norm;
       qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = mc.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
       qp.dev = dev; qp.k_ref = K_l(s_layer);

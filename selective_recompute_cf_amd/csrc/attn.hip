@@ -6,14 +6,17 @@
 //
 // bf16 path (head_dim 64/128): one block = 64 query rows of one kv head (64/G selected rows x
 // the G query heads sharing that kv head), 4 waves of 16 rows. Keys stream in blocks of 64
-// through double-buffered LDS: K row-major with a 16-byte XOR swizzle, V transposed (hd-major)
-// with keys permuted so that one 16-byte read gives the 8 keys an MFMA lane group needs.
+// through double-buffered LDS (two blocks of global loads in flight); K and V tiles are stored
+// row-major with a 16-byte-chunk XOR swizzle by key, and the V^T operand is read with gfx950's
+// transposing LDS read (ds_read_b64_tr_b16).
 // S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16: in this orientation every lane
 // holds one query row (lane % 16) for both S and O, so the online-softmax state needs no
 // cross-lane exchange beyond 2 xor-shuffles. Softmax in fp32 with exp2; P rounded to bf16 for
 // the PV product. Split-KV over key ranges, merged with log-sum-exp weights.
 //
 // fp32 path: one block per query row, one wave per query head, online softmax per 64 keys.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -21,11 +24,17 @@ namespace cf {
 
 constexpr int KB = 64;  // keys per step
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int NCH = HD / 8;  // 16-byte chunks per key row
+  constexpr int NCH = HD / 8;     // 16-byte chunks per key row
+  constexpr int SWM = NCH - 1;    // chunk c of tile key t is stored at c ^ (t & SWM)
+  constexpr int CH = KB * NCH / 256;  // chunks of each of K and V per thread per step
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][KB * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * KB];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][KB * HD];
   const int G = a.hq / a.hkv;
   const int rpt = 64 / G;  // selected rows per block
   // logical tile: query tile fastest, then split, then kv head: tiles reading the same K/V head
@@ -62,62 +71,47 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   float m_i = -INFINITY, l_i = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
 
-  constexpr int KCH = KB * NCH / 256;        // K chunks per thread per step
-  constexpr int VUN = (KB / 4) * NCH;        // V units (4 keys x 8 dims) per step
-  uint4 rk[KCH];
-  uint4 rv[4];
-  auto gload = [&](int kbase) {
-#pragma unroll
-    for (int it = 0; it < KCH; ++it) {
-      const int ci = tid + 256 * it;
-      const int t = ci / NCH, c = ci % NCH;
-      const int key = min(kbase + t, a.L - 1);
-      rk[it] = *reinterpret_cast<const uint4*>(K + (int64_t)key * kvd + c * 8);
-    }
-    if (tid < VUN) {
-      const int kq = tid / NCH, hc = tid % NCH;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int key = min(kbase + kq * 4 + q, a.L - 1);
-        rv[q] = *reinterpret_cast<const uint4*>(V + (int64_t)key * kvd + hc * 8);
-      }
-    }
+  // two register sets of prefetched K/V chunks. They are ext-vector values, not arrays, so they
+  // live in VGPRs whatever the compiler decides about unrolling (arrays here were demoted to LDS
+  // and scratch memory).
+  typedef uint32_t PVec __attribute__((ext_vector_type(4 * CH)));
+  PVec rk0, rv0, rk1, rv1;
+#define CF_ATTN_GLOAD(RK, RV, STEP)                                                   \
+  do {                                                                                \
+    const int kbase_ = kbeg + (STEP) * KB;                                            \
+    _Pragma("unroll") for (int it_ = 0; it_ < CH; ++it_) {                            \
+      const int ci_ = tid + 256 * it_;                                                \
+      const int t_ = ci_ / NCH, c_ = ci_ % NCH;                                       \
+      const int64_t off_ = (int64_t)min(kbase_ + t_, a.L - 1) * kvd + c_ * 8;         \
+      const uint4 xk_ = *reinterpret_cast<const uint4*>(K + off_);                    \
+      const uint4 xv_ = *reinterpret_cast<const uint4*>(V + off_);                    \
+      RK[4 * it_] = xk_.x; RK[4 * it_ + 1] = xk_.y; RK[4 * it_ + 2] = xk_.z; RK[4 * it_ + 3] = xk_.w; \
+      RV[4 * it_] = xv_.x; RV[4 * it_ + 1] = xv_.y; RV[4 * it_ + 2] = xv_.z; RV[4 * it_ + 3] = xv_.w; \
+    }                                                                                 \
+  } while (0)
+#define CF_ATTN_SSTORE(RK, RV, BUF)                                                   \
+  do {                                                                                \
+    _Pragma("unroll") for (int it_ = 0; it_ < CH; ++it_) {                            \
+      const int ci_ = tid + 256 * it_;                                                \
+      const int t_ = ci_ / NCH, c_ = ci_ % NCH;                                       \
+      const int off_ = t_ * HD + ((c_ ^ (t_ & SWM)) * 8);                             \
+      *reinterpret_cast<uint4*>(&Ks[BUF][off_]) =                                     \
+          make_uint4(RK[4 * it_], RK[4 * it_ + 1], RK[4 * it_ + 2], RK[4 * it_ + 3]);  \
+      *reinterpret_cast<uint4*>(&Vs[BUF][off_]) =                                     \
+          make_uint4(RV[4 * it_], RV[4 * it_ + 1], RV[4 * it_ + 2], RV[4 * it_ + 3]);  \
+    }                                                                                 \
+  } while (0)
+  // V^T operand through the transposing LDS read: within each 16-lane group, lane q reads the
+  // 4 dims 16nt + 4(q%4).. of tile key kb + q/4 and lane lr receives V[kb + 0..3][16nt + lr]
+  auto vread = [&](int buf, int kb, int nt) __attribute__((always_inline)) {
+    const int t = kb + lr / 4;
+    const int col = nt * 16 + 4 * (lr % 4);
+    const int c = col / 8;
+    const bf16* ptr = &Vs[buf][t * HD + ((c ^ (t & SWM)) * 8) + (col % 8)];
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < KCH; ++it) {
-      const int ci = tid + 256 * it;
-      const int t = ci / NCH, c = ci % NCH;
-      *reinterpret_cast<uint4*>(&Ks[buf][t * HD + ((c ^ (t & 7)) * 8)]) = rk[it];
-    }
-    if (tid < VUN) {
-      const int kq = tid / NCH, hc = tid % NCH;
-      const int t0 = kq * 4;  // keys t0..t0+3: t0 = 32m + 16t' + 4g'
-      const int mm = t0 / 32, tp = (t0 / 16) & 1, gp = (t0 / 4) & 3;
-      const int chunk = 4 * mm + gp, off = 4 * tp;
-      const bf16* v0 = reinterpret_cast<const bf16*>(&rv[0]);
-      const bf16* v1 = reinterpret_cast<const bf16*>(&rv[1]);
-      const bf16* v2 = reinterpret_cast<const bf16*>(&rv[2]);
-      const bf16* v3 = reinterpret_cast<const bf16*>(&rv[3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int n = hc * 8 + e;
-        bf16x4 pk;
-        pk[0] = v0[e]; pk[1] = v1[e]; pk[2] = v2[e]; pk[3] = v3[e];
-        *reinterpret_cast<bf16x4*>(&Vt[buf][n * KB + ((chunk ^ (n & 7)) * 8) + off]) = pk;
-      }
-    }
-  };
-
-  if (nkb > 0) {
-    gload(kbeg);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nkb; ++it) {
-    const int cur = it & 1;
+  auto step = [&](int it, int cur) __attribute__((always_inline)) {
     const int kbase = kbeg + it * KB;
-    if (it + 1 < nkb) gload(kbase + KB);
     f32x4 s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -126,18 +120,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < HD / 32; ++kk) {
         const int c = kk * 4 + lg;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[cur][t * HD + ((c ^ (t & 7)) * 8)]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[cur][t * HD + ((c ^ (t & SWM)) * 8)]);
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[kt], 0, 0, 0);
       }
     }
     // s[kt][i] = S[row r][key kbase + 16kt + 4lg + i]
     float mx = -INFINITY;
+    const int lim = min(p, kend - 1);  // last visible key of this row in this split
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kbase + kt * 16 + 4 * lg + i;
-        const float v = (key <= p && key < kend) ? s[kt][i] * sl2 : -INFINITY;
+        const float v = key <= lim ? s[kt][i] * sl2 : -INFINITY;
         s[kt][i] = v;
         mx = fmaxf(mx, v);
       }
@@ -170,17 +165,36 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) pf[mm][tp * 4 + i] = (bf16)s[2 * mm + tp][i];
 #pragma unroll
     for (int nt = 0; nt < HD / 16; ++nt) {
-      const int n = nt * 16 + lr;
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const int c = 4 * mm + lg;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vt[cur][n * KB + ((c ^ (n & 7)) * 8)]);
+        const i16x4 lo = vread(cur, 32 * mm + 4 * lg, nt);
+        const i16x4 hi = vread(cur, 32 * mm + 16 + 4 * lg, nt);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[mm], o[nt], 0, 0, 0);
       }
     }
-    if (it + 1 < nkb) sstore(cur ^ 1);
+  };
+
+  // two key blocks of loads in flight (register sets 0 and 1), double-buffered LDS
+  if (nkb > 0) CF_ATTN_GLOAD(rk0, rv0, 0);
+  if (nkb > 1) CF_ATTN_GLOAD(rk1, rv1, 1);
+  if (nkb > 0) CF_ATTN_SSTORE(rk0, rv0, 0);
+  __syncthreads();
+  // step `it` reloads set it%2 (free since its data went to LDS) and stores set (it+1)%2
+  for (int it = 0; it < nkb; it += 2) {
+    if (it + 2 < nkb) CF_ATTN_GLOAD(rk0, rv0, it + 2);
+    step(it, 0);
+    if (it + 1 < nkb) CF_ATTN_SSTORE(rk1, rv1, 1);
     __syncthreads();
+    if (it + 1 < nkb) {
+      if (it + 3 < nkb) CF_ATTN_GLOAD(rk1, rv1, it + 3);
+      step(it + 1, 1);
+      if (it + 2 < nkb) CF_ATTN_SSTORE(rk0, rv0, 0);
+      __syncthreads();
+    }
   }
+#undef CF_ATTN_GLOAD
+#undef CF_ATTN_SSTORE
   if (!row_ok) return;
   // o[nt][i] = O[row r][hd 16nt + 4lg + i] (unnormalised)
   if (a.splits > 1) {
@@ -292,10 +306,13 @@ void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* spli
   *splits = 1;
   *split_len = ((L + KB - 1) / KB) * KB;
   if (dt != BF16 || n == 0) return;
+  // split the keys only when the query tiles alone would leave resident-block slots (2 per CU)
+  // empty; each split keeps at least 512 keys (the merge re-reads every split's partial output)
   const int G = hq / hkv;
-  const int items = ((n + 64 / G - 1) / (64 / G)) * hkv;
+  const long items = (long)((n + 64 / G - 1) / (64 / G)) * hkv;
+  const long slots = 2L * n_cu;
   int s = 1;
-  while (s < 8 && items * s < 2 * n_cu && L / (2 * s) >= 512) s *= 2;
+  while (s < 8 && items * (s + 1) <= slots + slots / 8 && L / (s + 1) >= 512) ++s;
   *splits = s;
   *split_len = (((L + s - 1) / s + KB - 1) / KB) * KB;
 }

@@ -15,135 +15,181 @@
 
 namespace cf {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+// Tile configuration: BM x BN block tile, WGM x WGN waves (each a (BM/WGM) x (BN/WGN) wave tile
+// of 16x16 MFMA tiles), BK = 64, PF = 1 or 2 K steps of global loads in flight (register sets).
+template <int BM_, int BN_, int WGM_, int WGN_, int PF_, int MINB_, int SWZ_ = 0>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, PF = PF_, MINB = MINB_;
+  // LDS swizzle of the 16-byte chunks of a 128-byte tile row: chunk c of row r is stored at
+  // c ^ (r & 7) (SWZ 0) or c ^ ((r >> 1) & 7) (SWZ 1, rows paired across the two bank halves)
+  static constexpr int SWZ = SWZ_;
+  __device__ static __forceinline__ int swz(int r) { return SWZ ? ((r >> 1) & 7) : (r & 7); }
+  static constexpr int BK = 64;
+  static constexpr int THREADS = WGM * WGN * WAVE;
+  static constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
+  static constexpr int FM = TM / 16, FN = TN / 16;    // MFMA tiles per wave
+  static constexpr int ROWS_PER_PASS = THREADS / 8;   // 8 threads (16 B each) per 128-byte row
+  static constexpr int AP = BM / ROWS_PER_PASS, BP = BN / ROWS_PER_PASS;
+  static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "tile rows must split evenly");
+  static_assert(TM % 16 == 0 && TN % 32 == 0, "wave tile must be a multiple of 16 x 32");
+};
 
+// Weight row feeding tile row r of column tile n_tile. SwiGLU tiles interleave gate and up rows:
+// wave column wn owns tile rows [wn*TN, (wn+1)*TN), the first half gate rows and the second half
+// the up rows of the same TN/2 output columns.
+template <class C>
 __device__ __forceinline__ const bf16* b_row_ptr(const GemmArgs& a, int n_tile, int r) {
   if (a.epi == EPI_SWIGLU) {
-    const int part = r / 64, within = r % 64;
-    const int c0 = n_tile * 64 + part * 32;
-    const int row = min((within < 32 ? c0 + within : c0 + within - 32), a.N - 1);
-    return (const bf16*)(within < 32 ? a.B[0] : a.B[1]) + (int64_t)row * a.K;
+    const int part = r / C::TN, within = r % C::TN, h = C::TN / 2;
+    const int c0 = n_tile * (C::BN / 2) + part * h;
+    const int row = min(within < h ? c0 + within : c0 + within - h, a.N - 1);
+    return (const bf16*)(within < h ? a.B[0] : a.B[1]) + (int64_t)row * a.K;
   }
-  const int col = min(n_tile * BN + r, a.N - 1);
+  const int col = min(n_tile * C::BN + r, a.N - 1);
   if (col < a.nb0) return (const bf16*)a.B[0] + (int64_t)col * a.K;
   if (col < a.nb1) return (const bf16*)a.B[1] + (int64_t)(col - a.nb0) * a.K;
   return (const bf16*)a.B[2] + (int64_t)(col - a.nb1) * a.K;
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
+template <class C>
+__device__ __forceinline__ int n_tiles_of(const GemmArgs& a) {
+  return a.epi == EPI_SWIGLU ? (a.N + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, AP = C::AP, BP = C::BP, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) bf16 As[2][BM * BK];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * BK];
   // logical tile: M fastest, so the M tiles that share a weight tile are neighbours (same XCD)
   const int m_tiles = (a.M + BM - 1) / BM;
-  const int n_tiles = a.epi == EPI_SWIGLU ? (a.N + 63) / 64 : (a.N + BN - 1) / BN;
+  const int n_tiles = n_tiles_of<C>(a);
   const int t = xcd_tile(blockIdx.x, m_tiles * n_tiles * a.splits);
   const int m_tile = t % m_tiles, n_tile = (t / m_tiles) % n_tiles, split = t / (m_tiles * n_tiles);
   const int m0 = m_tile * BM;
   const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
 
   const int kps = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
   const int k_begin = split * kps;
   const int k_end = min(a.K, k_begin + kps);
   const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
 
-  // per-thread load slots: tile row p*32 + tid/8, 16-byte chunk tid%8
-  const int lc = tid % 8;
-  const bf16* arow[4];
-  const bf16* brow[4];
+  // per-thread load slots: tile row p * ROWS_PER_PASS + tid / 8, 16-byte chunk tid % 8
+  const int lc = tid % 8, lr = tid / 8;
+  const bf16* arow[AP];
+  const bf16* brow[BP];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = p * 32 + tid / 8;
-    arow[p] = (const bf16*)a.A + (int64_t)min(m0 + r, a.M - 1) * a.lda;
-    brow[p] = b_row_ptr(a, n_tile, r);
-  }
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
-    const int k = k0 + lc * 8;
+  for (int p = 0; p < AP; ++p) arow[p] = (const bf16*)a.A + (int64_t)min(m0 + p * C::ROWS_PER_PASS + lr, a.M - 1) * a.lda;
+#pragma unroll
+  for (int p = 0; p < BP; ++p) brow[p] = b_row_ptr<C>(a, n_tile, p * C::ROWS_PER_PASS + lr);
+
+  uint4 ra0[AP], rb0[BP], ra1[AP], rb1[BP];
+  auto gload = [&](uint4* ra, uint4* rb, int step) {
+    const int k = k_begin + step * BK + lc * 8;
     const bool ok = k < k_end;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (ok) {
-        ra[p] = *reinterpret_cast<const uint4*>(arow[p] + k);
-        rb[p] = *reinterpret_cast<const uint4*>(brow[p] + k);
-      } else {
-        ra[p] = make_uint4(0, 0, 0, 0);
-        rb[p] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
+    for (int p = 0; p < AP; ++p) ra[p] = ok ? *reinterpret_cast<const uint4*>(arow[p] + k) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = p * 32 + tid / 8;
-      const int off = r * BK + ((lc ^ (r & 7)) * 8);
-      *reinterpret_cast<uint4*>(&As[buf][off]) = ra[p];
-      *reinterpret_cast<uint4*>(&Bs[buf][off]) = rb[p];
+    for (int p = 0; p < BP; ++p) rb[p] = ok ? *reinterpret_cast<const uint4*>(brow[p] + k) : make_uint4(0, 0, 0, 0);
+  };
+  auto sstore = [&](const uint4* ra, const uint4* rb, int buf) {
+#pragma unroll
+    for (int p = 0; p < AP; ++p) {
+      const int r = p * C::ROWS_PER_PASS + lr;
+      *reinterpret_cast<uint4*>(&As[buf][r * BK + ((lc ^ C::swz(r)) * 8)]) = ra[p];
+    }
+#pragma unroll
+    for (int p = 0; p < BP; ++p) {
+      const int r = p * C::ROWS_PER_PASS + lr;
+      *reinterpret_cast<uint4*>(&Bs[buf][r * BK + ((lc ^ C::swz(r)) * 8)]) = rb[p];
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) {
-    gload(k_begin);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) gload(k_begin + (it + 1) * BK);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       const int ch = kk * 4 + lane / 16;
-      bf16x8 af[4], bfr[4];
+      bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + (lane % 16);
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][r * BK + ((ch ^ (r & 7)) * 8)]);
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * C::TM + i * 16 + (lane % 16);
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][r * BK + ((ch ^ C::swz(r)) * 8)]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + j * 16 + (lane % 16);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][r * BK + ((ch ^ (r & 7)) * 8)]);
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * C::TN + j * 16 + (lane % 16);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][r * BK + ((ch ^ C::swz(r)) * 8)]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (it + 1 < nk) sstore(cur ^ 1);
+  };
+
+  if constexpr (C::PF == 1) {
+    if (nk > 0) {
+      gload(ra0, rb0, 0);
+      sstore(ra0, rb0, 0);
+    }
     __syncthreads();
+    for (int it = 0; it < nk; ++it) {
+      if (it + 1 < nk) gload(ra0, rb0, it + 1);
+      compute(it & 1);
+      if (it + 1 < nk) sstore(ra0, rb0, (it + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    // two K steps of loads in flight: step s lives in register set s % 2 from its load (two
+    // iterations ahead) until it is stored to LDS at the end of the preceding iteration
+    if (nk > 0) gload(ra0, rb0, 0);
+    if (nk > 1) gload(ra1, rb1, 1);
+    if (nk > 0) sstore(ra0, rb0, 0);
+    __syncthreads();
+    auto body = [&](int it, uint4* la, uint4* lb, const uint4* sa, const uint4* sb) {
+      if (it + 2 < nk) gload(la, lb, it + 2);
+      compute(it & 1);
+      if (it + 1 < nk) sstore(sa, sb, (it + 1) & 1);
+      __syncthreads();
+    };
+    for (int it = 0; it < nk; it += 2) {
+      body(it, ra0, rb0, ra1, rb1);
+      if (it + 1 < nk) body(it + 1, ra1, rb1, ra0, rb0);
+    }
   }
 
-  // epilogue: acc[i][j][r] = C[m0 + wm*64 + i*16 + 4*(lane/16) + r][tile col wn*64 + j*16 + lane%16]
+  // epilogue: acc[i][j][r] = C[m0 + wm*TM + i*16 + 4*(lane/16) + r][tile col wn*TN + j*16 + lane%16]
   const int lrow = 4 * (lane / 16), lcol = lane % 16;
   if (a.epi == EPI_SWIGLU) {
     bf16* act = (bf16*)a.act;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 64 + i * 16 + lrow + r;
+        const int m = m0 + wm * C::TM + i * 16 + lrow + r;
         if (m >= a.M) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n_tile * 64 + wn * 32 + j * 16 + lcol;
+        for (int j = 0; j < FN / 2; ++j) {
+          const int col = n_tile * (BN / 2) + wn * (C::TN / 2) + j * 16 + lcol;
           if (col >= a.N) continue;
-          const float g = acc[i][j][r], u = acc[i][j + 2][r];
+          const float g = acc[i][j][r], u = acc[i][j + FN / 2][r];
           act[(int64_t)m * a.ld_act + col] = (bf16)(g / (1.0f + expf(-g)) * u);
         }
       }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 64 + i * 16 + lrow + r;
+      const int m = m0 + wm * C::TM + i * 16 + lrow + r;
       if (m >= a.M) continue;
       int64_t orow = m, rrow = m;
       if (a.epi == EPI_RESID) {
@@ -151,8 +197,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
         rrow = a.resid_rows ? clampi(a.resid_rows[m], 0, a.L - 1) : m;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n_tile * BN + wn * 64 + j * 16 + lcol;
+      for (int j = 0; j < FN; ++j) {
+        const int col = n_tile * BN + wn * C::TN + j * 16 + lcol;
         if (col >= a.N) continue;
         const float v = acc[i][j][r];
         if (a.epi == EPI_F32)
@@ -164,6 +210,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
 }
+
+template <class C>
+hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
+  const int tiles = ((a.M + C::BM - 1) / C::BM) *
+                    (a.epi == EPI_SWIGLU ? (a.N + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN) * a.splits;
+  hipLaunchKernelGGL(gemm_bf16_kernel<C>, dim3(tiles), dim3(C::THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+using GemmSmall = TileCfg<128, 128, 2, 2, 2, 2>;  // 2 blocks per CU
+using GemmBig = TileCfg<256, 256, 4, 4, 1, 1>;    // 16 waves, 1 block per CU
 
 // ----------------------------------------------------------------------------- fp32 path
 __device__ __forceinline__ const float* b_row_ptr_f32(const GemmArgs& a, int col) {
@@ -221,20 +278,37 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   }
 }
 
-int gemm_splits(Dt dt, int M, int N, int K, int epi, int n_cu) {
-  if (dt != BF16 || epi != EPI_RESID) return 1;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  int s = 1;
-  while (s < 4 && tiles * s * 2 <= 2 * n_cu && K / (s * 2) >= 1024) s *= 2;
-  return s;
+GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, int n_cu) {
+  GemmPlan best{GEMM_SMALL, 1};
+  if (dt != BF16) return best;
+  // relative time of one configuration: rounds of resident blocks x work of one block /
+  // per-block rate (GemmBig runs one block per CU at 1.28x the per-CU rate of two GemmSmall
+  // blocks, measured on the projection shapes); ties go to fewer splits
+  double best_cost = 1e300;
+  const int cols = swiglu ? 2 * N : N;
+  for (int c = 0; c < 2; ++c) {
+    const int bm = c ? GemmBig::BM : GemmSmall::BM, bn = c ? GemmBig::BN : GemmSmall::BN;
+    const int per_cu = c ? 1 : 2;
+    const double rate = c ? 1.28 : 1.0;
+    const long tiles = (long)((M + bm - 1) / bm) * ((cols + bn - 1) / bn);
+    for (int sp = 1; sp <= (allow_split ? 4 : 1); ++sp) {
+      if (sp > 1 && K / sp < 512) break;
+      const long slots = (long)n_cu * per_cu;
+      const long rounds = (tiles * sp + slots - 1) / slots;
+      const double cost = rounds * (double)bm * bn * ((double)K / sp) * per_cu / rate * (1.0 + 0.02 * (sp - 1));
+      if (cost < best_cost * 0.999) {
+        best_cost = cost;
+        best = GemmPlan{c, sp};
+      }
+    }
+  }
+  return best;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.dt == BF16) {
-    const int ncols = a.epi == EPI_SWIGLU ? (a.N + 63) / 64 : (a.N + BN - 1) / BN;
-    dim3 grid(ncols * ((a.M + BM - 1) / BM) * a.splits);
-    hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, a);
+    return a.cfg == GEMM_BIG ? launch_gemm_cfg<GemmBig>(a, st) : launch_gemm_cfg<GemmSmall>(a, st);
   } else {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, 1);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, a);

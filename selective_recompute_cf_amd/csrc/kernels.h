@@ -37,6 +37,7 @@ struct QkvPost {
   const float* cos_t; const float* sin_t;
   void* q_out; void* k_cache; void* v_cache;
   float* dev; const void* k_ref;
+  int splits; int64_t split_stride;    // qkv holds `splits` partial sums, split_stride floats apart
 };
 hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st);
 hipError_t launch_iota(int* out, int n, int start, hipStream_t st);
@@ -47,6 +48,11 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, con
                                 const int* resid_rows, float* out, const int* out_rows, int L,
                                 hipStream_t st);
 // act[m][c] = silu(gu[m][c]) * gu[m][F + c]  (fp32 path)
+// Split-K reduction of the O projection fused with the residual and the MLP RMSNorm:
+// hs[m] = hidden[rows[m]] + sum_s part[s][m];  x[m] = RMSNorm(hs[m]) * g (model dtype).
+hipError_t launch_reduce_resid_norm(Dt dt, const float* part, int splits, int M, int d, const float* hidden,
+                                    const int* rows, int L, float* hs, const float* g, float eps, void* x,
+                                    hipStream_t st);
 hipError_t launch_swiglu(Dt dt, const float* gu, int M, int F, void* act, hipStream_t st);
 hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void* b, int64_t ldb,
                             float* dev, int n, int kvd, hipStream_t st);
@@ -55,6 +61,7 @@ hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void
 enum Epi { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PARTIAL = 3 };
 struct GemmArgs {
   Dt dt;
+  int cfg;                             // tile configuration (GEMM_SMALL / GEMM_BIG), from gemm_plan
   const void* A; int64_t lda;          // [M][K]
   const void* B[3]; int nb0, nb1;      // weights [n][K] (row stride K): cols [0,nb0) from B[0],
                                        // [nb0,nb1) from B[1], [nb1,N) from B[2]
@@ -66,7 +73,12 @@ struct GemmArgs {
   const float* resid; const int* resid_rows; float* out; const int* out_rows; int L;  // EPI_RESID
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
-int gemm_splits(Dt dt, int M, int N, int K, int epi, int n_cu);
+enum GemmCfgId { GEMM_SMALL = 0, GEMM_BIG = 1 };
+struct GemmPlan { int cfg; int splits; };
+// Tile configuration and split-K factor for an M x N x K product: the pair that minimises
+// (rounds of resident blocks) x (work per block) under a per-configuration throughput model.
+// Split-K is only considered when allow_split (the epilogue is linear in the accumulator).
+GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, int n_cu);
 
 // ----------------------------------------------------------------- attention (attn.hip)
 struct AttnArgs {

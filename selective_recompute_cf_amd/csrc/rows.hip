@@ -160,6 +160,13 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
   const bool devmode = p.dev != nullptr;
   const int pos = devmode ? j : clampi(p.rows[j], 0, p.L - 1);
   const float* src = p.qkv + (int64_t)j * p.ld;
+  const int splits = p.splits > 1 ? p.splits : 1;
+  const int64_t sst = p.split_stride;
+  auto at = [&](int c) {  // projection value: the sum of the split-K partials
+    float v = src[c];
+    for (int s2 = 1; s2 < splits; ++s2) v += src[s2 * sst + c];
+    return v;
+  };
   const float c = lane < half ? p.cos_t[(int64_t)pos * half + lane] : 0.f;
   const float s = lane < half ? p.sin_t[(int64_t)pos * half + lane] : 0.f;
   const int nq = devmode ? 0 : p.hq;
@@ -172,9 +179,9 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
     if (h < nq + nkv) {
       const bool isq = h < nq;
       const int hh = isq ? h : h - nq;
-      const float* x = src + (isq ? hh * hd : koff + hh * hd);
-      float x1 = lane < half ? x[lane] : 0.f;
-      float x2 = lane < half ? x[lane + half] : 0.f;
+      const int xo = isq ? hh * hd : koff + hh * hd;
+      float x1 = lane < half ? at(xo + lane) : 0.f;
+      float x2 = lane < half ? at(xo + lane + half) : 0.f;
       if (p.qk_norm) {
         const float ss = wave_sum(x1 * x1 + x2 * x2);
         const float inv = 1.0f / sqrtf(ss / (float)hd + p.eps);
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
     } else {
       const int hh = h - nq - nkv;
       T* vc = (T*)p.v_cache + (int64_t)pos * kvd + hh * hd;
-      for (int e = lane; e < hd; e += WAVE) vc[e] = from_f<T>(src[voff + hh * hd + e]);
+      for (int e = lane; e < hd; e += WAVE) vc[e] = from_f<T>(at(voff + hh * hd + e));
     }
   }
   if (devmode) {
@@ -270,6 +277,53 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, con
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(M), dim3(256), 0, st, part, splits, M, N, resid, resid_rows,
                      out, out_rows, L);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- O-proj reduce
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_resid_norm_kernel(const float* __restrict__ part, int splits, int M, int d,
+                                                                const float* __restrict__ hidden,
+                                                                const int* __restrict__ rows, int L,
+                                                                float* __restrict__ hs, const float* __restrict__ g,
+                                                                float eps, T* __restrict__ x) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int64_t r = rows ? clampi(rows[m], 0, L - 1) : m;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float v[8], t[8];
+    load8(hidden + r * d + c, v);
+    for (int s = 0; s < splits; ++s) {
+      load8(part + ((int64_t)s * M + m) * d + c, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += t[e];
+    }
+    store8(hs + (int64_t)m * d + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float v[8], gg[8];
+    load8(hs + (int64_t)m * d + c, v);
+    load8(g + c, gg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * gg[e];
+    store8(x + (int64_t)m * d + c, v);
+  }
+}
+hipError_t launch_reduce_resid_norm(Dt dt, const float* part, int splits, int M, int d, const float* hidden,
+                                    const int* rows, int L, float* hs, const float* g, float eps, void* x,
+                                    hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL(reduce_resid_norm_kernel<bf16>, dim3(M), dim3(256), 0, st, part, splits, M, d, hidden, rows, L,
+                       hs, g, eps, (bf16*)x);
+  else
+    hipLaunchKernelGGL(reduce_resid_norm_kernel<float>, dim3(M), dim3(256), 0, st, part, splits, M, d, hidden, rows,
+                       L, hs, g, eps, (float*)x);
   return hipGetLastError();
 }
 
