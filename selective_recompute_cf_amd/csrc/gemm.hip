@@ -2,12 +2,14 @@
 // [out][in]). CacheBlend ("Selective Recompute Without Skipping"): the Q/K/V, O and MLP
 // projections run on the gathered selected rows only.
 //
-// bf16 path: MFMA v_mfma_f32_16x16x32_bf16 (gfx950), fp32 accumulation. Block tile 128x128x64,
-// 256 threads = 2x2 waves of 64x64 (4x4 MFMA tiles each). Global -> registers -> LDS with a
-// 16-byte-chunk XOR swizzle (chunk c of row r lives at c ^ (r & 7)), double-buffered LDS, one
-// barrier per K step. Epilogues: fp32 store, residual add with row gather/scatter, fused SwiGLU
-// (the block's 128 B rows are 64 gate + 64 up rows of the same 64 output columns, arranged so
-// every lane holds matching gate and up values), and split-K partials.
+// bf16 path: MFMA v_mfma_f32_16x16x32_bf16 (gfx950), fp32 accumulation, BK = 64. The main kernel
+// (gemm_bf16_dtl) streams A and B tiles straight from global memory into a ring of LDS stages
+// (direct-to-LDS loads, no register staging), block tile 128x256 with 8 waves of 64x64; the
+// register-staged kernel (gemm_bf16_kernel, 128x128) covers K % 64 != 0. Both keep tiles in LDS
+// with a 16-byte-chunk XOR swizzle (chunk c of row r lives at c ^ (r & 7)). Epilogues: fp32
+// store, residual add with row gather/scatter, fused SwiGLU (a block's B rows are gate and up
+// rows of the same output columns, arranged so every lane holds matching gate and up values),
+// and split-K partials.
 //
 // fp32 path: a plain LDS-tiled FMA GEMM (64x64x16), used for fp32 models.
 #include "common.h"
@@ -56,116 +58,11 @@ __device__ __forceinline__ int n_tiles_of(const GemmArgs& a) {
   return a.epi == EPI_SWIGLU ? (a.N + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
 }
 
+// Epilogue: acc[i][j][r] = C[m0 + wm*TM + i*16 + 4*(lane/16) + r][tile col wn*TN + j*16 + lane%16]
 template <class C>
-__global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, AP = C::AP, BP = C::BP, FM = C::FM, FN = C::FN;
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * BK];
-  // logical tile: M fastest, so the M tiles that share a weight tile are neighbours (same XCD)
-  const int m_tiles = (a.M + BM - 1) / BM;
-  const int n_tiles = n_tiles_of<C>(a);
-  const int t = xcd_tile(blockIdx.x, m_tiles * n_tiles * a.splits);
-  const int m_tile = t % m_tiles, n_tile = (t / m_tiles) % n_tiles, split = t / (m_tiles * n_tiles);
-  const int m0 = m_tile * BM;
-  const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
-
-  const int kps = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
-  const int k_begin = split * kps;
-  const int k_end = min(a.K, k_begin + kps);
-  const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-
-  // per-thread load slots: tile row p * ROWS_PER_PASS + tid / 8, 16-byte chunk tid % 8
-  const int lc = tid % 8, lr = tid / 8;
-  const bf16* arow[AP];
-  const bf16* brow[BP];
-#pragma unroll
-  for (int p = 0; p < AP; ++p) arow[p] = (const bf16*)a.A + (int64_t)min(m0 + p * C::ROWS_PER_PASS + lr, a.M - 1) * a.lda;
-#pragma unroll
-  for (int p = 0; p < BP; ++p) brow[p] = b_row_ptr<C>(a, n_tile, p * C::ROWS_PER_PASS + lr);
-
-  uint4 ra0[AP], rb0[BP], ra1[AP], rb1[BP];
-  auto gload = [&](uint4* ra, uint4* rb, int step) {
-    const int k = k_begin + step * BK + lc * 8;
-    const bool ok = k < k_end;
-#pragma unroll
-    for (int p = 0; p < AP; ++p) ra[p] = ok ? *reinterpret_cast<const uint4*>(arow[p] + k) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int p = 0; p < BP; ++p) rb[p] = ok ? *reinterpret_cast<const uint4*>(brow[p] + k) : make_uint4(0, 0, 0, 0);
-  };
-  auto sstore = [&](const uint4* ra, const uint4* rb, int buf) {
-#pragma unroll
-    for (int p = 0; p < AP; ++p) {
-      const int r = p * C::ROWS_PER_PASS + lr;
-      *reinterpret_cast<uint4*>(&As[buf][r * BK + ((lc ^ C::swz(r)) * 8)]) = ra[p];
-    }
-#pragma unroll
-    for (int p = 0; p < BP; ++p) {
-      const int r = p * C::ROWS_PER_PASS + lr;
-      *reinterpret_cast<uint4*>(&Bs[buf][r * BK + ((lc ^ C::swz(r)) * 8)]) = rb[p];
-    }
-  };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int cur) {
-#pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int ch = kk * 4 + lane / 16;
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * C::TM + i * 16 + (lane % 16);
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][r * BK + ((ch ^ C::swz(r)) * 8)]);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * C::TN + j * 16 + (lane % 16);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][r * BK + ((ch ^ C::swz(r)) * 8)]);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  if constexpr (C::PF == 1) {
-    if (nk > 0) {
-      gload(ra0, rb0, 0);
-      sstore(ra0, rb0, 0);
-    }
-    __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-      if (it + 1 < nk) gload(ra0, rb0, it + 1);
-      compute(it & 1);
-      if (it + 1 < nk) sstore(ra0, rb0, (it + 1) & 1);
-      __syncthreads();
-    }
-  } else {
-    // two K steps of loads in flight: step s lives in register set s % 2 from its load (two
-    // iterations ahead) until it is stored to LDS at the end of the preceding iteration
-    if (nk > 0) gload(ra0, rb0, 0);
-    if (nk > 1) gload(ra1, rb1, 1);
-    if (nk > 0) sstore(ra0, rb0, 0);
-    __syncthreads();
-    auto body = [&](int it, uint4* la, uint4* lb, const uint4* sa, const uint4* sb) {
-      if (it + 2 < nk) gload(la, lb, it + 2);
-      compute(it & 1);
-      if (it + 1 < nk) sstore(sa, sb, (it + 1) & 1);
-      __syncthreads();
-    };
-    for (int it = 0; it < nk; it += 2) {
-      body(it, ra0, rb0, ra1, rb1);
-      if (it + 1 < nk) body(it + 1, ra1, rb1, ra0, rb0);
-    }
-  }
-
-  // epilogue: acc[i][j][r] = C[m0 + wm*TM + i*16 + 4*(lane/16) + r][tile col wn*TN + j*16 + lane%16]
+__device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[C::FM][C::FN], int m0, int n_tile, int split,
+                                         int wm, int wn, int lane) {
+  constexpr int BN = C::BN, FM = C::FM, FN = C::FN;
   const int lrow = 4 * (lane / 16), lcol = lane % 16;
   if (a.epi == EPI_SWIGLU) {
     bf16* act = (bf16*)a.act;
@@ -212,6 +109,270 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_kernel(GemmArgs
 }
 
 template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, AP = C::AP, BP = C::BP, FM = C::FM, FN = C::FN;
+  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * BK];
+  // logical tile: M fastest, so the M tiles that share a weight tile are neighbours (same XCD)
+  const int m_tiles = (a.M + BM - 1) / BM;
+  const int n_tiles = n_tiles_of<C>(a);
+  const int t = xcd_tile(blockIdx.x, m_tiles * n_tiles * a.splits);
+  const int m_tile = t % m_tiles, n_tile = (t / m_tiles) % n_tiles, split = t / (m_tiles * n_tiles);
+  const int m0 = m_tile * BM;
+  const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+
+  const int kps = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
+  const int k_begin = split * kps;
+  const int k_end = min(a.K, k_begin + kps);
+  const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
+
+  // per-thread load slots: tile row p * ROWS_PER_PASS + tid / 8, 16-byte chunk tid % 8
+  const int lc = tid % 8, lr = tid / 8;
+  const bf16* arow[AP];
+  const bf16* brow[BP];
+#pragma unroll
+  for (int p = 0; p < AP; ++p) arow[p] = (const bf16*)a.A + (int64_t)min(m0 + p * C::ROWS_PER_PASS + lr, a.M - 1) * a.lda;
+#pragma unroll
+  for (int p = 0; p < BP; ++p) brow[p] = b_row_ptr<C>(a, n_tile, p * C::ROWS_PER_PASS + lr);
+
+  // Global loads are unconditional (a per-lane predicate would turn each into an exec-masked
+  // branch, and the wait-count insertion then drains every load before the next LDS store,
+  // collapsing the prefetch depth): the column is clamped into the row (K >= 8, K % 8 == 0) and
+  // chunks past the step's K range are zeroed when they are stored to LDS. A register set is
+  // one vector value (AP + BP 16-byte chunks), passed by value so it never leaves registers.
+  typedef uint32_t RVec __attribute__((ext_vector_type(4 * (AP + BP))));
+  auto gload = [&](int step) __attribute__((always_inline)) {
+    const int k = min(k_begin + step * BK + lc * 8, a.K - 8);
+    RVec r;
+#pragma unroll
+    for (int p = 0; p < AP + BP; ++p) {
+      const uint4 x = *reinterpret_cast<const uint4*>((p < AP ? arow[p] : brow[p - AP]) + k);
+      r[4 * p] = x.x, r[4 * p + 1] = x.y, r[4 * p + 2] = x.z, r[4 * p + 3] = x.w;
+    }
+    return r;
+  };
+  auto sstore = [&](RVec r, int buf, int step) __attribute__((always_inline)) {
+    const bool full = k_begin + (step + 1) * BK <= k_end;  // uniform: the whole step is in range
+    const bool ok = full || k_begin + step * BK + lc * 8 < k_end;
+#pragma unroll
+    for (int p = 0; p < AP + BP; ++p) {
+      const int row = (p < AP ? p : p - AP) * C::ROWS_PER_PASS + lr;
+      bf16* dst = (p < AP ? As[buf] : Bs[buf]) + row * BK + ((lc ^ C::swz(row)) * 8);
+      *reinterpret_cast<uint4*>(dst) = ok ? make_uint4(r[4 * p], r[4 * p + 1], r[4 * p + 2], r[4 * p + 3])
+                                          : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int cur) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      const int ch = kk * 4 + lane / 16;
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * C::TM + i * 16 + (lane % 16);
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[cur][r * BK + ((ch ^ C::swz(r)) * 8)]);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * C::TN + j * 16 + (lane % 16);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][r * BK + ((ch ^ C::swz(r)) * 8)]);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // The loads inside the loop are branch-free too (a branch around them makes the wait counts
+  // conservative at the join): past the last step they re-load the last step, which is never
+  // stored again.
+  const int last = max(nk - 1, 0);
+  if constexpr (C::PF == 1) {
+    RVec r0 = gload(0);
+    sstore(r0, 0, 0);
+    __syncthreads();
+    for (int it = 0; it < nk; ++it) {
+      r0 = gload(min(it + 1, last));
+      compute(it & 1);
+      if (it + 1 < nk) sstore(r0, (it + 1) & 1, it + 1);
+      __syncthreads();
+    }
+  } else {
+    // two K steps of loads in flight: step s is loaded into set s % 2 two steps ahead and stored
+    // to LDS buffer s % 2 at the end of step s - 1
+    RVec r0 = gload(0), r1 = gload(min(1, last));
+    sstore(r0, 0, 0);
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < nk; it += 2) {
+      r0 = gload(min(it + 2, last));
+      compute(0);
+      sstore(r1, 1, it + 1);
+      __syncthreads();
+      r1 = gload(min(it + 3, last));
+      compute(1);
+      if (it + 2 < nk) sstore(r0, 0, it + 2);
+      __syncthreads();
+    }
+    if (it < nk) compute(0);  // odd step count: the last step sits in buffer 0
+  }
+
+  epilogue<C>(a, acc, m0, n_tile, split, wm, wn, lane);
+}
+
+// ----------------------------------------------------------------------------- direct-to-LDS
+// Ring of S LDS stages filled by direct global->LDS 16-byte loads (global_load_lds_dwordx4: lane
+// l of a wave writes bytes [16 l, 16 l + 16) after the wave-uniform LDS base), so the K steps in
+// flight cost no registers and no LDS store instructions. One wave instruction fills 8 tile rows
+// (8 lanes x 16 B per 128-byte row); the XOR swizzle is applied on the global side: the lane that
+// lands in chunk slot c' of row r fetches global chunk c' ^ (r & 7). Requires K % 64 == 0.
+// Per K step s:
+//   read slice 1 of step s | load step s + S - 1 into the stage step s - 1 used | MFMAs slice 0
+//   wait for this wave's loads of step s + 1 and its own LDS reads | barrier
+//   read slice 0 of step s + 1 | MFMAs slice 1
+// The barrier publishes step s + 1 (every wave waited for its own loads of it) and retires all
+// reads of step s's stage before any wave issues the load that overwrites it (at step s + 1).
+template <int BM_, int BN_, int WGM_, int WGN_, int S_, int MINB_>
+struct DtlCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, S = S_, MINB = MINB_, SWZ = 0, BK = 64;
+  static constexpr int W = WGM * WGN, THREADS = W * WAVE;
+  static constexpr int TM = BM / WGM, TN = BN / WGN, FM = TM / 16, FN = TN / 16;
+  static constexpr int NL = (BM + BN) / (8 * W);  // load instructions per wave per K step
+  static constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
+  static_assert((BM + BN) % (8 * W) == 0 && BM % 8 == 0, "8-row load groups must split evenly");
+  static_assert((S - 2) * NL <= 63, "in-flight loads must fit the vmcnt counter");
+  __device__ static __forceinline__ int swz(int r) { return r & 7; }
+};
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+#define CF_WAITCNT(vm, lgkm) ((((vm) & 15) | (((vm) >> 4) << 14)) | 0x70 | (((lgkm) & 15) << 8))
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a) {
+  constexpr int BM = C::BM, BK = C::BK, FM = C::FM, FN = C::FN, S = C::S, NL = C::NL, W = C::W;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[S * C::STAGE];  // stage: BM A rows, then BN B rows
+  const int m_tiles = (a.M + BM - 1) / BM;
+  const int n_tiles = n_tiles_of<C>(a);
+  const int t = xcd_tile(blockIdx.x, m_tiles * n_tiles * a.splits);
+  const int m_tile = t % m_tiles, n_tile = (t / m_tiles) % n_tiles, split = t / (m_tiles * n_tiles);
+  const int m0 = m_tile * BM;
+  const int tid = threadIdx.x, lane = tid % WAVE, wave = tid / WAVE;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+
+  const int kps = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
+  const int k_begin = split * kps;
+  const int k_end = min(a.K, k_begin + kps);
+  const int nk = k_end > k_begin ? (k_end - k_begin) / BK : 0;
+
+  // load q of this wave covers combined tile rows [(q*W + wave)*8, +8): A rows first, then B rows
+  const bf16* src[NL];
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int row = (q * W + wave) * 8 + lane / 8;
+    const int r = row < BM ? row : row - BM;
+    const int c = (lane % 8) ^ C::swz(r);
+    const bf16* base = row < BM ? (const bf16*)a.A + (int64_t)min(m0 + r, a.M - 1) * a.lda : b_row_ptr<C>(a, n_tile, r);
+    src[q] = base + k_begin + c * 8;
+  }
+  // The load is issued from inline assembly: with the compiler builtin, the wait-count pass
+  // treats the pending LDS write as unordered and drains every outstanding LDS read before the
+  // next MFMA, which serialises the fragment reads with the matrix cores. The pass does not see
+  // these loads, so the waits for them are explicit (CF_WAITCNT below); its own vmcnt waits stay
+  // correct because vector-memory loads retire in order.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    const int stage = step % S;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 2u * (uint32_t)(stage * C::STAGE + (q * W + wave) * 8 * BK));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[q] + step * BK), "s"(dst) : "memory", "m0");
+    }
+  };
+
+  typedef uint32_t FVec __attribute__((ext_vector_type(4 * (FM + FN))));
+  typedef uint32_t U4 __attribute__((ext_vector_type(4)));
+  auto fread = [&](int stage, int kk) __attribute__((always_inline)) {
+    const int ch = kk * 4 + lane / 16;
+    const bf16* st = smem + stage * C::STAGE;
+    FVec f;
+#pragma unroll
+    for (int q = 0; q < FM + FN; ++q) {
+      const int r = q < FM ? wm * C::TM + q * 16 + (lane % 16) : BM + wn * C::TN + (q - FM) * 16 + (lane % 16);
+      const int rr = q < FM ? r : r - BM;
+      const U4 x = *reinterpret_cast<const U4*>(st + r * BK + ((ch ^ C::swz(rr)) * 8));
+      f[4 * q] = x[0], f[4 * q + 1] = x[1], f[4 * q + 2] = x[2], f[4 * q + 3] = x[3];
+    }
+    return f;
+  };
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fmma = [&](FVec f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const U4 av = {f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
+        const U4 bv = {f[4 * (FM + j)], f[4 * (FM + j) + 1], f[4 * (FM + j) + 2], f[4 * (FM + j) + 3]};
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                           __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
+      }
+  };
+  // a raw barrier: no fence, so the compiler adds no drain of the in-flight LDS loads; the
+  // empty asm statements keep LDS accesses from moving across it
+  auto barrier = []() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (nk > 0) {
+    const int last = nk - 1;
+    // past the last step the loads repeat the last step into a stage nobody reads again, which
+    // keeps the per-step load count (and so the wait counts) uniform
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) issue(min(p, last));
+    __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 15));
+    barrier();
+    FVec f0 = fread(0, 0), f1;
+    for (int s = 0; s < nk; ++s) {
+      f1 = fread(s % S, 1);
+      issue(min(s + S - 1, last));
+      __builtin_amdgcn_sched_barrier(0);
+      fmma(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 0));
+      barrier();
+      f0 = fread((s + 1) % S, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      fmma(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(CF_WAITCNT(0, 0));  // drain the trailing repeat loads
+  }
+  epilogue<C>(a, acc, m0, n_tile, split, wm, wn, lane);
+}
+
+template <class C>
+hipError_t launch_gemm_dtl(const GemmArgs& a, hipStream_t st) {
+  const int tiles = ((a.M + C::BM - 1) / C::BM) *
+                    (a.epi == EPI_SWIGLU ? (a.N + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN) * a.splits;
+  hipLaunchKernelGGL(gemm_bf16_dtl<C>, dim3(tiles), dim3(C::THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class C>
 hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
   const int tiles = ((a.M + C::BM - 1) / C::BM) *
                     (a.epi == EPI_SWIGLU ? (a.N + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN) * a.splits;
@@ -219,8 +380,8 @@ hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-using GemmSmall = TileCfg<128, 128, 2, 2, 2, 2>;  // 2 blocks per CU
-using GemmBig = TileCfg<256, 256, 4, 4, 1, 1>;    // 16 waves, 1 block per CU
+using GemmSmall = TileCfg<128, 128, 2, 2, 2, 2>;  // register-staged, 2 blocks per CU (K % 64 != 0)
+using GemmDtl = DtlCfg<128, 256, 2, 4, 3, 1>;     // 8 waves of 64x64, 3 x 48 KB LDS stages, 1 block per CU
 
 // ----------------------------------------------------------------------------- fp32 path
 __device__ __forceinline__ const float* b_row_ptr_f32(const GemmArgs& a, int col) {
@@ -280,26 +441,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, int n_cu) {
   GemmPlan best{GEMM_SMALL, 1};
-  if (dt != BF16) return best;
-  // relative time of one configuration: rounds of resident blocks x work of one block /
-  // per-block rate (GemmBig runs one block per CU at 1.28x the per-CU rate of two GemmSmall
-  // blocks, measured on the projection shapes); ties go to fewer splits
-  double best_cost = 1e300;
+  if (dt != BF16 || M <= 0 || N <= 0) return best;
+  // The direct-to-LDS kernel needs K % 64 == 0 (whole 64-wide K steps per split); otherwise the
+  // register-staged kernel. Split-K factor: fewest rounds of resident blocks x K per split, with
+  // a 2 % charge per extra split for the partial sums, K per split >= 512, at most 4 splits.
+  const bool dtl = K % 64 == 0;
+  best.cfg = dtl ? GEMM_DTL : GEMM_SMALL;
+  const int bm = dtl ? GemmDtl::BM : GemmSmall::BM, bn = dtl ? GemmDtl::BN : GemmSmall::BN;
+  const long slots = (long)n_cu * (dtl ? 1 : 2);
   const int cols = swiglu ? 2 * N : N;
-  for (int c = 0; c < 2; ++c) {
-    const int bm = c ? GemmBig::BM : GemmSmall::BM, bn = c ? GemmBig::BN : GemmSmall::BN;
-    const int per_cu = c ? 1 : 2;
-    const double rate = c ? 1.28 : 1.0;
-    const long tiles = (long)((M + bm - 1) / bm) * ((cols + bn - 1) / bn);
-    for (int sp = 1; sp <= (allow_split ? 4 : 1); ++sp) {
-      if (sp > 1 && K / sp < 512) break;
-      const long slots = (long)n_cu * per_cu;
-      const long rounds = (tiles * sp + slots - 1) / slots;
-      const double cost = rounds * (double)bm * bn * ((double)K / sp) * per_cu / rate * (1.0 + 0.02 * (sp - 1));
-      if (cost < best_cost * 0.999) {
-        best_cost = cost;
-        best = GemmPlan{c, sp};
-      }
+  const long tiles = (long)((M + bm - 1) / bm) * ((cols + bn - 1) / bn);
+  double best_cost = 1e300;
+  for (int sp = 1; sp <= (allow_split ? 4 : 1); ++sp) {
+    if (sp > 1 && K / sp < 512) break;
+    const long rounds = (tiles * sp + slots - 1) / slots;
+    const double cost = rounds * ((double)K / sp) * (1.0 + 0.02 * (sp - 1));
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best.splits = sp;
     }
   }
   return best;
@@ -308,11 +467,14 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.dt == BF16) {
-    return a.cfg == GEMM_BIG ? launch_gemm_cfg<GemmBig>(a, st) : launch_gemm_cfg<GemmSmall>(a, st);
-  } else {
-    dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, 1);
-    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, a);
+    if (a.cfg == GEMM_DTL) {
+      if (a.K % 64 != 0 || a.K < 64) return hipErrorInvalidValue;
+      return launch_gemm_dtl<GemmDtl>(a, st);
+    }
+    return launch_gemm_cfg<GemmSmall>(a, st);
   }
+  dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, 1);
+  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
