@@ -44,6 +44,9 @@ def main():
     ap.add_argument("--store-cache", default=None,
                     help="load the chunk store from this file if it exists, else build it and save it there")
     ap.add_argument("--prepare-only", action="store_true", help="build (and save) the chunk store, then exit")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (the reference for the FETCH_SIZE / "
+                         "WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path has no multi-GPU mode",
@@ -60,6 +63,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes 3 times")
+        return
     w = synth.WORKLOADS[args.workload]
     cfg = w.model
     N, U, L = w.n_ctx, w.n_query, w.n_total
@@ -167,9 +180,11 @@ def main():
     g_flops = rl.gemm_flops(work) * P
     g_ach = g_flops / (g_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(g_ach, 2), "peak": rl.BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g_ach / rl.BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "gemm_bf16_kernel",
+                "frac": round(g_ach / rl.BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_bf16_dtl (projection GEMMs, all block heights)",
                 "avg_launch_us": round(g_ms / g_launch * 1e3, 2),
                 "flops_per_launch": g_flops / g_launch, "launches_per_step": g_launch / P}
+    roofline.update(gemm_traffic(rl.gemm_bytes(work) / (g_launch / P)))
     log(f"[bench] gemm: {g_ach:.1f} TFLOP/s ({roofline['frac'] * 100:.1f}% of bf16 peak), "
         f"{roofline['avg_launch_us']} us/launch")
 
@@ -215,6 +230,26 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def gemm_traffic(alg_bytes_per_launch):
+    """HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE counter summary, if the
+    GEMM sources have not changed since the counters were taken (else traffic stays null)."""
+    from selective_recompute_cf_amd import profiles
+    path = os.path.join(ROOT, "profiles", "gemm_bf16_dtl_llama3-8b_hbm_traffic.json")
+    out = {"traffic_unit": "bytes per launch (HBM fetch + write, rocprofv3 counters)",
+           "algorithmic_bytes_per_launch": round(alg_bytes_per_launch)}
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except OSError:
+        out["traffic_note"] = "no counter summary"
+        return out
+    if t.get("source_sha256") != profiles.sources_sha256():
+        out["traffic_note"] = "GEMM sources changed since the counters were taken"
+        return out
+    out["traffic"] = round(t["traffic_bytes_per_launch"])
+    return out
 
 
 def cpu_baseline(w, k):

@@ -4,7 +4,7 @@
 //
 // bf16 path: MFMA v_mfma_f32_16x16x32_bf16 (gfx950), fp32 accumulation, BK = 64. The main kernel
 // (gemm_bf16_dtl) streams A and B tiles straight from global memory into a ring of LDS stages
-// (direct-to-LDS loads, no register staging), block tile 128x256 with 8 waves of 64x64; the
+// (direct-to-LDS loads, no register staging), block tiles {128, 96, 64} x 256 with 8 waves; the
 // register-staged kernel (gemm_bf16_kernel, 128x128) covers K % 64 != 0. Both keep tiles in LDS
 // with a 16-byte-chunk XOR swizzle (chunk c of row r lives at c ^ (r & 7)). Epilogues: fp32
 // store, residual add with row gather/scatter, fused SwiGLU (a block's B rows are gate and up
@@ -246,9 +246,10 @@ struct DtlCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, S = S_, MINB = MINB_, SWZ = 0, BK = 64;
   static constexpr int W = WGM * WGN, THREADS = W * WAVE;
   static constexpr int TM = BM / WGM, TN = BN / WGN, FM = TM / 16, FN = TN / 16;
-  static constexpr int NL = (BM + BN) / (8 * W);  // load instructions per wave per K step
+  static constexpr int G = (BM + BN) / 8;         // 8-row load groups per K step
+  static constexpr int NL = (G + W - 1) / W;      // load instructions per wave per K step
   static constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
-  static_assert((BM + BN) % (8 * W) == 0 && BM % 8 == 0, "8-row load groups must split evenly");
+  static_assert(BM % 8 == 0 && BN % 8 == 0 && NL * W - G <= W, "8-row load groups");
   static_assert((S - 2) * NL <= 63, "in-flight loads must fit the vmcnt counter");
   __device__ static __forceinline__ int swz(int r) { return r & 7; }
 };
@@ -273,11 +274,15 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
   const int k_end = min(a.K, k_begin + kps);
   const int nk = k_end > k_begin ? (k_end - k_begin) / BK : 0;
 
-  // load q of this wave covers combined tile rows [(q*W + wave)*8, +8): A rows first, then B rows
+  // load q of this wave covers combined tile rows [g*8, g*8 + 8), g = q*W + wave (A rows first,
+  // then B rows). When the groups do not split evenly over the waves, a wave's surplus slot
+  // repeats its previous group (same bytes to the same place), so every wave issues NL loads per
+  // step and the wait counts hold for all of them.
+  auto group = [&](int q) { const int g = q * W + wave; return g < C::G ? g : g - W; };
   const bf16* src[NL];
 #pragma unroll
   for (int q = 0; q < NL; ++q) {
-    const int row = (q * W + wave) * 8 + lane / 8;
+    const int row = group(q) * 8 + lane / 8;
     const int r = row < BM ? row : row - BM;
     const int c = (lane % 8) ^ C::swz(r);
     const bf16* base = row < BM ? (const bf16*)a.A + (int64_t)min(m0 + r, a.M - 1) * a.lda : b_row_ptr<C>(a, n_tile, r);
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
     const int stage = step % S;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 2u * (uint32_t)(stage * C::STAGE + (q * W + wave) * 8 * BK));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 2u * (uint32_t)(stage * C::STAGE + group(q) * 8 * BK));
       asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[q] + step * BK), "s"(dst) : "memory", "m0");
     }
   };
@@ -381,7 +386,10 @@ hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
 }
 
 using GemmSmall = TileCfg<128, 128, 2, 2, 2, 2>;  // register-staged, 2 blocks per CU (K % 64 != 0)
-using GemmDtl = DtlCfg<128, 256, 2, 4, 3, 1>;     // 8 waves of 64x64, 3 x 48 KB LDS stages, 1 block per CU
+// direct-to-LDS block heights for BN = 256, one block per CU, 8 waves each
+using GemmDtl128 = DtlCfg<128, 256, 2, 4, 3, 1>;  // waves 64x64, 3 x 48 KB stages
+using GemmDtl96 = DtlCfg<96, 256, 2, 4, 3, 1>;    // waves 48x64, 3 x 44 KB stages
+using GemmDtl64 = DtlCfg<64, 256, 1, 8, 4, 1>;    // waves 64x32, 4 x 40 KB stages
 
 // ----------------------------------------------------------------------------- fp32 path
 __device__ __forceinline__ const float* b_row_ptr_f32(const GemmArgs& a, int col) {
@@ -442,23 +450,36 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, int n_cu) {
   GemmPlan best{GEMM_SMALL, 1};
   if (dt != BF16 || M <= 0 || N <= 0) return best;
-  // The direct-to-LDS kernel needs K % 64 == 0 (whole 64-wide K steps per split); otherwise the
-  // register-staged kernel. Split-K factor: fewest rounds of resident blocks x K per split, with
-  // a 2 % charge per extra split for the partial sums, K per split >= 512, at most 4 splits.
+  // The direct-to-LDS kernels need K % 64 == 0 (whole 64-wide K steps per split); otherwise the
+  // register-staged kernel. Among the block heights and split-K factors (K per split >= 512, at
+  // most 4), pick the least
+  //   rounds of resident blocks x (block height x K per split) / per-CU rate
+  //   + the extra fp32 partial sums written and read back, (splits - 1) x M x N x 8 bytes,
+  // with per-CU rates relative to the 128-row block as measured on full rounds of the
+  // projection shapes (the lower blocks re-read the weight tiles more often). One cost unit is
+  // one 128-row block advancing one K column (about 0.12 ns on a full round); at about 5 TB/s
+  // the 8 bytes of one partial element (written once, read once) cost 0.0131 units.
+  struct Opt { int cfg, bm, per_cu; double rate; };
+  const Opt dtl_opts[3] = {{GEMM_DTL128, 128, 1, 1.0}, {GEMM_DTL96, 96, 1, 0.86}, {GEMM_DTL64, 64, 1, 0.75}};
+  const Opt small_opt[1] = {{GEMM_SMALL, 128, 2, 0.85}};
   const bool dtl = K % 64 == 0;
-  best.cfg = dtl ? GEMM_DTL : GEMM_SMALL;
-  const int bm = dtl ? GemmDtl::BM : GemmSmall::BM, bn = dtl ? GemmDtl::BN : GemmSmall::BN;
-  const long slots = (long)n_cu * (dtl ? 1 : 2);
+  const Opt* opts = dtl ? dtl_opts : small_opt;
+  const int n_opts = dtl ? 3 : 1;
+  const int bn = dtl ? 256 : 128;
   const int cols = swiglu ? 2 * N : N;
-  const long tiles = (long)((M + bm - 1) / bm) * ((cols + bn - 1) / bn);
   double best_cost = 1e300;
-  for (int sp = 1; sp <= (allow_split ? 4 : 1); ++sp) {
-    if (sp > 1 && K / sp < 512) break;
-    const long rounds = (tiles * sp + slots - 1) / slots;
-    const double cost = rounds * ((double)K / sp) * (1.0 + 0.02 * (sp - 1));
-    if (cost < best_cost * 0.999) {
-      best_cost = cost;
-      best.splits = sp;
+  for (int o = 0; o < n_opts; ++o) {
+    const long tiles = (long)((M + opts[o].bm - 1) / opts[o].bm) * ((cols + bn - 1) / bn);
+    const long slots = (long)n_cu * opts[o].per_cu;
+    for (int sp = 1; sp <= (allow_split ? 4 : 1); ++sp) {
+      if (sp > 1 && K / sp < 512) break;
+      const long rounds = (tiles * sp + slots - 1) / slots;
+      const double cost = rounds * opts[o].per_cu * (double)opts[o].bm * ((double)K / sp) / opts[o].rate +
+                          (sp - 1) * (double)M * N * 0.0131;
+      if (cost < best_cost * 0.999) {
+        best_cost = cost;
+        best = GemmPlan{opts[o].cfg, sp};
+      }
     }
   }
   return best;
@@ -467,11 +488,13 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   if (a.dt == BF16) {
-    if (a.cfg == GEMM_DTL) {
-      if (a.K % 64 != 0 || a.K < 64) return hipErrorInvalidValue;
-      return launch_gemm_dtl<GemmDtl>(a, st);
+    if (a.cfg != GEMM_SMALL && (a.K % 64 != 0 || a.K < 64)) return hipErrorInvalidValue;
+    switch (a.cfg) {
+      case GEMM_DTL128: return launch_gemm_dtl<GemmDtl128>(a, st);
+      case GEMM_DTL96: return launch_gemm_dtl<GemmDtl96>(a, st);
+      case GEMM_DTL64: return launch_gemm_dtl<GemmDtl64>(a, st);
+      default: return launch_gemm_cfg<GemmSmall>(a, st);
     }
-    return launch_gemm_cfg<GemmSmall>(a, st);
   }
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64, 1);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, st, a);

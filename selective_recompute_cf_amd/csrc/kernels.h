@@ -61,7 +61,7 @@ hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void
 enum Epi { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PARTIAL = 3 };
 struct GemmArgs {
   Dt dt;
-  int cfg;                             // kernel / tile configuration (GEMM_SMALL / GEMM_DTL), from gemm_plan
+  int cfg;                             // kernel / tile configuration (GemmCfgId), from gemm_plan
   const void* A; int64_t lda;          // [M][K]
   const void* B[3]; int nb0, nb1;      // weights [n][K] (row stride K): cols [0,nb0) from B[0],
                                        // [nb0,nb1) from B[1], [nb1,N) from B[2]
@@ -73,11 +73,12 @@ struct GemmArgs {
   const float* resid; const int* resid_rows; float* out; const int* out_rows; int L;  // EPI_RESID
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
-enum GemmCfgId { GEMM_SMALL = 0, GEMM_DTL = 1 };
+enum GemmCfgId { GEMM_SMALL = 0, GEMM_DTL128 = 1, GEMM_DTL96 = 2, GEMM_DTL64 = 3 };
 struct GemmPlan { int cfg; int splits; };
-// Kernel and split-K factor for an M x N x K product: the direct-to-LDS kernel when K % 64 == 0,
-// else the register-staged one; the split factor minimises (rounds of resident blocks) x (K per
-// split). Split-K is only considered when allow_split (the epilogue is linear in the accumulator).
+// Kernel, block height and split-K factor for an M x N x K product: a direct-to-LDS kernel when
+// K % 64 == 0 (else the register-staged one), choosing the pair that minimises (rounds of
+// resident blocks) x (work per block) / (per-CU rate of that block shape). Split-K is only
+// considered when allow_split (the epilogue is linear in the accumulator).
 GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, int n_cu);
 
 // ----------------------------------------------------------------- attention (attn.hip)

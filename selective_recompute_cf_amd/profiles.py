@@ -1,0 +1,205 @@
+"""Summaries of rocprofv3 output for the profile notes kept with the repository.
+
+* ``stats``: per-kernel calls, average and total duration from a ``--kernel-trace --stats`` run
+  (the ``*_kernel_stats.csv`` file).
+* ``traffic``: HBM bytes per dispatch of the kernels matching a name pattern, from two
+  ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs, each scaled by what the same counter reads for
+  a plain device copy of known size (``bench.py --copy-calibration``). The result also goes to a
+  JSON file that ``bench.py`` reads for ``roofline.traffic`` as long as the hash of the kernel
+  sources it records still matches.
+
+    python -m selective_recompute_cf_amd.profiles stats <kernel_stats.csv> <out.md> --command "..."
+    python -m selective_recompute_cf_amd.profiles traffic --fetch F.csv --write W.csv \
+        --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --pattern gemm_bf16 \
+        --out-md OUT.md --out-json OUT.json --command "..."
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import shutil
+import subprocess
+from collections import OrderedDict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+# sources whose compiled code the GEMM traffic figures describe
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/kernels.h")
+
+
+def sources_sha256(rel_paths=GEMM_SOURCES) -> str:
+    h = hashlib.sha256()
+    for rel in rel_paths:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def _demangle(name: str) -> str:
+    if not name.startswith("_Z"):
+        return name
+    if shutil.which("c++filt"):
+        out = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
+        if out and not out.startswith("_Z"):
+            return out
+    # names this c++filt cannot read (the bf16 type): namespace::name<element type>
+    m = re.match(r"_ZN(\d+)(\w+)", name)
+    if not m:
+        return name
+    n1 = int(m.group(1))
+    ns, rest = m.group(2)[:n1], m.group(2)[n1:]
+    m2 = re.match(r"(\d+)", rest)
+    if not m2:
+        return name
+    n2 = int(m2.group(1))
+    base = rest[len(m2.group(1)):len(m2.group(1)) + n2]
+    tail = rest[len(m2.group(1)) + n2:]
+    targ = "<__bf16>" if tail.startswith("IDF16b") else "<float>" if tail.startswith("IfE") else ""
+    return f"{ns}::{base}{targ}"
+
+
+def short_name(name: str) -> str:
+    """Kernel name without the argument list (template arguments kept)."""
+    name = _demangle(name.strip().strip('"'))
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def kernel_stats(path: str):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "total_ms": float(r["TotalDurationNs"]) / 1e6,
+                         "avg_us": float(r["AverageNs"]) / 1e3, "pct": float(r["Percentage"])})
+    rows.sort(key=lambda x: -x["total_ms"])
+    return rows
+
+
+def counter_per_dispatch(path: str, counter: str, pattern: str):
+    """[(kernel name, summed counter value)] per dispatch whose name matches `pattern`."""
+    per = OrderedDict()
+    rx = re.compile(pattern)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or not rx.search(r["Kernel_Name"]):
+                continue
+            key = (int(r["Dispatch_Id"]), short_name(r["Kernel_Name"]))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [(k[1], v) for k, v in per.items()]
+
+
+def copy_factor(path: str, counter: str, copy_bytes: int, pattern: str = "copyBuffer") -> float:
+    """Bytes per counter KiB: the copy moves copy_bytes in (FETCH) and out (WRITE) per dispatch."""
+    vals = [v for _, v in counter_per_dispatch(path, counter, pattern)]
+    if not vals:
+        raise SystemExit(f"no '{pattern}' dispatch with {counter} in {path}")
+    kib = sum(vals) / len(vals)
+    return copy_bytes / (kib * 1024.0)
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.csv)
+    tot = sum(r["total_ms"] for r in rows)
+    lines = [f"# {a.title}", "", "Command:", "", "```", a.command, "```", "",
+             f"rocprofv3 kernel-trace statistics, {sum(r['calls'] for r in rows)} dispatches, "
+             f"{tot:.2f} ms of kernel time in total.", "",
+             "| kernel | calls | avg us | total ms | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows[: a.top]:
+        lines.append(f"| `{r['name']}` | {r['calls']} | {r['avg_us']:.2f} | {r['total_ms']:.3f} | {r['pct']:.2f} |")
+    if a.group:
+        rx = re.compile(a.group)
+        g = [r for r in rows if rx.search(r["name"])]
+        calls = sum(r["calls"] for r in g)
+        ms = sum(r["total_ms"] for r in g)
+        lines += ["", f"Kernels matching `{a.group}` together: {calls} calls, {ms:.3f} ms, "
+                      f"average {ms / max(calls, 1) * 1e3:.2f} us per launch."]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def cmd_traffic(a):
+    ff = copy_factor(a.copy_fetch, "FETCH_SIZE", a.copy_bytes)
+    wf = copy_factor(a.copy_write, "WRITE_SIZE", a.copy_bytes)
+    fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.pattern)
+    write = counter_per_dispatch(a.write, "WRITE_SIZE", a.pattern)
+    if not fetch or not write:
+        raise SystemExit("no matching dispatches")
+    by_name = OrderedDict()
+    for (n, v) in fetch:
+        by_name.setdefault(n, {"fetch": [], "write": []})["fetch"].append(v * 1024 * ff)
+    for (n, v) in write:
+        by_name.setdefault(n, {"fetch": [], "write": []})["write"].append(v * 1024 * wf)
+    allf = [x for d in by_name.values() for x in d["fetch"]]
+    allw = [x for d in by_name.values() for x in d["write"]]
+    res = {
+        "kernel_pattern": a.pattern,
+        "source_sha256": sources_sha256(),
+        "copy_bytes": a.copy_bytes,
+        "fetch_factor": ff,
+        "write_factor": wf,
+        "dispatches": len(allf),
+        "fetch_bytes_per_launch": sum(allf) / len(allf),
+        "write_bytes_per_launch": sum(allw) / len(allw),
+        "command": a.command,
+        "per_kernel": {n: {"dispatches": len(d["fetch"]),
+                           "fetch_bytes_per_launch": sum(d["fetch"]) / max(len(d["fetch"]), 1),
+                           "write_bytes_per_launch": sum(d["write"]) / max(len(d["write"]), 1)}
+                       for n, d in by_name.items()},
+    }
+    res["traffic_bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
+    with open(a.out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    lines = [f"# {a.title}", "", "Commands:", "", "```", a.command, "```", "",
+             f"Copy calibration: a {a.copy_bytes / 2**30:.2f} GiB device copy reads FETCH_SIZE "
+             f"{a.copy_bytes / ff / 1024:.0f} KiB and WRITE_SIZE {a.copy_bytes / wf / 1024:.0f} KiB per dispatch, "
+             f"so FETCH_SIZE x {ff:.3f} and WRITE_SIZE x {wf:.3f} give bytes.", "",
+             f"Dispatches matching `{a.pattern}`: {len(allf)}; per launch on average "
+             f"{res['fetch_bytes_per_launch'] / 1e6:.2f} MB fetched + {res['write_bytes_per_launch'] / 1e6:.2f} MB "
+             f"written = {res['traffic_bytes_per_launch'] / 1e6:.2f} MB.", "",
+             "| kernel | dispatches | fetch MB / launch | write MB / launch |", "|---|---:|---:|---:|"]
+    for n, d in res["per_kernel"].items():
+        lines.append(f"| `{n}` | {d['dispatches']} | {d['fetch_bytes_per_launch'] / 1e6:.2f} | "
+                     f"{d['write_bytes_per_launch'] / 1e6:.2f} |")
+    lines += ["", f"Kernel sources hash (sha256 of {', '.join(GEMM_SOURCES)}): `{res['source_sha256']}`"]
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--title", default="Kernel statistics")
+    s.add_argument("--command", required=True)
+    s.add_argument("--top", type=int, default=25)
+    s.add_argument("--group", default=None, help="also total the kernels whose names match this pattern")
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--pattern", required=True)
+    t.add_argument("--out-md", required=True)
+    t.add_argument("--out-json", required=True)
+    t.add_argument("--title", default="HBM traffic per dispatch")
+    t.add_argument("--command", required=True)
+    a = ap.parse_args()
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()

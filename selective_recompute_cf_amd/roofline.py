@@ -54,6 +54,18 @@ def layer_gemm_flops(s: Shape, n: int) -> Dict[str, int]:
     }
 
 
+def layer_gemm_bytes(s: Shape, n: int) -> Dict[str, int]:
+    """Least HBM traffic of the four projections on n rows: weights and bf16 inputs read once,
+    outputs written once (fp32 for the projections feeding fp32 steps, bf16 for the SwiGLU
+    activations)."""
+    return {
+        "bytes:gemm/qkv": s.eb * (s.qd + 2 * s.kvd) * s.d + s.eb * n * s.d + 4 * n * (s.qd + 2 * s.kvd),
+        "bytes:gemm/o": s.eb * s.d * s.qd + s.eb * n * s.qd + 4 * n * s.d,
+        "bytes:gemm/gate_up": s.eb * 2 * s.F * s.d + s.eb * n * s.d + s.eb * n * s.F,
+        "bytes:gemm/down": s.eb * s.d * s.F + s.eb * n * s.F + 4 * n * s.d,
+    }
+
+
 def attention_flops(s: Shape, positions) -> int:
     """QK^T and PV of every selected row over its visible keys: 4 * Hq * hd * sum_j (p_j + 1)."""
     return 4 * s.hq * s.hd * sum(int(p) + 1 for p in positions)
@@ -78,8 +90,11 @@ def blend_step_work(s: Shape, N: int, U: int, k: int, sel_layer: int = 1, sel_po
         n = L if l < sel_layer else n_sel
         for key, f in layer_gemm_flops(s, n).items():
             add(key, f)
+        for key, f in layer_gemm_bytes(s, n).items():
+            add(key, f)
         add("attention", attention_flops(s, range(L)) if l < sel_layer else attention_flops(s, sel_all))
     add("gemm/k_sel", 2 * N * s.kvd * s.d)
+    add("bytes:gemm/k_sel", s.eb * s.kvd * s.d + s.eb * N * s.d + 4 * N * s.kvd)
     # HBM-bound steps (bytes)
     add("reposition", (s.n_layers - sel_layer) * 4 * N * s.kvd * s.eb)     # read K,V; write K,V
     add("qkv_post", 4 * N * s.kvd + s.eb * N * s.kvd + 4 * N)              # deviation pass
@@ -104,3 +119,7 @@ def full_step_work(s: Shape, L: int) -> Dict[str, float]:
 
 def gemm_flops(work: Dict[str, float]) -> float:
     return sum(v for key, v in work.items() if key.startswith("gemm/"))
+
+
+def gemm_bytes(work: Dict[str, float]) -> float:
+    return sum(v for key, v in work.items() if key.startswith("bytes:gemm/"))

@@ -1,0 +1,38 @@
+"""Host-side checks of the profile-summary helpers that feed bench.py's roofline.traffic."""
+import json
+import os
+
+from selective_recompute_cf_amd import profiles
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_short_names():
+    assert profiles.short_name("void cf::gemm_bf16_dtl<cf::DtlCfg<128, 256, 2, 4, 3, 1> >(cf::GemmArgs)") == \
+        "cf::gemm_bf16_dtl<cf::DtlCfg<128, 256, 2, 4, 3, 1> >"
+    assert profiles.short_name("_ZN2cf15qkv_post_kernelIDF16bEEvNS_7QkvPostE") == "cf::qkv_post_kernel<__bf16>"
+
+
+def test_counter_parsing_and_copy_factor(tmp_path):
+    hdr = ("Correlation_Id,Dispatch_Id,Agent_Id,Queue_Id,Process_Id,Thread_Id,Grid_Size,Kernel_Id,Kernel_Name,"
+           "Workgroup_Size,LDS_Block_Size,Scratch_Size,VGPR_Count,Accum_VGPR_Count,SGPR_Count,Counter_Name,"
+           "Counter_Value,Start_Timestamp,End_Timestamp\n")
+    p = tmp_path / "c.csv"
+    rows = [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0), (1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0),
+            (2, "void cf::gemm_bf16_dtl<X>(cf::GemmArgs)", "FETCH_SIZE", 100.0)]
+    p.write_text(hdr + "".join(f'{d},{d},"Agent 1",1,1,1,1,1,"{n}",256,0,0,8,0,16,"{c}",{v},0,1\n'
+                               for d, n, c, v in rows))
+    # two counter rows of one dispatch add up (per-XCD instances); 1 MiB copy -> 1024 KiB counted
+    assert profiles.counter_per_dispatch(str(p), "FETCH_SIZE", "gemm") == [("cf::gemm_bf16_dtl<X>", 100.0)]
+    assert abs(profiles.copy_factor(str(p), "FETCH_SIZE", 1 << 20) - 1.0) < 1e-12
+
+
+def test_committed_traffic_summary_is_well_formed():
+    path = os.path.join(ROOT, "profiles", "gemm_bf16_dtl_llama3-8b_hbm_traffic.json")
+    with open(path) as f:
+        t = json.load(f)
+    for key in ("source_sha256", "fetch_bytes_per_launch", "write_bytes_per_launch", "traffic_bytes_per_launch",
+                "fetch_factor", "write_factor", "command"):
+        assert key in t
+    assert t["traffic_bytes_per_launch"] == t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+    assert len(profiles.sources_sha256()) == 64
