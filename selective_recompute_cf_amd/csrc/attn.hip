@@ -4,11 +4,10 @@
 // blended K/V, n_sel x L instead of L x L; QCFuse Eq. 7: a selected position reads its prefix
 // through the partially fused cache.
 //
-// bf16 path (head_dim 64/128): one block = 64 query rows of one kv head (64/G selected rows x
-// the G query heads sharing that kv head), 4 waves of 16 rows. Keys stream in blocks of 64
-// through double-buffered LDS (two blocks of global loads in flight); K and V tiles are stored
-// row-major with a 16-byte-chunk XOR swizzle by key, and the V^T operand is read with gfx950's
-// transposing LDS read (ds_read_b64_tr_b16).
+// bf16 path (head_dim 64/128): one block = 128 query rows of one kv head, 8 waves; keys stream
+// in blocks of 64 through a 3-stage LDS ring filled by direct global->LDS loads; K and V tiles
+// are stored row-major with a 16-byte-chunk XOR swizzle by key, and the V^T operand is read with
+// gfx950's transposing LDS read (ds_read_b64_tr_b16).
 // S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16: in this orientation every lane
 // holds one query row (lane % 16) for both S and O, so the online-softmax state needs no
 // cross-lane exchange beyond 2 xor-shuffles. Softmax in fp32 with exp2; P rounded to bf16 for
@@ -25,23 +24,36 @@ namespace cf {
 constexpr int KB = 64;  // keys per step
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// One block = 128 query rows of one kv head (128/G selected rows x the G query heads), 8 waves
+// of 16 rows, so every K/V tile read from memory serves 128 rows. K and V tiles of 64 keys stream straight from global memory into a
+// ring of S LDS stages (global_load_lds_dwordx4 from inline assembly, as in the GEMM): lane l of
+// a load lands in 16-byte slot l of a 1 KB row group, so the swizzle is applied on the global
+// side (the lane that fills chunk slot c' of key t fetches chunk c' ^ (t & SWM)). Per key block:
+// wait for this wave's loads of the block | barrier | load the block S - 1 ahead into the stage
+// the previous block used | S^T, softmax, O^T on the block.
+#define CF_ATTN_WAITCNT(vm) ((((vm) & 15) | (((vm) >> 4) << 14)) | 0x70 | (15 << 8))
+
 template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_dtl_kernel(AttnArgs a) {
   constexpr int NCH = HD / 8;     // 16-byte chunks per key row
   constexpr int SWM = NCH - 1;    // chunk c of tile key t is stored at c ^ (t & SWM)
-  constexpr int CH = KB * NCH / 256;  // chunks of each of K and V per thread per step
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KB * HD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][KB * HD];
+  constexpr int S = 3;            // LDS stages
+  constexpr int TILE = KB * HD;   // elements of one K (or V) tile
+  constexpr int RPI = WAVE / NCH; // key rows per load instruction
+  constexpr int NI = 2 * KB / RPI;  // load instructions per key block (K then V)
+  constexpr int NW = 8;
+  constexpr int NL = NI / NW;     // per wave
+  static_assert(NI % NW == 0, "load instructions must split over the waves");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[S * 2 * TILE];
   const int G = a.hq / a.hkv;
-  const int rpt = 64 / G;  // selected rows per block
-  // logical tile: query tile fastest, then split, then kv head: tiles reading the same K/V head
-  // are neighbours and run on the same XCD
+  const int rpt = 128 / G;  // selected rows per block
+  // logical tile: query tile fastest (latest rows, which see the most keys, first), then split,
+  // then kv head; xcd_tile keeps each kv head's tiles on one XCD
   const int q_tiles = (a.n + rpt - 1) / rpt;
   const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
-  const int j0 = (lt % q_tiles) * rpt, split = (lt / q_tiles) % a.splits, g = lt / (q_tiles * a.splits);
+  const int j0 = (q_tiles - 1 - lt % q_tiles) * rpt, split = (lt / q_tiles) % a.splits, g = lt / (q_tiles * a.splits);
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
   const int lg = lane / 16, lr = lane % 16;
   const int r = w * 16 + lr;
@@ -56,8 +68,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const int kbeg = split * a.split_len;
   const int kend = min(min(pmax + 1, kbeg + a.split_len), a.L);
   const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
-  const bf16* K = (const bf16*)a.k + g * HD;
-  const bf16* V = (const bf16*)a.v + g * HD;
 
   bf16x8 qf[HD / 32];
   {
@@ -71,46 +81,43 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   float m_i = -INFINITY, l_i = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
 
-  // two register sets of prefetched K/V chunks. They are ext-vector values, not arrays, so they
-  // live in VGPRs whatever the compiler decides about unrolling (arrays here were demoted to LDS
-  // and scratch memory).
-  typedef uint32_t PVec __attribute__((ext_vector_type(4 * CH)));
-  PVec rk0, rv0, rk1, rv1;
-#define CF_ATTN_GLOAD(RK, RV, STEP)                                                   \
-  do {                                                                                \
-    const int kbase_ = kbeg + (STEP) * KB;                                            \
-    _Pragma("unroll") for (int it_ = 0; it_ < CH; ++it_) {                            \
-      const int ci_ = tid + 256 * it_;                                                \
-      const int t_ = ci_ / NCH, c_ = ci_ % NCH;                                       \
-      const int64_t off_ = (int64_t)min(kbase_ + t_, a.L - 1) * kvd + c_ * 8;         \
-      const uint4 xk_ = *reinterpret_cast<const uint4*>(K + off_);                    \
-      const uint4 xv_ = *reinterpret_cast<const uint4*>(V + off_);                    \
-      RK[4 * it_] = xk_.x; RK[4 * it_ + 1] = xk_.y; RK[4 * it_ + 2] = xk_.z; RK[4 * it_ + 3] = xk_.w; \
-      RV[4 * it_] = xv_.x; RV[4 * it_ + 1] = xv_.y; RV[4 * it_ + 2] = xv_.z; RV[4 * it_ + 3] = xv_.w; \
-    }                                                                                 \
-  } while (0)
-#define CF_ATTN_SSTORE(RK, RV, BUF)                                                   \
-  do {                                                                                \
-    _Pragma("unroll") for (int it_ = 0; it_ < CH; ++it_) {                            \
-      const int ci_ = tid + 256 * it_;                                                \
-      const int t_ = ci_ / NCH, c_ = ci_ % NCH;                                       \
-      const int off_ = t_ * HD + ((c_ ^ (t_ & SWM)) * 8);                             \
-      *reinterpret_cast<uint4*>(&Ks[BUF][off_]) =                                     \
-          make_uint4(RK[4 * it_], RK[4 * it_ + 1], RK[4 * it_ + 2], RK[4 * it_ + 3]);  \
-      *reinterpret_cast<uint4*>(&Vs[BUF][off_]) =                                     \
-          make_uint4(RV[4 * it_], RV[4 * it_ + 1], RV[4 * it_ + 2], RV[4 * it_ + 3]);  \
-    }                                                                                 \
-  } while (0)
+  // load q of this wave: instruction gi = q * NW + w covers key rows [ii * RPI, ii * RPI + RPI)
+  // of tensor gi / (NI / 2) (0 = K, 1 = V), ii = gi % (NI / 2)
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
+  const bf16* src[NL];
+  int trow[NL];
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
+    const int t = ii * RPI + lane / NCH;
+    const int c = (lane % NCH) ^ (t & SWM);
+    src[q] = (const bf16*)(tensor ? a.v : a.k) + g * HD + c * 8;
+    trow[q] = t;
+  }
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    const int stage = step % S;
+    const int kbase = kbeg + step * KB;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
+      const bf16* gp = src[q] + (int64_t)min(kbase + trow[q], a.L - 1) * kvd;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          lds0 + 2u * (uint32_t)(stage * 2 * TILE + tensor * TILE + ii * RPI * HD));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(dst) : "memory", "m0");
+    }
+  };
   // V^T operand through the transposing LDS read: within each 16-lane group, lane q reads the
   // 4 dims 16nt + 4(q%4).. of tile key kb + q/4 and lane lr receives V[kb + 0..3][16nt + lr]
-  auto vread = [&](int buf, int kb, int nt) __attribute__((always_inline)) {
+  auto vread = [&](const bf16* Vt, int kb, int nt) __attribute__((always_inline)) {
     const int t = kb + lr / 4;
     const int col = nt * 16 + 4 * (lr % 4);
     const int c = col / 8;
-    const bf16* ptr = &Vs[buf][t * HD + ((c ^ (t & SWM)) * 8) + (col % 8)];
+    const bf16* ptr = &Vt[t * HD + ((c ^ (t & SWM)) * 8) + (col % 8)];
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
   };
-  auto step = [&](int it, int cur) __attribute__((always_inline)) {
+  auto step = [&](int it) __attribute__((always_inline)) {
+    const bf16* Kt = smem + (it % S) * 2 * TILE;
+    const bf16* Vt = Kt + TILE;
     const int kbase = kbeg + it * KB;
     f32x4 s[4];
 #pragma unroll
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < HD / 32; ++kk) {
         const int c = kk * 4 + lg;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[cur][t * HD + ((c ^ (t & SWM)) * 8)]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Kt[t * HD + ((c ^ (t & SWM)) * 8)]);
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[kt], 0, 0, 0);
       }
     }
@@ -167,34 +174,30 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     for (int nt = 0; nt < HD / 16; ++nt) {
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const i16x4 lo = vread(cur, 32 * mm + 4 * lg, nt);
-        const i16x4 hi = vread(cur, 32 * mm + 16 + 4 * lg, nt);
+        const i16x4 lo = vread(Vt, 32 * mm + 4 * lg, nt);
+        const i16x4 hi = vread(Vt, 32 * mm + 16 + 4 * lg, nt);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[mm], o[nt], 0, 0, 0);
       }
     }
   };
 
-  // two key blocks of loads in flight (register sets 0 and 1), double-buffered LDS
-  if (nkb > 0) CF_ATTN_GLOAD(rk0, rv0, 0);
-  if (nkb > 1) CF_ATTN_GLOAD(rk1, rv1, 1);
-  if (nkb > 0) CF_ATTN_SSTORE(rk0, rv0, 0);
-  __syncthreads();
-  // step `it` reloads set it%2 (free since its data went to LDS) and stores set (it+1)%2
-  for (int it = 0; it < nkb; it += 2) {
-    if (it + 2 < nkb) CF_ATTN_GLOAD(rk0, rv0, it + 2);
-    step(it, 0);
-    if (it + 1 < nkb) CF_ATTN_SSTORE(rk1, rv1, 1);
-    __syncthreads();
-    if (it + 1 < nkb) {
-      if (it + 3 < nkb) CF_ATTN_GLOAD(rk1, rv1, it + 3);
-      step(it + 1, 1);
-      if (it + 2 < nkb) CF_ATTN_SSTORE(rk0, rv0, 0);
-      __syncthreads();
+  if (nkb > 0) {
+    const int last = nkb - 1;
+    // past the last block the loads repeat the last block into a stage nobody reads again, so
+    // every wave issues NL loads per block and the wait counts hold
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q) issue(min(q, last));
+    for (int it = 0; it < nkb; ++it) {
+      __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT((S - 2) * NL));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(min(it + S - 1, last));
+      step(it);
     }
+    __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT(0));
   }
-#undef CF_ATTN_GLOAD
-#undef CF_ATTN_SSTORE
   if (!row_ok) return;
   // o[nt][i] = O[row r][hd 16nt + 4lg + i] (unnormalised)
   if (a.splits > 1) {
@@ -306,11 +309,11 @@ void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* spli
   *splits = 1;
   *split_len = ((L + KB - 1) / KB) * KB;
   if (dt != BF16 || n == 0) return;
-  // split the keys only when the query tiles alone would leave resident-block slots (2 per CU)
-  // empty; each split keeps at least 512 keys (the merge re-reads every split's partial output)
+  // split the keys only when the query tiles alone would leave CUs idle (one 8-wave block per
+  // CU); each split keeps at least 512 keys (the merge re-reads every split's partial output)
   const int G = hq / hkv;
-  const long items = (long)((n + 64 / G - 1) / (64 / G)) * hkv;
-  const long slots = 2L * n_cu;
+  const long items = (long)((n + 128 / G - 1) / (128 / G)) * hkv;
+  const long slots = (long)n_cu;
   int s = 1;
   while (s < 8 && items * (s + 1) <= slots + slots / 8 && L / (s + 1) >= 512) ++s;
   *splits = s;
@@ -320,12 +323,12 @@ void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* spli
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n == 0) return hipSuccess;
   if (a.dt == BF16) {
-    const int G = a.hq / a.hkv, rpt = 64 / G;
+    const int G = a.hq / a.hkv, rpt = 128 / G;
     dim3 grid(((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
     if (a.hd == 128)
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(attn_dtl_kernel<128>, grid, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(attn_dtl_kernel<64>, grid, dim3(512), 0, st, a);
   } else {
     hipLaunchKernelGGL(attn_simple_kernel<float>, dim3(a.n), dim3(256), 0, st, a);
   }
