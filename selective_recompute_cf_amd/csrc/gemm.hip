@@ -12,6 +12,8 @@
 // and split-K partials.
 //
 // fp32 path: a plain LDS-tiled FMA GEMM (64x64x16), used for fp32 models.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,7 +31,9 @@ struct TileCfg {
   static constexpr int BK = 64;
   static constexpr int THREADS = WGM * WGN * WAVE;
   static constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
+  static constexpr int MT = 16;                       // MFMA tile edge (v_mfma_f32_16x16x32_bf16)
   static constexpr int FM = TM / 16, FN = TN / 16;    // MFMA tiles per wave
+  typedef f32x4 Acc;
   static constexpr int ROWS_PER_PASS = THREADS / 8;   // 8 threads (16 B each) per 128-byte row
   static constexpr int AP = BM / ROWS_PER_PASS, BP = BN / ROWS_PER_PASS;
   static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "tile rows must split evenly");
@@ -58,25 +62,33 @@ __device__ __forceinline__ int n_tiles_of(const GemmArgs& a) {
   return a.epi == EPI_SWIGLU ? (a.N + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
 }
 
-// Epilogue: acc[i][j][r] = C[m0 + wm*TM + i*16 + 4*(lane/16) + r][tile col wn*TN + j*16 + lane%16]
+// Accumulator element e of MFMA tile (i, j) sits at wave-tile row i*MT + acc_row(e, lane), column
+// j*MT + lane % MT: for the 16x16 tiles rows 4*(lane/16) + e (e < 4); for the 32x32 tiles rows
+// 8*(e/4) + 4*(lane/32) + e%4 (e < 16).
+template <int MT>
+__device__ __forceinline__ int acc_row(int e, int lane) {
+  return MT == 16 ? 4 * (lane / 16) + e : 8 * (e / 4) + 4 * (lane / 32) + (e % 4);
+}
+
 template <class C>
-__device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[C::FM][C::FN], int m0, int n_tile, int split,
-                                         int wm, int wn, int lane) {
-  constexpr int BN = C::BN, FM = C::FM, FN = C::FN;
-  const int lrow = 4 * (lane / 16), lcol = lane % 16;
+__device__ __forceinline__ void epilogue(const GemmArgs& a, typename C::Acc (&acc)[C::FM][C::FN], int m0, int n_tile,
+                                         int split, int wm, int wn, int lane) {
+  constexpr int BN = C::BN, FM = C::FM, FN = C::FN, MT = C::MT, NE = MT * MT / WAVE;
+  static_assert(FN % 2 == 0, "SwiGLU pairs gate and up tiles within a wave");
+  const int lcol = lane % MT;
   if (a.epi == EPI_SWIGLU) {
     bf16* act = (bf16*)a.act;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * C::TM + i * 16 + lrow + r;
+      for (int e = 0; e < NE; ++e) {
+        const int m = m0 + wm * C::TM + i * MT + acc_row<MT>(e, lane);
         if (m >= a.M) continue;
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
-          const int col = n_tile * (BN / 2) + wn * (C::TN / 2) + j * 16 + lcol;
+          const int col = n_tile * (BN / 2) + wn * (C::TN / 2) + j * MT + lcol;
           if (col >= a.N) continue;
-          const float g = acc[i][j][r], u = acc[i][j + FN / 2][r];
+          const float g = acc[i][j][e], u = acc[i][j + FN / 2][e];
           act[(int64_t)m * a.ld_act + col] = (bf16)(g / (1.0f + expf(-g)) * u);
         }
       }
@@ -85,8 +97,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[C::FM][
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * C::TM + i * 16 + lrow + r;
+    for (int e = 0; e < NE; ++e) {
+      const int m = m0 + wm * C::TM + i * MT + acc_row<MT>(e, lane);
       if (m >= a.M) continue;
       int64_t orow = m, rrow = m;
       if (a.epi == EPI_RESID) {
@@ -95,9 +107,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[C::FM][
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n_tile * BN + wn * C::TN + j * 16 + lcol;
+        const int col = n_tile * BN + wn * C::TN + j * MT + lcol;
         if (col >= a.N) continue;
-        const float v = acc[i][j][r];
+        const float v = acc[i][j][e];
         if (a.epi == EPI_F32)
           a.C[(int64_t)m * a.ldc + col] = v;
         else if (a.epi == EPI_PARTIAL)
@@ -164,11 +176,11 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_kernel(GemmArgs
     }
   };
 
-  f32x4 acc[FM][FN];
+  typename C::Acc acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = typename C::Acc{};
 
   auto compute = [&](int cur) {
 #pragma unroll
@@ -241,14 +253,21 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_kernel(GemmArgs
 //   read slice 0 of step s + 1 | MFMAs slice 1
 // The barrier publishes step s + 1 (every wave waited for its own loads of it) and retires all
 // reads of step s's stage before any wave issues the load that overwrites it (at step s + 1).
-template <int BM_, int BN_, int WGM_, int WGN_, int S_, int MINB_>
+template <int BM_, int BN_, int WGM_, int WGN_, int S_, int MINB_, int MT_ = 32>
 struct DtlCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, S = S_, MINB = MINB_, SWZ = 0, BK = 64;
   static constexpr int W = WGM * WGN, THREADS = W * WAVE;
-  static constexpr int TM = BM / WGM, TN = BN / WGN, FM = TM / 16, FN = TN / 16;
+  static constexpr int TM = BM / WGM, TN = BN / WGN;
+  // MFMA shape: MT = 32 (v_mfma_f32_32x32x16_bf16, k 16 per instruction, two per 32-wide k
+  // slice) or 16 (v_mfma_f32_16x16x32_bf16, one per slice).
+  static constexpr int MT = MT_, KI = MT == 32 ? 16 : 32, NSUB = 32 / KI;
+  static constexpr int FM = TM / MT, FN = TN / MT;
+  typedef typename std::conditional<MT == 32, f32x16, f32x4>::type Acc;
   static constexpr int G = (BM + BN) / 8;         // 8-row load groups per K step
   static constexpr int NL = (G + W - 1) / W;      // load instructions per wave per K step
   static constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
+  static_assert(MT == 16 || MT == 32, "MFMA tile edge");
+  static_assert(TM % MT == 0 && TN % MT == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BM % 8 == 0 && BN % 8 == 0 && NL * W - G <= W, "8-row load groups");
   static_assert((S - 2) * NL <= 63, "in-flight loads must fit the vmcnt counter");
   __device__ static __forceinline__ int swz(int r) { return r & 7; }
@@ -303,36 +322,49 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
     }
   };
 
-  typedef uint32_t FVec __attribute__((ext_vector_type(4 * (FM + FN))));
+  // operands of one 32-wide k slice: NSUB sub-steps x (FM A + FN B) fragments of 8 bf16 per lane
+  constexpr int NSUB = C::NSUB, MT = C::MT, NF = NSUB * (FM + FN);
+  typedef uint32_t FVec __attribute__((ext_vector_type(4 * NF)));
   typedef uint32_t U4 __attribute__((ext_vector_type(4)));
   auto fread = [&](int stage, int kk) __attribute__((always_inline)) {
-    const int ch = kk * 4 + lane / 16;
     const bf16* st = smem + stage * C::STAGE;
     FVec f;
 #pragma unroll
-    for (int q = 0; q < FM + FN; ++q) {
-      const int r = q < FM ? wm * C::TM + q * 16 + (lane % 16) : BM + wn * C::TN + (q - FM) * 16 + (lane % 16);
-      const int rr = q < FM ? r : r - BM;
-      const U4 x = *reinterpret_cast<const U4*>(st + r * BK + ((ch ^ C::swz(rr)) * 8));
-      f[4 * q] = x[0], f[4 * q + 1] = x[1], f[4 * q + 2] = x[2], f[4 * q + 3] = x[3];
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const int ch = kk * 4 + sub * (C::KI / 8) + lane / MT;
+#pragma unroll
+      for (int q = 0; q < FM + FN; ++q) {
+        const int r = q < FM ? wm * C::TM + q * MT + (lane % MT) : BM + wn * C::TN + (q - FM) * MT + (lane % MT);
+        const int rr = q < FM ? r : r - BM;
+        const U4 x = *reinterpret_cast<const U4*>(st + r * BK + ((ch ^ C::swz(rr)) * 8));
+        const int o = 4 * (sub * (FM + FN) + q);
+        f[o] = x[0], f[o + 1] = x[1], f[o + 2] = x[2], f[o + 3] = x[3];
+      }
     }
     return f;
   };
-  f32x4 acc[FM][FN];
+  typename C::Acc acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = typename C::Acc{};
   auto fmma = [&](FVec f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const U4 av = {f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
-        const U4 bv = {f[4 * (FM + j)], f[4 * (FM + j) + 1], f[4 * (FM + j) + 2], f[4 * (FM + j) + 3]};
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                           __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
-      }
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int oa = 4 * (sub * (FM + FN) + i), ob = 4 * (sub * (FM + FN) + FM + j);
+          const U4 av = {f[oa], f[oa + 1], f[oa + 2], f[oa + 3]};
+          const U4 bv = {f[ob], f[ob + 1], f[ob + 2], f[ob + 3]};
+          if constexpr (MT == 32)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                               __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                               __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
+        }
   };
   // a raw barrier: no fence, so the compiler adds no drain of the in-flight LDS loads; the
   // empty asm statements keep LDS accesses from moving across it
@@ -387,9 +419,10 @@ hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t st) {
 
 using GemmSmall = TileCfg<128, 128, 2, 2, 2, 2>;  // register-staged, 2 blocks per CU (K % 64 != 0)
 // direct-to-LDS block heights for BN = 256, one block per CU, 8 waves each
-using GemmDtl128 = DtlCfg<128, 256, 2, 4, 3, 1>;  // waves 64x64, 3 x 48 KB stages
-using GemmDtl96 = DtlCfg<96, 256, 2, 4, 3, 1>;    // waves 48x64, 3 x 44 KB stages
-using GemmDtl64 = DtlCfg<64, 256, 1, 8, 4, 1>;    // waves 64x32, 4 x 40 KB stages
+// (16x16 MFMA tiles: the 32x32 shape measured slower in this loop on every projection shape)
+using GemmDtl128 = DtlCfg<128, 256, 2, 4, 3, 1, 16>;  // waves 64x64, 3 x 48 KB stages
+using GemmDtl96 = DtlCfg<96, 256, 2, 4, 3, 1, 16>;    // waves 48x64, 3 x 44 KB stages
+using GemmDtl64 = DtlCfg<64, 256, 1, 8, 4, 1, 16>;    // waves 64x32, 4 x 40 KB stages
 
 // ----------------------------------------------------------------------------- fp32 path
 __device__ __forceinline__ const float* b_row_ptr_f32(const GemmArgs& a, int col) {
