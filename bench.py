@@ -44,6 +44,10 @@ def main():
     ap.add_argument("--store-cache", default=None,
                     help="load the chunk store from this file if it exists, else build it and save it there")
     ap.add_argument("--prepare-only", action="store_true", help="build (and save) the chunk store, then exit")
+    ap.add_argument("--sweeps", action="store_true",
+                    help="only run the kernel sweeps beyond the request's own sizes (re-position over all layers, "
+                         "deviation up to GB sizes, top-k up to 256M, measured copy and MFMA peaks), print them as one "
+                         "JSON line and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (the reference for the FETCH_SIZE / "
                          "WRITE_SIZE counters) and exit")
@@ -63,6 +67,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
+    if args.sweeps:
+        print(json.dumps(kernel_sweeps()), flush=True)
+        return
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -230,6 +237,102 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def _event_ms(fn, reps=5, warmup=2):
+    """Median HIP-event time (ms) of fn() on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return statistics.median(ts)
+
+
+def kernel_sweeps():
+    """The HBM-bound steps at sizes beyond one request, through the C ABI, against the published
+    peaks and the peaks measured here (a plain device copy; the library's MFMA loop)."""
+    import torch
+    import synth
+    import selective_recompute_cf_amd as cf
+    from selective_recompute_cf_amd import roofline as rl
+
+    res = {}
+    # measured peaks
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    t = _event_ms(lambda: cf.copy_loop(a, b))
+    copy_gbs = 2 * n / (t / 1e3) / 1e9
+    del a, b
+    out = torch.empty(64 * 256 * 256, dtype=torch.float32, device="cuda")
+    fl = {}
+    t = _event_ms(lambda: fl.__setitem__("f", cf.mfma_loop(out, 4, 20000)))
+    mfma_tf = fl["f"] / (t / 1e3) / 1e12
+    res["measured_peaks"] = {"hbm_copy_GBs": round(copy_gbs, 1), "copy": "4 GiB streaming copy (cf_copy_loop), read + write",
+                             "mfma_bf16_TFs": round(mfma_tf, 1),
+                             "mfma": "32x32x16 bf16 MFMA loop, 16 waves per CU, no memory traffic",
+                             "spec_hbm_GBs": rl.HBM_PEAK_GBS, "spec_bf16_TFs": rl.BF16_PEAK_TFLOPS}
+    log(f"[sweeps] copy {copy_gbs:.0f} GB/s, MFMA loop {mfma_tf:.0f} TF/s")
+
+    def frac(gbs):
+        return {"achieved_GBs": round(gbs, 1), "frac_spec": round(gbs / rl.HBM_PEAK_GBS, 4),
+                "frac_measured": round(gbs / copy_gbs, 4)}
+
+    # H1: re-position + stitch of every layer after the selection layer, in one call
+    rows = []
+    for name, Ly, N, kvd in (("llama3-8b 6x512, layers 1..31", 31, 3072, 1024),
+                             ("llama3-70b 16x1024, layers 1..79", 79, 16384, 1024)):
+        cfg = synth.LLAMA3_8B.replace(n_layers=Ly)
+        ctx = cf.Context.from_model_cfg(cfg, max_pos=2 * N + 1)
+        ks = torch.randn(Ly, N, kvd, device="cuda").to(torch.bfloat16)
+        vs = torch.randn_like(ks)
+        kb, vb = torch.empty_like(ks), torch.empty_like(vs)
+        chunk = 512 if N == 3072 else 1024
+        tab = [(i * chunk, 0, i * chunk, chunk) for i in range(N // chunk)]
+        t = _event_ms(lambda: ctx.rope_reposition(ks, vs, kb, vb, tab, 0, Ly))
+        byt = rl.kv_bytes_per_layer(N, 8, 128, 2) * 2 * Ly
+        rows.append({"case": name, "bytes": byt, "ms": round(t, 4), **frac(byt / (t / 1e3) / 1e9)})
+        del ks, vs, kb, vb
+        ctx.close()
+    res["reposition"] = rows
+    log(f"[sweeps] reposition {[r['achieved_GBs'] for r in rows]} GB/s")
+
+    # H2: deviation sum_c (K_new - K_ref)^2 over kvd = 1024, bf16 inputs
+    rows = []
+    for name, n_tok in (("one layer, 3072 rows", 3072), ("one layer, 16384 rows", 16384),
+                        ("all 32 layers of 3072 rows", 32 * 3072), ("1M rows", 1 << 20)):
+        kn = torch.randn(n_tok, 1024, device="cuda").to(torch.bfloat16)
+        kr = torch.randn_like(kn)
+        dev = torch.empty(n_tok, dtype=torch.float32, device="cuda")
+        t = _event_ms(lambda: cf.kv_deviation(kn, kr, dev))
+        byt = 2 * n_tok * 1024 * 2 + 4 * n_tok
+        rows.append({"case": name, "bytes": byt, "ms": round(t, 4), **frac(byt / (t / 1e3) / 1e9)})
+        del kn, kr, dev
+    res["deviation"] = rows
+    log(f"[sweeps] deviation {[r['achieved_GBs'] for r in rows]} GB/s")
+
+    # H3: token top-k (exact), k = 15% of n
+    rows = []
+    for n_tok in (3072, 16384, 16 << 20, 64 << 20, 256 << 20):
+        d = torch.rand(n_tok, device="cuda")
+        k = cf.budget(n_tok, 15, 100)
+        o = torch.empty(k, dtype=torch.int32, device="cuda")
+        ws = torch.empty(max(cf.topk_workspace_size(n_tok, "token"), 1), dtype=torch.uint8, device="cuda")
+        t = _event_ms(lambda: cf.topk_select(d, k, o, "token", None, ws))
+        byt = 4 * n_tok + 4 * k
+        rows.append({"n": n_tok, "k": k, "us": round(t * 1e3, 1), "bytes": byt, **frac(byt / (t / 1e3) / 1e9)})
+        del d, o, ws
+    res["topk_token"] = rows
+    log(f"[sweeps] topk {[(r['n'], r['us']) for r in rows]}")
+    return {"sweeps": res}
 
 
 def gemm_traffic(alg_bytes_per_launch):

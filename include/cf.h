@@ -119,6 +119,20 @@ const char* cf_version(void);
 cf_status cf_profile_enable(int32_t on);
 const char* cf_profile_report(void);
 
+/* Measurement aid: enqueue a matrix-core loop with no memory traffic (blocks_per_cu x CUs
+ * blocks of 256 threads, each wave issuing iters x 4 independent 32x32x16 bf16 MFMAs) to
+ * measure the achievable dense bf16 rate. out: device fp32 [blocks_per_cu * CUs * 256] (the
+ * sums, so the work is kept); *flops (host) receives the flop count of the launch. The caller
+ * times the stream. 1 <= blocks_per_cu <= 64, 1 <= iters. */
+cf_status cf_mfma_loop(int32_t device, int32_t blocks_per_cu, int32_t iters, float* out, double* flops,
+                       hipStream_t stream);
+
+/* Measurement aid: enqueue a streaming copy of `bytes` (a multiple of 16; both pointers 16-byte
+ * aligned device memory, not overlapping) with 16-byte loads and stores, one contiguous 256 KB
+ * range per workgroup: the reference for the achievable HBM rate of a read + write stream. The
+ * caller times it. */
+cf_status cf_copy_loop(int32_t device, const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 /* --------------------------------------------------------------------- cf_rope_reposition
  * QCFuse Eq. 4 (position remap Pi_i and stitching) with CacheBlend's rotation composition.
  * For each chunk i of the host table chunk_tab[m][4] = {store_row, src_pos, dst_pos, len}
@@ -157,7 +171,10 @@ cf_status cf_kv_deviation(const void* k_new, int32_t new_dtype, int64_t ld_new, 
  *    still owed are the window [a, a+r) of that span maximising P[a+r] - P[a], P being the
  *    span's fp64 running sum from its start (smallest a among equals). Exactly k tokens.
  * Results are exact (bit-identical to any implementation of the same order). 0 <= k <= n.
- * n_spans <= CF_MAX_SPANS. ws: device workspace of cf_topk_workspace_size(n, mode) bytes. */
+ * n_spans <= CF_MAX_SPANS. ws: device workspace of cf_topk_workspace_size(n, mode) bytes (span
+ * mode always; token mode from n = 65536 up, where the selection runs on the whole GPU; the
+ * size is 0 otherwise and ws may be NULL). A call without the workspace it needs fails with
+ * CF_EWORKSPACE before anything is enqueued. */
 #define CF_MAX_SPANS 256
 size_t cf_topk_workspace_size(int32_t n, int32_t mode);
 cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode,

@@ -21,7 +21,7 @@ MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
            "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
-           "cf_blend_prefill", "cf_profile_enable", "cf_profile_report"]
+           "cf_blend_prefill", "cf_profile_enable", "cf_profile_report", "cf_mfma_loop", "cf_copy_loop"]
 
 
 class CfError(RuntimeError):
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         "cf_version": (ctypes.c_char_p, []),
         "cf_profile_enable": (i32, [i32]),
         "cf_profile_report": (ctypes.c_char_p, []),
+        "cf_mfma_loop": (i32, [i32, i32, i32, vp, ctypes.POINTER(ctypes.c_double), vp]),
+        "cf_copy_loop": (i32, [i32, vp, vp, i64, vp]),
         "cf_rope_reposition": (i32, [vp, vp, vp, i64, i32, vp, vp, i64, i32, vp, i32, i32, i32, vp]),
         "cf_kv_deviation": (i32, [vp, i32, i64, vp, i32, i64, vp, i32, i32, vp]),
         "cf_topk_workspace_size": (sz, [i32, i32]),
@@ -90,6 +92,20 @@ def version() -> str:
 def profile_enable(on: bool = True):
     """Bracket every libcf kernel launch with HIP events (see cf_profile_enable)."""
     _check(lib().cf_profile_enable(1 if on else 0))
+
+
+def mfma_loop(out, blocks_per_cu: int, iters: int) -> float:
+    """Enqueue the matrix-core loop (cf_mfma_loop) on the current stream; returns its flop count."""
+    fl = ctypes.c_double(0.0)
+    _check(lib().cf_mfma_loop(out.device.index or 0, blocks_per_cu, iters, _ptr(out), ctypes.byref(fl),
+                              _stream(out.device)))
+    return fl.value
+
+
+def copy_loop(src, dst):
+    """Enqueue the streaming copy (cf_copy_loop) of src's bytes into dst on the current stream."""
+    _check(lib().cf_copy_loop(src.device.index or 0, _ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                              _stream(src.device)))
 
 
 def profile_report() -> dict:

@@ -168,7 +168,7 @@ PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode) {
   p.sel = take((size_t)L * 4);
   p.ident = take((size_t)L * 4);
   p.dev = take((size_t)std::max(N, 1) * 4);
-  p.topk = take(mode == CF_SEL_DOC_SPANS ? (size_t)(N + 1) * 8 : 0);
+  p.topk = take(cf_topk_workspace_size(N, mode));
   // the layer scratch serves full-row layers (R = L) and selected-row layers (R = k + U)
   const LayerWs a = layer_ws(c, L, L, mode == CF_SEL_ALL ? 0 : N), b = layer_ws(c, L, std::min(L, k + U));
   p.layer = take(std::max(a.total, b.total));
@@ -347,7 +347,7 @@ cf_status enqueue_select(const float* dev, int n, int k, int mode, const int32_t
                          double* ws, hipStream_t st) {
   if (k == 0) return CF_OK;
   if (mode == CF_SEL_TOKEN_TOPK) {
-    CF_RUN("topk_token", cf::launch_topk_token(dev, n, k, out, st));
+    CF_RUN("topk_token", cf::launch_topk_token(dev, n, k, out, ws, st));
   } else {
     cf::SpanArgs sp{};
     sp.n_spans = ns;
@@ -365,6 +365,35 @@ extern "C" {
 const char* cf_last_error(void) { return g_err.c_str(); }
 
 const char* cf_version(void) { return "libcf 0.1 (gfx950)"; }
+
+cf_status cf_mfma_loop(int32_t device, int32_t blocks_per_cu, int32_t iters, float* out, double* flops,
+                       hipStream_t st) {
+  g_err.clear();
+  CF_CHECK(blocks_per_cu >= 1 && blocks_per_cu <= 64 && iters >= 1, CF_EINVAL, "need 1 <= blocks_per_cu <= 64, iters >= 1");
+  CF_CHECK(out && flops, CF_EINVAL, "null pointer");
+  DeviceGuard guard(device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  int n_cu = 0;
+  CF_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n_cu > 0,
+           CF_EHIP, "cannot query the CU count");
+  *flops = cf::launch_mfma_loop(blocks_per_cu * n_cu, iters, out, st);
+  CF_CHECK(hipGetLastError() == hipSuccess, CF_EHIP, "launch failed");
+  return CF_OK;
+}
+
+cf_status cf_copy_loop(int32_t device, const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  g_err.clear();
+  CF_CHECK(src && dst && aligned16(src) && aligned16(dst), CF_EINVAL, "pointers must be non-null and 16-byte aligned");
+  CF_CHECK(bytes >= 0 && bytes % 16 == 0, CF_EINVAL, "bytes must be a non-negative multiple of 16");
+  const char *s = (const char*)src, *d = (const char*)dst;
+  CF_CHECK(s + bytes <= d || d + bytes <= s, CF_EINVAL, "source and destination overlap");
+  if (bytes == 0) return CF_OK;
+  DeviceGuard guard(device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  cf::launch_copy_loop(src, dst, bytes / 16, st);
+  CF_CHECK(hipGetLastError() == hipSuccess, CF_EHIP, "launch failed");
+  return CF_OK;
+}
 
 cf_status cf_profile_enable(int32_t on) {
   g_err.clear();
@@ -494,7 +523,9 @@ cf_status cf_kv_deviation(const void* k_new, int32_t new_dtype, int64_t ld_new, 
 }
 
 size_t cf_topk_workspace_size(int32_t n, int32_t mode) {
-  return mode == CF_SEL_DOC_SPANS && n >= 0 ? al((size_t)(n + 1) * 8) : 0;
+  if (n < 0) return 0;
+  if (mode == CF_SEL_DOC_SPANS) return al((size_t)(n + 1) * 8);
+  return mode == CF_SEL_TOKEN_TOPK ? al(cf::topk_token_ws_bytes(n)) : 0;
 }
 
 cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode, const int32_t* bounds, int32_t ns,
@@ -502,11 +533,10 @@ cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode, c
   g_err.clear();
   CF_CHECK(mode == CF_SEL_TOKEN_TOPK || mode == CF_SEL_DOC_SPANS, CF_EINVAL, "mode %d is not a selection mode", mode);
   CF_CHECK(n >= 0 && k >= 0 && k <= n, CF_EINVAL, "need 0 <= k <= n (k=%d, n=%d)", k, n);
-  if (mode == CF_SEL_DOC_SPANS) {
+  if (mode == CF_SEL_DOC_SPANS)
     if (cf_status s = check_spans(bounds, ns, n)) return s;
-    CF_CHECK(k == 0 || (ws && ws_bytes >= cf_topk_workspace_size(n, mode)), CF_EWORKSPACE,
-             "span mode needs %zu workspace bytes", cf_topk_workspace_size(n, mode));
-  }
+  CF_CHECK(k == 0 || cf_topk_workspace_size(n, mode) == 0 || (ws && ws_bytes >= cf_topk_workspace_size(n, mode)),
+           CF_EWORKSPACE, "this selection needs %zu workspace bytes", cf_topk_workspace_size(n, mode));
   if (k == 0) return CF_OK;
   CF_CHECK(dev && out, CF_EINVAL, "null pointer");
   return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), st);

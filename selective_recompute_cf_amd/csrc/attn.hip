@@ -28,7 +28,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // One block = 128 query rows of one kv head (128/G selected rows x the G query heads), 8 waves
 // of 16 rows, so every K/V tile read from memory serves 128 rows. K and V tiles of 64 keys stream straight from global memory into a
-// ring of S LDS stages (global_load_lds_dwordx4 from inline assembly, as in the GEMM): lane l of
+// ring of S LDS stages (global_load_lds_dwordx4 from inline assembly, as in the GEMM; M0 is set
+// right before each load and used by nothing else in the kernel): lane l of
 // a load lands in 16-byte slot l of a 1 KB row group, so the swizzle is applied on the global
 // side (the lane that fills chunk slot c' of key t fetches chunk c' ^ (t & SWM)). Per key block:
 // wait for this wave's loads of the block | barrier | load the block S - 1 ahead into the stage

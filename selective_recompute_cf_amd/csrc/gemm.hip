@@ -311,7 +311,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
   // treats the pending LDS write as unordered and drains every outstanding LDS read before the
   // next MFMA, which serialises the fragment reads with the matrix cores. The pass does not see
   // these loads, so the waits for them are explicit (CF_WAITCNT below); its own vmcnt waits stay
-  // correct because vector-memory loads retire in order.
+  // correct because vector-memory loads retire in order. M0 is written only here, right before
+  // each load (the compiler reserves M0 and does not use it in this kernel).
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
   auto issue = [&](int step) __attribute__((always_inline)) {
     const int stage = step % S;

@@ -57,6 +57,11 @@ hipError_t launch_swiglu(Dt dt, const float* gu, int M, int F, void* act, hipStr
 hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void* b, int64_t ldb,
                             float* dev, int n, int kvd, hipStream_t st);
 
+// ----------------------------------------------------------------- measurement (probe.hip)
+// Launches blocks x 256 threads of the MFMA loop; returns its flop count.
+double launch_mfma_loop(int blocks, int iters, float* out, hipStream_t st);
+void launch_copy_loop(const void* src, void* dst, int64_t n16, hipStream_t st);
+
 // ----------------------------------------------------------------- GEMM (gemm.hip)
 enum Epi { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PARTIAL = 3 };
 struct GemmArgs {
@@ -99,7 +104,9 @@ void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* spli
 // ----------------------------------------------------------------- selection (topk.hip)
 constexpr int MAX_SPANS = 256;
 struct SpanArgs { int n_spans; int b[MAX_SPANS + 1]; };
-hipError_t launch_topk_token(const float* dev, int n, int k, int* out, hipStream_t st);
+// ws: topk_token_ws_bytes(n) bytes (none below the large-n threshold, where one workgroup runs)
+size_t topk_token_ws_bytes(int n);
+hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws, hipStream_t st);
 hipError_t launch_topk_spans(const float* dev, int n, int k, const SpanArgs& sp, int* out,
                              double* ws, hipStream_t st);
 

@@ -1,4 +1,5 @@
-// Selection of the recompute set P (exact, deterministic; one workgroup of 1024 threads).
+// Selection of the recompute set P (exact, deterministic; one workgroup of 1024 threads, or the
+// whole GPU for large n in token mode).
 //
 // Token mode (CacheBlend "Quantifying the Damage": HKVD tokens; Request Order Matters §2.2):
 // the k positions of largest deviation, ties to the lower index, written ascending. Deviations
@@ -11,6 +12,8 @@
 // (mean desc, span index asc), whole spans taken while they fit (stopping at the first that
 // does not), the remainder filled by the window of largest fp64 running-sum difference in that
 // span (smallest start among equals).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -125,9 +128,232 @@ __global__ __launch_bounds__(TK_THREADS) void topk_token_kernel(const float* __r
   }
 }
 
-hipError_t launch_topk_token(const float* dev, int n, int k, int* out, hipStream_t st) {
+// ----------------------------------------------------------------------------- token, large n
+// The same exact selection spread over the whole GPU for n >= TK_MB_MIN: four 8-bit histogram
+// passes (LDS histograms merged with global atomics), each followed by a one-thread pick of the
+// digit; a per-block count of keys above / equal to the threshold key T; a one-block scan that
+// turns the counts into output offsets and ranks among equal keys (lower index first); and an
+// ordered write of each block's range. No block waits for another.
+constexpr int TK_MB_MIN = 1 << 16;
+constexpr int TK_MB_SEG = 16384;       // indices per count / write block (at least)
+constexpr int TK_MB_MAX_BLOCKS = 2048;
+
+struct TopkState {
+  uint32_t prefix[5];  // prefix[p]: the top 8p bits of T fixed by passes < p
+  int kk[5];           // kk[p]: keys still owed among those matching prefix[p]
+};
+
+static int tk_mb_blocks(int n) { return std::min(TK_MB_MAX_BLOCKS, (n + TK_MB_SEG - 1) / TK_MB_SEG); }
+
+size_t topk_token_ws_bytes(int n) {
+  if (n < TK_MB_MIN) return 0;
+  return 4 * 256 * sizeof(uint32_t) + 256 + (size_t)tk_mb_blocks(n) * 4 * sizeof(int);
+}
+
+__global__ __launch_bounds__(TK_THREADS) void tk_mb_init_kernel(uint32_t* hist, TopkState* st, int k) {
+  hist[threadIdx.x] = 0;  // 4 x 256 bins
+  if (threadIdx.x == 0) {
+    st->prefix[0] = 0;
+    st->kk[0] = k;
+  }
+}
+
+// 16 copies of the 256 bins per block (lane % 16 picks the copy): deviations, like most float
+// data, put most keys into a few top-byte bins, and same-address LDS atomics serialise
+constexpr int TK_HCOPIES = 16;
+
+__global__ __launch_bounds__(256) void tk_mb_hist_kernel(const float* __restrict__ dev, int n, int pass,
+                                                         const TopkState* __restrict__ st, uint32_t* hist) {
+  __shared__ uint32_t h[TK_HCOPIES][256];
+#pragma unroll
+  for (int c = 0; c < TK_HCOPIES; ++c) h[c][threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t prefix = st->prefix[pass];
+  const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+  const int shift = 24 - 8 * pass;
+  uint32_t* mine = h[threadIdx.x % TK_HCOPIES];
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+  auto add = [&](float x) {
+    const uint32_t key = order_key(x);
+    if ((key & mask) == prefix) atomicAdd(&mine[(key >> shift) & 255u], 1u);
+  };
+  const int64_t n4 = ((uintptr_t)dev & 15) == 0 ? n / 4 : 0;
+  for (int64_t i = gid; i < n4; i += stride) {
+    const float4 v = reinterpret_cast<const float4*>(dev)[i];
+    add(v.x), add(v.y), add(v.z), add(v.w);
+  }
+  for (int64_t i = 4 * n4 + gid; i < n; i += stride) add(dev[i]);
+  __syncthreads();
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < TK_HCOPIES; ++k) c += h[k][threadIdx.x];
+  if (c) atomicAdd(&hist[pass * 256 + threadIdx.x], c);
+}
+
+__global__ __launch_bounds__(256) void tk_mb_pick_kernel(int pass, TopkState* st, const uint32_t* hist) {
+  __shared__ int h[256];
+  h[threadIdx.x] = (int)hist[pass * 256 + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const int shift = 24 - 8 * pass;
+  const int kk = st->kk[pass];
+  int cum = 0;
+  for (int b = 255; b >= 0; --b) {
+    if (cum + h[b] >= kk) {
+      st->prefix[pass + 1] = st->prefix[pass] | ((uint32_t)b << shift);
+      st->kk[pass + 1] = kk - cum;
+      return;
+    }
+    cum += h[b];
+  }
+}
+
+// blk[2b], blk[2b+1]: keys above / equal to T in block b's index range
+__global__ __launch_bounds__(TK_THREADS) void tk_mb_count_kernel(const float* __restrict__ dev, int n, int seg,
+                                                                 const TopkState* __restrict__ st, int* blk) {
+  __shared__ int red[2][TK_THREADS / WAVE];
+  const uint32_t T = st->prefix[4];
+  const int b0 = blockIdx.x * seg, b1 = min(n, b0 + seg);
+  int gt = 0, eq = 0;
+  auto cnt = [&](float x) {
+    const uint32_t key = order_key(x);
+    gt += key > T;
+    eq += key == T;
+  };
+  // b0 is a multiple of 64, so with a 16-byte aligned dev the 4-wide loads are aligned
+  const bool vec = ((uintptr_t)dev & 15) == 0;
+  const int v1 = vec ? b0 + (b1 - b0) / 4 * 4 : b0;
+  for (int i = b0 + 4 * (int)threadIdx.x; i < v1; i += 4 * TK_THREADS) {
+    const float4 v = *reinterpret_cast<const float4*>(dev + i);
+    cnt(v.x), cnt(v.y), cnt(v.z), cnt(v.w);
+  }
+  for (int i = v1 + (int)threadIdx.x; i < b1; i += TK_THREADS) cnt(dev[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    gt += __shfl_xor(gt, o, WAVE);
+    eq += __shfl_xor(eq, o, WAVE);
+  }
+  const int w = threadIdx.x / WAVE;
+  if (threadIdx.x % WAVE == 0) red[0][w] = gt, red[1][w] = eq;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, e = 0;
+    for (int i = 0; i < TK_THREADS / WAVE; ++i) a += red[0][i], e += red[1][i];
+    blk[2 * blockIdx.x] = a;
+    blk[2 * blockIdx.x + 1] = e;
+  }
+}
+
+// off[2b]: output offset of block b; off[2b+1]: keys equal to T in blocks before b
+__global__ __launch_bounds__(TK_THREADS) void tk_mb_scan_kernel(int nb, const TopkState* __restrict__ st,
+                                                                const int* __restrict__ blk, int* off) {
+  __shared__ int wsum[TK_THREADS / WAVE];
+  __shared__ int total;
+  const int kk = st->kk[4];
+  const int per = (nb + TK_THREADS - 1) / TK_THREADS;
+  const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
+  int eq = 0;
+  for (int b = b0; b < b1; ++b) eq += blk[2 * b + 1];
+  int eq_before = block_excl_scan(eq, wsum, &total);
+  int sel = 0;
+  {
+    int e = eq_before;
+    for (int b = b0; b < b1; ++b) {
+      const int eb = blk[2 * b + 1];
+      sel += blk[2 * b] + min(max(kk - e, 0), eb);
+      e += eb;
+    }
+  }
+  int sel_before = block_excl_scan(sel, wsum, &total);
+  for (int b = b0; b < b1; ++b) {
+    const int eb = blk[2 * b + 1];
+    off[2 * b] = sel_before;
+    off[2 * b + 1] = eq_before;
+    sel_before += blk[2 * b] + min(max(kk - eq_before, 0), eb);
+    eq_before += eb;
+  }
+}
+
+// Each thread owns TK_EPT consecutive indices of a tile, so one pair of block scans orders
+// TK_THREADS * TK_EPT positions.
+constexpr int TK_EPT = 16;
+
+__global__ __launch_bounds__(TK_THREADS) void tk_mb_write_kernel(const float* __restrict__ dev, int n, int seg,
+                                                                 const TopkState* __restrict__ st,
+                                                                 const int* __restrict__ off, int k, int* out) {
+  __shared__ int wsum[TK_THREADS / WAVE];
+  __shared__ int total;
+  const uint32_t T = st->prefix[4];
+  const int kk = st->kk[4];
+  const int b0 = blockIdx.x * seg, b1 = min(n, b0 + seg);
+  int o_run = off[2 * blockIdx.x], e_run = off[2 * blockIdx.x + 1];
+  const bool vec = ((uintptr_t)dev & 15) == 0;  // b0 and i0 are multiples of 16 elements
+  for (int base = b0; base < b1; base += TK_THREADS * TK_EPT) {
+    const int i0 = base + (int)threadIdx.x * TK_EPT;
+    uint32_t key[TK_EPT];
+    int n_eq = 0;
+    if (vec && i0 + TK_EPT <= b1) {
+#pragma unroll
+      for (int e = 0; e < TK_EPT; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(dev + i0 + e);
+        key[e] = order_key(v.x), key[e + 1] = order_key(v.y), key[e + 2] = order_key(v.z), key[e + 3] = order_key(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < TK_EPT; ++e) key[e] = i0 + e < b1 ? order_key(dev[i0 + e]) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < TK_EPT; ++e) n_eq += i0 + e < b1 && key[e] == T;
+    int r = e_run + block_excl_scan(n_eq, wsum, &total);
+    const int eq_tile = total;
+    int n_take = 0;
+    {
+      int rr = r;
+#pragma unroll
+      for (int e = 0; e < TK_EPT; ++e) {
+        const bool in = i0 + e < b1, eq = in && key[e] == T;
+        n_take += in && (key[e] > T || (eq && rr < kk));
+        rr += eq;
+      }
+    }
+    int o = o_run + block_excl_scan(n_take, wsum, &total);
+    const int take_tile = total;
+#pragma unroll
+    for (int e = 0; e < TK_EPT; ++e) {
+      const bool in = i0 + e < b1, eq = in && key[e] == T;
+      if (in && (key[e] > T || (eq && r < kk))) {
+        if (o < k) out[o] = i0 + e;
+        ++o;
+      }
+      r += eq;
+    }
+    e_run += eq_tile;
+    o_run += take_tile;
+  }
+}
+
+hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws, hipStream_t st) {
   if (k <= 0 || n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_token_kernel, dim3(1), dim3(TK_THREADS), 0, st, dev, n, k, out);
+  if (n < TK_MB_MIN) {
+    hipLaunchKernelGGL(topk_token_kernel, dim3(1), dim3(TK_THREADS), 0, st, dev, n, k, out);
+    return hipGetLastError();
+  }
+  if (!ws) return hipErrorInvalidValue;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws);
+  TopkState* state = reinterpret_cast<TopkState*>(reinterpret_cast<char*>(ws) + 4 * 256 * sizeof(uint32_t));
+  int* blk = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + 4 * 256 * sizeof(uint32_t) + 256);
+  const int nb = tk_mb_blocks(n);
+  int* off = blk + 2 * nb;
+  const int seg = ((n + nb - 1) / nb + 63) / 64 * 64;  // block ranges start at multiples of 64
+  hipLaunchKernelGGL(tk_mb_init_kernel, dim3(1), dim3(TK_THREADS), 0, st, hist, state, k);
+  const int hist_blocks = std::min(4096, (n + 1023) / 1024);
+  for (int pass = 0; pass < 4; ++pass) {
+    hipLaunchKernelGGL(tk_mb_hist_kernel, dim3(hist_blocks), dim3(256), 0, st, dev, n, pass, state, hist);
+    hipLaunchKernelGGL(tk_mb_pick_kernel, dim3(1), dim3(256), 0, st, pass, state, hist);
+  }
+  hipLaunchKernelGGL(tk_mb_count_kernel, dim3(nb), dim3(TK_THREADS), 0, st, dev, n, seg, state, blk);
+  hipLaunchKernelGGL(tk_mb_scan_kernel, dim3(1), dim3(TK_THREADS), 0, st, nb, state, blk, off);
+  hipLaunchKernelGGL(tk_mb_write_kernel, dim3(nb), dim3(TK_THREADS), 0, st, dev, n, seg, state, off, k, out);
   return hipGetLastError();
 }
 

@@ -51,6 +51,9 @@ def test_topk_validation(L):
     good = (ctypes.c_int32 * 3)(0, 4, 10)
     assert L.cf_topk_select(None, 10, 3, 1, good, 2, None, None, 0, None) == cf.CF_EWORKSPACE
     assert cf.topk_workspace_size(10, "doc") >= 88 and cf.topk_workspace_size(10, "token") == 0
+    # token mode from n = 65536 on runs on the whole GPU and needs a workspace
+    assert cf.topk_workspace_size(65535, "token") == 0 and cf.topk_workspace_size(65536, "token") > 0
+    assert L.cf_topk_select(None, 1 << 20, 5, 0, None, 0, None, None, 0, None) == cf.CF_EWORKSPACE
 
 
 def test_deviation_validation(L):

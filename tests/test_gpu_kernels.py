@@ -114,6 +114,19 @@ def test_topk_bit_exact_vs_oracle(n):
                 assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (n, trial, k)
 
 
+@pytest.mark.parametrize("n", [(1 << 20) + 3, 3000017])
+def test_topk_large_n_multiblock_bit_exact(n):
+    """From n = 65536 on the selection runs on the whole GPU (histogram passes, block counts, a
+    scan and an ordered write); it must give the same unique answer as the oracle."""
+    rng = np.random.default_rng(n)
+    say(f"topk large n={n}")
+    for trial in range(2):
+        d = (rng.random(n).astype(np.float32) if trial == 0 else
+             rng.choice(np.array([0.0, -0.0, 1e-45, 0.5, 2.0, np.inf, np.nan], np.float32), n))
+        for k in sorted({1, n // 100, n // 2, n}):
+            assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (n, trial, k)
+
+
 @pytest.mark.parametrize("case", _golden.doc_span_cases())
 def test_doc_spans_golden(case):
     d, b, k, want = case
