@@ -182,6 +182,14 @@ def main():
                 ent.update(achieved=ach, unit="GB/s", peak=rl.HBM_PEAK_GBS, frac=ach / rl.HBM_PEAK_GBS,
                            algorithmic_bytes_per_step=work[name])
         kernels[name] = ent
+    # residual + RMSNorm steps, wherever they ran (a plain norm, or fused into a split-K reduction)
+    row_names = ("rmsnorm_rows", "reduce_resid_norm", "splitk_reduce")
+    r_ms = sum(v[1] for n, v in rep.items() if n in row_names)
+    if r_ms > 0:
+        ach = work["rows"] / (r_ms / P / 1e3) / 1e9
+        kernels["rows (" + " + ".join(row_names) + ")"] = {
+            "ms_per_step": r_ms / P, "achieved": ach, "unit": "GB/s", "peak": rl.HBM_PEAK_GBS,
+            "frac": ach / rl.HBM_PEAK_GBS, "algorithmic_bytes_per_step": work["rows"]}
     g_launch = sum(v[0] for n, v in rep.items() if n.startswith("gemm/"))
     g_ms = sum(v[1] for n, v in rep.items() if n.startswith("gemm/"))
     g_flops = rl.gemm_flops(work) * P

@@ -191,8 +191,14 @@ cf_status check_layer(const cf_ctx* c, const cf_layer_weights* w, int idx) {
 }
 
 // ------------------------------------------------------------------ one layer on rows `sel`
+// x_ready: the attention-norm input X of these rows is already in the workspace (written by the
+// previous layer on the same rows). next_norm: the next layer's attention-norm gain; when the down
+// projection is split along K, its reduction then also writes the next layer's X (bit-identical
+// to a separate normalisation) and *x_next is set.
 cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, void* kc, void* vc,
-                    const int* sel, int n, int L, char* ws, const LayerWs& lw, hipStream_t st) {
+                    const int* sel, int n, int L, char* ws, const LayerWs& lw, hipStream_t st,
+                    bool x_ready = false, const float* next_norm = nullptr, bool* x_next = nullptr) {
+  if (x_next) *x_next = false;
   if (n == 0) return CF_OK;
   const cf_model_cfg& m = c->cfg;
   const cf::Dt dt = dt_of(c);
@@ -205,7 +211,8 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   void* ACT = ws + lw.act;
 
   const LayerPlan& P = lw.plan;
-  CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, sel, n, L, d, w->attn_norm, m.rms_eps, X, d, st));
+  if (!x_ready)
+    CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, sel, n, L, d, w->attn_norm, m.rms_eps, X, d, st));
   cf::GemmArgs g{};
   g.dt = dt; g.cfg = P.qkv.cfg; g.splits = P.qkv.splits;
   g.A = X; g.lda = d;
@@ -244,7 +251,7 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   if (o.splits > 1) {
     o.epi = cf::EPI_PARTIAL; o.C = part; o.ldc = d;
     CF_RUN("gemm/o", cf::launch_gemm(o, st));
-    CF_RUN("reduce_resid_norm", cf::launch_reduce_resid_norm(dt, part, o.splits, n, d, hidden, sel, L, HS,
+    CF_RUN("reduce_resid_norm", cf::launch_reduce_resid_norm(dt, part, o.splits, n, d, hidden, sel, HS, nullptr, L,
                                                               w->mlp_norm, m.rms_eps, X, st));
   } else {
     o.epi = cf::EPI_RESID; o.resid = hidden; o.resid_rows = sel; o.out = HS; o.out_rows = nullptr;
@@ -270,7 +277,13 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   if (dn.splits > 1) {
     dn.epi = cf::EPI_PARTIAL; dn.C = part; dn.ldc = d;
     CF_RUN("gemm/down", cf::launch_gemm(dn, st));
-    CF_RUN("splitk_reduce", cf::launch_splitk_reduce(part, dn.splits, n, d, HS, nullptr, hidden, sel, L, st));
+    if (next_norm) {
+      CF_RUN("reduce_resid_norm", cf::launch_reduce_resid_norm(dt, part, dn.splits, n, d, HS, nullptr, hidden, sel, L,
+                                                                next_norm, m.rms_eps, X, st));
+      if (x_next) *x_next = true;
+    } else {
+      CF_RUN("splitk_reduce", cf::launch_splitk_reduce(part, dn.splits, n, d, HS, nullptr, hidden, sel, L, st));
+    }
   } else {
     dn.epi = cf::EPI_RESID; dn.resid = HS; dn.resid_rows = nullptr; dn.out = hidden; dn.out_rows = sel;
     CF_RUN("gemm/down", cf::launch_gemm(dn, st));
@@ -634,8 +647,15 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
       return s;
   CF_RUN("embed", cf::launch_embed(dt, tokens, L, embed, mc.vocab, mc.d_model, hidden, st));
   CF_RUN("iota", cf::launch_iota(ident, L, 0, st));
-  for (int l = 0; l < first_sel; ++l)
-    if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), ident, L, L, lws, lw_full, st)) return s;
+  // consecutive layers on the same rows hand the next attention-norm input over (see run_layer)
+  bool xr = false;
+  for (int l = 0; l < first_sel; ++l) {
+    const float* nn = l + 1 < first_sel ? layers[l + 1].attn_norm : nullptr;
+    bool xn = false;
+    if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), ident, L, L, lws, lw_full, st, xr, nn, &xn))
+      return s;
+    xr = xn;
+  }
 
   if (!full) {
     const cf_layer_weights* w = layers + s_layer;
@@ -666,8 +686,14 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
     }
     CF_RUN("iota", cf::launch_iota(sel + k, U, N, st));
     const LayerWs lw_sel = layer_ws(c, L, n_sel);
-    for (int l = s_layer; l < mc.n_layers; ++l)
-      if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st)) return s;
+    xr = false;
+    for (int l = s_layer; l < mc.n_layers; ++l) {
+      const float* nn = l + 1 < mc.n_layers ? layers[l + 1].attn_norm : nullptr;
+      bool xn = false;
+      if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st, xr, nn, &xn))
+        return s;
+      xr = xn;
+    }
   }
   if (U > 0)
     CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(cf::F32, hidden + (size_t)N * mc.d_model, nullptr, U, U, mc.d_model, final_norm,

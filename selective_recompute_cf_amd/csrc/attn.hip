@@ -26,27 +26,28 @@ constexpr int KB = 64;  // keys per step
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// One block = 128 query rows of one kv head (128/G selected rows x the G query heads), 8 waves
-// of 16 rows, so every K/V tile read from memory serves 128 rows. K and V tiles of 64 keys stream straight from global memory into a
-// ring of S LDS stages (global_load_lds_dwordx4 from inline assembly, as in the GEMM; M0 is set
-// right before each load and used by nothing else in the kernel): lane l of
-// a load lands in 16-byte slot l of a 1 KB row group, so the swizzle is applied on the global
-// side (the lane that fills chunk slot c' of key t fetches chunk c' ^ (t & SWM)). Per key block:
-// wait for this wave's loads of the block | barrier | load the block S - 1 ahead into the stage
-// the previous block used | S^T, softmax, O^T on the block.
+// One block = 128 query rows of one kv head (128/G selected rows x the G query heads), NW waves
+// of RG groups of 16 rows: every K/V fragment read from LDS serves the wave's RG row groups, and
+// every K/V tile read from memory serves the block's 128 rows. K and V tiles of 64 keys stream
+// straight from global memory into a ring of S LDS stages (global_load_lds_dwordx4 from inline
+// assembly, as in the GEMM; M0 is set right before each load and used by nothing else in the
+// kernel): lane l of a load lands in 16-byte slot l of a 1 KB row group, so the swizzle is
+// applied on the global side (the lane that fills chunk slot c' of key t fetches chunk
+// c' ^ (t & SWM)). Per key block: wait for this wave's loads of the block | barrier | load the
+// block S - 1 ahead into the stage the previous block used | S^T, softmax, O^T on the block.
 #define CF_ATTN_WAITCNT(vm) ((((vm) & 15) | (((vm) >> 4) << 14)) | 0x70 | (15 << 8))
 
-template <int HD>
-__global__ __launch_bounds__(512, 1) void attn_dtl_kernel(AttnArgs a) {
-  constexpr int NCH = HD / 8;     // 16-byte chunks per key row
-  constexpr int SWM = NCH - 1;    // chunk c of tile key t is stored at c ^ (t & SWM)
-  constexpr int S = 3;            // LDS stages
-  constexpr int TILE = KB * HD;   // elements of one K (or V) tile
-  constexpr int RPI = WAVE / NCH; // key rows per load instruction
+template <int HD, int NW, int RG, int S, int MINB>
+__global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
+  constexpr int NCH = HD / 8;       // 16-byte chunks per key row
+  constexpr int SWM = NCH - 1;      // chunk c of tile key t is stored at c ^ (t & SWM)
+  constexpr int TILE = KB * HD;     // elements of one K (or V) tile
+  constexpr int RPI = WAVE / NCH;   // key rows per load instruction
   constexpr int NI = 2 * KB / RPI;  // load instructions per key block (K then V)
-  constexpr int NW = 8;
-  constexpr int NL = NI / NW;     // per wave
+  constexpr int NL = NI / NW;       // per wave
+  static_assert(NW * RG * 16 == 128, "128 query rows per block");
   static_assert(NI % NW == 0, "load instructions must split over the waves");
+  static_assert(S >= 2 && (S - 2) * NL <= 63, "stages");
   __shared__ __attribute__((aligned(1024))) bf16 smem[S * 2 * TILE];
   const int G = a.hq / a.hkv;
   const int rpt = 128 / G;  // selected rows per block
@@ -57,29 +58,36 @@ __global__ __launch_bounds__(512, 1) void attn_dtl_kernel(AttnArgs a) {
   const int j0 = (q_tiles - 1 - lt % q_tiles) * rpt, split = (lt / q_tiles) % a.splits, g = lt / (q_tiles * a.splits);
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
   const int lg = lane / 16, lr = lane % 16;
-  const int r = w * 16 + lr;
-  const int jl = r / G, hl = r % G;
-  const int j = j0 + jl;
-  const bool row_ok = j < a.n;
-  const int jc = min(j, a.n - 1);
-  const int head = g * G + hl;
-  const int p = a.pos[jc];
   const int pmax = a.pos[min(j0 + rpt - 1, a.n - 1)];
   const int kvd = a.hkv * HD;
   const int kbeg = split * a.split_len;
   const int kend = min(min(pmax + 1, kbeg + a.split_len), a.L);
   const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
 
-  bf16x8 qf[HD / 32];
-  {
-    const bf16* qrow = (const bf16*)a.q + (int64_t)jc * a.ldq + head * HD;
+  // row group rg of this wave: block rows (w * RG + rg) * 16 + lr
+  int jrow[RG], head[RG], p[RG];
+  bf16x8 qf[RG][HD / 32];
 #pragma unroll
-    for (int kk = 0; kk < HD / 32; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * lg);
+  for (int rg = 0; rg < RG; ++rg) {
+    const int r = (w * RG + rg) * 16 + lr;
+    const int j = j0 + r / G;
+    jrow[rg] = j;
+    head[rg] = g * G + r % G;
+    const int jc = min(j, a.n - 1);
+    p[rg] = a.pos[jc];
+    const bf16* qrow = (const bf16*)a.q + (int64_t)jc * a.ldq + head[rg] * HD;
+#pragma unroll
+    for (int kk = 0; kk < HD / 32; ++kk) qf[rg][kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * lg);
   }
-  f32x4 o[HD / 16];
+  f32x4 o[RG][HD / 16];
+  float m_i[RG], l_i[RG];
 #pragma unroll
-  for (int nt = 0; nt < HD / 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_i = -INFINITY, l_i = 0.f;
+  for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+    for (int nt = 0; nt < HD / 16; ++nt) o[rg][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_i[rg] = -INFINITY;
+    l_i[rg] = 0.f;
+  }
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
 
   // load q of this wave: instruction gi = q * NW + w covers key rows [ii * RPI, ii * RPI + RPI)
@@ -120,57 +128,63 @@ __global__ __launch_bounds__(512, 1) void attn_dtl_kernel(AttnArgs a) {
     const bf16* Kt = smem + (it % S) * 2 * TILE;
     const bf16* Vt = Kt + TILE;
     const int kbase = kbeg + it * KB;
-    f32x4 s[4];
+    f32x4 s[RG][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) s[rg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int t = kt * 16 + lr;
 #pragma unroll
       for (int kk = 0; kk < HD / 32; ++kk) {
         const int c = kk * 4 + lg;
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Kt[t * HD + ((c ^ (t & SWM)) * 8)]);
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[kk], s[kt], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          s[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][kk], s[rg][kt], 0, 0, 0);
       }
     }
-    // s[kt][i] = S[row r][key kbase + 16kt + 4lg + i]
-    float mx = -INFINITY;
-    const int lim = min(p, kend - 1);  // last visible key of this row in this split
+    // s[rg][kt][i] = S[row of group rg][key kbase + 16kt + 4lg + i]
+    bf16x8 pf[RG][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int rg = 0; rg < RG; ++rg) {
+      float mx = -INFINITY;
+      const int lim = min(p[rg], kend - 1);  // last visible key of this row in this split
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kbase + kt * 16 + 4 * lg + i;
-        const float v = key <= lim ? s[kt][i] * sl2 : -INFINITY;
-        s[kt][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float m_new = fmaxf(m_i, mx);
-    const bool live = m_new != -INFINITY;
-    const float alpha = live ? exp2f(m_i - m_new) : 1.f;
-    float ps = 0.f;
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + kt * 16 + 4 * lg + i;
+          const float v = key <= lim ? s[rg][kt][i] * sl2 : -INFINITY;
+          s[rg][kt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float m_new = fmaxf(m_i[rg], mx);
+      const bool live = m_new != -INFINITY;
+      const float alpha = live ? exp2f(m_i[rg] - m_new) : 1.f;
+      float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = live ? exp2f(s[kt][i] - m_new) : 0.f;
-        s[kt][i] = e;
-        ps += e;
-      }
-    ps += __shfl_xor(ps, 16, WAVE);
-    ps += __shfl_xor(ps, 32, WAVE);
-    l_i = l_i * alpha + ps;
-    m_i = m_new;
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int nt = 0; nt < HD / 16; ++nt) o[nt] *= alpha;
-    bf16x8 pf[2];
+        for (int i = 0; i < 4; ++i) {
+          const float e = live ? exp2f(s[rg][kt][i] - m_new) : 0.f;
+          s[rg][kt][i] = e;
+          ps += e;
+        }
+      ps += __shfl_xor(ps, 16, WAVE);
+      ps += __shfl_xor(ps, 32, WAVE);
+      l_i[rg] = l_i[rg] * alpha + ps;
+      m_i[rg] = m_new;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm)
+      for (int nt = 0; nt < HD / 16; ++nt) o[rg][nt] *= alpha;
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp)
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pf[mm][tp * 4 + i] = (bf16)s[2 * mm + tp][i];
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pf[rg][mm][tp * 4 + i] = (bf16)s[rg][2 * mm + tp][i];
+    }
 #pragma unroll
     for (int nt = 0; nt < HD / 16; ++nt) {
 #pragma unroll
@@ -178,7 +192,9 @@ __global__ __launch_bounds__(512, 1) void attn_dtl_kernel(AttnArgs a) {
         const i16x4 lo = vread(Vt, 32 * mm + 4 * lg, nt);
         const i16x4 hi = vread(Vt, 32 * mm + 16 + 4 * lg, nt);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[mm], o[nt], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rg][mm], o[rg][nt], 0, 0, 0);
       }
     }
   };
@@ -199,30 +215,58 @@ __global__ __launch_bounds__(512, 1) void attn_dtl_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT(0));
   }
-  if (!row_ok) return;
-  // o[nt][i] = O[row r][hd 16nt + 4lg + i] (unnormalised)
-  if (a.splits > 1) {
-    float* op = a.o_part + (((int64_t)split * a.n + j) * a.hq + head) * HD;
+  // o[rg][nt][i] = O[row of group rg][hd 16nt + 4lg + i] (unnormalised)
 #pragma unroll
-    for (int nt = 0; nt < HD / 16; ++nt)
-      *reinterpret_cast<float4*>(op + nt * 16 + 4 * lg) = make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
-    if (lg == 0) {
-      float* ml = a.ml_part + (((int64_t)split * a.n + j) * a.hq + head) * 2;
-      ml[0] = m_i;
-      ml[1] = l_i;
-    }
-  } else {
-    const float inv = l_i > 0.f ? 1.0f / l_i : 0.f;
-    bf16* out = (bf16*)a.out + (int64_t)j * a.ldo + head * HD;
+  for (int rg = 0; rg < RG; ++rg) {
+    const int j = jrow[rg];
+    if (j >= a.n) continue;
+    if (a.splits > 1) {
+      float* op = a.o_part + (((int64_t)split * a.n + j) * a.hq + head[rg]) * HD;
 #pragma unroll
-    for (int nt = 0; nt < HD / 16; ++nt) {
-      bf16x4 v;
+      for (int nt = 0; nt < HD / 16; ++nt)
+        *reinterpret_cast<float4*>(op + nt * 16 + 4 * lg) =
+            make_float4(o[rg][nt][0], o[rg][nt][1], o[rg][nt][2], o[rg][nt][3]);
+      if (lg == 0) {
+        float* ml = a.ml_part + (((int64_t)split * a.n + j) * a.hq + head[rg]) * 2;
+        ml[0] = m_i[rg];
+        ml[1] = l_i[rg];
+      }
+    } else {
+      const float inv = l_i[rg] > 0.f ? 1.0f / l_i[rg] : 0.f;
+      bf16* out = (bf16*)a.out + (int64_t)j * a.ldo + head[rg] * HD;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[nt][i] * inv);
-      *reinterpret_cast<bf16x4*>(out + nt * 16 + 4 * lg) = v;
+      for (int nt = 0; nt < HD / 16; ++nt) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[rg][nt][i] * inv);
+        *reinterpret_cast<bf16x4*>(out + nt * 16 + 4 * lg) = v;
+      }
     }
   }
 }
+
+// Launch configuration: waves per block, 16-row groups per wave, LDS stages, blocks per CU.
+template <int NW, int RG, int S, int MINB>
+struct AttnCfg {
+  static constexpr int nw = NW, rg = RG, stages = S, minb = MINB;
+};
+
+template <class C>
+hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
+  const int G = a.hq / a.hkv, rpt = 128 / G;
+  dim3 grid(((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
+  if (a.hd == 128)
+    hipLaunchKernelGGL((attn_dtl_kernel<128, C::nw, C::rg, C::stages, C::minb>), grid, dim3(C::nw * WAVE), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_dtl_kernel<64, C::nw, C::rg, C::stages, C::minb>), grid, dim3(C::nw * WAVE), 0, st, a);
+  return hipGetLastError();
+}
+
+// split-KV launches (the selected rows of a blended layer): one 8-wave block per CU over a 3-stage
+// ring; unsplit launches (full causal layers, many query tiles): two blocks per CU over 2-stage
+// rings, whose phases interleave (measured faster on the 3136-row causal layer)
+using AttnSplit = AttnCfg<8, 1, 3, 1>;
+using AttnWide = AttnCfg<8, 1, 2, 2>;
 
 // Combine split-KV partials: weights 2^(m_s - max m) (scores are in log2 units).
 template <typename T>
@@ -323,16 +367,8 @@ void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* spli
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n == 0) return hipSuccess;
-  if (a.dt == BF16) {
-    const int G = a.hq / a.hkv, rpt = 128 / G;
-    dim3 grid(((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
-    if (a.hd == 128)
-      hipLaunchKernelGGL(attn_dtl_kernel<128>, grid, dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL(attn_dtl_kernel<64>, grid, dim3(512), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(attn_simple_kernel<float>, dim3(a.n), dim3(256), 0, st, a);
-  }
+  if (a.dt == BF16) return a.splits > 1 ? launch_attention_cfg<AttnSplit>(a, st) : launch_attention_cfg<AttnWide>(a, st);
+  hipLaunchKernelGGL(attn_simple_kernel<float>, dim3(a.n), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -47,12 +47,13 @@ hipError_t launch_copy_f32(float* dst, const float* src, int n, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, const float* resid,
                                 const int* resid_rows, float* out, const int* out_rows, int L,
                                 hipStream_t st);
+// Split-K reduction fused with the residual and the next RMSNorm:
+// out[out_rows[m]] = resid[resid_rows[m]] + sum_s part[s][m]; x[m] = RMSNorm(that row) * g (model
+// dtype); null row maps are the identity.
+hipError_t launch_reduce_resid_norm(Dt dt, const float* part, int splits, int M, int d, const float* resid,
+                                    const int* resid_rows, float* out, const int* out_rows, int L, const float* g,
+                                    float eps, void* x, hipStream_t st);
 // act[m][c] = silu(gu[m][c]) * gu[m][F + c]  (fp32 path)
-// Split-K reduction of the O projection fused with the residual and the MLP RMSNorm:
-// hs[m] = hidden[rows[m]] + sum_s part[s][m];  x[m] = RMSNorm(hs[m]) * g (model dtype).
-hipError_t launch_reduce_resid_norm(Dt dt, const float* part, int splits, int M, int d, const float* hidden,
-                                    const int* rows, int L, float* hs, const float* g, float eps, void* x,
-                                    hipStream_t st);
 hipError_t launch_swiglu(Dt dt, const float* gu, int M, int F, void* act, hipStream_t st);
 hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void* b, int64_t ldb,
                             float* dev, int n, int kvd, hipStream_t st);

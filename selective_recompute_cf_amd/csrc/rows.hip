@@ -280,26 +280,33 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, con
   return hipGetLastError();
 }
 
-// ----------------------------------------------------------------------------- O-proj reduce
+// ----------------------------------------------------------------------------- reduce + residual + norm
+// out[orow(m)] = resid[rrow(m)] + sum_s part[s][m]; x[m] = RMSNorm(out row) * g. Closes a split-K
+// projection and prepares the next bf16 GEMM input in one pass: after the O projection (residual
+// gathered from the selected rows, output h' dense, the MLP norm) and after the down projection
+// (residual h' dense, output scattered back to the selected rows, the next layer's attention norm).
 template <typename T>
 __global__ __launch_bounds__(256) void reduce_resid_norm_kernel(const float* __restrict__ part, int splits, int M, int d,
-                                                                const float* __restrict__ hidden,
-                                                                const int* __restrict__ rows, int L,
-                                                                float* __restrict__ hs, const float* __restrict__ g,
-                                                                float eps, T* __restrict__ x) {
+                                                                const float* __restrict__ resid,
+                                                                const int* __restrict__ rrows,
+                                                                float* __restrict__ out,
+                                                                const int* __restrict__ orows, int L,
+                                                                const float* __restrict__ g, float eps,
+                                                                T* __restrict__ x) {
   __shared__ float red[4];
   const int m = blockIdx.x;
-  const int64_t r = rows ? clampi(rows[m], 0, L - 1) : m;
+  const int64_t rr = rrows ? clampi(rrows[m], 0, L - 1) : m;
+  const int64_t orr = orows ? clampi(orows[m], 0, L - 1) : m;
   float ss = 0.f;
   for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
     float v[8], t[8];
-    load8(hidden + r * d + c, v);
+    load8(resid + rr * d + c, v);
     for (int s = 0; s < splits; ++s) {
       load8(part + ((int64_t)s * M + m) * d + c, t);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] += t[e];
     }
-    store8(hs + (int64_t)m * d + c, v);
+    store8(out + orr * d + c, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
   }
@@ -307,23 +314,23 @@ __global__ __launch_bounds__(256) void reduce_resid_norm_kernel(const float* __r
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
     float v[8], gg[8];
-    load8(hs + (int64_t)m * d + c, v);
+    load8(out + orr * d + c, v);
     load8(g + c, gg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * gg[e];
     store8(x + (int64_t)m * d + c, v);
   }
 }
-hipError_t launch_reduce_resid_norm(Dt dt, const float* part, int splits, int M, int d, const float* hidden,
-                                    const int* rows, int L, float* hs, const float* g, float eps, void* x,
-                                    hipStream_t st) {
+hipError_t launch_reduce_resid_norm(Dt dt, const float* part, int splits, int M, int d, const float* resid,
+                                    const int* resid_rows, float* out, const int* out_rows, int L, const float* g,
+                                    float eps, void* x, hipStream_t st) {
   if (M == 0) return hipSuccess;
   if (dt == BF16)
-    hipLaunchKernelGGL(reduce_resid_norm_kernel<bf16>, dim3(M), dim3(256), 0, st, part, splits, M, d, hidden, rows, L,
-                       hs, g, eps, (bf16*)x);
+    hipLaunchKernelGGL(reduce_resid_norm_kernel<bf16>, dim3(M), dim3(256), 0, st, part, splits, M, d, resid,
+                       resid_rows, out, out_rows, L, g, eps, (bf16*)x);
   else
-    hipLaunchKernelGGL(reduce_resid_norm_kernel<float>, dim3(M), dim3(256), 0, st, part, splits, M, d, hidden, rows,
-                       L, hs, g, eps, (float*)x);
+    hipLaunchKernelGGL(reduce_resid_norm_kernel<float>, dim3(M), dim3(256), 0, st, part, splits, M, d, resid,
+                       resid_rows, out, out_rows, L, g, eps, (float*)x);
   return hipGetLastError();
 }
 

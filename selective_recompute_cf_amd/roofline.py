@@ -101,8 +101,10 @@ def blend_step_work(s: Shape, N: int, U: int, k: int, sel_layer: int = 1, sel_po
     for l in range(s.n_layers):
         n = L if l < sel_layer else n_sel
         add("qkv_post", 4 * n * (s.qd + 2 * s.kvd) + s.eb * n * (s.qd + 2 * s.kvd))
-        add("rmsnorm_rows", 2 * (4 * n * s.d + s.eb * n * s.d))
-    add("rmsnorm_rows", 4 * N * s.d + s.eb * N * s.d + 2 * 4 * U * s.d)
+        # the two residual + RMSNorm steps of a layer (after the O and the down projection): read
+        # the projection result and the residual rows, write the new rows and the bf16 GEMM input
+        add("rows", 2 * n * s.d * (12 + s.eb))
+    add("rows", 4 * N * s.d + s.eb * N * s.d + 2 * 4 * U * s.d)  # selection-layer norm, final norm
     add("topk_token", 4 * N + 4 * k)
     add("embed", L * s.d * (s.eb + 4))
     return w
