@@ -13,6 +13,7 @@
 //
 // fp32 path: a plain LDS-tiled FMA GEMM (64x64x16), used for fp32 models.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -276,6 +277,15 @@ struct DtlCfg {
 // s_waitcnt immediate (gfx9 encoding): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
 #define CF_WAITCNT(vm, lgkm) ((((vm) & 15) | (((vm) >> 4) << 14)) | 0x70 | (((lgkm) & 15) << 8))
 
+// Scheduling pattern for NF LDS reads among NM MFMAs: read q is followed by MFMAs
+// [NM*q/NF, NM*(q+1)/NF) (the builtin needs constant arguments, hence the fold over q).
+template <int NM, int NF, int ID, int... Q>
+__device__ __forceinline__ void sched_interleave(std::integer_sequence<int, Q...>) {
+  ((__builtin_amdgcn_sched_group_barrier(0x100, 1, ID),
+    __builtin_amdgcn_sched_group_barrier(0x008, NM * (Q + 1) / NF - NM * Q / NF, ID)),
+   ...);
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a) {
   constexpr int BM = C::BM, BK = C::BK, FM = C::FM, FN = C::FN, S = C::S, NL = C::NL, W = C::W;
@@ -383,18 +393,24 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
     for (int p = 0; p < S - 1; ++p) issue(min(p, last));
     __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 15));
     barrier();
+    // The next slice's fragment reads are spread evenly between this slice's MFMAs (one LDS read,
+    // then its share of the NM MFMAs, repeated) rather than issued as one block ahead of them.
+    constexpr int NM = NSUB * FM * FN;
+    auto interleave = [](auto sync_id) __attribute__((always_inline)) {
+      sched_interleave<NM, NF, decltype(sync_id)::value>(std::make_integer_sequence<int, NF>{});
+    };
     FVec f0 = fread(0, 0), f1;
     for (int s = 0; s < nk; ++s) {
-      f1 = fread(s % S, 1);
       issue(min(s + S - 1, last));
-      __builtin_amdgcn_sched_barrier(0);
+      f1 = fread(s % S, 1);
       fmma(f0);
+      interleave(std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 0));
       barrier();
       f0 = fread((s + 1) % S, 0);
-      __builtin_amdgcn_sched_barrier(0);
       fmma(f1);
+      interleave(std::integral_constant<int, 1>{});
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(CF_WAITCNT(0, 0));  // drain the trailing repeat loads
