@@ -147,8 +147,9 @@ hipError_t launch_rmsnorm_rows(Dt out_dt, const float* x, const int* rows, int n
 }
 
 // ----------------------------------------------------------------------------- QKV post
-// One block per projected row. Wave w handles heads w, w+4, ...; lane j < hd/2 owns the RoPE
-// pair (j, j + hd/2) of its head. qk-norm (per-head RMS over hd) happens before RoPE, as in the
+// Store mode: block (row j, head group y), wave w handles head 4y + w, so every head's loads are
+// in flight at once. Deviation mode: one block per row, wave w handles heads w, w+4, ... (the
+// block sums the row's deviation). Lane j < hd/2 owns the RoPE pair (j, j + hd/2) of its head. qk-norm (per-head RMS over hd) happens before RoPE, as in the
 // decoder definition. In deviation mode (p.dev set) the rows hold K only and the rotated keys
 // are compared with the stitched keys instead of being stored (Request Order Matters Eq. 1).
 template <typename T>
@@ -175,7 +176,9 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
   const int koff = nq * hd, voff = koff + nkv * hd;
   const int qd = p.hq * hd, kvd = nkv * hd;
   float dacc = 0.f;
-  for (int h = w; h < nh; h += blockDim.x / WAVE) {
+  const int h0 = devmode ? w : blockIdx.y * (blockDim.x / WAVE) + w;
+  const int hstep = devmode ? blockDim.x / WAVE : nh;  // store mode: one head per wave
+  for (int h = h0; h < nh; h += hstep) {
     if (h < nq + nkv) {
       const bool isq = h < nq;
       const int hh = isq ? h : h - nq;
@@ -222,10 +225,12 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
 
 hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st) {
   if (p.n == 0) return hipSuccess;
+  const int nh = p.dev ? 1 : p.hq + 2 * p.hkv;
+  const dim3 grid(p.n, p.dev ? 1 : (nh + 3) / 4);
   if (dt == BF16)
-    hipLaunchKernelGGL(qkv_post_kernel<bf16>, dim3(p.n), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL(qkv_post_kernel<float>, dim3(p.n), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -293,12 +298,15 @@ __global__ __launch_bounds__(256) void reduce_resid_norm_kernel(const float* __r
                                                                 const int* __restrict__ orows, int L,
                                                                 const float* __restrict__ g, float eps,
                                                                 T* __restrict__ x) {
+  constexpr int KEEP = 4;  // chunks of 8 per thread kept in registers: rows up to 256 * 8 * 4 = 8192
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int64_t rr = rrows ? clampi(rrows[m], 0, L - 1) : m;
   const int64_t orr = orows ? clampi(orows[m], 0, L - 1) : m;
+  float keep[KEEP][8];
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+  int it = 0;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8, ++it) {
     float v[8], t[8];
     load8(resid + rr * d + c, v);
     for (int s = 0; s < splits; ++s) {
@@ -309,12 +317,21 @@ __global__ __launch_bounds__(256) void reduce_resid_norm_kernel(const float* __r
     store8(out + orr * d + c, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    if (it < KEEP)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keep[it < KEEP ? it : 0][e] = v[e];
   }
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+  it = 0;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8, ++it) {
     float v[8], gg[8];
-    load8(out + orr * d + c, v);
+    if (it < KEEP) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = keep[it < KEEP ? it : 0][e];
+    } else {
+      load8(out + orr * d + c, v);
+    }
     load8(g + c, gg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * gg[e];
