@@ -365,8 +365,9 @@ def gemm_traffic(alg_bytes_per_launch):
 
 def cpu_baseline(w, k):
     """The oracle (numpy, as written) on the host cores: blended prefill of the same request at full
-    width and length with 2 and with 4 layers; the per-layer cost of a selected-row layer is the
-    difference, extrapolated to the full depth. Chunk caches for the sample are prepared untimed."""
+    width and length with 2 and with 4 layers, three runs of each; the per-layer cost of a
+    selected-row layer is the difference of the medians, extrapolated to the full depth. Chunk
+    caches for the sample are prepared untimed."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
@@ -393,10 +394,14 @@ def cpu_baseline(w, k):
         ks, vs = np.concatenate(ks, 1), np.concatenate(vs, 1)
         spans = [i * w.chunk_len for i in range(w.n_chunks + 1)]
         times = {}
-        for ly in (2, 4):
-            t0 = time.perf_counter()
-            oracle.blend_prefill(model, toks, N, ks[:ly], vs[:ly], tab, w.sel_layer, k, w.mode, spans, np.float32, ly)
-            times[ly] = time.perf_counter() - t0
+        for ly in (2, 4):  # three runs of each depth (about 10 s of CPU work on a 16-core host); medians
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.blend_prefill(model, toks, N, ks[:ly], vs[:ly], tab, w.sel_layer, k, w.mode, spans, np.float32,
+                                     ly)
+                ts.append(time.perf_counter() - t0)
+            times[ly] = statistics.median(ts)
         per_layer = max(0.0, (times[4] - times[2]) / 2)
         t_full = times[2] + (cfg.n_layers - 2) * per_layer
     finally:
@@ -410,8 +415,8 @@ def cpu_baseline(w, k):
         pass
     log(f"[bench] CPU oracle: 2 layers {times[2]:.2f}s, 4 layers {times[4]:.2f}s -> {t_full:.1f}s extrapolated")
     return {"value": round(N / t_full, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{w.name}: oracle blend_prefill at full width and length timed with 2 and 4 layers "
-                       f"({times[2]:.2f}s, {times[4]:.2f}s); selected-row layer cost extrapolated to "
+            "sample": (f"{w.name}: oracle blend_prefill at full width and length timed with 2 and 4 layers, "
+                       f"3 runs each (medians {times[2]:.2f}s, {times[4]:.2f}s); selected-row layer cost extrapolated to "
                        f"{cfg.n_layers} layers = {t_full:.1f}s per request (extrapolated)"),
             "cpu_model": cpu_model}
 

@@ -6,9 +6,9 @@ Readings taken where the pages leave a step open (each is listed with its reason
 design notes of the repository):
 
 * selection layer ``s`` is a 0-based layer index; layers < s are recomputed on every row
-  (CacheBlend, "The Chicken-and-Egg Problem": fully prefill an early layer, pick its HKVD
-  tokens, reuse that set for the remaining layers; Request Order Matters §2.2: one
-  selection at a configured layer, no reranking),
+  (CacheBlend, "The Chicken-and-Egg Problem": one early layer runs over every row, its tokens
+  are ranked by KV deviation, and that set is kept for all later layers; Request Order
+  Matters §2.2: one selection at a configured layer, no reranking),
 * the deviation is the squared L2 norm of K only, over all kv heads and head dims
   (Request Order Matters §2.2 Eq. 1), accumulated in fp64 and returned as fp32,
 * budget k = max(1, floor(rho * N)) for rho > 0 and 0 for rho = 0, in integer arithmetic
