@@ -245,6 +245,210 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   }
 }
 
+// Pipelined variant: the barrier sits in the middle of a key block, after its S^T MFMAs, so the
+// next block's K fragments are read from LDS while this block's softmax runs. Per key block it:
+//   S^T MFMAs on the K fragments read during block it - 1
+//   wait for this wave's loads of block it + 1 | barrier
+//   load block it + S - 1 into the stage block it - 1 used | read block it + 1's K fragments
+//   softmax of block it | V^T reads and O^T MFMAs of block it
+// The barrier publishes block it + 1 (every wave waited for its own loads of it) and retires the
+// V reads of block it - 1, the last reads of the stage the new loads overwrite. S >= 3.
+template <int HD, int S, int MINB>
+__global__ __launch_bounds__(8 * WAVE, MINB) void attn_pipe_kernel(AttnArgs a) {
+  constexpr int NW = 8;
+  constexpr int NCH = HD / 8, SWM = NCH - 1, TILE = KB * HD, RPI = WAVE / NCH, NI = 2 * KB / RPI, NL = NI / NW;
+  static_assert(NI % NW == 0 && S >= 3 && (S - 3) * NL <= 63, "stages");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[S * 2 * TILE];
+  const int G = a.hq / a.hkv;
+  const int rpt = 128 / G;
+  const int q_tiles = (a.n + rpt - 1) / rpt;
+  const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
+  const int j0 = (q_tiles - 1 - lt % q_tiles) * rpt, split = (lt / q_tiles) % a.splits, g = lt / (q_tiles * a.splits);
+  const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
+  const int lg = lane / 16, lr = lane % 16;
+  const int pmax = a.pos[min(j0 + rpt - 1, a.n - 1)];
+  const int kvd = a.hkv * HD;
+  const int kbeg = split * a.split_len;
+  const int kend = min(min(pmax + 1, kbeg + a.split_len), a.L);
+  const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
+  const int r = w * 16 + lr;
+  const int j = j0 + r / G, head = g * G + r % G, jc = min(j, a.n - 1);
+  const int p = a.pos[jc];
+  bf16x8 qf[HD / 32];
+  {
+    const bf16* qrow = (const bf16*)a.q + (int64_t)jc * a.ldq + head * HD;
+#pragma unroll
+    for (int kk = 0; kk < HD / 32; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * lg);
+  }
+  f32x4 o[HD / 16];
+#pragma unroll
+  for (int nt = 0; nt < HD / 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_i = -INFINITY, l_i = 0.f;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
+  const bf16* src[NL];
+  int trow[NL];
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
+    const int t = ii * RPI + lane / NCH;
+    const int c = (lane % NCH) ^ (t & SWM);
+    src[q] = (const bf16*)(tensor ? a.v : a.k) + g * HD + c * 8;
+    trow[q] = t;
+  }
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    const int stage = step % S;
+    const int kbase = kbeg + step * KB;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
+      const bf16* gp = src[q] + (int64_t)min(kbase + trow[q], a.L - 1) * kvd;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          lds0 + 2u * (uint32_t)(stage * 2 * TILE + tensor * TILE + ii * RPI * HD));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(dst) : "memory", "m0");
+    }
+  };
+  typedef uint32_t KVec __attribute__((ext_vector_type(4 * 4 * (HD / 32))));  // the block's K fragments
+  auto kread = [&](int stage) __attribute__((always_inline)) {
+    const bf16* Kt = smem + stage * 2 * TILE;
+    KVec f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < HD / 32; ++kk) {
+        const int t = kt * 16 + lr, c = kk * 4 + lg;
+        const uint4 x = *reinterpret_cast<const uint4*>(&Kt[t * HD + ((c ^ (t & SWM)) * 8)]);
+        const int o4 = 4 * (kt * (HD / 32) + kk);
+        f[o4] = x.x, f[o4 + 1] = x.y, f[o4 + 2] = x.z, f[o4 + 3] = x.w;
+      }
+    return f;
+  };
+  auto vread = [&](const bf16* Vt, int kb, int nt) __attribute__((always_inline)) {
+    const int t = kb + lr / 4;
+    const int col = nt * 16 + 4 * (lr % 4);
+    const int c = col / 8;
+    const bf16* ptr = &Vt[t * HD + ((c ^ (t & SWM)) * 8) + (col % 8)];
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
+  };
+  auto barrier = []() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (nkb > 0) {
+    const int last = nkb - 1;
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q) issue(min(q, last));
+    __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT((S - 2) * NL));
+    barrier();
+    KVec kf = kread(0);
+    for (int it = 0; it < nkb; ++it) {
+      const int kbase = kbeg + it * KB;
+      f32x4 s[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < HD / 32; ++kk) {
+          const int o4 = 4 * (kt * (HD / 32) + kk);
+          const uint4 x = make_uint4(kf[o4], kf[o4 + 1], kf[o4 + 2], kf[o4 + 3]);
+          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), qf[kk], s[kt], 0, 0, 0);
+        }
+      }
+      // block it + 1 landed for this wave (loads of later blocks may stay in flight); lgkm drained
+      __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT((S - 3) * NL) & ~(15 << 8));
+      barrier();
+      issue(min(it + S - 1, last));
+      kf = kread((it + 1) % S);
+      const bf16* Vt = smem + (it % S) * 2 * TILE + TILE;
+      float mx = -INFINITY;
+      const int lim = min(p, kend - 1);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + kt * 16 + 4 * lg + i;
+          const float v = key <= lim ? s[kt][i] * sl2 : -INFINITY;
+          s[kt][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+      const float m_new = fmaxf(m_i, mx);
+      const bool live = m_new != -INFINITY;
+      const float alpha = live ? exp2f(m_i - m_new) : 1.f;
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = live ? exp2f(s[kt][i] - m_new) : 0.f;
+          s[kt][i] = e;
+          ps += e;
+        }
+      ps += __shfl_xor(ps, 16, WAVE);
+      ps += __shfl_xor(ps, 32, WAVE);
+      l_i = l_i * alpha + ps;
+      m_i = m_new;
+#pragma unroll
+      for (int nt = 0; nt < HD / 16; ++nt) o[nt] *= alpha;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pf[mm][tp * 4 + i] = (bf16)s[2 * mm + tp][i];
+#pragma unroll
+      for (int nt = 0; nt < HD / 16; ++nt) {
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const i16x4 lo = vread(Vt, 32 * mm + 4 * lg, nt);
+          const i16x4 hi = vread(Vt, 32 * mm + 16 + 4 * lg, nt);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[mm], o[nt], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT(0));
+  }
+  if (j >= a.n) return;
+  if (a.splits > 1) {
+    float* op = a.o_part + (((int64_t)split * a.n + j) * a.hq + head) * HD;
+#pragma unroll
+    for (int nt = 0; nt < HD / 16; ++nt)
+      *reinterpret_cast<float4*>(op + nt * 16 + 4 * lg) = make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
+    if (lg == 0) {
+      float* ml = a.ml_part + (((int64_t)split * a.n + j) * a.hq + head) * 2;
+      ml[0] = m_i;
+      ml[1] = l_i;
+    }
+  } else {
+    const float inv = l_i > 0.f ? 1.0f / l_i : 0.f;
+    bf16* out = (bf16*)a.out + (int64_t)j * a.ldo + head * HD;
+#pragma unroll
+    for (int nt = 0; nt < HD / 16; ++nt) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[nt][i] * inv);
+      *reinterpret_cast<bf16x4*>(out + nt * 16 + 4 * lg) = v;
+    }
+  }
+}
+
+template <int S, int MINB>
+hipError_t launch_attention_pipe(const AttnArgs& a, hipStream_t st) {
+  const int G = a.hq / a.hkv, rpt = 128 / G;
+  dim3 grid(((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
+  if (a.hd == 128)
+    hipLaunchKernelGGL((attn_pipe_kernel<128, S, MINB>), grid, dim3(8 * WAVE), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_pipe_kernel<64, S, MINB>), grid, dim3(8 * WAVE), 0, st, a);
+  return hipGetLastError();
+}
+
 // Launch configuration: waves per block, 16-row groups per wave, LDS stages, blocks per CU.
 template <int NW, int RG, int S, int MINB>
 struct AttnCfg {
@@ -262,10 +466,9 @@ hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// split-KV launches (the selected rows of a blended layer): one 8-wave block per CU over a 3-stage
-// ring; unsplit launches (full causal layers, many query tiles): two blocks per CU over 2-stage
-// rings, whose phases interleave (measured faster on the 3136-row causal layer)
-using AttnSplit = AttnCfg<8, 1, 3, 1>;
+// split-KV launches (the selected rows of a blended layer): the pipelined kernel, one block per CU
+// over a 4-stage ring; unsplit launches (full causal layers, many query tiles): two blocks per CU
+// over 2-stage rings, whose phases interleave (measured faster on the 3136-row causal layer)
 using AttnWide = AttnCfg<8, 1, 2, 2>;
 
 // Combine split-KV partials: weights 2^(m_s - max m) (scores are in log2 units).
@@ -367,7 +570,7 @@ void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* spli
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n == 0) return hipSuccess;
-  if (a.dt == BF16) return a.splits > 1 ? launch_attention_cfg<AttnSplit>(a, st) : launch_attention_cfg<AttnWide>(a, st);
+  if (a.dt == BF16) return a.splits > 1 ? launch_attention_pipe<4, 1>(a, st) : launch_attention_cfg<AttnWide>(a, st);
   hipLaunchKernelGGL(attn_simple_kernel<float>, dim3(a.n), dim3(256), 0, st, a);
   return hipGetLastError();
 }

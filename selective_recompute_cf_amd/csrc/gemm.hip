@@ -245,33 +245,43 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_kernel(GemmArgs
 // ----------------------------------------------------------------------------- direct-to-LDS
 // Ring of S LDS stages filled by direct global->LDS 16-byte loads (global_load_lds_dwordx4: lane
 // l of a wave writes bytes [16 l, 16 l + 16) after the wave-uniform LDS base), so the K steps in
-// flight cost no registers and no LDS store instructions. One wave instruction fills 8 tile rows
-// (8 lanes x 16 B per 128-byte row); the XOR swizzle is applied on the global side: the lane that
-// lands in chunk slot c' of row r fetches global chunk c' ^ (r & 7). Requires K % 64 == 0.
-// Per K step s:
-//   read slice 1 of step s | load step s + S - 1 into the stage step s - 1 used | MFMAs slice 0
+// flight cost no registers and no LDS store instructions. One wave instruction fills 1 KB: 8 tile
+// rows of 128 bytes (BK = 64) or 16 rows of 64 bytes (BK = 32). The XOR swizzle is applied on the
+// global side: the lane that lands in chunk slot c' of row r fetches global chunk c' ^ swz(r).
+// Requires K % BK == 0.
+// Each K step has two halves of BK/2 (one or two MFMA k sub-steps each). Per K step s:
+//   [S > 2: load step s + S - 1 into the stage of step s - 1] | read half 1 of step s | MFMAs half 0
 //   wait for this wave's loads of step s + 1 and its own LDS reads | barrier
-//   read slice 0 of step s + 1 | MFMAs slice 1
+//   [S = 2: load step s + 2 into the stage of step s] | read half 0 of step s + 1 | MFMAs half 1
 // The barrier publishes step s + 1 (every wave waited for its own loads of it) and retires all
-// reads of step s's stage before any wave issues the load that overwrites it (at step s + 1).
-template <int BM_, int BN_, int WGM_, int WGN_, int S_, int MINB_, int MT_ = 32>
+// reads of step s's stage before any wave issues the load that overwrites it.
+template <int BM_, int BN_, int WGM_, int WGN_, int S_, int MINB_, int MT_ = 32, int BK_ = 64>
 struct DtlCfg {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, S = S_, MINB = MINB_, SWZ = 0, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, S = S_, MINB = MINB_, SWZ = 0, BK = BK_;
   static constexpr int W = WGM * WGN, THREADS = W * WAVE;
   static constexpr int TM = BM / WGM, TN = BN / WGN;
-  // MFMA shape: MT = 32 (v_mfma_f32_32x32x16_bf16, k 16 per instruction, two per 32-wide k
-  // slice) or 16 (v_mfma_f32_16x16x32_bf16, one per slice).
-  static constexpr int MT = MT_, KI = MT == 32 ? 16 : 32, NSUB = 32 / KI;
+  // MFMA shape: MT = 32 (v_mfma_f32_32x32x16_bf16, k 16 per instruction) or 16
+  // (v_mfma_f32_16x16x32_bf16, k 32 per instruction)
+  static constexpr int MT = MT_, KI = MT == 32 ? 16 : 32;
+  static constexpr int HK = BK / 2, NSUB = HK / KI;  // k per half step; MFMA k sub-steps per half
+  static constexpr int CH = BK / 8;                  // 16-byte chunks per LDS row
+  static constexpr int RG = 512 / BK;                // rows per 1 KB load group
   static constexpr int FM = TM / MT, FN = TN / MT;
   typedef typename std::conditional<MT == 32, f32x16, f32x4>::type Acc;
-  static constexpr int G = (BM + BN) / 8;         // 8-row load groups per K step
-  static constexpr int NL = (G + W - 1) / W;      // load instructions per wave per K step
-  static constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
+  static constexpr int G = (BM + BN) / RG;         // load groups per K step
+  static constexpr int NL = (G + W - 1) / W;       // load instructions per wave per K step
+  static constexpr int STAGE = (BM + BN) * BK;     // bf16 elements per stage
   static_assert(MT == 16 || MT == 32, "MFMA tile edge");
+  static_assert(BK == 64 || BK == 32, "K step");
+  static_assert(NSUB >= 1, "a half step holds at least one MFMA k sub-step");
   static_assert(TM % MT == 0 && TN % MT == 0, "wave tile must be a multiple of the MFMA tile");
-  static_assert(BM % 8 == 0 && BN % 8 == 0 && NL * W - G <= W, "8-row load groups");
-  static_assert((S - 2) * NL <= 63, "in-flight loads must fit the vmcnt counter");
-  __device__ static __forceinline__ int swz(int r) { return r & 7; }
+  static_assert(BM % RG == 0 && BN % RG == 0 && NL * W - G <= W, "whole load groups");
+  static_assert(S >= 2 && (S - 1) * NL <= 63, "in-flight loads must fit the vmcnt counter");
+  // Conflict-free fragment reads: 8 or 16 consecutive lanes read consecutive rows at one logical
+  // chunk. 128-byte rows: r & 7 gives 8 consecutive rows 8 distinct chunks. 64-byte rows: rows
+  // r, r + 2, r + 4, r + 6 (same half of a 128-byte bank line) and r, r + 4, r + 8, r + 12 (same
+  // quarter of a 256-byte line) each get 4 distinct chunks.
+  __device__ static __forceinline__ int swz(int r) { return BK == 64 ? (r & 7) : (((r >> 1) ^ (r >> 3)) & 3); }
 };
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
@@ -303,17 +313,17 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
   const int k_end = min(a.K, k_begin + kps);
   const int nk = k_end > k_begin ? (k_end - k_begin) / BK : 0;
 
-  // load q of this wave covers combined tile rows [g*8, g*8 + 8), g = q*W + wave (A rows first,
-  // then B rows). When the groups do not split evenly over the waves, a wave's surplus slot
+  // load q of this wave covers combined tile rows [g*RG, (g + 1)*RG), g = q*W + wave (A rows
+  // first, then B rows). When the groups do not split evenly over the waves, a wave's surplus slot
   // repeats its previous group (same bytes to the same place), so every wave issues NL loads per
   // step and the wait counts hold for all of them.
   auto group = [&](int q) { const int g = q * W + wave; return g < C::G ? g : g - W; };
   const bf16* src[NL];
 #pragma unroll
   for (int q = 0; q < NL; ++q) {
-    const int row = group(q) * 8 + lane / 8;
+    const int row = group(q) * C::RG + lane / C::CH;
     const int r = row < BM ? row : row - BM;
-    const int c = (lane % 8) ^ C::swz(r);
+    const int c = (lane % C::CH) ^ C::swz(r);
     const bf16* base = row < BM ? (const bf16*)a.A + (int64_t)min(m0 + r, a.M - 1) * a.lda : b_row_ptr<C>(a, n_tile, r);
     src[q] = base + k_begin + c * 8;
   }
@@ -328,12 +338,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
     const int stage = step % S;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 2u * (uint32_t)(stage * C::STAGE + group(q) * 8 * BK));
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + 2u * (uint32_t)(stage * C::STAGE + group(q) * C::RG * BK));
       asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src[q] + step * BK), "s"(dst) : "memory", "m0");
     }
   };
 
-  // operands of one 32-wide k slice: NSUB sub-steps x (FM A + FN B) fragments of 8 bf16 per lane
+  // operands of one half step: NSUB sub-steps x (FM A + FN B) fragments of 8 bf16 per lane
   constexpr int NSUB = C::NSUB, MT = C::MT, NF = NSUB * (FM + FN);
   typedef uint32_t FVec __attribute__((ext_vector_type(4 * NF)));
   typedef uint32_t U4 __attribute__((ext_vector_type(4)));
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
     FVec f;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const int ch = kk * 4 + sub * (C::KI / 8) + lane / MT;
+      const int ch = kk * (C::HK / 8) + sub * (C::KI / 8) + lane / MT;
 #pragma unroll
       for (int q = 0; q < FM + FN; ++q) {
         const int r = q < FM ? wm * C::TM + q * MT + (lane % MT) : BM + wn * C::TN + (q - FM) * MT + (lane % MT);
@@ -387,13 +397,18 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
 
   if (nk > 0) {
     const int last = nk - 1;
-    // past the last step the loads repeat the last step into a stage nobody reads again, which
-    // keeps the per-step load count (and so the wait counts) uniform
+    // Two stages: a stage is refilled right after the barrier that retires its reads, which
+    // gives its load a whole step to land. More stages: it is refilled at the top of the next
+    // step (issuing right after the barrier delays the next half's fragment reads and measured
+    // slower), a load then has S - 1.5 steps to land.
+    constexpr bool EARLY = S == 2;
+    // past the last step the loads repeat the last step into its own stage (same bytes to the
+    // same place), which keeps the per-step load count (and so the wait counts) uniform
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p) issue(min(p, last));
-    __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 15));
+    for (int p = 0; p < (EARLY ? S : S - 1); ++p) issue(min(p, last));
+    __builtin_amdgcn_s_waitcnt(CF_WAITCNT((EARLY ? S - 1 : S - 2) * NL, 15));
     barrier();
-    // The next slice's fragment reads are spread evenly between this slice's MFMAs (one LDS read,
+    // The next half's fragment reads are spread evenly between this half's MFMAs (one LDS read,
     // then its share of the NM MFMAs, repeated) rather than issued as one block ahead of them.
     constexpr int NM = NSUB * FM * FN;
     auto interleave = [](auto sync_id) __attribute__((always_inline)) {
@@ -401,13 +416,14 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
     };
     FVec f0 = fread(0, 0), f1;
     for (int s = 0; s < nk; ++s) {
-      issue(min(s + S - 1, last));
+      if constexpr (!EARLY) issue(min(s + S - 1, last));  // the stage step s - 1 used
       f1 = fread(s % S, 1);
       fmma(f0);
       interleave(std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 0));
       barrier();
+      if constexpr (EARLY) issue(min(s + S, last));  // the stage step s used
       f0 = fread((s + 1) % S, 0);
       fmma(f1);
       interleave(std::integral_constant<int, 1>{});
@@ -440,6 +456,7 @@ using GemmSmall = TileCfg<128, 128, 2, 2, 2, 2>;  // register-staged, 2 blocks p
 using GemmDtl128 = DtlCfg<128, 256, 2, 4, 3, 1, 16>;  // waves 64x64, 3 x 48 KB stages
 using GemmDtl96 = DtlCfg<96, 256, 2, 4, 3, 1, 16>;    // waves 48x64, 3 x 44 KB stages
 using GemmDtl64 = DtlCfg<64, 256, 1, 8, 4, 1, 16>;    // waves 64x32, 4 x 40 KB stages
+using GemmDtl256 = DtlCfg<256, 256, 2, 4, 2, 1, 16>;  // waves 128x64, 2 x 64 KB stages (many rows)
 
 // ----------------------------------------------------------------------------- fp32 path
 __device__ __forceinline__ const float* b_row_ptr_f32(const GemmArgs& a, int col) {
@@ -510,11 +527,12 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
   // one 128-row block advancing one K column (about 0.12 ns on a full round); at about 5 TB/s
   // the 8 bytes of one partial element (written once, read once) cost 0.0131 units.
   struct Opt { int cfg, bm, per_cu; double rate; };
-  const Opt dtl_opts[3] = {{GEMM_DTL128, 128, 1, 1.0}, {GEMM_DTL96, 96, 1, 0.86}, {GEMM_DTL64, 64, 1, 0.75}};
+  const Opt dtl_opts[4] = {
+      {GEMM_DTL128, 128, 1, 1.0}, {GEMM_DTL96, 96, 1, 0.86}, {GEMM_DTL64, 64, 1, 0.75}, {GEMM_DTL256, 256, 1, 1.15}};
   const Opt small_opt[1] = {{GEMM_SMALL, 128, 2, 0.85}};
   const bool dtl = K % 64 == 0;
   const Opt* opts = dtl ? dtl_opts : small_opt;
-  const int n_opts = dtl ? 3 : 1;
+  const int n_opts = dtl ? 4 : 1;
   const int bn = dtl ? 256 : 128;
   const int cols = swiglu ? 2 * N : N;
   double best_cost = 1e300;
@@ -543,6 +561,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       case GEMM_DTL128: return launch_gemm_dtl<GemmDtl128>(a, st);
       case GEMM_DTL96: return launch_gemm_dtl<GemmDtl96>(a, st);
       case GEMM_DTL64: return launch_gemm_dtl<GemmDtl64>(a, st);
+      case GEMM_DTL256: return launch_gemm_dtl<GemmDtl256>(a, st);
       default: return launch_gemm_cfg<GemmSmall>(a, st);
     }
   }
