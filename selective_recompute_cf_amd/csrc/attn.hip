@@ -285,6 +285,11 @@ __global__ __launch_bounds__(8 * WAVE, MINB) void attn_pipe_kernel(AttnArgs a) {
   for (int nt = 0; nt < HD / 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_i = -INFINITY, l_i = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
+  // smallest position among the wave's 16 rows (lanes l, l + 16, l + 32, l + 48 share a row)
+  int p_min = p;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) p_min = min(p_min, __shfl_xor(p_min, off, WAVE));
+  p_min = __builtin_amdgcn_readfirstlane(p_min);
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
   const bf16* src[NL];
@@ -363,37 +368,52 @@ __global__ __launch_bounds__(8 * WAVE, MINB) void attn_pipe_kernel(AttnArgs a) {
       issue(min(it + S - 1, last));
       kf = kread((it + 1) % S);
       const bf16* Vt = smem + (it % S) * 2 * TILE + TILE;
+      // Scores stay unscaled; the running max m_i is kept in scaled (log2) units and each
+      // probability is exp2(score * sl2 - m) in one fused multiply-add. A key block that lies
+      // wholly below every row's position (and inside the split) needs no mask, and then every
+      // row has a finite maximum.
+      const bool unmasked = kbase + KB - 1 <= min(p_min, kend - 1);  // wave-uniform
+      if (!unmasked) {
+        const int lim = min(p, kend - 1) - kbase - 4 * lg;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kt * 16 + i > lim) s[kt][i] = -INFINITY;
+      }
       float mx = -INFINITY;
-      const int lim = min(p, kend - 1);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kbase + kt * 16 + 4 * lg + i;
-          const float v = key <= lim ? s[kt][i] * sl2 : -INFINITY;
-          s[kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float m_new = fmaxf(m_i, mx);
-      const bool live = m_new != -INFINITY;
-      const float alpha = live ? exp2f(m_i - m_new) : 1.f;
+      // The reference max moves only when a row's max grows by more than 8 (log2 units): the
+      // probabilities then stay below 2^8 (no overflow in fp32 or bf16), the result is the same
+      // softmax, and most steps skip rescaling the output accumulators. A row with no visible key
+      // yet (reference -inf) uses 0 for its exponents: its masked scores give exp2(-inf) = 0.
+      const float m_cand = fmaxf(m_i, mx * sl2);
+      const bool upd = m_cand > m_i + 8.f;
+      const float m_use = upd ? m_cand : m_i;
+      const float m_ref = m_use == -INFINITY ? 0.f : m_use;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_i - m_ref) : 1.f;  // exp2(-inf) = 0
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = live ? exp2f(s[kt][i] - m_new) : 0.f;
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_ref));
           s[kt][i] = e;
           ps += e;
         }
       ps += __shfl_xor(ps, 16, WAVE);
       ps += __shfl_xor(ps, 32, WAVE);
       l_i = l_i * alpha + ps;
-      m_i = m_new;
+      m_i = m_use;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
 #pragma unroll
-      for (int nt = 0; nt < HD / 16; ++nt) o[nt] *= alpha;
+        for (int nt = 0; nt < HD / 16; ++nt) o[nt] *= alpha;
+      }
       bf16x8 pf[2];
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
@@ -471,26 +491,32 @@ hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
 // over 2-stage rings, whose phases interleave (measured faster on the 3136-row causal layer)
 using AttnWide = AttnCfg<8, 1, 2, 2>;
 
-// Combine split-KV partials: weights 2^(m_s - max m) (scores are in log2 units).
+// Combine split-KV partials: weights 2^(m_s - max m) (scores are in log2 units). One thread per
+// 4 consecutive output elements of one (row, head): 16-byte partial loads, one 4-element store.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)a.n * a.hq * a.hd) return;
-  const int j = (int)(gid / (a.hq * a.hd));
-  {
-    const int idx = (int)(gid % (a.hq * a.hd));
-    const int head = idx / a.hd, d = idx % a.hd;
-    float mx = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.ml_part[(((int64_t)s * a.n + j) * a.hq + head) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float* ml = a.ml_part + (((int64_t)s * a.n + j) * a.hq + head) * 2;
-      const float wgt = ml[0] == -INFINITY ? 0.f : exp2f(ml[0] - mx);
-      num += wgt * a.o_part[(((int64_t)s * a.n + j) * a.hq + head) * a.hd + d];
-      den += wgt * ml[1];
-    }
-    ((T*)a.out)[(int64_t)j * a.ldo + idx] = from_f<T>(den > 0.f ? num / den : 0.f);
+  const unsigned q4 = (unsigned)a.hd / 4, per_row = (unsigned)a.hq * q4;
+  const unsigned gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (unsigned)a.n * per_row) return;
+  const int j = (int)(gid / per_row), idx = (int)(gid % per_row);
+  const int head = idx / (int)q4, d = (idx % (int)q4) * 4;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.ml_part[(((int64_t)s * a.n + j) * a.hq + head) * 2]);
+  float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const int64_t r = ((int64_t)s * a.n + j) * a.hq + head;
+    const float m = a.ml_part[r * 2], l = a.ml_part[r * 2 + 1];
+    const float wgt = m == -INFINITY ? 0.f : exp2f(m - mx);
+    const float4 o = *reinterpret_cast<const float4*>(a.o_part + r * a.hd + d);
+    n0 += wgt * o.x, n1 += wgt * o.y, n2 += wgt * o.z, n3 += wgt * o.w;
+    den += wgt * l;
   }
+  T* out = (T*)a.out + (int64_t)j * a.ldo + head * a.hd + d;
+  const bool ok = den > 0.f;
+  out[0] = from_f<T>(ok ? n0 / den : 0.f);
+  out[1] = from_f<T>(ok ? n1 / den : 0.f);
+  out[2] = from_f<T>(ok ? n2 / den : 0.f);
+  out[3] = from_f<T>(ok ? n3 / den : 0.f);
 }
 
 // ----------------------------------------------------------------------------- plain path
@@ -543,7 +569,7 @@ __global__ __launch_bounds__(256) void attn_simple_kernel(AttnArgs a) {
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st) {
   if (a.n == 0 || a.splits <= 1) return hipSuccess;
   {
-    const int64_t total = (int64_t)a.n * a.hq * a.hd;
+    const int64_t total = (int64_t)a.n * a.hq * (a.hd / 4);
     const dim3 grid((unsigned)((total + 255) / 256));
     if (a.dt == BF16)
       hipLaunchKernelGGL(attn_merge_kernel<bf16>, grid, dim3(256), 0, st, a);
