@@ -46,6 +46,15 @@ def overlap(a, b) -> float:
     return 1.0 if not a and not b else len(a & b) / max(len(a), 1)
 
 
+def selection_bar(sel16=None, sel32=None) -> float:
+    """Least overlap a GPU selection must have with the fp32 oracle's: 99%, or for bf16 models
+    the overlap that the oracle's own bf16-arithmetic run reaches minus 1% when that is lower
+    (which tokens sit at the top-k boundary is only fixed to within the arithmetic's rounding)."""
+    if sel16 is None:
+        return 0.99
+    return min(0.99, overlap(sel16, sel32) - 0.01)
+
+
 def context(cfg, max_pos, dtype=None):
     return cf.Context.from_model_cfg(cfg, max_pos=max_pos, dtype=dtype)
 

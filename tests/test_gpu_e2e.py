@@ -4,7 +4,8 @@ full recompute, deviation and selection on layer 1, selective recompute of the r
 
 Bars:
 * selection: the GPU's selected set equals the oracle's selection run on the GPU's own deviation
-  array (bit-exact) and overlaps the fp32 oracle's end-to-end selection by >= 99%;
+  array (bit-exact) and overlaps the fp32 oracle's end-to-end selection by >= 99% (bf16 models:
+  or by the overlap of the oracle's own bf16-arithmetic run minus 1%, when that is lower);
 * fp32 models: fused K/V and final normed query rows elementwise within 1e-4 + 1e-4 |ref|;
 * bf16 models: against the fp32 oracle, the norm-wise relative error of the final query rows, of
   the deviation and of the fused K/V (rows whose selection agrees) is at most twice the error
@@ -19,7 +20,7 @@ import pytest
 import oracle
 import synth
 from selective_recompute_cf_amd.device import DeviceModel
-from tests._gpu import compare, context, gpu_blend, gpu_chunk_store, host, overlap, say
+from tests._gpu import compare, context, gpu_blend, gpu_chunk_store, host, overlap, say, selection_bar
 
 pytestmark = pytest.mark.gpu
 
@@ -88,7 +89,7 @@ def _check(w, g, r32, r16, mode=None):
     ov = overlap(g["sel"], r32.sel)
     say(f"  selection overlap with fp32 oracle {ov:.4f} ({len(r32.sel)} tokens)"
         + ("" if r16 is None else f"; bf16-arithmetic oracle's own overlap {overlap(r16.sel, r32.sel):.4f}"))
-    assert ov >= 0.99
+    assert ov >= selection_bar(None if r16 is None else r16.sel, r32.sel)
     shape = g["k"].shape
     if r16 is None:  # fp32 model: fixed elementwise bar
         compare("dev", g["dev"], r32.dev, atol=1e-4 * float(np.median(r32.dev)), rtol=1e-3)

@@ -9,7 +9,8 @@ Pins:
   position, and its base position is that window position;
 * step-local parity at 0 < rho < 1: the oracle is fed the GPU's store state before each step
   (caches and base positions) and must reproduce the step: selection bit-exact on the GPU's own
-  deviation and >= 99% overlap with the oracle's selection; fused K/V and the normed query rows
+  deviation and >= 99% overlap with the oracle's selection (bf16: or the bf16-arithmetic oracle's
+  own overlap minus 1%, when lower); fused K/V and the normed query rows
   within the fp32 bound (tiny fp32 model) or the calibrated bf16 bound (Llama-3-8B width)."""
 import numpy as np
 import pytest
@@ -18,7 +19,7 @@ import oracle
 import synth
 from selective_recompute_cf_amd.device import DeviceModel
 from selective_recompute_cf_amd.rolling import RollingWindow
-from tests._gpu import compare, context, host, overlap, say
+from tests._gpu import compare, context, host, overlap, say, selection_bar
 
 pytestmark = pytest.mark.gpu
 
@@ -153,8 +154,9 @@ def test_write_back_step_local_parity_llama8b_width():
         bounds = [i * rw.doc_len for i in range(rw.n_docs + 1)]
         np.testing.assert_array_equal(sel, oracle.select_doc_spans(host(rw.dev), rw.k, bounds))
         ov = overlap(sel, r32.sel)
-        say(f"rolling llama8b-width step {step}: sources {[t[1] for t in table]}, k={rw.k}, overlap {ov:.3f}")
-        assert ov >= 0.99
+        say(f"rolling llama8b-width step {step}: sources {[t[1] for t in table]}, k={rw.k}, overlap {ov:.3f}; "
+            f"bf16-arithmetic oracle's own {overlap(r16.sel, r32.sel):.3f}")
+        assert ov >= selection_bar(r16.sel, r32.sel)
         for name, g, o16, o32 in (("out", host(rw.out), r16.out, r32.out), ("dev", host(rw.dev), r16.dev, r32.dev)):
             e_gpu, e_ref = _nrel(g, o32), _nrel(o16, o32)
             bound = 2.0 * e_ref + 2e-3
