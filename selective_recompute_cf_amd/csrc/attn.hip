@@ -89,6 +89,13 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
     l_i[rg] = 0.f;
   }
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
+  // smallest position among the wave's rows (lanes l, l + 16, l + 32, l + 48 share a row)
+  int p_min = p[0];
+#pragma unroll
+  for (int rg = 1; rg < RG; ++rg) p_min = min(p_min, p[rg]);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) p_min = min(p_min, __shfl_xor(p_min, off, WAVE));
+  p_min = __builtin_amdgcn_readfirstlane(p_min);
 
   // load q of this wave: instruction gi = q * NW + w covers key rows [ii * RPI, ii * RPI + RPI)
   // of tensor gi / (NI / 2) (0 = K, 1 = V), ii = gi % (NI / 2)
@@ -143,41 +150,50 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
           s[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][kk], s[rg][kt], 0, 0, 0);
       }
     }
-    // s[rg][kt][i] = S[row of group rg][key kbase + 16kt + 4lg + i]
+    // s[rg][kt][i] = S[row of group rg][key kbase + 16kt + 4lg + i]. Softmax as in the pipelined
+    // kernel: unscaled scores, masks only on blocks that reach past a row of the wave, exp2 of
+    // one fused multiply-add, and a reference max that moves only on growth above 8 (log2).
     bf16x8 pf[RG][2];
+    const bool unmasked = kbase + KB - 1 <= min(p_min, kend - 1);  // wave-uniform
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
+      if (!unmasked) {
+        const int lim = min(p[rg], kend - 1) - kbase - 4 * lg;  // last visible key, block-relative
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kt * 16 + i > lim) s[rg][kt][i] = -INFINITY;
+      }
       float mx = -INFINITY;
-      const int lim = min(p[rg], kend - 1);  // last visible key of this row in this split
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kbase + kt * 16 + 4 * lg + i;
-          const float v = key <= lim ? s[rg][kt][i] * sl2 : -INFINITY;
-          s[rg][kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rg][kt][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float m_new = fmaxf(m_i[rg], mx);
-      const bool live = m_new != -INFINITY;
-      const float alpha = live ? exp2f(m_i[rg] - m_new) : 1.f;
+      const float m_cand = fmaxf(m_i[rg], mx * sl2);
+      const bool upd = m_cand > m_i[rg] + 8.f;
+      const float m_use = upd ? m_cand : m_i[rg];
+      const float m_ref = m_use == -INFINITY ? 0.f : m_use;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_i[rg] - m_ref) : 1.f;
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = live ? exp2f(s[rg][kt][i] - m_new) : 0.f;
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[rg][kt][i], sl2, -m_ref));
           s[rg][kt][i] = e;
           ps += e;
         }
       ps += __shfl_xor(ps, 16, WAVE);
       ps += __shfl_xor(ps, 32, WAVE);
       l_i[rg] = l_i[rg] * alpha + ps;
-      m_i[rg] = m_new;
+      m_i[rg] = m_use;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
 #pragma unroll
-      for (int nt = 0; nt < HD / 16; ++nt) o[rg][nt] *= alpha;
+        for (int nt = 0; nt < HD / 16; ++nt) o[rg][nt] *= alpha;
+      }
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
