@@ -106,7 +106,7 @@ size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 // ------------------------------------------------------------------ workspace of one layer pass
 struct LayerPlan {
   cf::GemmPlan qkv, o, gu, down, ksel;
-  int attn_splits, attn_split_len;
+  int attn_splits, attn_split_len, attn_P;
 };
 
 LayerPlan layer_plan(const cf_ctx* c, int L, int R, int ksel_rows) {
@@ -119,12 +119,13 @@ LayerPlan layer_plan(const cf_ctx* c, int L, int R, int ksel_rows) {
   p.gu = cf::gemm_plan(dt, R, F, d, true, false, c->n_cu);
   p.down = cf::gemm_plan(dt, R, d, F, false, true, c->n_cu);
   p.ksel = cf::gemm_plan(dt, ksel_rows, kvd, d, false, true, c->n_cu);
-  cf::attn_plan(dt, R, L, m.n_q_heads, m.n_kv_heads, m.head_dim, c->n_cu, &p.attn_splits, &p.attn_split_len);
+  cf::attn_plan(dt, R, L, m.n_q_heads, m.n_kv_heads, m.head_dim, c->n_cu, &p.attn_splits, &p.attn_split_len,
+                &p.attn_P);
   return p;
 }
 
 struct LayerWs {
-  size_t x, qkv, q, ao, hs, act, gu, part, opart, mlpart, total;
+  size_t x, qkv, q, ao, hs, act, gu, part, opart, mlpart, sched, total;
   LayerPlan plan;
 };
 
@@ -149,8 +150,11 @@ LayerWs layer_ws(const cf_ctx* c, int L, int R, int ksel_rows = 0) {
   w.gu = take(m.dtype == CF_BF16 ? 0 : (size_t)R * 2 * F * 4);
   const int ps = std::max(p.o.splits, p.down.splits);
   w.part = take(ps > 1 ? (size_t)ps * R * d * 4 : 0);
-  w.opart = take(p.attn_splits > 1 ? (size_t)p.attn_splits * R * qd * 4 : 0);
-  w.mlpart = take(p.attn_splits > 1 ? (size_t)p.attn_splits * R * m.n_q_heads * 2 * 4 : 0);
+  // attention partial sums: split-KV [splits][R][hq][hd] or balanced pieces [hkv][P][128][hd]
+  const size_t pieces = (size_t)m.n_kv_heads * p.attn_P * 128;
+  w.opart = take(std::max(p.attn_splits > 1 ? (size_t)p.attn_splits * R * qd : 0, pieces * m.head_dim) * 4);
+  w.mlpart = take(std::max(p.attn_splits > 1 ? (size_t)p.attn_splits * R * m.n_q_heads : 0, pieces) * 2 * 4);
+  w.sched = take(p.attn_P > 0 ? sizeof(cf::AttnSched) : 0);
   w.total = off;
   return w;
 }
@@ -197,7 +201,8 @@ cf_status check_layer(const cf_ctx* c, const cf_layer_weights* w, int idx) {
 // to a separate normalisation) and *x_next is set.
 cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, void* kc, void* vc,
                     const int* sel, int n, int L, char* ws, const LayerWs& lw, hipStream_t st,
-                    bool x_ready = false, const float* next_norm = nullptr, bool* x_next = nullptr) {
+                    bool x_ready = false, const float* next_norm = nullptr, bool* x_next = nullptr,
+                    bool* sched_ready = nullptr) {
   if (x_next) *x_next = false;
   if (n == 0) return CF_OK;
   const cf_model_cfg& m = c->cfg;
@@ -235,8 +240,16 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   at.splits = P.attn_splits; at.split_len = P.attn_split_len;
   at.o_part = reinterpret_cast<float*>(ws + lw.opart);
   at.ml_part = reinterpret_cast<float*>(ws + lw.mlpart);
+  if (P.attn_P > 0) {
+    // the pieces depend only on the rows' positions: built once for layers that share `sel`
+    cf::AttnSched* sch = reinterpret_cast<cf::AttnSched*>(ws + lw.sched);
+    at.P = P.attn_P;
+    if (!sched_ready || !*sched_ready) CF_RUN("attn_sched", cf::launch_attention_sched(at, sch, st));
+    if (sched_ready) *sched_ready = true;
+    at.sched = sch;
+  }
   CF_RUN("attention", cf::launch_attention(at, st));
-  if (at.splits > 1) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
+  if (at.splits > 1 || at.sched) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
 
   float* part = reinterpret_cast<float*>(ws + lw.part);
   auto proj = [&](const cf::GemmPlan& pl, const void* A, int lda, const void* B, int K) {
@@ -648,11 +661,12 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
   CF_RUN("embed", cf::launch_embed(dt, tokens, L, embed, mc.vocab, mc.d_model, hidden, st));
   CF_RUN("iota", cf::launch_iota(ident, L, 0, st));
   // consecutive layers on the same rows hand the next attention-norm input over (see run_layer)
-  bool xr = false;
+  bool xr = false, sched_full = false;
   for (int l = 0; l < first_sel; ++l) {
     const float* nn = l + 1 < first_sel ? layers[l + 1].attn_norm : nullptr;
     bool xn = false;
-    if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), ident, L, L, lws, lw_full, st, xr, nn, &xn))
+    if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), ident, L, L, lws, lw_full, st, xr, nn, &xn,
+                                &sched_full))
       return s;
     xr = xn;
   }
@@ -687,10 +701,12 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
     CF_RUN("iota", cf::launch_iota(sel + k, U, N, st));
     const LayerWs lw_sel = layer_ws(c, L, n_sel);
     xr = false;
+    bool sched_sel = false;
     for (int l = s_layer; l < mc.n_layers; ++l) {
       const float* nn = l + 1 < mc.n_layers ? layers[l + 1].attn_norm : nullptr;
       bool xn = false;
-      if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st, xr, nn, &xn))
+      if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st, xr, nn, &xn,
+                                  &sched_sel))
         return s;
       xr = xn;
     }

@@ -54,14 +54,31 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   // logical tile: query tile fastest (latest rows, which see the most keys, first), then split,
   // then kv head; xcd_tile keeps each kv head's tiles on one XCD
   const int q_tiles = (a.n + rpt - 1) / rpt;
-  const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
-  const int j0 = (q_tiles - 1 - lt % q_tiles) * rpt, split = (lt / q_tiles) % a.splits, g = lt / (q_tiles * a.splits);
+  // the block's query tile j0.., kv head g, key range [kbeg, kend) and where its result goes
+  // (as in the pipelined kernel): piece or split-KV slot, else the normalised output
+  int j0, g, kbeg, kend, piece = -1, split = -1;
+  if (a.sched) {  // balanced pieces: blocks t * hkv + g
+    g = blockIdx.x % a.hkv;
+    const int t = blockIdx.x / a.hkv;
+    if (t >= a.sched->T) return;  // block-uniform
+    const int qt = a.sched->piece_qt[t], chunk = a.sched->chunk;
+    const int kb0 = (t - a.sched->off[qt]) * chunk, kb1 = min(kb0 + chunk, a.sched->c[qt]);
+    j0 = qt * rpt;
+    kbeg = kb0 * KB;
+    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kb1 * KB), a.L);
+    if (a.sched->off[qt + 1] - a.sched->off[qt] > 1) piece = t;
+  } else {
+    const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
+    j0 = (q_tiles - 1 - lt % q_tiles) * rpt;
+    const int sp = (lt / q_tiles) % a.splits;
+    g = lt / (q_tiles * a.splits);
+    kbeg = sp * a.split_len;
+    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kbeg + a.split_len), a.L);
+    if (a.splits > 1) split = sp;
+  }
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
   const int lg = lane / 16, lr = lane % 16;
-  const int pmax = a.pos[min(j0 + rpt - 1, a.n - 1)];
   const int kvd = a.hkv * HD;
-  const int kbeg = split * a.split_len;
-  const int kend = min(min(pmax + 1, kbeg + a.split_len), a.L);
   const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
 
   // row group rg of this wave: block rows (w * RG + rg) * 16 + lr
@@ -236,14 +253,16 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   for (int rg = 0; rg < RG; ++rg) {
     const int j = jrow[rg];
     if (j >= a.n) continue;
-    if (a.splits > 1) {
-      float* op = a.o_part + (((int64_t)split * a.n + j) * a.hq + head[rg]) * HD;
+    if (piece >= 0 || split >= 0) {
+      const int64_t slot = piece >= 0 ? ((int64_t)g * a.P + piece) * 128 + (w * RG + rg) * 16 + lr
+                                      : ((int64_t)split * a.n + j) * a.hq + head[rg];
+      float* op = a.o_part + slot * HD;
 #pragma unroll
       for (int nt = 0; nt < HD / 16; ++nt)
         *reinterpret_cast<float4*>(op + nt * 16 + 4 * lg) =
             make_float4(o[rg][nt][0], o[rg][nt][1], o[rg][nt][2], o[rg][nt][3]);
       if (lg == 0) {
-        float* ml = a.ml_part + (((int64_t)split * a.n + j) * a.hq + head[rg]) * 2;
+        float* ml = a.ml_part + slot * 2;
         ml[0] = m_i[rg];
         ml[1] = l_i[rg];
       }
@@ -278,14 +297,32 @@ __global__ __launch_bounds__(8 * WAVE, MINB) void attn_pipe_kernel(AttnArgs a) {
   const int G = a.hq / a.hkv;
   const int rpt = 128 / G;
   const int q_tiles = (a.n + rpt - 1) / rpt;
-  const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
-  const int j0 = (q_tiles - 1 - lt % q_tiles) * rpt, split = (lt / q_tiles) % a.splits, g = lt / (q_tiles * a.splits);
+  // the block's query tile j0.., kv head g, key range [kbeg, kend) and where its result goes:
+  // piece >= 0 writes partial sums to piece slot `piece`, split >= 0 to split-KV slot `split`,
+  // both negative writes the normalised output
+  int j0, g, kbeg, kend, piece = -1, split = -1;
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
   const int lg = lane / 16, lr = lane % 16;
-  const int pmax = a.pos[min(j0 + rpt - 1, a.n - 1)];
+  if (a.sched) {  // balanced pieces: blocks t * hkv + g (the kv heads spread over the XCDs)
+    g = blockIdx.x % a.hkv;
+    const int t = blockIdx.x / a.hkv;
+    if (t >= a.sched->T) return;  // block-uniform: no piece for this block
+    const int qt = a.sched->piece_qt[t], chunk = a.sched->chunk;
+    const int kb0 = (t - a.sched->off[qt]) * chunk, kb1 = min(kb0 + chunk, a.sched->c[qt]);
+    j0 = qt * rpt;
+    kbeg = kb0 * KB;
+    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kb1 * KB), a.L);
+    if (a.sched->off[qt + 1] - a.sched->off[qt] > 1) piece = t;
+  } else {
+    const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
+    j0 = (q_tiles - 1 - lt % q_tiles) * rpt;
+    const int sp = (lt / q_tiles) % a.splits;
+    g = lt / (q_tiles * a.splits);
+    kbeg = sp * a.split_len;
+    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kbeg + a.split_len), a.L);
+    if (a.splits > 1) split = sp;
+  }
   const int kvd = a.hkv * HD;
-  const int kbeg = split * a.split_len;
-  const int kend = min(min(pmax + 1, kbeg + a.split_len), a.L);
   const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
   const int r = w * 16 + lr;
   const int j = j0 + r / G, head = g * G + r % G, jc = min(j, a.n - 1);
@@ -451,13 +488,14 @@ __global__ __launch_bounds__(8 * WAVE, MINB) void attn_pipe_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT(0));
   }
   if (j >= a.n) return;
-  if (a.splits > 1) {
-    float* op = a.o_part + (((int64_t)split * a.n + j) * a.hq + head) * HD;
+  if (piece >= 0 || split >= 0) {
+    const int64_t slot = piece >= 0 ? ((int64_t)g * a.P + piece) * 128 + r : ((int64_t)split * a.n + j) * a.hq + head;
+    float* op = a.o_part + slot * HD;
 #pragma unroll
     for (int nt = 0; nt < HD / 16; ++nt)
       *reinterpret_cast<float4*>(op + nt * 16 + 4 * lg) = make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
     if (lg == 0) {
-      float* ml = a.ml_part + (((int64_t)split * a.n + j) * a.hq + head) * 2;
+      float* ml = a.ml_part + slot * 2;
       ml[0] = m_i;
       ml[1] = l_i;
     }
@@ -477,7 +515,7 @@ __global__ __launch_bounds__(8 * WAVE, MINB) void attn_pipe_kernel(AttnArgs a) {
 template <int S, int MINB>
 hipError_t launch_attention_pipe(const AttnArgs& a, hipStream_t st) {
   const int G = a.hq / a.hkv, rpt = 128 / G;
-  dim3 grid(((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
+  dim3 grid(a.sched ? a.P * a.hkv : ((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
   if (a.hd == 128)
     hipLaunchKernelGGL((attn_pipe_kernel<128, S, MINB>), grid, dim3(8 * WAVE), 0, st, a);
   else
@@ -494,7 +532,7 @@ struct AttnCfg {
 template <class C>
 hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
   const int G = a.hq / a.hkv, rpt = 128 / G;
-  dim3 grid(((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
+  dim3 grid(a.sched ? a.P * a.hkv : ((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
   if (a.hd == 128)
     hipLaunchKernelGGL((attn_dtl_kernel<128, C::nw, C::rg, C::stages, C::minb>), grid, dim3(C::nw * WAVE), 0, st, a);
   else
@@ -502,9 +540,10 @@ hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// split-KV launches (the selected rows of a blended layer): the pipelined kernel, one block per CU
-// over a 4-stage ring; unsplit launches (full causal layers, many query tiles): two blocks per CU
-// over 2-stage rings, whose phases interleave (measured faster on the 3136-row causal layer)
+// Unsplit launches (full causal layers, many query tiles) and balanced pieces (the selected rows of
+// a blended layer): two blocks per CU over 2-stage rings, whose phases interleave (measured faster
+// on both). Split-KV launches (only where balanced pieces do not fit: kv heads that do not divide
+// the CU count): the pipelined kernel, one block per CU over a 4-stage ring.
 using AttnWide = AttnCfg<8, 1, 2, 2>;
 
 // Combine split-KV partials: weights 2^(m_s - max m) (scores are in log2 units). One thread per
@@ -516,11 +555,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (gid >= (unsigned)a.n * per_row) return;
   const int j = (int)(gid / per_row), idx = (int)(gid % per_row);
   const int head = idx / (int)q4, d = (idx % (int)q4) * 4;
+  // slot of part s of this row: split s, or piece off[qt] + s of its query tile
+  int parts = a.splits;
+  int64_t base = (int64_t)j * a.hq + head, stride = (int64_t)a.n * a.hq;
+  if (a.sched) {
+    const int G = a.hq / a.hkv, rpt = 128 / G, qt = j / rpt;
+    const int first = a.sched->off[qt];
+    parts = a.sched->off[qt + 1] - first;
+    if (parts <= 1) return;  // a single piece wrote the normalised output itself
+    base = ((int64_t)(head / G) * a.P + first) * 128 + (j % rpt) * G + head % G;
+    stride = 128;
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.ml_part[(((int64_t)s * a.n + j) * a.hq + head) * 2]);
+  for (int s = 0; s < parts; ++s) mx = fmaxf(mx, a.ml_part[(base + s * stride) * 2]);
   float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const int64_t r = ((int64_t)s * a.n + j) * a.hq + head;
+  for (int s = 0; s < parts; ++s) {
+    const int64_t r = base + s * stride;
     const float m = a.ml_part[r * 2], l = a.ml_part[r * 2 + 1];
     const float wgt = m == -INFINITY ? 0.f : exp2f(m - mx);
     const float4 o = *reinterpret_cast<const float4*>(a.o_part + r * a.hd + d);
@@ -583,7 +633,7 @@ __global__ __launch_bounds__(256) void attn_simple_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st) {
-  if (a.n == 0 || a.splits <= 1) return hipSuccess;
+  if (a.n == 0 || (a.splits <= 1 && !a.sched)) return hipSuccess;
   {
     const int64_t total = (int64_t)a.n * a.hq * (a.hd / 4);
     const dim3 grid((unsigned)((total + 255) / 256));
@@ -595,9 +645,57 @@ hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len) {
+// One workgroup: key blocks per query tile, then the smallest piece length (in key blocks) whose
+// pieces fit in P blocks per kv head, then the piece table. The query tiles of the selected rows
+// see very different numbers of keys (the latest rows see them all); cutting every tile into
+// pieces of the same length gives each block about the same work.
+__global__ __launch_bounds__(256) void attn_sched_kernel(const int* __restrict__ pos, int n, int rpt, int P,
+                                                         AttnSched* __restrict__ s) {
+  __shared__ int c[ATTN_MAXQ];
+  __shared__ int best, sum_c, max_c;
+  const int Q = (n + rpt - 1) / rpt, tid = threadIdx.x;
+  for (int qt = tid; qt < Q; qt += blockDim.x) c[qt] = (pos[min((qt + 1) * rpt, n) - 1] + KB) / KB;
+  __syncthreads();
+  if (tid == 0) {
+    int sc = 0, mc = 0;
+    for (int qt = 0; qt < Q; ++qt) sc += c[qt], mc = max(mc, c[qt]);
+    sum_c = sc;
+    max_c = mc;
+    best = mc;  // one piece per tile always fits: Q <= P
+  }
+  __syncthreads();
+  // pieces of at least 8 key blocks (512 keys): shorter ones cost more in merging than they save
+  for (int chunk = max((sum_c + P - 1) / P, min(8, max_c)) + tid; chunk < max_c; chunk += blockDim.x) {
+    int pieces = 0;
+    for (int qt = 0; qt < Q; ++qt) pieces += (c[qt] + chunk - 1) / chunk;
+    if (pieces <= P) atomicMin(&best, chunk);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int chunk = best;
+    int t = 0;
+    for (int qt = 0; qt < Q; ++qt) {
+      s->off[qt] = t;
+      s->c[qt] = c[qt];
+      for (int e = (c[qt] + chunk - 1) / chunk; e > 0; --e) s->piece_qt[t++] = qt;
+    }
+    s->off[Q] = t;
+    s->T = t;
+    s->chunk = chunk;
+  }
+}
+
+hipError_t launch_attention_sched(const AttnArgs& a, AttnSched* s, hipStream_t st) {
+  const int rpt = 128 / (a.hq / a.hkv), Q = (a.n + rpt - 1) / rpt;
+  if (a.n <= 0 || Q > ATTN_MAXQ || a.P < Q || a.P > ATTN_MAXP) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, a.pos, a.n, rpt, a.P, s);
+  return hipGetLastError();
+}
+
+void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len, int* P) {
   *splits = 1;
   *split_len = ((L + KB - 1) / KB) * KB;
+  *P = 0;
   if (dt != BF16 || n == 0) return;
   // split the keys only when the query tiles alone would leave CUs idle (one 8-wave block per
   // CU); each split keeps at least 512 keys (the merge re-reads every split's partial output)
@@ -608,11 +706,17 @@ void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* spli
   while (s < 8 && items * (s + 1) <= slots + slots / 8 && L / (s + 1) >= 512) ++s;
   *splits = s;
   *split_len = (((L + s - 1) / s + KB - 1) / KB) * KB;
+  // when the query tiles fit in two blocks per CU, balanced pieces instead (2 n_cu / hkv blocks per
+  // kv head, run by the two-blocks-per-CU kernel): the tiles see very different numbers of keys, so
+  // whole tiles or equal splits of them leave most CUs waiting for the latest tiles
+  const int q_tiles = (n + 128 / G - 1) / (128 / G), per_head = 2 * n_cu / hkv;
+  if (n_cu % hkv == 0 && q_tiles <= ATTN_MAXQ && q_tiles <= per_head && per_head <= ATTN_MAXP) *P = per_head;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n == 0) return hipSuccess;
-  if (a.dt == BF16) return a.splits > 1 ? launch_attention_pipe<4, 1>(a, st) : launch_attention_cfg<AttnWide>(a, st);
+  if (a.dt == BF16)
+    return !a.sched && a.splits > 1 ? launch_attention_pipe<4, 1>(a, st) : launch_attention_cfg<AttnWide>(a, st);
   hipLaunchKernelGGL(attn_simple_kernel<float>, dim3(a.n), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -88,6 +88,12 @@ struct GemmPlan { int cfg; int splits; };
 GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, int n_cu);
 
 // ----------------------------------------------------------------- attention (attn.hip)
+// Work-balanced key pieces for the selected rows: query tile qt (128 / G consecutive rows) has c[qt]
+// key blocks of 64 up to its last row's position; it is cut into pieces of `chunk` key blocks,
+// pieces [off[qt], off[qt + 1]), piece t belonging to tile piece_qt[t]; T <= P pieces in all,
+// chunk the smallest for which they fit. Built on the device from the positions.
+constexpr int ATTN_MAXQ = 256, ATTN_MAXP = 256;
+struct AttnSched { int T, chunk; int off[ATTN_MAXQ + 1]; int c[ATTN_MAXQ]; int piece_qt[ATTN_MAXP]; };
 struct AttnArgs {
   Dt dt;
   const void* q; int64_t ldq;          // [n][hq*hd]
@@ -96,11 +102,15 @@ struct AttnArgs {
   int hq, hkv, hd;
   void* out; int64_t ldo;              // [n][hq*hd] (model dtype)
   int splits; int split_len;           // split-KV: keys [s*split_len, (s+1)*split_len)
-  float* o_part; float* ml_part;       // [splits][n][hq][hd], [splits][n][hq][2]
+  float* o_part; float* ml_part;       // [splits][n][hq][hd], [splits][n][hq][2]; balanced pieces:
+                                       // [hkv][P][128][hd], [hkv][P][128][2]
+  const AttnSched* sched; int P;       // balanced pieces (bf16): P blocks per kv head, else null
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);        // main pass
-hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st);  // split-KV merge (splits > 1)
-void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len);
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st);  // merge of split-KV or pieces
+hipError_t launch_attention_sched(const AttnArgs& a, AttnSched* s, hipStream_t st);  // pieces for a.pos
+// splits > 1: split-KV launch; *P > 0: balanced pieces instead (P blocks per kv head)
+void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len, int* P);
 
 // ----------------------------------------------------------------- selection (topk.hip)
 constexpr int MAX_SPANS = 256;
