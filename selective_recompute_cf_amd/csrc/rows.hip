@@ -223,8 +223,76 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
   }
 }
 
+// Store mode with 16-byte accesses: thread e of a head handles dims [4e, 4e + 4) of both halves
+// (the rotation pairs dim i with i + hd/2), so a head is hd/8 threads and a 256-thread block covers
+// 2048/hd heads of one row; qk-norm sums over the head's threads with xor shuffles.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void qkv_post_vec_kernel(QkvPost p) {
+  constexpr int HALF = HD / 2, TPH = HALF / 4, HPB = 256 / TPH;
+  const int j = blockIdx.x;
+  const int h = blockIdx.y * HPB + threadIdx.x / TPH, e = (threadIdx.x % TPH) * 4;
+  const int nq = p.hq, nkv = p.hkv, nh = nq + 2 * nkv;
+  if (h >= nh) return;  // whole heads: the shuffle groups below stay complete
+  const int pos = clampi(p.rows[j], 0, p.L - 1);
+  const float* src = p.qkv + (int64_t)j * p.ld;
+  const int splits = p.splits > 1 ? p.splits : 1;
+  auto at4 = [&](int c) {  // 4 projection values: the sum of the split-K partials
+    float4 v = *reinterpret_cast<const float4*>(src + c);
+    for (int s2 = 1; s2 < splits; ++s2) {
+      const float4 w = *reinterpret_cast<const float4*>(src + s2 * p.split_stride + c);
+      v.x += w.x, v.y += w.y, v.z += w.z, v.w += w.w;
+    }
+    return v;
+  };
+  const int kvd = nkv * HD;
+  auto store4 = [](T* dst, float a, float b, float c, float d) {
+    dst[0] = from_f<T>(a), dst[1] = from_f<T>(b), dst[2] = from_f<T>(c), dst[3] = from_f<T>(d);
+  };
+  if (h >= nq + nkv) {  // V: copied
+    const int hh = h - nq - nkv, xo = (nq + nkv) * HD + hh * HD;
+    const float4 a = at4(xo + e), b = at4(xo + e + HALF);
+    T* vc = (T*)p.v_cache + (int64_t)pos * kvd + hh * HD;
+    store4(vc + e, a.x, a.y, a.z, a.w);
+    store4(vc + e + HALF, b.x, b.y, b.z, b.w);
+    return;
+  }
+  const bool isq = h < nq;
+  const int hh = isq ? h : h - nq, xo = isq ? hh * HD : nq * HD + hh * HD;
+  float4 x1 = at4(xo + e), x2 = at4(xo + e + HALF);
+  if (p.qk_norm) {
+    float ss = x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w + x2.x * x2.x + x2.y * x2.y + x2.z * x2.z +
+               x2.w * x2.w;
+#pragma unroll
+    for (int off = 1; off < TPH; off <<= 1) ss += __shfl_xor(ss, off, WAVE);
+    const float inv = 1.0f / sqrtf(ss / (float)HD + p.eps);
+    const float* gn = isq ? p.qn : p.kn;
+    x1.x = x1.x * inv * gn[e], x1.y = x1.y * inv * gn[e + 1], x1.z = x1.z * inv * gn[e + 2];
+    x1.w = x1.w * inv * gn[e + 3];
+    x2.x = x2.x * inv * gn[e + HALF], x2.y = x2.y * inv * gn[e + HALF + 1], x2.z = x2.z * inv * gn[e + HALF + 2];
+    x2.w = x2.w * inv * gn[e + HALF + 3];
+  }
+  const float4 c = *reinterpret_cast<const float4*>(p.cos_t + (int64_t)pos * HALF + e);
+  const float4 sn = *reinterpret_cast<const float4*>(p.sin_t + (int64_t)pos * HALF + e);
+  T* dst = isq ? (T*)p.q_out + (int64_t)j * (nq * HD) + hh * HD : (T*)p.k_cache + (int64_t)pos * kvd + hh * HD;
+  store4(dst + e, x1.x * c.x - x2.x * sn.x, x1.y * c.y - x2.y * sn.y, x1.z * c.z - x2.z * sn.z, x1.w * c.w - x2.w * sn.w);
+  store4(dst + e + HALF, x1.x * sn.x + x2.x * c.x, x1.y * sn.y + x2.y * c.y, x1.z * sn.z + x2.z * c.z,
+         x1.w * sn.w + x2.w * c.w);
+}
+
 hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st) {
   if (p.n == 0) return hipSuccess;
+  if (!p.dev && (p.hd == 64 || p.hd == 128) && p.ld % 4 == 0 && p.split_stride % 4 == 0) {
+    const int nh = p.hq + 2 * p.hkv, hpb = 256 / (p.hd / 8);
+    const dim3 grid(p.n, (nh + hpb - 1) / hpb);
+    if (dt == BF16) {
+      if (p.hd == 128) hipLaunchKernelGGL((qkv_post_vec_kernel<bf16, 128>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((qkv_post_vec_kernel<bf16, 64>), grid, dim3(256), 0, st, p);
+    } else {
+      if (p.hd == 128) hipLaunchKernelGGL((qkv_post_vec_kernel<float, 128>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((qkv_post_vec_kernel<float, 64>), grid, dim3(256), 0, st, p);
+    }
+    return hipGetLastError();
+  }
   const int nh = p.dev ? 1 : p.hq + 2 * p.hkv;
   const dim3 grid(p.n, p.dev ? 1 : (nh + 3) / 4);
   if (dt == BF16)
