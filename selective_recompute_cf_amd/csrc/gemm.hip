@@ -457,6 +457,7 @@ using GemmDtl128 = DtlCfg<128, 256, 2, 4, 3, 1, 16>;  // waves 64x64, 3 x 48 KB 
 using GemmDtl96 = DtlCfg<96, 256, 2, 4, 3, 1, 16>;    // waves 48x64, 3 x 44 KB stages
 using GemmDtl64 = DtlCfg<64, 256, 1, 8, 4, 1, 16>;    // waves 64x32, 4 x 40 KB stages
 using GemmDtl256 = DtlCfg<256, 256, 2, 4, 2, 1, 16>;  // waves 128x64, 2 x 64 KB stages (many rows)
+using GemmDtl128n = DtlCfg<128, 192, 4, 2, 3, 1, 16>; // waves 32x96, 3 x 40 KB stages (finer weight tiles)
 
 // ----------------------------------------------------------------------------- fp32 path
 __device__ __forceinline__ const float* b_row_ptr_f32(const GemmArgs& a, int col) {
@@ -518,31 +519,33 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
   GemmPlan best{GEMM_SMALL, 1};
   if (dt != BF16 || M <= 0 || N <= 0) return best;
   // The direct-to-LDS kernels need K % 64 == 0 (whole 64-wide K steps per split); otherwise the
-  // register-staged kernel. Among the block heights and split-K factors (K per split >= 512, at
+  // register-staged kernel. Among the block shapes and split-K factors (K per split >= 512, at
   // most 4), pick the least
-  //   rounds of resident blocks x (block height x K per split) / per-CU rate
+  //   rounds of resident blocks x (block area / 256 x K per split) / per-CU rate
   //   + the extra fp32 partial sums written and read back, (splits - 1) x M x N x 8 bytes,
-  // with per-CU rates relative to the 128-row block as measured on full rounds of the
-  // projection shapes (the lower blocks re-read the weight tiles more often). One cost unit is
-  // one 128-row block advancing one K column (about 0.12 ns on a full round); at about 5 TB/s
-  // the 8 bytes of one partial element (written once, read once) cost 0.0131 units.
-  struct Opt { int cfg, bm, per_cu; double rate; };
-  const Opt dtl_opts[4] = {
-      {GEMM_DTL128, 128, 1, 1.0}, {GEMM_DTL96, 96, 1, 0.86}, {GEMM_DTL64, 64, 1, 0.75}, {GEMM_DTL256, 256, 1, 1.15}};
-  const Opt small_opt[1] = {{GEMM_SMALL, 128, 2, 0.85}};
+  // with per-CU rates relative to the 128x256 block as measured on whole rounds of gate/up
+  // products with the weights streaming from HBM (smaller blocks re-read the weight and
+  // activation tiles more often). One cost unit is one row of a 256-wide block advancing one K
+  // column (about 0.1 ns on a full round); at about 5 TB/s the 8 bytes of one partial element
+  // (written once, read once) cost 0.0131 units.
+  struct Opt { int cfg, bm, bn, per_cu; double rate; };
+  const Opt dtl_opts[5] = {{GEMM_DTL128, 128, 256, 1, 1.0},  {GEMM_DTL96, 96, 256, 1, 0.86},
+                           {GEMM_DTL64, 64, 256, 1, 0.65},   {GEMM_DTL256, 256, 256, 1, 1.15},
+                           {GEMM_DTL128N, 128, 192, 1, 1.0}};
+  const Opt small_opt[1] = {{GEMM_SMALL, 128, 128, 2, 0.85}};
   const bool dtl = K % 64 == 0;
   const Opt* opts = dtl ? dtl_opts : small_opt;
-  const int n_opts = dtl ? 4 : 1;
-  const int bn = dtl ? 256 : 128;
+  const int n_opts = dtl ? 5 : 1;
   const int cols = swiglu ? 2 * N : N;
   double best_cost = 1e300;
   for (int o = 0; o < n_opts; ++o) {
-    const long tiles = (long)((M + opts[o].bm - 1) / opts[o].bm) * ((cols + bn - 1) / bn);
+    const long tiles = (long)((M + opts[o].bm - 1) / opts[o].bm) * ((cols + opts[o].bn - 1) / opts[o].bn);
     const long slots = (long)n_cu * opts[o].per_cu;
+    const double work = (double)opts[o].bm * opts[o].bn / 256.0;  // of one block per K column
     for (int sp = 1; sp <= (allow_split ? 4 : 1); ++sp) {
       if (sp > 1 && K / sp < 512) break;
       const long rounds = (tiles * sp + slots - 1) / slots;
-      const double cost = rounds * opts[o].per_cu * (double)opts[o].bm * ((double)K / sp) / opts[o].rate +
+      const double cost = rounds * opts[o].per_cu * work * ((double)K / sp) / opts[o].rate +
                           (sp - 1) * (double)M * N * 0.0131;
       if (cost < best_cost * 0.999) {
         best_cost = cost;
@@ -562,6 +565,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       case GEMM_DTL96: return launch_gemm_dtl<GemmDtl96>(a, st);
       case GEMM_DTL64: return launch_gemm_dtl<GemmDtl64>(a, st);
       case GEMM_DTL256: return launch_gemm_dtl<GemmDtl256>(a, st);
+      case GEMM_DTL128N: return launch_gemm_dtl<GemmDtl128n>(a, st);
       default: return launch_gemm_cfg<GemmSmall>(a, st);
     }
   }
