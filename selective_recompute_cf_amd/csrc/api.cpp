@@ -106,7 +106,7 @@ size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 // ------------------------------------------------------------------ workspace of one layer pass
 struct LayerPlan {
   cf::GemmPlan qkv, o, gu, down, ksel;
-  int attn_splits, attn_split_len, attn_P;
+  int attn_P;
 };
 
 LayerPlan layer_plan(const cf_ctx* c, int L, int R, int ksel_rows) {
@@ -119,8 +119,7 @@ LayerPlan layer_plan(const cf_ctx* c, int L, int R, int ksel_rows) {
   p.gu = cf::gemm_plan(dt, R, F, d, true, false, c->n_cu);
   p.down = cf::gemm_plan(dt, R, d, F, false, true, c->n_cu);
   p.ksel = cf::gemm_plan(dt, ksel_rows, kvd, d, false, true, c->n_cu);
-  cf::attn_plan(dt, R, L, m.n_q_heads, m.n_kv_heads, m.head_dim, c->n_cu, &p.attn_splits, &p.attn_split_len,
-                &p.attn_P);
+  cf::attn_plan(dt, R, m.n_q_heads, m.n_kv_heads, c->n_cu, &p.attn_P);
   return p;
 }
 
@@ -150,10 +149,10 @@ LayerWs layer_ws(const cf_ctx* c, int L, int R, int ksel_rows = 0) {
   w.gu = take(m.dtype == CF_BF16 ? 0 : (size_t)R * 2 * F * 4);
   const int ps = std::max(p.o.splits, p.down.splits);
   w.part = take(ps > 1 ? (size_t)ps * R * d * 4 : 0);
-  // attention partial sums: split-KV [splits][R][hq][hd] or balanced pieces [hkv][P][128][hd]
+  // attention partial sums of the balanced pieces: [hkv][P][128][hd] and [hkv][P][128][2]
   const size_t pieces = (size_t)m.n_kv_heads * p.attn_P * 128;
-  w.opart = take(std::max(p.attn_splits > 1 ? (size_t)p.attn_splits * R * qd : 0, pieces * m.head_dim) * 4);
-  w.mlpart = take(std::max(p.attn_splits > 1 ? (size_t)p.attn_splits * R * m.n_q_heads : 0, pieces) * 2 * 4);
+  w.opart = take(pieces * m.head_dim * 4);
+  w.mlpart = take(pieces * 2 * 4);
   w.sched = take(p.attn_P > 0 ? sizeof(cf::AttnSched) : 0);
   w.total = off;
   return w;
@@ -237,7 +236,6 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   cf::AttnArgs at{};
   at.dt = dt; at.q = Q; at.ldq = qd; at.pos = sel; at.n = n; at.k = kc; at.v = vc; at.L = L;
   at.hq = m.n_q_heads; at.hkv = m.n_kv_heads; at.hd = hd; at.out = AO; at.ldo = qd;
-  at.splits = P.attn_splits; at.split_len = P.attn_split_len;
   at.o_part = reinterpret_cast<float*>(ws + lw.opart);
   at.ml_part = reinterpret_cast<float*>(ws + lw.mlpart);
   if (P.attn_P > 0) {
@@ -249,7 +247,7 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
     at.sched = sch;
   }
   CF_RUN("attention", cf::launch_attention(at, st));
-  if (at.splits > 1 || at.sched) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
+  if (at.sched) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
 
   float* part = reinterpret_cast<float*>(ws + lw.part);
   auto proj = [&](const cf::GemmPlan& pl, const void* A, int lda, const void* B, int K) {

@@ -51,12 +51,10 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 smem[S * 2 * TILE];
   const int G = a.hq / a.hkv;
   const int rpt = 128 / G;  // selected rows per block
-  // logical tile: query tile fastest (latest rows, which see the most keys, first), then split,
-  // then kv head; xcd_tile keeps each kv head's tiles on one XCD
   const int q_tiles = (a.n + rpt - 1) / rpt;
-  // the block's query tile j0.., kv head g, key range [kbeg, kend) and where its result goes
-  // (as in the pipelined kernel): piece or split-KV slot, else the normalised output
-  int j0, g, kbeg, kend, piece = -1, split = -1;
+  // the block's query tile j0.., kv head g, key range [kbeg, kend) and where its result goes:
+  // piece >= 0 writes partial sums to piece slot `piece`, else the normalised output
+  int j0, g, kbeg, kend, piece = -1;
   if (a.sched) {  // balanced pieces: blocks t * hkv + g
     g = blockIdx.x % a.hkv;
     const int t = blockIdx.x / a.hkv;
@@ -67,14 +65,12 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
     kbeg = kb0 * KB;
     kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kb1 * KB), a.L);
     if (a.sched->off[qt + 1] - a.sched->off[qt] > 1) piece = t;
-  } else {
-    const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
+  } else {  // whole query tiles, latest first (they see the most keys); each kv head on one XCD
+    const int lt = xcd_tile(blockIdx.x, q_tiles * a.hkv);
     j0 = (q_tiles - 1 - lt % q_tiles) * rpt;
-    const int sp = (lt / q_tiles) % a.splits;
-    g = lt / (q_tiles * a.splits);
-    kbeg = sp * a.split_len;
-    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kbeg + a.split_len), a.L);
-    if (a.splits > 1) split = sp;
+    g = lt / q_tiles;
+    kbeg = 0;
+    kend = min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, a.L);
   }
   const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
   const int lg = lane / 16, lr = lane % 16;
@@ -253,9 +249,8 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   for (int rg = 0; rg < RG; ++rg) {
     const int j = jrow[rg];
     if (j >= a.n) continue;
-    if (piece >= 0 || split >= 0) {
-      const int64_t slot = piece >= 0 ? ((int64_t)g * a.P + piece) * 128 + (w * RG + rg) * 16 + lr
-                                      : ((int64_t)split * a.n + j) * a.hq + head[rg];
+    if (piece >= 0) {
+      const int64_t slot = ((int64_t)g * a.P + piece) * 128 + (w * RG + rg) * 16 + lr;
       float* op = a.o_part + slot * HD;
 #pragma unroll
       for (int nt = 0; nt < HD / 16; ++nt)
@@ -280,249 +275,6 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   }
 }
 
-// Pipelined variant: the barrier sits in the middle of a key block, after its S^T MFMAs, so the
-// next block's K fragments are read from LDS while this block's softmax runs. Per key block it:
-//   S^T MFMAs on the K fragments read during block it - 1
-//   wait for this wave's loads of block it + 1 | barrier
-//   load block it + S - 1 into the stage block it - 1 used | read block it + 1's K fragments
-//   softmax of block it | V^T reads and O^T MFMAs of block it
-// The barrier publishes block it + 1 (every wave waited for its own loads of it) and retires the
-// V reads of block it - 1, the last reads of the stage the new loads overwrite. S >= 3.
-template <int HD, int S, int MINB>
-__global__ __launch_bounds__(8 * WAVE, MINB) void attn_pipe_kernel(AttnArgs a) {
-  constexpr int NW = 8;
-  constexpr int NCH = HD / 8, SWM = NCH - 1, TILE = KB * HD, RPI = WAVE / NCH, NI = 2 * KB / RPI, NL = NI / NW;
-  static_assert(NI % NW == 0 && S >= 3 && (S - 3) * NL <= 63, "stages");
-  __shared__ __attribute__((aligned(1024))) bf16 smem[S * 2 * TILE];
-  const int G = a.hq / a.hkv;
-  const int rpt = 128 / G;
-  const int q_tiles = (a.n + rpt - 1) / rpt;
-  // the block's query tile j0.., kv head g, key range [kbeg, kend) and where its result goes:
-  // piece >= 0 writes partial sums to piece slot `piece`, split >= 0 to split-KV slot `split`,
-  // both negative writes the normalised output
-  int j0, g, kbeg, kend, piece = -1, split = -1;
-  const int tid = threadIdx.x, lane = tid % WAVE, w = tid / WAVE;
-  const int lg = lane / 16, lr = lane % 16;
-  if (a.sched) {  // balanced pieces: blocks t * hkv + g (the kv heads spread over the XCDs)
-    g = blockIdx.x % a.hkv;
-    const int t = blockIdx.x / a.hkv;
-    if (t >= a.sched->T) return;  // block-uniform: no piece for this block
-    const int qt = a.sched->piece_qt[t], chunk = a.sched->chunk;
-    const int kb0 = (t - a.sched->off[qt]) * chunk, kb1 = min(kb0 + chunk, a.sched->c[qt]);
-    j0 = qt * rpt;
-    kbeg = kb0 * KB;
-    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kb1 * KB), a.L);
-    if (a.sched->off[qt + 1] - a.sched->off[qt] > 1) piece = t;
-  } else {
-    const int lt = xcd_tile(blockIdx.x, q_tiles * a.splits * a.hkv);
-    j0 = (q_tiles - 1 - lt % q_tiles) * rpt;
-    const int sp = (lt / q_tiles) % a.splits;
-    g = lt / (q_tiles * a.splits);
-    kbeg = sp * a.split_len;
-    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kbeg + a.split_len), a.L);
-    if (a.splits > 1) split = sp;
-  }
-  const int kvd = a.hkv * HD;
-  const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
-  const int r = w * 16 + lr;
-  const int j = j0 + r / G, head = g * G + r % G, jc = min(j, a.n - 1);
-  const int p = a.pos[jc];
-  bf16x8 qf[HD / 32];
-  {
-    const bf16* qrow = (const bf16*)a.q + (int64_t)jc * a.ldq + head * HD;
-#pragma unroll
-    for (int kk = 0; kk < HD / 32; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + 8 * lg);
-  }
-  f32x4 o[HD / 16];
-#pragma unroll
-  for (int nt = 0; nt < HD / 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_i = -INFINITY, l_i = 0.f;
-  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
-  // smallest position among the wave's 16 rows (lanes l, l + 16, l + 32, l + 48 share a row)
-  int p_min = p;
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) p_min = min(p_min, __shfl_xor(p_min, off, WAVE));
-  p_min = __builtin_amdgcn_readfirstlane(p_min);
-
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
-  const bf16* src[NL];
-  int trow[NL];
-#pragma unroll
-  for (int q = 0; q < NL; ++q) {
-    const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
-    const int t = ii * RPI + lane / NCH;
-    const int c = (lane % NCH) ^ (t & SWM);
-    src[q] = (const bf16*)(tensor ? a.v : a.k) + g * HD + c * 8;
-    trow[q] = t;
-  }
-  auto issue = [&](int step) __attribute__((always_inline)) {
-    const int stage = step % S;
-    const int kbase = kbeg + step * KB;
-#pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
-      const bf16* gp = src[q] + (int64_t)min(kbase + trow[q], a.L - 1) * kvd;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          lds0 + 2u * (uint32_t)(stage * 2 * TILE + tensor * TILE + ii * RPI * HD));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(dst) : "memory", "m0");
-    }
-  };
-  typedef uint32_t KVec __attribute__((ext_vector_type(4 * 4 * (HD / 32))));  // the block's K fragments
-  auto kread = [&](int stage) __attribute__((always_inline)) {
-    const bf16* Kt = smem + stage * 2 * TILE;
-    KVec f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int kk = 0; kk < HD / 32; ++kk) {
-        const int t = kt * 16 + lr, c = kk * 4 + lg;
-        const uint4 x = *reinterpret_cast<const uint4*>(&Kt[t * HD + ((c ^ (t & SWM)) * 8)]);
-        const int o4 = 4 * (kt * (HD / 32) + kk);
-        f[o4] = x.x, f[o4 + 1] = x.y, f[o4 + 2] = x.z, f[o4 + 3] = x.w;
-      }
-    return f;
-  };
-  auto vread = [&](const bf16* Vt, int kb, int nt) __attribute__((always_inline)) {
-    const int t = kb + lr / 4;
-    const int col = nt * 16 + 4 * (lr % 4);
-    const int c = col / 8;
-    const bf16* ptr = &Vt[t * HD + ((c ^ (t & SWM)) * 8) + (col % 8)];
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
-  };
-  auto barrier = []() __attribute__((always_inline)) {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  if (nkb > 0) {
-    const int last = nkb - 1;
-#pragma unroll
-    for (int q = 0; q < S - 1; ++q) issue(min(q, last));
-    __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT((S - 2) * NL));
-    barrier();
-    KVec kf = kread(0);
-    for (int it = 0; it < nkb; ++it) {
-      const int kbase = kbeg + it * KB;
-      f32x4 s[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < HD / 32; ++kk) {
-          const int o4 = 4 * (kt * (HD / 32) + kk);
-          const uint4 x = make_uint4(kf[o4], kf[o4 + 1], kf[o4 + 2], kf[o4 + 3]);
-          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), qf[kk], s[kt], 0, 0, 0);
-        }
-      }
-      // block it + 1 landed for this wave (loads of later blocks may stay in flight); lgkm drained
-      __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT((S - 3) * NL) & ~(15 << 8));
-      barrier();
-      issue(min(it + S - 1, last));
-      kf = kread((it + 1) % S);
-      const bf16* Vt = smem + (it % S) * 2 * TILE + TILE;
-      // Scores stay unscaled; the running max m_i is kept in scaled (log2) units and each
-      // probability is exp2(score * sl2 - m) in one fused multiply-add. A key block that lies
-      // wholly below every row's position (and inside the split) needs no mask, and then every
-      // row has a finite maximum.
-      const bool unmasked = kbase + KB - 1 <= min(p_min, kend - 1);  // wave-uniform
-      if (!unmasked) {
-        const int lim = min(p, kend - 1) - kbase - 4 * lg;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kt * 16 + i > lim) s[kt][i] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      // The reference max moves only when a row's max grows by more than 8 (log2 units): the
-      // probabilities then stay below 2^8 (no overflow in fp32 or bf16), the result is the same
-      // softmax, and most steps skip rescaling the output accumulators. A row with no visible key
-      // yet (reference -inf) uses 0 for its exponents: its masked scores give exp2(-inf) = 0.
-      const float m_cand = fmaxf(m_i, mx * sl2);
-      const bool upd = m_cand > m_i + 8.f;
-      const float m_use = upd ? m_cand : m_i;
-      const float m_ref = m_use == -INFINITY ? 0.f : m_use;
-      const float alpha = upd ? __builtin_amdgcn_exp2f(m_i - m_ref) : 1.f;  // exp2(-inf) = 0
-      float ps = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][i], sl2, -m_ref));
-          s[kt][i] = e;
-          ps += e;
-        }
-      ps += __shfl_xor(ps, 16, WAVE);
-      ps += __shfl_xor(ps, 32, WAVE);
-      l_i = l_i * alpha + ps;
-      m_i = m_use;
-      if (__builtin_amdgcn_ballot_w64(upd)) {
-#pragma unroll
-        for (int nt = 0; nt < HD / 16; ++nt) o[nt] *= alpha;
-      }
-      bf16x8 pf[2];
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pf[mm][tp * 4 + i] = (bf16)s[2 * mm + tp][i];
-#pragma unroll
-      for (int nt = 0; nt < HD / 16; ++nt) {
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const i16x4 lo = vread(Vt, 32 * mm + 4 * lg, nt);
-          const i16x4 hi = vread(Vt, 32 * mm + 16 + 4 * lg, nt);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[mm], o[nt], 0, 0, 0);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT(0));
-  }
-  if (j >= a.n) return;
-  if (piece >= 0 || split >= 0) {
-    const int64_t slot = piece >= 0 ? ((int64_t)g * a.P + piece) * 128 + r : ((int64_t)split * a.n + j) * a.hq + head;
-    float* op = a.o_part + slot * HD;
-#pragma unroll
-    for (int nt = 0; nt < HD / 16; ++nt)
-      *reinterpret_cast<float4*>(op + nt * 16 + 4 * lg) = make_float4(o[nt][0], o[nt][1], o[nt][2], o[nt][3]);
-    if (lg == 0) {
-      float* ml = a.ml_part + slot * 2;
-      ml[0] = m_i;
-      ml[1] = l_i;
-    }
-  } else {
-    const float inv = l_i > 0.f ? 1.0f / l_i : 0.f;
-    bf16* out = (bf16*)a.out + (int64_t)j * a.ldo + head * HD;
-#pragma unroll
-    for (int nt = 0; nt < HD / 16; ++nt) {
-      bf16x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[nt][i] * inv);
-      *reinterpret_cast<bf16x4*>(out + nt * 16 + 4 * lg) = v;
-    }
-  }
-}
-
-template <int S, int MINB>
-hipError_t launch_attention_pipe(const AttnArgs& a, hipStream_t st) {
-  const int G = a.hq / a.hkv, rpt = 128 / G;
-  dim3 grid(a.sched ? a.P * a.hkv : ((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
-  if (a.hd == 128)
-    hipLaunchKernelGGL((attn_pipe_kernel<128, S, MINB>), grid, dim3(8 * WAVE), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_pipe_kernel<64, S, MINB>), grid, dim3(8 * WAVE), 0, st, a);
-  return hipGetLastError();
-}
-
 // Launch configuration: waves per block, 16-row groups per wave, LDS stages, blocks per CU.
 template <int NW, int RG, int S, int MINB>
 struct AttnCfg {
@@ -532,7 +284,7 @@ struct AttnCfg {
 template <class C>
 hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
   const int G = a.hq / a.hkv, rpt = 128 / G;
-  dim3 grid(a.sched ? a.P * a.hkv : ((a.n + rpt - 1) / rpt) * a.hkv * a.splits);
+  dim3 grid(a.sched ? a.P * a.hkv : ((a.n + rpt - 1) / rpt) * a.hkv);
   if (a.hd == 128)
     hipLaunchKernelGGL((attn_dtl_kernel<128, C::nw, C::rg, C::stages, C::minb>), grid, dim3(C::nw * WAVE), 0, st, a);
   else
@@ -540,14 +292,13 @@ hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Unsplit launches (full causal layers, many query tiles) and balanced pieces (the selected rows of
-// a blended layer): two blocks per CU over 2-stage rings, whose phases interleave (measured faster
-// on both). Split-KV launches (only where balanced pieces do not fit: kv heads that do not divide
-// the CU count): the pipelined kernel, one block per CU over a 4-stage ring.
+// Whole query tiles (full causal layers) and balanced pieces (the selected rows of a blended
+// layer): two blocks per CU over 2-stage rings, whose phases interleave (measured faster on both
+// than one block per CU over deeper rings).
 using AttnWide = AttnCfg<8, 1, 2, 2>;
 
-// Combine split-KV partials: weights 2^(m_s - max m) (scores are in log2 units). One thread per
-// 4 consecutive output elements of one (row, head): 16-byte partial loads, one 4-element store.
+// Combine the pieces of a query tile: weights 2^(m_s - max m) (scores are in log2 units). One
+// thread per 4 consecutive output elements of one (row, head): 16-byte partial loads, one store.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const unsigned q4 = (unsigned)a.hd / 4, per_row = (unsigned)a.hq * q4;
@@ -555,17 +306,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (gid >= (unsigned)a.n * per_row) return;
   const int j = (int)(gid / per_row), idx = (int)(gid % per_row);
   const int head = idx / (int)q4, d = (idx % (int)q4) * 4;
-  // slot of part s of this row: split s, or piece off[qt] + s of its query tile
-  int parts = a.splits;
-  int64_t base = (int64_t)j * a.hq + head, stride = (int64_t)a.n * a.hq;
-  if (a.sched) {
-    const int G = a.hq / a.hkv, rpt = 128 / G, qt = j / rpt;
-    const int first = a.sched->off[qt];
-    parts = a.sched->off[qt + 1] - first;
-    if (parts <= 1) return;  // a single piece wrote the normalised output itself
-    base = ((int64_t)(head / G) * a.P + first) * 128 + (j % rpt) * G + head % G;
-    stride = 128;
-  }
+  // the row's parts: pieces off[qt] .. off[qt + 1] - 1 of its query tile
+  const int G = a.hq / a.hkv, rpt = 128 / G, qt = j / rpt;
+  const int first = a.sched->off[qt], parts = a.sched->off[qt + 1] - first;
+  if (parts <= 1) return;  // a single piece wrote the normalised output itself
+  const int64_t base = ((int64_t)(head / G) * a.P + first) * 128 + (j % rpt) * G + head % G, stride = 128;
   float mx = -INFINITY;
   for (int s = 0; s < parts; ++s) mx = fmaxf(mx, a.ml_part[(base + s * stride) * 2]);
   float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f, den = 0.f;
@@ -633,7 +378,7 @@ __global__ __launch_bounds__(256) void attn_simple_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st) {
-  if (a.n == 0 || (a.splits <= 1 && !a.sched)) return hipSuccess;
+  if (a.n == 0 || !a.sched) return hipSuccess;
   {
     const int64_t total = (int64_t)a.n * a.hq * (a.hd / 4);
     const dim3 grid((unsigned)((total + 255) / 256));
@@ -692,31 +437,20 @@ hipError_t launch_attention_sched(const AttnArgs& a, AttnSched* s, hipStream_t s
   return hipGetLastError();
 }
 
-void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len, int* P) {
-  *splits = 1;
-  *split_len = ((L + KB - 1) / KB) * KB;
+void attn_plan(Dt dt, int n, int hq, int hkv, int n_cu, int* P) {
+  // When the query tiles fit in two blocks per CU (the selected rows of a blended layer), balanced
+  // pieces (2 n_cu / hkv blocks per kv head): the tiles see very different numbers of keys, so
+  // whole tiles leave most CUs waiting for the latest ones. Otherwise whole tiles (many of them:
+  // full causal layers).
   *P = 0;
   if (dt != BF16 || n == 0) return;
-  // split the keys only when the query tiles alone would leave CUs idle (one 8-wave block per
-  // CU); each split keeps at least 512 keys (the merge re-reads every split's partial output)
-  const int G = hq / hkv;
-  const long items = (long)((n + 128 / G - 1) / (128 / G)) * hkv;
-  const long slots = (long)n_cu;
-  int s = 1;
-  while (s < 8 && items * (s + 1) <= slots + slots / 8 && L / (s + 1) >= 512) ++s;
-  *splits = s;
-  *split_len = (((L + s - 1) / s + KB - 1) / KB) * KB;
-  // when the query tiles fit in two blocks per CU, balanced pieces instead (2 n_cu / hkv blocks per
-  // kv head, run by the two-blocks-per-CU kernel): the tiles see very different numbers of keys, so
-  // whole tiles or equal splits of them leave most CUs waiting for the latest tiles
-  const int q_tiles = (n + 128 / G - 1) / (128 / G), per_head = 2 * n_cu / hkv;
+  const int G = hq / hkv, q_tiles = (n + 128 / G - 1) / (128 / G), per_head = 2 * n_cu / hkv;
   if (n_cu % hkv == 0 && q_tiles <= ATTN_MAXQ && q_tiles <= per_head && per_head <= ATTN_MAXP) *P = per_head;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n == 0) return hipSuccess;
-  if (a.dt == BF16)
-    return !a.sched && a.splits > 1 ? launch_attention_pipe<4, 1>(a, st) : launch_attention_cfg<AttnWide>(a, st);
+  if (a.dt == BF16) return launch_attention_cfg<AttnWide>(a, st);
   hipLaunchKernelGGL(attn_simple_kernel<float>, dim3(a.n), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -101,16 +101,15 @@ struct AttnArgs {
   const void* k; const void* v; int L; // cache [L][hkv*hd]
   int hq, hkv, hd;
   void* out; int64_t ldo;              // [n][hq*hd] (model dtype)
-  int splits; int split_len;           // split-KV: keys [s*split_len, (s+1)*split_len)
-  float* o_part; float* ml_part;       // [splits][n][hq][hd], [splits][n][hq][2]; balanced pieces:
-                                       // [hkv][P][128][hd], [hkv][P][128][2]
+  float* o_part; float* ml_part;       // pieces' partial sums: [hkv][P][128][hd], [hkv][P][128][2]
   const AttnSched* sched; int P;       // balanced pieces (bf16): P blocks per kv head, else null
+                                       // (whole query tiles)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);        // main pass
-hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st);  // merge of split-KV or pieces
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st);  // merge of the pieces
 hipError_t launch_attention_sched(const AttnArgs& a, AttnSched* s, hipStream_t st);  // pieces for a.pos
-// splits > 1: split-KV launch; *P > 0: balanced pieces instead (P blocks per kv head)
-void attn_plan(Dt dt, int n, int L, int hq, int hkv, int hd, int n_cu, int* splits, int* split_len, int* P);
+// *P > 0: balanced pieces with P blocks per kv head; 0: whole query tiles
+void attn_plan(Dt dt, int n, int hq, int hkv, int n_cu, int* P);
 
 // ----------------------------------------------------------------- selection (topk.hip)
 constexpr int MAX_SPANS = 256;
