@@ -84,16 +84,27 @@ __global__ __launch_bounds__(TK_THREADS) void topk_token_kernel(const float* __r
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int cum = 0;
-      for (int b = 255; b >= 0; --b) {
-        const int h = (int)hist[b];
-        if (cum + h >= kk) {
-          s_prefix = prefix | ((uint32_t)b << shift);
-          s_kk = kk - cum;
-          break;
-        }
-        cum += h;
+    // the digit: the bin b where the keys in bins above b number fewer than kk and those in bins
+    // b and above at least kk. Thread t < 256 takes bin 255 - t, so an inclusive scan over the
+    // threads counts the keys from the top bin down.
+    int h = 0, incl = 0;
+    if (threadIdx.x < 256) {
+      h = (int)hist[255 - threadIdx.x];
+      incl = h;
+#pragma unroll
+      for (int off = 1; off < WAVE; off <<= 1) {
+        const int y = __shfl_up(incl, off, WAVE);
+        if ((int)(threadIdx.x % WAVE) >= off) incl += y;
+      }
+      if (threadIdx.x % WAVE == WAVE - 1) wsum[threadIdx.x / WAVE] = incl;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      for (int wv = 0; wv < (int)threadIdx.x / WAVE; ++wv) incl += wsum[wv];
+      const int above = incl - h;
+      if (above < kk && incl >= kk) {
+        s_prefix = prefix | ((uint32_t)(255 - threadIdx.x) << shift);
+        s_kk = kk - above;
       }
     }
     __syncthreads();
