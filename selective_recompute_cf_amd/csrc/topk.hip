@@ -202,20 +202,24 @@ __global__ __launch_bounds__(256) void tk_mb_hist_kernel(const float* __restrict
 }
 
 __global__ __launch_bounds__(256) void tk_mb_pick_kernel(int pass, TopkState* st, const uint32_t* hist) {
-  __shared__ int h[256];
-  h[threadIdx.x] = (int)hist[pass * 256 + threadIdx.x];
+  // as in the one-workgroup kernel: thread t takes bin 255 - t and an inclusive scan over the
+  // threads counts the keys from the top bin down; the bin where the count first reaches kk wins
+  __shared__ int wtot[256 / WAVE];
+  const int t = threadIdx.x, lane = t % WAVE;
+  const int h = (int)hist[pass * 256 + 255 - t];
+  int incl = h;
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const int y = __shfl_up(incl, off, WAVE);
+    if (lane >= off) incl += y;
+  }
+  if (lane == WAVE - 1) wtot[t / WAVE] = incl;
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  const int shift = 24 - 8 * pass;
-  const int kk = st->kk[pass];
-  int cum = 0;
-  for (int b = 255; b >= 0; --b) {
-    if (cum + h[b] >= kk) {
-      st->prefix[pass + 1] = st->prefix[pass] | ((uint32_t)b << shift);
-      st->kk[pass + 1] = kk - cum;
-      return;
-    }
-    cum += h[b];
+  for (int wv = 0; wv < t / WAVE; ++wv) incl += wtot[wv];
+  const int kk = st->kk[pass], above = incl - h;
+  if (above < kk && incl >= kk) {
+    st->prefix[pass + 1] = st->prefix[pass] | ((uint32_t)(255 - t) << (24 - 8 * pass));
+    st->kk[pass + 1] = kk - above;
   }
 }
 
