@@ -1,7 +1,9 @@
 """GPU parity of one blended layer (cf_blend_layer) against the oracle's layer on the same inputs:
 gather + norm + QKV on the selected rows, qk-norm + RoPE, scatter into the cache, sparse-query
 causal attention over the whole cache, O projection, SwiGLU MLP, rows written back
-(CacheBlend, "Selective Recompute Without Skipping"; QCFuse Eq. 7)."""
+(CacheBlend, "Selective Recompute Without Skipping"; QCFuse Eq. 7). Selections: all rows, scattered
+rows + a tail, one row, and rows clustered at the start or at the end (which load the attention's
+key pieces very unevenly)."""
 import numpy as np
 import pytest
 
@@ -45,11 +47,15 @@ def _sel(L, kind, seed):
         return np.concatenate([body, np.arange(L - 16, L)])
     if kind == "one":
         return np.array([L // 2])
+    if kind == "early":  # clustered at the start + the tail: one query tile sees many more keys
+        return np.concatenate([np.arange((L - 16) // 6), np.arange(L - 16, L)])
+    if kind == "late":  # clustered at the end: every query tile sees nearly all keys
+        return np.arange(L - L // 5, L)
     raise ValueError(kind)
 
 
 @pytest.mark.parametrize("shape", list(SHAPES))
-@pytest.mark.parametrize("kind", ["all", "sparse", "one"])
+@pytest.mark.parametrize("kind", ["all", "sparse", "one", "early", "late"])
 def test_blend_layer_matches_oracle(shape, kind):
     import torch
     cfg, L = SHAPES[shape]
