@@ -13,7 +13,8 @@ default (fp64 where a step says so, and fp64 throughout when asked), following:
   stitching, Eq. 6 recompute ratio, Eq. 7 fused cache),
 * CacheBlend: Reusing KV Caches When Your Text Isn't a Prefix, sections "Quantifying the
   Damage" (KV deviation, HKVD tokens), "Selective Recompute Without Skipping" (the per-layer
-  blend pass) and "The Chicken-and-Egg Problem" (select once on an early layer),
+  blend pass) and "The Chicken-and-Egg Problem" (select once on an early layer, or narrow the
+  set layer by layer: gradual filtering),
 * Request Order Matters: Cache-History Sensitivity in Selective KV-Cache Reuse for Rolling
   Agents, §2.2 Eq. 1 (deviation), Eq. 2 (budget), §2.3 Eq. 3 (span score and the
   document-aligned policy), §4.1 (rolling window).
@@ -21,10 +22,11 @@ default (fp64 where a step says so, and fp64 throughout when asked), following:
 from .model import (rms_norm, rope, rope_angles, causal_attention, layer_rows, full_prefill, bf16_round,
                     chunk_prefill)
 from .blend import (budget, reposition, stitch, kv_deviation, select_topk, select_doc_spans,
-                    blend_prefill, direct_reuse, RollingWindow, BlendResult)
+                    blend_prefill, direct_reuse, RollingWindow, BlendResult, narrow, gradual_schedule)
 
 __all__ = [
     "bf16_round", "rms_norm", "rope", "rope_angles", "causal_attention", "layer_rows", "full_prefill",
     "chunk_prefill", "budget", "reposition", "stitch", "kv_deviation", "select_topk",
-    "select_doc_spans", "blend_prefill", "direct_reuse", "RollingWindow", "BlendResult",
+    "select_doc_spans", "blend_prefill", "direct_reuse", "RollingWindow", "BlendResult", "narrow",
+    "gradual_schedule",
 ]

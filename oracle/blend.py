@@ -22,7 +22,13 @@ design notes of the repository):
   computed as P[a+r] - P[a] over the span's fp64 running sum P; ties take the smallest a,
 * the query U follows the context, is never ranked and is recomputed at every layer >= s
   (QCFuse §2.1.1: U is processed online and is not part of the reusable cache),
-* at layer s only the selected rows and U replace the stitched cache (QCFuse Eq. 7).
+* at layer s only the selected rows and U replace the stitched cache (QCFuse Eq. 7),
+* gradual filtering (CacheBlend, "The Chicken-and-Egg Problem"): the page ranks the later
+  layers once by "attention deviation" and once, in its selection function, by a generic
+  per-token deviation; the KV deviation of Eq. 1 is taken for both. The recompute count of
+  each layer comes from a schedule k_s >= k_{s+1} >= ... (the page narrows r_1 > r_2 > ... toward
+  r); the set recomputed at layer l + 1 is the k_{l+1} rows of layer l's set with the largest
+  deviation measured at layer l, which is the only layer where all of them have fresh keys.
 """
 from __future__ import annotations
 
@@ -163,6 +169,42 @@ def select_doc_spans(d, k: int, bounds) -> np.ndarray:
     return np.array(sorted(chosen), dtype=np.int32)
 
 
+def narrow(prev_set, dev_prev, k: int) -> np.ndarray:
+    """Gradual filtering step (CacheBlend, "The Chicken-and-Egg Problem"): keep the k rows of
+    ``prev_set`` (ascending positions) whose deviation ``dev_prev`` (one value per row of
+    ``prev_set``, same order) is largest; equal deviations keep the lower position. Only rows
+    recomputed on the previous layer have a deviation there, so the set can only shrink.
+    Output: ascending int32 positions [k]."""
+    prev = np.asarray(prev_set, dtype=np.int64)
+    if len(dev_prev) != len(prev):
+        raise ValueError("one deviation per row of the previous set")
+    if not 0 <= k <= len(prev):
+        raise ValueError("k out of range")
+    return prev[select_topk(dev_prev, k)].astype(np.int32)
+
+
+def gradual_schedule(n_ctx: int, n_sched: int, first: Tuple[int, int], keep: Tuple[int, int],
+                     final: Tuple[int, int]) -> List[int]:
+    """Per-layer recompute counts for gradual filtering (CacheBlend, "The Chicken-and-Egg
+    Problem"): the first layer takes budget(N, r_1); each later layer keeps max(1,
+    floor(k_prev * keep)) of the previous set, as the page's selection function does, but never
+    fewer than the target budget(N, r) (the page narrows toward r, it does not undershoot it).
+    Ratios are (numerator, denominator) pairs; integer arithmetic only."""
+    k = budget(n_ctx, *first)
+    floor_k = budget(n_ctx, *final)
+    if floor_k > k:
+        raise ValueError("the final ratio must not exceed the first")
+    kn, kd = keep
+    if kn < 0 or kd <= 0 or kn > kd:
+        raise ValueError("keep fraction must be in [0, 1]")
+    out = []
+    for i in range(n_sched):
+        out.append(k)
+        if k > 0:
+            k = max(floor_k, max(1, (k * kn) // kd))
+    return out
+
+
 # ------------------------------------------------------------------ blended prefill
 
 @dataclasses.dataclass
@@ -173,11 +215,13 @@ class BlendResult:
     sel: np.ndarray      # selected context positions, ascending [k]
     dev: np.ndarray      # deviation at the selection layer [N] (empty for full prefill)
     hidden: np.ndarray   # residual stream [L, d] after the last layer
+    sets: Optional[List[np.ndarray]] = None        # gradual: the recompute set of layers s..Ly-1
+    layer_devs: Optional[List[np.ndarray]] = None  # gradual: deviation over the set, layers s+1..Ly-2
 
 
 def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer: int, k: int,
                   mode: str = "token", span_bounds=None, ft=np.float32, n_layers=None,
-                  bf16_ops=None) -> BlendResult:
+                  bf16_ops=None, k_sched: Optional[Sequence[int]] = None) -> BlendResult:
     """Blended prefill of one request: context C (n_ctx rows) followed by the query U.
 
     1. Stitch: layers s..Ly-1 of the request cache are the remapped chunk caches (QCFuse Eq. 4).
@@ -190,6 +234,12 @@ def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer
        and only their hidden rows change (CacheBlend "Selective Recompute Without Skipping";
        QCFuse Eq. 7).
     6. Output: the fused K/V of every layer and RMSNorm of the query rows.
+
+    With ``k_sched`` (token mode; Ly - s counts, k_sched[0] = k, non-increasing) the set narrows
+    layer by layer (gradual filtering, CacheBlend "The Chicken-and-Egg Problem"): at each layer
+    l < Ly - 1 the deviation of the current set's fresh keys against the stitched keys they are
+    about to replace is measured (at layer s it is the step-4 deviation), and layer l + 1
+    recomputes the k_sched[l + 1 - s] rows of that set with the largest deviation (``narrow``).
 
     mode "all" is ordinary full prefill of every row at every layer (QCFuse Eq. 2)."""
     cfg = model.cfg
@@ -228,13 +278,39 @@ def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer
         P = select_doc_spans(dev, k, span_bounds)
     else:
         raise ValueError("unknown mode " + str(mode))
-    sel = np.concatenate([P.astype(np.int64), np.arange(N, L)])
+    if k_sched is None:
+        sel = np.concatenate([P.astype(np.int64), np.arange(N, L)])
+        for l in range(s, ly):
+            w = w_s if l == s else model.layer(l)
+            if len(sel):
+                h[sel] = layer_rows(cfg, w, h[sel], sel, kc[l], vc[l], ft, bf16_ops)
+        out = rms_norm(h[N:], model.final_norm, cfg.rms_eps, ft)
+        return BlendResult(kc, vc, out, P, dev, h)
+
+    sched = [int(x) for x in k_sched]
+    if mode != "token":
+        raise ValueError("gradual filtering ranks single tokens")
+    if len(sched) != ly - s or sched[0] != k or any(b > a for a, b in zip(sched, sched[1:])) or sched[-1] < 0:
+        raise ValueError("k_sched needs Ly - s non-increasing counts starting at k")
+    cur = P
+    sets, layer_devs = [P], []
+    d_cur = None
     for l in range(s, ly):
         w = w_s if l == s else model.layer(l)
+        if l > s:
+            cur = narrow(cur, d_cur, sched[l - s])
+            sets.append(cur)
+        if l + 1 < ly:  # deviation over this layer's set, before its keys replace the stitched ones
+            if l == s:
+                d_cur = dev[cur]
+            else:
+                d_cur = kv_deviation(k_rows(cfg, w, h[cur], cur, ft, bf16_ops), kc[l, cur])
+                layer_devs.append(d_cur)
+        sel = np.concatenate([cur.astype(np.int64), np.arange(N, L)])
         if len(sel):
             h[sel] = layer_rows(cfg, w, h[sel], sel, kc[l], vc[l], ft, bf16_ops)
     out = rms_norm(h[N:], model.final_norm, cfg.rms_eps, ft)
-    return BlendResult(kc, vc, out, P, dev, h)
+    return BlendResult(kc, vc, out, P, dev, h, sets, layer_devs)
 
 
 def direct_reuse(model, tokens, n_ctx, k_store, v_store, chunk_table, ft=np.float32, n_layers=None,

@@ -406,6 +406,91 @@ def test_blend_error_falls_as_ratio_rises():
     assert errs[0] > errs[2] > errs[3] and errs[3] < 1e-9
 
 
+# ------------------------------------------------------------------ gradual filtering
+
+def test_gradual_constant_schedule_is_single_selection():
+    """CacheBlend, "The Chicken-and-Egg Problem": a schedule that never narrows is the single
+    selection on layer s, result for result."""
+    model = _Model(TINY)
+    chunks, q, toks = _request(TINY)
+    ks, vs, table = _store(model, chunks, n_layers=4)
+    N = sum(len(c) for c in chunks)
+    a = oracle.blend_prefill(model, toks, N, ks, vs, table, 1, 20, ft=F64, n_layers=4)
+    b = oracle.blend_prefill(model, toks, N, ks, vs, table, 1, 20, ft=F64, n_layers=4, k_sched=[20, 20, 20])
+    for x, y in [(a.k, b.k), (a.v, b.v), (a.out, b.out), (a.hidden, b.hidden), (a.sel, b.sel), (a.dev, b.dev)]:
+        np.testing.assert_array_equal(x, y)
+    assert all(np.array_equal(t, a.sel) for t in b.sets)
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_QK], ids=["llama-style", "qk-norm"])
+def test_gradual_sets_nest_and_follow_the_cache_change(cfg):
+    """Gradual filtering, checked from the outputs alone: every layer's set is inside the previous
+    one and has the scheduled size; context rows outside a layer's set keep the stitched keys
+    there; the deviation reported for layer l equals the squared change between the fused keys
+    and the stitched keys on that layer's set (an independent route to Eq. 1 of Request Order
+    Matters §2.2); and the next set is the brute-force top of that deviation, lower position
+    first among equals."""
+    ly, s = 5, 1
+    model = _Model(cfg)
+    chunks, q, toks = _request(cfg)
+    ks, vs, table = _store(model, chunks, n_layers=ly)
+    N = sum(len(c) for c in chunks)
+    sched = [40, 30, 22, 15]
+    res = oracle.blend_prefill(model, toks, N, ks, vs, table, s, sched[0], ft=F64, n_layers=ly, k_sched=sched)
+    kst, _ = oracle.stitch(ks, vs, table, N, range(ly), cfg.rope_theta, F64)
+    assert [len(t) for t in res.sets] == sched
+    np.testing.assert_array_equal(res.sets[0], res.sel)
+    assert len(res.layer_devs) == ly - s - 2
+    for i, P in enumerate(res.sets):
+        l = s + i
+        assert list(P) == sorted(set(P.tolist()))
+        if i:
+            assert set(P.tolist()) <= set(res.sets[i - 1].tolist())
+        outside = np.setdiff1d(np.arange(N), P)
+        np.testing.assert_array_equal(res.k[l, outside], kst[l, outside])
+        change = np.sum((res.k[l, P] - kst[l, P]).reshape(len(P), -1) ** 2, axis=1)
+        if i == 0:
+            np.testing.assert_allclose(change, res.dev[P], rtol=1e-6)
+            d = res.dev[P]
+        elif l + 1 < ly:
+            np.testing.assert_allclose(res.layer_devs[i - 1], change, rtol=1e-6)
+            d = res.layer_devs[i - 1]
+        if l + 1 < ly:
+            want = [int(P[j]) for j in _brute_topk(d.tolist(), sched[i + 1])]
+            assert res.sets[i + 1].tolist() == want
+    # the first narrowing keeps the top of the selection layer's full ranking
+    assert res.sets[1].tolist() == _brute_topk(res.dev.tolist(), sched[1])
+
+
+def test_gradual_deviation_of_a_full_layer_is_the_full_prefill_key_change():
+    """With every context row recomputed on layers s and s + 1 (schedule N, N, k), those layers
+    are exact full prefill, so the deviation measured at layer s + 1 is the squared distance
+    between full prefill's keys and the stitched keys, and the last layer recomputes its top k."""
+    ly, s = 4, 1
+    model = _Model(TINY)
+    chunks, q, toks = _request(TINY)
+    ks, vs, table = _store(model, chunks, n_layers=ly)
+    N = sum(len(c) for c in chunks)
+    res = oracle.blend_prefill(model, toks, N, ks, vs, table, s, N, ft=F64, n_layers=ly, k_sched=[N, N, 17])
+    K, _, _, _ = oracle.full_prefill(model, toks, F64, n_layers=ly)
+    kst, _ = oracle.stitch(ks, vs, table, N, range(ly), TINY.rope_theta, F64)
+    np.testing.assert_allclose(res.k[: s + 2], K[: s + 2], rtol=1e-12, atol=1e-13)
+    want = np.sum((K[s + 1, :N] - kst[s + 1]).reshape(N, -1) ** 2, axis=1)
+    np.testing.assert_allclose(res.layer_devs[0], want, rtol=1e-6)
+    assert res.sets[2].tolist() == _brute_topk(want.astype(np.float32).tolist(), 17)
+
+
+def test_gradual_schedule_hand_values():
+    """Schedule rule: first budget(N, r_1), then max(1, floor(k * keep)) per layer, never below
+    budget(N, r). Values worked by hand."""
+    assert oracle.gradual_schedule(3072, 6, (20, 100), (9, 10), (15, 100)) == [614, 552, 496, 460, 460, 460]
+    assert oracle.gradual_schedule(100, 5, (50, 100), (1, 2), (5, 100)) == [50, 25, 12, 6, 5]
+    assert oracle.gradual_schedule(100, 3, (0, 100), (1, 2), (0, 100)) == [0, 0, 0]
+    assert oracle.gradual_schedule(10, 4, (30, 100), (0, 1), (0, 100)) == [3, 1, 1, 1]
+    with pytest.raises(ValueError):
+        oracle.gradual_schedule(100, 3, (10, 100), (1, 2), (20, 100))
+
+
 def test_rolling_window_full_ratio_equals_full_prefill_each_step():
     """Request Order Matters §4.1 rolling window: with rho = 100% every step equals the full
     prefill of the current window whatever the history; in pristine mode at rho = 0 every step
