@@ -119,8 +119,13 @@ def main():
 
     sweep = [0, 5, 10, 15, 30, 50, 100]
     k_of = {r: cf.budget(N, r, 100) for r in sweep}
+    # gradual filtering (the set narrows layer by layer toward r): 20% or 30% on the selection layer
+    gradual = {f"{a}%->{w.rho_num}% x{b}/10": cf.gradual_schedule(N, Ly - w.sel_layer, (a, 100), (b, 10),
+                                                                  (w.rho_num, w.rho_den))
+               for a, b in [(20, 9), (30, 8)]} if w.mode == "token" and w.sel_layer < Ly else {}
     ws_bytes = max([ctx.blend_prefill_workspace_size(N, U, kk, w.mode) for kk in list(k_of.values()) + [k]] +
-                   [ctx.blend_prefill_workspace_size(N, U, N, "all")])
+                   [ctx.blend_prefill_workspace_size(N, U, N, "all")] +
+                   [ctx.blend_prefill_gradual_workspace_size(N, U, w.sel_layer, g) for g in gradual.values()])
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     k_out = torch.zeros(Ly, L, kvd, dtype=dt, device="cuda")
     v_out = torch.zeros_like(k_out)
@@ -215,6 +220,16 @@ def main():
             sweep_res["ratios"][f"{r}%"] = {"k": k_of[r], "blend_ms": round(tb, 3), "speedup": round(t_full / tb, 3)}
         log(f"[bench] full prefill {t_full:.2f} ms; speedups " +
             ", ".join(f"{r}: {v['speedup']}x" for r, v in sweep_res["ratios"].items()))
+        sweep_res["gradual"] = {}
+        for name, sch in gradual.items():
+            def run_g(sch=sch):
+                ctx.blend_prefill_gradual(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, ks, vs, table,
+                                          w.sel_layer, sch, k_out, v_out, out if U else None, ws)
+            _, pg = timed(run_g, 5, 2)
+            tg = statistics.median(pg)
+            sweep_res["gradual"][name] = {"schedule": sch, "rows_recomputed": sum(sch), "blend_ms": round(tg, 3),
+                                          "speedup": round(t_full / tg, 3)}
+            log(f"[bench] gradual {name}: {tg:.2f} ms ({t_full / tg:.2f}x), schedule {sch[:4]}..{sch[-1]}")
 
     # ---------------------------------------------------------------- CPU oracle baseline (bounded sample)
     cpu = None

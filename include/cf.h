@@ -228,6 +228,36 @@ cf_status cf_blend_prefill(const cf_ctx* ctx, const cf_layer_weights* layers, co
                            int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* --------------------------------------------------------------------- cf_blend_prefill_gradual
+ * Blended prefill with gradual filtering (CacheBlend, "The Chicken-and-Egg Problem"): the
+ * recompute set narrows layer by layer instead of staying fixed. Steps 1-4 are those of
+ * cf_blend_prefill in token mode with k = k_sched[0]. Then layer sel_layer + i recomputes
+ * k_sched[i] context rows (plus the U query rows):
+ *  - at each layer l = sel_layer + i with 0 < i < n_layers - sel_layer - 1, the deviation of the
+ *    set's fresh keys against the stitched keys they replace is measured (Request Order
+ *    Matters §2.2 Eq. 1, fused into the key store: the old key is read before it is
+ *    overwritten);
+ *  - when k_sched[i + 1] < k_sched[i], layer l + 1 recomputes the k_sched[i + 1] rows of layer
+ *    l's set with the largest deviation (ties keep the lower position); after layer sel_layer
+ *    this is the top of the selection-layer ranking.
+ *  k_sched: host int32 [n_layers - sel_layer], k_sched[0] <= N, non-increasing, >= 0.
+ *  out_sets: optional device int32 [sum of k_sched]: each layer's set, ascending, layer by layer.
+ *  out_devs: optional device fp32 [N + sum of k_sched[i] for 0 < i < n_layers - sel_layer - 1]:
+ *    the selection-layer deviation over the N context rows, then each such layer's deviation
+ *    over its set, in set order.
+ *  ws: device workspace of cf_blend_prefill_gradual_workspace_size(ctx, N, U, sel_layer,
+ *    k_sched) bytes (0 if the schedule is invalid). Other arguments, ownership and errors as in
+ *    cf_blend_prefill; an invalid schedule is CF_EINVAL. */
+size_t cf_blend_prefill_gradual_workspace_size(const cf_ctx* ctx, int32_t N, int32_t U, int32_t sel_layer,
+                                               const int32_t* k_sched /* host */);
+cf_status cf_blend_prefill_gradual(const cf_ctx* ctx, const cf_layer_weights* layers, const void* embed,
+                                   const float* final_norm, const int32_t* tokens, int32_t N, int32_t U,
+                                   const void* k_store, const void* v_store, int64_t store_layer_stride,
+                                   int32_t store_rows, const int32_t* chunk_tab /* host [m][4] */, int32_t m,
+                                   int32_t sel_layer, const int32_t* k_sched /* host */, void* k_out,
+                                   void* v_out, int64_t out_layer_stride, float* out_hidden, int32_t* out_sets,
+                                   float* out_devs, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

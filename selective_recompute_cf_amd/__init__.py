@@ -21,7 +21,8 @@ MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
            "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
-           "cf_blend_prefill", "cf_profile_enable", "cf_profile_report", "cf_mfma_loop", "cf_copy_loop"]
+           "cf_blend_prefill", "cf_blend_prefill_gradual_workspace_size", "cf_blend_prefill_gradual",
+           "cf_profile_enable", "cf_profile_report", "cf_mfma_loop", "cf_copy_loop"]
 
 
 class CfError(RuntimeError):
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
         "cf_blend_prefill_workspace_size": (sz, [vp, i32, i32, i32, i32]),
         "cf_blend_prefill": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32, vp,
                                    i32, i32, i32, i32, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "cf_blend_prefill_gradual_workspace_size": (sz, [vp, i32, i32, i32, vp]),
+        "cf_blend_prefill_gradual": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32,
+                                           vp, i32, i32, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -225,6 +229,29 @@ class Context:
                                       0 if ws is None else ws.numel(), _stream(tokens.device)))
 
 
+    def blend_prefill_gradual_workspace_size(self, N: int, U: int, sel_layer: int, k_sched: Sequence[int]) -> int:
+        sched, _ = _host_i32(k_sched)
+        return int(lib().cf_blend_prefill_gradual_workspace_size(self.handle, N, U, sel_layer, sched))
+
+    def blend_prefill_gradual(self, layers, embed, final_norm, tokens, N: int, U: int, k_store, v_store,
+                              chunk_tab, sel_layer: int, k_sched: Sequence[int], k_out, v_out, out_hidden, ws,
+                              out_sets=None, out_devs=None, store_rows: Optional[int] = None,
+                              store_layer_stride: Optional[int] = None, out_layer_stride: Optional[int] = None):
+        """cf_blend_prefill_gradual: k_sched holds n_layers - sel_layer per-layer counts."""
+        if len(k_sched) != self.cfg.n_layers - sel_layer:
+            raise ValueError("k_sched needs one count per layer from sel_layer on")
+        tab, nflat = _host_i32(chunk_tab)
+        sched, _ = _host_i32(k_sched)
+        sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
+        sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
+        ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        _check(lib().cf_blend_prefill_gradual(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
+                                              _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, sched,
+                                              _ptr(k_out), _ptr(v_out), ols, _ptr(out_hidden), _ptr(out_sets),
+                                              _ptr(out_devs), _ptr(ws), 0 if ws is None else ws.numel(),
+                                              _stream(tokens.device)))
+
+
 def layer_struct(t: dict) -> LayerWeights:
     """LayerWeights from a dict of device tensors (keys as in cf_layer_weights)."""
     return LayerWeights(*[_ptr(t.get(n)) for n, _ in LayerWeights._fields_])
@@ -263,3 +290,22 @@ def budget(n_ctx: int, rho_num: int, rho_den: int) -> int:
     if rho_num == 0 or n_ctx == 0:
         return 0
     return max(1, (n_ctx * rho_num) // rho_den)
+
+
+def gradual_schedule(n_ctx: int, n_sched: int, first=(20, 100), keep=(9, 10), final=(15, 100)) -> List[int]:
+    """Per-layer recompute counts for cf_blend_prefill_gradual (CacheBlend, "The Chicken-and-Egg
+    Problem": the set narrows from r_1 toward r). The first count is budget(N, r_1); each next
+    one keeps max(1, floor(previous * keep)) rows but never fewer than budget(N, r). Ratios are
+    (numerator, denominator) integer pairs."""
+    top = budget(n_ctx, *first)
+    low = budget(n_ctx, *final)
+    if low > top:
+        raise ValueError("the final ratio must not exceed the first")
+    num, den = keep
+    if num < 0 or den <= 0 or num > den:
+        raise ValueError("keep must be in [0, 1]")
+    counts, cur = [], top
+    while len(counts) < n_sched:
+        counts.append(cur)
+        cur = 0 if cur == 0 else max(low, (cur * num) // den, 1)
+    return counts

@@ -159,10 +159,11 @@ LayerWs layer_ws(const cf_ctx* c, int L, int R, int ksel_rows = 0) {
 }
 
 struct PrefillWs {
-  size_t hidden, sel, ident, dev, topk, layer, total;
+  size_t hidden, sel, sel2, ident, dev, dev2, devh, topk, layer, total;
 };
 
-PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode) {
+// ks: the per-layer counts of gradual filtering (nks of them, ks[0] = k), or null
+PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode, const int32_t* ks = nullptr, int nks = 0) {
   const int L = N + U;
   PrefillWs p{};
   size_t off = 0;
@@ -171,10 +172,20 @@ PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode) {
   p.sel = take((size_t)L * 4);
   p.ident = take((size_t)L * 4);
   p.dev = take((size_t)std::max(N, 1) * 4);
-  p.topk = take(cf_topk_workspace_size(N, mode));
   // the layer scratch serves full-row layers (R = L) and selected-row layers (R = k + U)
   const LayerWs a = layer_ws(c, L, L, mode == CF_SEL_ALL ? 0 : N), b = layer_ws(c, L, std::min(L, k + U));
-  p.layer = take(std::max(a.total, b.total));
+  size_t layer = std::max(a.total, b.total), topk = cf_topk_workspace_size(N, mode);
+  if (ks) {  // a second set buffer, the per-head and per-row deviations of a set, each set size's scratch
+    p.sel2 = take((size_t)L * 4);
+    p.dev2 = take((size_t)std::max(k, 1) * 4);
+    p.devh = take((size_t)std::max(k, 1) * c->cfg.n_kv_heads * 4);
+    for (int i = 0; i < nks; ++i) {
+      layer = std::max(layer, layer_ws(c, L, std::min(L, ks[i] + U)).total);
+      topk = std::max(topk, cf_topk_workspace_size(ks[i], mode));
+    }
+  }
+  p.topk = take(topk);
+  p.layer = take(layer);
   p.total = off;
   return p;
 }
@@ -198,10 +209,12 @@ cf_status check_layer(const cf_ctx* c, const cf_layer_weights* w, int idx) {
 // previous layer on the same rows). next_norm: the next layer's attention-norm gain; when the down
 // projection is split along K, its reduction then also writes the next layer's X (bit-identical
 // to a separate normalisation) and *x_next is set.
+// dev_heads: also measure, for the first n_dev rows, each kv head's squared distance between the
+// fresh key and the cached key it replaces ([n_dev][n_kv_heads]).
 cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, void* kc, void* vc,
                     const int* sel, int n, int L, char* ws, const LayerWs& lw, hipStream_t st,
                     bool x_ready = false, const float* next_norm = nullptr, bool* x_next = nullptr,
-                    bool* sched_ready = nullptr) {
+                    bool* sched_ready = nullptr, float* dev_heads = nullptr, int n_dev = 0) {
   if (x_next) *x_next = false;
   if (n == 0) return CF_OK;
   const cf_model_cfg& m = c->cfg;
@@ -231,6 +244,7 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   qp.hq = m.n_q_heads; qp.hkv = m.n_kv_heads; qp.hd = hd; qp.qk_norm = m.qk_norm;
   qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = m.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
   qp.q_out = Q; qp.k_cache = kc; qp.v_cache = vc;
+  qp.dev_heads = dev_heads; qp.n_dev = dev_heads ? n_dev : 0;
   CF_RUN("qkv_post", cf::launch_qkv_post(dt, qp, st));
 
   cf::AttnArgs at{};
@@ -595,13 +609,18 @@ size_t cf_blend_prefill_workspace_size(const cf_ctx* c, int32_t N, int32_t U, in
   return prefill_ws(c, N, U, std::max(0, std::min(k, N)), mode).total;
 }
 
-cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* embed, const float* final_norm,
-                           const int32_t* tokens, int32_t N, int32_t U, const void* k_store, const void* v_store,
-                           int64_t sls, int32_t store_rows, const int32_t* tab, int32_t m, int32_t s_layer, int32_t k,
-                           int32_t mode, const int32_t* bounds, int32_t ns, void* k_out, void* v_out, int64_t ols,
-                           float* out_hidden, int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
-                           hipStream_t st) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// The blended prefill of cf_blend_prefill, and with ks (host, n_layers - s_layer counts) the
+// gradual filtering of cf_blend_prefill_gradual: out_sel then receives every layer's set and
+// out_dev the selection-layer deviation followed by each later layer's deviation over its set.
+cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* embed, const float* final_norm,
+                  const int32_t* tokens, int32_t N, int32_t U, const void* k_store, const void* v_store, int64_t sls,
+                  int32_t store_rows, const int32_t* tab, int32_t m, int32_t s_layer, int32_t k, int32_t mode,
+                  const int32_t* bounds, int32_t ns, const int32_t* ks, void* k_out, void* v_out, int64_t ols,
+                  float* out_hidden, int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes, hipStream_t st) {
   if (cf_status s = check_ctx(c)) return s;
   const cf_model_cfg& mc = c->cfg;
   const int L = N + U;
@@ -634,7 +653,14 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
   } else {
     k = N;
   }
-  const PrefillWs pw = prefill_ws(c, N, U, k, mode);
+  const int nks = mc.n_layers - s_layer;
+  if (ks) {
+    CF_CHECK(mode == CF_SEL_TOKEN_TOPK, CF_EINVAL, "gradual filtering ranks single tokens (token mode)");
+    CF_CHECK(ks[0] == k, CF_EINVAL, "k_sched[0]=%d must equal k=%d", ks[0], k);
+    for (int i = 1; i < nks; ++i)
+      CF_CHECK(ks[i] >= 0 && ks[i] <= ks[i - 1], CF_EINVAL, "k_sched must be non-increasing and >= 0 (entry %d)", i);
+  }
+  const PrefillWs pw = prefill_ws(c, N, U, k, mode, ks, ks ? nks : 0);
   CF_CHECK(ws && aligned16(ws) && ws_bytes >= pw.total, CF_EWORKSPACE, "workspace: need %zu bytes, got %zu", pw.total,
            ws_bytes);
   DeviceGuard guard(c->device);
@@ -697,22 +723,106 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
       if (out_sel) CF_RUN("copy", cf::launch_copy_i32(out_sel, sel, k, st));
     }
     CF_RUN("iota", cf::launch_iota(sel + k, U, N, st));
-    const LayerWs lw_sel = layer_ws(c, L, n_sel);
     xr = false;
     bool sched_sel = false;
-    for (int l = s_layer; l < mc.n_layers; ++l) {
-      const float* nn = l + 1 < mc.n_layers ? layers[l + 1].attn_norm : nullptr;
-      bool xn = false;
-      if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st, xr, nn, &xn,
-                                  &sched_sel))
-        return s;
-      xr = xn;
+    if (!ks) {
+      const LayerWs lw_sel = layer_ws(c, L, n_sel);
+      for (int l = s_layer; l < mc.n_layers; ++l) {
+        const float* nn = l + 1 < mc.n_layers ? layers[l + 1].attn_norm : nullptr;
+        bool xn = false;
+        if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st, xr, nn,
+                                    &xn, &sched_sel))
+          return s;
+        xr = xn;
+      }
+    } else {
+      // gradual filtering: layer s + i recomputes ks[i] context rows. Layers s < l < Ly - 1 also
+      // measure the deviation of their set (fused into the key store); when the next count is
+      // smaller, the next set is the top of that deviation (at layer s: of the full ranking).
+      int* cur = sel;
+      int* nxt = reinterpret_cast<int*>(W + pw.sel2);
+      float* dev2 = reinterpret_cast<float*>(W + pw.dev2);
+      float* devh = reinterpret_cast<float*>(W + pw.devh);
+      double* tkws = reinterpret_cast<double*>(W + pw.topk);
+      size_t set_off = k, dev_off = N;
+      for (int i = 0; i < nks; ++i) {
+        const int l = s_layer + i, kl = ks[i];
+        const bool last = i + 1 == nks;
+        const bool narrows = !last && ks[i + 1] < kl;
+        const LayerWs lw = layer_ws(c, L, kl + U);
+        const float* nn = last || narrows ? nullptr : layers[l + 1].attn_norm;
+        float* dh = i > 0 && !last && kl > 0 ? devh : nullptr;
+        if (i > 0 && out_sel && kl > 0) CF_RUN("copy", cf::launch_copy_i32(out_sel + set_off, cur, kl, st));
+        if (i > 0) set_off += kl;
+        bool xn = false;
+        if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), cur, kl + U, L, lws, lw, st, xr, nn, &xn,
+                                    &sched_sel, dh, kl))
+          return s;
+        xr = xn;
+        if (dh) {
+          CF_RUN("dev_rows", cf::launch_dev_rows(devh, kl, mc.n_kv_heads, dev2, st));
+          if (out_dev) CF_RUN("copy", cf::launch_copy_f32(out_dev + dev_off, dev2, kl, st));
+          dev_off += kl;
+        }
+        if (narrows) {
+          const int kn = ks[i + 1];
+          if (i == 0) {
+            if (cf_status s = enqueue_select(dev, N, kn, CF_SEL_TOKEN_TOPK, nullptr, 0, nxt, tkws, st)) return s;
+            CF_RUN("iota", cf::launch_iota(nxt + kn, U, N, st));
+          } else {
+            if (cf_status s = enqueue_select(dev2, kl, kn, CF_SEL_TOKEN_TOPK, nullptr, 0, nxt, tkws, st)) return s;
+            CF_RUN("sel_map", cf::launch_sel_map(nxt, cur, kn, U, N, st));
+          }
+          std::swap(cur, nxt);
+          sched_sel = false;
+        }
+      }
     }
   }
   if (U > 0)
     CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(cf::F32, hidden + (size_t)N * mc.d_model, nullptr, U, U, mc.d_model, final_norm,
                                    mc.rms_eps, out_hidden, mc.d_model, st));
   return CF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* embed, const float* final_norm,
+                           const int32_t* tokens, int32_t N, int32_t U, const void* k_store, const void* v_store,
+                           int64_t sls, int32_t store_rows, const int32_t* tab, int32_t m, int32_t s_layer, int32_t k,
+                           int32_t mode, const int32_t* bounds, int32_t ns, void* k_out, void* v_out, int64_t ols,
+                           float* out_hidden, int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
+                           hipStream_t st) {
+  g_err.clear();
+  return prefill(c, layers, embed, final_norm, tokens, N, U, k_store, v_store, sls, store_rows, tab, m, s_layer, k, mode,
+                 bounds, ns, nullptr, k_out, v_out, ols, out_hidden, out_sel, out_dev, ws, ws_bytes, st);
+}
+
+size_t cf_blend_prefill_gradual_workspace_size(const cf_ctx* c, int32_t N, int32_t U, int32_t s_layer,
+                                               const int32_t* k_sched) {
+  if (!c || !k_sched || N < 0 || U < 0 || N + U <= 0 || s_layer < 0 || s_layer >= c->cfg.n_layers) return 0;
+  const int nks = c->cfg.n_layers - s_layer;
+  for (int i = 0; i < nks; ++i)
+    if (k_sched[i] < 0 || k_sched[i] > N || (i && k_sched[i] > k_sched[i - 1])) return 0;
+  return prefill_ws(c, N, U, k_sched[0], CF_SEL_TOKEN_TOPK, k_sched, nks).total;
+}
+
+cf_status cf_blend_prefill_gradual(const cf_ctx* c, const cf_layer_weights* layers, const void* embed,
+                                   const float* final_norm, const int32_t* tokens, int32_t N, int32_t U,
+                                   const void* k_store, const void* v_store, int64_t sls, int32_t store_rows,
+                                   const int32_t* tab, int32_t m, int32_t s_layer, const int32_t* k_sched,
+                                   void* k_out, void* v_out, int64_t ols, float* out_hidden, int32_t* out_sets,
+                                   float* out_devs, void* ws, size_t ws_bytes, hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  CF_CHECK(k_sched, CF_EINVAL, "null k_sched");
+  CF_CHECK(s_layer >= 0 && s_layer < c->cfg.n_layers, CF_EINVAL, "sel_layer %d outside [0, %d)", s_layer,
+           c->cfg.n_layers);
+  return prefill(c, layers, embed, final_norm, tokens, N, U, k_store, v_store, sls, store_rows, tab, m, s_layer,
+                 k_sched[0], CF_SEL_TOKEN_TOPK, nullptr, 0, k_sched, k_out, v_out, ols, out_hidden, out_sets, out_devs,
+                 ws, ws_bytes, st);
 }
 
 }  // extern "C"

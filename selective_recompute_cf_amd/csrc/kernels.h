@@ -29,7 +29,9 @@ hipError_t launch_rmsnorm_rows(Dt out_dt, const float* x, const int* rows, int n
                                const float* g, float eps, void* out, int64_t ldo, hipStream_t st);
 // Post-process fp32 projection rows: qk-norm, RoPE at pos = rows[j], Q -> q_out (model dtype),
 // K/V scattered into the cache at row pos. With dev != nullptr, only K is present (ld = kvd),
-// positions are j, and dev[j] = sum (rope(k) - k_ref[j])^2; nothing is stored.
+// positions are j, and dev[j] = sum (rope(k) - k_ref[j])^2; nothing is stored. With dev_heads
+// (store mode, hd 64 or 128), rows j < n_dev also get dev_heads[j * hkv + h] = sum over head h
+// of (rope(k) - the cached key it replaces)^2, read before the store.
 struct QkvPost {
   const float* qkv; int64_t ld;
   const int* rows; int n; int L;
@@ -38,8 +40,14 @@ struct QkvPost {
   void* q_out; void* k_cache; void* v_cache;
   float* dev; const void* k_ref;
   int splits; int64_t split_stride;    // qkv holds `splits` partial sums, split_stride floats apart
+  float* dev_heads; int n_dev;
 };
 hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st);
+// dev[j] = sum over h < hkv of dev_heads[j * hkv + h], in head order (j < n).
+hipError_t launch_dev_rows(const float* dev_heads, int n, int hkv, float* dev, hipStream_t st);
+// Narrowed recompute set: sel[j] = prev[sel[j]] for j < k (sel holds indices into prev on entry),
+// then sel[k + u] = n_ctx + u for u < U (the query rows).
+hipError_t launch_sel_map(int* sel, const int* prev, int k, int U, int n_ctx, hipStream_t st);
 hipError_t launch_iota(int* out, int n, int start, hipStream_t st);
 hipError_t launch_copy_i32(int* dst, const int* src, int n, hipStream_t st);
 hipError_t launch_copy_f32(float* dst, const float* src, int n, hipStream_t st);

@@ -274,9 +274,25 @@ __global__ __launch_bounds__(256) void qkv_post_vec_kernel(QkvPost p) {
   const float4 c = *reinterpret_cast<const float4*>(p.cos_t + (int64_t)pos * HALF + e);
   const float4 sn = *reinterpret_cast<const float4*>(p.sin_t + (int64_t)pos * HALF + e);
   T* dst = isq ? (T*)p.q_out + (int64_t)j * (nq * HD) + hh * HD : (T*)p.k_cache + (int64_t)pos * kvd + hh * HD;
-  store4(dst + e, x1.x * c.x - x2.x * sn.x, x1.y * c.y - x2.y * sn.y, x1.z * c.z - x2.z * sn.z, x1.w * c.w - x2.w * sn.w);
-  store4(dst + e + HALF, x1.x * sn.x + x2.x * c.x, x1.y * sn.y + x2.y * c.y, x1.z * sn.z + x2.z * c.z,
-         x1.w * sn.w + x2.w * c.w);
+  const float y1[4] = {x1.x * c.x - x2.x * sn.x, x1.y * c.y - x2.y * sn.y, x1.z * c.z - x2.z * sn.z,
+                       x1.w * c.w - x2.w * sn.w};
+  const float y2[4] = {x1.x * sn.x + x2.x * c.x, x1.y * sn.y + x2.y * c.y, x1.z * sn.z + x2.z * c.z,
+                       x1.w * sn.w + x2.w * c.w};
+  if (!isq && p.dev_heads && j < p.n_dev) {  // uniform over the head's TPH threads
+    // deviation of the fresh key from the stitched key it replaces (Request Order Matters Eq. 1),
+    // per head; the row sum over heads is taken by launch_dev_rows
+    float dd = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = y1[i] - to_f(dst[e + i]), b = y2[i] - to_f(dst[e + HALF + i]);
+      dd += a * a + b * b;
+    }
+#pragma unroll
+    for (int off = 1; off < TPH; off <<= 1) dd += __shfl_xor(dd, off, WAVE);
+    if (e == 0) p.dev_heads[(int64_t)j * nkv + hh] = dd;
+  }
+  store4(dst + e, y1[0], y1[1], y1[2], y1[3]);
+  store4(dst + e + HALF, y2[0], y2[1], y2[2], y2[3]);
 }
 
 hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st) {
@@ -293,12 +309,41 @@ hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st) {
     }
     return hipGetLastError();
   }
+  if (p.dev_heads) return hipErrorInvalidValue;  // the per-head deviation lives in the vector kernel only
   const int nh = p.dev ? 1 : p.hq + 2 * p.hkv;
   const dim3 grid(p.n, p.dev ? 1 : (nh + 3) / 4);
   if (dt == BF16)
     hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void dev_rows_kernel(const float* __restrict__ dh, int n, int hkv,
+                                                        float* __restrict__ dev) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
+  float s = 0.f;
+  for (int h = 0; h < hkv; ++h) s += dh[(int64_t)j * hkv + h];
+  dev[j] = s;
+}
+
+hipError_t launch_dev_rows(const float* dev_heads, int n, int hkv, float* dev, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dev_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, st, dev_heads, n, hkv, dev);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void sel_map_kernel(int* __restrict__ sel, const int* __restrict__ prev, int k,
+                                                       int U, int n_ctx) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < k) sel[j] = prev[sel[j]];
+  else if (j < k + U) sel[j] = n_ctx + (j - k);
+}
+
+hipError_t launch_sel_map(int* sel, const int* prev, int k, int U, int n_ctx, hipStream_t st) {
+  if (k + U <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_map_kernel, dim3((k + U + 255) / 256), dim3(256), 0, st, sel, prev, k, U, n_ctx);
   return hipGetLastError();
 }
 

@@ -104,3 +104,37 @@ def gpu_blend(ctx, dm, tokens, N, k_store, v_store, table, sel_layer, k, mode, s
         r["sel"] = sel.cpu().numpy()[:k]
         r["dev"] = dev.cpu().numpy()[:N]
     return r
+
+
+def gpu_blend_gradual(ctx, dm, tokens, N, k_store, v_store, table, sel_layer, k_sched):
+    """One cf_blend_prefill_gradual call; returns dict of host arrays, with "sets" (one array per
+    layer from sel_layer on) and "layer_devs" (one per layer strictly between sel_layer and the last)."""
+    import torch
+    L = len(tokens)
+    U = L - N
+    Ly, kvd, d = dm.n_layers, ctx.kv_dim, dm.cfg.d_model
+    dt = torch_dtype(dm.dtype)
+    k_sched = [int(x) for x in k_sched]
+    k_out = torch.zeros(Ly, L, kvd, dtype=dt, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    out = torch.zeros(max(U, 1), d, dtype=torch.float32, device="cuda")
+    sets = torch.full((max(sum(k_sched), 1),), -1, dtype=torch.int32, device="cuda")
+    n_dev = N + sum(k_sched[1:-1])
+    devs = torch.full((max(n_dev, 1),), -1.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ctx.blend_prefill_gradual_workspace_size(N, U, sel_layer, k_sched), dtype=torch.uint8,
+                     device="cuda")
+    tok = torch.from_numpy(np.asarray(tokens, np.int32)).cuda()
+    ctx.blend_prefill_gradual(dm.array, dm.embed, dm.final_norm, tok, N, U, k_store, v_store, table, sel_layer,
+                              k_sched, k_out, v_out, out if U else None, ws, out_sets=sets, out_devs=devs)
+    torch.cuda.synchronize()
+    s_host, d_host = sets.cpu().numpy(), devs.cpu().numpy()
+    r = dict(k=host(k_out), v=host(v_out), out=host(out)[:U], dev=d_host[:N], sets=[], layer_devs=[])
+    o = 0
+    for kk in k_sched:
+        r["sets"].append(s_host[o:o + kk])
+        o += kk
+    o = N
+    for kk in k_sched[1:-1]:
+        r["layer_devs"].append(d_host[o:o + kk])
+        o += kk
+    return r

@@ -70,6 +70,22 @@ def test_null_context_rejected(L):
                               None, None, 0, None, None, None, None, 0, None) == cf.CF_EINVAL
     assert L.cf_blend_layer_workspace_size(None, 10, 5) == 0
     assert L.cf_blend_prefill_workspace_size(None, 10, 5, 3, 0) == 0
+    sched = (ctypes.c_int32 * 2)(3, 2)
+    assert L.cf_blend_prefill_gradual(None, None, None, None, None, 10, 5, None, None, 0, 0, None, 0, 1, sched, None,
+                                      None, 0, None, None, None, None, 0, None) == cf.CF_EINVAL
+    assert L.cf_blend_prefill_gradual_workspace_size(None, 10, 5, 1, sched) == 0
+
+
+def test_gradual_schedule_host_logic_agrees_with_oracle():
+    for n in [0, 1, 10, 512, 3072, 10240]:
+        for first, keep, final in [((20, 100), (9, 10), (15, 100)), ((30, 100), (1, 2), (5, 100)),
+                                   ((15, 100), (1, 1), (15, 100)), ((0, 100), (1, 2), (0, 100)),
+                                   ((100, 100), (0, 1), (1, 100))]:
+            for n_sched in [1, 3, 31]:
+                assert cf.gradual_schedule(n, n_sched, first, keep, final) == \
+                    oracle.gradual_schedule(n, n_sched, first, keep, final)
+    with pytest.raises(ValueError):
+        cf.gradual_schedule(100, 3, (10, 100), (1, 2), (20, 100))
 
 
 def test_context_rejects_bad_shapes(L):

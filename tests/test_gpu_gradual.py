@@ -1,0 +1,203 @@
+"""GPU parity of cf_blend_prefill_gradual (gradual filtering, CacheBlend "The Chicken-and-Egg
+Problem") against the oracle's blend_prefill(k_sched=...), on seeded random-init models.
+
+Bars, per layer of the schedule:
+* the GPU's next set equals the oracle's narrowing run on the GPU's own deviation of the current
+  set (bit-exact: top-k and the index map), and each set overlaps the fp32 oracle's by the
+  selection bar of the single-selection tests;
+* fp32 models: deviations, fused K/V and the final query rows elementwise within 1e-4 + 1e-4 |ref|;
+* bf16 models: norm-wise error against the fp32 oracle at most twice that of the oracle's own
+  bf16-arithmetic run plus 2e-3 (K/V on the rows whose per-layer selection agrees);
+* a schedule that never narrows reproduces cf_blend_prefill bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import selective_recompute_cf_amd as cf
+import synth
+from selective_recompute_cf_amd.device import DeviceModel
+from tests._gpu import (compare, context, gpu_blend, gpu_blend_gradual, gpu_chunk_store, host, overlap, say,
+                        selection_bar)
+
+pytestmark = pytest.mark.gpu
+
+
+def nrel(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def _oracle(model, chunks, toks, N, s, sched, ly, bf16_ops):
+    ks, vs, table, row = [], [], [], 0
+    for c in chunks:
+        a, b = oracle.chunk_prefill(model, c, np.float32, ly, bf16_ops)
+        ks.append(a)
+        vs.append(b)
+        table.append((row, 0, row, len(c)))
+        row += len(c)
+    ks, vs = np.concatenate(ks, 1), np.concatenate(vs, 1)
+    return oracle.blend_prefill(model, toks, N, ks, vs, table, s, sched[0], "token", None, np.float32, ly, bf16_ops,
+                                k_sched=sched)
+
+
+def _setup(w, ly):
+    model = synth.Model(w.model)
+    chunks, _, toks = synth.request_tokens(w)
+    cfg = model.cfg
+    ctx = context(cfg.replace(n_layers=ly), max_pos=max(4096, len(toks) + 1))
+    dm = DeviceModel(model, n_layers=ly)
+    gk, gv, starts = gpu_chunk_store(ctx, dm, chunks)
+    table = [(st, 0, st, len(c)) for st, c in zip(starts, chunks)]
+    return model, chunks, toks, ctx, dm, gk, gv, table
+
+
+def _self_consistent(g, sched):
+    """The GPU's narrowing equals the oracle's narrowing applied to the GPU's own deviations."""
+    sets = g["sets"]
+    assert [len(t) for t in sets] == list(sched)
+    np.testing.assert_array_equal(sets[0], oracle.select_topk(g["dev"], sched[0]))
+    for i in range(1, len(sets)):
+        assert np.all(np.diff(sets[i]) > 0)
+        d = g["dev"][sets[i - 1]] if i == 1 else g["layer_devs"][i - 2]
+        np.testing.assert_array_equal(sets[i], oracle.narrow(sets[i - 1], d, sched[i]))
+
+
+def _layer_agree(N, L, s, ly, sets_a, sets_b):
+    """[ly, L] mask: rows of layer l >= s whose membership in that layer's set agrees (query rows and
+    layers < s always agree)."""
+    m = np.ones((ly, L), bool)
+    for i, (a, b) in enumerate(zip(sets_a, sets_b)):
+        x = np.zeros(L, bool)
+        y = np.zeros(L, bool)
+        x[np.asarray(a, int)] = True
+        y[np.asarray(b, int)] = True
+        m[s + i, :N] = x[:N] == y[:N]
+    return m
+
+
+def _run_and_check(w, ly, sched, s=1):
+    N, L = w.n_ctx, w.n_total
+    model, chunks, toks, ctx, dm, gk, gv, table = _setup(w, ly)
+    say(f"gradual {w.name} layers={ly} schedule={sched}")
+    g = gpu_blend_gradual(ctx, dm, toks, N, gk, gv, table, s, sched)
+    _self_consistent(g, sched)
+    r32 = _oracle(model, chunks, toks, N, s, sched, ly, False)
+    r16 = _oracle(model, chunks, toks, N, s, sched, ly, True) if model.cfg.dtype == "bf16" else None
+    for i, (gs, os32) in enumerate(zip(g["sets"], r32.sets)):
+        ov = overlap(gs, os32)
+        bar = selection_bar(None if r16 is None else r16.sets[i], os32)
+        say(f"  layer {s + i}: {len(gs)} rows, overlap with fp32 oracle {ov:.4f} (bar {bar:.4f})")
+        assert ov >= bar
+    shape = g["k"].shape
+    if r16 is None:
+        assert all(np.array_equal(a, b) for a, b in zip(g["sets"], r32.sets))
+        compare("dev", g["dev"], r32.dev, atol=1e-4 * float(np.median(r32.dev)), rtol=1e-3)
+        for i, (a, b) in enumerate(zip(g["layer_devs"], r32.layer_devs)):
+            compare(f"dev layer {s + 1 + i}", a, b, atol=1e-4 * float(np.median(r32.dev)), rtol=1e-3)
+        compare("out", g["out"], r32.out, "f32")
+        compare("K", g["k"], r32.k.reshape(shape), "f32")
+        compare("V", g["v"], r32.v.reshape(shape), "f32")
+        return g, r32
+    ag = _layer_agree(N, L, s, ly, g["sets"], r32.sets)
+    ao = _layer_agree(N, L, s, ly, r16.sets, r32.sets)
+    k32, v32 = r32.k.reshape(shape), r32.v.reshape(shape)
+    items = [("dev", g["dev"], r16.dev, r32.dev, r32.dev),
+             ("out", g["out"], r16.out, r32.out, r32.out),
+             ("K", g["k"][ag], r16.k.reshape(shape)[ao], k32[ag], k32[ao]),
+             ("V", g["v"][ag], r16.v.reshape(shape)[ao], v32[ag], v32[ao])]
+    for name, gv_, o16, gref, oref in items:
+        e_gpu, e_ref = nrel(gv_, gref), nrel(o16, oref)
+        bound = 2.0 * e_ref + 2e-3
+        say(f"  {name}: gpu vs fp32 oracle norm_rel={e_gpu:.3e}; bf16 oracle {e_ref:.3e}; bound {bound:.3e}")
+        assert e_gpu <= bound, name
+    # later-layer deviations on the rows that both sets hold
+    for i in range(len(g["layer_devs"])):
+        a_set, b_set = g["sets"][i + 1], r32.sets[i + 1]
+        common, ia, ib = np.intersect1d(a_set, b_set, return_indices=True)
+        _, ja, jb = np.intersect1d(r16.sets[i + 1], b_set, return_indices=True)
+        e_gpu = nrel(g["layer_devs"][i][ia], r32.layer_devs[i][ib])
+        e_ref = nrel(r16.layer_devs[i][ja], r32.layer_devs[i][jb])
+        say(f"  dev layer {s + 1 + i} ({len(common)} common rows): norm_rel={e_gpu:.3e}; bf16 oracle {e_ref:.3e}")
+        assert e_gpu <= 2.0 * e_ref + 2e-3
+    return g, r32
+
+
+def test_tiny_fp32_narrowing_schedule():
+    """fp32, 5 layers, 4 x 128 + 32: 25% on layer 1 narrowing by 0.8 per layer toward 15%."""
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(n_layers=5))
+    sched = cf.gradual_schedule(w.n_ctx, 4, (25, 100), (8, 10), (15, 100))
+    assert sched == [128, 102, 81, 76]
+    _run_and_check(w, 5, sched)
+
+
+def test_tiny_fp32_schedule_to_zero_and_sel_layer_2():
+    """Counts that reach 0 (only the query rows recomputed at the end), selection on layer 2."""
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(n_layers=5))
+    _run_and_check(w, 5, [60, 7, 0], s=2)
+
+
+def test_tiny_bf16_no_query_rows():
+    w = synth.WORKLOADS["tiny"].replace(n_query=0, model=synth.TINY.replace(dtype="bf16", n_layers=4))
+    _run_and_check(w, 4, [150, 100, 51])
+
+
+def test_gqa4_hd128_bf16():
+    m = synth.TINY.replace(name="mid", n_layers=4, d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                           d_ffn=2816, vocab=2000, rope_theta=5e5, dtype="bf16")
+    w = synth.Workload("mid-5x200+40", m, 5, 200, 40, 15, 100)
+    _run_and_check(w, 4, cf.gradual_schedule(w.n_ctx, 3, (30, 100), (7, 10), (15, 100)))
+
+
+def test_qknorm_hd64_bf16():
+    m = synth.TINY.replace(name="mid-qk", n_layers=4, d_model=512, n_q_heads=8, n_kv_heads=1, head_dim=64,
+                           d_ffn=1408, vocab=2000, rope_theta=1e6, rms_eps=1e-6, qk_norm=True, dtype="bf16")
+    w = synth.Workload("mid-qk-4x256+64", m, 4, 256, 64, 30, 100)
+    _run_and_check(w, 4, cf.gradual_schedule(w.n_ctx, 3, (40, 100), (8, 10), (30, 100)))
+
+
+def test_llama3_8b_shape_reduced_depth():
+    """Llama-3-8B shape at full width and request length (6 x 512 + 64), 4 layers: 20% on layer 1,
+    keeping 90% per layer toward 15%."""
+    w = synth.WORKLOADS["llama8b"]
+    sched = cf.gradual_schedule(w.n_ctx, 3, (20, 100), (9, 10), (15, 100))
+    assert sched == [614, 552, 496]
+    _run_and_check(w, 4, sched)
+
+
+def test_constant_schedule_is_single_selection_bit_for_bit():
+    """A schedule that never narrows runs the same kernels on the same rows as cf_blend_prefill
+    (plus the fused deviation reads), so every output is identical."""
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(dtype="bf16", n_layers=4))
+    N = w.n_ctx
+    model, chunks, toks, ctx, dm, gk, gv, table = _setup(w, 4)
+    k = oracle.budget(N, w.rho_num, w.rho_den)
+    g = gpu_blend_gradual(ctx, dm, toks, N, gk, gv, table, 1, [k, k, k])
+    one = gpu_blend(ctx, dm, toks, N, gk, gv, table, 1, k, "token")
+    for name in ["k", "v", "out", "dev"]:
+        np.testing.assert_array_equal(g[name], one[name], err_msg=name)
+    for t in g["sets"]:
+        np.testing.assert_array_equal(t, one["sel"])
+
+
+def test_invalid_schedules_rejected():
+    import torch
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(n_layers=3))
+    N, L = w.n_ctx, w.n_total
+    model, chunks, toks, ctx, dm, gk, gv, table = _setup(w, 3)
+    assert ctx.blend_prefill_gradual_workspace_size(N, L - N, 1, [10, 20]) == 0
+    assert ctx.blend_prefill_gradual_workspace_size(N, L - N, 1, [N + 1, 1]) == 0
+    ws = torch.empty(ctx.blend_prefill_gradual_workspace_size(N, L - N, 1, [20, 10]), dtype=torch.uint8, device="cuda")
+    k_out = torch.zeros(3, L, ctx.kv_dim, dtype=torch.float32, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    out = torch.zeros(L - N, dm.cfg.d_model, dtype=torch.float32, device="cuda")
+    tok = torch.from_numpy(np.asarray(toks, np.int32)).cuda()
+    for bad in ([10, 20], [20, -1], [N + 1, 1]):
+        with pytest.raises(cf.CfError) as e:
+            ctx.blend_prefill_gradual(dm.array, dm.embed, dm.final_norm, tok, N, L - N, gk, gv, table, 1, bad,
+                                      k_out, v_out, out, ws)
+        assert e.value.status == cf.CF_EINVAL
+    with pytest.raises(cf.CfError) as e:  # workspace sized for a smaller schedule
+        ctx.blend_prefill_gradual(dm.array, dm.embed, dm.final_norm, tok, N, L - N, gk, gv, table, 1, [N, N],
+                                  k_out, v_out, out, ws)
+    assert e.value.status == cf.CF_EWORKSPACE
