@@ -230,6 +230,8 @@ def main():
             sweep_res["gradual"][name] = {"schedule": sch, "rows_recomputed": sum(sch), "blend_ms": round(tg, 3),
                                           "speedup": round(t_full / tg, 3)}
             log(f"[bench] gradual {name}: {tg:.2f} ms ({t_full / tg:.2f}x), schedule {sch[:4]}..{sch[-1]}")
+        sweep_res["streamed"] = streamed_pipeline(ctx, dm, w, tok_dev, ks, vs, table, spans, k_out, v_out, out,
+                                                  k_of, sweep_res, timed)
 
     # ---------------------------------------------------------------- CPU oracle baseline (bounded sample)
     cpu = None
@@ -260,6 +262,62 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def streamed_pipeline(ctx, dm, w, tok_dev, ks, vs, table, spans, k_out, v_out, out, k_of, sweep_res, timed):
+    """The store in pinned host memory, loaded layer by layer under the recompute
+    (cf_blend_prefill_streamed), and the loading controller's ratio (CacheBlend, "Hiding Recompute
+    Behind I/O"): per-layer load time of one store layer, per-layer recompute time of one
+    cf_blend_layer pass at each ratio, r = max(r_load, 15%), and the streamed prefill against the
+    resident-store prefill at 15% and at the controller's r."""
+    import torch
+    import selective_recompute_cf_amd as cf
+    cfg = dm.cfg
+    N, U, L = w.n_ctx, w.n_query, w.n_total
+    kvd = cfg.n_kv_heads * cfg.head_dim
+    hk = torch.empty(ks.shape, dtype=ks.dtype, pin_memory=True)
+    hv = torch.empty(vs.shape, dtype=vs.dtype, pin_memory=True)
+    hk.copy_(ks)
+    hv.copy_(vs)
+    stage = torch.empty(2, N, kvd, dtype=ks.dtype, device="cuda")
+
+    def load_layer():
+        stage[0].copy_(hk[w.sel_layer], non_blocking=True)
+        stage[1].copy_(hv[w.sel_layer], non_blocking=True)
+
+    _, pl = timed(load_layer, 10, 3)
+    t_load = statistics.median(pl)
+    layer_bytes = 2 * N * kvd * ks.element_size()
+    # one selective layer pass at each ratio (selected rows: the first k context rows + the query)
+    hidden = (0.1 * torch.randn(L, cfg.d_model, device="cuda")).float()
+    kc, vc = k_out[w.sel_layer].clone(), v_out[w.sel_layer].clone()
+    t_layer = {}
+    for r, kk in k_of.items():
+        sel = torch.cat([torch.arange(kk), torch.arange(N, L)]).int().cuda()
+        lws = torch.empty(ctx.blend_layer_workspace_size(L, kk + U), dtype=torch.uint8, device="cuda")
+        _, pr = timed(lambda: ctx.blend_layer(dm.array[w.sel_layer], hidden, kc, vc, sel, lws), 5, 2)
+        t_layer[(r, 100)] = statistics.median(pr)
+    r_ctl = cf.loading_controller(t_load, t_layer, (w.rho_num, w.rho_den))
+    res = {"h2d_GBs": round(layer_bytes / (t_load / 1e3) / 1e9, 1), "load_ms_per_layer": round(t_load, 4),
+           "recompute_ms_per_layer": {f"{a}%": round(t, 4) for (a, _), t in t_layer.items()},
+           "controller_ratio": f"{r_ctl[0]}/{r_ctl[1]}", "runs": {}}
+    ws = torch.empty(max(ctx.blend_prefill_streamed_workspace_size(N, U, cf.budget(N, *q), w.mode, N)
+                         for q in [(w.rho_num, w.rho_den), r_ctl]), dtype=torch.uint8, device="cuda")
+    for q in dict.fromkeys([(w.rho_num, w.rho_den), r_ctl]):
+        kk = cf.budget(N, *q)
+
+        def run_s(kk=kk):
+            ctx.blend_prefill_streamed(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, hk, hv, table, w.sel_layer,
+                                       kk, w.mode, spans, k_out, v_out, out if U else None, ws)
+
+        _, ps = timed(run_s, 5, 2)
+        t_s = statistics.median(ps)
+        resident = sweep_res["ratios"].get(f"{q[0] * 100 // q[1]}%", {}).get("blend_ms") if q[1] == 100 else None
+        res["runs"][f"{q[0]}/{q[1]}"] = {"k": kk, "streamed_ms": round(t_s, 3), "resident_ms": resident,
+                                         "load_ms_all_layers": round(t_load * (cfg.n_layers - w.sel_layer), 3)}
+    log(f"[bench] streamed store: {res['h2d_GBs']} GB/s host->device, {t_load:.3f} ms load per layer; "
+        f"controller r = {res['controller_ratio']}; runs {res['runs']}")
+    return res
 
 
 def _event_ms(fn, reps=5, warmup=2):

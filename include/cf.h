@@ -228,6 +228,38 @@ cf_status cf_blend_prefill(const cf_ctx* ctx, const cf_layer_weights* layers, co
                            int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* --------------------------------------------------------------------- cf_blend_prefill_streamed
+ * cf_blend_prefill with the chunk store in host memory, loaded layer by layer while the
+ * previous layers are recomputed (CacheBlend, "Hiding Recompute Behind I/O": selective
+ * recompute of one layer runs while the next layer's cache is fetched). Layer l >= sel_layer
+ * of k_store/v_store (store_rows * kvd elements each, at element offset l * store_layer_stride)
+ * is copied host-to-device into one of two workspace staging slots on the context's copy
+ * stream, one layer ahead; the layer is re-positioned from its slot into k_out/v_out right
+ * before it is used, which frees the slot for layer l + 2. The copies begin after the work
+ * already enqueued on `stream` and every one of them is waited for on `stream`, so the call
+ * stays stream-ordered. Results are those of cf_blend_prefill with the same arguments.
+ *  k_store, v_store: PINNED host memory (hipHostMalloc or equivalent), same layout as in
+ *    cf_blend_prefill; other memory is rejected with CF_EINVAL. The caller keeps them unchanged
+ *    until the stream has passed the call.
+ *  ws: device workspace of cf_blend_prefill_streamed_workspace_size(ctx, N, U, k, mode,
+ *    store_rows) bytes.
+ * One streamed call per context is in flight at a time: a call first waits on the host for the
+ * previous streamed call of the same context to finish (copies queued behind an earlier,
+ * still running call stalled the enqueueing thread inside the runtime and slowed that call).
+ * The context's copy stream and events are shared by its calls: calls of this function on one
+ * context must be made from one host thread at a time. */
+size_t cf_blend_prefill_streamed_workspace_size(const cf_ctx* ctx, int32_t N, int32_t U, int32_t k,
+                                                int32_t mode, int32_t store_rows);
+cf_status cf_blend_prefill_streamed(const cf_ctx* ctx, const cf_layer_weights* layers, const void* embed,
+                                    const float* final_norm, const int32_t* tokens, int32_t N, int32_t U,
+                                    const void* k_store /* pinned host */, const void* v_store /* pinned host */,
+                                    int64_t store_layer_stride, int32_t store_rows,
+                                    const int32_t* chunk_tab /* host [m][4] */, int32_t m, int32_t sel_layer,
+                                    int32_t k, int32_t mode, const int32_t* span_bounds /* host */,
+                                    int32_t n_spans, void* k_out, void* v_out, int64_t out_layer_stride,
+                                    float* out_hidden, int32_t* out_sel, float* out_dev, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+
 /* --------------------------------------------------------------------- cf_blend_prefill_gradual
  * Blended prefill with gradual filtering (CacheBlend, "The Chicken-and-Egg Problem"): the
  * recompute set narrows layer by layer instead of staying fixed. Steps 1-4 are those of

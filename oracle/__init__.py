@@ -22,11 +22,12 @@ default (fp64 where a step says so, and fp64 throughout when asked), following:
 from .model import (rms_norm, rope, rope_angles, causal_attention, layer_rows, full_prefill, bf16_round,
                     chunk_prefill)
 from .blend import (budget, reposition, stitch, kv_deviation, select_topk, select_doc_spans,
-                    blend_prefill, direct_reuse, RollingWindow, BlendResult, narrow, gradual_schedule)
+                    blend_prefill, direct_reuse, RollingWindow, BlendResult, narrow, gradual_schedule,
+                    loading_ratio)
 
 __all__ = [
     "bf16_round", "rms_norm", "rope", "rope_angles", "causal_attention", "layer_rows", "full_prefill",
     "chunk_prefill", "budget", "reposition", "stitch", "kv_deviation", "select_topk",
     "select_doc_spans", "blend_prefill", "direct_reuse", "RollingWindow", "BlendResult", "narrow",
-    "gradual_schedule",
+    "gradual_schedule", "loading_ratio",
 ]

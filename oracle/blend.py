@@ -205,6 +205,19 @@ def gradual_schedule(n_ctx: int, n_sched: int, first: Tuple[int, int], keep: Tup
     return out
 
 
+def loading_ratio(load_ms: float, recompute_ms, floor=(15, 100)) -> Tuple[int, int]:
+    """CacheBlend's loading controller ("Hiding Recompute Behind I/O"): recompute is free while a
+    layer's recompute takes no longer than loading the next layer's cache, so the controller takes
+    the largest ratio r whose per-layer recompute time fits in the per-layer load time, then
+    clamps from below: r = max(r, r*), r* = ``floor``. ``recompute_ms`` maps (num, den) ratios to
+    measured per-layer times. Returns the chosen (num, den)."""
+    fits = [r for r, t in recompute_ms.items() if t <= load_ms]
+    best = max(fits, key=lambda r: r[0] / r[1]) if fits else None
+    if best is None or best[0] * floor[1] < floor[0] * best[1]:
+        return tuple(floor)
+    return tuple(best)
+
+
 # ------------------------------------------------------------------ blended prefill
 
 @dataclasses.dataclass

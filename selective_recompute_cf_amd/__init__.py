@@ -22,6 +22,7 @@ EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf
            "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
            "cf_blend_prefill", "cf_blend_prefill_gradual_workspace_size", "cf_blend_prefill_gradual",
+           "cf_blend_prefill_streamed_workspace_size", "cf_blend_prefill_streamed",
            "cf_profile_enable", "cf_profile_report", "cf_mfma_loop", "cf_copy_loop"]
 
 
@@ -73,6 +74,9 @@ def lib() -> ctypes.CDLL:
         "cf_blend_prefill": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32, vp,
                                    i32, i32, i32, i32, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "cf_blend_prefill_gradual_workspace_size": (sz, [vp, i32, i32, i32, vp]),
+        "cf_blend_prefill_streamed_workspace_size": (sz, [vp, i32, i32, i32, i32, i32]),
+        "cf_blend_prefill_streamed": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32,
+                                            vp, i32, i32, i32, i32, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "cf_blend_prefill_gradual": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32,
                                            vp, i32, i32, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
     }
@@ -229,6 +233,25 @@ class Context:
                                       0 if ws is None else ws.numel(), _stream(tokens.device)))
 
 
+    def blend_prefill_streamed_workspace_size(self, N: int, U: int, k: int, mode: str, store_rows: int) -> int:
+        return int(lib().cf_blend_prefill_streamed_workspace_size(self.handle, N, U, k, MODES[mode], store_rows))
+
+    def blend_prefill_streamed(self, layers, embed, final_norm, tokens, N: int, U: int, k_store, v_store,
+                               chunk_tab, sel_layer: int, k: int, mode: str, span_bounds, k_out, v_out, out_hidden,
+                               ws, out_sel=None, out_dev=None, store_rows: Optional[int] = None,
+                               store_layer_stride: Optional[int] = None, out_layer_stride: Optional[int] = None):
+        """cf_blend_prefill_streamed: k_store/v_store are pinned host tensors (pin_memory=True)."""
+        tab, nflat = _host_i32(chunk_tab)
+        spans, nb = _host_i32(span_bounds)
+        sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
+        sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
+        ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        _check(lib().cf_blend_prefill_streamed(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
+                                               _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, k,
+                                               MODES[mode], spans, max(0, nb - 1), _ptr(k_out), _ptr(v_out), ols,
+                                               _ptr(out_hidden), _ptr(out_sel), _ptr(out_dev), _ptr(ws),
+                                               0 if ws is None else ws.numel(), _stream(tokens.device)))
+
     def blend_prefill_gradual_workspace_size(self, N: int, U: int, sel_layer: int, k_sched: Sequence[int]) -> int:
         sched, _ = _host_i32(k_sched)
         return int(lib().cf_blend_prefill_gradual_workspace_size(self.handle, N, U, sel_layer, sched))
@@ -309,3 +332,17 @@ def gradual_schedule(n_ctx: int, n_sched: int, first=(20, 100), keep=(9, 10), fi
         counts.append(cur)
         cur = 0 if cur == 0 else max(low, (cur * num) // den, 1)
     return counts
+
+
+def loading_controller(load_ms: float, recompute_ms: dict, floor=(15, 100)):
+    """CacheBlend's loading controller ("Hiding Recompute Behind I/O"): the recompute ratio whose
+    per-layer recompute time still fits inside the per-layer cache load time, clamped from below
+    at ``floor`` (r = max(r_load, r*)). recompute_ms: {(num, den): measured per-layer ms}.
+    Returns (num, den)."""
+    best = None
+    for ratio, ms in recompute_ms.items():
+        if ms <= load_ms and (best is None or ratio[0] * best[1] > best[0] * ratio[1]):
+            best = ratio
+    if best is None or best[0] * floor[1] < floor[0] * best[1]:
+        return tuple(floor)
+    return tuple(best)

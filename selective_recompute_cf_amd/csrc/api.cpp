@@ -21,6 +21,13 @@ struct cf_ctx {
   int n_cu;
   float* cos_t;  // [max_pos][head_dim/2]
   float* sin_t;
+  // host-to-device copies of a chunk store in host memory (cf_blend_prefill_streamed): a copy
+  // stream (default priority) and, per staging slot, "copied" and "consumed" events
+  hipStream_t copy_st;
+  hipEvent_t start_ev, copied[2], consumed[2];
+  // end of the last two streamed calls (by call parity) and the number of streamed calls made
+  hipEvent_t done[2];
+  mutable long long streamed_calls;
 };
 
 namespace {
@@ -159,15 +166,18 @@ LayerWs layer_ws(const cf_ctx* c, int L, int R, int ksel_rows = 0) {
 }
 
 struct PrefillWs {
-  size_t hidden, sel, sel2, ident, dev, dev2, devh, topk, layer, total;
+  size_t hidden, sel, sel2, ident, dev, dev2, devh, topk, stage, layer, total;
 };
 
-// ks: the per-layer counts of gradual filtering (nks of them, ks[0] = k), or null
-PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode, const int32_t* ks = nullptr, int nks = 0) {
+// ks: the per-layer counts of gradual filtering (nks of them, ks[0] = k), or null.
+// stage_rows > 0: two staging slots of one store layer (K then V, stage_rows rows each).
+PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode, const int32_t* ks = nullptr, int nks = 0,
+                     int stage_rows = 0) {
   const int L = N + U;
   PrefillWs p{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  p.stage = take((size_t)2 * 2 * stage_rows * c->cfg.n_kv_heads * c->cfg.head_dim * esize(c));
   p.hidden = take((size_t)L * c->cfg.d_model * 4);
   p.sel = take((size_t)L * 4);
   p.ident = take((size_t)L * 4);
@@ -381,6 +391,17 @@ cf_status check_spans(const int32_t* b, int ns, int n) {
   return CF_OK;
 }
 
+// Frees what a context holds (members not yet created are null); the context's device is current.
+void destroy_ctx(cf_ctx* c) {
+  if (c->copy_st) (void)hipStreamSynchronize(c->copy_st);
+  for (hipEvent_t ev : {c->start_ev, c->copied[0], c->copied[1], c->consumed[0], c->consumed[1], c->done[0], c->done[1]})
+    if (ev) (void)hipEventDestroy(ev);
+  if (c->copy_st) (void)hipStreamDestroy(c->copy_st);
+  if (c->cos_t) (void)hipFree(c->cos_t);
+  if (c->sin_t) (void)hipFree(c->sin_t);
+  delete c;
+}
+
 cf_status enqueue_select(const float* dev, int n, int k, int mode, const int32_t* bounds, int ns, int* out,
                          double* ws, hipStream_t st) {
   if (k == 0) return CF_OK;
@@ -505,11 +526,14 @@ cf_status cf_ctx_create(const cf_model_cfg* cfg, int32_t max_pos, int32_t device
   if (e == hipSuccess) e = hipMalloc(&c->sin_t, bytes);
   if (e == hipSuccess) e = hipMemcpy(c->cos_t, cs.data(), bytes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->sin_t, sn.data(), bytes, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->copy_st, hipStreamNonBlocking);
+  hipEvent_t* evs[] = {&c->start_ev, &c->copied[0], &c->copied[1], &c->consumed[0], &c->consumed[1], &c->done[0],
+                       &c->done[1]};
+  for (hipEvent_t* ev : evs)
+    if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
   if (e != hipSuccess) {
-    if (c->cos_t) (void)hipFree(c->cos_t);
-    if (c->sin_t) (void)hipFree(c->sin_t);
-    delete c;
-    return fail(CF_EHIP, "RoPE table allocation: %s", hipGetErrorString(e));
+    destroy_ctx(c);
+    return fail(CF_EHIP, "context set-up: %s", hipGetErrorString(e));
   }
   *out = c;
   return CF_OK;
@@ -518,9 +542,7 @@ cf_status cf_ctx_create(const cf_model_cfg* cfg, int32_t max_pos, int32_t device
 void cf_ctx_destroy(cf_ctx* c) {
   if (!c) return;
   DeviceGuard guard(c->device);
-  if (c->cos_t) (void)hipFree(c->cos_t);
-  if (c->sin_t) (void)hipFree(c->sin_t);
-  delete c;
+  destroy_ctx(c);
 }
 
 cf_status cf_rope_reposition(const cf_ctx* c, const void* k_store, const void* v_store, int64_t sls,
@@ -616,11 +638,22 @@ namespace {
 // The blended prefill of cf_blend_prefill, and with ks (host, n_layers - s_layer counts) the
 // gradual filtering of cf_blend_prefill_gradual: out_sel then receives every layer's set and
 // out_dev the selection-layer deviation followed by each later layer's deviation over its set.
+bool pinned_host(const void* p) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // not a HIP allocation: clear the error so no later call reports it
+    return false;
+  }
+  return a.type == hipMemoryTypeHost;
+}
+
+// host_store: k_store/v_store are pinned host memory (cf_blend_prefill_streamed).
 cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* embed, const float* final_norm,
                   const int32_t* tokens, int32_t N, int32_t U, const void* k_store, const void* v_store, int64_t sls,
                   int32_t store_rows, const int32_t* tab, int32_t m, int32_t s_layer, int32_t k, int32_t mode,
                   const int32_t* bounds, int32_t ns, const int32_t* ks, void* k_out, void* v_out, int64_t ols,
-                  float* out_hidden, int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes, hipStream_t st) {
+                  float* out_hidden, int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes, hipStream_t st,
+                  bool host_store = false) {
   if (cf_status s = check_ctx(c)) return s;
   const cf_model_cfg& mc = c->cfg;
   const int L = N + U;
@@ -644,6 +677,9 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
     if (N > 0) {
       CF_CHECK(k_store && v_store && aligned16(k_store) && aligned16(v_store), CF_EINVAL,
                "chunk store null or misaligned");
+      if (host_store)
+        CF_CHECK(pinned_host(k_store) && pinned_host(v_store), CF_EINVAL,
+                 "the chunk store must be pinned host memory (hipHostMalloc)");
       CF_CHECK(store_rows >= 0 && sls >= store_rows * kvd && sls % 8 == 0, CF_ESHAPE,
                "store_layer_stride must hold store_rows*kvd elements and be a multiple of 8");
     }
@@ -660,7 +696,8 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
     for (int i = 1; i < nks; ++i)
       CF_CHECK(ks[i] >= 0 && ks[i] <= ks[i - 1], CF_EINVAL, "k_sched must be non-increasing and >= 0 (entry %d)", i);
   }
-  const PrefillWs pw = prefill_ws(c, N, U, k, mode, ks, ks ? nks : 0);
+  const bool streamed = host_store && !full && N > 0;
+  const PrefillWs pw = prefill_ws(c, N, U, k, mode, ks, ks ? nks : 0, streamed ? store_rows : 0);
   CF_CHECK(ws && aligned16(ws) && ws_bytes >= pw.total, CF_EWORKSPACE, "workspace: need %zu bytes, got %zu", pw.total,
            ws_bytes);
   DeviceGuard guard(c->device);
@@ -678,10 +715,51 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
   auto V_l = [&](int l) { return static_cast<char*>(v_out) + (size_t)l * ols * esize(c); };
 
   const int first_sel = full ? mc.n_layers : s_layer;
-  if (!full && N > 0 && first_sel < mc.n_layers)
+  if (!streamed && !full && N > 0 && first_sel < mc.n_layers)
     if (cf_status s = enqueue_reposition(c, k_store, v_store, sls, k_out, v_out, ols, tab, m, first_sel,
                                          mc.n_layers, st))
       return s;
+  // Streamed store: layer l's K/V go host -> slot (l - s) % 2 on the copy stream; the layer is
+  // re-positioned from its slot right before it is needed, which frees the slot for layer l + 2.
+  // The copies start after the caller's earlier work on `st` (the slots may still be in use by
+  // a previous call) and overlap this call's kernels; every copy is waited for on `st`.
+  const size_t slot_bytes = (size_t)store_rows * kvd * esize(c);
+  auto slot_k = [&](int l) { return W + pw.stage + (size_t)((l - first_sel) % 2) * 2 * slot_bytes; };
+  auto issue_copy = [&](int l) -> cf_status {
+    const int slot = (l - first_sel) % 2;
+    if (l - first_sel >= 2) CF_HIP(hipStreamWaitEvent(c->copy_st, c->consumed[slot], 0));
+    const size_t layer_off = (size_t)l * sls * esize(c);
+    CF_HIP(hipMemcpyAsync(slot_k(l), static_cast<const char*>(k_store) + layer_off, slot_bytes,
+                          hipMemcpyHostToDevice, c->copy_st));
+    CF_HIP(hipMemcpyAsync(slot_k(l) + slot_bytes, static_cast<const char*>(v_store) + layer_off, slot_bytes,
+                          hipMemcpyHostToDevice, c->copy_st));
+    CF_HIP(hipEventRecord(c->copied[slot], c->copy_st));
+    return CF_OK;
+  };
+  auto stitch_layer = [&](int l) -> cf_status {
+    if (!streamed) return CF_OK;
+    const int slot = (l - first_sel) % 2;
+    CF_HIP(hipStreamWaitEvent(st, c->copied[slot], 0));
+    if (cf_status s = enqueue_reposition(c, slot_k(l), slot_k(l) + slot_bytes, 0, K_l(l), V_l(l), ols, tab, m, 0, 1,
+                                         st))
+      return s;
+    CF_HIP(hipEventRecord(c->consumed[slot], st));
+    if (l + 2 < mc.n_layers) return issue_copy(l + 2);
+    return CF_OK;
+  };
+  if (streamed) {
+    // One streamed call of this context in flight at a time: a call waits on the host for the
+    // previous one to finish before it enqueues anything. Copies queued behind the work of an
+    // earlier, still running call have stalled the enqueueing thread inside the runtime and
+    // slowed the running call by up to a third; waiting costs only the start of this call's
+    // enqueue (its first kernels go out within microseconds).
+    const long long n = c->streamed_calls;
+    if (n >= 1) CF_HIP(hipEventSynchronize(c->done[(n - 1) % 2]));
+    CF_HIP(hipEventRecord(c->start_ev, st));
+    CF_HIP(hipStreamWaitEvent(c->copy_st, c->start_ev, 0));
+    for (int l = first_sel; l < std::min(first_sel + 2, mc.n_layers); ++l)
+      if (cf_status s = issue_copy(l)) return s;
+  }
   CF_RUN("embed", cf::launch_embed(dt, tokens, L, embed, mc.vocab, mc.d_model, hidden, st));
   CF_RUN("iota", cf::launch_iota(ident, L, 0, st));
   // consecutive layers on the same rows hand the next attention-norm input over (see run_layer)
@@ -698,6 +776,7 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
   if (!full) {
     const cf_layer_weights* w = layers + s_layer;
     const int n_sel = k + U;
+    if (cf_status s = stitch_layer(s_layer)) return s;
     if (N > 0) {
       // current keys of the context rows at the selection layer and their deviation
       void* X = lws + lw_full.x;  // the full-row layout holds N rows of X and of K
@@ -730,6 +809,8 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
       for (int l = s_layer; l < mc.n_layers; ++l) {
         const float* nn = l + 1 < mc.n_layers ? layers[l + 1].attn_norm : nullptr;
         bool xn = false;
+        if (l > s_layer)
+          if (cf_status s = stitch_layer(l)) return s;
         if (cf_status s = run_layer(c, layers + l, hidden, K_l(l), V_l(l), sel, n_sel, L, lws, lw_sel, st, xr, nn,
                                     &xn, &sched_sel))
           return s;
@@ -752,6 +833,8 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
         const LayerWs lw = layer_ws(c, L, kl + U);
         const float* nn = last || narrows ? nullptr : layers[l + 1].attn_norm;
         float* dh = i > 0 && !last && kl > 0 ? devh : nullptr;
+        if (i > 0)
+          if (cf_status s = stitch_layer(l)) return s;
         if (i > 0 && out_sel && kl > 0) CF_RUN("copy", cf::launch_copy_i32(out_sel + set_off, cur, kl, st));
         if (i > 0) set_off += kl;
         bool xn = false;
@@ -782,6 +865,10 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
   if (U > 0)
     CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(cf::F32, hidden + (size_t)N * mc.d_model, nullptr, U, U, mc.d_model, final_norm,
                                    mc.rms_eps, out_hidden, mc.d_model, st));
+  if (streamed) {
+    CF_HIP(hipEventRecord(c->done[c->streamed_calls % 2], st));
+    ++c->streamed_calls;
+  }
   return CF_OK;
 }
 
@@ -798,6 +885,25 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
   g_err.clear();
   return prefill(c, layers, embed, final_norm, tokens, N, U, k_store, v_store, sls, store_rows, tab, m, s_layer, k, mode,
                  bounds, ns, nullptr, k_out, v_out, ols, out_hidden, out_sel, out_dev, ws, ws_bytes, st);
+}
+
+size_t cf_blend_prefill_streamed_workspace_size(const cf_ctx* c, int32_t N, int32_t U, int32_t k, int32_t mode,
+                                                int32_t store_rows) {
+  if (!c || N < 0 || U < 0 || N + U <= 0 || store_rows < 0) return 0;
+  if (mode == CF_SEL_ALL) return prefill_ws(c, N, U, N, mode).total;
+  return prefill_ws(c, N, U, std::max(0, std::min(k, N)), mode, nullptr, 0, N > 0 ? store_rows : 0).total;
+}
+
+cf_status cf_blend_prefill_streamed(const cf_ctx* c, const cf_layer_weights* layers, const void* embed,
+                                    const float* final_norm, const int32_t* tokens, int32_t N, int32_t U,
+                                    const void* k_store, const void* v_store, int64_t sls, int32_t store_rows,
+                                    const int32_t* tab, int32_t m, int32_t s_layer, int32_t k, int32_t mode,
+                                    const int32_t* bounds, int32_t ns, void* k_out, void* v_out, int64_t ols,
+                                    float* out_hidden, int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
+                                    hipStream_t st) {
+  g_err.clear();
+  return prefill(c, layers, embed, final_norm, tokens, N, U, k_store, v_store, sls, store_rows, tab, m, s_layer, k, mode,
+                 bounds, ns, nullptr, k_out, v_out, ols, out_hidden, out_sel, out_dev, ws, ws_bytes, st, true);
 }
 
 size_t cf_blend_prefill_gradual_workspace_size(const cf_ctx* c, int32_t N, int32_t U, int32_t s_layer,

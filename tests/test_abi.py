@@ -74,6 +74,17 @@ def test_null_context_rejected(L):
     assert L.cf_blend_prefill_gradual(None, None, None, None, None, 10, 5, None, None, 0, 0, None, 0, 1, sched, None,
                                       None, 0, None, None, None, None, 0, None) == cf.CF_EINVAL
     assert L.cf_blend_prefill_gradual_workspace_size(None, 10, 5, 1, sched) == 0
+    assert L.cf_blend_prefill_streamed(None, None, None, None, None, 1, 0, None, None, 0, 0, None, 0, 0, 0, 0, None,
+                                       0, None, None, 0, None, None, None, None, 0, None) == cf.CF_EINVAL
+    assert L.cf_blend_prefill_streamed_workspace_size(None, 10, 5, 3, 0, 10) == 0
+
+
+def test_loading_controller_host_logic_agrees_with_oracle():
+    import itertools
+    tables = [{(5, 100): 1.0, (15, 100): 3.0, (30, 100): 6.0, (100, 100): 20.0},
+              {(1, 3): 2.0, (1, 2): 2.0, (3, 4): 9.0}, {}]
+    for t, load, floor in itertools.product(tables, [0.1, 2.0, 3.0, 6.5, 50.0], [(15, 100), (0, 1), (1, 3)]):
+        assert cf.loading_controller(load, t, floor) == oracle.loading_ratio(load, t, floor)
 
 
 def test_gradual_schedule_host_logic_agrees_with_oracle():

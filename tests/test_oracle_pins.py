@@ -491,6 +491,33 @@ def test_gradual_schedule_hand_values():
         oracle.gradual_schedule(100, 3, (10, 100), (1, 2), (20, 100))
 
 
+@pytest.mark.parametrize("row", _golden.page_numbers("hidden"))
+def test_loading_controller_page_table(row):
+    """CacheBlend blog, "Hiding Recompute Behind I/O": recompute at 15% is hidden behind the load
+    exactly when it is no slower than the load; the controller then raises r above 15% (7B),
+    otherwise it stays at the 15% floor (70B). Per-layer recompute time is taken proportional to
+    r, the page's own premise for solving T_recompute(r) = T_load."""
+    _, t15, load, hidden = row
+    t15, load, hidden = float(t15), float(load), int(hidden)
+    table = {(r, 100): t15 * r / 15 for r in (5, 10, 15, 20, 30, 50, 80, 100)}
+    r = oracle.loading_ratio(load, table)
+    assert (t15 <= load) == bool(hidden)
+    if hidden:  # largest tabulated r with t15 * r / 15 <= load
+        assert r == max((q for q in table if table[q] <= load), key=lambda q: q[0]) and r[0] > 15
+    else:
+        assert r == (15, 100)
+
+
+def test_loading_controller_hand_values():
+    table = {(5, 100): 1.0, (10, 100): 2.0, (15, 100): 3.0, (30, 100): 6.0, (50, 100): 10.0, (100, 100): 20.0}
+    assert oracle.loading_ratio(16.0, table) == (50, 100)
+    assert oracle.loading_ratio(6.0, table) == (30, 100)
+    assert oracle.loading_ratio(2.5, table) == (15, 100)   # only 5% and 10% fit: clamped up to 15%
+    assert oracle.loading_ratio(0.5, table) == (15, 100)   # nothing fits
+    assert oracle.loading_ratio(25.0, table) == (100, 100)
+    assert oracle.loading_ratio(2.5, table, floor=(5, 100)) == (10, 100)
+
+
 def test_rolling_window_full_ratio_equals_full_prefill_each_step():
     """Request Order Matters §4.1 rolling window: with rho = 100% every step equals the full
     prefill of the current window whatever the history; in pristine mode at rho = 0 every step
