@@ -30,7 +30,8 @@
  *    [out_features][in_features] (y = x W^T). Element type is the model dtype (CF_F32 or CF_BF16)
  *    except where an argument says fp32.
  *  - Streams: work is enqueued on `stream` (NULL = the null stream); no call synchronises the
- *    host with the device. Calls on different streams touching disjoint buffers are
+ *    host with the device, except that cf_blend_prefill_streamed first waits for the previous
+ *    streamed call of its context to finish. Calls on different streams touching disjoint buffers are
  *    independent; calls that share buffers must be ordered by the caller.
  *  - Errors: arguments are validated on the host before anything is enqueued. On failure the
  *    call returns a non-zero cf_status, enqueues nothing, and cf_last_error() describes the

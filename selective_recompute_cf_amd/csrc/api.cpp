@@ -1,6 +1,7 @@
 // libcf host side: argument validation, workspace layout, launch plan and the C ABI of
 // include/cf.h. Every step of the path is a kernel launch on the caller's stream; the host
-// never waits for the device inside a call.
+// never waits for the device inside a call (a streamed prefill waits only for the previous
+// streamed call of its context).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
