@@ -66,7 +66,9 @@ typedef enum { CF_F32 = 0, CF_BF16 = 1 } cf_dtype;
 typedef enum {
   CF_SEL_TOKEN_TOPK = 0, /* the k tokens of largest deviation (CacheBlend HKVD top-r%) */
   CF_SEL_DOC_SPANS = 1,  /* document-aligned spans (Request Order Matters §2.3) */
-  CF_SEL_ALL = 2         /* every row at every layer: ordinary full prefill (QCFuse Eq. 2) */
+  CF_SEL_ALL = 2,        /* every row at every layer: ordinary full prefill (QCFuse Eq. 2) */
+  CF_SEL_RANKED_SPANS = 3, /* spans in a caller-given order, e.g. random-document (Request Order Matters §2.3) */
+  CF_SEL_SPAN_HEADS = 4  /* the first tokens of every span (EPIC, as Request Order Matters §3 describes it) */
 } cf_select_mode;
 
 /* Decoder shape. Pre-norm layer: RMSNorm -> Q,K,V projections -> optional per-head RMS
@@ -171,10 +173,20 @@ cf_status cf_kv_deviation(const void* k_new, int32_t new_dtype, int64_t ld_new, 
  *    in the remaining budget, the walk stopping at the first span that does not; the r tokens
  *    still owed are the window [a, a+r) of that span maximising P[a+r] - P[a], P being the
  *    span's fp64 running sum from its start (smallest a among equals). Exactly k tokens.
+ *    Single-window is this mode with the one span {0, n}; fixed-chunk is this mode with equal
+ *    spans that cross the document bounds.
+ *  CF_SEL_RANKED_SPANS: random-document (Request Order Matters §2.3): span_bounds holds the
+ *    n_spans + 1 bounds followed by n_spans span indices, a permutation giving the order in
+ *    which spans are taken (the caller draws it); whole spans while they fit, then the first
+ *    r tokens of the first span that does not fit. dev is not read.
+ *  CF_SEL_SPAN_HEADS: EPIC's first tokens of every chunk (Request Order Matters §3) at the same
+ *    budget: T is the smallest head length with sum over spans of min(len, T) >= k, span j
+ *    gives its first min(len_j, T) tokens, and the last spans holding T give one token back each
+ *    until exactly k remain. dev is not read.
  * Results are exact (bit-identical to any implementation of the same order). 0 <= k <= n.
- * n_spans <= CF_MAX_SPANS. ws: device workspace of cf_topk_workspace_size(n, mode) bytes (span
- * mode always; token mode from n = 65536 up, where the selection runs on the whole GPU; the
- * size is 0 otherwise and ws may be NULL). A call without the workspace it needs fails with
+ * n_spans <= CF_MAX_SPANS. ws: device workspace of cf_topk_workspace_size(n, mode) bytes
+ * (document-aligned mode always; token mode from n = 65536 up, where the selection runs on the
+ * whole GPU; the size is 0 otherwise and ws may be NULL). A call without the workspace it needs fails with
  * CF_EWORKSPACE before anything is enqueued. */
 #define CF_MAX_SPANS 256
 size_t cf_topk_workspace_size(int32_t n, int32_t mode);

@@ -218,6 +218,91 @@ def loading_ratio(load_ms: float, recompute_ms, floor=(15, 100)) -> Tuple[int, i
     return tuple(best)
 
 
+def single_window_bounds(n_ctx: int) -> List[int]:
+    """Request Order Matters §2.3, single-window: the k-token window of largest total deviation
+    anywhere in the context. As one span [0, N), the document-aligned rule takes exactly that
+    window (a window of k tokens ranks the same by total or by mean)."""
+    return [0, int(n_ctx)]
+
+
+def fixed_chunk_bounds(n_ctx: int, size: int = 92, offset: int = 46) -> List[int]:
+    """Request Order Matters §2.3 and §4.4, fixed-chunk: equal spans of ``size`` tokens (92, the
+    median document length there) that cross document boundaries; the page shifts them off the
+    documents by an unstated offset (``offset``, half a span by default). Bounds 0, offset,
+    offset + size, ..., N (a leading span shorter than ``size`` and a ragged last one)."""
+    if size <= 0 or not 0 <= offset < max(size, 1):
+        raise ValueError("need size > 0 and 0 <= offset < size")
+    b = [0]
+    at = offset if offset > 0 else size
+    while at < n_ctx:
+        b.append(at)
+        at += size
+    b.append(int(n_ctx))
+    return b if n_ctx > 0 else [0, 0]
+
+
+def select_ranked_spans(n: int, k: int, bounds, order) -> np.ndarray:
+    """Request Order Matters §2.3, random-document: document spans taken in a given order
+    (the page draws a deterministic random order and ignores the deviation), whole spans while
+    they fit; the walk stops at the first span that does not fit and takes its first r tokens
+    (no deviation to pick a window by). Output: ascending int32 [k]."""
+    bounds = [int(b) for b in bounds]
+    order = [int(j) for j in order]
+    ns = len(bounds) - 1
+    if sorted(order) != list(range(ns)):
+        raise ValueError("order must be a permutation of the spans")
+    if not 0 <= k <= n or bounds[0] != 0 or bounds[-1] != n:
+        raise ValueError("bad arguments")
+    chosen, rem = [], k
+    for j in order:
+        if rem == 0:
+            break
+        a, b = bounds[j], bounds[j + 1]
+        if b - a <= rem:
+            chosen.extend(range(a, b))
+            rem -= b - a
+        else:
+            chosen.extend(range(a, a + rem))
+            rem = 0
+    return np.array(sorted(chosen), dtype=np.int32)
+
+
+def select_span_heads(n: int, k: int, bounds) -> np.ndarray:
+    """EPIC's LegoLink as Request Order Matters §3 describes it: a fixed set of initial tokens of
+    every reusable chunk. At an equal budget the k tokens are shared evenly (water-filling):
+    T is the smallest head length with sum_j min(len_j, T) >= k, chunk j gives its first
+    min(len_j, T) tokens, and the excess is taken back one token each from the last chunks whose
+    head is T long. Output: ascending int32 [k]."""
+    bounds = [int(b) for b in bounds]
+    lens = [b - a for a, b in zip(bounds[:-1], bounds[1:])]
+    if not 0 <= k <= n or bounds[0] != 0 or bounds[-1] != n:
+        raise ValueError("bad arguments")
+    T = 0
+    while sum(min(x, T) for x in lens) < k:
+        T += 1
+    heads = [min(x, T) for x in lens]
+    excess = sum(heads) - k
+    for j in reversed(range(len(lens))):
+        if excess == 0:
+            break
+        if heads[j] == T and T > 0:
+            heads[j] -= 1
+            excess -= 1
+    chosen = [i for j, t in enumerate(heads) for i in range(bounds[j], bounds[j] + t)]
+    return np.array(chosen, dtype=np.int32)
+
+
+def selection_stats(sel, d) -> Tuple[int, float]:
+    """Request Order Matters Table 2: how many separate contiguous regions the selection covers
+    (segments) and the share of the total selection-layer deviation its tokens carry (captured
+    deviation, fp64 sums)."""
+    sel = sorted(int(i) for i in sel)
+    segments = sum(1 for i, x in enumerate(sel) if i == 0 or x != sel[i - 1] + 1)
+    d = _canonical(d).astype(np.float64)
+    total = float(np.sum(d))
+    return segments, (float(np.sum(d[sel])) / total if total > 0 else 0.0)
+
+
 # ------------------------------------------------------------------ blended prefill
 
 @dataclasses.dataclass
@@ -289,6 +374,10 @@ def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer
         P = select_topk(dev, k)
     elif mode == "doc":
         P = select_doc_spans(dev, k, span_bounds)
+    elif mode == "ranked":  # span_bounds = (bounds, order)
+        P = select_ranked_spans(N, k, span_bounds[0], span_bounds[1])
+    elif mode == "heads":
+        P = select_span_heads(N, k, span_bounds)
     else:
         raise ValueError("unknown mode " + str(mode))
     if k_sched is None:

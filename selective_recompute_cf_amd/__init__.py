@@ -16,8 +16,9 @@ LIB_PATH = os.path.join(PKG, "libcf.so")
 
 CF_OK, CF_EINVAL, CF_ESHAPE, CF_EDTYPE, CF_EUNSUPPORTED, CF_EWORKSPACE, CF_EHIP = range(7)
 CF_F32, CF_BF16 = 0, 1
-CF_SEL_TOKEN_TOPK, CF_SEL_DOC_SPANS, CF_SEL_ALL = 0, 1, 2
-MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL}
+CF_SEL_TOKEN_TOPK, CF_SEL_DOC_SPANS, CF_SEL_ALL, CF_SEL_RANKED_SPANS, CF_SEL_SPAN_HEADS = 0, 1, 2, 3, 4
+MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL, "ranked": CF_SEL_RANKED_SPANS,
+         "heads": CF_SEL_SPAN_HEADS}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
            "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
@@ -146,6 +147,19 @@ def _host_i32(rows: Optional[Iterable[Iterable[int]]]):
     return arr, len(flat)
 
 
+def _span_arg(mode: str, span_bounds):
+    """Host span array and span count: the bounds, and for "ranked" (span_bounds = (bounds,
+    order)) the order after them."""
+    if span_bounds is None:
+        return None, 0
+    if mode == "ranked":
+        bounds, order = span_bounds
+        arr, _ = _host_i32(list(bounds) + list(order))
+        return arr, len(bounds) - 1
+    arr, nb = _host_i32(span_bounds)
+    return arr, max(0, nb - 1)
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
@@ -222,13 +236,13 @@ class Context:
                       store_layer_stride: Optional[int] = None, out_layer_stride: Optional[int] = None):
         """layers: a ctypes array of LayerWeights (see ``layer_array``)."""
         tab, nflat = _host_i32(chunk_tab)
-        spans, nb = _host_i32(span_bounds)
+        spans, ns = _span_arg(mode, span_bounds)
         sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
         sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
         ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
         _check(lib().cf_blend_prefill(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
                                       _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, k,
-                                      MODES[mode], spans, max(0, nb - 1), _ptr(k_out), _ptr(v_out), ols,
+                                      MODES[mode], spans, ns, _ptr(k_out), _ptr(v_out), ols,
                                       _ptr(out_hidden), _ptr(out_sel), _ptr(out_dev), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(tokens.device)))
 
@@ -242,13 +256,13 @@ class Context:
                                store_layer_stride: Optional[int] = None, out_layer_stride: Optional[int] = None):
         """cf_blend_prefill_streamed: k_store/v_store are pinned host tensors (pin_memory=True)."""
         tab, nflat = _host_i32(chunk_tab)
-        spans, nb = _host_i32(span_bounds)
+        spans, ns = _span_arg(mode, span_bounds)
         sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
         sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
         ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
         _check(lib().cf_blend_prefill_streamed(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
                                                _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, k,
-                                               MODES[mode], spans, max(0, nb - 1), _ptr(k_out), _ptr(v_out), ols,
+                                               MODES[mode], spans, ns, _ptr(k_out), _ptr(v_out), ols,
                                                _ptr(out_hidden), _ptr(out_sel), _ptr(out_dev), _ptr(ws),
                                                0 if ws is None else ws.numel(), _stream(tokens.device)))
 
@@ -300,8 +314,8 @@ def topk_workspace_size(n: int, mode: str) -> int:
 
 
 def topk_select(dev, k: int, out_idx, mode: str = "token", span_bounds=None, ws=None):
-    spans, nb = _host_i32(span_bounds)
-    _check(lib().cf_topk_select(_ptr(dev), dev.numel(), k, MODES[mode], spans, max(0, nb - 1), _ptr(out_idx),
+    spans, ns = _span_arg(mode, span_bounds)
+    _check(lib().cf_topk_select(_ptr(dev), dev.numel(), k, MODES[mode], spans, ns, _ptr(out_idx),
                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev.device)))
 
 
@@ -346,3 +360,37 @@ def loading_controller(load_ms: float, recompute_ms: dict, floor=(15, 100)):
     if best is None or best[0] * floor[1] < floor[0] * best[1]:
         return tuple(floor)
     return tuple(best)
+
+
+def single_window_bounds(n_ctx: int) -> List[int]:
+    """Span bounds for the single-window policy (Request Order Matters §2.3): one span over the
+    context, so that document-aligned selection takes the best k-token window."""
+    return [0, int(n_ctx)]
+
+
+def fixed_chunk_bounds(n_ctx: int, size: int = 92, offset: int = 46) -> List[int]:
+    """Span bounds for the fixed-chunk policy (Request Order Matters §2.3, §4.4): spans of `size`
+    tokens shifted by `offset` so that they cross document boundaries: 0, offset, offset + size,
+    ..., n_ctx (offset 0 starts the first full span at 0)."""
+    if size <= 0 or not 0 <= offset < size:
+        raise ValueError("need size > 0 and 0 <= offset < size")
+    out = [0]
+    nxt = offset or size
+    while nxt < n_ctx:
+        out.append(nxt)
+        nxt += size
+    out.append(int(n_ctx))
+    return out if n_ctx > 0 else [0, 0]
+
+
+def selection_stats(sel: Sequence[int], dev) -> tuple:
+    """(segments, captured deviation) of a selection (Request Order Matters Table 2): the number of
+    maximal runs of consecutive positions, and the share of the total deviation (fp64) that the
+    selected positions carry. dev: host array-like of the selection-layer deviation."""
+    import numpy as np
+    idx = np.unique(np.asarray(sel, dtype=np.int64))
+    runs = int(idx.size and 1 + np.count_nonzero(np.diff(idx) != 1))
+    d = np.asarray(dev, dtype=np.float64).copy()
+    d[np.isnan(d)] = np.inf
+    total = float(d.sum())
+    return runs, (float(d[idx].sum()) / total if total > 0 else 0.0)

@@ -384,11 +384,24 @@ cf_status enqueue_reposition(const cf_ctx* c, const void* ks, const void* vs, in
   return CF_OK;
 }
 
-cf_status check_spans(const int32_t* b, int ns, int n) {
+bool span_mode(int mode) {
+  return mode == CF_SEL_DOC_SPANS || mode == CF_SEL_RANKED_SPANS || mode == CF_SEL_SPAN_HEADS;
+}
+
+// Span bounds (and, for the ranked mode, the order after them: a permutation of the spans).
+cf_status check_spans(const int32_t* b, int ns, int n, int mode = CF_SEL_DOC_SPANS) {
   CF_CHECK(ns >= 1 && ns <= CF_MAX_SPANS, CF_EINVAL, "span count %d outside [1, %d]", ns, CF_MAX_SPANS);
   CF_CHECK(b, CF_EINVAL, "null span bounds");
   CF_CHECK(b[0] == 0 && b[ns] == n, CF_EINVAL, "span bounds must run from 0 to %d", n);
   for (int i = 0; i < ns; ++i) CF_CHECK(b[i] < b[i + 1], CF_EINVAL, "span bounds not strictly increasing at %d", i);
+  if (mode == CF_SEL_RANKED_SPANS) {
+    std::vector<char> seen(ns, 0);
+    for (int r = 0; r < ns; ++r) {
+      const int j = b[ns + 1 + r];
+      CF_CHECK(j >= 0 && j < ns && !seen[j], CF_EINVAL, "span order is not a permutation of the %d spans", ns);
+      seen[j] = 1;
+    }
+  }
   return CF_OK;
 }
 
@@ -411,7 +424,10 @@ cf_status enqueue_select(const float* dev, int n, int k, int mode, const int32_t
   } else {
     cf::SpanArgs sp{};
     sp.n_spans = ns;
+    sp.mode = mode == CF_SEL_RANKED_SPANS ? cf::SPAN_RANKED : mode == CF_SEL_SPAN_HEADS ? cf::SPAN_HEADS : cf::SPAN_DOC;
     for (int i = 0; i <= ns; ++i) sp.b[i] = bounds[i];
+    if (mode == CF_SEL_RANKED_SPANS)
+      for (int r = 0; r < ns; ++r) sp.order[r] = bounds[ns + 1 + r];
     CF_RUN("topk_spans", cf::launch_topk_spans(dev, n, k, sp, out, ws, st));
   }
   return CF_OK;
@@ -592,10 +608,10 @@ size_t cf_topk_workspace_size(int32_t n, int32_t mode) {
 cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode, const int32_t* bounds, int32_t ns,
                          int32_t* out, void* ws, size_t ws_bytes, hipStream_t st) {
   g_err.clear();
-  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || mode == CF_SEL_DOC_SPANS, CF_EINVAL, "mode %d is not a selection mode", mode);
+  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || span_mode(mode), CF_EINVAL, "mode %d is not a selection mode", mode);
   CF_CHECK(n >= 0 && k >= 0 && k <= n, CF_EINVAL, "need 0 <= k <= n (k=%d, n=%d)", k, n);
-  if (mode == CF_SEL_DOC_SPANS)
-    if (cf_status s = check_spans(bounds, ns, n)) return s;
+  if (span_mode(mode))
+    if (cf_status s = check_spans(bounds, ns, n, mode)) return s;
   CF_CHECK(k == 0 || cf_topk_workspace_size(n, mode) == 0 || (ws && ws_bytes >= cf_topk_workspace_size(n, mode)),
            CF_EWORKSPACE, "this selection needs %zu workspace bytes", cf_topk_workspace_size(n, mode));
   if (k == 0) return CF_OK;
@@ -661,8 +677,7 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
   const int64_t kvd = (int64_t)mc.n_kv_heads * mc.head_dim;
   CF_CHECK(N >= 0 && U >= 0 && L > 0, CF_EINVAL, "need N, U >= 0 and N + U > 0");
   CF_CHECK(L <= c->max_pos, CF_EINVAL, "L=%d exceeds max_pos=%d", L, c->max_pos);
-  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || mode == CF_SEL_DOC_SPANS || mode == CF_SEL_ALL, CF_EINVAL, "unknown mode %d",
-           mode);
+  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || span_mode(mode) || mode == CF_SEL_ALL, CF_EINVAL, "unknown mode %d", mode);
   CF_CHECK(layers, CF_EINVAL, "null layer array");
   for (int l = 0; l < mc.n_layers; ++l)
     if (cf_status s = check_layer(c, layers + l, l)) return s;
@@ -685,8 +700,8 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
                "store_layer_stride must hold store_rows*kvd elements and be a multiple of 8");
     }
     if (cf_status s = check_chunks(c, tab, m, store_rows, N, N)) return s;
-    if (mode == CF_SEL_DOC_SPANS && N > 0)
-      if (cf_status s = check_spans(bounds, ns, N)) return s;
+    if (span_mode(mode) && N > 0)
+      if (cf_status s = check_spans(bounds, ns, N, mode)) return s;
   } else {
     k = N;
   }

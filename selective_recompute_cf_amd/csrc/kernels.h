@@ -121,7 +121,11 @@ void attn_plan(Dt dt, int n, int hq, int hkv, int n_cu, int* P);
 
 // ----------------------------------------------------------------- selection (topk.hip)
 constexpr int MAX_SPANS = 256;
-struct SpanArgs { int n_spans; int b[MAX_SPANS + 1]; };
+// Span selections: mode 1 document-aligned (rank by mean deviation, best window in the first span
+// that does not fit), 3 ranked by order[] (deviation unused, head of the first span that does not
+// fit), 4 heads of every span (deviation unused, the budget shared evenly).
+enum SpanMode { SPAN_DOC = 1, SPAN_RANKED = 3, SPAN_HEADS = 4 };
+struct SpanArgs { int n_spans; int mode; int b[MAX_SPANS + 1]; int order[MAX_SPANS]; };
 // ws: topk_token_ws_bytes(n) bytes (none below the large-n threshold, where one workgroup runs)
 size_t topk_token_ws_bytes(int n);
 hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws, hipStream_t st);

@@ -392,34 +392,71 @@ __global__ __launch_bounds__(TK_THREADS) void topk_spans_kernel(const float* __r
   __shared__ int wsum[TK_THREADS / WAVE];
   __shared__ int total;
   const int ns = sp.n_spans;
-  // 1. span means (fp64, sequential within the span)
+  const bool doc = sp.mode == SPAN_DOC;
+  // take[j]: how many leading tokens of span j are selected (the whole span, a head, or none)
+  // 1. span means (fp64, sequential within the span); document-aligned only
   for (int j = threadIdx.x; j < ns; j += TK_THREADS) {
     double s = 0.0;
-    for (int i = sp.b[j]; i < sp.b[j + 1]; ++i) s += canon_d(dev[i]);
+    if (doc)
+      for (int i = sp.b[j]; i < sp.b[j + 1]; ++i) s += canon_d(dev[i]);
     score[j] = s / (double)(sp.b[j + 1] - sp.b[j]);
     take[j] = 0;
   }
   __syncthreads();
-  // 2. ranking by (score desc, index asc)
+  // 2. ranking: by (score desc, index asc), or the given order
   for (int j = threadIdx.x; j < ns; j += TK_THREADS) {
-    int r = 0;
-    for (int i = 0; i < ns; ++i) r += (score[i] > score[j] || (score[i] == score[j] && i < j)) ? 1 : 0;
-    order[r] = j;
+    if (doc) {
+      int r = 0;
+      for (int i = 0; i < ns; ++i) r += (score[i] > score[j] || (score[i] == score[j] && i < j)) ? 1 : 0;
+      order[r] = j;
+    } else {
+      order[j] = sp.order[j];
+    }
   }
   __syncthreads();
-  // 3. whole spans while they fit; remember the first that does not
-  if (threadIdx.x == 0) {
+  // 3. heads of every span: the smallest head length T with sum min(len, T) >= k (bisection),
+  //    then one token less for the last spans holding T until exactly k remain
+  if (sp.mode == SPAN_HEADS) {
+    if (threadIdx.x == 0) {
+      int lo = 0, hi = 0;
+      for (int j = 0; j < ns; ++j) hi = max(hi, sp.b[j + 1] - sp.b[j]);
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        int tot = 0;
+        for (int j = 0; j < ns; ++j) tot += min(sp.b[j + 1] - sp.b[j], mid);
+        if (tot >= k) hi = mid; else lo = mid + 1;
+      }
+      int excess = -k;
+      for (int j = 0; j < ns; ++j) {
+        take[j] = min(sp.b[j + 1] - sp.b[j], lo);
+        excess += take[j];
+      }
+      for (int j = ns - 1; j >= 0 && excess > 0; --j)
+        if (lo > 0 && take[j] == lo) --take[j], --excess;
+      s_part = -1;
+      s_rem = 0;
+      s_wa = -1;
+    }
+    __syncthreads();
+  }
+  // 3. whole spans while they fit; the first that does not gives its best window (document-
+  //    aligned) or its head (ranked)
+  else if (threadIdx.x == 0) {
     int rem = k, part = -1;
     for (int r = 0; r < ns && rem > 0; ++r) {
       const int j = order[r];
       const int len = sp.b[j + 1] - sp.b[j];
       if (len <= rem) {
-        take[j] = 1;
+        take[j] = len;
         rem -= len;
       } else {
         part = j;
         break;
       }
+    }
+    if (!doc && part >= 0) {
+      take[part] = rem;
+      part = -1;
     }
     s_part = part;
     s_rem = part >= 0 ? rem : 0;
@@ -486,7 +523,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_spans_kernel(const float* __r
       const int mid = (lo + hi + 1) / 2;
       if (sp.b[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    return take[lo] != 0 || (wa >= 0 && i >= wa && i < wa + wl);
+    return i - sp.b[lo] < take[lo] || (wa >= 0 && i >= wa && i < wa + wl);
   };
   compact(n, k, in_span_taken, out, wsum, &total);
 }

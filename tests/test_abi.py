@@ -116,3 +116,28 @@ def test_budget_host_logic_agrees_with_oracle():
             assert cf.budget(n, num, den) == oracle.budget(n, num, den)
     with pytest.raises(ValueError):
         cf.budget(10, 101, 100)
+
+
+def test_span_policy_host_logic_agrees_with_oracle():
+    import numpy as np
+    for n in [1, 30, 92, 300, 3072, 7728]:
+        for size, off in [(92, 46), (92, 0), (7, 3), (64, 63)]:
+            assert cf.fixed_chunk_bounds(n, size, off) == oracle.fixed_chunk_bounds(n, size, off)
+        assert cf.single_window_bounds(n) == oracle.single_window_bounds(n)
+    rng = np.random.default_rng(2)
+    for _ in range(100):
+        d = rng.random(50).astype(np.float32)
+        d[rng.integers(0, 50, 3)] = np.nan
+        sel = np.unique(rng.integers(0, 50, 12))
+        a, b = cf.selection_stats(sel, d), oracle.selection_stats(sel, d)
+        assert a[0] == b[0] and (a[1] == b[1] or abs(a[1] - b[1]) < 1e-12 or (np.isnan(a[1]) and np.isnan(b[1])))
+
+
+def test_ranked_span_order_validation(L):
+    bad = (ctypes.c_int32 * 7)(0, 3, 8, 10, 1, 1, 0)   # bounds then a non-permutation
+    assert L.cf_topk_select(None, 10, 3, cf.CF_SEL_RANKED_SPANS, bad, 3, None, None, 0, None) == cf.CF_EINVAL
+    assert "permutation" in L.cf_last_error().decode()
+    good = (ctypes.c_int32 * 7)(0, 3, 8, 10, 2, 0, 1)
+    assert L.cf_topk_select(None, 10, 0, cf.CF_SEL_RANKED_SPANS, good, 3, None, None, 0, None) == cf.CF_OK
+    assert L.cf_topk_select(None, 10, 3, cf.CF_SEL_SPAN_HEADS, good, 3, None, None, 0, None) == cf.CF_EINVAL
+    assert cf.topk_workspace_size(10, "ranked") == 0 and cf.topk_workspace_size(10, "heads") == 0

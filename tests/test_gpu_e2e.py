@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
+import selective_recompute_cf_amd as cf
 import synth
 from selective_recompute_cf_amd.device import DeviceModel
 from tests._gpu import compare, context, gpu_blend, gpu_chunk_store, host, overlap, say, selection_bar
@@ -197,3 +198,47 @@ def test_qwen3_8b_shape_reduced_depth():
     model, toks, g, r32, r16, *_ = _run(w, n_layers=2)
     assert len(g["sel"]) == 3072
     _check(w, g, r32, r16)
+
+
+@pytest.mark.parametrize("policy", ["single-window", "fixed-chunk", "random-document", "heads"])
+def test_span_policy_blends(policy):
+    """The span ablation policies and EPIC's chunk heads through cf_blend_prefill (tiny fp32
+    model, 3 layers, 15%): the selection the GPU makes equals the oracle's on the GPU's own
+    deviation (the two deviation-free policies equal the oracle's end-to-end selection), and the
+    outputs meet the fp32 bar."""
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(n_layers=3))
+    N = w.n_ctx
+    docs = [i * w.chunk_len for i in range(w.n_chunks + 1)]
+    if policy == "single-window":
+        mode, spans, ospans = "doc", cf.single_window_bounds(N), oracle.single_window_bounds(N)
+    elif policy == "fixed-chunk":
+        mode, spans, ospans = "doc", cf.fixed_chunk_bounds(N, 92, 46), oracle.fixed_chunk_bounds(N, 92, 46)
+    elif policy == "random-document":
+        order = np.random.default_rng(4).permutation(w.n_chunks).tolist()
+        mode, spans, ospans = "ranked", (docs, order), (docs, order)
+    else:
+        mode, spans, ospans = "heads", docs, docs
+    model = synth.Model(w.model)
+    chunks, _, toks = synth.request_tokens(w)
+    k = oracle.budget(N, w.rho_num, w.rho_den)
+    say(f"span policy {policy} k={k}")
+    ctx = context(model.cfg, max_pos=4096)
+    dm = DeviceModel(model, n_layers=3)
+    gk, gv, starts = gpu_chunk_store(ctx, dm, chunks)
+    table = [(s0, 0, s0, len(c)) for s0, c in zip(starts, chunks)]
+    g = gpu_blend(ctx, dm, toks, N, gk, gv, table, 1, k, mode, spans)
+    ks, vs = host(gk).reshape(3, N, w.model.n_kv_heads, w.model.head_dim), host(gv).reshape(3, N, w.model.n_kv_heads,
+                                                                                                w.model.head_dim)
+    r32 = oracle.blend_prefill(model, toks, N, ks, vs, table, 1, k, mode, ospans, np.float32, 3)
+    if mode == "doc":
+        np.testing.assert_array_equal(g["sel"], oracle.select_doc_spans(g["dev"], k, ospans))
+        assert overlap(g["sel"], r32.sel) >= 0.99
+    else:
+        np.testing.assert_array_equal(g["sel"], r32.sel)
+    segs, cap = cf.selection_stats(g["sel"], g["dev"])
+    assert (segs, round(cap, 9)) == tuple(round(x, 9) if isinstance(x, float) else x
+                                          for x in oracle.selection_stats(g["sel"], g["dev"]))
+    say(f"  segments {segs}, captured deviation {cap:.3f}")
+    if np.array_equal(g["sel"], r32.sel):
+        compare("out", g["out"], r32.out, "f32")
+        compare("K", g["k"], r32.k.reshape(g["k"].shape), "f32")

@@ -133,6 +133,40 @@ def test_doc_spans_golden(case):
     assert _gpu_topk(d, k, "doc", b) == want
 
 
+@pytest.mark.parametrize("policy", ["single-window", "fixed-chunk", "random-document", "heads"])
+@pytest.mark.parametrize("n_spans,span_len", [(1, 50), (6, 512), (84, 92), (256, 40)])
+def test_span_policies_bit_exact_vs_oracle(policy, n_spans, span_len):
+    """The ablation policies of Request Order Matters §2.3 (single-window and fixed-chunk through
+    the document-aligned mode over generated bounds, random-document as a ranked order drawn here)
+    and EPIC's chunk heads, against the oracle on the same arrays; ragged documents, ties."""
+    rng = np.random.default_rng(n_spans * 7 + span_len)
+    lens = np.maximum(1, rng.integers(span_len // 2, span_len * 3 // 2 + 1, n_spans))
+    docs = [0] + np.cumsum(lens).tolist()
+    n = docs[-1]
+    say(f"{policy} n_spans={n_spans} n={n}")
+    for trial in range(2):
+        d = rng.random(n).astype(np.float32) if trial == 0 else rng.integers(0, 3, n).astype(np.float32)
+        for k in sorted({0, 1, n // 20, n // 3, n - 1, n}):
+            if policy == "single-window":
+                b = cf.single_window_bounds(n)
+                want = oracle.select_doc_spans(d, k, oracle.single_window_bounds(n))
+                got = _gpu_topk(d, k, "doc", b)
+            elif policy == "fixed-chunk":
+                b = cf.fixed_chunk_bounds(n, 92, 46)
+                assert b == oracle.fixed_chunk_bounds(n, 92, 46)
+                want = oracle.select_doc_spans(d, k, b)
+                assert len(b) - 1 <= 256
+                got = _gpu_topk(d, k, "doc", b)
+            elif policy == "random-document":
+                order = rng.permutation(n_spans).tolist()
+                want = oracle.select_ranked_spans(n, k, docs, order)
+                got = _gpu_topk(d, k, "ranked", (docs, order))
+            else:
+                want = oracle.select_span_heads(n, k, docs)
+                got = _gpu_topk(d, k, "heads", docs)
+            assert got == want.tolist(), (trial, k)
+
+
 @pytest.mark.parametrize("n_spans,span_len", [(1, 50), (5, 7), (20, 512), (84, 92), (256, 40)])
 def test_doc_spans_bit_exact_vs_oracle(n_spans, span_len):
     rng = np.random.default_rng(n_spans * 1000 + span_len)

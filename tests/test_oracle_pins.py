@@ -333,6 +333,76 @@ def test_doc_spans_brute_force_properties():
             assert got == sorted(want)
 
 
+# ------------------------------------------------------------------ span policies (ablation controls)
+
+def test_span_policy_bounds_hand_values():
+    """Request Order Matters §2.3/§4.4: fixed 92-token spans offset across document boundaries
+    (offset 46 taken for the unstated shift); single-window is one span over the context."""
+    assert oracle.fixed_chunk_bounds(300) == [0, 46, 138, 230, 300]
+    assert oracle.fixed_chunk_bounds(92, 92, 0) == [0, 92]
+    assert oracle.fixed_chunk_bounds(30) == [0, 30]
+    assert oracle.single_window_bounds(7) == [0, 7]
+    b = oracle.fixed_chunk_bounds(3072)
+    assert len(b) == 35 and all(y - x == 92 for x, y in zip(b[1:-1], b[2:-1])) and b[-1] - b[-2] == 3072 - 46 - 32 * 92
+
+
+def test_single_window_is_the_brute_force_best_window():
+    """Single-window (the document-aligned rule over one span) against every window, with
+    integer-valued deviations so that every total is exact: largest total, smallest start."""
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        n = int(rng.integers(1, 30))
+        d = rng.integers(0, 4, n).astype(np.float32)
+        for k in range(0, n + 1):
+            got = oracle.select_doc_spans(d, k, oracle.single_window_bounds(n)).tolist()
+            tot = [sum(float(x) for x in d[a:a + k]) for a in range(n - k + 1)]
+            a = max(range(n - k + 1), key=lambda i: (tot[i], -i))
+            assert got == list(range(a, a + k))
+
+
+def test_ranked_spans_hand_values():
+    """Random-document: spans in the given order, whole while they fit, then the head of the
+    first that does not; the deviation plays no part."""
+    assert oracle.select_ranked_spans(10, 6, [0, 3, 8, 10], [2, 0, 1]).tolist() == [0, 1, 2, 3, 8, 9]
+    assert oracle.select_ranked_spans(10, 2, [0, 3, 8, 10], [1, 0, 2]).tolist() == [3, 4]
+    assert oracle.select_ranked_spans(10, 10, [0, 3, 8, 10], [1, 2, 0]).tolist() == list(range(10))
+    assert oracle.select_ranked_spans(10, 0, [0, 3, 8, 10], [1, 2, 0]).tolist() == []
+    with pytest.raises(ValueError):
+        oracle.select_ranked_spans(10, 3, [0, 3, 8, 10], [1, 1, 0])
+
+
+def test_span_heads_hand_values():
+    """EPIC's first tokens of every chunk, the budget shared evenly (water-filling)."""
+    assert oracle.select_span_heads(10, 5, [0, 4, 6, 10]).tolist() == [0, 1, 4, 5, 6]
+    assert oracle.select_span_heads(10, 6, [0, 1, 6, 10]).tolist() == [0, 1, 2, 3, 6, 7]
+    assert oracle.select_span_heads(10, 6, [0, 8, 9, 10]).tolist() == [0, 1, 2, 3, 8, 9]
+    assert oracle.select_span_heads(10, 10, [0, 8, 9, 10]).tolist() == list(range(10))
+    assert oracle.select_span_heads(12, 3, [0, 4, 8, 12]).tolist() == [0, 4, 8]
+    assert oracle.select_span_heads(12, 0, [0, 4, 8, 12]).tolist() == []
+
+
+def test_selection_stats_hand_values_and_topk_captures_most():
+    """Request Order Matters Table 2's diagnostics, worked by hand; and, as the table shows,
+    token top-k captures at least the deviation share of every span policy at the same k (it
+    maximises the selected total)."""
+    d = np.array([1, 1, 1, 0, 0, 4, 0, 2, 2, 1], np.float32)
+    assert oracle.selection_stats([0, 1, 2, 5, 7, 8], d) == (3, 11 / 12)
+    assert oracle.selection_stats([], d) == (0, 0.0)
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        d = rng.random(120).astype(np.float32) ** 3
+        bounds = [0, 20, 45, 60, 100, 120]
+        for k in [1, 17, 40, 90]:
+            best = oracle.selection_stats(oracle.select_topk(d, k), d)[1]
+            for sel in [oracle.select_doc_spans(d, k, bounds), oracle.select_doc_spans(d, k, [0, 120]),
+                        oracle.select_doc_spans(d, k, oracle.fixed_chunk_bounds(120, 23, 11)),
+                        oracle.select_ranked_spans(120, k, bounds, [3, 1, 4, 0, 2]),
+                        oracle.select_span_heads(120, k, bounds)]:
+                assert len(sel) == k
+                assert oracle.selection_stats(sel, d)[1] <= best + 1e-12
+            assert oracle.selection_stats(oracle.select_doc_spans(d, k, [0, 120]), d)[0] == 1
+
+
 @pytest.mark.parametrize("row", _golden.page_numbers("budget"))
 def test_budget_page_numbers(row):
     n, num, den, k = map(int, row)
