@@ -303,6 +303,66 @@ def selection_stats(sel, d) -> Tuple[int, float]:
     return segments, (float(np.sum(d[sel])) / total if total > 0 else 0.0)
 
 
+# ------------------------------------------------------------------ query-aware scores
+
+def query_attention_mass(cfg, q, q_pos, k_cache, n_ctx: int, ft=np.float32, rnd=None) -> np.ndarray:
+    """QCFuse §3.2.1, Attn^l(Q_U, K_C)_t: the attention weight that the query rows put on context
+    position t, summed over query rows and heads. Each row's weights are its softmax over every
+    cache row it sees (t <= its position, scale 1/sqrt(hd), query head h on kv head h // (Hq /
+    Hkv)), so a row's weights sum to 1 over context and query rows together; only the context
+    columns t < n_ctx are returned (fp64 sums)."""
+    q = np.asarray(q, dtype=ft)
+    kc = np.asarray(k_cache, dtype=ft)
+    n, hq, hd = q.shape
+    group = hq // kc.shape[1]
+    visible = np.arange(kc.shape[0])[None, :] <= np.asarray(q_pos).reshape(n)[:, None]
+    mass = np.zeros(n_ctx, dtype=np.float64)
+    for h in range(hq):
+        s = (q[:, h, :] @ kc[:, h // group, :].T) * ft(1.0 / np.sqrt(hd))
+        s = np.where(visible, s, ft(-np.inf))
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        mass += p[:, :n_ctx].astype(np.float64).sum(axis=0)
+    return mass
+
+
+def query_scores(model, tokens, n_ctx, k_stitched, v_stitched, layer_set, ft=np.float32, bf16_ops=None,
+                 return_cache=False):
+    """Query-aware importance (QCFuse §3.2.1 Eq. 9-10; Eq. 20 for a layer subset, the ProphetKV-style
+    full view with full-context probing): the query rows U run through the layers with the whole
+    stitched cache as their prefix, which they only read (no context entry is refreshed; their
+    own K/V go to rows n_ctx.. as usual), and I(t) sums the attention mass of Attn^l over the
+    layers in ``layer_set``. Returns fp32 [n_ctx]. k_stitched/v_stitched: [Ly, L, Hkv, hd] with
+    every layer stitched; copies are used."""
+    cfg = model.cfg
+    tokens = np.asarray(tokens)
+    L, N = len(tokens), int(n_ctx)
+    layers = sorted(set(int(l) for l in layer_set))
+    kc = np.array(k_stitched, dtype=ft, copy=True)
+    vc = np.array(v_stitched, dtype=ft, copy=True)
+    rnd = rounding(cfg, bf16_ops)
+    h = np.asarray(model.embed[tokens[N:]], dtype=ft)
+    pos = np.arange(N, L)
+    score = np.zeros(N, dtype=np.float64)
+    for l in range(max(layers) + 1 if layers else 0):
+        w = model.layer(l)
+        if l in layers:  # the layer's query states, as layer_rows forms them, against the cache they see
+            a = _r(rnd, rms_norm(h, w.attn_norm, cfg.rms_eps, ft), ft)
+            n = len(pos)
+            q = (a @ np.asarray(w.wq, ft).T).reshape(n, cfg.n_q_heads, cfg.head_dim)
+            k = k_rows(cfg, w, h, pos, ft, bf16_ops)
+            if cfg.qk_norm:
+                q = rms_norm(q, w.q_norm, cfg.rms_eps, ft)
+            q = _r(rnd, rope(q, pos, cfg.rope_theta, ft), ft)
+            seen = kc[l].copy()
+            seen[pos] = _r(rnd, k, ft)
+            score += query_attention_mass(cfg, q, pos, seen, N, ft)
+        h = layer_rows(cfg, w, h, pos, kc[l], vc[l], ft, bf16_ops)
+    if return_cache:
+        return score.astype(np.float32), kc, vc
+    return score.astype(np.float32)
+
+
 # ------------------------------------------------------------------ blended prefill
 
 @dataclasses.dataclass
@@ -378,6 +438,10 @@ def blend_prefill(model, tokens, n_ctx, k_store, v_store, chunk_table, sel_layer
         P = select_ranked_spans(N, k, span_bounds[0], span_bounds[1])
     elif mode == "heads":
         P = select_span_heads(N, k, span_bounds)
+    elif mode == "given":  # span_bounds = the recompute set (e.g. the top of query_scores)
+        P = np.asarray(sorted(int(i) for i in span_bounds), dtype=np.int32)
+        if len(P) != k or len(set(P.tolist())) != k or (k and not 0 <= P[0] <= P[-1] < N):
+            raise ValueError("the given set must hold k distinct context positions")
     else:
         raise ValueError("unknown mode " + str(mode))
     if k_sched is None:

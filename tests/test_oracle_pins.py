@@ -178,9 +178,11 @@ def test_attention_brute_force_loop():
 
 # ------------------------------------------------------------------ whole decoder vs torch
 
-def _torch_decoder(model, tokens, n_layers):
+def _torch_decoder(model, tokens, n_layers, mass_from=None):
     """Independent decoder written with torch library ops: F.rms_norm, complex-number RoPE,
-    scaled_dot_product_attention, F.silu. Returns K, V per layer and the normed output."""
+    scaled_dot_product_attention, F.silu. Returns K, V per layer and the normed output; with
+    mass_from = N, also each layer's causal-softmax weight on columns < N summed over the rows
+    >= N and the heads."""
     cfg = model.cfg
     hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     n = len(tokens)
@@ -193,7 +195,7 @@ def _torch_decoder(model, tokens, n_layers):
         z = torch.complex(x[..., : hd // 2], x[..., hd // 2:]) * rot[:, None, :]
         return torch.cat([z.real, z.imag], dim=-1)
 
-    ks, vs = [], []
+    ks, vs, masses = [], [], []
     for l in range(n_layers):
         w = model.layer(l)
         T = lambda a: torch.tensor(np.asarray(a), dtype=d)
@@ -207,11 +209,19 @@ def _torch_decoder(model, tokens, n_layers):
         q, k = rotary(q), rotary(k)
         ks.append(k.numpy())
         vs.append(v.numpy())
+        if mass_from is not None:
+            N0 = mass_from
+            causal = torch.ones(n, n, dtype=torch.bool).tril()
+            sc = torch.einsum("qhd,khd->hqk", q, k.repeat_interleave(hq // hkv, dim=1)) / math.sqrt(hd)
+            pr = torch.softmax(sc.masked_fill(~causal, float("-inf")), dim=-1)
+            masses.append(pr[:, N0:, :N0].sum(dim=(0, 1)).numpy())
         o = torch.tensor(_sdpa_gqa(q.numpy(), k.numpy(), v.numpy())).reshape(n, hq * hd)
         h = h + F.linear(o, T(w.wo))
         b = F.rms_norm(h, (cfg.d_model,), T(w.mlp_norm), eps=cfg.rms_eps)
         h = h + F.linear(F.silu(F.linear(b, T(w.w_gate))) * F.linear(b, T(w.w_up)), T(w.w_down))
     out = F.rms_norm(h, (cfg.d_model,), torch.tensor(model.final_norm, dtype=d), eps=cfg.rms_eps)
+    if mass_from is not None:
+        return np.stack(ks), np.stack(vs), out.numpy(), masses
     return np.stack(ks), np.stack(vs), out.numpy()
 
 
@@ -331,6 +341,68 @@ def test_doc_spans_brute_force_properties():
                 rem = 0
                 break
             assert got == sorted(want)
+
+
+# ------------------------------------------------------------------ query-aware scores
+
+def _stitched(model, chunks, toks, ly):
+    ks, vs, table = _store(model, chunks, n_layers=ly)
+    N = sum(len(c) for c in chunks)
+    kst, vst = oracle.stitch(ks, vs, table, N, range(ly), model.cfg.rope_theta, F64, n_total=len(toks))
+    return N, ks, vs, table, kst, vst
+
+
+def test_query_mass_rows_sum_to_one_and_match_torch_softmax():
+    """QCFuse §3.2.1: each query row spreads weight 1 per head over the rows it sees, so the mass
+    over all columns is rows x heads; the context columns equal torch's causal softmax summed over
+    rows and heads (an independent library route)."""
+    rng = np.random.default_rng(9)
+    n, hq, hkv, hd, L = 6, 4, 2, 16, 40
+    q = rng.standard_normal((n, hq, hd))
+    kc = rng.standard_normal((L, hkv, hd))
+    pos = np.arange(L - n, L)
+    assert abs(oracle.query_attention_mass(TINY, q, pos, kc, L, F64).sum() - n * hq) < 1e-9
+    N = L - n
+    got = oracle.query_attention_mass(TINY, q, pos, kc, N, F64)
+    tq, tk = torch.from_numpy(q), torch.from_numpy(kc)
+    mask = torch.arange(L)[None, :] <= torch.from_numpy(pos)[:, None]
+    want = torch.zeros(N, dtype=torch.float64)
+    for h in range(hq):
+        sc = (tq[:, h] @ tk[:, h // (hq // hkv)].T) / math.sqrt(hd)
+        want += torch.softmax(sc.masked_fill(~mask, float("-inf")), dim=1)[:, :N].sum(0)
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_QK], ids=["llama-style", "qk-norm"])
+def test_query_scores_single_chunk_match_torch_decoder_attention(cfg):
+    """With one chunk the stitched cache is exact, so the probe is full prefill: layer l's score is
+    the torch decoder's causal-softmax weight on the context columns, summed over the query rows
+    and heads (independent q/k, RoPE and softmax)."""
+    model = _Model(cfg)
+    chunks, q, toks = _request(cfg, n_chunks=1, clen=30, nq=9)
+    N, ks, vs, table, kst, vst = _stitched(model, chunks, toks, 3)
+    *_, masses = _torch_decoder(model, toks, 3, mass_from=N)
+    for l in range(3):
+        np.testing.assert_allclose(oracle.query_scores(model, toks, N, kst, vst, [l], F64), masses[l], rtol=1e-5,
+                                   atol=1e-7)
+
+
+def test_query_scores_probe_is_direct_reuse_and_adds_over_layers():
+    """The full-view probe forwards the query over the stitched cache without refreshing context
+    entries: its query-row K/V equal direct reuse's (pinned by the rho = 0 endpoint) and its context
+    rows stay stitched; Eq. 10 sums per-layer masses, so a layer set scores the sum of its layers."""
+    model = _Model(TINY)
+    chunks, q, toks = _request(TINY)
+    N, ks, vs, table, kst, vst = _stitched(model, chunks, toks, 3)
+    total, kc, vc = oracle.query_scores(model, toks, N, kst, vst, [0, 1, 2], F64, return_cache=True)
+    K, V, _ = oracle.direct_reuse(model, toks, N, ks, vs, table, F64, n_layers=3)
+    np.testing.assert_allclose(kc[:, N:], K[:, N:], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(vc[:, N:], V[:, N:], rtol=1e-10, atol=1e-12)
+    np.testing.assert_array_equal(kc[:, :N], kst[:, :N])
+    parts = [oracle.query_scores(model, toks, N, kst, vst, [l], F64) for l in range(3)]
+    np.testing.assert_allclose(total, parts[0] + parts[1] + parts[2], rtol=1e-5)
+    n_rows, hq = len(toks) - N, TINY.n_q_heads
+    assert 0 < total.sum() < 3 * n_rows * hq and np.all(total >= 0)
 
 
 # ------------------------------------------------------------------ span policies (ablation controls)
