@@ -68,7 +68,8 @@ typedef enum {
   CF_SEL_DOC_SPANS = 1,  /* document-aligned spans (Request Order Matters §2.3) */
   CF_SEL_ALL = 2,        /* every row at every layer: ordinary full prefill (QCFuse Eq. 2) */
   CF_SEL_RANKED_SPANS = 3, /* spans in a caller-given order, e.g. random-document (Request Order Matters §2.3) */
-  CF_SEL_SPAN_HEADS = 4  /* the first tokens of every span (EPIC, as Request Order Matters §3 describes it) */
+  CF_SEL_SPAN_HEADS = 4, /* the first tokens of every span (EPIC, as Request Order Matters §3 describes it) */
+  CF_SEL_GIVEN = 5       /* cf_blend_prefill only: the caller's set, read from out_sel (e.g. the top of cf_query_scores) */
 } cf_select_mode;
 
 /* Decoder shape. Pre-norm layer: RMSNorm -> Q,K,V projections -> optional per-head RMS
@@ -226,7 +227,9 @@ cf_status cf_blend_layer(const cf_ctx* ctx, const cf_layer_weights* w /* host st
  *  layers: host array [n_layers] of device-pointer structs; embed [vocab][d_model];
  *  final_norm fp32 [d_model]; chunk store as in cf_rope_reposition;
  *  k_out/v_out: [n_layers] layers of [L][kvd], out_layer_stride elements apart (>= L*kvd);
- *  out_sel: optional device int32 [k], the selected context positions ascending;
+ *  out_sel: optional device int32 [k], the selected context positions ascending; with mode
+ *    CF_SEL_GIVEN it is an input: the k strictly ascending context positions to recompute (the
+ *    selection-layer deviation is then not measured and out_dev is left untouched);
  *  out_dev: optional device fp32 [N], the deviation at the selection layer.
  *  0 <= k <= N; 0 <= sel_layer < n_layers; ws from cf_blend_prefill_workspace_size. */
 size_t cf_blend_prefill_workspace_size(const cf_ctx* ctx, int32_t N, int32_t U, int32_t k,
@@ -240,6 +243,28 @@ cf_status cf_blend_prefill(const cf_ctx* ctx, const cf_layer_weights* layers, co
                            void* v_out, int64_t out_layer_stride, float* out_hidden,
                            int32_t* out_sel, float* out_dev, void* ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/* --------------------------------------------------------------------- cf_query_scores
+ * Query-aware token importance (QCFuse §3.2.1 Eq. 9-10; Eq. 20 for a subset of layers): the U
+ * query tokens run through layers 0 .. max(layer_set) as ordinary rows at positions N .. N+U-1
+ * over the stitched cache, which they only read (context rows [0, N) are never written; the
+ * query rows' own K/V are written to rows [N, L) of each layer, as the blend would). At each
+ * layer l in layer_set the attention weight that the query rows put on context position t
+ * (each row's softmax over the rows it sees, summed over query rows and heads) is added:
+ *   scores[t] = sum over l in layer_set of Attn^l(Q_U, K_C)_t,  t < N.
+ * The top of these scores (cf_topk_select, token mode) is a query-aware recompute set; pass it
+ * to cf_blend_prefill with mode CF_SEL_GIVEN.
+ *  tokens: device int32 [L = N + U] (only the U query tokens at N.. are read).
+ *  k_cache, v_cache: the stitched cache (cf_rope_reposition of every layer), [n_layers] layers
+ *    of [L][kvd] out_layer_stride elements apart.
+ *  layer_set: host int32 [n_set], strictly increasing layer ids.
+ *  scores: device fp32 [N] (written, not accumulated across calls).
+ *  ws: device workspace of cf_query_scores_workspace_size(ctx, N, U) bytes. N > 0, U > 0. */
+size_t cf_query_scores_workspace_size(const cf_ctx* ctx, int32_t N, int32_t U);
+cf_status cf_query_scores(const cf_ctx* ctx, const cf_layer_weights* layers, const void* embed,
+                          const int32_t* tokens, int32_t N, int32_t U, void* k_cache, void* v_cache,
+                          int64_t out_layer_stride, const int32_t* layer_set /* host */, int32_t n_set,
+                          float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------- cf_blend_prefill_streamed
  * cf_blend_prefill with the chunk store in host memory, loaded layer by layer while the

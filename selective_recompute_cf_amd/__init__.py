@@ -16,14 +16,15 @@ LIB_PATH = os.path.join(PKG, "libcf.so")
 
 CF_OK, CF_EINVAL, CF_ESHAPE, CF_EDTYPE, CF_EUNSUPPORTED, CF_EWORKSPACE, CF_EHIP = range(7)
 CF_F32, CF_BF16 = 0, 1
-CF_SEL_TOKEN_TOPK, CF_SEL_DOC_SPANS, CF_SEL_ALL, CF_SEL_RANKED_SPANS, CF_SEL_SPAN_HEADS = 0, 1, 2, 3, 4
+CF_SEL_TOKEN_TOPK, CF_SEL_DOC_SPANS, CF_SEL_ALL, CF_SEL_RANKED_SPANS, CF_SEL_SPAN_HEADS, CF_SEL_GIVEN = range(6)
 MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL, "ranked": CF_SEL_RANKED_SPANS,
-         "heads": CF_SEL_SPAN_HEADS}
+         "heads": CF_SEL_SPAN_HEADS, "given": CF_SEL_GIVEN}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
            "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
            "cf_blend_prefill", "cf_blend_prefill_gradual_workspace_size", "cf_blend_prefill_gradual",
-           "cf_blend_prefill_streamed_workspace_size", "cf_blend_prefill_streamed",
+           "cf_blend_prefill_streamed_workspace_size", "cf_blend_prefill_streamed", "cf_query_scores_workspace_size",
+           "cf_query_scores",
            "cf_profile_enable", "cf_profile_report", "cf_mfma_loop", "cf_copy_loop"]
 
 
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
                                    i32, i32, i32, i32, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "cf_blend_prefill_gradual_workspace_size": (sz, [vp, i32, i32, i32, vp]),
         "cf_blend_prefill_streamed_workspace_size": (sz, [vp, i32, i32, i32, i32, i32]),
+        "cf_query_scores_workspace_size": (sz, [vp, i32, i32]),
+        "cf_query_scores": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, i32, i32, vp, vp, i64, vp, i32, vp, vp, sz,
+                                  vp]),
         "cf_blend_prefill_streamed": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32,
                                             vp, i32, i32, i32, i32, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "cf_blend_prefill_gradual": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32,
@@ -246,6 +250,19 @@ class Context:
                                       _ptr(out_hidden), _ptr(out_sel), _ptr(out_dev), _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(tokens.device)))
 
+
+    def query_scores_workspace_size(self, N: int, U: int) -> int:
+        return int(lib().cf_query_scores_workspace_size(self.handle, N, U))
+
+    def query_scores(self, layers, embed, tokens, N: int, U: int, k_cache, v_cache, layer_set: Sequence[int], scores,
+                     ws, out_layer_stride: Optional[int] = None):
+        """cf_query_scores: scores (fp32 [N]) = the query rows' attention mass on each context position,
+        summed over the layers in layer_set; k_cache/v_cache hold the stitched cache of every layer."""
+        lset, nset = _host_i32(list(layer_set))
+        ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        _check(lib().cf_query_scores(self.handle, layers, _ptr(embed), _ptr(tokens), N, U, _ptr(k_cache),
+                                     _ptr(v_cache), ols, lset, nset, _ptr(scores), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(tokens.device)))
 
     def blend_prefill_streamed_workspace_size(self, N: int, U: int, k: int, mode: str, store_rows: int) -> int:
         return int(lib().cf_blend_prefill_streamed_workspace_size(self.handle, N, U, k, MODES[mode], store_rows))

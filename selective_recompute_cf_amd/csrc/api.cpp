@@ -220,12 +220,19 @@ cf_status check_layer(const cf_ctx* c, const cf_layer_weights* w, int idx) {
 // previous layer on the same rows). next_norm: the next layer's attention-norm gain; when the down
 // projection is split along K, its reduction then also writes the next layer's X (bit-identical
 // to a separate normalisation) and *x_next is set.
+// Attention mass of the layer's rows on the context keys [0, n_ctx), added to score (QCFuse
+// Eq. 10): ml [n][hq][2] and part [hkv][n_ctx] are scratch; first = this layer starts the sum.
+struct MassHook {
+  float* ml; float* part; float* score; int n_ctx; bool first;
+};
+
 // dev_heads: also measure, for the first n_dev rows, each kv head's squared distance between the
 // fresh key and the cached key it replaces ([n_dev][n_kv_heads]).
 cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, void* kc, void* vc,
                     const int* sel, int n, int L, char* ws, const LayerWs& lw, hipStream_t st,
                     bool x_ready = false, const float* next_norm = nullptr, bool* x_next = nullptr,
-                    bool* sched_ready = nullptr, float* dev_heads = nullptr, int n_dev = 0) {
+                    bool* sched_ready = nullptr, float* dev_heads = nullptr, int n_dev = 0,
+                    const MassHook* mass = nullptr) {
   if (x_next) *x_next = false;
   if (n == 0) return CF_OK;
   const cf_model_cfg& m = c->cfg;
@@ -271,8 +278,16 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
     if (sched_ready) *sched_ready = true;
     at.sched = sch;
   }
+  at.ml_out = mass ? mass->ml : nullptr;
   CF_RUN("attention", cf::launch_attention(at, st));
   if (at.sched) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
+  if (mass) {
+    cf::QMassArgs qm{};
+    qm.q = Q; qm.ldq = qd; qm.n = n; qm.k = kc; qm.n_ctx = mass->n_ctx;
+    qm.hq = m.n_q_heads; qm.hkv = m.n_kv_heads; qm.hd = hd;
+    qm.ml = mass->ml; qm.part = mass->part; qm.score = mass->score;
+    CF_RUN("query_mass", cf::launch_query_mass(dt, qm, mass->first ? 1 : 0, st));
+  }
 
   float* part = reinterpret_cast<float*>(ws + lw.part);
   auto proj = [&](const cf::GemmPlan& pl, const void* A, int lda, const void* B, int K) {
@@ -383,6 +398,8 @@ cf_status enqueue_reposition(const cf_ctx* c, const void* ks, const void* vs, in
   }
   return CF_OK;
 }
+
+constexpr int SEL_GIVEN = CF_SEL_GIVEN;
 
 bool span_mode(int mode) {
   return mode == CF_SEL_DOC_SPANS || mode == CF_SEL_RANKED_SPANS || mode == CF_SEL_SPAN_HEADS;
@@ -677,7 +694,9 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
   const int64_t kvd = (int64_t)mc.n_kv_heads * mc.head_dim;
   CF_CHECK(N >= 0 && U >= 0 && L > 0, CF_EINVAL, "need N, U >= 0 and N + U > 0");
   CF_CHECK(L <= c->max_pos, CF_EINVAL, "L=%d exceeds max_pos=%d", L, c->max_pos);
-  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || span_mode(mode) || mode == CF_SEL_ALL, CF_EINVAL, "unknown mode %d", mode);
+  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || span_mode(mode) || mode == CF_SEL_ALL || mode == SEL_GIVEN, CF_EINVAL,
+           "unknown mode %d", mode);
+  CF_CHECK(mode != SEL_GIVEN || k == 0 || out_sel, CF_EINVAL, "mode CF_SEL_GIVEN reads the set from out_sel");
   CF_CHECK(layers, CF_EINVAL, "null layer array");
   for (int l = 0; l < mc.n_layers; ++l)
     if (cf_status s = check_layer(c, layers + l, l)) return s;
@@ -793,7 +812,9 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
     const cf_layer_weights* w = layers + s_layer;
     const int n_sel = k + U;
     if (cf_status s = stitch_layer(s_layer)) return s;
-    if (N > 0) {
+    if (mode == SEL_GIVEN) {
+      if (k > 0) CF_RUN("copy", cf::launch_copy_i32(sel, out_sel, k, st));
+    } else if (N > 0) {
       // current keys of the context rows at the selection layer and their deviation
       void* X = lws + lw_full.x;  // the full-row layout holds N rows of X and of K
       float* KN = reinterpret_cast<float*>(lws + lw_full.qkv);
@@ -901,6 +922,84 @@ cf_status cf_blend_prefill(const cf_ctx* c, const cf_layer_weights* layers, cons
   g_err.clear();
   return prefill(c, layers, embed, final_norm, tokens, N, U, k_store, v_store, sls, store_rows, tab, m, s_layer, k, mode,
                  bounds, ns, nullptr, k_out, v_out, ols, out_hidden, out_sel, out_dev, ws, ws_bytes, st);
+}
+
+namespace {
+
+struct ScoresWs {
+  size_t hidden, sel, ml, part, layer, total;
+};
+
+ScoresWs scores_ws(const cf_ctx* c, int N, int U) {
+  const int L = N + U;
+  ScoresWs p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  p.hidden = take((size_t)L * c->cfg.d_model * 4);
+  p.sel = take((size_t)U * 4);
+  p.ml = take((size_t)U * c->cfg.n_q_heads * 2 * 4);
+  p.part = take((size_t)c->cfg.n_kv_heads * N * 4);
+  p.layer = take(layer_ws(c, L, U).total);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+size_t cf_query_scores_workspace_size(const cf_ctx* c, int32_t N, int32_t U) {
+  if (!c || N <= 0 || U <= 0) return 0;
+  return scores_ws(c, N, U).total;
+}
+
+cf_status cf_query_scores(const cf_ctx* c, const cf_layer_weights* layers, const void* embed, const int32_t* tokens,
+                          int32_t N, int32_t U, void* k_cache, void* v_cache, int64_t ols, const int32_t* layer_set,
+                          int32_t n_set, float* scores, void* ws, size_t ws_bytes, hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  const cf_model_cfg& mc = c->cfg;
+  const int L = N + U;
+  const int64_t kvd = (int64_t)mc.n_kv_heads * mc.head_dim;
+  CF_CHECK(N > 0 && U > 0, CF_EINVAL, "need N > 0 context rows and U > 0 query rows");
+  CF_CHECK(L <= c->max_pos, CF_EINVAL, "L=%d exceeds max_pos=%d", L, c->max_pos);
+  CF_CHECK(layer_set && n_set > 0, CF_EINVAL, "empty layer set");
+  for (int i = 0; i < n_set; ++i)
+    CF_CHECK(layer_set[i] >= 0 && layer_set[i] < mc.n_layers && (i == 0 || layer_set[i] > layer_set[i - 1]), CF_EINVAL,
+             "layer set must be strictly increasing layer ids in [0, %d)", mc.n_layers);
+  const int last = layer_set[n_set - 1];
+  for (int l = 0; l <= last; ++l)
+    if (cf_status s = check_layer(c, layers + l, l)) return s;
+  CF_CHECK(embed && tokens && scores && aligned16(embed), CF_EINVAL, "null or misaligned embed, tokens or scores");
+  CF_CHECK(k_cache && v_cache && aligned16(k_cache) && aligned16(v_cache), CF_EINVAL, "cache null or misaligned");
+  CF_CHECK(ols >= L * kvd && ols % 8 == 0, CF_ESHAPE, "layer stride must be >= L*kvd and a multiple of 8");
+  const ScoresWs pw = scores_ws(c, N, U);
+  CF_CHECK(ws && aligned16(ws) && ws_bytes >= pw.total, CF_EWORKSPACE, "workspace: need %zu bytes, got %zu", pw.total,
+           ws_bytes);
+  DeviceGuard guard(c->device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  char* W = static_cast<char*>(ws);
+  float* hidden = reinterpret_cast<float*>(W + pw.hidden);
+  int* sel = reinterpret_cast<int*>(W + pw.sel);
+  const LayerWs lw = layer_ws(c, L, U);
+  const cf::Dt dt = dt_of(c);
+  // the query rows only: embeddings into rows N.., positions N..L-1
+  CF_RUN("embed", cf::launch_embed(dt, tokens + N, U, embed, mc.vocab, mc.d_model, hidden + (size_t)N * mc.d_model, st));
+  CF_RUN("iota", cf::launch_iota(sel, U, N, st));
+  bool xr = false, sched = false;
+  int set_i = 0;
+  for (int l = 0; l <= last; ++l) {
+    char* kl = static_cast<char*>(k_cache) + (size_t)l * ols * esize(c);
+    char* vl = static_cast<char*>(v_cache) + (size_t)l * ols * esize(c);
+    MassHook mh{reinterpret_cast<float*>(W + pw.ml), reinterpret_cast<float*>(W + pw.part), scores, N, set_i == 0};
+    const bool scored = set_i < n_set && layer_set[set_i] == l;
+    const float* nn = l < last ? layers[l + 1].attn_norm : nullptr;
+    bool xn = false;
+    if (cf_status s = run_layer(c, layers + l, hidden, kl, vl, sel, U, L, W + pw.layer, lw, st, xr, nn, &xn, &sched,
+                                nullptr, 0, scored ? &mh : nullptr))
+      return s;
+    xr = xn;
+    if (scored) ++set_i;
+  }
+  return CF_OK;
 }
 
 size_t cf_blend_prefill_streamed_workspace_size(const cf_ctx* c, int32_t N, int32_t U, int32_t k, int32_t mode,

@@ -262,6 +262,11 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
         ml[1] = l_i[rg];
       }
     } else {
+      if (a.ml_out && lg == 0) {
+        float* ml = a.ml_out + ((int64_t)j * a.hq + head[rg]) * 2;
+        ml[0] = m_i[rg] == -INFINITY ? 0.f : m_i[rg];
+        ml[1] = l_i[rg];
+      }
       const float inv = l_i[rg] > 0.f ? 1.0f / l_i[rg] : 0.f;
       bf16* out = (bf16*)a.out + (int64_t)j * a.ldo + head[rg] * HD;
 #pragma unroll
@@ -324,6 +329,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
   T* out = (T*)a.out + (int64_t)j * a.ldo + head * a.hd + d;
   const bool ok = den > 0.f;
+  if (a.ml_out && d == 0) {
+    a.ml_out[((int64_t)j * a.hq + head) * 2] = mx == -INFINITY ? 0.f : mx;
+    a.ml_out[((int64_t)j * a.hq + head) * 2 + 1] = den;
+  }
   out[0] = from_f<T>(ok ? n0 / den : 0.f);
   out[1] = from_f<T>(ok ? n1 / den : 0.f);
   out[2] = from_f<T>(ok ? n2 / den : 0.f);
@@ -371,6 +380,10 @@ __global__ __launch_bounds__(256) void attn_simple_kernel(AttnArgs a) {
       m = m_new;
     }
     T* out = (T*)a.out + (int64_t)j * a.ldo + head * hd;
+    if (a.ml_out && lane == 0) {  // natural-log max to log2 units
+      a.ml_out[((int64_t)j * a.hq + head) * 2] = m * 1.4426950408889634f;
+      a.ml_out[((int64_t)j * a.hq + head) * 2 + 1] = l;
+    }
     if (lane < hd) out[lane] = from_f<T>(acc0 / l);
     if (lane + WAVE < hd) out[lane + WAVE] = from_f<T>(acc1 / l);
     __builtin_amdgcn_wave_barrier();

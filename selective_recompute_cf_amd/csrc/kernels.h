@@ -112,12 +112,26 @@ struct AttnArgs {
   float* o_part; float* ml_part;       // pieces' partial sums: [hkv][P][128][hd], [hkv][P][128][2]
   const AttnSched* sched; int P;       // balanced pieces (bf16): P blocks per kv head, else null
                                        // (whole query tiles)
+  float* ml_out;                       // optional [n][hq][2]: each row's softmax max and sum (log2
+                                       // units: weights are exp2(s log2(e) / sqrt(hd) - m) / l)
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);        // main pass
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st);  // merge of the pieces
 hipError_t launch_attention_sched(const AttnArgs& a, AttnSched* s, hipStream_t st);  // pieces for a.pos
 // *P > 0: balanced pieces with P blocks per kv head; 0: whole query tiles
 void attn_plan(Dt dt, int n, int hq, int hkv, int n_cu, int* P);
+
+// ----------------------------------------------------------------- query-aware scores (qmass.hip)
+// Attention mass of n query rows (Q [n][hq*hd] with row stride ldq, softmax max/sum ml [n][hq][2]
+// from the layer's attention) on the context keys k [0, n_ctx) (cache [.][hkv*hd]): part [hkv][n_ctx]
+// scratch, score[t] = (first ? 0 : score[t]) + the mass on t summed over rows and heads.
+struct QMassArgs {
+  const void* q; int64_t ldq; int n;
+  const void* k; int n_ctx;
+  int hq, hkv, hd;
+  const float* ml; float* part; float* score;
+};
+hipError_t launch_query_mass(Dt dt, const QMassArgs& a, int first, hipStream_t st);
 
 // ----------------------------------------------------------------- selection (topk.hip)
 constexpr int MAX_SPANS = 256;

@@ -77,6 +77,9 @@ def test_null_context_rejected(L):
     assert L.cf_blend_prefill_streamed(None, None, None, None, None, 1, 0, None, None, 0, 0, None, 0, 0, 0, 0, None,
                                        0, None, None, 0, None, None, None, None, 0, None) == cf.CF_EINVAL
     assert L.cf_blend_prefill_streamed_workspace_size(None, 10, 5, 3, 0, 10) == 0
+    lset = (ctypes.c_int32 * 1)(0)
+    assert L.cf_query_scores(None, None, None, None, 10, 5, None, None, 0, lset, 1, None, None, 0, None) == cf.CF_EINVAL
+    assert L.cf_query_scores_workspace_size(None, 10, 5) == 0
 
 
 def test_loading_controller_host_logic_agrees_with_oracle():
