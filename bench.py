@@ -232,6 +232,8 @@ def main():
             log(f"[bench] gradual {name}: {tg:.2f} ms ({t_full / tg:.2f}x), schedule {sch[:4]}..{sch[-1]}")
         sweep_res["streamed"] = streamed_pipeline(ctx, dm, w, tok_dev, ks, vs, table, spans, k_out, v_out, out,
                                                   k_of, sweep_res, timed)
+        sweep_res["query_aware"] = query_aware(ctx, dm, w, tok_dev, ks, vs, table, k_out, v_out, out, k, sweep_res,
+                                               timed)
 
     # ---------------------------------------------------------------- CPU oracle baseline (bounded sample)
     cpu = None
@@ -317,6 +319,45 @@ def streamed_pipeline(ctx, dm, w, tok_dev, ks, vs, table, spans, k_out, v_out, o
                                          "load_ms_all_layers": round(t_load * (cfg.n_layers - w.sel_layer), 3)}
     log(f"[bench] streamed store: {res['h2d_GBs']} GB/s host->device, {t_load:.3f} ms load per layer; "
         f"controller r = {res['controller_ratio']}; runs {res['runs']}")
+    return res
+
+
+def query_aware(ctx, dm, w, tok_dev, ks, vs, table, k_out, v_out, out, k, sweep_res, timed):
+    """QCFuse's query-aware selection (§3.2.1 Eq. 10 over all layers, Eq. 20 over three middle
+    layers) on the same request: the probe of the query rows over the stitched cache with the
+    per-layer attention mass (cf_query_scores), the top-k of the scores, and the blend of that
+    set from layer 0 (CF_SEL_GIVEN); times per step and the selection's share of the total."""
+    import torch
+    import selective_recompute_cf_amd as cf
+    cfg = dm.cfg
+    N, U, L, Ly = w.n_ctx, w.n_query, w.n_total, cfg.n_layers
+    kvd = cfg.n_kv_heads * cfg.head_dim
+    kb = torch.empty(Ly, L, kvd, dtype=ks.dtype, device="cuda")
+    vb = torch.empty_like(kb)
+    ctx.rope_reposition(ks, vs, kb, vb, table, 0, Ly)
+    scores = torch.empty(N, dtype=torch.float32, device="cuda")
+    sel = torch.empty(max(k, 1), dtype=torch.int32, device="cuda")
+    wsq = torch.empty(ctx.query_scores_workspace_size(N, U), dtype=torch.uint8, device="cuda")
+    wst = torch.empty(max(ctx.blend_prefill_workspace_size(N, U, k, "given"), cf.topk_workspace_size(N, "token"), 1),
+                      dtype=torch.uint8, device="cuda")
+    mid = Ly // 2
+    res = {}
+    for name, lset in [("all_layers", list(range(Ly))), ("three_middle_layers", [mid - 1, mid, mid + 1])]:
+        def select(lset=lset):
+            ctx.query_scores(dm.array, dm.embed, tok_dev, N, U, kb, vb, lset, scores, wsq)
+            cf.topk_select(scores, k, sel, "token", None, wst)
+
+        def blend_given():
+            ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, ks, vs, table, 0, k, "given", None,
+                              k_out, v_out, out if U else None, wst, out_sel=sel)
+
+        _, p_sel = timed(select, 5, 2)
+        _, p_bl = timed(blend_given, 5, 2)
+        t_sel, t_bl = statistics.median(p_sel), statistics.median(p_bl)
+        res[name] = {"layers": len(lset), "select_ms": round(t_sel, 3), "blend_ms": round(t_bl, 3),
+                     "total_ms": round(t_sel + t_bl, 3), "selection_share": round(t_sel / (t_sel + t_bl), 3),
+                     "speedup_vs_full_prefill": round(sweep_res["full_prefill_ms"] / (t_sel + t_bl), 3)}
+    log(f"[bench] query-aware: {res}")
     return res
 
 

@@ -26,15 +26,27 @@ import subprocess
 from collections import OrderedDict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# sources whose compiled code the GEMM traffic figures describe
-GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/kernels.h")
+# sources whose compiled code the GEMM traffic figures describe: the GEMM file, the common header
+# and the GEMM section of the shared declarations header (from its section marker to the next)
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/kernels.h#GEMM (gemm.hip)")
+
+
+def _source_text(rel: str) -> bytes:
+    path, _, section = rel.partition("#")
+    with open(os.path.join(PKG, path), "rb") as f:
+        text = f.read()
+    if not section:
+        return text
+    lines = text.decode().splitlines(keepends=True)
+    start = next(i for i, l in enumerate(lines) if l.startswith("// ---") and l.rstrip().endswith(section))
+    end = next((i for i in range(start + 1, len(lines)) if lines[i].startswith("// ---")), len(lines))
+    return "".join(lines[start:end]).encode()
 
 
 def sources_sha256(rel_paths=GEMM_SOURCES) -> str:
     h = hashlib.sha256()
     for rel in rel_paths:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+        h.update(rel.encode() + b"\0" + _source_text(rel) + b"\0")
     return h.hexdigest()
 
 
