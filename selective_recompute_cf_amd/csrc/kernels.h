@@ -87,7 +87,9 @@ struct GemmArgs {
   const float* resid; const int* resid_rows; float* out; const int* out_rows; int L;  // EPI_RESID
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
-enum GemmCfgId { GEMM_SMALL = 0, GEMM_DTL128 = 1, GEMM_DTL96 = 2, GEMM_DTL64 = 3, GEMM_DTL256 = 4, GEMM_DTL128N = 5 };
+enum GemmCfgId {
+  GEMM_SMALL = 0, GEMM_DTL128 = 1, GEMM_DTL96 = 2, GEMM_DTL64 = 3, GEMM_DTL256 = 4, GEMM_DTL128N = 5, GEMM_DTL64N = 6
+};
 struct GemmPlan { int cfg; int splits; };
 // Kernel, block height and split-K factor for an M x N x K product: a direct-to-LDS kernel when
 // K % 64 == 0 (else the register-staged one), choosing the pair that minimises (rounds of
