@@ -536,10 +536,11 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
   const Opt small_opt[1] = {{GEMM_SMALL, 128, 128, 2, 0.85}};
   const bool dtl = K % 64 == 0;
   const Opt* opts = dtl ? dtl_opts : small_opt;
-  // 64x128 blocks, two per CU, only when every row fits one block: the weights then stream once
-  // from HBM, and the finer column tiles put every CU on that stream (measured 20-25% faster at
-  // 64 rows, slower from 128 rows on, where the row tiles share each weight tile)
-  const int n_opts = dtl ? (M <= 64 ? 6 : 5) : 1;
+  // 64x128 blocks, two per CU, for few rows: the weights stream about once from HBM and the finer
+  // column tiles put every CU on that stream. Measured faster on every projection at 64 rows and
+  // on the split-K ones at 128 (down 37.6 against 53.0 us); slower on gate/up from 128 rows and
+  // on the others from about 200, where the row tiles share each weight tile.
+  const int n_opts = dtl ? (M <= 64 || (M <= 128 && !swiglu) ? 6 : 5) : 1;
   const int cols = swiglu ? 2 * N : N;
   double best_cost = 1e300;
   for (int o = 0; o < n_opts; ++o) {
