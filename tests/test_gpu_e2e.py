@@ -242,3 +242,51 @@ def test_span_policy_blends(policy):
     if np.array_equal(g["sel"], r32.sel):
         compare("out", g["out"], r32.out, "f32")
         compare("K", g["k"], r32.k.reshape(g["k"].shape), "f32")
+
+
+def test_prefill_replays_from_a_hip_graph():
+    """cf_blend_prefill enqueues kernels only (no memset, event or host wait), so a caller can
+    capture it in a HIP graph: every replay, with eager calls in between, equals the eager result
+    bit for bit."""
+    import torch
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(dtype="bf16", n_layers=3))
+    N, L = w.n_ctx, w.n_total
+    model = synth.Model(w.model)
+    chunks, _, toks = synth.request_tokens(w)
+    ctx = context(model.cfg, max_pos=4096)
+    dm = DeviceModel(model, n_layers=3)
+    gk, gv, starts = gpu_chunk_store(ctx, dm, chunks)
+    table = [(s0, 0, s0, len(c)) for s0, c in zip(starts, chunks)]
+    k = oracle.budget(N, w.rho_num, w.rho_den)
+    tok = torch.from_numpy(np.asarray(toks, np.int32)).cuda()
+    k_out = torch.zeros(3, L, ctx.kv_dim, dtype=torch.bfloat16, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    out = torch.zeros(L - N, dm.cfg.d_model, dtype=torch.float32, device="cuda")
+    sel = torch.zeros(k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(ctx.blend_prefill_workspace_size(N, L - N, k, "token"), dtype=torch.uint8, device="cuda")
+
+    def run():
+        ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok, N, L - N, gk, gv, table, 1, k, "token", None, k_out,
+                          v_out, out, ws, out_sel=sel)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, k_out, v_out, sel)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (out, k_out, v_out, sel):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((out, k_out, v_out, sel), ref):
+            assert torch.equal(a, b), f"replay {rep}"
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0])
