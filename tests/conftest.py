@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped, not failed, where no GPU is visible; on a GPU machine they run.
+    # GPU tests are skipped, not failed, where no GPU is visible; on a machine with one they run.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
