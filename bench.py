@@ -234,6 +234,8 @@ def main():
                                                   k_of, sweep_res, timed)
         sweep_res["query_aware"] = query_aware(ctx, dm, w, tok_dev, ks, vs, table, k_out, v_out, out, k, sweep_res,
                                                timed)
+        if args.workload == "llama8b":
+            sweep_res["rolling_window"] = rolling_steps(dm)
 
     # ---------------------------------------------------------------- CPU oracle baseline (bounded sample)
     cpu = None
@@ -319,6 +321,41 @@ def streamed_pipeline(ctx, dm, w, tok_dev, ks, vs, table, spans, k_out, v_out, o
                                          "load_ms_all_layers": round(t_load * (cfg.n_layers - w.sel_layer), 3)}
     log(f"[bench] streamed store: {res['h2d_GBs']} GB/s host->device, {t_load:.3f} ms load per layer; "
         f"controller r = {res['controller_ratio']}; runs {res['runs']}")
+    return res
+
+
+def rolling_steps(dm, steps=4):
+    """The rolling-agent window at the same model shape (Request Order Matters §4.1: 20 documents of
+    512 tokens, a fresh 64-token query per step, 5%): time per step of the blend and the write-back,
+    token top-k against document-aligned spans. Arriving documents are prefilled before each timed
+    step (the arrival path), as the window driver does."""
+    import torch
+    import synth
+    import selective_recompute_cf_amd as cf
+    from selective_recompute_cf_amd.rolling import RollingWindow
+    w = synth.WORKLOADS["rolling"]
+    cfg = dm.cfg
+    ctx = cf.Context.from_model_cfg(cfg, max_pos=w.n_total + w.chunk_len * (steps + 4) + 1)
+    res = {"workload": w.name}
+    for mode in ("token", "doc"):
+        rw = RollingWindow(ctx, dm, w.n_chunks, w.chunk_len, w.n_query, w.rho_num, w.rho_den,
+                           lambda j: synth.doc_tokens(j, w.chunk_len, cfg.vocab),
+                           lambda r: synth.query_tokens(r, w.n_query, cfg.vocab), mode=mode)
+        times = []
+        for i in range(steps + 1):
+            rw.prepare()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rw.step()
+            e1.record()
+            torch.cuda.synchronize()
+            if i:  # the first step warms up
+                times.append(e0.elapsed_time(e1))
+        res[mode] = {"k": rw.k, "step_ms": round(statistics.median(times), 3),
+                     "context_tokens_per_s": round(rw.N / (statistics.median(times) / 1e3), 1)}
+        del rw
+    log(f"[bench] rolling window: {res}")
     return res
 
 
