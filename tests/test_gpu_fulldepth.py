@@ -1,8 +1,10 @@
 """The Llama-3-8B-shaped request at full depth (32 layers, 6 x 512 + 64, k = 460), in the launch
-configuration the benchmark times, checked through properties that hold at any size (a CPU oracle
-run of all 32 layers at this width is too slow for a test):
-* the first layers of the 32-layer run equal a 3-layer run bit for bit (a layer's results depend
-  only on the layers before it), and the 3-layer run is held to the oracle by test_gpu_e2e;
+configuration the benchmark times, and the Qwen3-8B-shaped one (36 layers, 10 x 1024 + 128, 30%,
+qk-norm), checked through properties that hold at any size (a CPU oracle run of every layer at
+this width is too slow for a test):
+* the first three layers of the full-depth run equal a 3-layer run bit for bit (a layer's results
+  depend only on the layers before it), and the 3-layer runs are held to the oracle by
+  test_gpu_e2e;
 * the selection is the exact top-k of the GPU's own selection-layer deviation;
 * context rows outside the selection keep the re-positioned store at every layer >= 1, and the
   selected and query rows are rewritten at every layer;
@@ -19,13 +21,14 @@ from tests._gpu import context, gpu_blend, gpu_chunk_store, host, say
 pytestmark = pytest.mark.gpu
 
 
-def test_llama3_8b_full_depth_properties():
+@pytest.mark.parametrize("name,layers,k_want", [("llama8b", 32, 460), ("qwen8b", 36, 3072)])
+def test_full_depth_properties(name, layers, k_want):
     import torch
-    w = synth.WORKLOADS["llama8b"]
+    w = synth.WORKLOADS[name]
     N, L, U = w.n_ctx, w.n_total, w.n_query
     cfg = w.model
-    assert cfg.n_layers == 32
-    say("full depth: uploading 32 layers")
+    assert cfg.n_layers == layers
+    say(f"full depth {name}: uploading {layers} layers")
     model = synth.Model(cfg, cache_layers=False)
     chunks, _, toks = synth.request_tokens(w)
     ctx = context(cfg, max_pos=L + 1)
@@ -33,14 +36,14 @@ def test_llama3_8b_full_depth_properties():
     gk, gv, starts = gpu_chunk_store(ctx, dm, chunks)
     table = [(s0, 0, s0, len(c)) for s0, c in zip(starts, chunks)]
     k = oracle.budget(N, w.rho_num, w.rho_den)
-    assert k == 460
-    say("full depth: blended prefill, 32 layers")
+    assert k == k_want
+    say(f"full depth {name}: blended prefill")
     g = gpu_blend(ctx, dm, toks, N, gk, gv, table, w.sel_layer, k, "token")
-    for name in ("k", "v", "out", "dev"):
-        assert np.isfinite(g[name]).all(), name
+    for key in ("k", "v", "out", "dev"):
+        assert np.isfinite(g[key]).all(), key
     np.testing.assert_array_equal(g["sel"], oracle.select_topk(g["dev"], k))
 
-    # layers 0..2 of the 32-layer run are those of a 3-layer run (same kernels, same plans)
+    # layers 0..2 of the full-depth run are those of a 3-layer run (same kernels, same plans)
     say("full depth: 3-layer run of the same model")
     ctx3 = context(cfg.replace(n_layers=3), max_pos=L + 1)
     dm3 = DeviceModel(model, n_layers=3)
