@@ -2,9 +2,9 @@
 configuration the benchmark times, and the Qwen3-8B-shaped one (36 layers, 10 x 1024 + 128, 30%,
 qk-norm), checked through properties that hold at any size (a CPU oracle run of every layer at
 this width is too slow for a test):
-* the first three layers of the full-depth run equal a 3-layer run bit for bit (a layer's results
-  depend only on the layers before it), and the 3-layer runs are held to the oracle by
-  test_gpu_e2e;
+* the first layers of the full-depth run equal the short run (3 layers for the Llama shape, 2 for
+  the Qwen shape) bit for bit, a layer's results depending only on the layers before it; the
+  short runs are the ones test_gpu_e2e holds to the oracle;
 * the selection is the exact top-k of the GPU's own selection-layer deviation;
 * context rows outside the selection keep the re-positioned store at every layer >= 1, and the
   selected and query rows are rewritten at every layer;
@@ -21,8 +21,8 @@ from tests._gpu import context, gpu_blend, gpu_chunk_store, host, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,layers,k_want", [("llama8b", 32, 460), ("qwen8b", 36, 3072)])
-def test_full_depth_properties(name, layers, k_want):
+@pytest.mark.parametrize("name,layers,k_want,short", [("llama8b", 32, 460, 3), ("qwen8b", 36, 3072, 2)])
+def test_full_depth_properties(name, layers, k_want, short):
     import torch
     w = synth.WORKLOADS[name]
     N, L, U = w.n_ctx, w.n_total, w.n_query
@@ -43,13 +43,13 @@ def test_full_depth_properties(name, layers, k_want):
         assert np.isfinite(g[key]).all(), key
     np.testing.assert_array_equal(g["sel"], oracle.select_topk(g["dev"], k))
 
-    # layers 0..2 of the full-depth run are those of a 3-layer run (same kernels, same plans)
-    say("full depth: 3-layer run of the same model")
-    ctx3 = context(cfg.replace(n_layers=3), max_pos=L + 1)
-    dm3 = DeviceModel(model, n_layers=3)
-    g3 = gpu_blend(ctx3, dm3, toks, N, gk[:3], gv[:3], table, w.sel_layer, k, "token")
-    np.testing.assert_array_equal(g["k"][:3], g3["k"])
-    np.testing.assert_array_equal(g["v"][:3], g3["v"])
+    # the first layers of the full-depth run are those of the short run (same kernels, same plans)
+    say(f"full depth: {short}-layer run of the same model")
+    ctx3 = context(cfg.replace(n_layers=short), max_pos=L + 1)
+    dm3 = DeviceModel(model, n_layers=short)
+    g3 = gpu_blend(ctx3, dm3, toks, N, gk[:short], gv[:short], table, w.sel_layer, k, "token")
+    np.testing.assert_array_equal(g["k"][:short], g3["k"])
+    np.testing.assert_array_equal(g["v"][:short], g3["v"])
     np.testing.assert_array_equal(g["sel"], g3["sel"])
     np.testing.assert_array_equal(g["dev"], g3["dev"])
     del dm3
