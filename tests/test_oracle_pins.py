@@ -343,6 +343,89 @@ def test_doc_spans_brute_force_properties():
             assert got == sorted(want)
 
 
+# ------------------------------------------------------------------ blend mechanics at 0 < rho < 1
+
+def _torch_blend(model, tokens, N, chunks, sel_layer, P, n_layers):
+    """Blended prefill written independently with torch library ops (float64): chunk caches from
+    standalone prefill (the torch decoder), stitched by complex-number rotation by the position
+    offset, layers < s on every row, then on rows P + query: fresh K/V written into the cache at
+    their positions first, each row attending with a causal mask by absolute position over the
+    whole cache, O projection, SwiGLU; returns (K, V, normed query rows)."""
+    cfg = model.cfg
+    hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    d = torch.float64
+    L = len(tokens)
+    T = lambda a: torch.tensor(np.asarray(a), dtype=d)
+    freqs = 1.0 / (cfg.rope_theta ** (torch.arange(0, hd, 2, dtype=d) / hd))
+
+    def rotate(x, pos):  # x [n, heads, hd] by positions pos [n]
+        rot = torch.polar(torch.ones(len(pos), hd // 2, dtype=d), torch.outer(torch.as_tensor(pos, dtype=d), freqs))
+        z = torch.complex(x[..., : hd // 2], x[..., hd // 2:]) * rot[:, None, :]
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    K = torch.zeros(n_layers, L, hkv, hd, dtype=d)
+    V = torch.zeros_like(K)
+    at = 0
+    for c in chunks:  # standalone caches at positions 0.., moved to their request positions
+        kc, vc, _ = _torch_decoder(model, c, n_layers)
+        for l in range(n_layers):
+            K[l, at:at + len(c)] = rotate(torch.from_numpy(kc[l]), np.full(len(c), at))
+            V[l, at:at + len(c)] = torch.from_numpy(vc[l])
+        at += len(c)
+
+    def layer(l, h_rows, pos):
+        w = model.layer(l)
+        n = len(pos)
+        a = F.rms_norm(h_rows, (cfg.d_model,), T(w.attn_norm), eps=cfg.rms_eps)
+        q = F.linear(a, T(w.wq)).view(n, hq, hd)
+        k = F.linear(a, T(w.wk)).view(n, hkv, hd)
+        v = F.linear(a, T(w.wv)).view(n, hkv, hd)
+        if cfg.qk_norm:
+            q = F.rms_norm(q, (hd,), T(w.q_norm), eps=cfg.rms_eps)
+            k = F.rms_norm(k, (hd,), T(w.k_norm), eps=cfg.rms_eps)
+        q, k = rotate(q, pos), rotate(k, pos)
+        K[l, pos], V[l, pos] = k, v
+        kk = K[l].repeat_interleave(hq // hkv, dim=1)
+        vv = V[l].repeat_interleave(hq // hkv, dim=1)
+        sc = torch.einsum("qhd,khd->hqk", q, kk) / math.sqrt(hd)
+        sc = sc.masked_fill(~(torch.arange(L)[None, :] <= torch.as_tensor(pos)[:, None])[None], float("-inf"))
+        o = torch.einsum("hqk,khd->qhd", torch.softmax(sc, dim=-1), vv).reshape(n, hq * hd)
+        h1 = h_rows + F.linear(o, T(w.wo))
+        b = F.rms_norm(h1, (cfg.d_model,), T(w.mlp_norm), eps=cfg.rms_eps)
+        return h1 + F.linear(F.silu(F.linear(b, T(w.w_gate))) * F.linear(b, T(w.w_up)), T(w.w_down))
+
+    h = torch.tensor(model.embed[tokens], dtype=d)
+    allpos = np.arange(L)
+    for l in range(sel_layer):
+        h = layer(l, h, allpos)
+    rows = np.concatenate([np.asarray(P, np.int64), np.arange(N, L)])
+    for l in range(sel_layer, n_layers):
+        h[rows] = layer(l, h[rows], rows)
+    out = F.rms_norm(h[N:], (cfg.d_model,), torch.tensor(model.final_norm, dtype=d), eps=cfg.rms_eps)
+    return K.numpy(), V.numpy(), out.numpy()
+
+
+@pytest.mark.parametrize("cfg,s", [(TINY, 1), (TINY_QK, 1), (TINY, 2)], ids=["llama-s1", "qk-norm-s1", "llama-s2"])
+def test_blend_at_intermediate_ratio_matches_torch_blend(cfg, s):
+    """The blend mechanics at 0 < rho < 1, which no page prints values for, against the
+    independent torch implementation above for the same recompute set (the oracle's own top-k
+    of its deviation): stitching, full early layers, scatter before attention, sparse-query
+    attention over the fused cache, the query rows, the final norm."""
+    model = _Model(cfg)
+    chunks, q, toks = _request(cfg)
+    ks, vs, table = _store(model, chunks, n_layers=4)
+    N = sum(len(c) for c in chunks)
+    res = oracle.blend_prefill(model, toks, N, ks, vs, table, s, 20, ft=F64, n_layers=4)
+    assert 0 < len(res.sel) < N
+    K, V, out = _torch_blend(model, toks, N, chunks, s, res.sel, 4)
+    np.testing.assert_allclose(res.k, K, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(res.v, V, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(res.out, out, rtol=1e-9, atol=1e-11)
+    # and the given-set mode reproduces it
+    g = oracle.blend_prefill(model, toks, N, ks, vs, table, s, 20, "given", res.sel, ft=F64, n_layers=4)
+    np.testing.assert_array_equal(g.out, res.out)
+
+
 # ------------------------------------------------------------------ query-aware scores
 
 def _stitched(model, chunks, toks, ly):
