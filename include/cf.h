@@ -272,10 +272,10 @@ cf_status cf_query_scores(const cf_ctx* ctx, const cf_layer_weights* layers, con
  * recompute of one layer runs while the next layer's cache is fetched). Layer l >= sel_layer
  * of k_store/v_store (store_rows * kvd elements each, at element offset l * store_layer_stride)
  * is copied host-to-device into one of two workspace staging slots on the context's copy
- * stream, one layer ahead; the layer is re-positioned from its slot into k_out/v_out right
- * before it is used, which frees the slot for layer l + 2. The copies begin after the work
- * already enqueued on `stream` and every one of them is waited for on `stream`, so the call
- * stays stream-ordered. Results are those of cf_blend_prefill with the same arguments.
+ * stream, two layers ahead, and re-positioned from its slot into k_out/v_out on that same
+ * stream, which then refills the slot with layer l + 2; `stream` waits for layer l right
+ * before using it. The copy stream's work begins after the work already enqueued on `stream`
+ * and every part of it is waited for on `stream`, so the call stays stream-ordered. Results are those of cf_blend_prefill with the same arguments.
  *  k_store, v_store: PINNED host memory (hipHostMalloc or equivalent), same layout as in
  *    cf_blend_prefill; other memory is rejected with CF_EINVAL. The caller keeps them unchanged
  *    until the stream has passed the call.

@@ -23,9 +23,9 @@ struct cf_ctx {
   float* cos_t;  // [max_pos][head_dim/2]
   float* sin_t;
   // host-to-device copies of a chunk store in host memory (cf_blend_prefill_streamed): a copy
-  // stream (default priority) and, per staging slot, "copied" and "consumed" events
+  // stream (default priority), the call-start event and, per staging slot, a layer-ready event
   hipStream_t copy_st;
-  hipEvent_t start_ev, copied[2], consumed[2];
+  hipEvent_t start_ev, copied[2];
   // end of the last two streamed calls (by call parity) and the number of streamed calls made
   hipEvent_t done[2];
   mutable long long streamed_calls;
@@ -425,7 +425,7 @@ cf_status check_spans(const int32_t* b, int ns, int n, int mode = CF_SEL_DOC_SPA
 // Frees what a context holds (members not yet created are null); the context's device is current.
 void destroy_ctx(cf_ctx* c) {
   if (c->copy_st) (void)hipStreamSynchronize(c->copy_st);
-  for (hipEvent_t ev : {c->start_ev, c->copied[0], c->copied[1], c->consumed[0], c->consumed[1], c->done[0], c->done[1]})
+  for (hipEvent_t ev : {c->start_ev, c->copied[0], c->copied[1], c->done[0], c->done[1]})
     if (ev) (void)hipEventDestroy(ev);
   if (c->copy_st) (void)hipStreamDestroy(c->copy_st);
   if (c->cos_t) (void)hipFree(c->cos_t);
@@ -561,8 +561,7 @@ cf_status cf_ctx_create(const cf_model_cfg* cfg, int32_t max_pos, int32_t device
   if (e == hipSuccess) e = hipMemcpy(c->cos_t, cs.data(), bytes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->sin_t, sn.data(), bytes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->copy_st, hipStreamNonBlocking);
-  hipEvent_t* evs[] = {&c->start_ev, &c->copied[0], &c->copied[1], &c->consumed[0], &c->consumed[1], &c->done[0],
-                       &c->done[1]};
+  hipEvent_t* evs[] = {&c->start_ev, &c->copied[0], &c->copied[1], &c->done[0], &c->done[1]};
   for (hipEvent_t* ev : evs)
     if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -754,32 +753,30 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
     if (cf_status s = enqueue_reposition(c, k_store, v_store, sls, k_out, v_out, ols, tab, m, first_sel,
                                          mc.n_layers, st))
       return s;
-  // Streamed store: layer l's K/V go host -> slot (l - s) % 2 on the copy stream; the layer is
-  // re-positioned from its slot right before it is needed, which frees the slot for layer l + 2.
-  // The copies start after the caller's earlier work on `st` (the slots may still be in use by
-  // a previous call) and overlap this call's kernels; every copy is waited for on `st`.
+  // Streamed store: on the copy stream, layer l's K/V go host -> slot (l - s) % 2 and are
+  // re-positioned from there into k_out/v_out[l]; an event then marks layer l ready, and the
+  // compute stream waits for it right before layer l. The copy stream's own order keeps a slot
+  // from being refilled (layer l + 2) before its re-position has read it, so the compute stream
+  // records nothing. The copy stream starts after the caller's earlier work on `st` (the slots
+  // and k_out may still be in use by a previous call) and runs one layer ahead of the compute.
   const size_t slot_bytes = (size_t)store_rows * kvd * esize(c);
   auto slot_k = [&](int l) { return W + pw.stage + (size_t)((l - first_sel) % 2) * 2 * slot_bytes; };
-  auto issue_copy = [&](int l) -> cf_status {
-    const int slot = (l - first_sel) % 2;
-    if (l - first_sel >= 2) CF_HIP(hipStreamWaitEvent(c->copy_st, c->consumed[slot], 0));
+  auto load_layer = [&](int l) -> cf_status {
     const size_t layer_off = (size_t)l * sls * esize(c);
     CF_HIP(hipMemcpyAsync(slot_k(l), static_cast<const char*>(k_store) + layer_off, slot_bytes,
                           hipMemcpyHostToDevice, c->copy_st));
     CF_HIP(hipMemcpyAsync(slot_k(l) + slot_bytes, static_cast<const char*>(v_store) + layer_off, slot_bytes,
                           hipMemcpyHostToDevice, c->copy_st));
-    CF_HIP(hipEventRecord(c->copied[slot], c->copy_st));
+    if (cf_status s = enqueue_reposition(c, slot_k(l), slot_k(l) + slot_bytes, 0, K_l(l), V_l(l), ols, tab, m, 0, 1,
+                                         c->copy_st))
+      return s;
+    CF_HIP(hipEventRecord(c->copied[(l - first_sel) % 2], c->copy_st));
     return CF_OK;
   };
   auto stitch_layer = [&](int l) -> cf_status {
     if (!streamed) return CF_OK;
-    const int slot = (l - first_sel) % 2;
-    CF_HIP(hipStreamWaitEvent(st, c->copied[slot], 0));
-    if (cf_status s = enqueue_reposition(c, slot_k(l), slot_k(l) + slot_bytes, 0, K_l(l), V_l(l), ols, tab, m, 0, 1,
-                                         st))
-      return s;
-    CF_HIP(hipEventRecord(c->consumed[slot], st));
-    if (l + 2 < mc.n_layers) return issue_copy(l + 2);
+    CF_HIP(hipStreamWaitEvent(st, c->copied[(l - first_sel) % 2], 0));
+    if (l + 2 < mc.n_layers) return load_layer(l + 2);  // its record of this parity comes after the wait
     return CF_OK;
   };
   if (streamed) {
@@ -793,7 +790,7 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
     CF_HIP(hipEventRecord(c->start_ev, st));
     CF_HIP(hipStreamWaitEvent(c->copy_st, c->start_ev, 0));
     for (int l = first_sel; l < std::min(first_sel + 2, mc.n_layers); ++l)
-      if (cf_status s = issue_copy(l)) return s;
+      if (cf_status s = load_layer(l)) return s;
   }
   CF_RUN("embed", cf::launch_embed(dt, tokens, L, embed, mc.vocab, mc.d_model, hidden, st));
   CF_RUN("iota", cf::launch_iota(ident, L, 0, st));
