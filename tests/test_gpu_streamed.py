@@ -133,3 +133,34 @@ def test_store_must_be_pinned_host_memory():
     g = _streamed(ctx, dm, toks, N, _pinned(gk), _pinned(gv), table, 1, k, "token")
     torch.cuda.synchronize()
     _same(g, gpu_blend(ctx, dm, toks, N, gk, gv, table, 1, k, "token"))
+
+
+@pytest.mark.parametrize("mode", ["ranked", "heads", "token"])
+def test_permuted_store_span_modes_no_query(mode):
+    """A store that holds one spare chunk (NaN rows that no table entry names) and then the request's
+    chunks in reverse order, a request without query rows, and the span modes: the streamed call
+    equals the resident call on that store, and both equal the resident call on the store laid out
+    in request order (the table's store rows alone decide where each chunk is read)."""
+    import torch
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(dtype="bf16", n_layers=4))
+    N, cl = w.n_ctx, w.chunk_len
+    model, chunks, toks, ctx, dm, gk, gv, table = _setup(w, 4)
+    toks = toks[:N]
+    k = oracle.budget(N, w.rho_num, w.rho_den)
+    docs = [i * cl for i in range(w.n_chunks + 1)]
+    order = np.random.default_rng(9).permutation(w.n_chunks).tolist()
+    spans = {"ranked": (docs, order), "heads": docs, "token": None}[mode]
+    spare = torch.full((4, cl, ctx.kv_dim), float("nan"), dtype=gk.dtype, device="cuda")
+    rev = list(range(w.n_chunks))[::-1]
+    pk = torch.cat([spare] + [gk[:, docs[i]:docs[i + 1]] for i in rev], dim=1).contiguous()
+    pv = torch.cat([spare] + [gv[:, docs[i]:docs[i + 1]] for i in rev], dim=1).contiguous()
+    ptable = [(cl * (1 + rev.index(i)), 0, docs[i], cl) for i in range(w.n_chunks)]
+    say(f"permuted store, mode {mode}, k={k}, no query rows")
+    want = gpu_blend(ctx, dm, toks, N, gk, gv, table, 1, k, mode, spans)
+    res = gpu_blend(ctx, dm, toks, N, pk, pv, ptable, 1, k, mode, spans)
+    for name in ["k", "v", "out", "sel", "dev"]:
+        np.testing.assert_array_equal(res[name], want[name], err_msg=name)
+    assert np.isfinite(want["k"]).all() and want["out"].shape[0] == 0
+    g = _streamed(ctx, dm, toks, N, _pinned(pk), _pinned(pv), ptable, 1, k, mode, spans)
+    torch.cuda.synchronize()
+    _same(g, want)
