@@ -275,7 +275,9 @@ cf_status cf_query_scores(const cf_ctx* ctx, const cf_layer_weights* layers, con
  * stream, two layers ahead, and re-positioned from its slot into k_out/v_out on that same
  * stream, which then refills the slot with layer l + 2; `stream` waits for layer l right
  * before using it. The copy stream's work begins after the work already enqueued on `stream`
- * and every part of it is waited for on `stream`, so the call stays stream-ordered. Results are those of cf_blend_prefill with the same arguments.
+ * and every part of it is waited for on `stream`, so the call stays stream-ordered; this holds
+ * for a call that fails after its first copy was queued too (the error is returned after
+ * `stream` has been made to wait for the copy stream). Results are those of cf_blend_prefill with the same arguments.
  *  k_store, v_store: PINNED host memory (hipHostMalloc or equivalent), same layout as in
  *    cf_blend_prefill; other memory is rejected with CF_EINVAL. The caller keeps them unchanged
  *    until the stream has passed the call.

@@ -758,7 +758,17 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
   // compute stream waits for it right before layer l. The copy stream's own order keeps a slot
   // from being refilled (layer l + 2) before its re-position has read it, so the compute stream
   // records nothing. The copy stream starts after the caller's earlier work on `st` (the slots
-  // and k_out may still be in use by a previous call) and runs one layer ahead of the compute.
+  // and k_out may still be in use by a previous call) and runs up to two layers ahead of the
+  // compute. If the call fails after the copy stream has started, the guard below makes `st`
+  // wait for everything queued on it, so the caller's buffers are stream-ordered either way.
+  struct CopyJoin {
+    const cf_ctx* c;
+    hipStream_t st;
+    bool on;
+    ~CopyJoin() {
+      if (on && hipEventRecord(c->start_ev, c->copy_st) == hipSuccess) (void)hipStreamWaitEvent(st, c->start_ev, 0);
+    }
+  } join{c, st, false};
   const size_t slot_bytes = (size_t)store_rows * kvd * esize(c);
   auto slot_k = [&](int l) { return W + pw.stage + (size_t)((l - first_sel) % 2) * 2 * slot_bytes; };
   auto load_layer = [&](int l) -> cf_status {
@@ -789,6 +799,7 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
     if (n >= 1) CF_HIP(hipEventSynchronize(c->done[(n - 1) % 2]));
     CF_HIP(hipEventRecord(c->start_ev, st));
     CF_HIP(hipStreamWaitEvent(c->copy_st, c->start_ev, 0));
+    join.on = true;
     for (int l = first_sel; l < std::min(first_sel + 2, mc.n_layers); ++l)
       if (cf_status s = load_layer(l)) return s;
   }
@@ -900,6 +911,7 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
     CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(cf::F32, hidden + (size_t)N * mc.d_model, nullptr, U, U, mc.d_model, final_norm,
                                    mc.rms_eps, out_hidden, mc.d_model, st));
   if (streamed) {
+    join.on = false;  // every layer the copy stream loaded has been waited for on `st`
     CF_HIP(hipEventRecord(c->done[c->streamed_calls % 2], st));
     ++c->streamed_calls;
   }
