@@ -164,6 +164,19 @@ def _span_arg(mode: str, span_bounds):
     return arr, max(0, nb - 1)
 
 
+def _room(t, n: int, name: str, dtype=None):
+    """Raise CF_EDTYPE unless t (when given) has the dtype, CF_EINVAL unless its storage holds n elements from its
+    data pointer on. The library reads and writes through raw pointers and cannot see allocation
+    sizes, so this is where a short or mistyped buffer is caught before any kernel runs."""
+    if t is None or n <= 0:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise CfError(CF_EDTYPE, f"{name}: dtype {t.dtype}, expected {dtype}")
+    avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if n > avail:
+        raise CfError(CF_EINVAL, f"{name}: needs {n} elements from its start, has {avail}")
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
@@ -207,6 +220,25 @@ class Context:
     def kv_dim(self) -> int:
         return self.cfg.n_kv_heads * self.cfg.head_dim
 
+    def _tdt(self):
+        torch = _torch()
+        return torch.bfloat16 if self.cfg.dtype == CF_BF16 else torch.float32
+
+    def _room_prefill(self, tokens, N, U, embed, final_norm, k_store, v_store, sls, sr, k_out, v_out, ols,
+                      out_hidden):
+        """Sizes and dtypes of the buffers every prefill call shares."""
+        torch = _torch()
+        Ly, kvd, d, dt = self.cfg.n_layers, self.kv_dim, self.cfg.d_model, self._tdt()
+        _room(tokens, N + U, "tokens", torch.int32)
+        _room(embed, self.cfg.vocab * d, "embed", dt)
+        _room(final_norm, d, "final_norm", torch.float32)
+        if sr > 0:
+            _room(k_store, (Ly - 1) * sls + sr * kvd, "k_store", dt)
+            _room(v_store, (Ly - 1) * sls + sr * kvd, "v_store", dt)
+        _room(k_out, (Ly - 1) * ols + (N + U) * kvd, "k_out", dt)
+        _room(v_out, (Ly - 1) * ols + (N + U) * kvd, "v_out", dt)
+        _room(out_hidden, U * d, "out_hidden", torch.float32)
+
     # ------------------------------------------------------------------ entry points
     def rope_reposition(self, k_store, v_store, k_blend, v_blend, chunk_tab: Sequence[Sequence[int]],
                         layer_begin: int, layer_end: int, store_rows: Optional[int] = None,
@@ -218,6 +250,11 @@ class Context:
         br = blend_rows if blend_rows is not None else k_blend.shape[-2]
         sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
         bls = blend_layer_stride if blend_layer_stride is not None else br * self.kv_dim
+        if layer_end > layer_begin:
+            for t, nm in ((k_store, "k_store"), (v_store, "v_store")):
+                _room(t, (layer_end - 1) * sls + sr * self.kv_dim, nm, self._tdt())
+            for t, nm in ((k_blend, "k_blend"), (v_blend, "v_blend")):
+                _room(t, (layer_end - 1) * bls + br * self.kv_dim, nm, self._tdt())
         _check(lib().cf_rope_reposition(self.handle, _ptr(k_store), _ptr(v_store), sls, sr, _ptr(k_blend),
                                         _ptr(v_blend), bls, br, tab, nflat // 4, layer_begin, layer_end,
                                         _stream(k_blend.device)))
@@ -226,7 +263,13 @@ class Context:
         return int(lib().cf_blend_layer_workspace_size(self.handle, L, n_sel))
 
     def blend_layer(self, weights: LayerWeights, hidden, k_cache, v_cache, sel, ws):
+        torch = _torch()
         n_sel = 0 if sel is None else int(sel.numel())
+        L = hidden.shape[0]
+        _room(hidden, L * self.cfg.d_model, "hidden", torch.float32)
+        _room(k_cache, L * self.kv_dim, "k_cache", self._tdt())
+        _room(v_cache, L * self.kv_dim, "v_cache", self._tdt())
+        _room(sel, n_sel, "sel", torch.int32)
         _check(lib().cf_blend_layer(self.handle, ctypes.byref(weights), _ptr(hidden), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(sel), n_sel, hidden.shape[0], _ptr(ws), 0 if ws is None else ws.numel(),
                                     _stream(hidden.device)))
@@ -244,6 +287,10 @@ class Context:
         sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
         sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
         ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        self._room_prefill(tokens, N, U, embed, final_norm, k_store, v_store, sls, sr, k_out, v_out, ols, out_hidden)
+        if mode != "all":
+            _room(out_sel, k, "out_sel", _torch().int32)
+            _room(out_dev, N, "out_dev", _torch().float32)
         _check(lib().cf_blend_prefill(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
                                       _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, k,
                                       MODES[mode], spans, ns, _ptr(k_out), _ptr(v_out), ols,
@@ -260,6 +307,13 @@ class Context:
         summed over the layers in layer_set; k_cache/v_cache hold the stitched cache of every layer."""
         lset, nset = _host_i32(list(layer_set))
         ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        torch = _torch()
+        ext = (self.cfg.n_layers - 1) * ols + (N + U) * self.kv_dim
+        _room(tokens, N + U, "tokens", torch.int32)
+        _room(embed, self.cfg.vocab * self.cfg.d_model, "embed", self._tdt())
+        _room(k_cache, ext, "k_cache", self._tdt())
+        _room(v_cache, ext, "v_cache", self._tdt())
+        _room(scores, N, "scores", torch.float32)
         _check(lib().cf_query_scores(self.handle, layers, _ptr(embed), _ptr(tokens), N, U, _ptr(k_cache),
                                      _ptr(v_cache), ols, lset, nset, _ptr(scores), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(tokens.device)))
@@ -277,6 +331,10 @@ class Context:
         sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
         sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
         ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        self._room_prefill(tokens, N, U, embed, final_norm, k_store, v_store, sls, sr, k_out, v_out, ols, out_hidden)
+        if mode != "all":
+            _room(out_sel, k, "out_sel", _torch().int32)
+            _room(out_dev, N, "out_dev", _torch().float32)
         _check(lib().cf_blend_prefill_streamed(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
                                                _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, k,
                                                MODES[mode], spans, ns, _ptr(k_out), _ptr(v_out), ols,
@@ -299,6 +357,10 @@ class Context:
         sr = store_rows if store_rows is not None else (0 if k_store is None else k_store.shape[-2])
         sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
         ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        self._room_prefill(tokens, N, U, embed, final_norm, k_store, v_store, sls, sr, k_out, v_out, ols, out_hidden)
+        ks = [int(x) for x in k_sched]
+        _room(out_sets, sum(ks), "out_sets", _torch().int32)
+        _room(out_devs, N + sum(ks[1:-1]), "out_devs", _torch().float32)
         _check(lib().cf_blend_prefill_gradual(self.handle, layers, _ptr(embed), _ptr(final_norm), _ptr(tokens), N, U,
                                               _ptr(k_store), _ptr(v_store), sls, sr, tab, nflat // 4, sel_layer, sched,
                                               _ptr(k_out), _ptr(v_out), ols, _ptr(out_hidden), _ptr(out_sets),
@@ -322,6 +384,10 @@ def kv_deviation(k_new, k_ref, dev, kv_dim: Optional[int] = None):
     """dev[i] = sum_c (k_new[i, c] - k_ref[i, c])^2; 2-D tensors [n, >= kv_dim]."""
     n = k_new.shape[0]
     kvd = kv_dim if kv_dim is not None else k_new.shape[1]
+    if n > 0:
+        _room(k_new, (n - 1) * k_new.stride(0) + kvd, "k_new")
+        _room(k_ref, (n - 1) * k_ref.stride(0) + kvd, "k_ref")
+        _room(dev, n, "dev", _torch().float32)
     _check(lib().cf_kv_deviation(_ptr(k_new), _dtype_code(k_new), k_new.stride(0), _ptr(k_ref), _dtype_code(k_ref),
                                  k_ref.stride(0), _ptr(dev), n, kvd, _stream(dev.device)))
 
@@ -332,6 +398,7 @@ def topk_workspace_size(n: int, mode: str) -> int:
 
 def topk_select(dev, k: int, out_idx, mode: str = "token", span_bounds=None, ws=None):
     spans, ns = _span_arg(mode, span_bounds)
+    _room(out_idx, k, "out_idx", _torch().int32)
     _check(lib().cf_topk_select(_ptr(dev), dev.numel(), k, MODES[mode], spans, ns, _ptr(out_idx),
                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev.device)))
 

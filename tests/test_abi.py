@@ -144,3 +144,23 @@ def test_ranked_span_order_validation(L):
     assert L.cf_topk_select(None, 10, 0, cf.CF_SEL_RANKED_SPANS, good, 3, None, None, 0, None) == cf.CF_OK
     assert L.cf_topk_select(None, 10, 3, cf.CF_SEL_SPAN_HEADS, good, 3, None, None, 0, None) == cf.CF_EINVAL
     assert cf.topk_workspace_size(10, "ranked") == 0 and cf.topk_workspace_size(10, "heads") == 0
+
+
+def test_binding_checks_buffer_extent_and_dtype():
+    """The binding's buffer check: the storage from a tensor's data pointer must hold the elements
+    the call will touch (a view's offset counts), and the dtype must be the expected one."""
+    import torch
+    base = torch.zeros(3, 10, 4)
+    cf._room(base, 120, "a", torch.float32)
+    cf._room(base[:, 2:], 120 - 8, "view")  # from element 8 on
+    cf._room(None, 10**9, "absent")
+    cf._room(base, 0, "nothing touched")
+    with pytest.raises(cf.CfError) as e:
+        cf._room(base, 121, "a")
+    assert e.value.status == cf.CF_EINVAL and "121" in str(e.value)
+    with pytest.raises(cf.CfError) as e:
+        cf._room(base[1:], 120 - 39, "view")
+    assert e.value.status == cf.CF_EINVAL
+    with pytest.raises(cf.CfError) as e:
+        cf._room(base.to(torch.bfloat16), 1, "a", torch.float32)
+    assert e.value.status == cf.CF_EDTYPE

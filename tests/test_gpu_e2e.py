@@ -290,3 +290,49 @@ def test_prefill_replays_from_a_hip_graph():
         run()
         torch.cuda.synchronize()
         assert torch.equal(out, ref[0])
+
+
+def test_short_or_mistyped_buffers_rejected_before_launch():
+    """The binding holds every buffer to the call's sizes and the model dtype: a short K/V output,
+    token array, selection output or store, and a mistyped output raise before anything is enqueued,
+    so the outputs keep their contents; the same call with the right buffers then succeeds."""
+    import torch
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(n_layers=2))
+    N, L = w.n_ctx, w.n_total
+    U = L - N
+    model = synth.Model(w.model)
+    chunks, _, toks = synth.request_tokens(w)
+    ctx = context(model.cfg, max_pos=4096)
+    dm = DeviceModel(model, n_layers=2)
+    gk, gv, starts = gpu_chunk_store(ctx, dm, chunks)
+    table = [(s0, 0, s0, len(c)) for s0, c in zip(starts, chunks)]
+    k = oracle.budget(N, w.rho_num, w.rho_den)
+    kvd, d = ctx.kv_dim, dm.cfg.d_model
+    k_out = torch.full((2, L, kvd), 7.0, device="cuda")
+    v_out = torch.full_like(k_out, 7.0)
+    out = torch.full((U, d), 7.0, device="cuda")
+    sel = torch.full((k,), -1, dtype=torch.int32, device="cuda")
+    dev = torch.zeros(N, device="cuda")
+    ws = torch.empty(ctx.blend_prefill_workspace_size(N, U, k, "token"), dtype=torch.uint8, device="cuda")
+    tok = torch.from_numpy(np.asarray(toks, np.int32)).cuda()
+    good = dict(tokens=tok, k_store=gk, v_store=gv, k_out=k_out, v_out=v_out, out_sel=sel)
+
+    def call(**kw):
+        a = {**good, **kw}
+        ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, a["tokens"], N, U, a["k_store"], a["v_store"], table, 1,
+                          k, "token", None, a["k_out"], a["v_out"], out, ws, out_sel=a["out_sel"], out_dev=dev,
+                          store_rows=N)
+
+    bad = [dict(k_out=torch.zeros(2, L - 1, kvd, device="cuda")), dict(tokens=tok[:-1].clone()),
+           dict(out_sel=torch.zeros(k - 1, dtype=torch.int32, device="cuda")), dict(k_store=gk[:, :-1].clone()),
+           dict(v_out=v_out.to(torch.bfloat16)), dict(out_sel=sel.long())]
+    for i, kw in enumerate(bad):
+        with pytest.raises(cf.CfError) as e:
+            call(**kw)
+        assert e.value.status in (cf.CF_EINVAL, cf.CF_EDTYPE), i
+        say(f"  rejected ({i}): {e.value}")
+    torch.cuda.synchronize()
+    assert bool((k_out == 7.0).all()) and bool((out == 7.0).all()) and bool((sel == -1).all())
+    call()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), gpu_blend(ctx, dm, toks, N, gk, gv, table, 1, k, "token")["out"])
