@@ -7,6 +7,7 @@ import re
 import pytest
 
 import oracle
+import synth
 import selective_recompute_cf_amd as cf
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -164,3 +165,47 @@ def test_binding_checks_buffer_extent_and_dtype():
     with pytest.raises(cf.CfError) as e:
         cf._room(base.to(torch.bfloat16), 1, "a", torch.float32)
     assert e.value.status == cf.CF_EDTYPE
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch):
+    """No fallback: with libcf.so absent, every entry point raises instead of computing anything."""
+    monkeypatch.setattr(cf, "LIB_PATH", os.path.join(os.path.dirname(cf.LIB_PATH), "absent", "libcf.so"))
+    monkeypatch.setattr(cf, "_lib", None)
+    for call in (cf.lib, cf.version, lambda: cf.topk_workspace_size(10, "token"),
+                 lambda: cf.Context.from_model_cfg(synth.TINY, max_pos=64)):
+        with pytest.raises(RuntimeError, match="missing"):
+            call()
+
+
+def _oracle_imports(path):
+    """(enclosing function or None, line) of every import of the oracle package in a source file."""
+    import ast
+    tree = ast.parse(open(path).read())
+    found = []
+
+    def walk(node, fn):
+        for child in ast.iter_child_nodes(node):
+            f = child.name if isinstance(child, (ast.FunctionDef, ast.AsyncFunctionDef)) else fn
+            names = []
+            if isinstance(child, ast.Import):
+                names = [a.name for a in child.names]
+            elif isinstance(child, ast.ImportFrom):
+                names = [child.module or ""]
+            if any(n == "oracle" or n.startswith("oracle.") for n in names):
+                found.append((f, child.lineno))
+            walk(child, f)
+    walk(tree, None)
+    return found
+
+
+def test_oracle_only_reached_from_tests_smoke_and_cpu_baseline():
+    """The product package never imports the oracle; bench.py only in its cpu_baseline leg and
+    __graft_entry__.py only in smoke()."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "selective_recompute_cf_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                assert _oracle_imports(os.path.join(dirpath, f)) == [], f
+    assert {fn for fn, _ in _oracle_imports(os.path.join(root, "bench.py"))} <= {"cpu_baseline"}
+    assert {fn for fn, _ in _oracle_imports(os.path.join(root, "__graft_entry__.py"))} <= {"smoke"}
