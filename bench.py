@@ -44,6 +44,9 @@ def main():
     ap.add_argument("--store-cache", default=None,
                     help="load the chunk store from this file if it exists, else build it and save it there")
     ap.add_argument("--prepare-only", action="store_true", help="build (and save) the chunk store, then exit")
+    ap.add_argument("--store", choices=["device", "host"], default="device",
+                    help="where the chunk store lives for the timed step: resident in HBM (cf_blend_prefill), or "
+                         "in pinned host memory, streamed in per layer (cf_blend_prefill_streamed; PCIe-inclusive)")
     ap.add_argument("--sweeps", action="store_true",
                     help="only run the kernel sweeps beyond the request's own sizes (re-position over all layers, "
                          "deviation up to GB sizes, top-k up to 256M, measured copy and MFMA peaks), print them as one "
@@ -126,6 +129,12 @@ def main():
     ws_bytes = max([ctx.blend_prefill_workspace_size(N, U, kk, w.mode) for kk in list(k_of.values()) + [k]] +
                    [ctx.blend_prefill_workspace_size(N, U, N, "all")] +
                    [ctx.blend_prefill_gradual_workspace_size(N, U, w.sel_layer, g) for g in gradual.values()])
+    if args.store == "host":
+        ws_bytes = max(ws_bytes, ctx.blend_prefill_streamed_workspace_size(N, U, k, w.mode, N))
+        hks = torch.empty(ks.shape, dtype=ks.dtype, pin_memory=True)
+        hvs = torch.empty(vs.shape, dtype=vs.dtype, pin_memory=True)
+        hks.copy_(ks)
+        hvs.copy_(vs)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     k_out = torch.zeros(Ly, L, kvd, dtype=dt, device="cuda")
     v_out = torch.zeros_like(k_out)
@@ -135,6 +144,12 @@ def main():
     def blend(kk=k):
         ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, ks, vs, table, w.sel_layer, kk, w.mode,
                           spans, k_out, v_out, out if U else None, ws, out_sel=sel)
+
+    def blend_host_store():
+        ctx.blend_prefill_streamed(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, hks, hvs, table, w.sel_layer, k,
+                                   w.mode, spans, k_out, v_out, out if U else None, ws, out_sel=sel)
+
+    step = blend_host_store if args.store == "host" else blend
 
     def full():
         ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok_dev, N, U, None, None, None, 0, 0, "all", None,
@@ -157,7 +172,7 @@ def main():
 
     # ---------------------------------------------------------------- headline timing
     log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps")
-    wall, per = timed(blend, args.steps, args.warmup)
+    wall, per = timed(step, args.steps, args.warmup)
     value = N * args.steps / wall
     ms_step = wall / args.steps * 1e3
     sel_host = sel[:k].cpu().numpy()
@@ -167,7 +182,7 @@ def main():
     P = args.profile_steps
     cf.profile_enable(True)
     for _ in range(P):
-        blend()
+        step()
     torch.cuda.synchronize()
     rep = cf.profile_report()
     cf.profile_enable(False)
@@ -259,6 +274,7 @@ def main():
         "config": {"workload": w.name, "model_shape": cfg.name, "layers": Ly, "n_ctx": N, "n_query": U,
                    "chunks": f"{w.n_chunks}x{w.chunk_len}", "recompute_ratio": f"{w.rho_num}/{w.rho_den}",
                    "k": k, "selection": w.mode, "selection_layer": w.sel_layer,
+                   "chunk_store": "HBM" if args.store == "device" else "pinned host memory, streamed per layer",
                    "all_tokens_per_s": round((N + U) * args.steps / wall, 1)},
         "roofline": roofline,
         "kernels": kernels,

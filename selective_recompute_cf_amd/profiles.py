@@ -9,9 +9,16 @@
   sources it records still matches.
 
     python -m selective_recompute_cf_amd.profiles stats <kernel_stats.csv> <out.md> --command "..."
+* ``overlap``: from a ``--kernel-trace --memory-copy-trace`` run, how much of the host-to-device
+  copy time (and of the kernels matching a side pattern, e.g. the copy stream's re-position)
+  falls inside the execution intervals of the other kernels, counted from the first dispatch of
+  a start kernel on.
+
     python -m selective_recompute_cf_amd.profiles traffic --fetch F.csv --write W.csv \
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --pattern gemm_bf16 \
         --out-md OUT.md --out-json OUT.json --command "..."
+    python -m selective_recompute_cf_amd.profiles overlap <kernel_trace.csv> <memory_copy_trace.csv> <out.md> \
+        --start embed_kernel --side reposition --command "..."
 """
 from __future__ import annotations
 
@@ -190,6 +197,60 @@ def cmd_traffic(a):
         f.write("\n".join(lines) + "\n")
 
 
+def _union(intervals):
+    out = []
+    for s, e in sorted(intervals):
+        if out and s <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], e)
+        else:
+            out.append([s, e])
+    return out
+
+
+def _covered(union, s, e):
+    """Length of [s, e) inside the (sorted, disjoint) union."""
+    import bisect
+    i = max(0, bisect.bisect_right([u[0] for u in union], s) - 1)
+    c = 0
+    while i < len(union) and union[i][0] < e:
+        c += max(0, min(e, union[i][1]) - max(s, union[i][0]))
+        i += 1
+    return c
+
+
+def cmd_overlap(a):
+    kt = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+          for r in csv.DictReader(open(a.kernel_trace))]
+    cp = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+          for r in csv.DictReader(open(a.copy_trace)) if r["Direction"] == "MEMORY_COPY_HOST_TO_DEVICE"]
+    starts = [s for s, _, n in kt if a.start in n]
+    if not starts:
+        raise SystemExit(f"no '{a.start}' dispatch in {a.kernel_trace}")
+    t0 = min(starts)
+    side = [(s, e) for s, e, n in kt if s >= t0 and a.side in n]
+    main_u = _union([(s, e) for s, e, n in kt if s >= t0 and a.side not in n])
+    copies = [(s, e) for s, e in cp if s >= t0]
+    if not copies:
+        raise SystemExit("no host-to-device copy after the start kernel")
+    c_tot = sum(e - s for s, e in copies)
+    c_cov = sum(_covered(main_u, s, e) for s, e in copies)
+    s_tot = sum(e - s for s, e in side)
+    s_cov = sum(_covered(main_u, s, e) for s, e in side)
+    m_tot = sum(e - s for s, e in main_u)
+    lines = [f"# {a.title}", "", "Commands:", "", "```", a.command, "```", "",
+             f"Counted from the first `{a.start}` dispatch on; the other kernels are every dispatch whose name does "
+             f"not contain `{a.side}`.", "",
+             f"- Host-to-device copies: {len(copies)}, {c_tot / 1e6:.2f} ms in total, "
+             f"{c_tot / len(copies) / 1e3:.1f} us on average; {c_cov / 1e6:.2f} ms "
+             f"({100 * c_cov / c_tot:.1f}%) of it while other kernels ran.",
+             f"- `{a.side}` dispatches: {len(side)}, {s_tot / 1e6:.2f} ms in total"
+             + (f", {s_tot / len(side) / 1e3:.1f} us on average; {s_cov / 1e6:.2f} ms ({100 * s_cov / s_tot:.1f}%) "
+                f"of it while other kernels ran." if side else "."),
+             f"- The other kernels were busy (union of their intervals) for {m_tot / 1e6:.2f} ms."]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -209,8 +270,16 @@ def main():
     t.add_argument("--out-json", required=True)
     t.add_argument("--title", default="HBM traffic per dispatch")
     t.add_argument("--command", required=True)
+    o = sub.add_parser("overlap")
+    o.add_argument("kernel_trace")
+    o.add_argument("copy_trace")
+    o.add_argument("out")
+    o.add_argument("--start", required=True, help="count from the first dispatch whose name contains this")
+    o.add_argument("--side", required=True, help="kernels on the copy stream, reported like the copies")
+    o.add_argument("--title", default="Copy and compute overlap")
+    o.add_argument("--command", required=True)
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "overlap": cmd_overlap}[a.cmd](a)
 
 
 if __name__ == "__main__":

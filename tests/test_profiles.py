@@ -1,6 +1,7 @@
 """Host-side checks of the profile-summary helpers that feed bench.py's roofline.traffic."""
 import json
 import os
+import sys
 
 from selective_recompute_cf_amd import profiles
 
@@ -36,3 +37,25 @@ def test_committed_traffic_summary_is_well_formed():
         assert key in t
     assert t["traffic_bytes_per_launch"] == t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
     assert len(profiles.sources_sha256()) == 64
+
+
+def test_copy_overlap_summary(tmp_path, monkeypatch):
+    """Hand-worked traces: kernels busy on [0, 100) and [150, 300) ns; copies on [50, 170)
+    (70 of 120 covered) and [320, 340) (none); one side kernel on [90, 160) (20 of 70 covered,
+    and not part of the busy union itself); nothing before the start kernel counts."""
+    kt = tmp_path / "k.csv"
+    cp = tmp_path / "c.csv"
+    kt.write_text("Kernel_Name,Start_Timestamp,End_Timestamp\n"
+                  "early,-50,-10\nembed_kernel,0,40\ngemm,30,100\ngemm,150,300\nreposition_kernel,90,160\n")
+    cp.write_text("Direction,Start_Timestamp,End_Timestamp\n"
+                  "MEMORY_COPY_HOST_TO_DEVICE,-40,-20\nMEMORY_COPY_HOST_TO_DEVICE,50,170\n"
+                  "MEMORY_COPY_DEVICE_TO_HOST,0,500\nMEMORY_COPY_HOST_TO_DEVICE,320,340\n")
+    out = tmp_path / "o.md"
+    monkeypatch.setattr(sys, "argv", ["profiles", "overlap", str(kt), str(cp), str(out), "--start", "embed_kernel",
+                                      "--side", "reposition", "--command", "x"])
+    profiles.main()
+    text = out.read_text()
+    assert "Host-to-device copies: 2, 0.00 ms in total" in text
+    assert "(50.0%)" in text  # (70 + 0) / (120 + 20)
+    assert "(28.6%)" in text  # (10 + 10) / 70
+    assert profiles._covered(profiles._union([(0, 100), (150, 300), (30, 60)]), 50, 170) == 70
