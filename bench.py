@@ -40,6 +40,8 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--profile-steps", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--full-compare", action="store_true",
+                    help="with --no-sweep: still time full prefill of the same request, for the step's speedup")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--store-cache", default=None,
                     help="load the chunk store from this file if it exists, else build it and save it there")
@@ -90,7 +92,8 @@ def main():
     kvd, Ly = cfg.kv_dim, cfg.n_layers
     log(f"[bench] workload {w.name}: N={N} U={U} k={k} layers={Ly}; generating and uploading weights")
     t0 = time.time()
-    dm = DeviceModel(synth.Model(cfg, cache_layers=False))
+    dm = DeviceModel(synth.Model(cfg, cache_layers=False),
+                     on_layer=lambda l: log(f"[bench]   layer {l + 1} of {Ly} on GPU") if (l + 1) % 10 == 0 else None)
     log(f"[bench] weights on GPU ({dm.weight_bytes() / 1e9:.1f} GB) in {time.time() - t0:.1f}s")
     ctx = cf.Context.from_model_cfg(cfg, max_pos=L + 1)
     chunks, _, toks = synth.request_tokens(w)
@@ -219,7 +222,7 @@ def main():
                 "kernel": "gemm_bf16_dtl (projection GEMMs, all block heights)",
                 "avg_launch_us": round(g_ms / g_launch * 1e3, 2),
                 "flops_per_launch": g_flops / g_launch, "launches_per_step": g_launch / P}
-    roofline.update(gemm_traffic(rl.gemm_bytes(work) / (g_launch / P)))
+    roofline.update(gemm_traffic(rl.gemm_bytes(work) / (g_launch / P), args.workload))
     log(f"[bench] gemm: {g_ach:.1f} TFLOP/s ({roofline['frac'] * 100:.1f}% of bf16 peak), "
         f"{roofline['avg_launch_us']} us/launch")
 
@@ -251,6 +254,14 @@ def main():
                                                timed)
         if args.workload == "llama8b":
             sweep_res["rolling_window"] = rolling_steps(dm)
+    elif args.full_compare:
+        # full prefill of the same request next to the timed step only (the whole sweep is long at 70B size)
+        _, pf = timed(full, 2, 1)
+        t_full, t_step = statistics.median(pf), statistics.median(per)
+        sweep_res = {"full_prefill_ms": round(t_full, 3),
+                     "ratios": {f"{w.rho_num * 100 // w.rho_den}%": {"k": k, "blend_ms": round(t_step, 3),
+                                                                     "speedup": round(t_full / t_step, 3)}}}
+        log(f"[bench] full prefill {t_full:.2f} ms; blended step {t_step:.2f} ms: {t_full / t_step:.2f}x")
 
     # ---------------------------------------------------------------- CPU oracle baseline (bounded sample)
     cpu = None
@@ -510,13 +521,17 @@ def kernel_sweeps():
     return {"sweeps": res}
 
 
-def gemm_traffic(alg_bytes_per_launch):
-    """HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE counter summary, if the
-    GEMM sources have not changed since the counters were taken (else traffic stays null)."""
+def gemm_traffic(alg_bytes_per_launch, workload="llama8b"):
+    """HBM bytes per GEMM launch from the committed FETCH_SIZE / WRITE_SIZE counter summary of the
+    Llama-3-8B-shaped workload, if that is the workload and the GEMM sources have not changed since
+    the counters were taken (else traffic stays null)."""
     from selective_recompute_cf_amd import profiles
     path = os.path.join(ROOT, "profiles", "gemm_bf16_dtl_llama3-8b_hbm_traffic.json")
     out = {"traffic_unit": "bytes per launch (HBM fetch + write, rocprofv3 counters)",
            "algorithmic_bytes_per_launch": round(alg_bytes_per_launch)}
+    if workload != "llama8b":
+        out["traffic_note"] = "counters were taken on the Llama-3-8B-shaped workload only"
+        return out
     try:
         with open(path) as f:
             t = json.load(f)

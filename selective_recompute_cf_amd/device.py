@@ -2,7 +2,7 @@
 cf_layer_weights array that libcf reads. No compute happens here."""
 from __future__ import annotations
 
-from typing import List, Optional
+from typing import Callable, List, Optional
 
 import numpy as np
 
@@ -28,9 +28,10 @@ class DeviceModel:
 
     ``host`` is any object with ``cfg`` (shape fields and ``dtype``), ``layer(l)`` returning
     per-layer arrays named as in cf_layer_weights ([out, in] matrices, fp32 gains), ``embed``
-    [vocab, d] and ``final_norm`` [d]."""
+    [vocab, d] and ``final_norm`` [d]. ``on_layer(l)`` is called after layer l is on the device."""
 
-    def __init__(self, host, device="cuda", n_layers: Optional[int] = None, with_embed: bool = True):
+    def __init__(self, host, device="cuda", n_layers: Optional[int] = None, with_embed: bool = True,
+                 on_layer: Optional[Callable[[int], None]] = None):
         import torch
         self.cfg = host.cfg
         self.dtype = host.cfg.dtype
@@ -44,6 +45,8 @@ class DeviceModel:
                 if g is not None:
                     t[n] = torch.from_numpy(np.ascontiguousarray(g, np.float32)).to(device)
             self.layers.append(t)
+            if on_layer is not None:
+                on_layer(l)
         self.embed = to_device(host.embed, self.dtype, device) if with_embed else None
         self.final_norm = torch.from_numpy(np.ascontiguousarray(host.final_norm, np.float32)).to(device)
         self.array = layer_array(self.layers)
