@@ -125,10 +125,12 @@ def main():
 
     sweep = [0, 5, 10, 15, 30, 50, 100]
     k_of = {r: cf.budget(N, r, 100) for r in sweep}
-    # gradual filtering (the set narrows layer by layer toward r): 20% or 30% on the selection layer
+    # gradual filtering (the set narrows layer by layer toward r): 20% or 30% on the selection layer,
+    # where that is above r
     gradual = {f"{a}%->{w.rho_num}% x{b}/10": cf.gradual_schedule(N, Ly - w.sel_layer, (a, 100), (b, 10),
                                                                   (w.rho_num, w.rho_den))
-               for a, b in [(20, 9), (30, 8)]} if w.mode == "token" and w.sel_layer < Ly else {}
+               for a, b in [(20, 9), (30, 8)] if a * w.rho_den > 100 * w.rho_num} \
+        if w.mode == "token" and w.sel_layer < Ly else {}
     ws_bytes = max([ctx.blend_prefill_workspace_size(N, U, kk, w.mode) for kk in list(k_of.values()) + [k]] +
                    [ctx.blend_prefill_workspace_size(N, U, N, "all")] +
                    [ctx.blend_prefill_gradual_workspace_size(N, U, w.sel_layer, g) for g in gradual.values()])
