@@ -125,12 +125,7 @@ def main():
 
     sweep = [0, 5, 10, 15, 30, 50, 100]
     k_of = {r: cf.budget(N, r, 100) for r in sweep}
-    # gradual filtering (the set narrows layer by layer toward r): 20% or 30% on the selection layer,
-    # where that is above r
-    gradual = {f"{a}%->{w.rho_num}% x{b}/10": cf.gradual_schedule(N, Ly - w.sel_layer, (a, 100), (b, 10),
-                                                                  (w.rho_num, w.rho_den))
-               for a, b in [(20, 9), (30, 8)] if a * w.rho_den > 100 * w.rho_num} \
-        if w.mode == "token" and w.sel_layer < Ly else {}
+    gradual = gradual_schedules(w)
     ws_bytes = max([ctx.blend_prefill_workspace_size(N, U, kk, w.mode) for kk in list(k_of.values()) + [k]] +
                    [ctx.blend_prefill_workspace_size(N, U, N, "all")] +
                    [ctx.blend_prefill_gradual_workspace_size(N, U, w.sel_layer, g) for g in gradual.values()])
@@ -521,6 +516,19 @@ def kernel_sweeps():
     res["topk_token"] = rows
     log(f"[sweeps] topk {[(r['n'], r['us']) for r in rows]}")
     return {"sweeps": res}
+
+
+def gradual_schedules(w):
+    """Gradual filtering schedules timed next to the step (the set narrows layer by layer toward the
+    workload's ratio r): 20% or 30% on the selection layer, kept 90% or 80% per layer, where that
+    start is above r; token selection only."""
+    import selective_recompute_cf_amd as cf
+    Ly = w.model.n_layers
+    if w.mode != "token" or w.sel_layer >= Ly:
+        return {}
+    return {f"{a}%->{w.rho_num}% x{b}/10": cf.gradual_schedule(w.n_ctx, Ly - w.sel_layer, (a, 100), (b, 10),
+                                                               (w.rho_num, w.rho_den))
+            for a, b in [(20, 9), (30, 8)] if a * w.rho_den > 100 * w.rho_num}
 
 
 def gemm_traffic(alg_bytes_per_launch, workload="llama8b"):
