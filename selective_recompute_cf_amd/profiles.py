@@ -9,6 +9,9 @@
   sources it records still matches.
 
     python -m selective_recompute_cf_amd.profiles stats <kernel_stats.csv> <out.md> --command "..."
+* ``counters``: per kernel group, the average of each counter per dispatch over ``--pmc`` passes,
+  with the matrix-core busy share, the waiting share, the LDS bank-conflict share and vector-ALU
+  instructions per MFMA instruction.
 * ``overlap``: from a ``--kernel-trace --memory-copy-trace`` run, how much of the host-to-device
   copy time (and of the kernels matching a side pattern, e.g. the copy stream's re-position)
   falls inside the execution intervals of the other kernels, counted from the first dispatch of
@@ -251,6 +254,62 @@ def cmd_overlap(a):
         f.write("\n".join(lines) + "\n")
 
 
+CLOCK_GHZ = 2.4  # MI355X peak engine clock
+SIMDS = 256 * 4  # compute units x SIMDs per unit
+
+
+def cmd_counters(a):
+    """Per kernel group: each counter's average per dispatch over one or more --pmc passes, and the
+    derived shares: matrix-core busy = SQ_VALU_MFMA_BUSY_CYCLES / (dispatch time x clock x SIMDs);
+    waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; LDS bank conflicts = SQ_LDS_BANK_CONFLICT /
+    SQ_LDS_IDX_ACTIVE; vector-ALU instructions per MFMA instruction."""
+    groups = [(g.split("=", 1)[0], re.compile(g.split("=", 1)[1])) for g in a.group]
+    val = {g: {} for g, _ in groups}   # counter -> [sum, dispatches]
+    dur = {g: {} for g, _ in groups}   # counter -> summed dispatch ns (for the MFMA share)
+    for path in a.csv:
+        for r in csv.DictReader(open(path)):
+            for g, rx in groups:
+                if rx.search(r["Kernel_Name"]):
+                    c = r["Counter_Name"]
+                    v = val[g].setdefault(c, [0.0, 0])
+                    v[0] += float(r["Counter_Value"])
+                    v[1] += 1
+                    dur[g][c] = dur[g].get(c, 0) + int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                    break
+    lines = [f"# {a.title}", "", "Commands:", "", "```", a.command, "```", "",
+             f"Derived shares: matrix cores busy = SQ_VALU_MFMA_BUSY_CYCLES / (dispatch time x {CLOCK_GHZ} GHz x "
+             f"{SIMDS} SIMDs); waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; LDS bank conflicts = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; VALU per MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA.", "",
+             "| group | dispatches | matrix cores busy | waiting | LDS bank conflicts | VALU per MFMA |",
+             "|---|---:|---:|---:|---:|---:|"]
+
+    def avg(g, c):
+        v = val[g].get(c)
+        return v[0] / v[1] if v and v[1] else None
+
+    def pct(x):
+        return "n/a" if x is None else f"{100 * x:.1f}%"
+
+    for g, _ in groups:
+        if not val[g]:
+            continue
+        n = max(v[1] for v in val[g].values())
+        mf = val[g].get("SQ_VALU_MFMA_BUSY_CYCLES")
+        busy = mf[0] / (dur[g]["SQ_VALU_MFMA_BUSY_CYCLES"] * CLOCK_GHZ * SIMDS) if mf else None
+        wc, wi = avg(g, "SQ_WAVE_CYCLES"), avg(g, "SQ_WAIT_INST_ANY")
+        li, lb = avg(g, "SQ_LDS_IDX_ACTIVE"), avg(g, "SQ_LDS_BANK_CONFLICT")
+        iv, im = avg(g, "SQ_INSTS_VALU"), avg(g, "SQ_INSTS_MFMA")
+        lines.append(f"| {g} | {n} | {pct(busy)} | {pct(wi / wc if wi is not None and wc else None)} | "
+                     f"{pct(lb / li if lb is not None and li else None)} | "
+                     f"{'n/a' if not (iv and im) else f'{iv / im:.2f}'} |")
+    lines += ["", "Average per dispatch:", "", "| group | counter | value |", "|---|---|---:|"]
+    for g, _ in groups:
+        for c in sorted(val[g]):
+            lines.append(f"| {g} | {c} | {avg(g, c):.0f} |")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -278,8 +337,14 @@ def main():
     o.add_argument("--side", required=True, help="kernels on the copy stream, reported like the copies")
     o.add_argument("--title", default="Copy and compute overlap")
     o.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+", help="counter_collection.csv files of one or more --pmc passes")
+    c.add_argument("--out", required=True)
+    c.add_argument("--group", action="append", required=True, help="NAME=REGEX over kernel names")
+    c.add_argument("--title", default="Counters per kernel group")
+    c.add_argument("--command", required=True)
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "overlap": cmd_overlap}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "overlap": cmd_overlap, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -59,3 +59,22 @@ def test_copy_overlap_summary(tmp_path, monkeypatch):
     assert "(50.0%)" in text  # (70 + 0) / (120 + 20)
     assert "(28.6%)" in text  # (10 + 10) / 70
     assert profiles._covered(profiles._union([(0, 100), (150, 300), (30, 60)]), 50, 170) == 70
+
+
+def test_counter_shares(tmp_path, monkeypatch):
+    """Derived shares on hand-made passes: one 10 us dispatch with 12 288 000 MFMA-busy SIMD cycles
+    (= half of 10 us x 2.4 GHz x 1024 SIMDs), 300 of 1000 wave cycles waiting, 25 of 100 LDS cycles
+    in bank conflicts, 8 VALU instructions per 2 MFMA."""
+    head = "Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+    p1 = tmp_path / "p1.csv"
+    p2 = tmp_path / "p2.csv"
+    p1.write_text(head + "".join(f"attn_dtl_kernel,{c},{v},0,10000\n" for c, v in
+                                 [("SQ_VALU_MFMA_BUSY_CYCLES", 12288000), ("SQ_WAVE_CYCLES", 1000),
+                                  ("SQ_WAIT_INST_ANY", 300), ("SQ_INSTS_MFMA", 2)]) + "other,SQ_WAVE_CYCLES,5,0,1\n")
+    p2.write_text(head + "".join(f"attn_dtl_kernel,{c},{v},0,10000\n" for c, v in
+                                 [("SQ_LDS_IDX_ACTIVE", 100), ("SQ_LDS_BANK_CONFLICT", 25), ("SQ_INSTS_VALU", 8)]))
+    out = tmp_path / "c.md"
+    monkeypatch.setattr(sys, "argv", ["profiles", "counters", str(p1), str(p2), "--out", str(out), "--group",
+                                      "attention=attn_dtl", "--command", "x"])
+    profiles.main()
+    assert "| attention | 1 | 50.0% | 30.0% | 25.0% | 4.00 |" in out.read_text()
