@@ -182,8 +182,11 @@ def cmd_traffic(a):
                        for n, d in by_name.items()},
     }
     res["traffic_bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
-    with open(a.out_json, "w") as f:
-        json.dump(res, f, indent=1)
+    if a.out_json:
+        with open(a.out_json, "w") as f:
+            json.dump(res, f, indent=1)
+    # average durations from a kernel-trace run without counters, for the bytes' rate
+    avg_us = {r["name"]: r["avg_us"] for r in kernel_stats(a.durations)} if a.durations else {}
     lines = [f"# {a.title}", "", "Commands:", "", "```", a.command, "```", "",
              f"Copy calibration: a {a.copy_bytes / 2**30:.2f} GiB device copy reads FETCH_SIZE "
              f"{a.copy_bytes / ff / 1024:.0f} KiB and WRITE_SIZE {a.copy_bytes / wf / 1024:.0f} KiB per dispatch, "
@@ -191,11 +194,26 @@ def cmd_traffic(a):
              f"Dispatches matching `{a.pattern}`: {len(allf)}; per launch on average "
              f"{res['fetch_bytes_per_launch'] / 1e6:.2f} MB fetched + {res['write_bytes_per_launch'] / 1e6:.2f} MB "
              f"written = {res['traffic_bytes_per_launch'] / 1e6:.2f} MB.", "",
-             "| kernel | dispatches | fetch MB / launch | write MB / launch |", "|---|---:|---:|---:|"]
+             "| kernel | dispatches | fetch MB / launch | write MB / launch |"
+             + (" avg us | GB/s | of 8 TB/s |" if avg_us else ""),
+             "|---|---:|---:|---:|" + ("---:|---:|---:|" if avg_us else "")]
     for n, d in res["per_kernel"].items():
-        lines.append(f"| `{n}` | {d['dispatches']} | {d['fetch_bytes_per_launch'] / 1e6:.2f} | "
-                     f"{d['write_bytes_per_launch'] / 1e6:.2f} |")
-    lines += ["", f"Kernel sources hash (sha256 of {', '.join(GEMM_SOURCES)}): `{res['source_sha256']}`"]
+        row = (f"| `{n}` | {d['dispatches']} | {d['fetch_bytes_per_launch'] / 1e6:.2f} | "
+               f"{d['write_bytes_per_launch'] / 1e6:.2f} |")
+        if avg_us:
+            us = avg_us.get(n)
+            if us:
+                gbs = (d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"]) / (us * 1e3)
+                row += f" {us:.2f} | {gbs:.0f} | {100 * gbs / 8000:.0f}% |"
+            else:
+                row += " n/a | n/a | n/a |"
+        lines.append(row)
+    if avg_us:
+        lines += ["", "Rates divide the counted bytes by the average duration of the same kernel in the kernel-trace "
+                      "run (no counters): bytes served by the MALL count as traffic, so a rate can exceed what HBM "
+                      "alone delivers."]
+    if a.out_json:
+        lines += ["", f"Kernel sources hash (sha256 of {', '.join(GEMM_SOURCES)}): `{res['source_sha256']}`"]
     with open(a.out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -326,7 +344,8 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--pattern", required=True)
     t.add_argument("--out-md", required=True)
-    t.add_argument("--out-json", required=True)
+    t.add_argument("--out-json", default=None, help="also write the JSON that bench.py reads (GEMM traffic)")
+    t.add_argument("--durations", default=None, help="kernel_stats.csv of a run without counters: adds GB/s")
     t.add_argument("--title", default="HBM traffic per dispatch")
     t.add_argument("--command", required=True)
     o = sub.add_parser("overlap")
