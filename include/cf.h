@@ -163,6 +163,24 @@ cf_status cf_kv_deviation(const void* k_new, int32_t new_dtype, int64_t ld_new, 
                           int32_t ref_dtype, int64_t ld_ref, float* dev, int32_t n_tok,
                           int32_t kv_dim, hipStream_t stream);
 
+/* --------------------------------------------------------------------- cf_selection_deviation
+ * The selection-layer step of the method as one call (Request Order Matters §2.2 Eq. 1 at the
+ * configured selection layer; CacheBlend, "Quantifying the Damage"): for the N context rows of
+ * hidden (fp32, row stride d_model, rows 0..N-1 at positions 0..N-1) the current keys are
+ *   K_i = RoPE_i(knorm(RMSNorm(h_i; w->attn_norm) Wk^T))      (knorm only for qk_norm models)
+ * and dev[i] = sum over the kvd entries of (K_i - k_ref[i])^2, accumulated in fp32; k_ref is this
+ * layer's stitched cache ([>= N][kvd], model dtype, the output of cf_rope_reposition). K_i is
+ * compared in fp32 and stored nowhere. The RMSNorm rows are rounded to the model dtype before the
+ * projection, as in every layer. cf_blend_prefill runs exactly these launches (same plan, same
+ * results bit for bit) at its selection layer.
+ *  w: host struct of device pointers (wk, attn_norm and, for qk_norm, k_norm are read).
+ *  dev: device fp32 [N]. ws: device workspace of cf_selection_deviation_workspace_size(ctx, N)
+ *  bytes. N = 0 enqueues nothing. */
+size_t cf_selection_deviation_workspace_size(const cf_ctx* ctx, int32_t N);
+cf_status cf_selection_deviation(const cf_ctx* ctx, const cf_layer_weights* w /* host struct */,
+                                 const float* hidden, int32_t N, const void* k_ref, float* dev, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 /* --------------------------------------------------------------------- cf_topk_select
  * Choose k of the n positions by their deviation dev (fp32 [n]) and write them ascending to
  * out_idx (int32 [k]).
@@ -329,6 +347,56 @@ cf_status cf_blend_prefill_gradual(const cf_ctx* ctx, const cf_layer_weights* la
                                    int32_t sel_layer, const int32_t* k_sched /* host */, void* k_out,
                                    void* v_out, int64_t out_layer_stride, float* out_hidden, int32_t* out_sets,
                                    float* out_devs, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------- policy arithmetic (host)
+ * The integer and scalar bookkeeping of the method. These functions read and write host memory
+ * only, take no context or stream, never touch the device, and return CF_EINVAL (with
+ * cf_last_error text) on a bad argument, leaving outputs untouched unless stated otherwise.
+ * Ratios are exact rationals num/den with 0 <= num <= den and den > 0. */
+
+/* Recompute budget (Request Order Matters §2.2 Eq. 2; ratio as in QCFuse §2.1.3 Eq. 6):
+ * *k = max(1, floor(n_ctx * num / den)) when num > 0 and n_ctx > 0, else 0 (the direct-reuse
+ * endpoint). Integer arithmetic: floating point puts 0.15 * 3072 and 0.29 * 100 just below the
+ * integer. n_ctx >= 0 counts context tokens only (the query is never ranked). */
+cf_status cf_budget(int32_t n_ctx, int32_t rho_num, int32_t rho_den, int32_t* k);
+
+/* Gradual-filtering schedule (CacheBlend, "The Chicken-and-Egg Problem": the recompute ratio
+ * narrows r_1 > r_2 > ... toward r, each layer keeping part of the previous layer's set):
+ * k_sched[0] = budget(n_ctx, first), then k_sched[i+1] = max(budget(n_ctx, final),
+ * max(1, floor(k_sched[i] * keep))) while k_sched[i] > 0 (0 stays 0). Writes n_sched counts to
+ * k_sched (host int32 [n_sched]), the layout cf_blend_prefill_gradual reads. The final ratio
+ * must not exceed the first. */
+cf_status cf_gradual_schedule(int32_t n_ctx, int32_t n_sched, int32_t first_num, int32_t first_den,
+                              int32_t keep_num, int32_t keep_den, int32_t final_num, int32_t final_den,
+                              int32_t* k_sched);
+
+/* Loading controller (CacheBlend, "Hiding Recompute Behind I/O"): among the n candidate ratios
+ * ratios[i] = {num, den} (host int32 [n][2]) whose measured per-layer recompute time
+ * recompute_ms[i] (host double [n]) is at most the per-layer cache load time load_ms, take the
+ * largest (the first among equal ratios), then clamp it from below at the floor r* = floor_num /
+ * floor_den: r = max(r_load, r*). With no candidate fitting, r = r*. */
+cf_status cf_loading_ratio(double load_ms, const int32_t* ratios, const double* recompute_ms, int32_t n,
+                           int32_t floor_num, int32_t floor_den, int32_t* out_num, int32_t* out_den);
+
+/* Span bounds of the span-policy ablations (Request Order Matters §2.3 and §4.4), for
+ * cf_topk_select / cf_blend_prefill in CF_SEL_DOC_SPANS mode. bounds: host int32 [cap]; *n_bounds
+ * receives the number of bounds (spans + 1) even when cap is too small (then CF_EINVAL).
+ *  single-window: the one span {0, n_ctx}, so the document-aligned rule takes the k-token window
+ *    of largest total deviation anywhere in the context.
+ *  fixed-chunk: spans of `size` tokens that cross document bounds, shifted by `offset`
+ *    (0 <= offset < size; the page's offset is unstated): 0, offset, offset + size, ..., n_ctx
+ *    (offset 0 gives 0, size, 2 size, ...). n_ctx = 0 gives {0, 0}. */
+cf_status cf_single_window_bounds(int32_t n_ctx, int32_t* bounds, int32_t cap, int32_t* n_bounds);
+cf_status cf_fixed_chunk_bounds(int32_t n_ctx, int32_t size, int32_t offset, int32_t* bounds, int32_t cap,
+                                int32_t* n_bounds);
+
+/* Selection diagnostics of Request Order Matters §4.4 Table 2 for k distinct positions sel (host
+ * int32 [k], any order, each in [0, n)) and the selection-layer deviation dev (host fp32 [n]):
+ * *segments = the number of maximal runs of consecutive selected positions; *captured = the share
+ * of the total deviation that the selected positions carry, both totals summed in fp64 with NaN
+ * counted as +inf (0 when the total is 0). */
+cf_status cf_selection_stats(const int32_t* sel, int32_t k, const float* dev, int32_t n, int32_t* segments,
+                             double* captured);
 
 #ifdef __cplusplus
 }

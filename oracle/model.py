@@ -153,6 +153,18 @@ def k_rows(cfg, w, h_rows, pos, ft=np.float32, bf16_ops=None):
     return rope(k, pos, cfg.rope_theta, ft)
 
 
+def kv_rows(cfg, w, h_rows, pos, ft=np.float32):
+    """Fresh K and V of the given rows as a layer writes them into its cache (before any storage
+    rounding): K = RoPE_pos(knorm(RMSNorm(h) @ Wk^T)), V = RMSNorm(h) @ Wv^T; [n, Hkv, hd] each."""
+    n = h_rows.shape[0]
+    a = rms_norm(h_rows, w.attn_norm, cfg.rms_eps, ft)
+    k = (a @ np.asarray(w.wk, ft).T).reshape(n, cfg.n_kv_heads, cfg.head_dim)
+    v = (a @ np.asarray(w.wv, ft).T).reshape(n, cfg.n_kv_heads, cfg.head_dim)
+    if cfg.qk_norm:
+        k = rms_norm(k, w.k_norm, cfg.rms_eps, ft)
+    return rope(k, pos, cfg.rope_theta, ft), v
+
+
 def full_prefill(model, tokens, ft=np.float32, n_layers=None, bf16_ops=None):
     """QCFuse §2.1.1 Eq. 2: every layer on every token at positions 0..n-1, causal.
 

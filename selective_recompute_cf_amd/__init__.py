@@ -24,7 +24,9 @@ EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
            "cf_blend_prefill", "cf_blend_prefill_gradual_workspace_size", "cf_blend_prefill_gradual",
            "cf_blend_prefill_streamed_workspace_size", "cf_blend_prefill_streamed", "cf_query_scores_workspace_size",
-           "cf_query_scores",
+           "cf_query_scores", "cf_selection_deviation_workspace_size", "cf_selection_deviation",
+           "cf_budget", "cf_gradual_schedule", "cf_loading_ratio", "cf_single_window_bounds",
+           "cf_fixed_chunk_bounds", "cf_selection_stats",
            "cf_profile_enable", "cf_profile_report", "cf_mfma_loop", "cf_copy_loop"]
 
 
@@ -84,6 +86,15 @@ def lib() -> ctypes.CDLL:
                                             vp, i32, i32, i32, i32, vp, i32, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
         "cf_blend_prefill_gradual": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, i32, i32, vp, vp, i64, i32,
                                            vp, i32, i32, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "cf_selection_deviation_workspace_size": (sz, [vp, i32]),
+        "cf_selection_deviation": (i32, [vp, ctypes.POINTER(LayerWeights), vp, i32, vp, vp, vp, sz, vp]),
+        "cf_budget": (i32, [i32, i32, i32, ctypes.POINTER(i32)]),
+        "cf_gradual_schedule": (i32, [i32, i32, i32, i32, i32, i32, i32, i32, vp]),
+        "cf_loading_ratio": (i32, [ctypes.c_double, vp, vp, i32, i32, i32, ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32)]),
+        "cf_single_window_bounds": (i32, [i32, vp, i32, ctypes.POINTER(i32)]),
+        "cf_fixed_chunk_bounds": (i32, [i32, i32, i32, vp, i32, ctypes.POINTER(i32)]),
+        "cf_selection_stats": (i32, [vp, i32, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -274,6 +285,20 @@ class Context:
                                     _ptr(sel), n_sel, hidden.shape[0], _ptr(ws), 0 if ws is None else ws.numel(),
                                     _stream(hidden.device)))
 
+    def selection_deviation_workspace_size(self, N: int) -> int:
+        return int(lib().cf_selection_deviation_workspace_size(self.handle, N))
+
+    def selection_deviation(self, weights: LayerWeights, hidden, N: int, k_ref, dev, ws):
+        """cf_selection_deviation: dev[i] (fp32 [N]) = squared distance between the current keys of
+        hidden rows 0..N-1 (fp32 [>= N, d]) and the stitched keys k_ref ([>= N, kvd])."""
+        torch = _torch()
+        _room(hidden, N * self.cfg.d_model, "hidden", torch.float32)
+        _room(k_ref, N * self.kv_dim, "k_ref", self._tdt())
+        _room(dev, N, "dev", torch.float32)
+        _check(lib().cf_selection_deviation(self.handle, ctypes.byref(weights), _ptr(hidden), N, _ptr(k_ref),
+                                            _ptr(dev), _ptr(ws), 0 if ws is None else ws.numel(),
+                                            _stream(hidden.device)))
+
     def blend_prefill_workspace_size(self, N: int, U: int, k: int, mode: str) -> int:
         return int(lib().cf_blend_prefill_workspace_size(self.handle, N, U, k, MODES[mode]))
 
@@ -404,77 +429,67 @@ def topk_select(dev, k: int, out_idx, mode: str = "token", span_bounds=None, ws=
 
 
 def budget(n_ctx: int, rho_num: int, rho_den: int) -> int:
-    """k = max(1, floor(rho * N)) for rho > 0, 0 for rho = 0, in integer arithmetic
-    (Request Order Matters §2.2 Eq. 2)."""
-    if rho_num < 0 or rho_den <= 0 or rho_num > rho_den:
-        raise ValueError("ratio must be in [0, 1]")
-    if rho_num == 0 or n_ctx == 0:
-        return 0
-    return max(1, (n_ctx * rho_num) // rho_den)
+    """cf_budget: k = max(1, floor(rho * N)) for rho > 0, 0 for rho = 0 (integer arithmetic)."""
+    k = ctypes.c_int32(0)
+    _check(lib().cf_budget(int(n_ctx), int(rho_num), int(rho_den), ctypes.byref(k)))
+    return int(k.value)
 
 
 def gradual_schedule(n_ctx: int, n_sched: int, first=(20, 100), keep=(9, 10), final=(15, 100)) -> List[int]:
-    """Per-layer recompute counts for cf_blend_prefill_gradual (CacheBlend, "The Chicken-and-Egg
-    Problem": the set narrows from r_1 toward r). The first count is budget(N, r_1); each next
-    one keeps max(1, floor(previous * keep)) rows but never fewer than budget(N, r). Ratios are
+    """cf_gradual_schedule: per-layer recompute counts for cf_blend_prefill_gradual. Ratios are
     (numerator, denominator) integer pairs."""
-    top = budget(n_ctx, *first)
-    low = budget(n_ctx, *final)
-    if low > top:
-        raise ValueError("the final ratio must not exceed the first")
-    num, den = keep
-    if num < 0 or den <= 0 or num > den:
-        raise ValueError("keep must be in [0, 1]")
-    counts, cur = [], top
-    while len(counts) < n_sched:
-        counts.append(cur)
-        cur = 0 if cur == 0 else max(low, (cur * num) // den, 1)
-    return counts
+    out = (ctypes.c_int32 * max(1, int(n_sched)))()
+    _check(lib().cf_gradual_schedule(int(n_ctx), int(n_sched), int(first[0]), int(first[1]), int(keep[0]),
+                                     int(keep[1]), int(final[0]), int(final[1]), out))
+    return [int(out[i]) for i in range(int(n_sched))]
 
 
 def loading_controller(load_ms: float, recompute_ms: dict, floor=(15, 100)):
-    """CacheBlend's loading controller ("Hiding Recompute Behind I/O"): the recompute ratio whose
-    per-layer recompute time still fits inside the per-layer cache load time, clamped from below
-    at ``floor`` (r = max(r_load, r*)). recompute_ms: {(num, den): measured per-layer ms}.
-    Returns (num, den)."""
-    best = None
-    for ratio, ms in recompute_ms.items():
-        if ms <= load_ms and (best is None or ratio[0] * best[1] > best[0] * ratio[1]):
-            best = ratio
-    if best is None or best[0] * floor[1] < floor[0] * best[1]:
-        return tuple(floor)
-    return tuple(best)
+    """cf_loading_ratio: the largest candidate ratio whose per-layer recompute time fits inside the
+    per-layer load time, clamped from below at ``floor``. recompute_ms: {(num, den): ms}. Returns
+    (num, den)."""
+    items = list(recompute_ms.items())
+    n = len(items)
+    rat, ms = _host_i32([[int(a), int(b)] for (a, b), _ in items])
+    tms = (ctypes.c_double * max(1, n))(*[float(t) for _, t in items])
+    a, b = ctypes.c_int32(0), ctypes.c_int32(1)
+    _check(lib().cf_loading_ratio(float(load_ms), rat, tms, n, int(floor[0]), int(floor[1]), ctypes.byref(a),
+                                  ctypes.byref(b)))
+    return int(a.value), int(b.value)
+
+
+def _bounds_call(fn, *args) -> List[int]:
+    nb = ctypes.c_int32(0)
+    cap = 64
+    while True:
+        out = (ctypes.c_int32 * cap)()
+        st = fn(*args, out, cap, ctypes.byref(nb))
+        if st == CF_OK:
+            return [int(out[i]) for i in range(nb.value)]
+        if nb.value <= cap:
+            _check(st)
+        cap = int(nb.value)
 
 
 def single_window_bounds(n_ctx: int) -> List[int]:
-    """Span bounds for the single-window policy (Request Order Matters §2.3): one span over the
-    context, so that document-aligned selection takes the best k-token window."""
-    return [0, int(n_ctx)]
+    """cf_single_window_bounds: the one span [0, n_ctx)."""
+    return _bounds_call(lib().cf_single_window_bounds, int(n_ctx))
 
 
 def fixed_chunk_bounds(n_ctx: int, size: int = 92, offset: int = 46) -> List[int]:
-    """Span bounds for the fixed-chunk policy (Request Order Matters §2.3, §4.4): spans of `size`
-    tokens shifted by `offset` so that they cross document boundaries: 0, offset, offset + size,
-    ..., n_ctx (offset 0 starts the first full span at 0)."""
-    if size <= 0 or not 0 <= offset < size:
-        raise ValueError("need size > 0 and 0 <= offset < size")
-    out = [0]
-    nxt = offset or size
-    while nxt < n_ctx:
-        out.append(nxt)
-        nxt += size
-    out.append(int(n_ctx))
-    return out if n_ctx > 0 else [0, 0]
+    """cf_fixed_chunk_bounds: spans of `size` tokens shifted by `offset`: 0, offset, offset + size, ...,
+    n_ctx."""
+    return _bounds_call(lib().cf_fixed_chunk_bounds, int(n_ctx), int(size), int(offset))
 
 
 def selection_stats(sel: Sequence[int], dev) -> tuple:
-    """(segments, captured deviation) of a selection (Request Order Matters Table 2): the number of
-    maximal runs of consecutive positions, and the share of the total deviation (fp64) that the
-    selected positions carry. dev: host array-like of the selection-layer deviation."""
+    """cf_selection_stats: (segments, captured deviation) of a selection. dev: host array-like of the
+    selection-layer deviation."""
     import numpy as np
-    idx = np.unique(np.asarray(sel, dtype=np.int64))
-    runs = int(idx.size and 1 + np.count_nonzero(np.diff(idx) != 1))
-    d = np.asarray(dev, dtype=np.float64).copy()
-    d[np.isnan(d)] = np.inf
-    total = float(d.sum())
-    return runs, (float(d[idx].sum()) / total if total > 0 else 0.0)
+    s = np.ascontiguousarray(np.asarray(sel, dtype=np.int32).ravel())
+    d = np.ascontiguousarray(np.asarray(dev, dtype=np.float32).ravel())
+    seg, cap = ctypes.c_int32(0), ctypes.c_double(0.0)
+    _check(lib().cf_selection_stats(s.ctypes.data if s.size else None, int(s.size),
+                                    d.ctypes.data if d.size else None, int(d.size), ctypes.byref(seg),
+                                    ctypes.byref(cap)))
+    return int(seg.value), float(cap.value)

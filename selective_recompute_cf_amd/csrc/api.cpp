@@ -14,6 +14,7 @@
 
 #include "cf.h"
 #include "kernels.h"
+#include "status.h"
 
 struct cf_ctx {
   cf_model_cfg cfg;
@@ -44,6 +45,18 @@ cf_status fail(cf_status s, const char* fmt, ...) {
   g_err = buf;
   return s;
 }
+
+}  // namespace
+
+namespace cf {
+void clear_error() { g_err.clear(); }
+cf_status set_error(cf_status s, const char* msg) {
+  g_err = msg;
+  return s;
+}
+}  // namespace cf
+
+namespace {
 
 #define CF_CHECK(cond, status, ...) \
   do {                              \
@@ -339,6 +352,35 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
     dn.epi = cf::EPI_RESID; dn.resid = HS; dn.resid_rows = nullptr; dn.out = hidden; dn.out_rows = sel;
     CF_RUN("gemm/down", cf::launch_gemm(dn, st));
   }
+  return CF_OK;
+}
+
+// Current keys of the N context rows at the selection layer and their deviation from the
+// stitched keys (Request Order Matters §2.2 Eq. 1): X = RMSNorm(h[0..N)) in the model dtype,
+// K = X Wk^T (fp32, `plan` picks the block shape and split-K factor), then qk-norm and RoPE at
+// position i, and dev[i] = sum over the kvd entries of (K_i - k_ref[i])^2 in fp32. k_ref is the
+// layer's stitched cache [>= N][kvd]; X holds N x d_model elements, KN splits x N x kvd floats.
+cf_status enqueue_sel_deviation(const cf_ctx* c, const cf_layer_weights* w, const float* hidden, int N, int L,
+                                const void* k_ref, float* dev, void* X, float* KN, const cf::GemmPlan& plan,
+                                hipStream_t st) {
+  const cf_model_cfg& mc = c->cfg;
+  const cf::Dt dt = dt_of(c);
+  const int kvd = mc.n_kv_heads * mc.head_dim;
+  CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, nullptr, N, L, mc.d_model, w->attn_norm, mc.rms_eps, X,
+                                                 mc.d_model, st));
+  cf::GemmArgs g{};
+  g.dt = dt; g.cfg = plan.cfg; g.splits = plan.splits;
+  g.A = X; g.lda = mc.d_model; g.B[0] = g.B[1] = g.B[2] = w->wk; g.nb0 = g.nb1 = kvd;
+  g.M = N; g.N = kvd; g.K = mc.d_model; g.epi = g.splits > 1 ? cf::EPI_PARTIAL : cf::EPI_F32;
+  g.C = KN; g.ldc = kvd;
+  CF_RUN("gemm/k_sel", cf::launch_gemm(g, st));
+  cf::QkvPost qp{};
+  qp.qkv = KN; qp.ld = kvd; qp.rows = nullptr; qp.n = N; qp.L = L;
+  qp.splits = g.splits; qp.split_stride = (int64_t)N * kvd;
+  qp.hq = mc.n_q_heads; qp.hkv = mc.n_kv_heads; qp.hd = mc.head_dim; qp.qk_norm = mc.qk_norm;
+  qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = mc.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
+  qp.dev = dev; qp.k_ref = k_ref;
+  CF_RUN("qkv_post", cf::launch_qkv_post(dt, qp, st));
   return CF_OK;
 }
 
@@ -658,6 +700,36 @@ cf_status cf_blend_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidd
   return run_layer(c, w, hidden, kc, vc, sel, n_sel, L, static_cast<char*>(ws), lw, st);
 }
 
+size_t cf_selection_deviation_workspace_size(const cf_ctx* c, int32_t N) {
+  if (!c || N <= 0) return 0;
+  const cf_model_cfg& m = c->cfg;
+  const int kvd = m.n_kv_heads * m.head_dim;
+  const cf::GemmPlan p = cf::gemm_plan(dt_of(c), N, kvd, m.d_model, false, true, c->n_cu);
+  return al((size_t)N * m.d_model * esize(c)) + al((size_t)p.splits * N * kvd * 4);
+}
+
+cf_status cf_selection_deviation(const cf_ctx* c, const cf_layer_weights* w, const float* hidden, int32_t N,
+                                 const void* k_ref, float* dev, void* ws, size_t ws_bytes, hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  CF_CHECK(N >= 0 && N <= c->max_pos, CF_EINVAL, "N=%d outside [0, max_pos=%d]", N, c->max_pos);
+  if (cf_status s = check_layer(c, w, 0)) return s;
+  if (N == 0) return CF_OK;
+  CF_CHECK(hidden && k_ref && dev, CF_EINVAL, "null pointer");
+  CF_CHECK(aligned16(hidden) && aligned16(k_ref), CF_EINVAL, "hidden and k_ref must be 16-byte aligned");
+  const size_t need = cf_selection_deviation_workspace_size(c, N);
+  CF_CHECK(ws && aligned16(ws) && ws_bytes >= need, CF_EWORKSPACE, "workspace: need %zu bytes, got %zu", need,
+           ws_bytes);
+  DeviceGuard guard(c->device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  const cf_model_cfg& m = c->cfg;
+  const int kvd = m.n_kv_heads * m.head_dim;
+  const cf::GemmPlan p = cf::gemm_plan(dt_of(c), N, kvd, m.d_model, false, true, c->n_cu);
+  char* W = static_cast<char*>(ws);
+  return enqueue_sel_deviation(c, w, hidden, N, N, k_ref, dev, W, reinterpret_cast<float*>(
+                               W + al((size_t)N * m.d_model * esize(c))), p, st);
+}
+
 size_t cf_blend_prefill_workspace_size(const cf_ctx* c, int32_t N, int32_t U, int32_t k, int32_t mode) {
   if (!c || N < 0 || U < 0 || N + U <= 0) return 0;
   if (mode == CF_SEL_ALL) k = N;
@@ -824,23 +896,10 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
       if (k > 0) CF_RUN("copy", cf::launch_copy_i32(sel, out_sel, k, st));
     } else if (N > 0) {
       // current keys of the context rows at the selection layer and their deviation
-      void* X = lws + lw_full.x;  // the full-row layout holds N rows of X and of K
-      float* KN = reinterpret_cast<float*>(lws + lw_full.qkv);
-      CF_RUN("rmsnorm_rows", cf::launch_rmsnorm_rows(dt, hidden, nullptr, N, L, mc.d_model, w->attn_norm, mc.rms_eps, X,
-                                                     mc.d_model, st));
-      cf::GemmArgs g{};
-      g.dt = dt; g.cfg = lw_full.plan.ksel.cfg; g.splits = lw_full.plan.ksel.splits;
-      g.A = X; g.lda = mc.d_model; g.B[0] = g.B[1] = g.B[2] = w->wk; g.nb0 = g.nb1 = (int)kvd;
-      g.M = N; g.N = (int)kvd; g.K = mc.d_model; g.epi = g.splits > 1 ? cf::EPI_PARTIAL : cf::EPI_F32;
-      g.C = KN; g.ldc = kvd;
-      CF_RUN("gemm/k_sel", cf::launch_gemm(g, st));
-      cf::QkvPost qp{};
-      qp.qkv = KN; qp.ld = kvd; qp.rows = nullptr; qp.n = N; qp.L = L;
-      qp.splits = g.splits; qp.split_stride = (int64_t)N * kvd;
-      qp.hq = mc.n_q_heads; qp.hkv = mc.n_kv_heads; qp.hd = mc.head_dim; qp.qk_norm = mc.qk_norm;
-      qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = mc.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
-      qp.dev = dev; qp.k_ref = K_l(s_layer);
-      CF_RUN("qkv_post", cf::launch_qkv_post(dt, qp, st));
+      // (the full-row layout holds N rows of X and of K)
+      if (cf_status s = enqueue_sel_deviation(c, w, hidden, N, L, K_l(s_layer), dev, lws + lw_full.x,
+                                              reinterpret_cast<float*>(lws + lw_full.qkv), lw_full.plan.ksel, st))
+        return s;
       if (cf_status s = enqueue_select(dev, N, k, mode, bounds, ns, sel, reinterpret_cast<double*>(W + pw.topk), st))
         return s;
       if (out_dev) CF_RUN("copy", cf::launch_copy_f32(out_dev, dev, N, st));

@@ -1,0 +1,208 @@
+"""Teacher-forced, per-layer parity of the HIP path against the oracle.
+
+The request runs on the GPU one call at a time, in the launch configuration of cf_blend_prefill:
+re-position + stitch of every layer (cf_rope_reposition), the layers before the selection layer on
+every row, the selection-layer deviation (cf_selection_deviation) and selection (cf_topk_select),
+then cf_blend_layer on the selected rows and the query rows at every later layer. Before each
+checked layer the GPU's own inputs (the fp32 residual rows and the layer's K/V cache) are copied
+to the host, and the oracle runs that one layer on exactly those inputs in fp32
+(QCFuse §2.1.3 Eq. 7; CacheBlend, "Selective Recompute Without Skipping"). The GPU's outputs must
+then meet the element-wise bf16 bar |gpu - oracle| <= 2e-2 + 1e-2 |oracle| at every element of:
+* the fresh K and V of every recomputed row (oracle.kv_rows on the same input rows),
+* the layer output of the recomputed rows (oracle.layer_rows); for layers with many rows a seeded
+  sample of rows, each computed by the oracle against the GPU's cache, whose recomputed rows have
+  just been held to the K/V bar,
+and rows outside the set must keep their hidden state and cache entries bit for bit.
+
+At the selection layer the oracle recomputes the current keys of every context row from the GPU's
+hidden rows and the deviation against the GPU's stitched keys (oracle.k_rows, oracle.kv_deviation).
+sqrt(d_i) = ||K_i - K_ref_i|| is 1-Lipschitz in K_i, so a current key within the element-wise bar
+moves sqrt(d_i) by at most the bar's l2 norm over the row; every GPU deviation must lie in that
+band. The GPU's selection must equal the oracle's selection rule applied to the GPU's deviation bit
+for bit, and overlap the oracle's selection from its own deviation by >= 99%.
+
+Finally cf_blend_prefill of the same request must reproduce the layer-by-layer run bit for bit
+(every layer's fused K/V, the deviation and the selection), and its output rows must equal the
+oracle's final RMSNorm of the GPU's last hidden rows, so the element-wise checks hold for the
+benchmarked call itself."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import selective_recompute_cf_amd as cf
+from tests._gpu import TOL, host, overlap, say, torch_dtype
+
+ATOL, RTOL = TOL["bf16"]
+
+
+class Keep:
+    """Host model view for DeviceModel that holds on to the host arrays of the layers in `keep`
+    (the oracle reads them later) and lets the others go once they are on the device."""
+
+    def __init__(self, model, keep):
+        self.m = model
+        self.cfg = model.cfg
+        self.keep = set(int(l) for l in keep)
+        self.kept = {}
+
+    @property
+    def embed(self):
+        return self.m.embed
+
+    @property
+    def final_norm(self):
+        return self.m.final_norm
+
+    def layer(self, l):
+        w = self.m.layer(l)
+        if l in self.keep:
+            self.kept[l] = w
+        return w
+
+
+def elementwise(name, gpu, ref, atol=ATOL, rtol=RTOL, stats=None):
+    """Assert |gpu - ref| <= atol + rtol |ref| at every element; print and record the figures."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    err = np.abs(gpu - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    nrel = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-30))
+    r = dict(max_abs=float(err.max(initial=0.0)), norm_rel=nrel, misses=int(bad.sum()), n=int(err.size),
+             max_ratio=float((err / (atol + rtol * np.abs(ref))).max(initial=0.0)))
+    say(f"    {name}: max_abs={r['max_abs']:.3e} norm_rel={nrel:.3e} worst/bar={r['max_ratio']:.3f} "
+        f"misses={r['misses']}/{r['n']}")
+    if stats is not None:
+        stats[name] = r
+    assert np.isfinite(gpu).all(), f"{name}: non-finite GPU values"
+    assert r["misses"] == 0, f"{name}: {r['misses']} of {r['n']} elements outside |d| <= {atol} + {rtol}|ref|"
+    return r
+
+
+def _select(mode, d, k, spans):
+    if mode == "token":
+        return oracle.select_topk(d, k)
+    if mode == "doc":
+        return oracle.select_doc_spans(d, k, spans)
+    raise ValueError(mode)
+
+
+def _sample_rows(n, sample, U, seed):
+    """Indices into a recompute set of n rows: all of them, or `sample` seeded ones that always
+    include the first and last rows, the first query row and the rows at 128-row tile edges."""
+    if sample is None or n <= sample:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    must = {0, n - 1, max(0, n - U), min(n - 1, 127), min(n - 1, 128)}
+    rest = rng.choice(n, size=sample, replace=False)
+    return np.unique(np.concatenate([np.fromiter(must, np.int64), rest]))
+
+
+def teacher_forced(ctx, dm, keep, tokens, N, k, mode, spans, k_store, v_store, table, s=1, check=(),
+                   sample=None, seed=0, prefill=True):
+    """Run one request layer by layer on the GPU and hold every layer in `check` to the oracle (see
+    the module docstring). `sample` caps the rows whose layer output the oracle computes per layer
+    (None: all). Returns {layer: {quantity: stats}} plus "selection" and "prefill" entries."""
+    import torch
+    cfg = dm.cfg
+    Ly = dm.n_layers
+    L = len(tokens)
+    U = L - N
+    hkv, hd, d = cfg.n_kv_heads, cfg.head_dim, cfg.d_model
+    kvd = hkv * hd
+    dt = torch_dtype(cfg.dtype)
+    check = set(int(l) for l in check)
+    out = {}
+    # stitched cache of every layer (layers below s are overwritten by their full recompute)
+    kb = torch.zeros(Ly, L, kvd, dtype=dt, device="cuda")
+    vb = torch.zeros_like(kb)
+    ctx.rope_reposition(k_store, v_store, kb, vb, table, 0, Ly)
+    hidden = torch.from_numpy(np.ascontiguousarray(keep.embed[np.asarray(tokens)], np.float32)).cuda()
+    iota = torch.arange(L, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(ctx.blend_layer_workspace_size(L, L), ctx.blend_layer_workspace_size(L, k + U),
+                         ctx.selection_deviation_workspace_size(N),
+                         cf.topk_workspace_size(N, mode), 1), dtype=torch.uint8, device="cuda")
+    dev = torch.zeros(max(N, 1), dtype=torch.float32, device="cuda")
+    P = torch.zeros(max(k, 1), dtype=torch.int32, device="cuda")
+    rows_all = np.arange(L)
+    rows_sel, sel_t = None, None
+    for l in range(Ly):
+        if l == s:
+            ctx.selection_deviation(dm.array[s], hidden, N, kb[s], dev, ws)
+            cf.topk_select(dev[:N], k, P, mode, spans, ws)
+            torch.cuda.synchronize()
+            d_g = dev.cpu().numpy()[:N]
+            P_g = P.cpu().numpy()[:k]
+            st = {}
+            if s in check:
+                h_ctx = host(hidden)[:N]
+                kref = host(kb[s])[:N].reshape(N, hkv, hd)
+                k_o = oracle.k_rows(cfg, keep.kept[s], h_ctx, np.arange(N))
+                d_o = oracle.kv_deviation(k_o, kref)
+                band = np.sqrt(np.sum((ATOL + RTOL * np.abs(k_o.reshape(N, -1).astype(np.float64))) ** 2, axis=1))
+                gap = np.abs(np.sqrt(d_g.astype(np.float64)) - np.sqrt(d_o.astype(np.float64)))
+                st["dev"] = dict(max_gap_over_band=float((gap / band).max(initial=0.0)),
+                                 misses=int((gap > band).sum()), n=N,
+                                 norm_rel=float(np.linalg.norm(d_g - d_o) / max(np.linalg.norm(d_o), 1e-30)))
+                ov = overlap(P_g, _select(mode, d_o, k, spans))
+                st["overlap"] = ov
+                say(f"  layer {s} selection: sqrt(dev) gap / band max {st['dev']['max_gap_over_band']:.3f}, "
+                    f"misses {st['dev']['misses']}/{N}, norm_rel {st['dev']['norm_rel']:.3e}; overlap with the "
+                    f"oracle's selection {ov:.4f} ({k} tokens)")
+                assert st["dev"]["misses"] == 0, "deviation outside the band a key within the bar allows"
+                assert ov >= 0.99, f"selection overlap {ov:.4f} < 0.99"
+            np.testing.assert_array_equal(P_g, _select(mode, d_g, k, spans))
+            out["selection"] = st
+            rows_sel = np.concatenate([P_g.astype(np.int64), np.arange(N, L)])
+            sel_t = torch.from_numpy(rows_sel.astype(np.int32)).cuda()
+        rows = rows_all if l < s else rows_sel
+        rows_t = iota if l < s else sel_t
+        chk = l in check
+        if chk:
+            h_in, kc_in, vc_in = host(hidden), host(kb[l]).reshape(L, hkv, hd), host(vb[l]).reshape(L, hkv, hd)
+        ctx.blend_layer(dm.array[l], hidden, kb[l], vb[l], rows_t, ws)
+        if not chk:
+            continue
+        torch.cuda.synchronize()
+        h_out, kc_out, vc_out = host(hidden), host(kb[l]).reshape(L, hkv, hd), host(vb[l]).reshape(L, hkv, hd)
+        W = keep.kept[l]
+        say(f"  layer {l}: {len(rows)} rows recomputed of {L}")
+        st = {}
+        other = np.setdiff1d(rows_all, rows)
+        assert np.array_equal(h_out[other], h_in[other]), f"layer {l}: rows outside the set changed"
+        assert np.array_equal(kc_out[other], kc_in[other]) and np.array_equal(vc_out[other], vc_in[other]), \
+            f"layer {l}: cache rows outside the set changed"
+        k_o, v_o = oracle.kv_rows(cfg, W, h_in[rows], rows)
+        elementwise(f"layer {l} K", kc_out[rows], k_o, stats=st)
+        elementwise(f"layer {l} V", vc_out[rows], v_o, stats=st)
+        S = _sample_rows(len(rows), sample, U, seed + l)
+        if len(S) == len(rows):  # the oracle's own layer on the GPU's inputs
+            kc_t, vc_t = kc_in.copy(), vc_in.copy()
+        else:  # sampled rows against the GPU's cache, whose recomputed rows met the bar above
+            kc_t, vc_t = kc_out.copy(), vc_out.copy()
+        h_o = oracle.layer_rows(cfg, W, h_in[rows[S]], rows[S], kc_t, vc_t)
+        elementwise(f"layer {l} h ({len(S)} rows)", h_out[rows[S]], h_o, stats=st)
+        out[l] = st
+    if prefill:
+        torch.cuda.synchronize()
+        h_fin = host(hidden)
+        tok = torch.from_numpy(np.asarray(tokens, np.int32)).cuda()
+        k_out = torch.zeros_like(kb)
+        v_out = torch.zeros_like(vb)
+        o_rows = torch.zeros(max(U, 1), d, dtype=torch.float32, device="cuda")
+        sel2 = torch.full((max(k, 1),), -1, dtype=torch.int32, device="cuda")
+        dev2 = torch.zeros(max(N, 1), dtype=torch.float32, device="cuda")
+        wsp = torch.empty(ctx.blend_prefill_workspace_size(N, U, k, mode), dtype=torch.uint8, device="cuda")
+        ctx.blend_prefill(dm.array, dm.embed, dm.final_norm, tok, N, U, k_store, v_store, table, s, k, mode, spans,
+                          k_out, v_out, o_rows if U else None, wsp, out_sel=sel2, out_dev=dev2)
+        torch.cuda.synchronize()
+        assert torch.equal(k_out, kb) and torch.equal(v_out, vb), "cf_blend_prefill differs from the layer loop"
+        assert torch.equal(sel2[:k], P[:k]) and torch.equal(dev2[:N], dev[:N])
+        ref = oracle.rms_norm(h_fin[N:], keep.final_norm, cfg.rms_eps)
+        st = {}
+        if U:
+            elementwise("final out", host(o_rows)[:U], ref, atol=1e-5, rtol=1e-5, stats=st)
+        out["prefill"] = st
+        say("  cf_blend_prefill equals the layer-by-layer run bit for bit")
+    return out

@@ -99,8 +99,9 @@ def test_gradual_schedule_host_logic_agrees_with_oracle():
             for n_sched in [1, 3, 31]:
                 assert cf.gradual_schedule(n, n_sched, first, keep, final) == \
                     oracle.gradual_schedule(n, n_sched, first, keep, final)
-    with pytest.raises(ValueError):
+    with pytest.raises(cf.CfError) as e:
         cf.gradual_schedule(100, 3, (10, 100), (1, 2), (20, 100))
+    assert e.value.status == cf.CF_EINVAL
 
 
 def test_context_rejects_bad_shapes(L):
@@ -118,8 +119,10 @@ def test_budget_host_logic_agrees_with_oracle():
     for n in [0, 1, 7, 10, 512, 3072, 7720, 10240, 16384]:
         for num, den in [(0, 100), (1, 100), (5, 100), (15, 100), (29, 100), (30, 100), (1, 3), (100, 100)]:
             assert cf.budget(n, num, den) == oracle.budget(n, num, den)
-    with pytest.raises(ValueError):
-        cf.budget(10, 101, 100)
+    for args in [(10, 101, 100), (10, -1, 100), (10, 1, 0), (-1, 1, 2)]:
+        with pytest.raises(cf.CfError) as e:
+            cf.budget(*args)
+        assert e.value.status == cf.CF_EINVAL
 
 
 def test_span_policy_host_logic_agrees_with_oracle():
@@ -135,6 +138,36 @@ def test_span_policy_host_logic_agrees_with_oracle():
         sel = np.unique(rng.integers(0, 50, 12))
         a, b = cf.selection_stats(sel, d), oracle.selection_stats(sel, d)
         assert a[0] == b[0] and (a[1] == b[1] or abs(a[1] - b[1]) < 1e-12 or (np.isnan(a[1]) and np.isnan(b[1])))
+
+
+def test_policy_calls_validate_and_report_sizes(L):
+    """The policy arithmetic entry points reject bad arguments with CF_EINVAL and report the
+    number of bounds a too-small array would have needed."""
+    k = ctypes.c_int32(-7)
+    assert L.cf_budget(10, 1, 2, None) == cf.CF_EINVAL
+    assert L.cf_budget(10, 3, 2, ctypes.byref(k)) == cf.CF_EINVAL and k.value == -7
+    assert "ratio" in L.cf_last_error().decode()
+    assert L.cf_budget(3072, 15, 100, ctypes.byref(k)) == cf.CF_OK and k.value == 460 and L.cf_last_error() == b""
+    nb = ctypes.c_int32(0)
+    small = (ctypes.c_int32 * 2)()
+    assert L.cf_fixed_chunk_bounds(300, 92, 46, small, 2, ctypes.byref(nb)) == cf.CF_EINVAL and nb.value == 5
+    assert L.cf_fixed_chunk_bounds(300, 92, 92, small, 2, ctypes.byref(nb)) == cf.CF_EINVAL
+    assert L.cf_single_window_bounds(5, small, 2, ctypes.byref(nb)) == cf.CF_OK and list(small) == [0, 5]
+    sched = (ctypes.c_int32 * 3)()
+    assert L.cf_gradual_schedule(100, 3, 20, 100, 3, 2, 15, 100, sched) == cf.CF_EINVAL  # keep > 1
+    seg, cap = ctypes.c_int32(0), ctypes.c_double(0)
+    dup = (ctypes.c_int32 * 2)(3, 3)
+    dev = (ctypes.c_float * 5)(1, 2, 3, 4, 5)
+    assert L.cf_selection_stats(dup, 2, dev, 5, ctypes.byref(seg), ctypes.byref(cap)) == cf.CF_EINVAL
+    out = (ctypes.c_int32 * 2)(1, 5)
+    assert L.cf_selection_stats(out, 2, dev, 5, ctypes.byref(seg), ctypes.byref(cap)) == cf.CF_EINVAL
+    ok = (ctypes.c_int32 * 2)(4, 3)
+    assert L.cf_selection_stats(ok, 2, dev, 5, ctypes.byref(seg), ctypes.byref(cap)) == cf.CF_OK
+    assert seg.value == 1 and abs(cap.value - 9 / 15) < 1e-15
+    rat = (ctypes.c_int32 * 2)(1, 0)
+    ms = (ctypes.c_double * 1)(1.0)
+    a, b = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert L.cf_loading_ratio(2.0, rat, ms, 1, 15, 100, ctypes.byref(a), ctypes.byref(b)) == cf.CF_EINVAL
 
 
 def test_ranked_span_order_validation(L):
@@ -171,7 +204,8 @@ def test_product_path_fails_loudly_without_the_library(monkeypatch):
     """No fallback: with libcf.so absent, every entry point raises instead of computing anything."""
     monkeypatch.setattr(cf, "LIB_PATH", os.path.join(os.path.dirname(cf.LIB_PATH), "absent", "libcf.so"))
     monkeypatch.setattr(cf, "_lib", None)
-    for call in (cf.lib, cf.version, lambda: cf.topk_workspace_size(10, "token"),
+    for call in (cf.lib, cf.version, lambda: cf.topk_workspace_size(10, "token"), lambda: cf.budget(10, 1, 2),
+                 lambda: cf.gradual_schedule(10, 2), lambda: cf.fixed_chunk_bounds(100),
                  lambda: cf.Context.from_model_cfg(synth.TINY, max_pos=64)):
         with pytest.raises(RuntimeError, match="missing"):
             call()

@@ -236,6 +236,20 @@ def test_full_prefill_matches_torch_decoder(cfg):
     np.testing.assert_allclose(out, out2, rtol=1e-9, atol=1e-10)
 
 
+@pytest.mark.parametrize("cfg", [TINY, TINY_QK], ids=["llama-style", "qk-norm"])
+def test_kv_rows_match_torch_decoder_first_layer(cfg):
+    """oracle.kv_rows (a layer's fresh K and V of given rows) against the independent torch
+    decoder's first-layer K/V: its input rows are the embeddings, at positions 0..n-1."""
+    model = _Model(cfg)
+    toks = np.random.default_rng(8).integers(0, cfg.vocab, 33)
+    K2, V2, _ = _torch_decoder(model, toks, 1)
+    k, v = oracle.kv_rows(cfg, model.layer(0), np.asarray(model.embed[toks], F64), np.arange(len(toks)), F64)
+    np.testing.assert_allclose(k, K2[0], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(v, V2[0], rtol=1e-10, atol=1e-11)
+    kk = oracle.k_rows(cfg, model.layer(0), np.asarray(model.embed[toks], F64), np.arange(len(toks)), F64)
+    np.testing.assert_allclose(kk, K2[0], rtol=1e-10, atol=1e-11)
+
+
 # ------------------------------------------------------------------ deviation
 
 def test_kv_deviation_closed_form():
