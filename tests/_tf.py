@@ -8,10 +8,17 @@ checked layer the GPU's own inputs (the fp32 residual rows and the layer's K/V c
 to the host, and the oracle runs that one layer on exactly those inputs in fp32
 (QCFuse §2.1.3 Eq. 7; CacheBlend, "Selective Recompute Without Skipping"). The GPU's outputs must
 then meet the element-wise bf16 bar |gpu - oracle| <= 2e-2 + 1e-2 |oracle| at every element of:
-* the fresh K and V of every recomputed row (oracle.kv_rows on the same input rows),
-* the layer output of the recomputed rows (oracle.layer_rows); for layers with many rows a seeded
+* the fresh K and V of every recomputed row, against the fp32 oracle (oracle.kv_rows on the same
+  input rows);
+* the layer output (the fp32 residual rows) of the recomputed rows, against the oracle's layer in
+  its bf16-arithmetic mode (oracle.layer_rows with bf16_ops: the operands a BF16 stack rounds are
+  rounded, sums stay fp32; that mode is pinned against an independent torch decoder). Against the
+  fp32 oracle the hidden rows cannot meet the bar: one bf16 layer at Llama-3-8B width lands 8.9e-3
+  norm-wise from fp32 with about 12% of the elements outside it, whatever the implementation, so
+  there the GPU must stay within 1.25x the bf16 arithmetic's own norm-wise distance, and the
+  element counts are printed. For layers with many rows the layer output is checked on a seeded
   sample of rows, each computed by the oracle against the GPU's cache, whose recomputed rows have
-  just been held to the K/V bar,
+  just been held to the K/V bar;
 and rows outside the set must keep their hidden state and cache entries bit for bit.
 
 At the selection layer the oracle recomputes the current keys of every context row from the GPU's
@@ -78,6 +85,17 @@ def elementwise(name, gpu, ref, atol=ATOL, rtol=RTOL, stats=None):
     assert np.isfinite(gpu).all(), f"{name}: non-finite GPU values"
     assert r["misses"] == 0, f"{name}: {r['misses']} of {r['n']} elements outside |d| <= {atol} + {rtol}|ref|"
     return r
+
+
+# How far beyond the distance of bf16 arithmetic itself (the oracle's bf16 mode, pinned against an
+# independent torch decoder that rounds the same operands) a layer's hidden rows may land from fp32.
+H_FLOOR_FACTOR = 1.25
+
+
+def _nrel(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
 def _select(mode, d, k, spans):
@@ -177,12 +195,25 @@ def teacher_forced(ctx, dm, keep, tokens, N, k, mode, spans, k_store, v_store, t
         elementwise(f"layer {l} K", kc_out[rows], k_o, stats=st)
         elementwise(f"layer {l} V", vc_out[rows], v_o, stats=st)
         S = _sample_rows(len(rows), sample, U, seed + l)
-        if len(S) == len(rows):  # the oracle's own layer on the GPU's inputs
-            kc_t, vc_t = kc_in.copy(), vc_in.copy()
-        else:  # sampled rows against the GPU's cache, whose recomputed rows met the bar above
-            kc_t, vc_t = kc_out.copy(), vc_out.copy()
-        h_o = oracle.layer_rows(cfg, W, h_in[rows[S]], rows[S], kc_t, vc_t)
-        elementwise(f"layer {l} h ({len(S)} rows)", h_out[rows[S]], h_o, stats=st)
+        h_ref = {}
+        for bf in (True, False):
+            if len(S) == len(rows):  # the oracle's own layer on the GPU's inputs
+                kc_t, vc_t = kc_in.copy(), vc_in.copy()
+            else:  # sampled rows against the GPU's cache, whose recomputed rows met the bar above
+                kc_t, vc_t = kc_out.copy(), vc_out.copy()
+            h_ref[bf] = oracle.layer_rows(cfg, W, h_in[rows[S]], rows[S], kc_t, vc_t, bf16_ops=bf)
+        g = h_out[rows[S]]
+        elementwise(f"layer {l} h vs bf16-arithmetic oracle ({len(S)} rows)", g, h_ref[True], stats=st)
+        # against fp32: the GPU may add little beyond the distance of BF16 arithmetic itself
+        e_gpu = _nrel(g, h_ref[False])
+        e_bf = _nrel(h_ref[True], h_ref[False])
+        bad = np.abs(g - h_ref[False]) > ATOL + RTOL * np.abs(h_ref[False])
+        bad16 = np.abs(h_ref[True] - h_ref[False]) > ATOL + RTOL * np.abs(h_ref[False])
+        st["h_fp32"] = dict(norm_rel=e_gpu, bf16_arith_norm_rel=e_bf, misses=int(bad.sum()),
+                            bf16_arith_misses=int(bad16.sum()), n=int(bad.size))
+        say(f"    layer {l} h vs fp32 oracle: norm_rel={e_gpu:.3e} (bf16 arithmetic itself {e_bf:.3e}); "
+            f"elements outside (2e-2, 1e-2): {int(bad.sum())}/{bad.size} (bf16 arithmetic itself {int(bad16.sum())})")
+        assert e_gpu <= H_FLOOR_FACTOR * e_bf + 1e-5, f"layer {l}: h is further from fp32 than bf16 arithmetic allows"
         out[l] = st
     if prefill:
         torch.cuda.synchronize()

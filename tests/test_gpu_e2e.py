@@ -4,16 +4,14 @@ full recompute, deviation and selection on layer 1, selective recompute of the r
 
 Bars:
 * selection: the GPU's selected set equals the oracle's selection run on the GPU's own deviation
-  array (bit-exact) and overlaps the fp32 oracle's end-to-end selection by >= 99% (bf16 models:
-  or by the overlap of the oracle's own bf16-arithmetic run minus 1%, when that is lower);
+  array (bit-exact) and overlaps the fp32 oracle's end-to-end selection by >= 99% (fp32 models) or
+  >= 97% (bf16 models), every token selected by only one side being a near tie (tests/_gpu.py);
 * fp32 models: fused K/V and final normed query rows elementwise within 1e-4 + 1e-4 |ref|;
-* bf16 models: against the fp32 oracle, the norm-wise relative error of the final query rows, of
-  the deviation and of the fused K/V (rows whose selection agrees) is at most twice the error
-  that the oracle's own bf16-arithmetic evaluation of the same request shows against the fp32
-  oracle, plus 2e-3. A fixed elementwise bound cannot hold for stacked bf16 layers (bf16
-  rounding alone moves a 32-layer result by several percent), so the bound is measured, per
-  request, from the arithmetic. Single layers meet the fixed (2e-2, 1e-2) bound elementwise
-  (test_gpu_layer)."""
+* bf16 models: against the fp32 oracle, the norm-wise drift of the final query rows, of the
+  deviation, of the chunk caches and of the fused K/V (rows whose selection agrees) within 2e-2 per
+  stacked layer, and no head-sized chunk of any row more than 4x that (tests/_gpu.py explains the
+  allowance); the element counts outside the (2e-2, 1e-2) bar are printed. The element-wise bar
+  itself is held layer by layer on the GPU's own inputs (test_gpu_teacher_forced)."""
 import numpy as np
 import pytest
 
@@ -21,31 +19,27 @@ import oracle
 import selective_recompute_cf_amd as cf
 import synth
 from selective_recompute_cf_amd.device import DeviceModel
-from tests._gpu import compare, context, gpu_blend, gpu_chunk_store, host, overlap, say, selection_bar
+from tests._gpu import compare, context, e2e_bf16, e2e_selection, gpu_blend, gpu_chunk_store, host, overlap, say
 
 pytestmark = pytest.mark.gpu
 
 
-def nrel(a, b) -> float:
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
-
-
-def _oracle(model, chunks, toks, w, N, k, mode, spans, ly, bf16_ops):
+def _oracle(model, chunks, toks, w, N, k, mode, spans, ly):
     ks, vs, table, row = [], [], [], 0
     for c in chunks:
-        a, b = oracle.chunk_prefill(model, c, np.float32, ly, bf16_ops)
+        a, b = oracle.chunk_prefill(model, c, np.float32, ly)
         ks.append(a)
         vs.append(b)
         table.append((row, 0, row, len(c)))
         row += len(c)
     ks, vs = np.concatenate(ks, 1), np.concatenate(vs, 1)
-    r = oracle.blend_prefill(model, toks, N, ks, vs, table, w.sel_layer, k, mode, spans, np.float32, ly, bf16_ops)
+    r = oracle.blend_prefill(model, toks, N, ks, vs, table, w.sel_layer, k, mode, spans, np.float32, ly)
     return r, ks, vs
 
 
 def _run(w, n_layers=None, mode=None, k=None):
+    """GPU blend and the fp32 oracle's blend of the workload; returns (model, tokens, gpu result,
+    oracle result, ctx, device model, (store K, store V, chunk table, spans))."""
     model = synth.Model(w.model)
     chunks, _, toks = synth.request_tokens(w)
     ly = w.model.n_layers if n_layers is None else n_layers
@@ -61,13 +55,10 @@ def _run(w, n_layers=None, mode=None, k=None):
     spans = [i * w.chunk_len for i in range(w.n_chunks + 1)]
     g = gpu_blend(ctx, dm, toks, N, gk, gv, table, w.sel_layer, k, mode, spans)
     g["store_k"], g["store_v"] = host(gk), host(gv)
-    r32, ks32, vs32 = _oracle(model, chunks, toks, w, N, k, mode, spans, ly, False)
-    r16 = None
-    if cfg.dtype == "bf16":
-        r16, ks16, vs16 = _oracle(model, chunks, toks, w, N, k, mode, spans, ly, True)
-        r16.store_k, r16.store_v = ks16, vs16
+    r32, ks32, vs32 = _oracle(model, chunks, toks, w, N, k, mode, spans, ly)
     r32.store_k, r32.store_v = ks32, vs32
-    return model, toks, g, r32, r16, ctx, dm, (gk, gv, table, spans)
+    g["layers"] = ly
+    return model, toks, g, r32, ctx, dm, (gk, gv, table, spans)
 
 
 def _rows_agree(N, L, sel_a, sel_b):
@@ -80,61 +71,48 @@ def _rows_agree(N, L, sel_a, sel_b):
     return agree
 
 
-def _check(w, g, r32, r16, mode=None):
+def _check(w, g, r32, mode=None):
     mode = mode or w.mode
     N, L = w.n_ctx, w.n_total
+    ly = g["layers"]
     bounds = [i * w.chunk_len for i in range(w.n_chunks + 1)]
-    want = (oracle.select_topk(g["dev"], len(g["sel"])) if mode == "token" else
-            oracle.select_doc_spans(g["dev"], len(g["sel"]), bounds))
+    k = len(g["sel"])
+    want = (oracle.select_topk(g["dev"], k) if mode == "token" else oracle.select_doc_spans(g["dev"], k, bounds))
     np.testing.assert_array_equal(g["sel"], want)
-    ov = overlap(g["sel"], r32.sel)
-    say(f"  selection overlap with fp32 oracle {ov:.4f} ({len(r32.sel)} tokens)"
-        + ("" if r16 is None else f"; bf16-arithmetic oracle's own overlap {overlap(r16.sel, r32.sel):.4f}"))
-    assert ov >= selection_bar(None if r16 is None else r16.sel, r32.sel)
+    bf16 = w.model.dtype == "bf16"
+    e2e_selection(g["sel"], r32.sel, r32.dev, k, bf16, mode == "token")
     shape = g["k"].shape
-    if r16 is None:  # fp32 model: fixed elementwise bar
+    if not bf16:  # fp32 model: fixed elementwise bar
         compare("dev", g["dev"], r32.dev, atol=1e-4 * float(np.median(r32.dev)), rtol=1e-3)
         compare("store K", g["store_k"], r32.store_k.reshape(g["store_k"].shape), "f32")
         compare("out", g["out"], r32.out, "f32")
         compare("K", g["k"], r32.k.reshape(shape), "f32")
         compare("V", g["v"], r32.v.reshape(shape), "f32")
         return
-    agree_g = _rows_agree(N, L, g["sel"], r32.sel)
-    agree_o = _rows_agree(N, L, r16.sel, r32.sel)
-    items = [
-        ("dev", g["dev"], r16.dev, r32.dev, None, None),
-        ("store K", g["store_k"], r16.store_k.reshape(g["store_k"].shape), r32.store_k.reshape(g["store_k"].shape), None, None),
-        ("store V", g["store_v"], r16.store_v.reshape(g["store_v"].shape), r32.store_v.reshape(g["store_v"].shape), None, None),
-        ("out", g["out"], r16.out, r32.out, None, None),
-        ("K", g["k"], r16.k.reshape(shape), r32.k.reshape(shape), agree_g, agree_o),
-        ("V", g["v"], r16.v.reshape(shape), r32.v.reshape(shape), agree_g, agree_o),
-    ]
-    for name, gv, ov16, ov32, ag, ao in items:
-        if ag is not None:
-            gv, gref, ov16, oref = gv[:, ag], ov32[:, ag], ov16[:, ao], ov32[:, ao]
-        else:
-            gref, oref = ov32, ov32
-        e_gpu, e_ref = nrel(gv, gref), nrel(ov16, oref)
-        bound = 2.0 * e_ref + 2e-3
-        el = np.abs(np.asarray(gv, np.float64) - gref) > 2e-2 + 1e-2 * np.abs(gref)
-        say(f"  {name}: gpu vs fp32 oracle norm_rel={e_gpu:.3e}; bf16 oracle vs fp32 oracle {e_ref:.3e}; "
-            f"bound {bound:.3e}; elementwise (2e-2,1e-2) misses {int(el.sum())}/{el.size}")
-        assert e_gpu <= bound, name
+    hd = w.model.head_dim
+    agree = _rows_agree(N, L, g["sel"], r32.sel)
+    e2e_bf16("dev", g["dev"], r32.dev, w.sel_layer + 1, hd)
+    e2e_bf16("store K", g["store_k"], r32.store_k.reshape(g["store_k"].shape), ly, hd)
+    e2e_bf16("store V", g["store_v"], r32.store_v.reshape(g["store_v"].shape), ly, hd)
+    if len(g["out"]):
+        e2e_bf16("out", g["out"], r32.out, ly, min(128, w.model.d_model))
+    e2e_bf16("K", g["k"][:, agree], r32.k.reshape(shape)[:, agree], ly, hd)
+    e2e_bf16("V", g["v"][:, agree], r32.v.reshape(shape)[:, agree], ly, hd)
 
 
 def test_tiny_fp32_workload():
     """C1 as configured: fp32, 2 layers, 4x128 + 32, top-15% selected on layer 1."""
     w = synth.WORKLOADS["tiny"]
-    model, toks, g, r32, r16, *_ = _run(w)
+    model, toks, g, r32, *_ = _run(w)
     assert len(g["sel"]) == 76
-    _check(w, g, r32, r16)
+    _check(w, g, r32)
 
 
 def test_tiny_bf16_three_layers_doc_spans():
     w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(dtype="bf16", n_layers=3), mode="doc",
                                         rho_num=30, rho_den=100)
-    model, toks, g, r32, r16, *_ = _run(w)
-    _check(w, g, r32, r16)
+    model, toks, g, r32, *_ = _run(w)
+    _check(w, g, r32)
 
 
 @pytest.mark.parametrize("mode", ["token", "doc"])
@@ -142,16 +120,16 @@ def test_gqa4_hd128_bf16(mode):
     m = synth.TINY.replace(name="mid", n_layers=3, d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
                            d_ffn=2816, vocab=2000, rope_theta=5e5, dtype="bf16")
     w = synth.Workload("mid-5x200+40", m, 5, 200, 40, 15, 100, mode=mode)
-    model, toks, g, r32, r16, *_ = _run(w)
-    _check(w, g, r32, r16)
+    model, toks, g, r32, *_ = _run(w)
+    _check(w, g, r32)
 
 
 def test_qknorm_bf16():
     m = synth.TINY.replace(name="mid-qk", n_layers=3, d_model=512, n_q_heads=8, n_kv_heads=1, head_dim=64,
                            d_ffn=1408, vocab=2000, rope_theta=1e6, rms_eps=1e-6, qk_norm=True, dtype="bf16")
     w = synth.Workload("mid-qk-4x256+64", m, 4, 256, 64, 30, 100)
-    model, toks, g, r32, r16, *_ = _run(w)
-    _check(w, g, r32, r16)
+    model, toks, g, r32, *_ = _run(w)
+    _check(w, g, r32)
 
 
 def test_endpoints_full_ratio_and_direct_reuse():
@@ -160,7 +138,7 @@ def test_endpoints_full_ratio_and_direct_reuse():
     the fixed elementwise bar applies)."""
     w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(n_layers=3))
     N, L = w.n_ctx, w.n_total
-    model, toks, g, r32, r16, ctx, dm, (gk, gv, table, spans) = _run(w, k=N)
+    model, toks, g, r32, ctx, dm, (gk, gv, table, spans) = _run(w, k=N)
     full = gpu_blend(ctx, dm, toks, N, None, None, None, 0, 0, "all")
     np.testing.assert_array_equal(g["out"], full["out"])
     np.testing.assert_array_equal(g["k"], full["k"])
@@ -177,7 +155,7 @@ def test_first_chunk_never_selected_and_empty_query():
     """The first chunk has no preceding context, so its deviation is ~0 and it is never picked
     while k <= N - |c_1|; U = 0 (no query rows) is a valid request."""
     w = synth.WORKLOADS["tiny"].replace(n_query=0, model=synth.TINY.replace(dtype="bf16"))
-    model, toks, g, r32, r16, *_ = _run(w)
+    model, toks, g, r32, *_ = _run(w)
     assert g["out"].shape[0] == 0
     assert np.all(g["sel"] >= w.chunk_len)
     assert np.max(g["dev"][: w.chunk_len]) < 1e-3 * np.median(g["dev"][w.chunk_len:])
@@ -187,17 +165,17 @@ def test_llama3_8b_shape_reduced_depth():
     """Llama-3-8B shape at full width and full request length (6 x 512 + 64, k = 460), 3 layers.
     The selection (layer 1) is the one the full-depth request makes."""
     w = synth.WORKLOADS["llama8b"]
-    model, toks, g, r32, r16, *_ = _run(w, n_layers=3)
+    model, toks, g, r32, *_ = _run(w, n_layers=3)
     assert len(g["sel"]) == 460
-    _check(w, g, r32, r16)
+    _check(w, g, r32)
 
 
 def test_qwen3_8b_shape_reduced_depth():
     """Qwen3-8B shape (qk-norm, theta 1e6) at full width and length (10 x 1024 + 128, k = 3072), 2 layers."""
     w = synth.WORKLOADS["qwen8b"]
-    model, toks, g, r32, r16, *_ = _run(w, n_layers=2)
+    model, toks, g, r32, *_ = _run(w, n_layers=2)
     assert len(g["sel"]) == 3072
-    _check(w, g, r32, r16)
+    _check(w, g, r32)
 
 
 @pytest.mark.parametrize("policy", ["single-window", "fixed-chunk", "random-document", "heads"])

@@ -4,8 +4,10 @@ oracle.query_scores, and of the query-aware blend (cf_blend_prefill with the top
 as a given set) against the oracle's blend of the same set.
 
 Bars: fp32 models elementwise (scores within 1e-4 relative plus 1e-6 of the largest score);
-bf16 models norm-wise, at most twice the error of the oracle's own bf16-arithmetic evaluation
-plus 2e-3, the calibration of the end-to-end tests; the probe never writes context rows."""
+bf16 models against the fp32 oracle under the end-to-end bf16 bars of the blend tests (norm-wise
+drift of the scores within 2e-2 per layer the probe runs, no 128-position chunk 4x further; the
+top-10% sets overlapping by >= 97%, every disagreement a near tie); the probe never writes context
+rows."""
 import numpy as np
 import pytest
 
@@ -13,7 +15,7 @@ import oracle
 import selective_recompute_cf_amd as cf
 import synth
 from selective_recompute_cf_amd.device import DeviceModel
-from tests._gpu import compare, context, gpu_blend, gpu_chunk_store, host, overlap, say
+from tests._gpu import compare, context, e2e_bf16, e2e_selection, gpu_blend, gpu_chunk_store, host, overlap, say
 
 pytestmark = pytest.mark.gpu
 
@@ -51,13 +53,12 @@ def _gpu_scores(ctx, dm, toks, N, kb, vb, layer_set):
     return scores.cpu().numpy()
 
 
-def _oracle_scores(model, toks, N, gk, gv, table, ly, layer_set, bf16_ops):
+def _oracle_scores(model, toks, N, gk, gv, table, ly, layer_set):
     cfg = model.cfg
     shape = (ly, gk.shape[1], cfg.n_kv_heads, cfg.head_dim)
     ks, vs = host(gk).reshape(shape), host(gv).reshape(shape)
-    kst, vst = oracle.stitch(ks, vs, table, N, range(ly), cfg.rope_theta, np.float32, n_total=len(toks),
-                             rnd=oracle.bf16_round if bf16_ops and cfg.dtype == "bf16" else None)
-    return oracle.query_scores(model, toks, N, kst, vst, layer_set, np.float32, bf16_ops), ks, vs
+    kst, vst = oracle.stitch(ks, vs, table, N, range(ly), cfg.rope_theta, np.float32, n_total=len(toks))
+    return oracle.query_scores(model, toks, N, kst, vst, layer_set, np.float32), ks, vs
 
 
 def _check(w, ly, layer_set):
@@ -67,20 +68,14 @@ def _check(w, ly, layer_set):
     k_ctx_before = host(kb[:, :N])
     g = _gpu_scores(ctx, dm, toks, N, kb, vb, layer_set)
     np.testing.assert_array_equal(host(kb[:, :N]), k_ctx_before)  # context rows only read
-    o32, *_ = _oracle_scores(model, toks, N, gk, gv, table, ly, layer_set, False)
+    o32, *_ = _oracle_scores(model, toks, N, gk, gv, table, ly, layer_set)
     assert np.isfinite(g).all()
     if model.cfg.dtype != "bf16":
         compare("scores", g, o32, atol=1e-6 * float(o32.max()), rtol=1e-4)
         return g, o32
-    o16, *_ = _oracle_scores(model, toks, N, gk, gv, table, ly, layer_set, True)
-    e_gpu, e_ref = nrel(g, o32), nrel(o16, o32)
+    e2e_bf16("scores", g, o32, max(layer_set) + 1, 128)
     k = max(1, N // 10)
-    ov, ov_ref = overlap(oracle.select_topk(g, k), oracle.select_topk(o32, k)), \
-        overlap(oracle.select_topk(o16, k), oracle.select_topk(o32, k))
-    say(f"  scores: gpu vs fp32 oracle {e_gpu:.3e}; bf16 oracle {e_ref:.3e}; top-10% overlap {ov:.3f} "
-        f"(bf16 oracle {ov_ref:.3f})")
-    assert e_gpu <= 2 * e_ref + 2e-3
-    assert ov >= min(0.99, ov_ref - 0.02)
+    e2e_selection(oracle.select_topk(g, k), oracle.select_topk(o32, k), o32, k, True)
     return g, o32
 
 

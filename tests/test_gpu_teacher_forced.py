@@ -11,7 +11,9 @@ selected rows, K loops of 4096-28672, multi-piece sparse-query attention at L = 
   by -512 from the GPU's written-back store, document 20 prefilled at position 0) checked at
   layers 0, 1, 2 and 31.
 * Llama-3-70B shape, 16 x 1024 + 256, 10%, at full width and length with 4 layers (the depth
-  does not change any launch plan): every layer checked (layer outputs on 384 sampled rows)."""
+  does not change any launch plan): every layer checked (layer outputs on 384 sampled rows).
+* Smaller shapes with ragged tiles (GQA 4 at head_dim 128, qk-norm at head_dim 64 with one kv head,
+  document-aligned spans on the tiny model in bf16): every layer, every row."""
 import numpy as np
 import pytest
 
@@ -35,7 +37,8 @@ def _request(w, depth, check, sample):
     dm = DeviceModel(keep)
     gk, gv, starts = gpu_chunk_store(ctx, dm, chunks)
     table = [(s0, 0, s0, len(c)) for s0, c in zip(starts, chunks)]
-    return teacher_forced(ctx, dm, keep, toks, N, k, w.mode, None, gk, gv, table, w.sel_layer, check, sample)
+    spans = [i * w.chunk_len for i in range(w.n_chunks + 1)] if w.mode == "doc" else None
+    return teacher_forced(ctx, dm, keep, toks, N, k, w.mode, spans, gk, gv, table, w.sel_layer, check, sample)
 
 
 def test_llama3_8b_every_layer():
@@ -77,3 +80,21 @@ def test_rolling_window_write_back_step():
     say(f"teacher-forced {w.name} step 1: N={rw.N} L={rw.L} k={rw.k}, re-position offsets {sorted(set(deltas))}")
     torch.cuda.synchronize()
     teacher_forced(ctx, dm, keep, toks, rw.N, rw.k, "doc", spans, rw.k_store, rw.v_store, table, 1, check, 384)
+
+
+MID = {
+    "gqa4-hd128": synth.Workload("mid-5x200+40", synth.TINY.replace(
+        name="mid", n_layers=3, d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, d_ffn=2816, vocab=2000,
+        rope_theta=5e5, dtype="bf16"), 5, 200, 40, 15, 100),
+    "qknorm-hd64": synth.Workload("mid-qk-4x256+64", synth.TINY.replace(
+        name="mid-qk", n_layers=3, d_model=512, n_q_heads=8, n_kv_heads=1, head_dim=64, d_ffn=1408, vocab=2000,
+        rope_theta=1e6, rms_eps=1e-6, qk_norm=True, dtype="bf16"), 4, 256, 64, 30, 100),
+    "tiny-bf16-doc": synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(dtype="bf16", n_layers=3), mode="doc",
+                                                      rho_num=30, rho_den=100),
+}
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_small_shapes_every_layer(name):
+    w = MID[name]
+    _request(w, w.model.n_layers, range(w.model.n_layers), None)

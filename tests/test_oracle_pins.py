@@ -816,6 +816,90 @@ def test_bf16_model_pure_math_path_matches_torch_and_rounding_is_small():
     assert 1e-5 < rel < 2e-2
 
 
+def _torch_decoder_bf16(model, tokens, n_layers, skip=()):
+    """Independent decoder in torch fp32 that rounds to bfloat16 (torch's own conversion) exactly
+    the operands a BF16 serving stack rounds: the normed rows entering the projections, Q, every
+    K/V cache entry, the unnormalised softmax weights entering the product with V (the normaliser
+    is their unrounded sum), the attention output and the SwiGLU activation; sums stay fp32.
+    `skip` names rounding points to leave out (to show that the comparison sees a dropped one)."""
+    cfg = model.cfg
+    hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    n = len(tokens)
+    f32 = torch.float32
+
+    def r(x, what):
+        return x if what in skip else x.to(torch.bfloat16).to(f32)
+
+    h = torch.tensor(model.embed[tokens], dtype=f32)
+    freqs = 1.0 / (cfg.rope_theta ** (torch.arange(0, hd, 2, dtype=torch.float64) / hd))
+    rot = torch.polar(torch.ones(n, hd // 2, dtype=torch.float64),
+                      torch.outer(torch.arange(n, dtype=torch.float64), freqs))
+
+    def rotary(x):
+        x = x.to(torch.float64)
+        z = torch.complex(x[..., : hd // 2], x[..., hd // 2:]) * rot[:, None, :]
+        return torch.cat([z.real, z.imag], dim=-1).to(f32)
+
+    causal = torch.ones(n, n, dtype=torch.bool).tril()
+    ks, vs = [], []
+    for l in range(n_layers):
+        w = model.layer(l)
+        T = lambda a: torch.tensor(np.asarray(a), dtype=f32)
+        a = r(F.rms_norm(h, (cfg.d_model,), T(w.attn_norm), eps=cfg.rms_eps), "a")
+        q = F.linear(a, T(w.wq)).view(n, hq, hd)
+        k = F.linear(a, T(w.wk)).view(n, hkv, hd)
+        v = F.linear(a, T(w.wv)).view(n, hkv, hd)
+        if cfg.qk_norm:
+            q = F.rms_norm(q, (hd,), T(w.q_norm), eps=cfg.rms_eps)
+            k = F.rms_norm(k, (hd,), T(w.k_norm), eps=cfg.rms_eps)
+        q, k = r(rotary(q), "q"), r(rotary(k), "kv")
+        v = r(v, "kv")
+        ks.append(k.numpy())
+        vs.append(v.numpy())
+        o = torch.empty(n, hq, hd, dtype=f32)
+        for hh in range(hq):
+            g = hh // (hq // hkv)
+            sc = torch.matmul(q[:, hh], k[:, g].T) * (1.0 / math.sqrt(hd))
+            sc = sc.masked_fill(~causal, float("-inf"))
+            p = torch.exp(sc - sc.amax(dim=1, keepdim=True))
+            o[:, hh] = torch.matmul(r(p, "p"), v[:, g]) / p.sum(dim=1, keepdim=True)
+        h = h + F.linear(r(o.reshape(n, hq * hd), "o"), T(w.wo))
+        b = r(F.rms_norm(h, (cfg.d_model,), T(w.mlp_norm), eps=cfg.rms_eps), "b")
+        act = F.silu(F.linear(b, T(w.w_gate))) * F.linear(b, T(w.w_up))
+        h = h + F.linear(r(act, "act"), T(w.w_down))
+    out = F.rms_norm(h, (cfg.d_model,), torch.tensor(model.final_norm, dtype=f32), eps=cfg.rms_eps)
+    return np.stack(ks), np.stack(vs), out.numpy()
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_QK, TINY.replace(d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                                              d_ffn=1408)],
+                         ids=["llama-style", "qk-norm", "gqa4-hd128"])
+def test_bf16_arithmetic_mode_matches_torch_bf16_decoder(cfg):
+    """The oracle's bf16-arithmetic mode (a printed diagnostic of how far BF16 arithmetic itself
+    lands from fp32) against the independent torch decoder that rounds the same operands, on one
+    layer (every rounding point of the mode sits inside a layer): the K/V it stores are equal bit
+    for bit, and the layer's normed output is equal up to fp32 summation order (which resolves a
+    few bf16 ties differently), while leaving out any single rounding point moves the output
+    further (each planted omission is checked against the threshold)."""
+    cfg = cfg.replace(dtype="bf16")
+    model = _Model(cfg)
+    toks = np.random.default_rng(15).integers(0, cfg.vocab, 48)
+    Kb, Vb, outb, _ = oracle.full_prefill(model, toks, np.float32, n_layers=1, bf16_ops=True)
+    K2, V2, out2 = _torch_decoder_bf16(model, toks, 1)
+
+    def nrel(a, b):
+        return float(np.linalg.norm(np.asarray(a, F64) - b) / np.linalg.norm(np.asarray(b, F64)))
+
+    np.testing.assert_array_equal(Kb, K2)
+    np.testing.assert_array_equal(Vb, V2)
+    same = nrel(outb, out2)
+    assert same < 2.5e-5, same
+    for point in ("a", "q", "kv", "p", "o", "b", "act"):
+        Km, Vm, outm = _torch_decoder_bf16(model, toks, 1, skip=(point,))
+        moved = max(nrel(Kb, Km), nrel(Vb, Vm), nrel(outb, outm))
+        assert moved > max(4e-5, 2 * same), (point, moved, same)
+
+
 def test_synthetic_inputs_are_deterministic():
     a = synth.layer_weights(TINY, 1)
     b = synth.layer_weights(TINY, 1)
