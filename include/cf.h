@@ -284,6 +284,55 @@ cf_status cf_query_scores(const cf_ctx* ctx, const cf_layer_weights* layers, con
                           int64_t out_layer_stride, const int32_t* layer_set /* host */, int32_t n_set,
                           float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* --------------------------------------------------------------------- chunk-anchor query probing
+ * QCFuse's compressed token view (§3.3): a few anchor tokens per chunk stand in for the whole
+ * context when the query is probed, and the resulting query states score the original context
+ * positions at a few critical layers (§3.4).
+ *
+ * cf_key_norms: Knorm's anchor score (QCFuse §3.3.1): norms[r] = the squared L2 norm of store row
+ * r's keys over layers [layer_begin, layer_end) and all kv heads (fp32), for the store_rows rows of
+ * a chunk store laid out as in cf_rope_reposition (RoPE preserves the norm, so stored keys at any
+ * position give the same score). norms: device fp32 [store_rows]. */
+cf_status cf_key_norms(const cf_ctx* ctx, const void* k_store, int64_t store_layer_stride, int32_t store_rows,
+                       int32_t layer_begin, int32_t layer_end, float* norms, hipStream_t stream);
+
+/* Anchor positions (QCFuse §3.3.1 Eq. 14-15), host arithmetic like the policy functions below:
+ * for each chunk i of the host table chunk_tab[m][4] = {store_row, src_pos, dst_pos, len}, the
+ * ceil(r_a * len) chunk-local positions of highest score G_i (equal scores: the lower position;
+ * r_a = ra_num / ra_den), written as request positions dst_pos + r, all chunks together in
+ * ascending order into anchors (host int32 [cap]); *n_anchors receives the count even when cap is
+ * too small (then CF_EINVAL).
+ *  CF_ANCHOR_SINK: G_i(r) = -r, the first tokens of each chunk (scores unused, may be NULL);
+ *  CF_ANCHOR_KNORM: G_i(r) = scores[store_row + r] (host fp32, e.g. cf_key_norms copied back),
+ *    the largest key norms; CF_ANCHOR_KNORM_LOW: the smallest (NaN ranks as +inf in both). */
+typedef enum { CF_ANCHOR_SINK = 0, CF_ANCHOR_KNORM = 1, CF_ANCHOR_KNORM_LOW = 2 } cf_anchor_rule;
+cf_status cf_anchor_positions(int32_t rule, const int32_t* chunk_tab /* host [m][4] */, int32_t m, int32_t ra_num,
+                              int32_t ra_den, const float* scores /* host */, int32_t store_rows,
+                              int32_t* anchors /* host */, int32_t cap, int32_t* n_anchors);
+
+/* cf_query_scores_anchored: anchor-conditioned query probing (QCFuse §3.3.2 Eq. 15-17) and
+ * critical-layer scoring (§3.4 Eq. 18 and Eq. 20). The U query tokens (positions N..N+U-1) run
+ * through layers 0..max(layer_set) with only the n_anchors rows of the stitched cache at the
+ * given positions as their prefix (each anchor keeps its request position, its keys being the
+ * re-positioned PIC entries, Eq. 16); at each layer l of layer_set the probe's query states score
+ * every original context position t against the full stitched keys of that layer:
+ *   scores[t] = sum over l in layer_set of the softmax weight the query rows (summed over rows and
+ *   heads) put on context row t, each row's softmax running over all N context rows and the query
+ *   rows up to itself (as in cf_query_scores, which this equals when every context position is an
+ *   anchor).
+ * The query rows' K/V of each scored layer are written to rows [N, L) of that layer of the caller's
+ * cache; context rows are only read.
+ *  anchors: device int32 [n_anchors], strictly increasing positions in [0, N) (values are clamped
+ *    in the kernels; other arrays give unspecified results). 0 <= n_anchors <= N.
+ *  Other arguments as in cf_query_scores; ws: cf_query_scores_anchored_workspace_size(ctx, N, U,
+ *  n_anchors) bytes. */
+size_t cf_query_scores_anchored_workspace_size(const cf_ctx* ctx, int32_t N, int32_t U, int32_t n_anchors);
+cf_status cf_query_scores_anchored(const cf_ctx* ctx, const cf_layer_weights* layers, const void* embed,
+                                   const int32_t* tokens, int32_t N, int32_t U, void* k_cache, void* v_cache,
+                                   int64_t out_layer_stride, const int32_t* anchors, int32_t n_anchors,
+                                   const int32_t* layer_set /* host */, int32_t n_set, float* scores, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
 /* --------------------------------------------------------------------- cf_blend_prefill_streamed
  * cf_blend_prefill with the chunk store in host memory, loaded layer by layer while the
  * previous layers are recomputed (CacheBlend, "Hiding Recompute Behind I/O": selective

@@ -20,17 +20,19 @@ default (fp64 where a step says so, and fp64 throughout when asked), following:
   document-aligned policy), §4.1 (rolling window).
 """
 from .model import (rms_norm, rope, rope_angles, causal_attention, layer_rows, full_prefill, bf16_round,
-                    chunk_prefill, k_rows, kv_rows)
+                    chunk_prefill, k_rows, kv_rows, attention_at, layer_rows_over)
 from .blend import (budget, reposition, stitch, kv_deviation, select_topk, select_doc_spans,
                     blend_prefill, direct_reuse, RollingWindow, BlendResult, narrow, gradual_schedule,
                     loading_ratio, single_window_bounds, fixed_chunk_bounds, select_ranked_spans,
-                    select_span_heads, selection_stats, query_attention_mass, query_scores)
+                    select_span_heads, selection_stats, query_attention_mass, query_scores, anchor_count,
+                    key_norms, select_anchors, anchored_query_scores)
 
 __all__ = [
     "bf16_round", "rms_norm", "rope", "rope_angles", "causal_attention", "layer_rows", "full_prefill", "k_rows",
-    "kv_rows",
+    "kv_rows", "attention_at", "layer_rows_over",
     "chunk_prefill", "budget", "reposition", "stitch", "kv_deviation", "select_topk",
     "select_doc_spans", "blend_prefill", "direct_reuse", "RollingWindow", "BlendResult", "narrow",
     "gradual_schedule", "loading_ratio", "single_window_bounds", "fixed_chunk_bounds",
     "select_ranked_spans", "select_span_heads", "selection_stats", "query_attention_mass", "query_scores",
+    "anchor_count", "key_norms", "select_anchors", "anchored_query_scores",
 ]

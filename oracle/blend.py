@@ -37,7 +37,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .model import rms_norm, rope, layer_rows, k_rows, full_prefill, rounding, _r
+from .model import rms_norm, rope, layer_rows, k_rows, full_prefill, rounding, _r, layer_rows_over
 
 
 # ------------------------------------------------------------------ budget
@@ -360,6 +360,81 @@ def query_scores(model, tokens, n_ctx, k_stitched, v_stitched, layer_set, ft=np.
         h = layer_rows(cfg, w, h, pos, kc[l], vc[l], ft, bf16_ops)
     if return_cache:
         return score.astype(np.float32), kc, vc
+    return score.astype(np.float32)
+
+
+# ------------------------------------------------------------------ chunk-anchor query probing
+
+def anchor_count(chunk_len: int, ra_num: int, ra_den: int) -> int:
+    """QCFuse §3.3.1 Eq. 14: ceil(r_a |c_i|) anchors per chunk, r_a = ra_num / ra_den (integers)."""
+    if ra_num < 0 or ra_den <= 0 or ra_num > ra_den or chunk_len < 0:
+        raise ValueError("bad anchor ratio or chunk length")
+    return (chunk_len * ra_num + ra_den - 1) // ra_den
+
+
+def key_norms(k_chunk) -> np.ndarray:
+    """Knorm's score (QCFuse §3.3.1): the squared L2 norm of each token's key-cache tensor, over
+    every layer, kv head and head dim of the stored PIC keys. k_chunk: [Ly, n, Hkv, hd]. fp64 sums,
+    returned as fp64 [n] (ranking by the norm or by its square is the same)."""
+    k = np.asarray(k_chunk, dtype=np.float64)
+    return np.sum(k * k, axis=(0, 2, 3))
+
+
+def select_anchors(chunk_len: int, ra_num: int, ra_den: int, rule: str = "sink", scores=None) -> np.ndarray:
+    """QCFuse §3.3.1 Eq. 14: A_i = TopK(G_i, ceil(r_a |c_i|)), chunk-local positions ascending.
+    rule "sink": G_i(r) = -r (the tokens at the start of the chunk); "knorm": G_i(r) = the key
+    norm score of position r (largest kept); "knorm_low": G_i(r) = minus that score (smallest kept).
+    Equal scores keep the lower position."""
+    n_a = anchor_count(chunk_len, ra_num, ra_den)
+    if rule == "sink":
+        g = -np.arange(chunk_len, dtype=np.float64)
+    elif rule in ("knorm", "knorm_low"):
+        g = np.asarray(scores, dtype=np.float64)
+        if len(g) != chunk_len:
+            raise ValueError("one score per chunk position")
+        g = g if rule == "knorm" else -g
+    else:
+        raise ValueError("unknown anchor rule " + str(rule))
+    order = np.argsort(-g, kind="stable")  # stable: equal scores keep the lower position first
+    return np.sort(order[:n_a]).astype(np.int32)
+
+
+def anchored_query_scores(model, tokens, n_ctx, k_stitched, v_stitched, anchors, layer_set, ft=np.float32,
+                          return_cache=False):
+    """Anchor-conditioned query probing and critical-layer scoring (QCFuse §3.3.2 Eq. 15-17, §3.4
+    Eq. 18-20). ``anchors``: ascending request positions of the chunk anchors (A_i of each chunk at
+    its request offset, Eq. 15). The query rows U (positions N..L-1) run through the layers with
+    only the anchor rows of the stitched cache as their prefix, each anchor at its original request
+    position (Eq. 16-17: the anchor KV are the re-positioned PIC entries). At each layer l of
+    ``layer_set`` the anchor-conditioned query states score every original context position t
+    against the full stitched context keys (Eq. 18, Eq. 20): the softmax weight of a query row on
+    row t among all context rows and the query rows up to itself, summed over query rows and heads
+    (the weights of the full-view probe, query_scores, read the same way). Returns fp32 [n_ctx]."""
+    cfg = model.cfg
+    tokens = np.asarray(tokens)
+    L, N = len(tokens), int(n_ctx)
+    anchors = np.asarray(anchors, dtype=np.int64)
+    if len(anchors) and (np.any(np.diff(anchors) <= 0) or anchors[0] < 0 or anchors[-1] >= N):
+        raise ValueError("anchors must be strictly increasing context positions")
+    layers = sorted(set(int(l) for l in layer_set))
+    h = np.asarray(model.embed[tokens[N:]], dtype=ft)
+    pos = np.arange(N, L)
+    score = np.zeros(N, dtype=np.float64)
+    kc = np.array(k_stitched, dtype=ft, copy=True)
+    for l in range(max(layers) + 1 if layers else 0):
+        w = model.layer(l)
+        h_next, k_new, v_new = layer_rows_over(cfg, w, h, pos, kc[l][anchors], anchors, v_stitched[l][anchors], ft)
+        if l in layers:  # Eq. 18: the probe's query states against the full context keys of this layer
+            a = rms_norm(h, w.attn_norm, cfg.rms_eps, ft)
+            q = (a @ np.asarray(w.wq, ft).T).reshape(len(pos), cfg.n_q_heads, cfg.head_dim)
+            if cfg.qk_norm:
+                q = rms_norm(q, w.q_norm, cfg.rms_eps, ft)
+            q = rope(q, pos, cfg.rope_theta, ft)
+            kc[l][pos] = k_new
+            score += query_attention_mass(cfg, q, pos, kc[l], N, ft)
+        h = h_next
+    if return_cache:
+        return score.astype(np.float32), kc
     return score.astype(np.float32)
 
 

@@ -106,6 +106,28 @@ def causal_attention(q, q_pos, k_cache, v_cache, ft=np.float32, rnd=None):
     return out
 
 
+def attention_at(q, q_pos, keys, key_pos, values, ft=np.float32):
+    """Softmax attention of queries q [n, Hq, hd] at positions q_pos [n] over a set of cached rows
+    given with their own positions: keys/values [m, Hkv, hd] at key_pos [m] (any order, any gaps);
+    row t is visible to a query at p iff key_pos[t] <= p. Scale 1/sqrt(hd); query head h reads kv
+    head h // (Hq / Hkv). With key_pos = 0..L-1 this is causal_attention."""
+    q = np.asarray(q, dtype=ft)
+    kc = np.asarray(keys, dtype=ft)
+    vc = np.asarray(values, dtype=ft)
+    n, hq, hd = q.shape
+    group = hq // kc.shape[1]
+    visible = np.asarray(key_pos).reshape(1, -1) <= np.asarray(q_pos).reshape(n, 1)
+    scale = ft(1.0 / np.sqrt(hd))
+    out = np.empty((n, hq, hd), dtype=ft)
+    for h in range(hq):
+        g = h // group
+        s = (q[:, h, :] @ kc[:, g, :].T) * scale
+        s = np.where(visible, s, ft(-np.inf))
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (p @ vc[:, g, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 def silu(z):
     return z / (1 + np.exp(-z))
 
@@ -139,6 +161,30 @@ def layer_rows(cfg, w, h_rows, pos, k_cache, v_cache, ft=np.float32, bf16_ops=No
     b = _r(rnd, rms_norm(h1, w.mlp_norm, eps, ft), ft)
     act = silu(b @ np.asarray(w.w_gate, ft).T) * (b @ np.asarray(w.w_up, ft).T)
     return h1 + _r(rnd, act, ft) @ np.asarray(w.w_down, ft).T
+
+
+def layer_rows_over(cfg, w, h_rows, pos, keys, key_pos, values, ft=np.float32):
+    """One decoder layer applied to the rows ``h_rows`` [n, d] at positions ``pos`` when the cache
+    they read is a set of rows with explicit positions (keys/values [m, Hkv, hd] at key_pos [m])
+    rather than rows 0..L-1: the rows' fresh K/V join that set at their own positions before the
+    attention, as in layer_rows. Returns (layer output [n, d], fresh K, fresh V)."""
+    n = h_rows.shape[0]
+    hq, hkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    eps = cfg.rms_eps
+    a = rms_norm(h_rows, w.attn_norm, eps, ft)
+    q = (a @ np.asarray(w.wq, ft).T).reshape(n, hq, hd)
+    if cfg.qk_norm:
+        q = rms_norm(q, w.q_norm, eps, ft)
+    q = rope(q, pos, cfg.rope_theta, ft)
+    k, v = kv_rows(cfg, w, h_rows, pos, ft)
+    ks = np.concatenate([np.asarray(keys, ft), k])
+    vs = np.concatenate([np.asarray(values, ft), v])
+    kp = np.concatenate([np.asarray(key_pos, np.int64), np.asarray(pos, np.int64)])
+    o = attention_at(q, pos, ks, kp, vs, ft).reshape(n, hq * hd)
+    h1 = np.asarray(h_rows, ft) + o @ np.asarray(w.wo, ft).T
+    b = rms_norm(h1, w.mlp_norm, eps, ft)
+    act = silu(b @ np.asarray(w.w_gate, ft).T) * (b @ np.asarray(w.w_up, ft).T)
+    return h1 + act @ np.asarray(w.w_down, ft).T, k, v
 
 
 def k_rows(cfg, w, h_rows, pos, ft=np.float32, bf16_ops=None):

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libcf.so")
 CF_OK, CF_EINVAL, CF_ESHAPE, CF_EDTYPE, CF_EUNSUPPORTED, CF_EWORKSPACE, CF_EHIP = range(7)
 CF_F32, CF_BF16 = 0, 1
 CF_SEL_TOKEN_TOPK, CF_SEL_DOC_SPANS, CF_SEL_ALL, CF_SEL_RANKED_SPANS, CF_SEL_SPAN_HEADS, CF_SEL_GIVEN = range(6)
+ANCHOR_RULES = {"sink": 0, "knorm": 1, "knorm_low": 2}
 MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL, "ranked": CF_SEL_RANKED_SPANS,
          "heads": CF_SEL_SPAN_HEADS, "given": CF_SEL_GIVEN}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
@@ -26,7 +27,8 @@ EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf
            "cf_blend_prefill_streamed_workspace_size", "cf_blend_prefill_streamed", "cf_query_scores_workspace_size",
            "cf_query_scores", "cf_selection_deviation_workspace_size", "cf_selection_deviation",
            "cf_budget", "cf_gradual_schedule", "cf_loading_ratio", "cf_single_window_bounds",
-           "cf_fixed_chunk_bounds", "cf_selection_stats",
+           "cf_fixed_chunk_bounds", "cf_selection_stats", "cf_key_norms", "cf_anchor_positions",
+           "cf_query_scores_anchored_workspace_size", "cf_query_scores_anchored",
            "cf_profile_enable", "cf_profile_report", "cf_mfma_loop", "cf_copy_loop"]
 
 
@@ -95,6 +97,11 @@ def lib() -> ctypes.CDLL:
         "cf_single_window_bounds": (i32, [i32, vp, i32, ctypes.POINTER(i32)]),
         "cf_fixed_chunk_bounds": (i32, [i32, i32, i32, vp, i32, ctypes.POINTER(i32)]),
         "cf_selection_stats": (i32, [vp, i32, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double)]),
+        "cf_key_norms": (i32, [vp, vp, i64, i32, i32, i32, vp, vp]),
+        "cf_anchor_positions": (i32, [i32, vp, i32, i32, i32, vp, i32, vp, i32, ctypes.POINTER(i32)]),
+        "cf_query_scores_anchored_workspace_size": (sz, [vp, i32, i32, i32]),
+        "cf_query_scores_anchored": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, i32, i32, vp, vp, i64, vp, i32,
+                                           vp, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -343,6 +350,41 @@ class Context:
                                      _ptr(v_cache), ols, lset, nset, _ptr(scores), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(tokens.device)))
 
+    def key_norms(self, k_store, norms, layer_begin: int = 0, layer_end: Optional[int] = None,
+                  store_rows: Optional[int] = None, store_layer_stride: Optional[int] = None):
+        """cf_key_norms: norms (fp32 [store_rows]) = squared key norm of each store row over the layers."""
+        le = self.cfg.n_layers if layer_end is None else layer_end
+        sr = store_rows if store_rows is not None else k_store.shape[-2]
+        sls = store_layer_stride if store_layer_stride is not None else sr * self.kv_dim
+        if sr > 0 and le > layer_begin:
+            _room(k_store, (le - 1) * sls + sr * self.kv_dim, "k_store", self._tdt())
+            _room(norms, sr, "norms", _torch().float32)
+        _check(lib().cf_key_norms(self.handle, _ptr(k_store), sls, sr, layer_begin, le, _ptr(norms),
+                                  _stream(norms.device)))
+
+    def query_scores_anchored_workspace_size(self, N: int, U: int, n_anchors: int) -> int:
+        return int(lib().cf_query_scores_anchored_workspace_size(self.handle, N, U, n_anchors))
+
+    def query_scores_anchored(self, layers, embed, tokens, N: int, U: int, k_cache, v_cache, anchors,
+                              layer_set: Sequence[int], scores, ws, out_layer_stride: Optional[int] = None):
+        """cf_query_scores_anchored: the query rows probe only the anchor rows (device int32 tensor of
+        ascending context positions) of the stitched cache; scores as in query_scores."""
+        torch = _torch()
+        lset, nset = _host_i32(list(layer_set))
+        ols = out_layer_stride if out_layer_stride is not None else (N + U) * self.kv_dim
+        ext = (self.cfg.n_layers - 1) * ols + (N + U) * self.kv_dim
+        n_a = 0 if anchors is None else int(anchors.numel())
+        _room(tokens, N + U, "tokens", torch.int32)
+        _room(embed, self.cfg.vocab * self.cfg.d_model, "embed", self._tdt())
+        _room(k_cache, ext, "k_cache", self._tdt())
+        _room(v_cache, ext, "v_cache", self._tdt())
+        _room(anchors, n_a, "anchors", torch.int32)
+        _room(scores, N, "scores", torch.float32)
+        _check(lib().cf_query_scores_anchored(self.handle, layers, _ptr(embed), _ptr(tokens), N, U, _ptr(k_cache),
+                                              _ptr(v_cache), ols, _ptr(anchors) if n_a else None, n_a, lset, nset,
+                                              _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel(),
+                                              _stream(tokens.device)))
+
     def blend_prefill_streamed_workspace_size(self, N: int, U: int, k: int, mode: str, store_rows: int) -> int:
         return int(lib().cf_blend_prefill_streamed_workspace_size(self.handle, N, U, k, MODES[mode], store_rows))
 
@@ -493,3 +535,23 @@ def selection_stats(sel: Sequence[int], dev) -> tuple:
                                     d.ctypes.data if d.size else None, int(d.size), ctypes.byref(seg),
                                     ctypes.byref(cap)))
     return int(seg.value), float(cap.value)
+
+
+def anchor_positions(rule: str, chunk_tab, ratio=(1, 10), scores=None, store_rows: int = 0) -> List[int]:
+    """cf_anchor_positions: request positions of the chunk anchors (QCFuse Eq. 14-15), ascending.
+    rule "sink", "knorm" or "knorm_low"; scores: host fp32 array-like of per-store-row key norms."""
+    import numpy as np
+    tab, nflat = _host_i32(chunk_tab)
+    sc = None if scores is None else np.ascontiguousarray(np.asarray(scores, dtype=np.float32).ravel())
+    sr = int(store_rows) if sc is None else max(int(store_rows), int(sc.size))
+    nb = ctypes.c_int32(0)
+    cap = 64
+    while True:
+        out = (ctypes.c_int32 * cap)()
+        st = lib().cf_anchor_positions(ANCHOR_RULES[rule], tab, nflat // 4, int(ratio[0]), int(ratio[1]),
+                                       None if sc is None else sc.ctypes.data, sr, out, cap, ctypes.byref(nb))
+        if st == CF_OK:
+            return [int(out[i]) for i in range(nb.value)]
+        if nb.value <= cap:
+            _check(st)
+        cap = int(nb.value)

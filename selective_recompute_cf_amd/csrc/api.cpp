@@ -245,7 +245,7 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
                     const int* sel, int n, int L, char* ws, const LayerWs& lw, hipStream_t st,
                     bool x_ready = false, const float* next_norm = nullptr, bool* x_next = nullptr,
                     bool* sched_ready = nullptr, float* dev_heads = nullptr, int n_dev = 0,
-                    const MassHook* mass = nullptr) {
+                    const MassHook* mass = nullptr, int rope_off = 0) {
   if (x_next) *x_next = false;
   if (n == 0) return CF_OK;
   const cf_model_cfg& m = c->cfg;
@@ -275,7 +275,7 @@ cf_status run_layer(const cf_ctx* c, const cf_layer_weights* w, float* hidden, v
   qp.hq = m.n_q_heads; qp.hkv = m.n_kv_heads; qp.hd = hd; qp.qk_norm = m.qk_norm;
   qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = m.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
   qp.q_out = Q; qp.k_cache = kc; qp.v_cache = vc;
-  qp.dev_heads = dev_heads; qp.n_dev = dev_heads ? n_dev : 0;
+  qp.dev_heads = dev_heads; qp.n_dev = dev_heads ? n_dev : 0; qp.rope_off = rope_off;
   CF_RUN("qkv_post", cf::launch_qkv_post(dt, qp, st));
 
   cf::AttnArgs at{};
@@ -1066,6 +1066,150 @@ cf_status cf_query_scores(const cf_ctx* c, const cf_layer_weights* layers, const
       return s;
     xr = xn;
     if (scored) ++set_i;
+  }
+  return CF_OK;
+}
+
+cf_status cf_key_norms(const cf_ctx* c, const void* k_store, int64_t sls, int32_t store_rows, int32_t lb, int32_t le,
+                       float* norms, hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  const int64_t kvd = (int64_t)c->cfg.n_kv_heads * c->cfg.head_dim;
+  CF_CHECK(lb >= 0 && lb < le && le <= c->cfg.n_layers, CF_EINVAL, "layer range [%d, %d) outside [0, %d] or empty", lb,
+           le, c->cfg.n_layers);
+  CF_CHECK(store_rows >= 0, CF_EINVAL, "negative row count");
+  if (store_rows == 0) return CF_OK;
+  CF_CHECK(k_store && norms, CF_EINVAL, "null pointer");
+  CF_CHECK(sls >= store_rows * kvd, CF_ESHAPE, "store_layer_stride must hold store_rows * kvd elements");
+  DeviceGuard guard(c->device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  CF_RUN("key_norms", cf::launch_key_norms(dt_of(c), k_store, sls, store_rows, (int)kvd, lb, le, norms, st));
+  return CF_OK;
+}
+
+namespace {
+
+struct AnchoredWs {
+  size_t hidden, sel, pos, kc, vc, ml, part, sched, layer, total;
+};
+
+AnchoredWs anchored_ws(const cf_ctx* c, int N, int U, int n_a) {
+  const int R = n_a + U;
+  const size_t kvd = (size_t)c->cfg.n_kv_heads * c->cfg.head_dim;
+  AnchoredWs p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  p.hidden = take((size_t)R * c->cfg.d_model * 4);
+  p.sel = take((size_t)U * 4);
+  p.pos = take((size_t)U * 4);
+  p.kc = take((size_t)R * kvd * esize(c));
+  p.vc = take((size_t)R * kvd * esize(c));
+  p.ml = take((size_t)U * c->cfg.n_q_heads * 2 * 4);
+  p.part = take((size_t)c->cfg.n_kv_heads * N * 4);
+  p.sched = take(sizeof(cf::AttnSched));
+  p.layer = take(layer_ws(c, R, U).total);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+size_t cf_query_scores_anchored_workspace_size(const cf_ctx* c, int32_t N, int32_t U, int32_t n_anchors) {
+  if (!c || N <= 0 || U <= 0 || n_anchors < 0 || n_anchors > N) return 0;
+  return anchored_ws(c, N, U, n_anchors).total;
+}
+
+cf_status cf_query_scores_anchored(const cf_ctx* c, const cf_layer_weights* layers, const void* embed,
+                                   const int32_t* tokens, int32_t N, int32_t U, void* k_cache, void* v_cache,
+                                   int64_t ols, const int32_t* anchors, int32_t n_a, const int32_t* layer_set,
+                                   int32_t n_set, float* scores, void* ws, size_t ws_bytes, hipStream_t st) {
+  g_err.clear();
+  if (cf_status s = check_ctx(c)) return s;
+  const cf_model_cfg& mc = c->cfg;
+  const int L = N + U, R = n_a + U;
+  const int64_t kvd = (int64_t)mc.n_kv_heads * mc.head_dim;
+  const int qd = mc.n_q_heads * mc.head_dim;
+  CF_CHECK(N > 0 && U > 0, CF_EINVAL, "need N > 0 context rows and U > 0 query rows");
+  CF_CHECK(n_a >= 0 && n_a <= N, CF_EINVAL, "anchor count %d outside [0, N=%d]", n_a, N);
+  CF_CHECK(n_a == 0 || anchors, CF_EINVAL, "null anchor array");
+  CF_CHECK(L <= c->max_pos, CF_EINVAL, "L=%d exceeds max_pos=%d", L, c->max_pos);
+  CF_CHECK(layer_set && n_set > 0, CF_EINVAL, "empty layer set");
+  for (int i = 0; i < n_set; ++i)
+    CF_CHECK(layer_set[i] >= 0 && layer_set[i] < mc.n_layers && (i == 0 || layer_set[i] > layer_set[i - 1]), CF_EINVAL,
+             "layer set must be strictly increasing layer ids in [0, %d)", mc.n_layers);
+  const int last = layer_set[n_set - 1];
+  for (int l = 0; l <= last; ++l)
+    if (cf_status s = check_layer(c, layers + l, l)) return s;
+  CF_CHECK(embed && tokens && scores && aligned16(embed), CF_EINVAL, "null or misaligned embed, tokens or scores");
+  CF_CHECK(k_cache && v_cache && aligned16(k_cache) && aligned16(v_cache), CF_EINVAL, "cache null or misaligned");
+  CF_CHECK(ols >= L * kvd && ols % 8 == 0, CF_ESHAPE, "layer stride must be >= L*kvd and a multiple of 8");
+  const AnchoredWs pw = anchored_ws(c, N, U, n_a);
+  CF_CHECK(ws && aligned16(ws) && ws_bytes >= pw.total, CF_EWORKSPACE, "workspace: need %zu bytes, got %zu", pw.total,
+           ws_bytes);
+  DeviceGuard guard(c->device);
+  CF_CHECK(guard.ok, CF_EHIP, "hipSetDevice failed");
+  char* W = static_cast<char*>(ws);
+  float* hidden = reinterpret_cast<float*>(W + pw.hidden);
+  int* sel = reinterpret_cast<int*>(W + pw.sel);   // the query rows in the compact cache: n_a .. R-1
+  int* pos = reinterpret_cast<int*>(W + pw.pos);   // their request positions: N .. L-1
+  char* kc = W + pw.kc;
+  char* vc = W + pw.vc;
+  float* ml = reinterpret_cast<float*>(W + pw.ml);
+  cf::AttnSched* sched2 = reinterpret_cast<cf::AttnSched*>(W + pw.sched);
+  char* lws = W + pw.layer;
+  const LayerWs lw = layer_ws(c, R, U);
+  const cf::Dt dt = dt_of(c);
+  const size_t es = esize(c);
+  // the query rows: embeddings into compact rows n_a.., RoPE at their request positions N..
+  CF_RUN("embed", cf::launch_embed(dt, tokens + N, U, embed, mc.vocab, mc.d_model, hidden + (size_t)n_a * mc.d_model,
+                                   st));
+  CF_RUN("iota", cf::launch_iota(sel, U, n_a, st));
+  CF_RUN("iota", cf::launch_iota(pos, U, N, st));
+  bool xr = false, sched = false, sched_score = false;
+  int set_i = 0;
+  for (int l = 0; l <= last; ++l) {
+    char* kl = static_cast<char*>(k_cache) + (size_t)l * ols * es;
+    char* vl = static_cast<char*>(v_cache) + (size_t)l * ols * es;
+    // compact anchor cache of this layer (QCFuse Eq. 16): the stitched rows at the anchors, whose
+    // keys already carry the anchors' request positions; the query rows follow them
+    CF_RUN("gather_rows", cf::launch_gather_rows(dt, kl, kvd, N, anchors, n_a, (int)kvd, kc, kvd, st));
+    CF_RUN("gather_rows", cf::launch_gather_rows(dt, vl, kvd, N, anchors, n_a, (int)kvd, vc, kvd, st));
+    const bool scored = set_i < n_set && layer_set[set_i] == l;
+    const float* nn = l < last ? layers[l + 1].attn_norm : nullptr;
+    bool xn = false;
+    // the probe (Eq. 17): the query rows over the anchors and themselves, positions N.. for RoPE
+    if (cf_status s = run_layer(c, layers + l, hidden, kc, vc, sel, U, R, lws, lw, st, xr, nn, &xn, &sched, nullptr,
+                                0, nullptr, N - n_a))
+      return s;
+    xr = xn;
+    if (!scored) continue;
+    ++set_i;
+    // scoring (Eq. 18, Eq. 20): the probe's query states of this layer against the full stitched
+    // context keys; the query rows' own keys go to rows N..L-1 of the caller's cache, as in the
+    // full-view probe, and their softmax runs over the context rows and the query rows up to each
+    CF_RUN("gather_rows", cf::launch_gather_rows(dt, kc + (size_t)n_a * kvd * es, kvd, U, nullptr, U, (int)kvd,
+                                                 kl + (size_t)N * kvd * es, kvd, st));
+    CF_RUN("gather_rows", cf::launch_gather_rows(dt, vc + (size_t)n_a * kvd * es, kvd, U, nullptr, U, (int)kvd,
+                                                 vl + (size_t)N * kvd * es, kvd, st));
+    cf::AttnArgs at{};
+    at.dt = dt; at.q = lws + lw.q; at.ldq = qd; at.pos = pos; at.n = U; at.k = kl; at.v = vl; at.L = L;
+    at.hq = mc.n_q_heads; at.hkv = mc.n_kv_heads; at.hd = mc.head_dim; at.out = lws + lw.ao; at.ldo = qd;
+    at.o_part = reinterpret_cast<float*>(lws + lw.opart);
+    at.ml_part = reinterpret_cast<float*>(lws + lw.mlpart);
+    if (lw.plan.attn_P > 0) {
+      at.P = lw.plan.attn_P;
+      if (!sched_score) CF_RUN("attn_sched", cf::launch_attention_sched(at, sched2, st));
+      sched_score = true;
+      at.sched = sched2;
+    }
+    at.ml_out = ml;
+    CF_RUN("attention", cf::launch_attention(at, st));
+    if (at.sched) CF_RUN("attn_merge", cf::launch_attention_merge(at, st));
+    cf::QMassArgs qm{};
+    qm.q = lws + lw.q; qm.ldq = qd; qm.n = U; qm.k = kl; qm.n_ctx = N;
+    qm.hq = mc.n_q_heads; qm.hkv = mc.n_kv_heads; qm.hd = mc.head_dim;
+    qm.ml = ml; qm.part = reinterpret_cast<float*>(W + pw.part); qm.score = scores;
+    CF_RUN("query_mass", cf::launch_query_mass(dt, qm, set_i == 1 ? 1 : 0, st));
   }
   return CF_OK;
 }

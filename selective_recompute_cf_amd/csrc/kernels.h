@@ -41,6 +41,7 @@ struct QkvPost {
   float* dev; const void* k_ref;
   int splits; int64_t split_stride;    // qkv holds `splits` partial sums, split_stride floats apart
   float* dev_heads; int n_dev;
+  int rope_off;                        // RoPE position = stored row + rope_off (0: the row itself)
 };
 hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st);
 // dev[j] = sum over h < hkv of dev_heads[j * hkv + h], in head order (j < n).
@@ -65,6 +66,14 @@ hipError_t launch_reduce_resid_norm(Dt dt, const float* part, int splits, int M,
 hipError_t launch_swiglu(Dt dt, const float* gu, int M, int F, void* act, hipStream_t st);
 hipError_t launch_deviation(Dt dn, const void* a, int64_t lda, Dt dr, const void* b, int64_t ldb,
                             float* dev, int n, int kvd, hipStream_t st);
+// dst[j] = src[idx ? idx[j] (clamped to [0, src_rows)) : j] for j < n; rows of row_elems elements
+// (row_elems * element size a multiple of 16 bytes), leading dimensions in elements.
+hipError_t launch_gather_rows(Dt dt, const void* src, int64_t src_ld, int src_rows, const int* idx, int n,
+                              int row_elems, void* dst, int64_t dst_ld, hipStream_t st);
+// norms[r] = sum over layers [lb, le) of the squared entries of K[l][r] (rows of kvd elements,
+// layers sls elements apart), fp32.
+hipError_t launch_key_norms(Dt dt, const void* k, int64_t sls, int rows, int kvd, int lb, int le, float* norms,
+                            hipStream_t st);
 
 // ----------------------------------------------------------------- measurement (probe.hip)
 // Launches blocks x 256 threads of the MFMA loop; returns its flop count.

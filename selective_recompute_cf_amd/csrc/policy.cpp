@@ -1,5 +1,6 @@
 // libcf host-side policy arithmetic: the recompute budget, the gradual-filtering schedule, the
-// loading controller, the span bounds of the span-policy ablations and the selection diagnostics.
+// loading controller, the span bounds of the span-policy ablations, the chunk-anchor positions and
+// the selection diagnostics.
 // These are plain host computations on host arrays (no device memory, no stream); they live in the
 // library so that every step of the method, including its integer bookkeeping, is one C call.
 #include <algorithm>
@@ -100,6 +101,44 @@ cf_status cf_fixed_chunk_bounds(int32_t n_ctx, int32_t size, int32_t offset, int
   *n_bounds = (int32_t)b.size();
   if ((int64_t)b.size() > cap) return bad(CF_EINVAL, "bounds array too small (n_bounds holds the size needed)");
   std::copy(b.begin(), b.end(), bounds);
+  return CF_OK;
+}
+
+cf_status cf_anchor_positions(int32_t rule, const int32_t* chunk_tab, int32_t m, int32_t ra_num, int32_t ra_den,
+                              const float* scores, int32_t store_rows, int32_t* anchors, int32_t cap,
+                              int32_t* n_anchors) {
+  cf::clear_error();
+  if (!n_anchors || m < 0 || (m > 0 && !chunk_tab) || (cap > 0 && !anchors)) return bad(CF_EINVAL, "bad arguments");
+  if (rule != CF_ANCHOR_SINK && rule != CF_ANCHOR_KNORM && rule != CF_ANCHOR_KNORM_LOW)
+    return bad(CF_EINVAL, "unknown anchor rule");
+  if (!ratio_ok(ra_num, ra_den)) return bad(CF_EINVAL, "anchor ratio must be num/den with 0 <= num <= den, den > 0");
+  if (rule != CF_ANCHOR_SINK && !scores) return bad(CF_EINVAL, "key-norm anchors need the per-row scores");
+  std::vector<int32_t> out;
+  std::vector<int32_t> idx;
+  for (int32_t i = 0; i < m; ++i) {
+    const int32_t row = chunk_tab[4 * i], dst = chunk_tab[4 * i + 2], len = chunk_tab[4 * i + 3];
+    if (len <= 0 || row < 0 || dst < 0 || (rule != CF_ANCHOR_SINK && (int64_t)row + len > store_rows))
+      return bad(CF_EINVAL, "chunk rows outside the store or empty chunk");
+    const int64_t n_a = ((int64_t)len * ra_num + ra_den - 1) / ra_den;  // ceil(r_a |c_i|)
+    idx.resize(len);
+    for (int32_t r = 0; r < len; ++r) idx[r] = r;
+    if (rule != CF_ANCHOR_SINK) {
+      // TopK of the score (largest norm, or smallest for the low rule); equal scores keep the lower
+      // position; NaN ranks as +inf
+      const float* g = scores + row;
+      const bool low = rule == CF_ANCHOR_KNORM_LOW;
+      auto key = [&](int32_t r) { const double v = g[r]; return std::isnan(v) ? INFINITY : (low ? -v : v); };
+      std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return key(a) > key(b); });
+    }
+    std::sort(idx.begin(), idx.begin() + n_a);
+    for (int64_t r = 0; r < n_a; ++r) out.push_back(dst + idx[r]);
+  }
+  std::sort(out.begin(), out.end());
+  for (size_t i = 1; i < out.size(); ++i)
+    if (out[i] == out[i - 1]) return bad(CF_EINVAL, "chunk destinations overlap");
+  *n_anchors = (int32_t)out.size();
+  if ((int64_t)out.size() > cap) return bad(CF_EINVAL, "anchor array too small (n_anchors holds the size needed)");
+  std::copy(out.begin(), out.end(), anchors);
   return CF_OK;
 }
 

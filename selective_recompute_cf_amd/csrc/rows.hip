@@ -168,8 +168,9 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPost p) {
     for (int s2 = 1; s2 < splits; ++s2) v += src[s2 * sst + c];
     return v;
   };
-  const float c = lane < half ? p.cos_t[(int64_t)pos * half + lane] : 0.f;
-  const float s = lane < half ? p.sin_t[(int64_t)pos * half + lane] : 0.f;
+  const int64_t rp = (int64_t)pos + p.rope_off;  // RoPE position (the stored row plus an offset)
+  const float c = lane < half ? p.cos_t[rp * half + lane] : 0.f;
+  const float s = lane < half ? p.sin_t[rp * half + lane] : 0.f;
   const int nq = devmode ? 0 : p.hq;
   const int nkv = p.hkv;
   const int nh = nq + nkv + (devmode ? 0 : nkv);
@@ -271,8 +272,9 @@ __global__ __launch_bounds__(256) void qkv_post_vec_kernel(QkvPost p) {
     x2.x = x2.x * inv * gn[e + HALF], x2.y = x2.y * inv * gn[e + HALF + 1], x2.z = x2.z * inv * gn[e + HALF + 2];
     x2.w = x2.w * inv * gn[e + HALF + 3];
   }
-  const float4 c = *reinterpret_cast<const float4*>(p.cos_t + (int64_t)pos * HALF + e);
-  const float4 sn = *reinterpret_cast<const float4*>(p.sin_t + (int64_t)pos * HALF + e);
+  const int64_t rp = (int64_t)pos + p.rope_off;  // RoPE position (the stored row plus an offset)
+  const float4 c = *reinterpret_cast<const float4*>(p.cos_t + rp * HALF + e);
+  const float4 sn = *reinterpret_cast<const float4*>(p.sin_t + rp * HALF + e);
   T* dst = isq ? (T*)p.q_out + (int64_t)j * (nq * HD) + hh * HD : (T*)p.k_cache + (int64_t)pos * kvd + hh * HD;
   const float y1[4] = {x1.x * c.x - x2.x * sn.x, x1.y * c.y - x2.y * sn.y, x1.z * c.z - x2.z * sn.z,
                        x1.w * c.w - x2.w * sn.w};
@@ -316,6 +318,60 @@ hipError_t launch_qkv_post(Dt dt, const QkvPost& p, hipStream_t st) {
     hipLaunchKernelGGL(qkv_post_kernel<bf16>, grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(qkv_post_kernel<float>, grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// dst[j] = src[idx ? clamp(idx[j]) : j] for j < n, rows of row16 16-byte words: a 256-thread block
+// copies 4 rows, one wave per row, with 16-byte accesses.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src, int64_t src_ld,
+                                                          int src_rows, const int* __restrict__ idx, int n,
+                                                          int row16, char* __restrict__ dst, int64_t dst_ld) {
+  const int j = blockIdx.x * 4 + threadIdx.x / 64;
+  if (j >= n) return;
+  const int r = idx ? clampi(idx[j], 0, src_rows - 1) : j;
+  const uint4* s = reinterpret_cast<const uint4*>(src + (int64_t)r * src_ld);
+  uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)j * dst_ld);
+  for (int e = threadIdx.x % 64; e < row16; e += 64) d[e] = s[e];
+}
+
+hipError_t launch_gather_rows(Dt dt, const void* src, int64_t src_ld, int src_rows, const int* idx, int n,
+                              int row_elems, void* dst, int64_t dst_ld, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int es = dt == BF16 ? 2 : 4;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((n + 3) / 4), dim3(256), 0, st, (const char*)src, src_ld * es,
+                     src_rows, idx, n, row_elems * es / 16, (char*)dst, dst_ld * es);
+  return hipGetLastError();
+}
+
+// norms[r] = sum over layers [lb, le) and the kvd entries of K[l][r]^2 (fp32, layer by layer, each
+// row's entries summed across one wave): one wave per store row.
+template <typename T>
+__global__ __launch_bounds__(256) void key_norms_kernel(const T* __restrict__ k, int64_t sls, int rows, int kvd,
+                                                        int lb, int le, float* __restrict__ norms) {
+  const int r = blockIdx.x * 4 + threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+  if (r >= rows) return;
+  float acc = 0.f;
+  for (int l = lb; l < le; ++l) {
+    const T* row = k + (int64_t)l * sls + (int64_t)r * kvd;
+    float part = 0.f;
+    for (int c = lane; c < kvd; c += WAVE) {
+      const float x = to_f(row[c]);
+      part += x * x;
+    }
+    acc += wave_sum(part);
+  }
+  if (lane == 0) norms[r] = acc;
+}
+
+hipError_t launch_key_norms(Dt dt, const void* k, int64_t sls, int rows, int kvd, int lb, int le, float* norms,
+                            hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL(key_norms_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, st, (const bf16*)k, sls, rows,
+                       kvd, lb, le, norms);
+  else
+    hipLaunchKernelGGL(key_norms_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)k, sls, rows,
+                       kvd, lb, le, norms);
   return hipGetLastError();
 }
 

@@ -6,19 +6,19 @@ every row, the selection-layer deviation (cf_selection_deviation) and selection 
 then cf_blend_layer on the selected rows and the query rows at every later layer. Before each
 checked layer the GPU's own inputs (the fp32 residual rows and the layer's K/V cache) are copied
 to the host, and the oracle runs that one layer on exactly those inputs in fp32
-(QCFuse §2.1.3 Eq. 7; CacheBlend, "Selective Recompute Without Skipping"). The GPU's outputs must
-then meet the element-wise bf16 bar |gpu - oracle| <= 2e-2 + 1e-2 |oracle| at every element of:
-* the fresh K and V of every recomputed row, against the fp32 oracle (oracle.kv_rows on the same
-  input rows);
-* the layer output (the fp32 residual rows) of the recomputed rows, against the oracle's layer in
-  its bf16-arithmetic mode (oracle.layer_rows with bf16_ops: the operands a BF16 stack rounds are
-  rounded, sums stay fp32; that mode is pinned against an independent torch decoder). Against the
-  fp32 oracle the hidden rows cannot meet the bar: one bf16 layer at Llama-3-8B width lands 8.9e-3
-  norm-wise from fp32 with about 12% of the elements outside it, whatever the implementation, so
-  there the GPU must stay within 1.25x the bf16 arithmetic's own norm-wise distance, and the
-  element counts are printed. For layers with many rows the layer output is checked on a seeded
-  sample of rows, each computed by the oracle against the GPU's cache, whose recomputed rows have
-  just been held to the K/V bar;
+(QCFuse §2.1.3 Eq. 7; CacheBlend, "Selective Recompute Without Skipping"). Then:
+* the fresh K and V of every recomputed row must meet the element-wise bf16 bar
+  |gpu - oracle| <= 2e-2 + 1e-2 |oracle| at every element, against the fp32 oracle (oracle.kv_rows
+  on the same input rows);
+* the layer output (the fp32 residual rows) cannot meet that bar against the fp32 oracle with any
+  bf16 arithmetic: one bf16 layer at Llama-3-8B width lands 8.9e-3 norm-wise from fp32, with about
+  12% of the elements outside the bar, in the oracle's own bf16-arithmetic evaluation
+  (oracle.layer_rows with bf16_ops, pinned against an independent torch decoder that rounds the same
+  operands). The GPU's hidden rows are therefore held to that floor: norm-wise within 1.25x of it,
+  and every head-sized piece of every row within 2x of the floor there (hidden_vs_floor), with the
+  element counts printed. For layers with many rows the layer output is checked on a seeded sample
+  of rows, each computed by the oracle against the GPU's cache, whose recomputed rows have just
+  been held to the K/V bar;
 and rows outside the set must keep their hidden state and cache entries bit for bit.
 
 At the selection layer the oracle recomputes the current keys of every context row from the GPU's
@@ -90,12 +90,43 @@ def elementwise(name, gpu, ref, atol=ATOL, rtol=RTOL, stats=None):
 # How far beyond the distance of bf16 arithmetic itself (the oracle's bf16 mode, pinned against an
 # independent torch decoder that rounds the same operands) a layer's hidden rows may land from fp32.
 H_FLOOR_FACTOR = 1.25
+H_CHUNK_FACTOR = 2.0
 
 
 def _nrel(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def hidden_vs_floor(name, gpu, f32, b16, chunk):
+    """The GPU's hidden rows against the fp32 oracle, measured against the distance that BF16
+    arithmetic itself puts between the two (b16: the oracle's bf16-arithmetic evaluation of the same
+    layer on the same inputs, pinned against an independent torch decoder). The GPU rounds at the
+    same points but not always the same values (its softmax weights are exponentiated against a
+    running maximum, not the row's final one), so it is compared with the floor's size, not with its
+    values: norm-wise within 1.25x of the floor, and no `chunk`-element piece of any row further
+    than 2x the larger of the floor there and the floor's median piece (a wrong row, head or tile
+    is caught). Element counts outside (2e-2, 1e-2) are printed for both."""
+    g = np.asarray(gpu, np.float64)
+    f = np.asarray(f32, np.float64)
+    b = np.asarray(b16, np.float64)
+    assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
+    e_gpu, e_bf = _nrel(g, f), _nrel(b, f)
+    n_c = g.size // chunk
+    eg = np.linalg.norm((g - f).reshape(n_c, chunk), axis=1)
+    eb = np.linalg.norm((b - f).reshape(n_c, chunk), axis=1)
+    floor = np.maximum(eb, np.median(eb))
+    worst = float((eg / floor).max())
+    bar = ATOL + RTOL * np.abs(f)
+    miss_g, miss_b = int((np.abs(g - f) > bar).sum()), int((np.abs(b - f) > bar).sum())
+    say(f"    {name} vs fp32 oracle: norm_rel={e_gpu:.3e} (bf16 arithmetic itself {e_bf:.3e}, ratio "
+        f"{e_gpu / max(e_bf, 1e-30):.3f}); worst {chunk}-chunk / floor {worst:.3f}; elements outside (2e-2, 1e-2): "
+        f"{miss_g}/{g.size} (bf16 arithmetic itself {miss_b})")
+    assert e_gpu <= H_FLOOR_FACTOR * e_bf + 1e-6, f"{name}: further from fp32 than bf16 arithmetic"
+    assert worst <= H_CHUNK_FACTOR, f"{name}: a {chunk}-element piece is {worst:.2f}x the bf16 floor there"
+    return dict(norm_rel=e_gpu, bf16_norm_rel=e_bf, worst_chunk_over_floor=worst, misses=miss_g,
+                bf16_misses=miss_b, n=int(g.size))
 
 
 def _select(mode, d, k, spans):
@@ -203,17 +234,7 @@ def teacher_forced(ctx, dm, keep, tokens, N, k, mode, spans, k_store, v_store, t
                 kc_t, vc_t = kc_out.copy(), vc_out.copy()
             h_ref[bf] = oracle.layer_rows(cfg, W, h_in[rows[S]], rows[S], kc_t, vc_t, bf16_ops=bf)
         g = h_out[rows[S]]
-        elementwise(f"layer {l} h vs bf16-arithmetic oracle ({len(S)} rows)", g, h_ref[True], stats=st)
-        # against fp32: the GPU may add little beyond the distance of BF16 arithmetic itself
-        e_gpu = _nrel(g, h_ref[False])
-        e_bf = _nrel(h_ref[True], h_ref[False])
-        bad = np.abs(g - h_ref[False]) > ATOL + RTOL * np.abs(h_ref[False])
-        bad16 = np.abs(h_ref[True] - h_ref[False]) > ATOL + RTOL * np.abs(h_ref[False])
-        st["h_fp32"] = dict(norm_rel=e_gpu, bf16_arith_norm_rel=e_bf, misses=int(bad.sum()),
-                            bf16_arith_misses=int(bad16.sum()), n=int(bad.size))
-        say(f"    layer {l} h vs fp32 oracle: norm_rel={e_gpu:.3e} (bf16 arithmetic itself {e_bf:.3e}); "
-            f"elements outside (2e-2, 1e-2): {int(bad.sum())}/{bad.size} (bf16 arithmetic itself {int(bad16.sum())})")
-        assert e_gpu <= H_FLOOR_FACTOR * e_bf + 1e-5, f"layer {l}: h is further from fp32 than bf16 arithmetic allows"
+        st["h"] = hidden_vs_floor(f"layer {l} h ({len(S)} rows)", g, h_ref[False], h_ref[True], cfg.head_dim)
         out[l] = st
     if prefill:
         torch.cuda.synchronize()

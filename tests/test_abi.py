@@ -243,3 +243,32 @@ def test_oracle_only_reached_from_tests_smoke_and_cpu_baseline():
                 assert _oracle_imports(os.path.join(dirpath, f)) == [], f
     assert {fn for fn, _ in _oracle_imports(os.path.join(root, "bench.py"))} <= {"cpu_baseline"}
     assert {fn for fn, _ in _oracle_imports(os.path.join(root, "__graft_entry__.py"))} <= {"smoke"}
+
+
+def test_anchor_positions_host_logic_agrees_with_oracle():
+    """cf_anchor_positions (QCFuse Eq. 14-15) against oracle.select_anchors chunk by chunk: Sink and
+    both key-norm directions, ragged chunks stored out of request order, integer-valued scores with
+    many ties (lower position first), anchor ratios from 0 to 1."""
+    import numpy as np
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        m = int(rng.integers(1, 7))
+        lens = rng.integers(1, 60, m).tolist()
+        order = rng.permutation(m)  # store rows in a shuffled order; request positions in chunk order
+        rows, at = {}, 0
+        for i in order:
+            rows[i] = at
+            at += lens[i]
+        dst = np.concatenate([[0], np.cumsum(lens)[:-1]]).tolist()
+        tab = [(rows[i], int(rng.integers(0, 5)), dst[i], lens[i]) for i in range(m)]
+        scores = rng.integers(0, 6, at).astype(np.float32)
+        for ratio in [(0, 1), (1, 10), (1, 3), (7, 10), (1, 1)]:
+            for rule in ("sink", "knorm", "knorm_low"):
+                got = cf.anchor_positions(rule, tab, ratio, scores if rule != "sink" else None, at)
+                want = np.concatenate([dst[i] + oracle.select_anchors(
+                    lens[i], ratio[0], ratio[1], rule, scores[rows[i]:rows[i] + lens[i]]) for i in range(m)])
+                assert got == sorted(want.tolist()), (trial, ratio, rule)
+    with pytest.raises(cf.CfError):
+        cf.anchor_positions("knorm", [(0, 0, 0, 10)], (1, 10), None, 10)  # key norms need scores
+    with pytest.raises(cf.CfError):
+        cf.anchor_positions("sink", [(0, 0, 0, 10)], (11, 10))

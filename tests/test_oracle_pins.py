@@ -502,6 +502,109 @@ def test_query_scores_probe_is_direct_reuse_and_adds_over_layers():
     assert 0 < total.sum() < 3 * n_rows * hq and np.all(total >= 0)
 
 
+# ------------------------------------------------------------------ chunk-anchor query probing (QCFuse §3.3)
+
+def test_attention_at_explicit_positions():
+    """attention_at with key positions 0..L-1 in any order is causal attention; with gaps it is
+    torch SDPA under an explicit boolean visibility mask (independent library routine)."""
+    rng = np.random.default_rng(21)
+    L, hq, hkv, hd = 40, 4, 2, 8
+    q = rng.standard_normal((L, hq, hd))
+    k = rng.standard_normal((L, hkv, hd))
+    v = rng.standard_normal((L, hkv, hd))
+    perm = rng.permutation(L)
+    got = oracle.attention_at(q, np.arange(L), k[perm], perm, v[perm], F64)
+    np.testing.assert_allclose(got, oracle.causal_attention(q, np.arange(L), k, v, F64), rtol=1e-12, atol=1e-13)
+    keep = np.sort(rng.choice(L - 8, 12, replace=False))
+    qp = np.arange(L - 8, L)
+    got = oracle.attention_at(q[qp], qp, k[keep], keep, v[keep], F64)
+    mask = torch.tensor(keep[None, :] <= qp[:, None])
+    qt = torch.tensor(q[qp]).permute(1, 0, 2)
+    kt = torch.tensor(k[keep]).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    vt = torch.tensor(v[keep]).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    want = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_QK], ids=["llama-style", "qk-norm"])
+def test_layer_over_full_prefix_is_layer_rows(cfg):
+    """layer_rows_over with the whole stitched cache as its explicit-position prefix equals
+    layer_rows on the same rows over that cache (the query rows' K/V written at their rows)."""
+    model = _Model(cfg)
+    chunks, q, toks = _request(cfg)
+    N, ks, vs, table, kst, vst = _stitched(model, chunks, toks, 1)
+    L = len(toks)
+    h = np.asarray(model.embed[toks[N:]], F64)
+    pos = np.arange(N, L)
+    out, k_new, v_new = oracle.layer_rows_over(cfg, model.layer(0), h, pos, kst[0][:N], np.arange(N), vst[0][:N], F64)
+    kc, vc = kst[0].copy(), vst[0].copy()
+    want = oracle.layer_rows(cfg, model.layer(0), h, pos, kc, vc, F64)
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(k_new, kc[N:], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(v_new, vc[N:], rtol=1e-13, atol=1e-14)
+
+
+def test_anchor_counts_and_sink_anchors_by_hand():
+    """Eq. 14: ceil(r_a |c_i|) anchors; Sink keeps the first tokens of each chunk."""
+    assert oracle.anchor_count(512, 1, 10) == 52 and oracle.anchor_count(100, 1, 10) == 10
+    assert oracle.anchor_count(1024, 1, 10) == 103 and oracle.anchor_count(7, 0, 1) == 0
+    assert oracle.anchor_count(7, 1, 1) == 7 and oracle.anchor_count(1, 1, 100) == 1
+    np.testing.assert_array_equal(oracle.select_anchors(512, 1, 10, "sink"), np.arange(52))
+    np.testing.assert_array_equal(oracle.select_anchors(9, 1, 2, "sink"), np.arange(5))
+    with pytest.raises(ValueError):
+        oracle.anchor_count(10, 3, 2)
+
+
+def test_knorm_anchors_match_brute_force():
+    """Knorm ranks positions by the norm of their key-cache tensors (every layer and head): against
+    scores summed with Python floats and a plain sort, largest (knorm) and smallest (knorm_low)
+    first, equal scores keeping the lower position."""
+    rng = np.random.default_rng(22)
+    ly, n, hkv, hd = 3, 37, 2, 4
+    k = rng.integers(-3, 4, (ly, n, hkv, hd)).astype(np.float32)  # small integers: many exact ties
+    norms = oracle.key_norms(k)
+    for r in range(n):
+        assert norms[r] == sum(float(x) ** 2 for x in k[:, r].ravel())
+    for num, den in [(1, 10), (1, 3), (1, 1), (0, 1)]:
+        m = oracle.anchor_count(n, num, den)
+        hi = sorted(range(n), key=lambda r: (-norms[r], r))[:m]
+        lo = sorted(range(n), key=lambda r: (norms[r], r))[:m]
+        np.testing.assert_array_equal(oracle.select_anchors(n, num, den, "knorm", norms), sorted(hi))
+        np.testing.assert_array_equal(oracle.select_anchors(n, num, den, "knorm_low", norms), sorted(lo))
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_QK], ids=["llama-style", "qk-norm"])
+def test_anchored_probe_with_every_anchor_is_the_full_view_probe(cfg):
+    """With every context position kept as an anchor (r_a = 1) the anchor view is the whole stitched
+    context at its request positions, so the anchored scores equal the full-view scores (Eq. 10 / 20),
+    for all layers and for a critical-layer subset."""
+    model = _Model(cfg)
+    chunks, q, toks = _request(cfg)
+    N, ks, vs, table, kst, vst = _stitched(model, chunks, toks, 3)
+    for lset in ([0, 1, 2], [1]):
+        full = oracle.query_scores(model, toks, N, kst, vst, lset, F64)
+        got = oracle.anchored_query_scores(model, toks, N, kst, vst, np.arange(N), lset, F64)
+        np.testing.assert_allclose(got, full, rtol=1e-10, atol=1e-12)
+
+
+def test_anchored_probe_sees_only_anchors():
+    """The probe reads only the anchor rows: the stitched value of a non-anchor context row is read
+    neither by the probe nor by the scoring (which reads context keys only), so changing it changes
+    no score; changing an anchor's value changes the query states and so the scores."""
+    model = _Model(TINY)
+    chunks, q, toks = _request(TINY)
+    N, ks, vs, table, kst, vst = _stitched(model, chunks, toks, 2)
+    anchors = np.concatenate([np.arange(c0, c0 + 3) for c0 in range(0, N, len(chunks[0]))])
+    base = oracle.anchored_query_scores(model, toks, N, kst, vst, anchors, [1], F64)
+    v2 = vst.copy()
+    other = np.setdiff1d(np.arange(N), anchors)[5]
+    v2[:, other] += 10.0  # values of a non-anchor row: never read by the probe or the scoring
+    np.testing.assert_array_equal(oracle.anchored_query_scores(model, toks, N, kst, v2, anchors, [1], F64), base)
+    v3 = vst.copy()
+    v3[0, anchors[4]] += 10.0  # an anchor's layer-0 value conditions the layer-1 query states
+    assert not np.allclose(oracle.anchored_query_scores(model, toks, N, kst, v3, anchors, [1], F64), base)
+
+
 # ------------------------------------------------------------------ span policies (ablation controls)
 
 def test_span_policy_bounds_hand_values():
