@@ -213,6 +213,22 @@ cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode,
                          const int32_t* span_bounds /* host */, int32_t n_spans, int32_t* out_idx,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* --------------------------------------------------------------------- cf_topk_select_noalloc
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): cf_topk_select with the same arguments, modes, results
+ * (bit for bit) and errors, but no workspace argument. The scratch it needs lives in a fixed device
+ * array of CF_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends; the call allocates and frees nothing. A selection needing more scratch than that
+ * (cf_topk_workspace_size(n, mode) > CF_NOALLOC_SCRATCH_BYTES: document-aligned spans beyond
+ * n = 524287; token mode fits any n) fails with CF_EWORKSPACE before anything is enqueued. Every
+ * call on one GPU uses that GPU's one array (the current device's), and the kernels initialise what
+ * they read: calls that may overlap on one GPU (other streams, other threads) race on it and must be
+ * ordered by the caller, e.g. on one stream. */
+#define CF_NOALLOC_SCRATCH_BYTES (4u << 20)
+cf_status cf_topk_select_noalloc(const float* dev, int32_t n, int32_t k, int32_t mode,
+                                 const int32_t* span_bounds /* host */, int32_t n_spans, int32_t* out_idx,
+                                 hipStream_t stream);
+
 /* --------------------------------------------------------------------- cf_blend_layer
  * One decoder layer run only on the rows sel[0..n_sel) (CacheBlend, "Selective Recompute
  * Without Skipping"): gather + RMSNorm -> Q,K,V on those rows -> qk-norm + RoPE at position

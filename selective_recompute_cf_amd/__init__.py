@@ -21,7 +21,7 @@ ANCHOR_RULES = {"sink": 0, "knorm": 1, "knorm_low": 2}
 MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL, "ranked": CF_SEL_RANKED_SPANS,
          "heads": CF_SEL_SPAN_HEADS, "given": CF_SEL_GIVEN}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
-           "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select",
+           "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select", "cf_topk_select_noalloc",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
            "cf_blend_prefill", "cf_blend_prefill_gradual_workspace_size", "cf_blend_prefill_gradual",
            "cf_blend_prefill_streamed_workspace_size", "cf_blend_prefill_streamed", "cf_query_scores_workspace_size",
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "cf_kv_deviation": (i32, [vp, i32, i64, vp, i32, i64, vp, i32, i32, vp]),
         "cf_topk_workspace_size": (sz, [i32, i32]),
         "cf_topk_select": (i32, [vp, i32, i32, i32, vp, i32, vp, vp, sz, vp]),
+        "cf_topk_select_noalloc": (i32, [vp, i32, i32, i32, vp, i32, vp, vp]),
         "cf_blend_layer_workspace_size": (sz, [vp, i32, i32]),
         "cf_blend_layer": (i32, [vp, ctypes.POINTER(LayerWeights), vp, vp, vp, vp, i32, i32, vp, sz, vp]),
         "cf_blend_prefill_workspace_size": (sz, [vp, i32, i32, i32, i32]),
@@ -468,6 +469,14 @@ def topk_select(dev, k: int, out_idx, mode: str = "token", span_bounds=None, ws=
     _room(out_idx, k, "out_idx", _torch().int32)
     _check(lib().cf_topk_select(_ptr(dev), dev.numel(), k, MODES[mode], spans, ns, _ptr(out_idx),
                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev.device)))
+
+
+def topk_select_noalloc(dev, k: int, out_idx, mode: str = "token", span_bounds=None):
+    """cf_topk_select_noalloc: cf_topk_select without a workspace (the library's fixed scratch)."""
+    spans, ns = _span_arg(mode, span_bounds)
+    _room(out_idx, k, "out_idx", _torch().int32)
+    _check(lib().cf_topk_select_noalloc(_ptr(dev), dev.numel(), k, MODES[mode], spans, ns, _ptr(out_idx),
+                                        _stream(dev.device)))
 
 
 def budget(n_ctx: int, rho_num: int, rho_den: int) -> int:

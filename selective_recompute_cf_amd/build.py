@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcf.so")
-SOURCES = ["api.cpp", "policy.cpp", "rows.hip", "topk.hip", "gemm.hip", "attn.hip", "qmass.hip", "probe.hip"]
+SOURCES = ["api.cpp", "policy.cpp", "rows.hip", "topk.hip", "gemm.hip", "attn.hip", "qmass.hip", "probe.hip", "noalloc.hip"]
 ARCH = os.environ.get("CF_OFFLOAD_ARCH", "gfx950")
 # packed fp32 instructions stay off: hipcc must not emit v_pk_{add,mul,fma}_f32 here
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",

@@ -677,6 +677,23 @@ cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode, c
   return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), st);
 }
 
+cf_status cf_topk_select_noalloc(const float* dev, int32_t n, int32_t k, int32_t mode, const int32_t* bounds,
+                                 int32_t ns, int32_t* out, hipStream_t st) {
+  g_err.clear();
+  CF_CHECK(mode == CF_SEL_TOKEN_TOPK || span_mode(mode), CF_EINVAL, "mode %d is not a selection mode", mode);
+  CF_CHECK(n >= 0 && k >= 0 && k <= n, CF_EINVAL, "need 0 <= k <= n (k=%d, n=%d)", k, n);
+  if (span_mode(mode))
+    if (cf_status s = check_spans(bounds, ns, n, mode)) return s;
+  const size_t need = cf_topk_workspace_size(n, mode);
+  CF_CHECK(need <= CF_NOALLOC_SCRATCH_BYTES, CF_EWORKSPACE,
+           "this selection needs %zu scratch bytes; the fixed scratch holds %u", need, CF_NOALLOC_SCRATCH_BYTES);
+  if (k == 0) return CF_OK;
+  CF_CHECK(dev && out, CF_EINVAL, "null pointer");
+  void* ws = nullptr;
+  if (need > 0) CF_HIP(cf::noalloc_scratch(&ws));
+  return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), st);
+}
+
 size_t cf_blend_layer_workspace_size(const cf_ctx* c, int32_t L, int32_t n_sel) {
   if (!c || L <= 0 || n_sel < 0) return 0;
   return layer_ws(c, L, std::min(n_sel, L)).total;

@@ -157,4 +157,9 @@ hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws,
 hipError_t launch_topk_spans(const float* dev, int n, int k, const SpanArgs& sp, int* out,
                              double* ws, hipStream_t st);
 
+// ----------------------------------------------------------------- fixed scratch (noalloc.hip)
+// Device address of the library's fixed scratch array (CF_NOALLOC_SCRATCH_BYTES) on the current
+// device, looked up with that device current on the first call per device and kept.
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace cf
