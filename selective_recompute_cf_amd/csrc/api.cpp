@@ -380,7 +380,7 @@ cf_status enqueue_sel_deviation(const cf_ctx* c, const cf_layer_weights* w, cons
   qp.hq = mc.n_q_heads; qp.hkv = mc.n_kv_heads; qp.hd = mc.head_dim; qp.qk_norm = mc.qk_norm;
   qp.qn = w->q_norm; qp.kn = w->k_norm; qp.eps = mc.rms_eps; qp.cos_t = c->cos_t; qp.sin_t = c->sin_t;
   qp.dev = dev; qp.k_ref = k_ref;
-  CF_RUN("qkv_post", cf::launch_qkv_post(dt, qp, st));
+  CF_RUN("qkv_post/dev", cf::launch_qkv_post(dt, qp, st));
   return CF_OK;
 }
 

@@ -97,14 +97,24 @@ def blend_step_work(s: Shape, N: int, U: int, k: int, sel_layer: int = 1, sel_po
     add("bytes:gemm/k_sel", s.eb * s.kvd * s.d + s.eb * N * s.d + 4 * N * s.kvd)
     # HBM-bound steps (bytes)
     add("reposition", (s.n_layers - sel_layer) * 4 * N * s.kvd * s.eb)     # read K,V; write K,V
-    add("qkv_post", 4 * N * s.kvd + s.eb * N * s.kvd + 4 * N)              # deviation pass
+    # deviation of the N context keys (H2), as the method needs it with the key projection fused:
+    # read the stitched keys, write one fp32 per row (the fresh keys never need to reach HBM)
+    add("h2_deviation", N * s.kvd * s.eb + 4 * N)
+    # gather + norm + K/V scatter of the recomputed rows (H4/H6): the fp32 residual rows read once
+    # and the K/V rows written once per layer; the selection layer's norm of the N context rows and
+    # the final norm of the U query rows
     for l in range(s.n_layers):
         n = L if l < sel_layer else n_sel
-        add("qkv_post", 4 * n * (s.qd + 2 * s.kvd) + s.eb * n * (s.qd + 2 * s.kvd))
-        # the two residual + RMSNorm steps of a layer (after the O and the down projection): read
-        # the projection result and the residual rows, write the new rows and the bf16 GEMM input
-        add("rows", 2 * n * s.d * (12 + s.eb))
-    add("rows", 4 * N * s.d + s.eb * N * s.d + 2 * 4 * U * s.d)  # selection-layer norm, final norm
+        add("h4h6_rows", n * s.d * 4 + 2 * n * s.kvd * s.eb)
+    add("h4h6_rows", 4 * N * s.d + 2 * 4 * U * s.d)
+    # what the current, unfused row kernels move (not algorithmic): the fp32 projection outputs and
+    # split-K partial sums round-trip through memory
+    add("unfused:deviation", 4 * N * s.kvd + s.eb * N * s.kvd + 4 * N)
+    for l in range(s.n_layers):
+        n = L if l < sel_layer else n_sel
+        add("unfused:qkv_post", 4 * n * (s.qd + 2 * s.kvd) + s.eb * n * (s.qd + 2 * s.kvd))
+        add("unfused:rows", 2 * n * s.d * (12 + s.eb))
+    add("unfused:rows", 4 * N * s.d + s.eb * N * s.d + 2 * 4 * U * s.d)
     add("topk_token", 4 * N + 4 * k)
     add("embed", L * s.d * (s.eb + 4))
     return w
