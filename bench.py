@@ -274,6 +274,8 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline (bounded sample)
     cpu, north = None, None
     if not args.no_cpu_baseline:
+        blend()  # the timed request again (deterministic): the sweeps above reused the output buffers
+        torch.cuda.synchronize()
         gpu_res = dict(sel=sel[:k].cpu().numpy(), k=k_out.float().cpu().numpy(), v=v_out.float().cpu().numpy(),
                        out=out[:U].cpu().numpy())
         cpu, north = cpu_baseline(w, k, gpu_res)
