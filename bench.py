@@ -405,7 +405,8 @@ def rolling_steps(dm, steps=50):
 def query_aware(ctx, dm, w, tok_dev, ks, vs, table, k_out, v_out, out, k, sweep_res, timed):
     """QCFuse's query-aware selection (§3.2.1 Eq. 10 over all layers, Eq. 20 over three middle
     layers) on the same request: the probe of the query rows over the stitched cache with the
-    per-layer attention mass (cf_query_scores), the top-k of the scores, and the blend of that
+    per-layer attention mass (cf_query_scores), or over the chunk anchors only (§3.3, Sink or Knorm
+    anchors at r_a = 0.1, cf_query_scores_anchored), the top-k of the scores, and the blend of that
     set from layer 0 (CF_SEL_GIVEN); times per step and the selection's share of the total."""
     import torch
     import selective_recompute_cf_amd as cf
@@ -422,9 +423,23 @@ def query_aware(ctx, dm, w, tok_dev, ks, vs, table, k_out, v_out, out, k, sweep_
                       dtype=torch.uint8, device="cuda")
     mid = Ly // 2
     res = {}
-    for name, lset in [("all_layers", list(range(Ly))), ("three_middle_layers", [mid - 1, mid, mid + 1])]:
-        def select(lset=lset):
-            ctx.query_scores(dm.array, dm.embed, tok_dev, N, U, kb, vb, lset, scores, wsq)
+    # QCFuse's chunk anchors at r_a = 0.1 (§3.3.3): Sink, and Knorm from the store's key norms (offline, untimed)
+    norms = torch.empty(ks.shape[1], dtype=torch.float32, device="cuda")
+    ctx.key_norms(ks, norms)
+    anchors = {"sink": cf.anchor_positions("sink", table, (1, 10)),
+               "knorm": cf.anchor_positions("knorm", table, (1, 10), norms.cpu().numpy(), ks.shape[1])}
+    anchors = {r: torch.tensor(a, dtype=torch.int32, device="cuda") for r, a in anchors.items()}
+    wsa = torch.empty(max(ctx.query_scores_anchored_workspace_size(N, U, int(a.numel())) for a in anchors.values()),
+                      dtype=torch.uint8, device="cuda")
+    cases = [("all_layers", list(range(Ly)), None), ("three_middle_layers", [mid - 1, mid, mid + 1], None)]
+    cases += [(f"anchors_{r}_r0.1_three_middle_layers", [mid - 1, mid, mid + 1], r) for r in anchors]
+    cases += [(f"anchors_{r}_r0.1_all_layers", list(range(Ly)), r) for r in anchors]
+    for name, lset, rule in cases:
+        def select(lset=lset, rule=rule):
+            if rule is None:
+                ctx.query_scores(dm.array, dm.embed, tok_dev, N, U, kb, vb, lset, scores, wsq)
+            else:
+                ctx.query_scores_anchored(dm.array, dm.embed, tok_dev, N, U, kb, vb, anchors[rule], lset, scores, wsa)
             cf.topk_select(scores, k, sel, "token", None, wst)
 
         def blend_given():
@@ -434,7 +449,8 @@ def query_aware(ctx, dm, w, tok_dev, ks, vs, table, k_out, v_out, out, k, sweep_
         _, p_sel = timed(select, 5, 2)
         _, p_bl = timed(blend_given, 5, 2)
         t_sel, t_bl = statistics.median(p_sel), statistics.median(p_bl)
-        res[name] = {"layers": len(lset), "select_ms": round(t_sel, 3), "blend_ms": round(t_bl, 3),
+        res[name] = {"layers": len(lset), "anchors": None if rule is None else int(anchors[rule].numel()),
+                     "select_ms": round(t_sel, 3), "blend_ms": round(t_bl, 3),
                      "total_ms": round(t_sel + t_bl, 3), "selection_share": round(t_sel / (t_sel + t_bl), 3),
                      "speedup_vs_full_prefill": round(sweep_res["full_prefill_ms"] / (t_sel + t_bl), 3)}
     log(f"[bench] query-aware: {res}")

@@ -148,6 +148,14 @@ def cmd_stats(a):
         ms = sum(r["total_ms"] for r in g)
         lines += ["", f"Kernels matching `{a.group}` together: {calls} calls, {ms:.3f} ms, "
                       f"average {ms / max(calls, 1) * 1e3:.2f} us per launch."]
+        if a.tail_trace:
+            # the last dispatches of the group are the event-timed steps when nothing runs after them
+            with open(a.tail_trace) as f:
+                tr = [r for r in csv.DictReader(f) if rx.search(short_name(r["Kernel_Name"]))]
+            tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[-a.tail:]]
+            lines += [f"The last {len(d)} of them in the kernel trace (the event-timed steps, which run last): "
+                      f"average {sum(d) / max(len(d), 1):.2f} us per launch."]
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -338,6 +346,8 @@ def main():
     s.add_argument("--command", required=True)
     s.add_argument("--top", type=int, default=25)
     s.add_argument("--group", default=None, help="also total the kernels whose names match this pattern")
+    s.add_argument("--tail-trace", default=None, help="kernel_trace.csv: also average the group's last --tail dispatches")
+    s.add_argument("--tail", type=int, default=0)
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)

@@ -39,3 +39,22 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "exactly one GPU" in r.stderr
+
+
+def test_row_step_and_deviation_bytes_are_the_scope_numerators():
+    """The row steps (gather + norm + K/V scatter) and the selection-layer deviation are credited with
+    the bytes the method must move, worked by hand for the Llama-3-8B request: per layer n_sel x d
+    fp32 residual rows read once plus n_sel x kvd keys and values written once (all L rows on the
+    full layer 0), plus the selection layer's norm of the N context rows and the final norm of the U
+    query rows; the deviation reads the N stitched keys and writes N floats."""
+    from selective_recompute_cf_amd import roofline as rl
+    s = rl.shape_of(synth.LLAMA3_8B)
+    N, U, k = 3072, 64, 460
+    L, n = N + U, k + U
+    w = rl.blend_step_work(s, N, U, k, 1)
+    per = lambda rows: rows * 4096 * 4 + 2 * rows * 1024 * 2
+    assert w["h4h6_rows"] == per(L) + 31 * per(n) + 4 * N * 4096 + 2 * 4 * U * 4096
+    assert w["h2_deviation"] == N * 1024 * 2 + 4 * N
+    assert abs(w["h4h6_rows"] / 1e6 - 449.33) < 0.01  # MB per request: 64.2 + 31 x 10.7 + 50.3 + 2.1
+    # the unfused kernels' traffic is reported apart and is larger
+    assert w["unfused:rows"] + w["unfused:qkv_post"] > w["h4h6_rows"]
