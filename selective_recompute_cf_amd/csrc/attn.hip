@@ -33,14 +33,28 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // assembly, as in the GEMM; M0 is set right before each load and used by nothing else in the
 // kernel): lane l of a load lands in 16-byte slot l of a 1 KB row group, so the swizzle is
 // applied on the global side (the lane that fills chunk slot c' of key t fetches chunk
-// c' ^ (t & SWM)). Per key block: wait for this wave's loads of the block | barrier | load the
-// block S - 1 ahead into the stage the previous block used | S^T, softmax, O^T on the block.
+// c' ^ (t & SWM), or c' ^ vswz(t) in a V tile). Per key block: wait for this wave's loads of the
+// block | barrier | load the block S - 1 ahead into the stage the previous block used | S^T,
+// softmax, O^T on the block.
+//
+// Swizzle of the V tiles. The K fragment reads (16 keys x one 16-byte chunk per 16 lanes) are
+// conflict-free with chunk c of key t at c ^ (t & 15); the transposing V reads are not (each 32-lane
+// half reads 8 consecutive keys x two neighbouring chunks, which that XOR maps onto the same 8
+// physical chunks: a 2-way bank conflict on every read, measured on gfx950). At head_dim 128 the V
+// tiles therefore rotate the key's low 4 bits left by one, which spreads each half's 16 chunk reads
+// over all 16 chunks (measured conflict-free) while staying a permutation of the chunks per key.
+template <int HD>
+__device__ __forceinline__ int vswz(int t) {
+  if constexpr (HD == 128) return ((t & 7) << 1) | ((t >> 3) & 1);
+  else return t & (HD / 8 - 1);
+}
+
 #define CF_ATTN_WAITCNT(vm) ((((vm) & 15) | (((vm) >> 4) << 14)) | 0x70 | (15 << 8))
 
 template <int HD, int NW, int RG, int S, int MINB>
 __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   constexpr int NCH = HD / 8;       // 16-byte chunks per key row
-  constexpr int SWM = NCH - 1;      // chunk c of tile key t is stored at c ^ (t & SWM)
+  constexpr int SWM = NCH - 1;      // chunk c of K tile key t is stored at c ^ (t & SWM)
   constexpr int TILE = KB * HD;     // elements of one K (or V) tile
   constexpr int RPI = WAVE / NCH;   // key rows per load instruction
   constexpr int NI = 2 * KB / RPI;  // load instructions per key block (K then V)
@@ -119,7 +133,7 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   for (int q = 0; q < NL; ++q) {
     const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
     const int t = ii * RPI + lane / NCH;
-    const int c = (lane % NCH) ^ (t & SWM);
+    const int c = (lane % NCH) ^ (tensor ? vswz<HD>(t) : (t & SWM));
     src[q] = (const bf16*)(tensor ? a.v : a.k) + g * HD + c * 8;
     trow[q] = t;
   }
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
     const int t = kb + lr / 4;
     const int col = nt * 16 + 4 * (lr % 4);
     const int c = col / 8;
-    const bf16* ptr = &Vt[t * HD + ((c ^ (t & SWM)) * 8) + (col % 8)];
+    const bf16* ptr = &Vt[t * HD + ((c ^ vswz<HD>(t)) * 8) + (col % 8)];
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
   };
   auto step = [&](int it) __attribute__((always_inline)) {
@@ -183,13 +197,21 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rg][kt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-      const float m_cand = fmaxf(m_i[rg], mx * sl2);
-      const bool upd = m_cand > m_i[rg] + 8.f;
-      const float m_use = upd ? m_cand : m_i[rg];
+      // A row's reference moves only if some lane of the row sees a score above it by more than 8,
+      // so the cross-lane maximum is needed only when some lane of the wave does (after the first
+      // block, rarely); otherwise every row keeps its reference, whatever the row maximum is.
+      bool upd = false;
+      float m_use = m_i[rg];
+      if (__builtin_amdgcn_ballot_w64(mx * sl2 > m_i[rg] + 8.f)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float m_cand = fmaxf(m_i[rg], mx * sl2);
+        upd = m_cand > m_i[rg] + 8.f;
+        m_use = upd ? m_cand : m_i[rg];
+      }
       const float m_ref = m_use == -INFINITY ? 0.f : m_use;
       const float alpha = upd ? __builtin_amdgcn_exp2f(m_i[rg] - m_ref) : 1.f;
+      // the row sum stays split over the row's four lanes (each its own keys) until the end
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -199,8 +221,6 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
           s[rg][kt][i] = e;
           ps += e;
         }
-      ps += __shfl_xor(ps, 16, WAVE);
-      ps += __shfl_xor(ps, 32, WAVE);
       l_i[rg] = l_i[rg] * alpha + ps;
       m_i[rg] = m_use;
       if (__builtin_amdgcn_ballot_w64(upd)) {
@@ -243,6 +263,12 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
       step(it);
     }
     __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT(0));
+  }
+  // the row sums over the four lanes of each row
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    l_i[rg] += __shfl_xor(l_i[rg], 16, WAVE);
+    l_i[rg] += __shfl_xor(l_i[rg], 32, WAVE);
   }
   // o[rg][nt][i] = O[row of group rg][hd 16nt + 4lg + i] (unnormalised)
 #pragma unroll
