@@ -87,8 +87,10 @@ hipEvent_t prof_event() {
     g_pool.pop_back();
     return e;
   }
+  // timing only, never a memory order for a reader: without the system-scope release a default
+  // event adds after a kernel (an L2 write-back), which would be timed as part of the launch
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

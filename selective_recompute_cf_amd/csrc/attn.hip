@@ -69,16 +69,15 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   // the block's query tile j0.., kv head g, key range [kbeg, kend) and where its result goes:
   // piece >= 0 writes partial sums to piece slot `piece`, else the normalised output
   int j0, g, kbeg, kend, piece = -1;
-  if (a.sched) {  // balanced pieces: blocks t * hkv + g
+  if (a.sched) {  // balanced pieces: blocks t * hkv + g, t < P <= ATTN_MAXP
     g = blockIdx.x % a.hkv;
     const int t = blockIdx.x / a.hkv;
-    if (t >= a.sched->T) return;  // block-uniform
-    const int qt = a.sched->piece_qt[t], chunk = a.sched->chunk;
-    const int kb0 = (t - a.sched->off[qt]) * chunk, kb1 = min(kb0 + chunk, a.sched->c[qt]);
-    j0 = qt * rpt;
-    kbeg = kb0 * KB;
-    kend = min(min(a.pos[min(j0 + rpt - 1, a.n - 1)] + 1, kb1 * KB), a.L);
-    if (a.sched->off[qt + 1] - a.sched->off[qt] > 1) piece = t;
+    const int4 pc = a.sched->piece[t];  // read beside T: one round trip before the first loads
+    if (t >= a.sched->T) return;        // block-uniform
+    j0 = pc.x;
+    kbeg = pc.y;
+    kend = pc.z;
+    piece = pc.w;
   } else {  // whole query tiles, latest first (they see the most keys); each kv head on one XCD
     const int lt = xcd_tile(blockIdx.x, q_tiles * a.hkv);
     j0 = (q_tiles - 1 - lt % q_tiles) * rpt;
@@ -90,6 +89,37 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   const int lg = lane / 16, lr = lane % 16;
   const int kvd = a.hkv * HD;
   const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
+
+  // load q of this wave: instruction gi = q * NW + w covers key rows [ii * RPI, ii * RPI + RPI)
+  // of tensor gi / (NI / 2) (0 = K, 1 = V), ii = gi % (NI / 2)
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
+  const bf16* src[NL];
+  int trow[NL];
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
+    const int t = ii * RPI + lane / NCH;
+    const int c = (lane % NCH) ^ (tensor ? vswz<HD>(t) : (t & SWM));
+    src[q] = (const bf16*)(tensor ? a.v : a.k) + g * HD + c * 8;
+    trow[q] = t;
+  }
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    const int stage = step % S;
+    const int kbase = kbeg + step * KB;
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
+      const bf16* gp = src[q] + (int64_t)min(kbase + trow[q], a.L - 1) * kvd;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          lds0 + 2u * (uint32_t)(stage * 2 * TILE + tensor * TILE + ii * RPI * HD));
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(dst) : "memory", "m0");
+    }
+  };
+  // the first S - 1 key blocks go out before the queries are read: their latency overlaps
+  if (nkb > 0) {
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q) issue(min(q, nkb - 1));
+  }
 
   // row group rg of this wave: block rows (w * RG + rg) * 16 + lr
   int jrow[RG], head[RG], p[RG];
@@ -124,31 +154,6 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   for (int off = 1; off < 16; off <<= 1) p_min = min(p_min, __shfl_xor(p_min, off, WAVE));
   p_min = __builtin_amdgcn_readfirstlane(p_min);
 
-  // load q of this wave: instruction gi = q * NW + w covers key rows [ii * RPI, ii * RPI + RPI)
-  // of tensor gi / (NI / 2) (0 = K, 1 = V), ii = gi % (NI / 2)
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
-  const bf16* src[NL];
-  int trow[NL];
-#pragma unroll
-  for (int q = 0; q < NL; ++q) {
-    const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
-    const int t = ii * RPI + lane / NCH;
-    const int c = (lane % NCH) ^ (tensor ? vswz<HD>(t) : (t & SWM));
-    src[q] = (const bf16*)(tensor ? a.v : a.k) + g * HD + c * 8;
-    trow[q] = t;
-  }
-  auto issue = [&](int step) __attribute__((always_inline)) {
-    const int stage = step % S;
-    const int kbase = kbeg + step * KB;
-#pragma unroll
-    for (int q = 0; q < NL; ++q) {
-      const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
-      const bf16* gp = src[q] + (int64_t)min(kbase + trow[q], a.L - 1) * kvd;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          lds0 + 2u * (uint32_t)(stage * 2 * TILE + tensor * TILE + ii * RPI * HD));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(dst) : "memory", "m0");
-    }
-  };
   // V^T operand through the transposing LDS read: within each 16-lane group, lane q reads the
   // 4 dims 16nt + 4(q%4).. of tile key kb + q/4 and lane lr receives V[kb + 0..3][16nt + lr]
   auto vread = [&](const bf16* Vt, int kb, int nt) __attribute__((always_inline)) {
@@ -177,9 +182,9 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
           s[rg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][kk], s[rg][kt], 0, 0, 0);
       }
     }
-    // s[rg][kt][i] = S[row of group rg][key kbase + 16kt + 4lg + i]. Softmax as in the pipelined
-    // kernel: unscaled scores, masks only on blocks that reach past a row of the wave, exp2 of
-    // one fused multiply-add, and a reference max that moves only on growth above 8 (log2).
+    // s[rg][kt][i] = S[row of group rg][key kbase + 16kt + 4lg + i]. Softmax: unscaled scores,
+    // masks only on blocks that reach past a row of the wave, exp2 of one fused multiply-add, and
+    // a reference max that moves only on growth above 8 (log2).
     bf16x8 pf[RG][2];
     const bool unmasked = kbase + KB - 1 <= min(p_min, kend - 1);  // wave-uniform
 #pragma unroll
@@ -251,9 +256,8 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   if (nkb > 0) {
     const int last = nkb - 1;
     // past the last block the loads repeat the last block into a stage nobody reads again, so
-    // every wave issues NL loads per block and the wait counts hold
-#pragma unroll
-    for (int q = 0; q < S - 1; ++q) issue(min(q, last));
+    // every wave issues NL loads per block and the wait counts hold (the query loads, issued
+    // after the first blocks, only make the first wait stricter)
     for (int it = 0; it < nkb; ++it) {
       __builtin_amdgcn_s_waitcnt(CF_ATTN_WAITCNT((S - 2) * NL));
       asm volatile("" ::: "memory");
@@ -435,7 +439,7 @@ hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t st) {
 // pieces of the same length gives each block about the same work.
 constexpr int MIN_PIECE = 2;  // key blocks (128 keys); 1 to 12 measured within 0.3% of each other
 
-__global__ __launch_bounds__(256) void attn_sched_kernel(const int* __restrict__ pos, int n, int rpt, int P,
+__global__ __launch_bounds__(256) void attn_sched_kernel(const int* __restrict__ pos, int n, int rpt, int P, int L,
                                                          AttnSched* __restrict__ s) {
   __shared__ int c[ATTN_MAXQ];
   __shared__ int best, sum_c, max_c;
@@ -462,19 +466,22 @@ __global__ __launch_bounds__(256) void attn_sched_kernel(const int* __restrict__
     int t = 0;
     for (int qt = 0; qt < Q; ++qt) {
       s->off[qt] = t;
-      s->c[qt] = c[qt];
-      for (int e = (c[qt] + chunk - 1) / chunk; e > 0; --e) s->piece_qt[t++] = qt;
+      const int np = (c[qt] + chunk - 1) / chunk, j0 = qt * rpt;
+      const int last_pos = pos[min(j0 + rpt - 1, n - 1)];
+      for (int e = 0; e < np; ++e, ++t) {
+        const int kb0 = e * chunk, kb1 = min(kb0 + chunk, c[qt]);
+        s->piece[t] = make_int4(j0, kb0 * KB, min(min(last_pos + 1, kb1 * KB), L), np > 1 ? t : -1);
+      }
     }
     s->off[Q] = t;
     s->T = t;
-    s->chunk = chunk;
   }
 }
 
 hipError_t launch_attention_sched(const AttnArgs& a, AttnSched* s, hipStream_t st) {
   const int rpt = 128 / (a.hq / a.hkv), Q = (a.n + rpt - 1) / rpt;
   if (a.n <= 0 || Q > ATTN_MAXQ || a.P < Q || a.P > ATTN_MAXP) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, a.pos, a.n, rpt, a.P, s);
+  hipLaunchKernelGGL(attn_sched_kernel, dim3(1), dim3(256), 0, st, a.pos, a.n, rpt, a.P, a.L, s);
   return hipGetLastError();
 }
 

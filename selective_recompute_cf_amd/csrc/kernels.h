@@ -107,12 +107,17 @@ struct GemmPlan { int cfg; int splits; };
 GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, int n_cu);
 
 // ----------------------------------------------------------------- attention (attn.hip)
-// Work-balanced key pieces for the selected rows: query tile qt (128 / G consecutive rows) has c[qt]
+// Work-balanced key pieces for the selected rows: query tile qt (128 / G consecutive rows) has c
 // key blocks of 64 up to its last row's position; it is cut into pieces of `chunk` key blocks,
-// pieces [off[qt], off[qt + 1]), piece t belonging to tile piece_qt[t]; T <= P pieces in all,
-// chunk the smallest for which they fit. Built on the device from the positions.
+// pieces [off[qt], off[qt + 1]); T <= P pieces in all, chunk the smallest for which they fit.
+// Built on the device from the positions. piece[t] holds what the block running piece t needs, in
+// one record: its tile's first row, its key range [kbeg, kend) and its partial-sum slot (t when
+// the tile has several pieces, else -1).
 constexpr int ATTN_MAXQ = 256, ATTN_MAXP = 256;
-struct AttnSched { int T, chunk; int off[ATTN_MAXQ + 1]; int c[ATTN_MAXQ]; int piece_qt[ATTN_MAXP]; };
+struct AttnSched {
+  int4 piece[ATTN_MAXP];
+  int T; int off[ATTN_MAXQ + 1];
+};
 struct AttnArgs {
   Dt dt;
   const void* q; int64_t ldq;          // [n][hq*hd]
