@@ -687,6 +687,44 @@ def cpu_baseline(w, k, gpu=None, runs=2):
              "layer_by_layer": "K/V of every layer within the bar element-wise and the selection overlap 1.0 when "
                                "the oracle is fed the GPU's own layer inputs (tests/test_gpu_teacher_forced.py)"}
     log(f"[bench] north-star parity vs the fp32 oracle: overlap {ov:.4f}; out {north['out']}; K {north['K']}")
+
+    # The same request through the oracle in its bf16-arithmetic mode (bf16 rounding at the points where
+    # the GPU path stores bf16: normed rows, Q, K/V, softmax weights, attention output, SwiGLU
+    # activation; chunk caches prefilled the same way), untimed: how far bf16 arithmetic alone drifts
+    # from the fp32 oracle at full depth, beside the GPU's own distance from each.
+    t0 = time.perf_counter()
+    ctx_mgr = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        kb, vb = [], []
+        for c in chunks:
+            a, b = oracle.chunk_prefill(model, c, np.float32, bf16_ops=True)
+            kb.append(a)
+            vb.append(b)
+        kb, vb = np.concatenate(kb, 1), np.concatenate(vb, 1)
+        rb = oracle.blend_prefill(model, toks, N, kb, vb, tab, w.sel_layer, k, w.mode, spans, np.float32,
+                                  bf16_ops=True)
+    finally:
+        if ctx_mgr is not None:
+            ctx_mgr.__exit__(None, None, None)
+
+    def vs(sel_a, out_a, k_a, v_a, sel_b, out_b, k_b, v_b):
+        both = np.zeros(L, bool)
+        x, y = np.zeros(N, bool), np.zeros(N, bool)
+        x[sel_a] = True
+        y[sel_b] = True
+        both[:N] = x == y
+        both[N:] = True
+        return {"selection_overlap": round(len(set(np.asarray(sel_a).tolist()) & set(np.asarray(sel_b).tolist())) /
+                                           max(k, 1), 4),
+                "out": stats(out_a, out_b), "K": stats(k_a[:, both], k_b[:, both]),
+                "V": stats(v_a[:, both], v_b[:, both])}
+
+    north["bf16_arithmetic_oracle_vs_fp32_oracle"] = vs(rb.sel, rb.out, rb.k.reshape(shape), rb.v.reshape(shape),
+                                                        res.sel, res.out, res.k.reshape(shape), res.v.reshape(shape))
+    north["gpu_vs_bf16_arithmetic_oracle"] = vs(gpu["sel"], gpu["out"], gpu["k"], gpu["v"],
+                                                rb.sel, rb.out, rb.k.reshape(shape), rb.v.reshape(shape))
+    log(f"[bench] bf16-arithmetic oracle ({time.perf_counter() - t0:.1f}s) vs the fp32 oracle: "
+        f"{north['bf16_arithmetic_oracle_vs_fp32_oracle']}; GPU vs it: {north['gpu_vs_bf16_arithmetic_oracle']}")
     return cpu, north
 
 
