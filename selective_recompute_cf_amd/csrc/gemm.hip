@@ -527,8 +527,10 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
   // with per-CU rates relative to the 128x256 block as measured on whole rounds of gate/up
   // products with the weights streaming from HBM (smaller blocks re-read the weight and
   // activation tiles more often). One cost unit is one row of a 256-wide block advancing one K
-  // column (about 0.1 ns on a full round); at about 5 TB/s the 8 bytes of one partial element
-  // (written once, read once) cost 0.0131 units.
+  // column (about 0.1 ns on a full round); the 8 bytes of one partial element (written once, then
+  // read once by the short reduce or post-processing kernel, which moves about 4 TB/s) cost 0.02
+  // units. (At 0.0131 the 3136-row QKV product took two splits: 187 against 176 us for one in the
+  // standalone harness, before its post-processing read twice the partial sums.)
   struct Opt { int cfg, bm, bn, per_cu; double rate; };
   const Opt dtl_opts[6] = {{GEMM_DTL128, 128, 256, 1, 1.0},  {GEMM_DTL96, 96, 256, 1, 0.86},
                            {GEMM_DTL64, 64, 256, 1, 0.65},   {GEMM_DTL256, 256, 256, 1, 1.15},
@@ -551,7 +553,7 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
       if (sp > 1 && K / sp < 512) break;
       const long rounds = (tiles * sp + slots - 1) / slots;
       const double cost = rounds * opts[o].per_cu * work * ((double)K / sp) / opts[o].rate +
-                          (sp - 1) * (double)M * N * 0.0131;
+                          (sp - 1) * (double)M * N * 0.02;
       if (cost < best_cost * 0.999) {
         best_cost = cost;
         best = GemmPlan{opts[o].cfg, sp};
