@@ -78,3 +78,26 @@ def test_counter_shares(tmp_path, monkeypatch):
                                       "attention=attn_dtl", "--command", "x"])
     profiles.main()
     assert "| attention | 1 | 50.0% | 30.0% | 25.0% | 4.00 |" in out.read_text()
+
+
+def test_stats_group_and_tail_window(tmp_path, monkeypatch):
+    """Kernel statistics with a group total, and the group's last dispatches in the trace (the event-timed
+    steps run last): two GEMM launches of 10 and 30 us in the statistics average 20 us; in the trace the
+    last two of three GEMM dispatches (by start time, not file order) last 40 and 20 us, average 30 us."""
+    stats = tmp_path / "s.csv"
+    stats.write_text("Name,Calls,TotalDurationNs,AverageNs,Percentage\n"
+                     "void cf::gemm_bf16_dtl<X>(cf::GemmArgs),2,40000,20000,80\n"
+                     "cf::attn_dtl_kernel(cf::AttnArgs),1,10000,10000,20\n")
+    trace = tmp_path / "t.csv"
+    trace.write_text("Kernel_Name,Start_Timestamp,End_Timestamp\n"
+                     "void cf::gemm_bf16_dtl<X>(cf::GemmArgs),500,20500\n"
+                     "void cf::gemm_bf16_dtl<X>(cf::GemmArgs),0,10000\n"
+                     "cf::attn_dtl_kernel(cf::AttnArgs),100000,900000\n"
+                     "void cf::gemm_bf16_dtl<X>(cf::GemmArgs),100,40100\n")
+    out = tmp_path / "o.md"
+    monkeypatch.setattr(sys, "argv", ["profiles", "stats", str(stats), str(out), "--group", "gemm_bf16_dtl",
+                                      "--tail-trace", str(trace), "--tail", "2", "--command", "x"])
+    profiles.main()
+    text = out.read_text()
+    assert "together: 2 calls, 0.040 ms, average 20.00 us per launch." in text
+    assert "The last 2 of them in the kernel trace" in text and "average 30.00 us per launch." in text
