@@ -58,3 +58,37 @@ def test_row_step_and_deviation_bytes_are_the_scope_numerators():
     assert abs(w["h4h6_rows"] / 1e6 - 449.33) < 0.01  # MB per request: 64.2 + 31 x 10.7 + 50.3 + 2.1
     # the unfused kernels' traffic is reported apart and is larger
     assert w["unfused:rows"] + w["unfused:qkv_post"] > w["h4h6_rows"]
+
+
+def test_cpu_leg_compares_against_both_oracle_modes():
+    """The CPU leg's end-to-end comparisons on the tiny bf16 model, fed the fp32 oracle's own result
+    as the GPU's: against the fp32 oracle everything agrees exactly; the bf16-arithmetic oracle sits a
+    small non-zero distance from it; and the 'GPU' (here the fp32 result) is exactly that distance
+    from the bf16-arithmetic oracle, in both directions of the comparison."""
+    import numpy as np
+    import oracle
+    w = synth.WORKLOADS["tiny"].replace(model=synth.TINY.replace(dtype="bf16", n_layers=2))
+    k = synth_budget(w)
+    model = synth.Model(w.model)
+    chunks, _, toks = synth.request_tokens(w)
+    ks, vs, tab, row = [], [], [], 0
+    for c in chunks:
+        a, b = oracle.chunk_prefill(model, c, np.float32)
+        ks.append(a)
+        vs.append(b)
+        tab.append((row, 0, row, len(c)))
+        row += len(c)
+    spans = [i * w.chunk_len for i in range(w.n_chunks + 1)]
+    r = oracle.blend_prefill(model, toks, w.n_ctx, np.concatenate(ks, 1), np.concatenate(vs, 1), tab, w.sel_layer, k,
+                             w.mode, spans, np.float32)
+    Ly, L = w.model.n_layers, w.n_total
+    gpu = dict(sel=r.sel[:k], k=r.k.reshape(Ly, L, -1), v=r.v.reshape(Ly, L, -1), out=r.out)
+    cpu, north = bench.cpu_baseline(w, k, gpu, runs=1)
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0
+    assert north["selection_overlap"] == 1.0
+    for t in ("out", "K", "V"):
+        assert north[t]["norm_rel"] == 0.0 and north[t]["outside_bar_frac"] == 0.0
+    b16, g16 = north["bf16_arithmetic_oracle_vs_fp32_oracle"], north["gpu_vs_bf16_arithmetic_oracle"]
+    for t in ("out", "K", "V"):
+        assert 1e-5 < b16[t]["norm_rel"] < 2e-2
+        assert abs(g16[t]["max_abs"] - b16[t]["max_abs"]) < 1e-6
