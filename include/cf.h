@@ -205,10 +205,15 @@ cf_status cf_selection_deviation(const cf_ctx* ctx, const cf_layer_weights* w /*
  * Results are exact (bit-identical to any implementation of the same order). 0 <= k <= n.
  * n_spans <= CF_MAX_SPANS. ws: device workspace of cf_topk_workspace_size(n, mode) bytes
  * (document-aligned mode always; token mode from n = 65536 up, where the selection runs on the
- * whole GPU; the size is 0 otherwise and ws may be NULL). A call without the workspace it needs fails with
+ * whole GPU; the size is 0 otherwise and ws may be NULL). Token mode also runs with less, down to
+ * cf_topk_workspace_min_size(n, mode) bytes: beyond that minimum the workspace holds a list of the
+ * keys left undecided after two histogram passes (8 bytes each, room for n / 16 at the full size);
+ * when they do not fit, the selection reads all n values twice more instead, with the same result.
+ * For the other modes the two sizes are equal. A call with less than the minimum fails with
  * CF_EWORKSPACE before anything is enqueued. */
 #define CF_MAX_SPANS 256
 size_t cf_topk_workspace_size(int32_t n, int32_t mode);
+size_t cf_topk_workspace_min_size(int32_t n, int32_t mode);
 cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode,
                          const int32_t* span_bounds /* host */, int32_t n_spans, int32_t* out_idx,
                          void* ws, size_t ws_bytes, hipStream_t stream);
@@ -219,8 +224,9 @@ cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode,
  * (bit for bit) and errors, but no workspace argument. The scratch it needs lives in a fixed device
  * array of CF_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
  * ends; the call allocates and frees nothing. A selection needing more scratch than that
- * (cf_topk_workspace_size(n, mode) > CF_NOALLOC_SCRATCH_BYTES: document-aligned spans beyond
- * n = 524287; token mode fits any n) fails with CF_EWORKSPACE before anything is enqueued. Every
+ * (cf_topk_workspace_min_size(n, mode) > CF_NOALLOC_SCRATCH_BYTES: document-aligned spans beyond
+ * n = 524287; token mode fits any n, its candidate list taking the rest of the array) fails with
+ * CF_EWORKSPACE before anything is enqueued. Every
  * call on one GPU uses that GPU's one array (the current device's), and the kernels initialise what
  * they read: calls that may overlap on one GPU (other streams, other threads) race on it and must be
  * ordered by the caller, e.g. on one stream. */

@@ -21,7 +21,8 @@ ANCHOR_RULES = {"sink": 0, "knorm": 1, "knorm_low": 2}
 MODES = {"token": CF_SEL_TOKEN_TOPK, "doc": CF_SEL_DOC_SPANS, "all": CF_SEL_ALL, "ranked": CF_SEL_RANKED_SPANS,
          "heads": CF_SEL_SPAN_HEADS, "given": CF_SEL_GIVEN}
 EXPORTS = ["cf_ctx_create", "cf_ctx_destroy", "cf_last_error", "cf_version", "cf_rope_reposition",
-           "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_select", "cf_topk_select_noalloc",
+           "cf_kv_deviation", "cf_topk_workspace_size", "cf_topk_workspace_min_size", "cf_topk_select",
+           "cf_topk_select_noalloc",
            "cf_blend_layer_workspace_size", "cf_blend_layer", "cf_blend_prefill_workspace_size",
            "cf_blend_prefill", "cf_blend_prefill_gradual_workspace_size", "cf_blend_prefill_gradual",
            "cf_blend_prefill_streamed_workspace_size", "cf_blend_prefill_streamed", "cf_query_scores_workspace_size",
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "cf_rope_reposition": (i32, [vp, vp, vp, i64, i32, vp, vp, i64, i32, vp, i32, i32, i32, vp]),
         "cf_kv_deviation": (i32, [vp, i32, i64, vp, i32, i64, vp, i32, i32, vp]),
         "cf_topk_workspace_size": (sz, [i32, i32]),
+        "cf_topk_workspace_min_size": (sz, [i32, i32]),
         "cf_topk_select": (i32, [vp, i32, i32, i32, vp, i32, vp, vp, sz, vp]),
         "cf_topk_select_noalloc": (i32, [vp, i32, i32, i32, vp, i32, vp, vp]),
         "cf_blend_layer_workspace_size": (sz, [vp, i32, i32]),
@@ -462,6 +464,12 @@ def kv_deviation(k_new, k_ref, dev, kv_dim: Optional[int] = None):
 
 def topk_workspace_size(n: int, mode: str) -> int:
     return int(lib().cf_topk_workspace_size(n, MODES[mode]))
+
+
+def topk_workspace_min_size(n: int, mode: str) -> int:
+    """cf_topk_workspace_min_size: the least workspace cf_topk_select runs with (token mode then keeps
+    fewer undecided keys in its candidate list and may read the values twice more; same result)."""
+    return int(lib().cf_topk_workspace_min_size(n, MODES[mode]))
 
 
 def topk_select(dev, k: int, out_idx, mode: str = "token", span_bounds=None, ws=None):

@@ -182,7 +182,7 @@ LayerWs layer_ws(const cf_ctx* c, int L, int R, int ksel_rows = 0) {
 }
 
 struct PrefillWs {
-  size_t hidden, sel, sel2, ident, dev, dev2, devh, topk, stage, layer, total;
+  size_t hidden, sel, sel2, ident, dev, dev2, devh, topk, topk_bytes, stage, layer, total;
 };
 
 // ks: the per-layer counts of gradual filtering (nks of them, ks[0] = k), or null.
@@ -211,6 +211,7 @@ PrefillWs prefill_ws(const cf_ctx* c, int N, int U, int k, int mode, const int32
     }
   }
   p.topk = take(topk);
+  p.topk_bytes = topk;
   p.layer = take(layer);
   p.total = off;
   return p;
@@ -478,10 +479,10 @@ void destroy_ctx(cf_ctx* c) {
 }
 
 cf_status enqueue_select(const float* dev, int n, int k, int mode, const int32_t* bounds, int ns, int* out,
-                         double* ws, hipStream_t st) {
+                         double* ws, size_t ws_bytes, hipStream_t st) {
   if (k == 0) return CF_OK;
   if (mode == CF_SEL_TOKEN_TOPK) {
-    CF_RUN("topk_token", cf::launch_topk_token(dev, n, k, out, ws, st));
+    CF_RUN("topk_token", cf::launch_topk_token(dev, n, k, out, ws, ws_bytes, st));
   } else {
     cf::SpanArgs sp{};
     sp.n_spans = ns;
@@ -665,6 +666,11 @@ size_t cf_topk_workspace_size(int32_t n, int32_t mode) {
   return mode == CF_SEL_TOKEN_TOPK ? al(cf::topk_token_ws_bytes(n)) : 0;
 }
 
+size_t cf_topk_workspace_min_size(int32_t n, int32_t mode) {
+  if (n < 0) return 0;
+  return mode == CF_SEL_TOKEN_TOPK ? cf::topk_token_ws_min_bytes(n) : cf_topk_workspace_size(n, mode);
+}
+
 cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode, const int32_t* bounds, int32_t ns,
                          int32_t* out, void* ws, size_t ws_bytes, hipStream_t st) {
   g_err.clear();
@@ -672,11 +678,12 @@ cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode, c
   CF_CHECK(n >= 0 && k >= 0 && k <= n, CF_EINVAL, "need 0 <= k <= n (k=%d, n=%d)", k, n);
   if (span_mode(mode))
     if (cf_status s = check_spans(bounds, ns, n, mode)) return s;
-  CF_CHECK(k == 0 || cf_topk_workspace_size(n, mode) == 0 || (ws && ws_bytes >= cf_topk_workspace_size(n, mode)),
-           CF_EWORKSPACE, "this selection needs %zu workspace bytes", cf_topk_workspace_size(n, mode));
+  const size_t need = cf_topk_workspace_min_size(n, mode);
+  CF_CHECK(k == 0 || need == 0 || (ws && ws_bytes >= need), CF_EWORKSPACE,
+           "this selection needs at least %zu workspace bytes", need);
   if (k == 0) return CF_OK;
   CF_CHECK(dev && out, CF_EINVAL, "null pointer");
-  return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), st);
+  return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), ws_bytes, st);
 }
 
 cf_status cf_topk_select_noalloc(const float* dev, int32_t n, int32_t k, int32_t mode, const int32_t* bounds,
@@ -686,14 +693,16 @@ cf_status cf_topk_select_noalloc(const float* dev, int32_t n, int32_t k, int32_t
   CF_CHECK(n >= 0 && k >= 0 && k <= n, CF_EINVAL, "need 0 <= k <= n (k=%d, n=%d)", k, n);
   if (span_mode(mode))
     if (cf_status s = check_spans(bounds, ns, n, mode)) return s;
-  const size_t need = cf_topk_workspace_size(n, mode);
+  // token mode's candidate list takes what the scratch holds beyond the minimum
+  const size_t need = cf_topk_workspace_min_size(n, mode);
   CF_CHECK(need <= CF_NOALLOC_SCRATCH_BYTES, CF_EWORKSPACE,
            "this selection needs %zu scratch bytes; the fixed scratch holds %u", need, CF_NOALLOC_SCRATCH_BYTES);
   if (k == 0) return CF_OK;
   CF_CHECK(dev && out, CF_EINVAL, "null pointer");
   void* ws = nullptr;
   if (need > 0) CF_HIP(cf::noalloc_scratch(&ws));
-  return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), st);
+  return enqueue_select(dev, n, k, mode, bounds, ns, out, reinterpret_cast<double*>(ws), CF_NOALLOC_SCRATCH_BYTES,
+                        st);
 }
 
 size_t cf_blend_layer_workspace_size(const cf_ctx* c, int32_t L, int32_t n_sel) {
@@ -919,7 +928,8 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
       if (cf_status s = enqueue_sel_deviation(c, w, hidden, N, L, K_l(s_layer), dev, lws + lw_full.x,
                                               reinterpret_cast<float*>(lws + lw_full.qkv), lw_full.plan.ksel, st))
         return s;
-      if (cf_status s = enqueue_select(dev, N, k, mode, bounds, ns, sel, reinterpret_cast<double*>(W + pw.topk), st))
+      if (cf_status s = enqueue_select(dev, N, k, mode, bounds, ns, sel, reinterpret_cast<double*>(W + pw.topk),
+                                       pw.topk_bytes, st))
         return s;
       if (out_dev) CF_RUN("copy", cf::launch_copy_f32(out_dev, dev, N, st));
       if (out_sel) CF_RUN("copy", cf::launch_copy_i32(out_sel, sel, k, st));
@@ -973,10 +983,12 @@ cf_status prefill(const cf_ctx* c, const cf_layer_weights* layers, const void* e
         if (narrows) {
           const int kn = ks[i + 1];
           if (i == 0) {
-            if (cf_status s = enqueue_select(dev, N, kn, CF_SEL_TOKEN_TOPK, nullptr, 0, nxt, tkws, st)) return s;
+            if (cf_status s = enqueue_select(dev, N, kn, CF_SEL_TOKEN_TOPK, nullptr, 0, nxt, tkws, pw.topk_bytes, st))
+              return s;
             CF_RUN("iota", cf::launch_iota(nxt + kn, U, N, st));
           } else {
-            if (cf_status s = enqueue_select(dev2, kl, kn, CF_SEL_TOKEN_TOPK, nullptr, 0, nxt, tkws, st)) return s;
+            if (cf_status s = enqueue_select(dev2, kl, kn, CF_SEL_TOKEN_TOPK, nullptr, 0, nxt, tkws, pw.topk_bytes, st))
+              return s;
             CF_RUN("sel_map", cf::launch_sel_map(nxt, cur, kn, U, N, st));
           }
           std::swap(cur, nxt);

@@ -156,9 +156,13 @@ constexpr int MAX_SPANS = 256;
 // fit), 4 heads of every span (deviation unused, the budget shared evenly).
 enum SpanMode { SPAN_DOC = 1, SPAN_RANKED = 3, SPAN_HEADS = 4 };
 struct SpanArgs { int n_spans; int mode; int b[MAX_SPANS + 1]; int order[MAX_SPANS]; };
-// ws: topk_token_ws_bytes(n) bytes (none below the large-n threshold, where one workgroup runs)
+// ws: topk_token_ws_bytes(n) bytes (none below the large-n threshold, where one workgroup runs). At
+// least topk_token_ws_min_bytes(n) are required; what lies beyond them holds the candidate list
+// (8 bytes per candidate), and with less room than the threshold's bin needs the selection reads
+// all n keys twice more instead (same result).
 size_t topk_token_ws_bytes(int n);
-hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws, hipStream_t st);
+size_t topk_token_ws_min_bytes(int n);
+hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws, size_t ws_bytes, hipStream_t st);
 hipError_t launch_topk_spans(const float* dev, int n, int k, const SpanArgs& sp, int* out,
                              double* ws, hipStream_t st);
 

@@ -55,6 +55,17 @@ def test_topk_validation(L):
     # token mode from n = 65536 on runs on the whole GPU and needs a workspace
     assert cf.topk_workspace_size(65535, "token") == 0 and cf.topk_workspace_size(65536, "token") > 0
     assert L.cf_topk_select(None, 1 << 20, 5, 0, None, 0, None, None, 0, None) == cf.CF_EWORKSPACE
+    # from the minimum up any workspace is accepted (the rest holds candidates: n / 16 at the full size)
+    for n in (1 << 16, 1 << 20, 3000017, (1 << 28) + 5):
+        lo, hi = cf.topk_workspace_min_size(n, "token"), cf.topk_workspace_size(n, "token")
+        assert 0 < lo < 64 << 10 and hi >= lo + 8 * (n // 16), n
+    for mode in ("doc", "ranked", "heads"):
+        assert cf.topk_workspace_min_size(1000, mode) == cf.topk_workspace_size(1000, mode)
+    assert cf.topk_workspace_min_size(65535, "token") == 0
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: both calls fail on the host
+    lo = cf.topk_workspace_min_size(1 << 20, "token")
+    assert L.cf_topk_select(None, 1 << 20, 5, 0, None, 0, None, fake, lo - 1, None) == cf.CF_EWORKSPACE
+    assert L.cf_topk_select(None, 1 << 20, 5, 0, None, 0, None, fake, lo, None) == cf.CF_EINVAL  # null values
 
 
 def test_deviation_validation(L):

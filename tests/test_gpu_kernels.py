@@ -127,6 +127,46 @@ def test_topk_large_n_multiblock_bit_exact(n):
             assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (n, trial, k)
 
 
+def _order_keys(d):
+    """Order-preserving 32-bit keys of float32 values (NaN as +inf, -0 as +0), for the test to find
+    how many values share the threshold key's top 16 bits."""
+    u = np.asarray(d, np.float32).view(np.uint32).copy()
+    u[(u & 0x7FFFFFFF) > 0x7F800000] = 0x7F800000
+    u[(u & 0x7FFFFFFF) == 0] = 0
+    neg = (u & 0x80000000) != 0
+    return np.where(neg, ~u, u | 0x80000000).astype(np.uint32)
+
+
+@pytest.mark.parametrize("n", [(1 << 18) + 5, 2000003])
+def test_topk_candidate_list_capacity_edges(n):
+    """The whole-GPU selection keeps the values that share the threshold key's top 16 bits in a
+    candidate list when the workspace has room for all of them, and otherwise reads all n values
+    twice more. Workspaces with room for exactly that many, one fewer, none, and the full size, and
+    a value array 4 bytes off 16-byte alignment, must all give the oracle's unique answer."""
+    torch = _torch()
+    rng = np.random.default_rng(n)
+    d = rng.standard_normal(n).astype(np.float32) ** 2  # skewed, as deviations are
+    d[rng.integers(0, n, n // 100)] = np.float32(1.0)   # a block of ties
+    d[rng.integers(0, n, 50)] = np.nan
+    buf = torch.from_numpy(np.concatenate([np.zeros(1, np.float32), d])).cuda()
+    aligned = buf[1:].clone()
+    keys = _order_keys(d)
+    srt = np.sort(keys)[::-1]
+    base = cf.topk_workspace_min_size(n, "token")
+    for k in (1, n // 7, n // 2, n):
+        want = oracle.select_topk(d, k).tolist()
+        h = int(np.count_nonzero((keys >> 16) == (srt[k - 1] >> 16)))
+        say(f"topk capacity n={n} k={k} h={h}")
+        for room in (h, h - 1, 0, None):
+            nbytes = cf.topk_workspace_size(n, "token") if room is None else base + 8 * room
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            for vals in (aligned, buf[1:]):
+                out = torch.full((k,), -1, dtype=torch.int32, device="cuda")
+                cf.topk_select(vals, k, out, "token", None, ws)
+                torch.cuda.synchronize()
+                assert out.cpu().numpy().tolist() == want, (n, k, room, vals.data_ptr() % 16)
+
+
 @pytest.mark.parametrize("case", _golden.doc_span_cases())
 def test_doc_spans_golden(case):
     d, b, k, want = case
