@@ -5,7 +5,7 @@
 // through the partially fused cache.
 //
 // bf16 path (head_dim 64/128): one block = 128 query rows of one kv head, 8 waves; keys stream
-// in blocks of 64 through a 3-stage LDS ring filled by direct global->LDS loads; K and V tiles
+// in blocks of 64 through a ring of LDS stages filled by direct global->LDS loads; K and V tiles
 // are stored row-major with a 16-byte-chunk XOR swizzle by key, and the V^T operand is read with
 // gfx950's transposing LDS read (ds_read_b64_tr_b16).
 // S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16: in this orientation every lane
@@ -91,28 +91,37 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
   const int nkb = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
 
   // load q of this wave: instruction gi = q * NW + w covers key rows [ii * RPI, ii * RPI + RPI)
-  // of tensor gi / (NI / 2) (0 = K, 1 = V), ii = gi % (NI / 2)
+  // of tensor gi / (NI / 2) (0 = K, 1 = V), ii = gi % (NI / 2). The tile row of a lane is
+  // ii * RPI + lane / NCH; ii * RPI is wave-uniform and, for every q, congruent to w * RPI modulo
+  // NCH, so the swizzled chunk of a lane is one value for all its K loads and one for all its V
+  // loads. Each load is the scalar base of the head's K or V columns plus a 32-bit lane offset.
+  static_assert((NI / 2) % NW == 0 && (NW * RPI) % NCH == 0, "one swizzled chunk per lane and tensor");
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
-  const bf16* src[NL];
-  int trow[NL];
-#pragma unroll
-  for (int q = 0; q < NL; ++q) {
-    const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
-    const int t = ii * RPI + lane / NCH;
-    const int c = (lane % NCH) ^ (tensor ? vswz<HD>(t) : (t & SWM));
-    src[q] = (const bf16*)(tensor ? a.v : a.k) + g * HD + c * 8;
-    trow[q] = t;
-  }
+  const bf16* kbase_p = (const bf16*)a.k + g * HD;
+  const bf16* vbase_p = (const bf16*)a.v + g * HD;
+  const int t0 = (w * RPI) % KB + lane / NCH;  // congruent modulo NCH to every load's tile row
+  const uint32_t colk = 16u * (uint32_t)((lane % NCH) ^ (t0 & SWM));
+  const uint32_t colv = 16u * (uint32_t)((lane % NCH) ^ vswz<HD>(t0));
+  const int lrow = lane / NCH;
+  const uint32_t row_bytes = 2u * (uint32_t)kvd;
   auto issue = [&](int step) __attribute__((always_inline)) {
     const int stage = step % S;
     const int kbase = kbeg + step * KB;
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const int gi = q * NW + w, tensor = gi / (NI / 2), ii = gi % (NI / 2);
-      const bf16* gp = src[q] + (int64_t)min(kbase + trow[q], a.L - 1) * kvd;
+      // with (NI / 2) % NW == 0 the tensor depends on q alone: the first NL / 2 loads are K
+      constexpr int HALF = NL / 2;
+      const bool vt = q >= HALF;
+      const int ii = (q % HALF) * NW + w;
+      const uint32_t off = (uint32_t)min(kbase + ii * RPI + lrow, a.L - 1) * row_bytes + (vt ? colv : colk);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          lds0 + 2u * (uint32_t)(stage * 2 * TILE + tensor * TILE + ii * RPI * HD));
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(dst) : "memory", "m0");
+          lds0 + 2u * (uint32_t)(stage * 2 * TILE + (vt ? TILE : 0) + ii * RPI * HD));
+      if (vt)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(vbase_p), "s"(dst)
+                     : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(kbase_p), "s"(dst)
+                     : "memory", "m0");
     }
   };
   // the first S - 1 key blocks go out before the queries are read: their latency overlaps
@@ -239,17 +248,32 @@ __global__ __launch_bounds__(NW * WAVE, MINB) void attn_dtl_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) pf[rg][mm][tp * 4 + i] = (bf16)s[rg][2 * mm + tp][i];
     }
+    // O^T += V^T P^T over fragments f = 2 nt + mm. At 4 waves per SIMD the kernel has 128 VGPRs,
+    // and left alone the compiler reads each fragment's V^T operand (two transposing reads) into
+    // the same registers right before its product, exposing the LDS latency on all 16 products;
+    // here each operand is read two fragments ahead (the groups are pinned for the scheduler)
+    auto vfrag = [&](int f) __attribute__((always_inline)) {
+      const int nt = f / 2, mm = f % 2;
+      const i16x4 lo = vread(Vt, 32 * mm + 4 * lg, nt);
+      const i16x4 hi = vread(Vt, 32 * mm + 16 + 4 * lg, nt);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NF = 2 * (HD / 16);
+    bf16x8 vcur = vfrag(0), vn1 = vfrag(1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int nt = 0; nt < HD / 16; ++nt) {
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const i16x4 lo = vread(Vt, 32 * mm + 4 * lg, nt);
-        const i16x4 hi = vread(Vt, 32 * mm + 16 + 4 * lg, nt);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-          o[rg][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rg][mm], o[rg][nt], 0, 0, 0);
+    for (int f = 0; f < NF; ++f) {
+      bf16x8 vn2 = vn1;
+      if (f + 2 < NF) {
+        vn2 = vfrag(f + 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        o[rg][f / 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur, pf[rg][f % 2], o[rg][f / 2], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RG, 0);
+      vcur = vn1;
+      vn1 = vn2;
     }
   };
 
@@ -318,6 +342,8 @@ struct AttnCfg {
 
 template <class C>
 hipError_t launch_attention_cfg(const AttnArgs& a, hipStream_t st) {
+  // the tile loads address a head's K/V columns with 32-bit byte offsets from the cache start
+  if ((int64_t)a.L * a.hkv * a.hd * 2 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const int G = a.hq / a.hkv, rpt = 128 / G;
   dim3 grid(a.sched ? a.P * a.hkv : ((a.n + rpt - 1) / rpt) * a.hkv);
   if (a.hd == 128)
