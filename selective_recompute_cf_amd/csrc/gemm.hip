@@ -414,20 +414,36 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void gemm_bf16_dtl(GemmArgs a)
     auto interleave = [](auto sync_id) __attribute__((always_inline)) {
       sched_interleave<NM, NF, decltype(sync_id)::value>(std::make_integer_sequence<int, NF>{});
     };
-    FVec f0 = fread(0, 0), f1;
-    for (int s = 0; s < nk; ++s) {
-      if constexpr (!EARLY) issue(min(s + S - 1, last));  // the stage step s - 1 used
-      f1 = fread(s % S, 1);
-      fmma(f0);
-      interleave(std::integral_constant<int, 0>{});
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 0));
-      barrier();
-      if constexpr (EARLY) issue(min(s + S, last));  // the stage step s used
-      f0 = fread((s + 1) % S, 0);
-      fmma(f1);
-      interleave(std::integral_constant<int, 1>{});
-      __builtin_amdgcn_sched_barrier(0);
+    // the 256-row tile (full-row layers) keeps the single path: at its 256 registers a second
+    // path makes the compiler spill
+    constexpr bool SKIP = BM <= 128;
+    if (!SKIP || m0 + wm * C::TM < a.M) {  // wave-uniform: some of this wave's rows are real
+      FVec f0 = fread(0, 0), f1;
+      for (int s = 0; s < nk; ++s) {
+        if constexpr (!EARLY) issue(min(s + S - 1, last));  // the stage step s - 1 used
+        f1 = fread(s % S, 1);
+        fmma(f0);
+        interleave(std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 0));
+        barrier();
+        if constexpr (EARLY) issue(min(s + S, last));  // the stage step s used
+        f0 = fread((s + 1) % S, 0);
+        fmma(f1);
+        interleave(std::integral_constant<int, 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (SKIP) {
+      // every row of this wave lies past M (the padding of the last row tile): it still issues
+      // its share of the tile loads and meets every barrier, but reads no fragments and runs no
+      // MFMAs, so the matrix cores of its SIMD are left to the other waves and blocks (its
+      // accumulators stay zero, and the epilogue skips rows past M)
+      for (int s = 0; s < nk; ++s) {
+        if constexpr (!EARLY) issue(min(s + S - 1, last));
+        __builtin_amdgcn_s_waitcnt(CF_WAITCNT((S - 2) * NL, 0));
+        barrier();
+        if constexpr (EARLY) issue(min(s + S, last));
+      }
     }
     __builtin_amdgcn_s_waitcnt(CF_WAITCNT(0, 0));  // drain the trailing repeat loads
   }
