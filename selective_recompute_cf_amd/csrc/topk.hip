@@ -164,7 +164,9 @@ struct TopkState {
 };
 static_assert(sizeof(TopkState) <= 256, "state slot");
 
-static int tk_mb_blocks(int n) { return std::min(TK_MB_MAX_BLOCKS, (n + TK_MB_SEG - 1) / TK_MB_SEG); }
+static int tk_mb_blocks(int n) {
+  return (int)std::min<int64_t>(TK_MB_MAX_BLOCKS, ((int64_t)n + TK_MB_SEG - 1) / TK_MB_SEG);
+}
 
 // histograms, state, per-block counts and offsets; the candidate list follows
 static size_t tk_mb_fixed_bytes(int n) {
