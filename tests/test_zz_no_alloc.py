@@ -3,7 +3,7 @@ graph capture or in loops that cannot allocate) against cf_topk_select with a ca
 bit-identical selections on two calls in a row, the second with a smaller input, for token top-k
 on the whole-GPU path (n >= 65536, which uses the scratch), on the one-workgroup path, and for
 document-aligned spans; a selection whose scratch would exceed the fixed array is rejected on the
-host before anything is enqueued."""
+host before anything is enqueued; and the call captured in a HIP graph replays correctly on new values."""
 import numpy as np
 import pytest
 
@@ -54,3 +54,46 @@ def test_noalloc_rejects_selections_beyond_the_scratch():
     assert e.value.status == cf.CF_EWORKSPACE and "scratch" in str(e.value)
     torch.cuda.synchronize()
     assert bool((out == -3).all())
+
+
+@pytest.mark.parametrize("n,k", [(3_000_017, 450_002), (5000, 750)])
+def test_noalloc_selection_replays_from_a_hip_graph(n, k):
+    """The callers this entry point is for include code under HIP graph capture: captured once (on
+    the whole-GPU path and on the one-workgroup path), then replayed three times with new values
+    copied into the captured input, with eager calls and syncs in between; every replay equals a
+    workspace call on the same values."""
+    import torch
+    d = torch.empty(n, device="cuda")
+    out = torch.full((k,), -1, dtype=torch.int32, device="cuda")
+    want = torch.full((k,), -2, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(cf.topk_workspace_size(n, "token"), 1), dtype=torch.uint8, device="cuda")
+
+    def values(seed):
+        g = torch.Generator().manual_seed(seed)
+        v = torch.rand(n, generator=g)
+        v[torch.randint(0, n, (n // 50,), generator=g)] = 0.5  # ties at one value
+        return v.cuda()
+
+    d.copy_(values(31))
+    side = torch.cuda.Stream()  # warm-up off the capture: the scratch address is looked up here
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cf.topk_select_noalloc(d, k, out, "token")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cf.topk_select_noalloc(d, k, out, "token")
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"noalloc graph n={n} replay {rep}")
+        d.copy_(values(32 + rep))
+        out.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        cf.topk_select(d, k, want, "token", None, ws)  # eager, with a workspace, between replays
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        np.testing.assert_array_equal(got, want.cpu().numpy())
+        assert np.all(np.diff(got) > 0)
