@@ -473,6 +473,7 @@ using GemmDtl128 = DtlCfg<128, 256, 2, 4, 3, 1, 16>;  // waves 64x64, 3 x 48 KB 
 using GemmDtl96 = DtlCfg<96, 256, 2, 4, 3, 1, 16>;    // waves 48x64, 3 x 44 KB stages
 using GemmDtl64 = DtlCfg<64, 256, 1, 8, 4, 1, 16>;    // waves 64x32, 4 x 40 KB stages
 using GemmDtl256 = DtlCfg<256, 256, 2, 4, 2, 1, 16>;  // waves 128x64, 2 x 64 KB stages (many rows)
+using GemmDtl224 = DtlCfg<224, 256, 2, 4, 2, 1, 16>;  // waves 112x64, 2 x 60 KB stages (3136 rows = 14 tiles)
 using GemmDtl128n = DtlCfg<128, 192, 4, 2, 3, 1, 16>; // waves 32x96, 3 x 40 KB stages (finer weight tiles)
 using GemmDtl64n = DtlCfg<64, 128, 1, 4, 3, 2, 16>;   // 4 waves 64x32, 3 x 24 KB stages, 2 blocks per CU (few rows)
 
@@ -548,9 +549,10 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
   // units. (At 0.0131 the 3136-row QKV product took two splits: 187 against 176 us for one in the
   // standalone harness, before its post-processing read twice the partial sums.)
   struct Opt { int cfg, bm, bn, per_cu; double rate; };
-  const Opt dtl_opts[6] = {{GEMM_DTL128, 128, 256, 1, 1.0},  {GEMM_DTL96, 96, 256, 1, 0.86},
+  const Opt dtl_opts[7] = {{GEMM_DTL128, 128, 256, 1, 1.0},  {GEMM_DTL96, 96, 256, 1, 0.86},
                            {GEMM_DTL64, 64, 256, 1, 0.65},   {GEMM_DTL256, 256, 256, 1, 1.15},
-                           {GEMM_DTL128N, 128, 192, 1, 1.0}, {GEMM_DTL64N, 64, 128, 2, 0.7}};
+                           {GEMM_DTL128N, 128, 192, 1, 1.0}, {GEMM_DTL224, 224, 256, 1, 1.05},
+                           {GEMM_DTL64N, 64, 128, 2, 0.7}};
   const Opt small_opt[1] = {{GEMM_SMALL, 128, 128, 2, 0.85}};
   const bool dtl = K % 64 == 0;
   const Opt* opts = dtl ? dtl_opts : small_opt;
@@ -558,7 +560,7 @@ GemmPlan gemm_plan(Dt dt, int M, int N, int K, bool swiglu, bool allow_split, in
   // column tiles put every CU on that stream. Measured faster on every projection at 64 rows and
   // on the split-K ones at 128 (down 37.6 against 53.0 us); slower on gate/up from 128 rows and
   // on the others from about 200, where the row tiles share each weight tile.
-  const int n_opts = dtl ? (M <= 64 || (M <= 128 && !swiglu) ? 6 : 5) : 1;
+  const int n_opts = dtl ? (M <= 64 || (M <= 128 && !swiglu) ? 7 : 6) : 1;
   const int cols = swiglu ? 2 * N : N;
   double best_cost = 1e300;
   for (int o = 0; o < n_opts; ++o) {
@@ -588,6 +590,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       case GEMM_DTL96: return launch_gemm_dtl<GemmDtl96>(a, st);
       case GEMM_DTL64: return launch_gemm_dtl<GemmDtl64>(a, st);
       case GEMM_DTL256: return launch_gemm_dtl<GemmDtl256>(a, st);
+      case GEMM_DTL224: return launch_gemm_dtl<GemmDtl224>(a, st);
       case GEMM_DTL128N: return launch_gemm_dtl<GemmDtl128n>(a, st);
       case GEMM_DTL64N: return launch_gemm_dtl<GemmDtl64n>(a, st);
       default: return launch_gemm_cfg<GemmSmall>(a, st);

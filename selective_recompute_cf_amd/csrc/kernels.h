@@ -97,7 +97,8 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 enum GemmCfgId {
-  GEMM_SMALL = 0, GEMM_DTL128 = 1, GEMM_DTL96 = 2, GEMM_DTL64 = 3, GEMM_DTL256 = 4, GEMM_DTL128N = 5, GEMM_DTL64N = 6
+  GEMM_SMALL = 0, GEMM_DTL128 = 1, GEMM_DTL96 = 2, GEMM_DTL64 = 3, GEMM_DTL256 = 4, GEMM_DTL128N = 5, GEMM_DTL64N = 6,
+  GEMM_DTL224 = 7
 };
 struct GemmPlan { int cfg; int splits; };
 // Kernel, block height and split-K factor for an M x N x K product: a direct-to-LDS kernel when
