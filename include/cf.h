@@ -206,11 +206,13 @@ cf_status cf_selection_deviation(const cf_ctx* ctx, const cf_layer_weights* w /*
  * n_spans <= CF_MAX_SPANS. ws: device workspace of cf_topk_workspace_size(n, mode) bytes
  * (document-aligned mode always; token mode from n = 65536 up, where the selection runs on the
  * whole GPU; the size is 0 otherwise and ws may be NULL). Token mode also runs with less, down to
- * cf_topk_workspace_min_size(n, mode) bytes: beyond that minimum the workspace holds a list of the
- * keys left undecided after two histogram passes (8 bytes each, room for n / 16 at the full size);
- * when they do not fit, the selection reads all n values twice more instead, with the same result.
- * For the other modes the two sizes are equal. A call with less than the minimum fails with
- * CF_EWORKSPACE before anything is enqueued. */
+ * cf_topk_workspace_min_size(n, mode) bytes (about n / 4 + 140 KB: a 2-bit map of the n values,
+ * sampled keys and per-range counts): beyond that minimum the workspace holds the values left
+ * undecided by a sampled band around the threshold (4 bytes each: a list of up to n / 16 first,
+ * then per-range slices; the full size has room for n / 16 in each); when they do not fit, the
+ * selection falls back to histogram passes over all n values, with the same result. For the other
+ * modes the two sizes are equal. A call with less than the minimum fails with CF_EWORKSPACE before
+ * anything is enqueued. */
 #define CF_MAX_SPANS 256
 size_t cf_topk_workspace_size(int32_t n, int32_t mode);
 size_t cf_topk_workspace_min_size(int32_t n, int32_t mode);
@@ -225,8 +227,8 @@ cf_status cf_topk_select(const float* dev, int32_t n, int32_t k, int32_t mode,
  * array of CF_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
  * ends; the call allocates and frees nothing. A selection needing more scratch than that
  * (cf_topk_workspace_min_size(n, mode) > CF_NOALLOC_SCRATCH_BYTES: document-aligned spans beyond
- * n = 524287; token mode fits any n, its candidate list taking the rest of the array) fails with
- * CF_EWORKSPACE before anything is enqueued. Every
+ * n = 524287, token mode beyond about 15.8 million values, its undecided values taking the rest of the
+ * array) fails with CF_EWORKSPACE before anything is enqueued. Every
  * call on one GPU uses that GPU's one array (the current device's), and the kernels initialise what
  * they read: calls that may overlap on one GPU (other streams, other threads) race on it and must be
  * ordered by the caller, e.g. on one stream. */

@@ -15,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcf.so")
 
 CF_OK, CF_EINVAL, CF_ESHAPE, CF_EDTYPE, CF_EUNSUPPORTED, CF_EWORKSPACE, CF_EHIP = range(7)
+CF_NOALLOC_SCRATCH_BYTES = 4 << 20  # include/cf.h: the fixed scratch of cf_topk_select_noalloc
 CF_F32, CF_BF16 = 0, 1
 CF_SEL_TOKEN_TOPK, CF_SEL_DOC_SPANS, CF_SEL_ALL, CF_SEL_RANKED_SPANS, CF_SEL_SPAN_HEADS, CF_SEL_GIVEN = range(6)
 ANCHOR_RULES = {"sink": 0, "knorm": 1, "knorm_low": 2}

@@ -158,9 +158,10 @@ constexpr int MAX_SPANS = 256;
 enum SpanMode { SPAN_DOC = 1, SPAN_RANKED = 3, SPAN_HEADS = 4 };
 struct SpanArgs { int n_spans; int mode; int b[MAX_SPANS + 1]; int order[MAX_SPANS]; };
 // ws: topk_token_ws_bytes(n) bytes (none below the large-n threshold, where one workgroup runs). At
-// least topk_token_ws_min_bytes(n) are required; what lies beyond them holds the candidate list
-// (8 bytes per candidate), and with less room than the threshold's bin needs the selection reads
-// all n keys twice more instead (same result).
+// least topk_token_ws_min_bytes(n) are required (state, sampled keys, per-range counts and a 2-bit
+// map of the n keys); what lies beyond them holds the undecided keys (4 bytes each: a list of up to
+// n / 16, then per-range slices), and with less room the selection falls back to histogram passes
+// over all n keys (same result).
 size_t topk_token_ws_bytes(int n);
 size_t topk_token_ws_min_bytes(int n);
 hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws, size_t ws_bytes, hipStream_t st);

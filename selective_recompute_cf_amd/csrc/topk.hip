@@ -140,76 +140,455 @@ __global__ __launch_bounds__(TK_THREADS) void topk_token_kernel(const float* __r
 }
 
 // ----------------------------------------------------------------------------- token, large n
-// The same exact selection spread over the whole GPU for n >= TK_MB_MIN. Two 8-bit histogram
-// passes over the n keys (LDS histograms merged with global atomics), each followed by a
-// one-thread pick of the digit, fix the top 16 bits of the threshold key T. One collect pass then
-// counts, per block range, the keys whose top 16 bits lie above T's and appends the keys that
-// share them (the only ones still undecided) to a candidate list with their indices. The last two
-// digits of T and the per-range counts of keys above / equal to T come from that list alone. A
-// one-block scan turns the counts into output offsets and ranks among equal keys (lower index
-// first), and an ordered write of each block's range, the fourth and last read of the n keys,
-// writes the positions. When the threshold's 16-bit bin holds more keys than the candidate list
-// has room for (known from the second histogram before anything is collected), the last two
-// digits and the counts come from passes over all n keys instead. No block waits for another.
+// The same exact selection spread over the whole GPU for n >= TK_MB_MIN, reading the n keys once
+// in the usual case.
+//
+// The index range is cut into sub-ranges of sw indices, one wave each. A one-block pass draws a
+// stratified sample of TK_SAMPLE keys (one at a hashed offset inside each of TK_SAMPLE equal
+// strata) and takes two of its order statistics as bounds lo <= hi that bracket the threshold key
+// T (the k-th largest) with a margin of four standard deviations of the sample rank. One pass
+// over the n keys then writes a map of 2 bits per index (taken: key > hi; undecided: lo <= key <=
+// hi) and appends the undecided keys, in index order, to their sub-range's slice of a candidate
+// list, counting both per sub-range. If fewer than k keys lie above hi and at least k at or above
+// lo, T lies in the band: when lo == hi it is lo itself; otherwise, if the undecided keys fit the
+// list, T is the (k - above)-th largest candidate, which 8-bit digit passes over the (small) list
+// find (a digit that lo and hi share needs no pass). The candidates of each sub-range are then
+// counted above / equal to T, a one-block scan turns the counts into output offsets and ranks
+// among equal keys (lower index first), and the ordered write reads only the map and the
+// candidates.
+//
+// Otherwise (a sample that missed, or too many undecided keys for the workspace) two 8-bit
+// histogram passes over the n keys fix T's top 16 bits and the same collect pass runs with the
+// keys sharing them as the undecided band; if those do not fit either, the last two digits come
+// from histograms over all n keys and a counting pass over the n keys rewrites the map against T
+// itself (taken: key > T; undecided: key == T). Every route gives the same positions; no block
+// waits for another.
 constexpr int TK_MB_MIN = 1 << 16;
-constexpr int TK_MB_SEG = 16384;       // indices per count / write block (at least)
-constexpr int TK_MB_MAX_BLOCKS = 2048;
-constexpr int TK_HIST_BLOCKS = 1024;   // histogram blocks (grid-stride), fewer merges into the global bins
+constexpr int TK_SUB_MIN = 1024;      // indices per sub-range at least (a multiple of 1024)
+constexpr int TK_MAX_SUB = 4096;      // sub-ranges at most: every wave of a per-range kernel resident at once
+constexpr int TK_SUB_PER = (TK_MAX_SUB + TK_THREADS - 1) / TK_THREADS;  // sub-ranges per scan thread
+constexpr int TK_HIST_BLOCKS = 1024;  // histogram blocks over all n (grid-stride)
+constexpr int TK_SAMPLE = 32768;      // sampled keys
+constexpr int TK_SPT = TK_SAMPLE / TK_THREADS;  // per thread: strata 32 t .. 32 t + 31
+constexpr int TK_COARSE = 8;          // every 8th sampled key (4096, evenly spread) for the coarse band
+constexpr int TK_WPB = 4;             // waves (sub-ranges) per block in the per-range kernels
+
+enum : int { TK_UNSET = 0, TK_SAMPLED = 1, TK_FALLBACK = 2, TK_BIN = 3, TK_OVERFLOW = 4, TK_EXACT = 5 };
 
 struct TopkState {
-  uint32_t prefix[5];  // prefix[p]: the top 8p bits of T fixed by passes < p
+  uint32_t prefix[5];  // prefix[p]: the top 8p bits of T fixed by digit passes < p
   int kk[5];           // kk[p]: keys still owed among those matching prefix[p]
-  int overflow;        // 1: the threshold's 16-bit bin does not fit the candidate list
-  int n_cand;          // candidates appended by the collect pass
+  uint32_t lo, hi;     // the undecided band of the current collect pass
+  int mode;            // TK_*: which route the selection takes
+  int n_cand;          // keys in the candidate list
 };
 static_assert(sizeof(TopkState) <= 256, "state slot");
 
-static int tk_mb_blocks(int n) {
-  return (int)std::min<int64_t>(TK_MB_MAX_BLOCKS, ((int64_t)n + TK_MB_SEG - 1) / TK_MB_SEG);
+// sw: indices per sub-range, n_sub: sub-ranges (n_sub * sw >= n; 64-bit: n may be near INT_MAX)
+static void tk_geom(int n, int& sw, int& n_sub) {
+  const int64_t per = ((int64_t)n + TK_MAX_SUB - 1) / TK_MAX_SUB;
+  sw = (int)std::max<int64_t>(TK_SUB_MIN, (per + TK_SUB_MIN - 1) / TK_SUB_MIN * TK_SUB_MIN);
+  n_sub = (int)(((int64_t)n + sw - 1) / sw);
 }
 
-// histograms, state, per-block counts and offsets; the candidate list follows
+// per sub-range: taken, undecided and equal counts, candidate offset, output offset, equal keys before
+constexpr int TK_SUB_ARRAYS = 6;
+static size_t tk_sub_bytes(int n_sub) { return ((size_t)n_sub * TK_SUB_ARRAYS * sizeof(int) + 255) / 256 * 256; }
+
+constexpr size_t TK_HEAD_BYTES = 4 * 256 * sizeof(uint32_t) + 256 + TK_SAMPLE * sizeof(uint32_t);
+
+// histograms, state, sampled keys, per-sub-range arrays and the 2-bit map; the candidate slices
+// and list follow
 static size_t tk_mb_fixed_bytes(int n) {
-  return 4 * 256 * sizeof(uint32_t) + 256 + (size_t)tk_mb_blocks(n) * 4 * sizeof(int);
+  int sw, n_sub;
+  tk_geom(n, sw, n_sub);
+  return TK_HEAD_BYTES + tk_sub_bytes(n_sub) + (size_t)n_sub * sw / 4;
 }
 
 size_t topk_token_ws_min_bytes(int n) { return n < TK_MB_MIN ? 0 : tk_mb_fixed_bytes(n); }
 
 size_t topk_token_ws_bytes(int n) {
   if (n < TK_MB_MIN) return 0;
-  return tk_mb_fixed_bytes(n) + (size_t)(n / 16) * 2 * sizeof(uint32_t);  // room for n/16 candidates
+  int sw, n_sub;
+  tk_geom(n, sw, n_sub);
+  // a list of n/16 candidates, then slices of sw/16 per sub-range
+  return tk_mb_fixed_bytes(n) + (size_t)(n / 16) * sizeof(uint32_t) + (size_t)n_sub * (sw / 16) * sizeof(uint32_t);
 }
 
-__global__ __launch_bounds__(TK_THREADS) void tk_mb_init_kernel(uint32_t* hist, TopkState* st, int k) {
+__device__ __forceinline__ uint32_t tk_hash(uint32_t x) {  // Wellons' "lowbias32" integer hash
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+  const int lane = threadIdx.x % WAVE;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const int y = __shfl_up(x, o, WAVE);
+    if (lane >= o) x += y;
+  }
+  total = __shfl(x, WAVE - 1, WAVE);
+  return x - v;
+}
+
+__device__ __forceinline__ int wave_isum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// orders one wave's LDS writes before its other lanes' reads (no block barrier)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16 copies of the 256 bins (lane % 16 picks the copy): most float keys fall into a few top-byte
+// bins, and same-address LDS atomics serialise. Rows of 257 words put the copies of a bin in
+// different banks.
+constexpr int TK_HCOPIES = 16;
+
+struct TkSel {
+  uint32_t h[2][TK_HCOPIES][257];
+  int wtot[2][256 / WAVE];
+  uint32_t pre[2];
+  int rem[2];
+  int cnt[2];
+};
+
+// Two radix selects in one block (4 passes of 8 bits, shared): the keys at descending ranks
+// r0 and r1 (1-based; a search with act false is skipped) among key[j] for j = 0, STEP, 2 STEP, ...
+// that lie in [blo, bhi]. Every thread of the block calls it.
+template <int STEP>
+__device__ void tk_select2(const uint32_t (&key)[TK_SPT], uint32_t blo, uint32_t bhi, int r0, int r1, bool a0,
+                           bool a1, TkSel& s, uint32_t& out0, uint32_t& out1) {
+  __syncthreads();  // earlier readers of s are done
+  if (threadIdx.x == 0) {
+    s.pre[0] = s.pre[1] = 0;
+    s.rem[0] = r0;
+    s.rem[1] = r1;
+  }
+  const int lane = threadIdx.x % WAVE, q = (threadIdx.x / 256) & 1, t = threadIdx.x % 256;
+  const bool act_mine = q == 0 ? a0 : a1;
+  for (int pass = 0; pass < 4; ++pass) {
+    for (int i = threadIdx.x; i < 2 * TK_HCOPIES * 257; i += TK_THREADS) (&s.h[0][0][0])[i] = 0u;
+    __syncthreads();
+    const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
+    const int shift = 24 - 8 * pass;
+    const uint32_t p0 = s.pre[0], p1 = s.pre[1], pre_mine = s.pre[q];
+    const int r_mine = s.rem[q];
+    const int c = threadIdx.x % TK_HCOPIES;
+#pragma unroll
+    for (int j = 0; j < TK_SPT; j += STEP) {
+      const uint32_t x = key[j];
+      if (x < blo || x > bhi) continue;
+      const uint32_t d = (x >> shift) & 255u;
+      if (a0 && (x & mask) == p0) atomicAdd(&s.h[0][c][d], 1u);
+      if (a1 && (x & mask) == p1) atomicAdd(&s.h[1][c][d], 1u);
+    }
+    __syncthreads();
+    // threads 0..511: search q takes bin 255 - t; counts accumulate from the top bin down
+    int cnt = 0;
+    if (threadIdx.x < 512)
+#pragma unroll
+      for (int cc = 0; cc < TK_HCOPIES; ++cc) cnt += (int)s.h[q][cc][255 - t];
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+      const int y = __shfl_up(incl, off, WAVE);
+      if (lane >= off) incl += y;
+    }
+    if (threadIdx.x < 512 && lane == WAVE - 1) s.wtot[q][t / WAVE] = incl;
+    __syncthreads();
+    if (threadIdx.x < 512 && act_mine) {
+      for (int wv = 0; wv < t / WAVE; ++wv) incl += s.wtot[q][wv];
+      const int above = incl - cnt;
+      if (above < r_mine && incl >= r_mine) {
+        s.pre[q] = pre_mine | ((uint32_t)(255 - t) << shift);
+        s.rem[q] = r_mine - above;
+      }
+    }
+    __syncthreads();
+  }
+  out0 = s.pre[0];
+  out1 = s.pre[1];
+}
+
+// The stratified sample, one key a thread over many blocks (random reads need many CUs): stratum s
+// (indices [s n / S, (s + 1) n / S)) gives the key at a hashed offset inside it, stored at
+// (s % 32) * 1024 + s / 32 so that the selecting block reads its keys coalesced.
+__global__ __launch_bounds__(256) void tk_mb_gather_kernel(const float* __restrict__ dev, int n, uint32_t* skey) {
+  const int sidx = blockIdx.x * 256 + (int)threadIdx.x;
+  const int64_t jit = (int64_t)(((uint64_t)tk_hash((uint32_t)sidx) * (uint32_t)n) >> 32);  // in [0, n)
+  const int64_t pos = ((int64_t)sidx * n + jit) / TK_SAMPLE;                               // in stratum sidx
+  skey[(sidx % TK_SPT) * TK_THREADS + sidx / TK_SPT] = order_key(dev[pos]);
+}
+
+// Bounds of the undecided band from the sample: the keys at descending sample ranks
+// mu -/+ (4 sd + 2), mu = k S / n, sd = sqrt(S p (1 - p)), p = k / n. A coarse band from every 8th
+// sampled key (ranks mu' -/+ (6 sd' + 3) of those 4096) first, then the exact order statistics
+// among the sampled keys inside it, so that the histograms see few keys. A rank below 1 leaves hi
+// at the largest key, one past S leaves lo at the smallest; a target outside the coarse band
+// (which only widens the band) takes the coarse bound or the extreme key.
+// Also clears the digit histograms and the state.
+__global__ __launch_bounds__(TK_THREADS) void tk_mb_sample_kernel(const uint32_t* __restrict__ skey, int n, int k,
+                                                                  uint32_t* hist, TopkState* st) {
+  __shared__ TkSel s;
   hist[threadIdx.x] = 0;  // 4 x 256 bins
   if (threadIdx.x == 0) {
     st->prefix[0] = 0;
-    st->kk[0] = k;
-    st->overflow = 0;
+    st->kk[0] = 0;
+    st->mode = TK_UNSET;
     st->n_cand = 0;
+  }
+  uint32_t key[TK_SPT];  // key[j]: stratum TK_SPT * thread + j
+#pragma unroll
+  for (int j = 0; j < TK_SPT; ++j) key[j] = skey[j * TK_THREADS + threadIdx.x];
+  const double p = (double)k / n;
+  constexpr int S1 = TK_SAMPLE / TK_COARSE;
+  const double mu1 = p * S1, sd1 = sqrt(S1 * p * (1.0 - p));
+  const double ch_r = floor(mu1 - 6.0 * sd1 - 3.0), cl_r = ceil(mu1 + 6.0 * sd1 + 3.0);
+  const bool ca0 = ch_r >= 1.0, ca1 = cl_r <= (double)S1;
+  uint32_t ch = 0xffffffffu, cl = 0u;
+  tk_select2<TK_COARSE>(key, 0u, 0xffffffffu, ca0 ? (int)ch_r : 0, ca1 ? (int)cl_r : 0, ca0, ca1, s, ch, cl);
+  if (!ca0) ch = 0xffffffffu;
+  if (!ca1) cl = 0u;
+  // sampled keys above the coarse band and inside it
+  int above = 0, inside = 0;
+#pragma unroll
+  for (int j = 0; j < TK_SPT; ++j) {
+    above += key[j] > ch;
+    inside += key[j] >= cl && key[j] <= ch;
+  }
+  above = wave_isum(above);
+  inside = wave_isum(inside);
+  if (threadIdx.x == 0) s.cnt[0] = s.cnt[1] = 0;
+  __syncthreads();
+  if (threadIdx.x % WAVE == 0) atomicAdd(&s.cnt[0], above), atomicAdd(&s.cnt[1], inside);
+  __syncthreads();
+  const int c_above = s.cnt[0], c_in = s.cnt[1];
+  const double mu = p * TK_SAMPLE, sd = sqrt(TK_SAMPLE * p * (1.0 - p));
+  const double rh = floor(mu - 4.0 * sd - 2.0), rl = ceil(mu + 4.0 * sd + 2.0);
+  const bool act_h = rh >= 1.0, act_l = rl <= (double)TK_SAMPLE;
+  const int rh2 = act_h ? (int)rh - c_above : 0, rl2 = act_l ? (int)rl - c_above : 0;
+  const bool sh = act_h && rh2 >= 1 && rh2 <= c_in, sl = act_l && rl2 >= 1 && rl2 <= c_in;
+  uint32_t hi = 0xffffffffu, lo = 0u;
+  tk_select2<1>(key, cl, ch, sh ? rh2 : 0, sl ? rl2 : 0, sh, sl, s, hi, lo);
+  if (threadIdx.x == 0) {
+    st->hi = !act_h ? 0xffffffffu : sh ? hi : rh2 < 1 ? 0xffffffffu : cl;
+    st->lo = !act_l ? 0u : sl ? lo : rl2 < 1 ? ch : 0u;
   }
 }
 
-// 16 copies of the 256 bins per block (lane % 16 picks the copy): deviations, like most float
-// data, put most keys into a few top-byte bins, and same-address LDS atomics serialise. Passes 0
-// and 1 read the n keys; passes 2 and 3 read the candidate list unless it overflowed.
-constexpr int TK_HCOPIES = 16;
+// 16 keys of one step per lane: v[4 j + e] is index base + 256 j + 4 lane + e (0 past n), so that
+// each load instruction covers 1 KB
+__device__ __forceinline__ void tk_load_step(const float* __restrict__ dev, int64_t n, int64_t base, bool vec,
+                                             float (&v)[16]) {
+  const int lane = threadIdx.x % WAVE;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i0 = base + 256 * j + 4 * lane;
+    if (vec && i0 + 4 <= n) {
+      const float4 x = *reinterpret_cast<const float4*>(dev + i0);
+      v[4 * j] = x.x, v[4 * j + 1] = x.y, v[4 * j + 2] = x.z, v[4 * j + 3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = i0 + e < n ? dev[i0 + e] : 0.f;
+    }
+  }
+}
 
+// Walks the indices [i_begin, i_begin + sw) that lie below n, 1024 per step. Per index, the map
+// gets bit 2e "taken" (key > hi) and bit 2e + 1 "undecided" (lo <= key <= hi) for index 4b + e in
+// byte b; undecided keys are staged in the wave's LDS buffer in index order and written to
+// cand[0..cap) (counted beyond cap, not written). A step's stores are issued at the start of the
+// next step, before that step's loads of the following keys: a wait for a load also waits for
+// every memory operation issued before it, so no store sits between a load and its use. Returns
+// the lane's taken count and the wave's undecided count (the same in every lane).
+template <bool MAP>
+__device__ __forceinline__ void tk_walk(const float* __restrict__ dev, int64_t n, int64_t i_begin, int sw,
+                                        uint32_t lo, uint32_t hi, bool vec, uint8_t* map, uint32_t* cand,
+                                        int cap, uint32_t* stage, int& n_taken, int& n_und) {
+  const int lane = threadIdx.x % WAVE;
+  const uint64_t below = (1ull << lane) - 1;
+  const int64_t i_end = i_begin + sw;
+  int a = 0, m = 0;
+  float cur[16], nxt[16];
+  uint32_t bytes = 0;     // the previous step's map bytes (sub-step j in bits 8j..8j+7)
+  int staged = 0;         // the previous step's staged candidates (wave-uniform)
+  int64_t prev = -1;      // the previous step's first index
+  auto flush = [&]() {
+    if (MAP && prev >= 0)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) map[(prev + 256 * j) / 4 + lane] = (uint8_t)(bytes >> (8 * j));
+    if (cand && staged) {
+      wave_sync();
+      for (int i = lane; i < staged; i += WAVE)
+        if (m + i < cap) cand[m + i] = stage[i];
+      wave_sync();  // the stage is read before this step writes it
+    }
+    m += staged;
+  };
+  tk_load_step(dev, n, i_begin, vec, nxt);
+  for (int64_t base = i_begin; base < i_end; base += 1024) {
+#pragma unroll
+    for (int x = 0; x < 16; ++x) cur[x] = nxt[x];
+    flush();
+    if (base + 1024 < i_end) tk_load_step(dev, n, base + 1024, vec, nxt);
+    bytes = 0;
+    staged = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t byte = 0;
+      bool und[4];
+      uint32_t key[4];
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = base + 256 * j + 4 * lane + e < n;
+        key[e] = order_key(cur[4 * j + e]);
+        const bool up = in && key[e] > hi;
+        und[e] = in && key[e] >= lo && key[e] <= hi;
+        byte |= (uint32_t)up << (2 * e) | (uint32_t)und[e] << (2 * e + 1);
+        a += up;
+        const uint64_t bal = __ballot(und[e]);
+        before += __popcll(bal & below);
+        tot += __popcll(bal);
+      }
+      bytes |= byte << (8 * j);
+      if (cand && tot) {
+        int s = staged + before;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (und[e]) stage[s++] = key[e];
+      }
+      staged += tot;
+    }
+    prev = base;
+  }
+  flush();
+  n_taken = a;
+  n_und = m;
+}
+
+// Round 0 (the sample's band) always; round 1 (T's 16-bit bin) only when the sample route failed.
+__global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_collect_kernel(const float* __restrict__ dev, int n, int sw,
+                                                                      int n_sub, int round,
+                                                                      const TopkState* __restrict__ st, int* sub_a,
+                                                                      int* sub_m, uint8_t* map, uint32_t* slices,
+                                                                      int cap_w) {
+  if (round == 1 && st->mode != TK_FALLBACK) return;
+  __shared__ uint32_t stage[TK_WPB][1024];
+  const int r = blockIdx.x * TK_WPB + (int)threadIdx.x / WAVE;
+  if (r >= n_sub) return;  // whole waves
+  const bool vec = ((uintptr_t)dev & 15) == 0;
+  int a, m;
+  tk_walk<true>(dev, n, (int64_t)r * sw, sw, st->lo, st->hi, vec, map, slices + (size_t)r * cap_w, cap_w,
+                stage[threadIdx.x / WAVE], a, m);
+  a = wave_isum(a);
+  if (threadIdx.x % WAVE == 0) sub_a[r] = a, sub_m[r] = m;
+}
+
+// Candidate offsets and the route: round 0 checks that T lies in the sample's band, then whether
+// the band is one key or fits the list; round 1 (after the bin picks) only whether the bin's keys
+// fit. Each thread loads its TK_SUB_PER entries at once.
+__global__ __launch_bounds__(TK_THREADS) void tk_mb_scan_cand_kernel(int n_sub, int k, int round, int cap_c,
+                                                                     TopkState* st, const int* __restrict__ sub_a,
+                                                                     const int* __restrict__ sub_m, int* coff) {
+  if (round == 1 && st->mode != TK_FALLBACK) return;
+  __shared__ int wsum[TK_THREADS / WAVE];
+  __shared__ int total;
+  const int r0 = (int)threadIdx.x * TK_SUB_PER;
+  int vm[TK_SUB_PER], va[TK_SUB_PER];
+#pragma unroll
+  for (int j = 0; j < TK_SUB_PER; ++j) {
+    const bool in = r0 + j < n_sub;
+    vm[j] = in ? sub_m[r0 + j] : 0;
+    va[j] = in ? sub_a[r0 + j] : 0;
+  }
+  int m = 0, a = 0;
+#pragma unroll
+  for (int j = 0; j < TK_SUB_PER; ++j) m += vm[j], a += va[j];
+  int mb = block_excl_scan(m, wsum, &total);
+  const int tm = total;
+#pragma unroll
+  for (int j = 0; j < TK_SUB_PER; ++j) {
+    if (r0 + j < n_sub) coff[r0 + j] = mb;
+    mb += vm[j];
+  }
+  (void)block_excl_scan(a, wsum, &total);
+  const int ta = total;
+  if (threadIdx.x == 0) {
+    if (round == 0) {
+      const bool in_band = ta < k && (int64_t)ta + tm >= k;
+      const bool one_key = in_band && st->lo == st->hi;
+      const bool ok = in_band && !one_key && tm <= cap_c;
+      st->mode = one_key ? TK_EXACT : ok ? TK_SAMPLED : TK_FALLBACK;
+      st->kk[0] = ok ? k - ta : k;
+      st->n_cand = ok ? tm : 0;
+      if (one_key) st->prefix[4] = st->lo, st->kk[4] = k - ta;
+    } else {
+      const bool fit = tm <= cap_c;
+      st->mode = fit ? TK_BIN : TK_OVERFLOW;
+      st->n_cand = fit ? tm : 0;
+    }
+  }
+}
+
+// Moves each sub-range's candidates to its place in the list; a sub-range whose slice overflowed
+// reads its keys again.
+__global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_compact_kernel(const float* __restrict__ dev, int n, int sw,
+                                                                      int n_sub, int round,
+                                                                      const TopkState* __restrict__ st,
+                                                                      const int* __restrict__ sub_m,
+                                                                      const int* __restrict__ coff,
+                                                                      const uint32_t* __restrict__ slices, int cap_w,
+                                                                      uint32_t* cand, int cap_c) {
+  const int mode = st->mode;
+  if (!((round == 0 && mode == TK_SAMPLED) || (round == 1 && mode == TK_BIN))) return;
+  __shared__ uint32_t stage[TK_WPB][1024];
+  const int r = blockIdx.x * TK_WPB + (int)threadIdx.x / WAVE;
+  if (r >= n_sub) return;
+  const int m = sub_m[r], o = coff[r];
+  if (m <= cap_w) {
+    const uint32_t* src = slices + (size_t)r * cap_w;
+    for (int j = threadIdx.x % WAVE; j < m; j += WAVE) cand[o + j] = src[j];
+  } else {
+    const bool vec = ((uintptr_t)dev & 15) == 0;
+    int a, mm;
+    tk_walk<false>(dev, n, (int64_t)r * sw, sw, st->lo, st->hi, vec, nullptr, cand + o, cap_c - o,
+                   stage[threadIdx.x / WAVE], a, mm);
+  }
+}
+
+// Digit histograms: from the candidate list on the sampled route (a digit that lo and hi share is
+// every candidate's and needs no histogram) and on the bin route (the last two digits), else from
+// all n keys. Over the list only enough blocks for 16 keys a thread take part, so that few blocks
+// merge into the global bins.
 __global__ __launch_bounds__(256) void tk_mb_hist_kernel(const float* __restrict__ dev, int n, int pass,
                                                          const TopkState* __restrict__ st,
                                                          const uint32_t* __restrict__ cand, uint32_t* hist) {
-  const bool from_cand = pass >= 2 && !st->overflow;
+  const int mode = st->mode;
+  const int shift = 24 - 8 * pass;
+  if (mode == TK_EXACT || (mode == TK_SAMPLED && ((st->lo ^ st->hi) >> shift) == 0)) return;
+  const bool from_cand = mode == TK_SAMPLED || (pass >= 2 && mode == TK_BIN);
   const int m = from_cand ? st->n_cand : n;
-  if (from_cand && (int64_t)blockIdx.x * blockDim.x >= m) return;  // block-uniform: no candidate here
-  __shared__ uint32_t h[TK_HCOPIES][257];  // rows of 257 words: the copies of a bin in different banks
+  const int64_t used = from_cand ? std::min<int64_t>(gridDim.x, ((int64_t)m + 4095) / 4096) : gridDim.x;
+  if ((int64_t)blockIdx.x >= used) return;  // block-uniform
+  __shared__ uint32_t h[TK_HCOPIES][257];
 #pragma unroll
   for (int c = 0; c < TK_HCOPIES; ++c) h[c][threadIdx.x] = 0;
   __syncthreads();
   const uint32_t prefix = st->prefix[pass];
   const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
-  const int shift = 24 - 8 * pass;
   uint32_t* mine = h[threadIdx.x % TK_HCOPIES];
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, stride = used * blockDim.x;
   auto add = [&](uint32_t key) {
     if ((key & mask) == prefix) atomicAdd(&mine[(key >> shift) & 255u], 1u);
   };
@@ -230,10 +609,19 @@ __global__ __launch_bounds__(256) void tk_mb_hist_kernel(const float* __restrict
   if (c) atomicAdd(&hist[pass * 256 + threadIdx.x], c);
 }
 
-__global__ __launch_bounds__(256) void tk_mb_pick_kernel(int pass, TopkState* st, const uint32_t* hist,
-                                                         int cap) {
-  // as in the one-workgroup kernel: thread t takes bin 255 - t and an inclusive scan over the
-  // threads counts the keys from the top bin down; the bin where the count first reaches kk wins
+__global__ __launch_bounds__(256) void tk_mb_pick_kernel(int pass, TopkState* st, const uint32_t* hist) {
+  const int mode = st->mode;
+  if (mode == TK_EXACT) return;
+  const int shift = 24 - 8 * pass;
+  if (mode == TK_SAMPLED && ((st->lo ^ st->hi) >> shift) == 0) {  // a digit lo and hi share
+    if (threadIdx.x == 0) {
+      st->prefix[pass + 1] = st->lo & (0xffffffffu << shift);
+      st->kk[pass + 1] = st->kk[pass];
+    }
+    return;
+  }
+  // thread t takes bin 255 - t and an inclusive scan over the threads counts the keys from the top
+  // bin down; the bin where the count first reaches kk wins
   __shared__ int wtot[256 / WAVE];
   const int t = threadIdx.x, lane = t % WAVE;
   const int h = (int)hist[pass * 256 + 255 - t];
@@ -248,267 +636,180 @@ __global__ __launch_bounds__(256) void tk_mb_pick_kernel(int pass, TopkState* st
   for (int wv = 0; wv < t / WAVE; ++wv) incl += wtot[wv];
   const int kk = st->kk[pass], above = incl - h;
   if (above < kk && incl >= kk) {
-    st->prefix[pass + 1] = st->prefix[pass] | ((uint32_t)(255 - t) << (24 - 8 * pass));
+    const uint32_t p = st->prefix[pass] | ((uint32_t)(255 - t) << shift);
+    st->prefix[pass + 1] = p;
     st->kk[pass + 1] = kk - above;
-    if (pass == 1) st->overflow = h > cap;  // h keys share T's top 16 bits
+    if (pass == 1 && mode == TK_FALLBACK) st->lo = p, st->hi = p | 0xffffu;  // T's 16-bit bin
   }
 }
 
-// Collect pass over block b's index range (the count / write partition): blk[2b] = keys whose top
-// 16 bits exceed T's, blk[2b+1] = 0; keys sharing T's top 16 bits go to the candidate list. They
-// are staged in LDS (wave-aggregated LDS atomics) and reserve their global slots with one atomic
-// per flush of the stage, so a block's candidates land contiguously and the one global counter
-// sees about one atomic per block. The list holds at most cap entries: the pick of pass 1 set the
-// overflow flag otherwise, and then this pass does nothing.
-constexpr int TK_CSTAGE = 8192;  // staged candidates per block: 64 KB of LDS
-constexpr int TK_CTILE = 4 * TK_THREADS;
-
-__global__ __launch_bounds__(TK_THREADS) void tk_mb_collect_kernel(const float* __restrict__ dev, int n, int seg,
-                                                                   TopkState* st, int* blk, uint32_t* ckey,
-                                                                   int* cidx) {
-  if (st->overflow) return;
-  __shared__ uint32_t sk[TK_CSTAGE];
-  __shared__ int si[TK_CSTAGE];
-  __shared__ int red[TK_THREADS / WAVE];
-  __shared__ int cnt, gbase;
-  const uint32_t p16 = st->prefix[2] >> 16;
-  const int b0 = blockIdx.x * seg, b1 = (int)min((int64_t)n, (int64_t)b0 + seg);
-  const int lane = threadIdx.x % WAVE;
-  if (threadIdx.x == 0) cnt = 0;
-  int gt = 0;
-  auto visit = [&](uint32_t key, int i, bool in) {
-    const uint32_t d = key >> 16;
-    gt += in && d > p16;
-    const bool c = in && d == p16;
-    const uint64_t bal = __ballot(c);
-    if (bal == 0) return;
-    int base = 0;
-    if (lane == 0) base = atomicAdd(&cnt, __popcll(bal));
-    base = __shfl(base, 0, WAVE);
-    if (c) {
-      const int slot = base + __popcll(bal & ((1ull << lane) - 1));
-      sk[slot] = key;
-      si[slot] = i;
-    }
-  };
-  // moves the staged candidates to the global list; every thread of the block calls it
-  auto flush = [&]() {
-    if (threadIdx.x == 0) gbase = cnt ? atomicAdd(&st->n_cand, cnt) : 0;
-    __syncthreads();
-    const int m = cnt, g = gbase;
-    for (int j = threadIdx.x; j < m; j += TK_THREADS) {
-      ckey[g + j] = sk[j];
-      cidx[g + j] = si[j];
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) cnt = 0;
-    __syncthreads();  // the reset is seen before any wave stages again
-  };
-  // b0 is a multiple of 64, so with a 16-byte aligned dev the 4-wide loads are aligned. Tiles of
-  // TK_CTILE indices: each tile adds at most TK_CTILE candidates, so the stage is flushed before a
-  // tile whenever less room than that is left; every lane of a wave runs the same iterations, so
-  // the ballots see the whole wave
-  const bool vec = ((uintptr_t)dev & 15) == 0;
-  const int v1 = vec ? b0 + (b1 - b0) / 4 * 4 : b0;
-  for (int64_t base = b0; base < b1; base += TK_CTILE) {
-    __syncthreads();
-    if (cnt > TK_CSTAGE - TK_CTILE) flush();
-    if (base + TK_CTILE <= v1) {
-      const int i = (int)base + 4 * (int)threadIdx.x;
-      const float4 v = *reinterpret_cast<const float4*>(dev + i);
-      visit(order_key(v.x), i, true), visit(order_key(v.y), i + 1, true), visit(order_key(v.z), i + 2, true),
-          visit(order_key(v.w), i + 3, true);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t i = base + e * TK_THREADS + (int)threadIdx.x;
-        const bool in = i < b1;
-        visit(in ? order_key(dev[i]) : 0u, in ? (int)i : 0, in);
-      }
-    }
-  }
-  __syncthreads();
-  flush();
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) gt += __shfl_xor(gt, o, WAVE);
-  const int w = threadIdx.x / WAVE;
-  if (lane == 0) red[w] = gt;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int a = 0;
-    for (int i = 0; i < TK_THREADS / WAVE; ++i) a += red[i];
-    blk[2 * blockIdx.x] = a;
-    blk[2 * blockIdx.x + 1] = 0;
-  }
-}
-
-// Adds each candidate above / equal to T to its block range's counts. A wave's candidates come in
-// runs from one range (a collect block flushes its staged candidates at once), so the lanes
-// sharing a range are counted together: one atomic per range and wave.
-__global__ __launch_bounds__(256) void tk_mb_count_cand_kernel(int seg, const TopkState* __restrict__ st,
-                                                               const uint32_t* __restrict__ ckey,
-                                                               const int* __restrict__ cidx, int* blk) {
-  if (st->overflow) return;
-  const int m = st->n_cand;
+// Per sub-range: keys above / equal to T. From the candidates on the sampled and bin routes (keys
+// above the band were counted by the collect pass); when the band is the one key T, its undecided
+// keys are the equal ones; on the overflow route from all of the sub-range's keys, rewriting its
+// map against T (taken: key > T, undecided: key == T).
+__global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_count_kernel(const float* __restrict__ dev, int n, int sw,
+                                                                    int n_sub, const TopkState* __restrict__ st,
+                                                                    int* sub_a, const int* __restrict__ sub_m,
+                                                                    int* sub_e, const int* __restrict__ coff,
+                                                                    const uint32_t* __restrict__ cand, uint8_t* map) {
+  const int r = blockIdx.x * TK_WPB + (int)threadIdx.x / WAVE;
+  if (r >= n_sub) return;
   const uint32_t T = st->prefix[4];
-  const int lane = threadIdx.x % WAVE;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  // whole waves step together so the ballots see every lane
-  for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < m; base += stride) {
-    const int64_t i = base + threadIdx.x;
-    const bool in = i < m;
-    const uint32_t key = in ? ckey[i] : 0u;
-    const int b = in ? cidx[i] / seg : -1;
-    uint64_t todo = __ballot(in && key >= T);
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int bl = __shfl(b, leader, WAVE);
-      const uint64_t same = todo & __ballot(b == bl);
-      const int gt = __popcll(same & __ballot(key > T)), eq = __popcll(same) - gt;
-      if (lane == leader) {
-        if (gt) atomicAdd(&blk[2 * bl], gt);
-        if (eq) atomicAdd(&blk[2 * bl + 1], eq);
-      }
-      todo &= ~same;
+  const int mode = st->mode;
+  const bool lane0 = threadIdx.x % WAVE == 0;
+  if (mode == TK_EXACT) {
+    if (lane0) sub_e[r] = sub_m[r];
+  } else if (mode == TK_OVERFLOW) {
+    const bool vec = ((uintptr_t)dev & 15) == 0;
+    int a, e;
+    tk_walk<true>(dev, n, (int64_t)r * sw, sw, T, T, vec, map, nullptr, 0, nullptr, a, e);
+    a = wave_isum(a);
+    if (lane0) sub_a[r] = a, sub_e[r] = e;
+  } else {
+    const int m = sub_m[r], o = coff[r];
+    int gt = 0, eq = 0;
+    for (int j = threadIdx.x % WAVE; j < m; j += WAVE) {
+      const uint32_t key = cand[o + j];
+      gt += key > T;
+      eq += key == T;
     }
+    gt = wave_isum(gt);
+    eq = wave_isum(eq);
+    if (lane0) sub_a[r] += gt, sub_e[r] = eq;
   }
 }
 
-// blk[2b], blk[2b+1]: keys above / equal to T in block b's index range, from all n keys (overflow)
-__global__ __launch_bounds__(TK_THREADS) void tk_mb_count_kernel(const float* __restrict__ dev, int n, int seg,
-                                                                 const TopkState* __restrict__ st, int* blk) {
-  if (!st->overflow) return;  // the collect pass and the candidate list gave the counts
-  __shared__ int red[2][TK_THREADS / WAVE];
-  const uint32_t T = st->prefix[4];
-  const int b0 = blockIdx.x * seg, b1 = (int)min((int64_t)n, (int64_t)b0 + seg);
-  int gt = 0, eq = 0;
-  auto cnt = [&](float x) {
-    const uint32_t key = order_key(x);
-    gt += key > T;
-    eq += key == T;
-  };
-  // b0 is a multiple of 64, so with a 16-byte aligned dev the 4-wide loads are aligned
-  const bool vec = ((uintptr_t)dev & 15) == 0;
-  const int v1 = vec ? b0 + (b1 - b0) / 4 * 4 : b0;
-  for (int64_t i = b0 + 4 * (int)threadIdx.x; i < v1; i += 4 * TK_THREADS) {
-    const float4 v = *reinterpret_cast<const float4*>(dev + i);
-    cnt(v.x), cnt(v.y), cnt(v.z), cnt(v.w);
-  }
-  for (int64_t i = v1 + (int)threadIdx.x; i < b1; i += TK_THREADS) cnt(dev[i]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    gt += __shfl_xor(gt, o, WAVE);
-    eq += __shfl_xor(eq, o, WAVE);
-  }
-  const int w = threadIdx.x / WAVE;
-  if (threadIdx.x % WAVE == 0) red[0][w] = gt, red[1][w] = eq;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int a = 0, e = 0;
-    for (int i = 0; i < TK_THREADS / WAVE; ++i) a += red[0][i], e += red[1][i];
-    blk[2 * blockIdx.x] = a;
-    blk[2 * blockIdx.x + 1] = e;
-  }
-}
-
-// off[2b]: output offset of block b; off[2b+1]: keys equal to T in blocks before b
-__global__ __launch_bounds__(TK_THREADS) void tk_mb_scan_kernel(int nb, const TopkState* __restrict__ st,
-                                                                const int* __restrict__ blk, int* off) {
+// ooff[r]: output offset of sub-range r; eqb[r]: keys equal to T in sub-ranges before r
+__global__ __launch_bounds__(TK_THREADS) void tk_mb_scan_out_kernel(int n_sub, const TopkState* __restrict__ st,
+                                                                    const int* __restrict__ sub_a,
+                                                                    const int* __restrict__ sub_e, int* ooff,
+                                                                    int* eqb) {
   __shared__ int wsum[TK_THREADS / WAVE];
   __shared__ int total;
   const int kk = st->kk[4];
-  const int per = (nb + TK_THREADS - 1) / TK_THREADS;
-  const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
+  const int r0 = (int)threadIdx.x * TK_SUB_PER;
+  int va[TK_SUB_PER], ve[TK_SUB_PER];
+#pragma unroll
+  for (int j = 0; j < TK_SUB_PER; ++j) {
+    const bool in = r0 + j < n_sub;
+    va[j] = in ? sub_a[r0 + j] : 0;
+    ve[j] = in ? sub_e[r0 + j] : 0;
+  }
   int eq = 0;
-  for (int b = b0; b < b1; ++b) eq += blk[2 * b + 1];
+#pragma unroll
+  for (int j = 0; j < TK_SUB_PER; ++j) eq += ve[j];
   int eq_before = block_excl_scan(eq, wsum, &total);
   int sel = 0;
   {
     int e = eq_before;
-    for (int b = b0; b < b1; ++b) {
-      const int eb = blk[2 * b + 1];
-      sel += blk[2 * b] + min(max(kk - e, 0), eb);
-      e += eb;
+#pragma unroll
+    for (int j = 0; j < TK_SUB_PER; ++j) {
+      sel += va[j] + min(max(kk - e, 0), ve[j]);
+      e += ve[j];
     }
   }
   int sel_before = block_excl_scan(sel, wsum, &total);
-  for (int b = b0; b < b1; ++b) {
-    const int eb = blk[2 * b + 1];
-    off[2 * b] = sel_before;
-    off[2 * b + 1] = eq_before;
-    sel_before += blk[2 * b] + min(max(kk - eq_before, 0), eb);
-    eq_before += eb;
+#pragma unroll
+  for (int j = 0; j < TK_SUB_PER; ++j) {
+    if (r0 + j < n_sub) ooff[r0 + j] = sel_before, eqb[r0 + j] = eq_before;
+    sel_before += va[j] + min(max(kk - eq_before, 0), ve[j]);
+    eq_before += ve[j];
   }
 }
 
-// Each thread owns TK_EPT consecutive indices of a tile (one 16-byte load, coalesced across the
-// wave), so one block scan orders TK_THREADS * TK_EPT positions. The scan runs over (keys equal to
-// T) << 16 | (keys above T) per thread (a tile's counts fit 16 bits): keys equal to T are taken in
-// index order while fewer than kk of them precede, so the positions taken before a thread are its
-// keys-above prefix plus min(equal prefix, kk - equal keys of earlier tiles). The next tile's keys
-// are loaded before the current tile's scan; a tile's positions are staged in LDS and written out
-// contiguously.
-constexpr int TK_EPT = 4;
-static_assert(TK_THREADS * TK_EPT < (1 << 16), "packed tile counts");
-
-__device__ __forceinline__ void tk_load_tile(const float* __restrict__ dev, int64_t i0, int b1, bool vec,
-                                             uint32_t (&key)[TK_EPT]) {
-  if (vec && i0 + TK_EPT <= b1) {
-#pragma unroll
-    for (int e = 0; e < TK_EPT; e += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(dev + i0 + e);
-      key[e] = order_key(v.x), key[e + 1] = order_key(v.y), key[e + 2] = order_key(v.z), key[e + 3] = order_key(v.w);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < TK_EPT; ++e) key[e] = i0 + e < b1 ? order_key(dev[i0 + e]) : 0u;
-  }
-}
-
-__global__ __launch_bounds__(TK_THREADS) void tk_mb_write_kernel(const float* __restrict__ dev, int n, int seg,
-                                                                 const TopkState* __restrict__ st,
-                                                                 const int* __restrict__ off, int k, int* out) {
-  constexpr int TILE = TK_THREADS * TK_EPT;
-  __shared__ int wsum[TK_THREADS / WAVE];
-  __shared__ int total;
-  __shared__ int stage[TILE];
+// Ordered write of sub-range r from its map: each lane takes one 32-bit word (16 consecutive
+// indices) per step; the words of 16 steps are loaded together (a store between a load and its use
+// makes the wait cover every earlier memory operation, so loads are batched rather than prefetched
+// one step ahead). Undecided indices take their keys from the sub-range's candidates in order,
+// which the wave reads 1024 at a time into its LDS buffer (when the band is the one key T, or on
+// the overflow route, they are the keys equal to T); keys equal to T are taken in index order while
+// fewer than kk precede them. Two wave scans order the lanes; the step's positions are staged in
+// the wave's LDS buffer and written out contiguously.
+__global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_write_kernel(int n, int sw, int n_sub, int k,
+                                                                    const TopkState* __restrict__ st,
+                                                                    const uint32_t* __restrict__ map,
+                                                                    const int* __restrict__ sub_m,
+                                                                    const int* __restrict__ coff,
+                                                                    const int* __restrict__ ooff,
+                                                                    const int* __restrict__ eqb,
+                                                                    const uint32_t* __restrict__ cand, int cap_c,
+                                                                    int* out) {
+  __shared__ int stage_all[TK_WPB][1024];
+  __shared__ uint32_t cbuf_all[TK_WPB][1024];
+  const int r = blockIdx.x * TK_WPB + (int)threadIdx.x / WAVE;
+  if (r >= n_sub) return;
+  int* stage = stage_all[threadIdx.x / WAVE];
+  uint32_t* cbuf = cbuf_all[threadIdx.x / WAVE];
+  const int lane = threadIdx.x % WAVE;
   const uint32_t T = st->prefix[4];
   const int kk = st->kk[4];
-  const int b0 = blockIdx.x * seg, b1 = (int)min((int64_t)n, (int64_t)b0 + seg);
-  int o_run = off[2 * blockIdx.x], e_run = off[2 * blockIdx.x + 1];
-  const bool vec = ((uintptr_t)dev & 15) == 0;  // b0 and i0 are multiples of 4 elements
-  uint32_t key[TK_EPT], nxt[TK_EPT];
-  if (b0 < b1) tk_load_tile(dev, b0 + (int)threadIdx.x * TK_EPT, b1, vec, nxt);
-  for (int64_t base = b0; base < b1; base += TILE) {
-    const int64_t i0 = base + (int)threadIdx.x * TK_EPT;
+  const bool all_eq = st->mode == TK_OVERFLOW || st->mode == TK_EXACT;
+  int o_run = ooff[r], e_run = eqb[r], c_run = all_eq ? 0 : coff[r];
+  const int c_stop = all_eq ? 0 : min(cap_c, c_run + sub_m[r]);
+  int buf_base = c_run, buf_end = c_run;  // candidate ordinals held in cbuf
+  const int64_t i_begin = (int64_t)r * sw, i_end = std::min<int64_t>(n, i_begin + sw);
+  const int64_t last_word = (i_begin + sw) / 16 - 1;  // the sub-range's map words end here
+  constexpr int BATCH = 16;
+  uint32_t mw[BATCH];
+  for (int64_t base = i_begin; base < i_end; base += 1024) {
+    const int step = (int)((base - i_begin) / 1024) % BATCH;
+    if (step == 0)
 #pragma unroll
-    for (int e = 0; e < TK_EPT; ++e) key[e] = nxt[e];
-    if (base + TILE < b1) tk_load_tile(dev, i0 + TILE, b1, vec, nxt);
-    int n_eq = 0, n_gt = 0;
+      for (int i = 0; i < BATCH; ++i) mw[i] = map[std::min<int64_t>(base / 16 + 64 * i + lane, last_word)];
+    uint32_t w = mw[0];
 #pragma unroll
-    for (int e = 0; e < TK_EPT; ++e) {
-      const bool in = i0 + e < b1;
-      n_eq += in && key[e] == T;
-      n_gt += in && key[e] > T;
+    for (int i = 1; i < BATCH; ++i)
+      if (step == i) w = mw[i];
+    uint32_t take = w & 0x55555555u, eqm = 0;
+    const uint32_t und = (w >> 1) & 0x55555555u;
+    if (all_eq) {
+      eqm = und;
+    } else {
+      int mtot;
+      const int mpre = wave_excl_scan(__popc(und), mtot);
+      if (c_run + mtot > buf_end) {  // wave-uniform: refill from c_run (mtot <= 1024)
+        wave_sync();
+        buf_base = c_run;
+        buf_end = min(c_stop, c_run + 1024);
+        const int cnt = buf_end - buf_base;  // >= mtot >= 1
+        uint32_t v[1024 / WAVE];
+#pragma unroll
+        for (int i = 0; i < 1024 / WAVE; ++i) v[i] = cand[buf_base + min(lane + WAVE * i, cnt - 1)];
+#pragma unroll
+        for (int i = 0; i < 1024 / WAVE; ++i)
+          if (lane + WAVE * i < cnt) cbuf[lane + WAVE * i] = v[i];
+        wave_sync();
+      }
+      int c = c_run + mpre - buf_base;
+      for (uint32_t rest = und; rest; rest &= rest - 1) {
+        const uint32_t bit = rest & (0u - rest);
+        const uint32_t key = c < 1024 ? cbuf[c] : 0u;
+        ++c;
+        if (key > T) take |= bit;
+        else if (key == T) eqm |= bit;
+      }
+      c_run += mtot;
     }
-    const int pre = block_excl_scan((n_eq << 16) | n_gt, wsum, &total);
-    const int tot = total;
-    const int owed = max(kk - e_run, 0);  // keys equal to T still to take at this tile's start
-    int r = e_run + (pre >> 16);
-    int o = (pre & 0xffff) + min(pre >> 16, owed);  // within the tile
-#pragma unroll
-    for (int e = 0; e < TK_EPT; ++e) {
-      const bool in = i0 + e < b1, eq = in && key[e] == T;
-      if (in && (key[e] > T || (eq && r < kk))) stage[o++] = (int)(i0 + e);
-      r += eq;
+    int ptot;
+    const int pk = wave_excl_scan((__popc(eqm) << 16) | __popc(take), ptot);
+    const int owed = max(kk - e_run, 0);  // keys equal to T still to take at this step's start
+    int o = (pk & 0xffff) + min(pk >> 16, owed);
+    // equal keys of this lane still owed (fewer than kk precede them): its first ones in index order
+    int eq_owed = min(max(kk - e_run - (pk >> 16), 0), __popc(eqm));
+    for (uint32_t rest = eqm; eq_owed > 0; --eq_owed) {
+      take |= rest & (0u - rest);
+      rest &= rest - 1;
     }
-    const int take = (tot & 0xffff) + min(tot >> 16, owed);
-    __syncthreads();
-    for (int j = threadIdx.x; j < take; j += TK_THREADS)
-      if (o_run + j < k) out[o_run + j] = stage[j];
-    // the next tile's scan starts with a barrier, so stage is not overwritten while it is read
-    e_run += tot >> 16;
-    o_run += take;
+    const int idx0 = (int)(base + 16 * lane);
+    for (uint32_t rest = take; rest; rest &= rest - 1, ++o)
+      if (o < 1024) stage[o] = idx0 + (__ffs(rest) - 1) / 2;
+    const int taken = (ptot & 0xffff) + min(ptot >> 16, owed);
+    wave_sync();
+    for (int i = lane; i < taken; i += WAVE)
+      if (o_run + i < k) out[o_run + i] = stage[i];
+    wave_sync();  // the stage is read before the next step writes it
+    e_run += ptot >> 16;
+    o_run += taken;
   }
 }
 
@@ -520,29 +821,52 @@ hipError_t launch_topk_token(const float* dev, int n, int k, int* out, void* ws,
   }
   const size_t fixed = tk_mb_fixed_bytes(n);
   if (!ws || ws_bytes < fixed) return hipErrorInvalidValue;
+  int sw, n_sub;
+  tk_geom(n, sw, n_sub);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w);
   TopkState* state = reinterpret_cast<TopkState*>(w + 4 * 256 * sizeof(uint32_t));
-  int* blk = reinterpret_cast<int*>(w + 4 * 256 * sizeof(uint32_t) + 256);
-  const int nb = tk_mb_blocks(n);
-  int* off = blk + 2 * nb;
-  // candidate list: keys, then indices, in what the workspace holds beyond the fixed part
-  const int cap = (int)std::min<size_t>((ws_bytes - fixed) / (2 * sizeof(uint32_t)), (size_t)n);
-  uint32_t* ckey = reinterpret_cast<uint32_t*>(w + fixed);
-  int* cidx = reinterpret_cast<int*>(ckey + cap);
-  const int seg = (int)((((int64_t)n + nb - 1) / nb + 63) / 64 * 64);  // block ranges start at multiples of 64
-  hipLaunchKernelGGL(tk_mb_init_kernel, dim3(1), dim3(TK_THREADS), 0, st, hist, state, k);
+  uint32_t* skey = reinterpret_cast<uint32_t*>(w + 4 * 256 * sizeof(uint32_t) + 256);
+  int* sub = reinterpret_cast<int*>(w + TK_HEAD_BYTES);
+  int *sub_a = sub, *sub_m = sub + n_sub, *sub_e = sub + 2 * n_sub, *coff = sub + 3 * n_sub, *ooff = sub + 4 * n_sub,
+      *eqb = sub + 5 * n_sub;
+  uint8_t* map = reinterpret_cast<uint8_t*>(w + TK_HEAD_BYTES + tk_sub_bytes(n_sub));
+  // beyond the fixed part: up to n/16 list entries first, then up to sw/16 slice entries per
+  // sub-range, then whatever is left extends the list
+  size_t room = (ws_bytes - fixed) / sizeof(uint32_t);
+  size_t cap_c = std::min<size_t>((size_t)n / 16, room);
+  room -= cap_c;
+  const size_t cap_w = std::min<size_t>((size_t)sw / 16, room / n_sub);
+  room -= cap_w * n_sub;
+  cap_c += std::min<size_t>((size_t)n - cap_c, room);
+  uint32_t* slices = reinterpret_cast<uint32_t*>(w + fixed);
+  uint32_t* cand = slices + cap_w * n_sub;
+  const int gw = (n_sub + TK_WPB - 1) / TK_WPB, cw = (int)cap_w, cc = (int)cap_c;
   const int hist_blocks = (int)std::min<int64_t>(TK_HIST_BLOCKS, ((int64_t)n + 1023) / 1024);
-  for (int pass = 0; pass < 4; ++pass) {
-    if (pass == 2)
-      hipLaunchKernelGGL(tk_mb_collect_kernel, dim3(nb), dim3(TK_THREADS), 0, st, dev, n, seg, state, blk, ckey, cidx);
-    hipLaunchKernelGGL(tk_mb_hist_kernel, dim3(hist_blocks), dim3(256), 0, st, dev, n, pass, state, ckey, hist);
-    hipLaunchKernelGGL(tk_mb_pick_kernel, dim3(1), dim3(256), 0, st, pass, state, hist, cap);
+  hipLaunchKernelGGL(tk_mb_gather_kernel, dim3(TK_SAMPLE / 256), dim3(256), 0, st, dev, n, skey);
+  hipLaunchKernelGGL(tk_mb_sample_kernel, dim3(1), dim3(TK_THREADS), 0, st, skey, n, k, hist, state);
+  for (int round = 0; round < 2; ++round) {
+    if (round == 1)
+      for (int pass = 0; pass < 2; ++pass) {
+        hipLaunchKernelGGL(tk_mb_hist_kernel, dim3(hist_blocks), dim3(256), 0, st, dev, n, pass, state, cand, hist);
+        hipLaunchKernelGGL(tk_mb_pick_kernel, dim3(1), dim3(256), 0, st, pass, state, hist);
+      }
+    hipLaunchKernelGGL(tk_mb_collect_kernel, dim3(gw), dim3(TK_WPB * WAVE), 0, st, dev, n, sw, n_sub, round, state,
+                       sub_a, sub_m, map, slices, cw);
+    hipLaunchKernelGGL(tk_mb_scan_cand_kernel, dim3(1), dim3(TK_THREADS), 0, st, n_sub, k, round, cc, state, sub_a,
+                       sub_m, coff);
+    hipLaunchKernelGGL(tk_mb_compact_kernel, dim3(gw), dim3(TK_WPB * WAVE), 0, st, dev, n, sw, n_sub, round, state,
+                       sub_m, coff, slices, cw, cand, cc);
   }
-  hipLaunchKernelGGL(tk_mb_count_cand_kernel, dim3(hist_blocks), dim3(256), 0, st, seg, state, ckey, cidx, blk);
-  hipLaunchKernelGGL(tk_mb_count_kernel, dim3(nb), dim3(TK_THREADS), 0, st, dev, n, seg, state, blk);
-  hipLaunchKernelGGL(tk_mb_scan_kernel, dim3(1), dim3(TK_THREADS), 0, st, nb, state, blk, off);
-  hipLaunchKernelGGL(tk_mb_write_kernel, dim3(nb), dim3(TK_THREADS), 0, st, dev, n, seg, state, off, k, out);
+  for (int pass = 2; pass < 4; ++pass) {
+    hipLaunchKernelGGL(tk_mb_hist_kernel, dim3(hist_blocks), dim3(256), 0, st, dev, n, pass, state, cand, hist);
+    hipLaunchKernelGGL(tk_mb_pick_kernel, dim3(1), dim3(256), 0, st, pass, state, hist);
+  }
+  hipLaunchKernelGGL(tk_mb_count_kernel, dim3(gw), dim3(TK_WPB * WAVE), 0, st, dev, n, sw, n_sub, state, sub_a, sub_m,
+                     sub_e, coff, cand, map);
+  hipLaunchKernelGGL(tk_mb_scan_out_kernel, dim3(1), dim3(TK_THREADS), 0, st, n_sub, state, sub_a, sub_e, ooff, eqb);
+  hipLaunchKernelGGL(tk_mb_write_kernel, dim3(gw), dim3(TK_WPB * WAVE), 0, st, n, sw, n_sub, k, state,
+                     reinterpret_cast<const uint32_t*>(map), sub_m, coff, ooff, eqb, cand, cc, out);
   return hipGetLastError();
 }
 

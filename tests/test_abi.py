@@ -55,13 +55,24 @@ def test_topk_validation(L):
     # token mode from n = 65536 on runs on the whole GPU and needs a workspace
     assert cf.topk_workspace_size(65535, "token") == 0 and cf.topk_workspace_size(65536, "token") > 0
     assert L.cf_topk_select(None, 1 << 20, 5, 0, None, 0, None, None, 0, None) == cf.CF_EWORKSPACE
-    # from the minimum up any workspace is accepted (the rest holds candidates: n / 16 at the full size)
+    # from the minimum (the 2-bit map of the n values, per-range counts, 128 KB of sampled keys) up
+    # any workspace is accepted; the rest holds candidates: a list of n / 16 and slices of 1 / 16
+    # of each range at the full size
     for n in (1 << 16, 1 << 20, 3000017, (1 << 28) + 5):
         lo, hi = cf.topk_workspace_min_size(n, "token"), cf.topk_workspace_size(n, "token")
-        assert 0 < lo < 64 << 10 and hi >= lo + 8 * (n // 16), n
+        assert n // 4 <= lo < n // 4 + (n // 1024) * 24 + (192 << 10) and hi >= lo + 4 * (n // 16) + 4 * (n // 16), n
     for mode in ("doc", "ranked", "heads"):
         assert cf.topk_workspace_min_size(1000, mode) == cf.topk_workspace_size(1000, mode)
     assert cf.topk_workspace_min_size(65535, "token") == 0
+    # the no-allocation entry point holds the token-mode minimum (mostly the 2-bit map) up to about
+    # 15.8 million values; beyond, it refuses on the host before anything is enqueued
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cf.h")).read()
+    assert "#define CF_NOALLOC_SCRATCH_BYTES (4u << 20)" in hdr and cf.CF_NOALLOC_SCRATCH_BYTES == 4 << 20
+    big = 16_000_000
+    assert cf.topk_workspace_min_size(big, "token") > cf.CF_NOALLOC_SCRATCH_BYTES
+    assert L.cf_topk_select_noalloc(None, big, 5, 0, None, 0, None, None) == cf.CF_EWORKSPACE
+    assert cf.topk_workspace_min_size(15_000_000, "token") <= cf.CF_NOALLOC_SCRATCH_BYTES
+    assert L.cf_topk_select_noalloc(None, 15_000_000, 5, 0, None, 0, None, None) == cf.CF_EINVAL  # null values
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: both calls fail on the host
     lo = cf.topk_workspace_min_size(1 << 20, "token")
     assert L.cf_topk_select(None, 1 << 20, 5, 0, None, 0, None, fake, lo - 1, None) == cf.CF_EWORKSPACE

@@ -116,13 +116,23 @@ def test_topk_bit_exact_vs_oracle(n):
 
 @pytest.mark.parametrize("n", [(1 << 20) + 3, 3000017])
 def test_topk_large_n_multiblock_bit_exact(n):
-    """From n = 65536 on the selection runs on the whole GPU (histogram passes, block counts, a
-    scan and an ordered write); it must give the same unique answer as the oracle."""
+    """From n = 65536 on the selection runs on the whole GPU (a sampled band around the threshold,
+    a collect pass, digit passes over the candidates, per-range counts, a scan and an ordered
+    write; histogram passes over all n values when the band misses or does not fit); it must give
+    the same unique answer as the oracle. Uniform values take the sampled route; values sorted by
+    index put every undecided value into a few ranges, whose candidate slices overflow and are
+    read again; heavy ties and a constant array leave the band too large for the list."""
     rng = np.random.default_rng(n)
     say(f"topk large n={n}")
-    for trial in range(2):
-        d = (rng.random(n).astype(np.float32) if trial == 0 else
-             rng.choice(np.array([0.0, -0.0, 1e-45, 0.5, 2.0, np.inf, np.nan], np.float32), n))
+    for trial in range(4):
+        if trial == 0:
+            d = rng.random(n).astype(np.float32)
+        elif trial == 1:
+            d = rng.choice(np.array([0.0, -0.0, 1e-45, 0.5, 2.0, np.inf, np.nan], np.float32), n)
+        elif trial == 2:  # ascending with runs of equal values
+            d = np.sort(rng.integers(0, n // 3, n)).astype(np.float32)
+        else:
+            d = np.full(n, 0.25, np.float32)
         for k in sorted({1, n // 100, n // 2, n}):
             assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (n, trial, k)
 
@@ -139,10 +149,12 @@ def _order_keys(d):
 
 @pytest.mark.parametrize("n", [(1 << 18) + 5, 2000003])
 def test_topk_candidate_list_capacity_edges(n):
-    """The whole-GPU selection keeps the values that share the threshold key's top 16 bits in a
-    candidate list when the workspace has room for all of them, and otherwise reads all n values
-    twice more. Workspaces with room for exactly that many, one fewer, none, and the full size, and
-    a value array 4 bytes off 16-byte alignment, must all give the oracle's unique answer."""
+    """When the sampled band does not fit the workspace's candidate list, the whole-GPU selection
+    falls back to the values that share the threshold key's top 16 bits, and when those do not fit
+    either, it reads all n values twice more. Workspaces with list room (4 bytes a value, the first
+    n / 16 entries ahead of the per-range slices) for exactly that many, one fewer, none, and the
+    full size, and a value array 4 bytes off 16-byte alignment, must all give the oracle's unique
+    answer."""
     torch = _torch()
     rng = np.random.default_rng(n)
     d = rng.standard_normal(n).astype(np.float32) ** 2  # skewed, as deviations are
@@ -156,9 +168,10 @@ def test_topk_candidate_list_capacity_edges(n):
     for k in (1, n // 7, n // 2, n):
         want = oracle.select_topk(d, k).tolist()
         h = int(np.count_nonzero((keys >> 16) == (srt[k - 1] >> 16)))
+        assert h <= n // 16  # so that room for h list entries is exactly h
         say(f"topk capacity n={n} k={k} h={h}")
         for room in (h, h - 1, 0, None):
-            nbytes = cf.topk_workspace_size(n, "token") if room is None else base + 8 * room
+            nbytes = cf.topk_workspace_size(n, "token") if room is None else base + 4 * room
             ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
             for vals in (aligned, buf[1:]):
                 out = torch.full((k,), -1, dtype=torch.int32, device="cuda")
