@@ -224,16 +224,30 @@ __device__ __forceinline__ uint32_t tk_hash(uint32_t x) {  // Wellons' "lowbias3
   return x;
 }
 
+// Exclusive scan over the wave's 64 lanes with DPP moves (row shifts within each row of 16 lanes,
+// then the row totals broadcast down): six adds and no LDS traffic. total: the wave's sum.
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
-  const int lane = threadIdx.x % WAVE;
   int x = v;
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const int y = __shfl_up(x, o, WAVE);
-    if (lane >= o) x += y;
-  }
-  total = __shfl(x, WAVE - 1, WAVE);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+  total = __builtin_amdgcn_readlane(x, WAVE - 1);
   return x - v;
+}
+
+// The walk's keys: the order-preserving key without the -0 and positive-NaN rewrites (those are
+// absorbed by the walk's bounds, see tk_bounds); negative NaNs, which would order below -inf, are
+// mapped to +inf's key here. tk_canon finishes the canonical key for a stored candidate.
+__device__ __forceinline__ uint32_t tk_raw_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t r = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return r < 0x007fffffu ? 0xff800000u : r;
+}
+__device__ __forceinline__ uint32_t tk_canon(uint32_t r) {
+  return r == 0x7fffffffu ? 0x80000000u : (r > 0xff800000u ? 0xff800000u : r);  // -0 -> +0, NaN -> +inf
 }
 
 __device__ __forceinline__ int wave_isum(int v) {
@@ -404,20 +418,75 @@ __device__ __forceinline__ void tk_load_step(const float* __restrict__ dev, int6
   }
 }
 
+// One step of tk_walk: the map bytes of the step's 1024 indices (sub-step j in bits 8j..8j+7 of
+// bytes) and, when STAGE, its undecided keys in index order at stage[0..), the others written to
+// the lane's spare word stage[1024 + lane]. Returns the step's undecided count (wave-uniform).
+template <bool FULL>
+__device__ __forceinline__ int tk_classify(const float (&cur)[16], int64_t base, int64_t n, uint32_t lo2,
+                                           uint32_t span, uint32_t hi2, bool stage_keys, uint32_t* stage,
+                                           uint32_t& bytes) {
+  const int lane = threadIdx.x % WAVE;
+  int staged = 0;
+  bytes = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t key[4], und[4];
+    uint32_t byte = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[e] = tk_raw_key(cur[4 * j + e]);
+      bool up = key[e] > hi2, u = key[e] - lo2 <= span;
+      if (!FULL) {
+        const bool in = base + 256 * j + 4 * lane + e < n;
+        up = up && in;
+        u = u && in;
+      }
+      und[e] = u ? 1u : 0u;
+      byte |= (up ? 1u << (2 * e) : 0u) | (u ? 2u << (2 * e) : 0u);
+    }
+    bytes |= byte << (8 * j);
+    uint64_t bal[4];
+    int tot = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bal[e] = __ballot(und[e] != 0);
+      tot += __popcll(bal[e]);
+    }
+    if (stage_keys && tot) {  // wave-uniform
+      uint32_t slot = staged;  // + undecided keys of lower lanes in this sub-step
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        slot = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[e], slot));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        stage[und[e] ? slot : 1024u + lane] = key[e];
+        slot += und[e];
+      }
+    }
+    staged += tot;
+  }
+  return staged;
+}
+
 // Walks the indices [i_begin, i_begin + sw) that lie below n, 1024 per step. Per index, the map
 // gets bit 2e "taken" (key > hi) and bit 2e + 1 "undecided" (lo <= key <= hi) for index 4b + e in
-// byte b; undecided keys are staged in the wave's LDS buffer in index order and written to
-// cand[0..cap) (counted beyond cap, not written). A step's stores are issued at the start of the
-// next step, before that step's loads of the following keys: a wait for a load also waits for
-// every memory operation issued before it, so no store sits between a load and its use. Returns
-// the lane's taken count and the wave's undecided count (the same in every lane).
+// byte b; undecided keys (raw: tk_canon gives the canonical key) are staged in the wave's LDS
+// buffer in index order and written to cand[0..cap) (counted beyond cap, not written). The bounds
+// are moved so that raw keys compare as canonical ones: -0's raw key sits just below +0's, and
+// positive NaNs' above +inf's, where no canonical key lies. A step's stores are issued at the start
+// of the next step, before that step's loads of the following keys (a wait for a load also waits
+// for every memory operation issued before it). Returns the lane's taken count and the wave's
+// undecided count (the same in every lane). stage: 1024 + 64 words (the last 64 take the writes
+// of keys that are not staged).
 template <bool MAP>
 __device__ __forceinline__ void tk_walk(const float* __restrict__ dev, int64_t n, int64_t i_begin, int sw,
                                         uint32_t lo, uint32_t hi, bool vec, uint8_t* map, uint32_t* cand,
                                         int cap, uint32_t* stage, int& n_taken, int& n_und) {
   const int lane = threadIdx.x % WAVE;
-  const uint64_t below = (1ull << lane) - 1;
   const int64_t i_end = i_begin + sw;
+  const uint32_t lo2 = lo - (lo == 0x80000000u);
+  const uint32_t hi2 = hi >= 0xff800000u ? 0xffffffffu : hi - (hi == 0x7fffffffu);
+  const uint32_t span = hi2 - lo2;
   int a = 0, m = 0;
   float cur[16], nxt[16];
   uint32_t bytes = 0;     // the previous step's map bytes (sub-step j in bits 8j..8j+7)
@@ -441,35 +510,12 @@ __device__ __forceinline__ void tk_walk(const float* __restrict__ dev, int64_t n
     for (int x = 0; x < 16; ++x) cur[x] = nxt[x];
     flush();
     if (base + 1024 < i_end) tk_load_step(dev, n, base + 1024, vec, nxt);
-    bytes = 0;
-    staged = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t byte = 0;
-      bool und[4];
-      uint32_t key[4];
-      int before = 0, tot = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool in = base + 256 * j + 4 * lane + e < n;
-        key[e] = order_key(cur[4 * j + e]);
-        const bool up = in && key[e] > hi;
-        und[e] = in && key[e] >= lo && key[e] <= hi;
-        byte |= (uint32_t)up << (2 * e) | (uint32_t)und[e] << (2 * e + 1);
-        a += up;
-        const uint64_t bal = __ballot(und[e]);
-        before += __popcll(bal & below);
-        tot += __popcll(bal);
-      }
-      bytes |= byte << (8 * j);
-      if (cand && tot) {
-        int s = staged + before;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (und[e]) stage[s++] = key[e];
-      }
-      staged += tot;
-    }
+    // wave-uniform: a step with no index past n classifies without bounds checks
+    if (base + 1024 <= n)
+      staged = tk_classify<true>(cur, base, n, lo2, span, hi2, cand != nullptr, stage, bytes);
+    else
+      staged = tk_classify<false>(cur, base, n, lo2, span, hi2, cand != nullptr, stage, bytes);
+    a += __popc(bytes & 0x55555555u);
     prev = base;
   }
   flush();
@@ -484,7 +530,7 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_collect_kernel(const floa
                                                                       int* sub_m, uint8_t* map, uint32_t* slices,
                                                                       int cap_w) {
   if (round == 1 && st->mode != TK_FALLBACK) return;
-  __shared__ uint32_t stage[TK_WPB][1024];
+  __shared__ uint32_t stage[TK_WPB][1024 + WAVE];
   const int r = blockIdx.x * TK_WPB + (int)threadIdx.x / WAVE;
   if (r >= n_sub) return;  // whole waves
   const bool vec = ((uintptr_t)dev & 15) == 0;
@@ -552,7 +598,7 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_compact_kernel(const floa
                                                                       uint32_t* cand, int cap_c) {
   const int mode = st->mode;
   if (!((round == 0 && mode == TK_SAMPLED) || (round == 1 && mode == TK_BIN))) return;
-  __shared__ uint32_t stage[TK_WPB][1024];
+  __shared__ uint32_t stage[TK_WPB][1024 + WAVE];
   const int r = blockIdx.x * TK_WPB + (int)threadIdx.x / WAVE;
   if (r >= n_sub) return;
   const int m = sub_m[r], o = coff[r];
@@ -593,7 +639,7 @@ __global__ __launch_bounds__(256) void tk_mb_hist_kernel(const float* __restrict
     if ((key & mask) == prefix) atomicAdd(&mine[(key >> shift) & 255u], 1u);
   };
   if (from_cand) {
-    for (int64_t i = gid; i < m; i += stride) add(cand[i]);
+    for (int64_t i = gid; i < m; i += stride) add(tk_canon(cand[i]));
   } else {
     const int64_t n4 = ((uintptr_t)dev & 15) == 0 ? n / 4 : 0;
     for (int64_t i = gid; i < n4; i += stride) {
@@ -669,7 +715,7 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_count_kernel(const float*
     const int m = sub_m[r], o = coff[r];
     int gt = 0, eq = 0;
     for (int j = threadIdx.x % WAVE; j < m; j += WAVE) {
-      const uint32_t key = cand[o + j];
+      const uint32_t key = tk_canon(cand[o + j]);
       gt += key > T;
       eq += key == T;
     }
@@ -718,13 +764,13 @@ __global__ __launch_bounds__(TK_THREADS) void tk_mb_scan_out_kernel(int n_sub, c
 }
 
 // Ordered write of sub-range r from its map: each lane takes one 32-bit word (16 consecutive
-// indices) per step; the words of 16 steps are loaded together (a store between a load and its use
-// makes the wait cover every earlier memory operation, so loads are batched rather than prefetched
-// one step ahead). Undecided indices take their keys from the sub-range's candidates in order,
-// which the wave reads 1024 at a time into its LDS buffer (when the band is the one key T, or on
-// the overflow route, they are the keys equal to T); keys equal to T are taken in index order while
-// fewer than kk precede them. Two wave scans order the lanes; the step's positions are staged in
-// the wave's LDS buffer and written out contiguously.
+// indices) per step; the words of 4 steps are loaded together and the 4 steps unrolled (a store
+// between a load and its use makes the wait cover every earlier memory operation, so loads are
+// batched rather than prefetched one step ahead). Undecided indices take their keys from the
+// sub-range's candidates in order, which the wave reads 1024 at a time into its LDS buffer (when
+// the band is the one key T, or on the overflow route, they are the keys equal to T); keys equal to
+// T are taken in index order while fewer than kk precede them. Two wave scans order the lanes; the
+// step's positions are staged in the wave's LDS buffer and written out contiguously.
 __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_write_kernel(int n, int sw, int n_sub, int k,
                                                                     const TopkState* __restrict__ st,
                                                                     const uint32_t* __restrict__ map,
@@ -747,19 +793,11 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_write_kernel(int n, int s
   int o_run = ooff[r], e_run = eqb[r], c_run = all_eq ? 0 : coff[r];
   const int c_stop = all_eq ? 0 : min(cap_c, c_run + sub_m[r]);
   int buf_base = c_run, buf_end = c_run;  // candidate ordinals held in cbuf
-  const int64_t i_begin = (int64_t)r * sw, i_end = std::min<int64_t>(n, i_begin + sw);
-  const int64_t last_word = (i_begin + sw) / 16 - 1;  // the sub-range's map words end here
-  constexpr int BATCH = 16;
-  uint32_t mw[BATCH];
-  for (int64_t base = i_begin; base < i_end; base += 1024) {
-    const int step = (int)((base - i_begin) / 1024) % BATCH;
-    if (step == 0)
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) mw[i] = map[std::min<int64_t>(base / 16 + 64 * i + lane, last_word)];
-    uint32_t w = mw[0];
-#pragma unroll
-    for (int i = 1; i < BATCH; ++i)
-      if (step == i) w = mw[i];
+  const int i_begin = r * sw;  // r * sw < n <= INT_MAX
+  const int steps = (int)((std::min<int64_t>(n, (int64_t)i_begin + sw) - i_begin + 1023) / 1024);
+  const uint32_t* mr = map + (size_t)i_begin / 16;  // the sub-range's sw / 16 map words
+  const int last = sw / 16 - 1;
+  auto step = [&](uint32_t w, int idx_step) {  // idx_step: the step's first index
     uint32_t take = w & 0x55555555u, eqm = 0;
     const uint32_t und = (w >> 1) & 0x55555555u;
     if (all_eq) {
@@ -783,7 +821,7 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_write_kernel(int n, int s
       int c = c_run + mpre - buf_base;
       for (uint32_t rest = und; rest; rest &= rest - 1) {
         const uint32_t bit = rest & (0u - rest);
-        const uint32_t key = c < 1024 ? cbuf[c] : 0u;
+        const uint32_t key = c < 1024 ? tk_canon(cbuf[c]) : 0u;
         ++c;
         if (key > T) take |= bit;
         else if (key == T) eqm |= bit;
@@ -795,12 +833,12 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_write_kernel(int n, int s
     const int owed = max(kk - e_run, 0);  // keys equal to T still to take at this step's start
     int o = (pk & 0xffff) + min(pk >> 16, owed);
     // equal keys of this lane still owed (fewer than kk precede them): its first ones in index order
-    int eq_owed = min(max(kk - e_run - (pk >> 16), 0), __popc(eqm));
+    int eq_owed = min(max(owed - (pk >> 16), 0), __popc(eqm));
     for (uint32_t rest = eqm; eq_owed > 0; --eq_owed) {
       take |= rest & (0u - rest);
       rest &= rest - 1;
     }
-    const int idx0 = (int)(base + 16 * lane);
+    const int idx0 = idx_step + 16 * lane;
     for (uint32_t rest = take; rest; rest &= rest - 1, ++o)
       if (o < 1024) stage[o] = idx0 + (__ffs(rest) - 1) / 2;
     const int taken = (ptot & 0xffff) + min(ptot >> 16, owed);
@@ -810,6 +848,14 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_write_kernel(int n, int s
     wave_sync();  // the stage is read before the next step writes it
     e_run += ptot >> 16;
     o_run += taken;
+  };
+  for (int s0 = 0; s0 < steps; s0 += 4) {
+    uint32_t mw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mw[q] = mr[min((s0 + q) * WAVE + lane, last)];
+    // every word is used (a step past the last runs on an empty word), so the loads stay together
+#pragma unroll
+    for (int q = 0; q < 4; ++q) step(s0 + q < steps ? mw[q] : 0u, i_begin + (s0 + q) * 1024);
   }
 }
 
