@@ -335,7 +335,7 @@ __device__ void tk_select2(const uint32_t (&key)[TK_SPT], uint32_t blo, uint32_t
 }
 
 // The stratified sample, one key a thread over many blocks (random reads need many CUs): stratum s
-// (indices [s n / S, (s + 1) n / S)) gives the key at a hashed offset inside it, stored at
+// (indices from s n / S to (s + 1) n / S, rounded down) gives the key at a hashed offset inside it, stored at
 // (s % 32) * 1024 + s / 32 so that the selecting block reads its keys coalesced.
 __global__ __launch_bounds__(256) void tk_mb_gather_kernel(const float* __restrict__ dev, int n, uint32_t* skey) {
   const int sidx = blockIdx.x * 256 + (int)threadIdx.x;

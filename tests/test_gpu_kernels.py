@@ -180,6 +180,37 @@ def test_topk_candidate_list_capacity_edges(n):
                 assert out.cpu().numpy().tolist() == want, (n, k, room, vals.data_ptr() % 16)
 
 
+def _sample_positions(n, s=32768):
+    """The whole-GPU selection's stratified sample: stratum j of s gives the value at a hashed offset
+    inside [j n / s, (j + 1) n / s) (Wellons' lowbias32 integer hash of j, scaled to n)."""
+    j = np.arange(s, dtype=np.uint64)
+    x = j.astype(np.uint32)
+    x ^= x >> np.uint32(16)
+    x = (x * np.uint32(0x7FEB352D)).astype(np.uint32)
+    x ^= x >> np.uint32(15)
+    x = (x * np.uint32(0x846CA68B)).astype(np.uint32)
+    x ^= x >> np.uint32(16)
+    jit = (x.astype(np.uint64) * np.uint64(n)) >> np.uint64(32)
+    return ((j * np.uint64(n) + jit) // np.uint64(s)).astype(np.int64)
+
+
+@pytest.mark.parametrize("direction", ["sample_low", "sample_high"])
+def test_topk_sampled_band_that_misses(direction):
+    """Values planted at exactly the sampled positions make the sample misjudge the distribution: too
+    many values lie above its band (sample_low) or too few at or above it (sample_high), so the
+    selection must take the fallback route (histograms over all n values, then the threshold's 16-bit
+    bin) and still give the oracle's unique answer."""
+    n = (1 << 20) + 3
+    rng = np.random.default_rng(7)
+    d = rng.random(n).astype(np.float32) + np.float32(1.0)
+    pos = _sample_positions(n)
+    assert pos.min() >= 0 and pos.max() < n and np.all(np.diff(pos) >= 0)
+    d[pos] = np.float32(1e-3) if direction == "sample_low" else np.float32(1e3)
+    say(f"topk band miss {direction} n={n}")
+    for k in (n // 7, n // 2):
+        assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (direction, k)
+
+
 @pytest.mark.parametrize("case", _golden.doc_span_cases())
 def test_doc_spans_golden(case):
     d, b, k, want = case
