@@ -855,7 +855,8 @@ __global__ __launch_bounds__(TK_WPB * WAVE) void tk_mb_write_kernel(int n, int s
     for (int q = 0; q < 4; ++q) mw[q] = mr[min((s0 + q) * WAVE + lane, last)];
     // every word is used (a step past the last runs on an empty word), so the loads stay together
 #pragma unroll
-    for (int q = 0; q < 4; ++q) step(s0 + q < steps ? mw[q] : 0u, i_begin + (s0 + q) * 1024);
+    for (int q = 0; q < 4; ++q)  // (an empty step's index is clamped: it must not pass INT_MAX)
+      step(s0 + q < steps ? mw[q] : 0u, i_begin + min(s0 + q, steps - 1) * 1024);
   }
 }
 

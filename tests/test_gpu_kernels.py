@@ -180,6 +180,35 @@ def test_topk_candidate_list_capacity_edges(n):
                 assert out.cpu().numpy().tolist() == want, (n, k, room, vals.data_ptr() % 16)
 
 
+def test_topk_whole_gpu_at_int32_max():
+    """n = 2^31 - 1, the largest n the ABI takes (the index arithmetic of every pass in 64 bits where it
+    can pass INT_MAX): too large for the oracle, so the unique answer is pinned by its properties,
+    checked on the GPU with torch: k positions strictly ascending, every selected value at least every
+    unselected one, and among the values equal to the threshold exactly the lowest-index ones taken.
+    Uniform [0, 1) float32 values tie often at this n, so the tie rule is exercised."""
+    torch = _torch()
+    n = (1 << 31) - 1
+    k = n * 15 // 100
+    say(f"topk int32 max n={n} k={k}")
+    g = torch.Generator(device="cuda").manual_seed(11)
+    d = torch.rand(n, device="cuda", generator=g)
+    out = torch.empty(k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(cf.topk_workspace_size(n, "token"), dtype=torch.uint8, device="cuda")
+    cf.topk_select(d, k, out, "token", None, ws)
+    torch.cuda.synchronize()
+    del ws
+    sel = out.long()
+    del out
+    assert bool((sel[1:] > sel[:-1]).all()) and int(sel[0]) >= 0 and int(sel[-1]) < n
+    mask = torch.zeros(n, dtype=torch.bool, device="cuda")
+    mask[sel] = True
+    t = d[sel].min()
+    assert float(d.masked_fill(mask, -1.0).max()) <= float(t)  # values lie in [0, 1)
+    eq = torch.nonzero(d == t).squeeze(1)  # ascending; a few hundred at this n
+    eq_sel = sel[d[sel] == t]
+    assert len(eq_sel) >= 1 and torch.equal(eq_sel, eq[: len(eq_sel)])
+
+
 def _sample_positions(n, s=32768):
     """The whole-GPU selection's stratified sample: stratum j of s gives the value at a hashed offset
     inside [j n / s, (j + 1) n / s) (Wellons' lowbias32 integer hash of j, scaled to n)."""
