@@ -143,10 +143,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_token_kernel(const float* __r
 // The same exact selection spread over the whole GPU for n >= TK_MB_MIN, reading the n keys once
 // in the usual case.
 //
-// The index range is cut into sub-ranges of sw indices, one wave each. A one-block pass draws a
-// stratified sample of TK_SAMPLE keys (one at a hashed offset inside each of TK_SAMPLE equal
-// strata) and takes two of its order statistics as bounds lo <= hi that bracket the threshold key
-// T (the k-th largest) with a margin of four standard deviations of the sample rank. One pass
+// The index range is cut into sub-ranges of sw indices, one wave each. A gather over many blocks
+// draws a stratified sample of TK_SAMPLE keys (one at a hashed offset inside each of TK_SAMPLE
+// near-equal strata), and one block takes two of its order statistics as bounds lo <= hi that
+// bracket the threshold key T (the k-th largest) with a margin of four standard deviations of the
+// sample rank. One pass
 // over the n keys then writes a map of 2 bits per index (taken: key > hi; undecided: lo <= key <=
 // hi) and appends the undecided keys, in index order, to their sub-range's slice of a candidate
 // list, counting both per sub-range. If fewer than k keys lie above hi and at least k at or above
