@@ -297,7 +297,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded uniform-random tokens, N(0,0.02) random-init weights)",
-        "config": {"workload": w.name, "model_shape": cfg.name, "layers": Ly, "n_ctx": N, "n_query": U,
+        "config": {"workload": w.name, "dims": cfg.name, "layers": Ly, "n_ctx": N, "n_query": U,
                    "chunks": f"{w.n_chunks}x{w.chunk_len}", "recompute_ratio": f"{w.rho_num}/{w.rho_den}",
                    "k": k, "selection": w.mode, "selection_layer": w.sel_layer,
                    "chunk_store": "HBM" if args.store == "device" else "pinned host memory, streamed per layer",
