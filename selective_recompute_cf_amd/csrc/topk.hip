@@ -269,8 +269,10 @@ __device__ __forceinline__ void wave_sync() {
 // different banks.
 constexpr int TK_HCOPIES = 16;
 
+constexpr int TK_SCOPIES = 4;  // the sample's selects see few keys a thread: fewer copies to clear and add
+
 struct TkSel {
-  uint32_t h[2][TK_HCOPIES][257];
+  uint32_t h[2][TK_SCOPIES][257];
   int wtot[2][256 / WAVE];
   uint32_t pre[2];
   int rem[2];
@@ -292,13 +294,13 @@ __device__ void tk_select2(const uint32_t (&key)[TK_SPT], uint32_t blo, uint32_t
   const int lane = threadIdx.x % WAVE, q = (threadIdx.x / 256) & 1, t = threadIdx.x % 256;
   const bool act_mine = q == 0 ? a0 : a1;
   for (int pass = 0; pass < 4; ++pass) {
-    for (int i = threadIdx.x; i < 2 * TK_HCOPIES * 257; i += TK_THREADS) (&s.h[0][0][0])[i] = 0u;
+    for (int i = threadIdx.x; i < 2 * TK_SCOPIES * 257; i += TK_THREADS) (&s.h[0][0][0])[i] = 0u;
     __syncthreads();
     const uint32_t mask = pass == 0 ? 0u : (0xffffffffu << (32 - 8 * pass));
     const int shift = 24 - 8 * pass;
     const uint32_t p0 = s.pre[0], p1 = s.pre[1], pre_mine = s.pre[q];
     const int r_mine = s.rem[q];
-    const int c = threadIdx.x % TK_HCOPIES;
+    const int c = threadIdx.x % TK_SCOPIES;
 #pragma unroll
     for (int j = 0; j < TK_SPT; j += STEP) {
       const uint32_t x = key[j];
@@ -312,7 +314,7 @@ __device__ void tk_select2(const uint32_t (&key)[TK_SPT], uint32_t blo, uint32_t
     int cnt = 0;
     if (threadIdx.x < 512)
 #pragma unroll
-      for (int cc = 0; cc < TK_HCOPIES; ++cc) cnt += (int)s.h[q][cc][255 - t];
+      for (int cc = 0; cc < TK_SCOPIES; ++cc) cnt += (int)s.h[q][cc][255 - t];
     int incl = cnt;
 #pragma unroll
     for (int off = 1; off < WAVE; off <<= 1) {
