@@ -91,12 +91,12 @@ QWEN3_8B = ModelCfg("qwen3-8b-shape", 36, 4096, 32, 8, 128, 12288, 151936, 1.0e6
 LLAMA3_70B = ModelCfg("llama-3-70b-shape", 80, 8192, 64, 8, 128, 28672, 128256, 5.0e5, 1e-5, False, "bf16")
 
 WORKLOADS: Dict[str, Workload] = {
-    "tiny": Workload("tiny-4x128+32-r15", TINY, 4, 128, 32, 15, 100),
-    "llama8b": Workload("llama3-8b-6x512+64-r15", LLAMA3_8B, 6, 512, 64, 15, 100),
-    "qwen8b": Workload("qwen3-8b-10x1024+128-r30", QWEN3_8B, 10, 1024, 128, 30, 100),
-    "rolling": Workload("rolling-llama3-8b-20x512+64-r5", LLAMA3_8B, 20, 512, 64, 5, 100,
+    "tiny": Workload("tiny-4x128+32-rho15", TINY, 4, 128, 32, 15, 100),
+    "llama8b": Workload("llama3-8b-6x512+64-rho15", LLAMA3_8B, 6, 512, 64, 15, 100),
+    "qwen8b": Workload("qwen3-8b-10x1024+128-rho30", QWEN3_8B, 10, 1024, 128, 30, 100),
+    "rolling": Workload("rolling-llama3-8b-20x512+64-rho5", LLAMA3_8B, 20, 512, 64, 5, 100,
                         mode="doc", steps=50),
-    "llama70b": Workload("llama3-70b-16x1024+256-r10", LLAMA3_70B, 16, 1024, 256, 10, 100),
+    "llama70b": Workload("llama3-70b-16x1024+256-rho10", LLAMA3_70B, 16, 1024, 256, 10, 100),
 }
 
 
