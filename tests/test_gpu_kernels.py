@@ -137,6 +137,19 @@ def test_topk_large_n_multiblock_bit_exact(n):
             assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (n, trial, k)
 
 
+def test_topk_whole_gpu_16m_bit_exact():
+    """n = 2^24 + 7: sub-ranges of 4096 indices (four write steps each, a ragged last one), against the
+    oracle on skewed values like squared key deviations and on values with runs of ties."""
+    n = (1 << 24) + 7
+    rng = np.random.default_rng(24)
+    say(f"topk 16M n={n}")
+    for trial in range(2):
+        d = ((rng.standard_normal(n).astype(np.float32) ** 2) * np.float32(3.0) if trial == 0 else
+             np.round(rng.random(n) * 1000).astype(np.float32))
+        for k in (n * 15 // 100, n // 2 + 1):
+            assert _gpu_topk(d, k) == oracle.select_topk(d, k).tolist(), (trial, k)
+
+
 def _order_keys(d):
     """Order-preserving 32-bit keys of float32 values (NaN as +inf, -0 as +0), for the test to find
     how many values share the threshold key's top 16 bits."""
