@@ -51,6 +51,52 @@ def test_reposition_matches_oracle(dtype, hd):
     assert np.all(kb[0] == 7.0) and np.all(kb[1:, ~covered] == 7.0)
 
 
+@pytest.mark.parametrize("Ly,N,chunk", [(31, 3072, 512), (79, 16384, 1024)])
+def test_reposition_full_size_sampled_layers(Ly, N, chunk):
+    """The launch the sweep times: every layer after the selection layer of the Llama-3-8B-shaped
+    request (31 x 6 x 512 rows) and of the 70B-shaped one (79 x 16 x 1024 rows) re-positioned in one
+    call, chunks encoded at position 0 and placed at their request offsets. Seeded bf16 inputs drawn
+    on the GPU; the first, a middle and the last layer are compared with the oracle over every row."""
+    torch = _torch()
+    cfg = synth.LLAMA3_8B.replace(n_layers=Ly)
+    H, hd, kvd = cfg.n_kv_heads, cfg.head_dim, cfg.kv_dim
+    say(f"reposition full size Ly={Ly} N={N}")
+    ctx = context(cfg, max_pos=2 * N + 1)
+    g = torch.Generator(device="cuda").manual_seed(N + Ly)
+    ks = torch.randn((Ly, N, kvd), device="cuda", generator=g).to(torch.bfloat16)
+    vs = torch.randn((Ly, N, kvd), device="cuda", generator=g).to(torch.bfloat16)
+    kb, vb = torch.empty_like(ks), torch.empty_like(vs)
+    table = [(i * chunk, 0, i * chunk, chunk) for i in range(N // chunk)]
+    ctx.rope_reposition(ks, vs, kb, vb, table, 0, Ly)
+    torch.cuda.synchronize()
+    for layer in (0, Ly // 2, Ly - 1):
+        k_in = host(ks[layer]).reshape(1, N, H, hd)
+        v_in = host(vs[layer]).reshape(1, N, H, hd)
+        kref, vref = oracle.stitch(k_in, v_in, table, N, [0], cfg.rope_theta, np.float64, n_total=N)
+        compare(f"K layer {layer}", host(kb[layer]).reshape(N, H, hd), kref[0], atol=1e-6, rtol=2.0 ** -8)
+        np.testing.assert_array_equal(host(vb[layer]).reshape(N, H, hd), vref[0])
+    ctx.close()
+
+
+@pytest.mark.parametrize("n", [32 * 3072, 1 << 20])
+def test_deviation_full_size_sampled_rows(n):
+    """The deviation launches the sweep times (all 32 layers of the request's 3072 rows at once, and
+    a million rows), kvd = 1024, bf16 inputs drawn on the GPU from a seed; 2000 sampled rows against
+    the oracle."""
+    torch = _torch()
+    say(f"deviation full size n={n}")
+    g = torch.Generator(device="cuda").manual_seed(n)
+    kn = torch.randn((n, 1024), device="cuda", generator=g).to(torch.bfloat16)
+    kr = torch.randn((n, 1024), device="cuda", generator=g).to(torch.bfloat16)
+    dev = torch.empty(n, dtype=torch.float32, device="cuda")
+    cf.kv_deviation(kn, kr, dev)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(n).choice(n, 2000, replace=False))
+    idx = torch.from_numpy(rows).cuda()
+    want = oracle.kv_deviation(host(kn[idx]), host(kr[idx]))
+    compare("dev", host(dev[idx]), want, atol=0.0, rtol=1e-5)
+
+
 def test_reposition_rejects_bad_chunks():
     torch = _torch()
     cfg = synth.TINY
